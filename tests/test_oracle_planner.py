@@ -1,0 +1,91 @@
+"""Pins of the oracle's leaf planner: the leaves partition the tile grid, fit
+the budget unless they are a single tile, their overlap counts equal the
+binning's brute-force counts, and the plan is the depth-first result of the
+halving rule (re-derived here with brute-force per-tile counts)."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from differentiable_gaussian_splatting_amd import scenes
+
+COST = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=4096)
+
+
+def brute_counts(rect_c, TW, TH):
+    cnt = np.zeros((TH, TW), np.int64)
+    for x0, y0, x1, y1 in rect_c:
+        cnt[y0:y1, x0:x1] += 1
+    return cnt
+
+
+def replan(cnt, W, H, budget):
+    """The halving rule, with the overlap count of a region taken by brute force."""
+    out = []
+
+    def est(r):
+        tx0, ty0, tx1, ty1 = r
+        I = int(cnt[ty0:ty1, tx0:tx1].sum())
+        P = (min(tx1 * 16, W) - tx0 * 16) * (min(ty1 * 16, H) - ty0 * 16)
+        T = (tx1 - tx0) * (ty1 - ty0)
+        return COST["b_isect"] * I + COST["b_pixel"] * P + COST["b_tile"] * T + COST["b_const"]
+
+    def rec(r):
+        tx0, ty0, tx1, ty1 = r
+        e = est(r)
+        w, h = tx1 - tx0, ty1 - ty0
+        if e <= budget or (w == 1 and h == 1):
+            out.append((tx0, ty0, tx1, ty1, e))
+            return
+        if w >= h:
+            m = tx0 + w // 2
+            rec((tx0, ty0, m, ty1)); rec((m, ty0, tx1, ty1))
+        else:
+            m = ty0 + h // 2
+            rec((tx0, ty0, tx1, m)); rec((tx0, m, tx1, ty1))
+
+    rec((0, 0, cnt.shape[1], cnt.shape[0]))
+    return out
+
+
+@pytest.mark.parametrize("budget", [10**9, 400_000, 90_000, 20_000, 1])
+def test_planner_partition_budget_and_rule(oracle_lib, budget):
+    w = scenes.make_workload("c3_gmm4k", n=20_000, width=400, height=250, posed=True)
+    cam = w.camera
+    p = oracle_lib.project(cam, w.scene, "f32")
+    rect_c = p["rect"][p["cand"]]
+    leaves, sat = oracle_lib.plan_leaves(cam, rect_c, budget, COST, with_sat=True)
+    TW, TH = cam.tiles_x, cam.tiles_y
+    cover = np.zeros((TH, TW), np.int64)
+    for L in leaves:
+        cover[L["ty0"]:L["ty1"], L["tx0"]:L["tx1"]] += 1
+        if not L["over_budget"]:
+            assert L["est_bytes"] <= budget
+        else:
+            assert (L["tx1"] - L["tx0"], L["ty1"] - L["ty0"]) == (1, 1) and L["est_bytes"] > budget
+    assert (cover == 1).all()
+    cnt = brute_counts(rect_c, TW, TH)
+    assert int(sat[-1, -1]) == int(cnt.sum())
+    expect = replan(cnt, cam.width, cam.height, budget)
+    got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in leaves]
+    assert got == expect
+    # a leaf's estimate uses the same overlap count the binning produces
+    for L in leaves[:: max(1, len(leaves) // 7)]:
+        b = oracle_lib.bin_leaf(TW, oracle_lib.rect(L["tx0"], L["ty0"], L["tx1"], L["ty1"]),
+                                rect_c, p["depth"][p["cand"]])
+        r = oracle_lib.rect(L["tx0"], L["ty0"], L["tx1"], L["ty1"])
+        assert oracle_lib.leaf_estimate(cam, r, b["n_isect"], COST) == L["est_bytes"]
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 200), st.integers(1, 150), st.integers(0, 60), st.integers(1, 200_000),
+       st.integers(0, 2**31 - 1))
+def test_planner_random_rects(oracle_lib, W, H, n, budget, seed):
+    rng = np.random.default_rng(seed)
+    cam = scenes.pinhole_camera(W, H)
+    TW, TH = cam.tiles_x, cam.tiles_y
+    x0 = rng.integers(0, TW, n); x1 = np.minimum(TW, x0 + 1 + rng.integers(0, TW, n))
+    y0 = rng.integers(0, TH, n); y1 = np.minimum(TH, y0 + 1 + rng.integers(0, TH, n))
+    rect_c = np.stack([x0, y0, x1, y1], 1).astype(np.int32).reshape(-1, 4)
+    leaves = oracle_lib.plan_leaves(cam, rect_c, budget, COST)
+    got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in leaves]
+    assert got == replan(brute_counts(rect_c, TW, TH), W, H, budget)

@@ -1,0 +1,209 @@
+"""Pins of the oracle's binning, compositing and losses: brute force on tiny
+inputs, closed-form images, transmittance invariants, SSIM closed forms."""
+import math
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from differentiable_gaussian_splatting_amd import scenes
+from tests.test_oracle_projection import one_scene
+
+SQRT_PI = math.sqrt(math.pi)
+
+
+# ------------------------------------------------------------------ binning
+
+@settings(max_examples=200, deadline=None)
+@given(st.data())
+def test_binning_brute_force(oracle_lib, data):
+    TW = data.draw(st.integers(1, 9))
+    TH = data.draw(st.integers(1, 7))
+    n = data.draw(st.integers(0, 40))
+    rects, depths = [], []
+    for _ in range(n):
+        x0 = data.draw(st.integers(0, TW - 1)); x1 = data.draw(st.integers(x0 + 1, TW))
+        y0 = data.draw(st.integers(0, TH - 1)); y1 = data.draw(st.integers(y0 + 1, TH))
+        rects.append((x0, y0, x1, y1))
+        depths.append(data.draw(st.sampled_from([0.5, 1.0, 1.5, 2.0, 7.25, 1e3])))  # many ties
+    lx0 = data.draw(st.integers(0, TW - 1)); lx1 = data.draw(st.integers(lx0 + 1, TW))
+    ly0 = data.draw(st.integers(0, TH - 1)); ly1 = data.draw(st.integers(ly0 + 1, TH))
+    rect = np.array(rects, np.int32).reshape(-1, 4)
+    depth = np.array(depths, np.float32)
+    leaf = oracle_lib.rect(lx0, ly0, lx1, ly1)
+    b = oracle_lib.bin_leaf(TW, leaf, rect, depth)
+    # brute force: all (tile, depth, slot) triples, sorted as tuples
+    ent = sorted((ty * TW + tx, float(depth[j]), j) for j, (x0, y0, x1, y1) in enumerate(rects)
+                 for ty in range(max(y0, ly0), min(y1, ly1)) for tx in range(max(x0, lx0), min(x1, lx1)))
+    assert b["n_isect"] == len(ent)
+    assert b["values"].tolist() == [e[2] for e in ent]
+    keys = [(e[0] << 32) | int(np.float32(e[1]).view(np.uint32)) for e in ent]
+    assert b["keys"].tolist() == keys
+    cnt = [sum(1 for e in ent if e[0] == ty * TW + tx) for ty in range(ly0, ly1) for tx in range(lx0, lx1)]
+    assert b["counts"].tolist() == cnt
+    assert b["offsets"].tolist() == list(np.concatenate([[0], np.cumsum(cnt)]).astype(int))
+
+
+# ------------------------------------------------------------------ compositing
+
+def single(cam, mu, ls, q, logit, rgb_target):
+    # degree-0 colour c: coefficient (c - 0.5) * 2 sqrt(pi)
+    sh = (np.asarray(rgb_target, np.float64) - 0.5) * 2 * SQRT_PI
+    return one_scene([mu], [ls], [q], [logit], sh.reshape(1, 1, 3), 0)
+
+
+@pytest.mark.parametrize("mode", ["reference", "parity"])
+def test_single_gaussian_closed_form(oracle_lib, mode):
+    cam = scenes.pinhole_camera(80, 56)
+    sc = single(cam, [0.13, -0.07, 3.0], [-2.3, -2.9, -2.6], [0.8, 0.1, -0.3, 0.5], 1.7, [0.9, 0.4, 0.2])
+    r = oracle_lib.train_view(cam, sc, np.zeros((3, 56, 80), np.float32), mode=mode)
+    p = r["proj64"]
+    A, B, Cc = p["conic"][0]
+    x, y = p["xy"][0]
+    o = p["opacity"][0]
+    rgb = p["rgb"][0]
+    tx0, ty0, tx1, ty1 = r["proj32"]["rect"][0]
+    py, px = np.mgrid[0:56, 0:80] + 0.5
+    dx, dy = px - x, py - y
+    al = np.minimum(0.99, o * np.exp(-0.5 * (A * dx * dx + Cc * dy * dy) - B * dx * dy))
+    inside = (px >= 16 * tx0) & (px < 16 * tx1) & (py >= 16 * ty0) & (py < 16 * ty1)
+    al = np.where((al >= 1 / 255) & inside, al, 0.0)
+    exp_img = rgb[:, None, None] * al[None]
+    tol = 1e-12 if mode == "reference" else 2e-6
+    np.testing.assert_allclose(r["image"], exp_img, atol=tol)
+    assert (al > 0).sum() > 50
+
+
+@pytest.mark.parametrize("mode", ["reference", "parity"])
+def test_transmittance_partition_of_unity(oracle_lib, mode):
+    # all colours 1 and black background: out = sum alpha_i T_i = 1 - T_final
+    rng = np.random.default_rng(4)
+    w = scenes.make_workload("c1_small", n=1500, width=64, height=48, posed=True)
+    sc = w.scene
+    sc.sh[:] = np.float32(0.5 * 2 * SQRT_PI)
+    r = oracle_lib.train_view(w.camera, sc, w.target, mode=mode)
+    assert (r["proj32"]["rgb"][r["proj32"]["cand"]] == 1).all() or mode == "reference"
+    tol = 1e-12 if mode == "reference" else 3e-6
+    for ch in range(3):
+        np.testing.assert_allclose(r["image"][ch], 1 - r["t_final"], atol=tol)
+    assert r["t_final"].min() >= 1e-4
+    assert (r["t_final"] < 0.5).mean() > 0.2 and (r["t_final"] < 2e-4).any()
+    del rng
+
+
+def test_depth_order_two_gaussians(oracle_lib):
+    cam = scenes.pinhole_camera(64, 64)
+    # same footprint centre, different depths; the nearer one is listed second
+    sc = one_scene([[0, 0, 6.0], [0, 0, 3.0]], [[-2.0] * 3, [-2.6] * 3], [[1, 0, 0, 0]] * 2, [0.2, -0.4],
+                   np.stack([(np.array([0.1, 0.9, 0.3]) - 0.5) * 2 * SQRT_PI,
+                             (np.array([0.8, 0.2, 0.6]) - 0.5) * 2 * SQRT_PI]).reshape(2, 1, 3), 0)
+    r = oracle_lib.train_view(cam, sc, np.zeros((3, 64, 64), np.float32), mode="reference")
+    p = r["proj64"]
+
+    def alpha(i):
+        A, B, Cc = p["conic"][i]
+        d = np.array([32.5, 32.5]) - p["xy"][i]
+        return min(0.99, p["opacity"][i] * math.exp(-0.5 * (A * d[0] ** 2 + Cc * d[1] ** 2) - B * d[0] * d[1]))
+
+    a_near, a_far = alpha(1), alpha(0)
+    exp_px = p["rgb"][1] * a_near + p["rgb"][0] * a_far * (1 - a_near)
+    np.testing.assert_allclose(r["image"][:, 32, 32], exp_px, rtol=1e-12)
+
+
+def test_stop_before_transmittance_falls_below_threshold(oracle_lib):
+    cam = scenes.pinhole_camera(32, 32)
+    # three nearly opaque, wide Gaussians on the axis: alpha clamps to 0.99;
+    # after the first T = 0.01, the second would take T to 1e-4 (below in f32)
+    n = 3
+    sc = one_scene([[0, 0, 3.0], [0, 0, 3.5], [0, 0, 4.0]], [[3.0] * 3] * n, [[1, 0, 0, 0]] * n,
+                   [12.0] * n, np.tile((np.array([0.25, 0.5, 1.0]) - 0.5) * 2 * SQRT_PI, (n, 1)).reshape(n, 1, 3), 0)
+    r = oracle_lib.train_view(cam, sc, np.zeros((3, 32, 32), np.float32), mode="parity")
+    assert (r["last"] == 1).all()
+    np.testing.assert_allclose(r["t_final"], np.float32(1) - np.float32(0.99), rtol=0)
+    np.testing.assert_allclose(r["image"][:, 5, 7], np.float32(0.99) * np.array([0.25, 0.5, 1.0], np.float32),
+                               rtol=1e-6)
+
+
+def test_permutation_invariance_bitwise(oracle_lib):
+    rng = np.random.default_rng(8)
+    w = scenes.make_workload("c2_hd", n=500, width=96, height=80, posed=True)
+    sc = w.scene
+    r1 = oracle_lib.train_view(w.camera, sc, w.target)
+    perm = rng.permutation(sc.n)
+    sc2 = scenes.Scene(sc.means[perm], sc.log_scales[perm], sc.quats[perm], sc.logits[perm], sc.sh[perm], 3)
+    r2 = oracle_lib.train_view(w.camera, sc2, w.target)
+    d = r1["proj32"]["depth"][r1["ids"]]
+    assert np.unique(d).size == d.size
+    assert np.array_equal(r1["image"], r2["image"])
+    assert np.array_equal(r1["last"] > 0, r2["last"] > 0)
+    inv = np.argsort(perm)
+    np.testing.assert_allclose(r2["grad3d"][inv], r1["grad3d"], rtol=1e-9, atol=1e-15)
+
+
+# ------------------------------------------------------------------ losses
+
+def test_l1_constant_images(oracle_lib):
+    cam = scenes.pinhole_camera(40, 24)
+    img = np.full((3, 24, 40), 0.75)
+    tgt = np.full((3, 24, 40), 0.25, np.float32)
+    d = np.zeros((3, 24, 40))
+    L = oracle_lib.loss_l1(cam, oracle_lib.full_rect(cam), img, tgt, d)
+    assert L == pytest.approx(0.5, rel=1e-15)
+    np.testing.assert_allclose(d, 1 / (3 * 40 * 24))
+
+
+def gauss_window():
+    g = np.exp(-((np.arange(11) - 5.0) ** 2) / (2 * 1.5 ** 2))
+    return g / g.sum()
+
+
+def test_ssim_identical_images_is_one(oracle_lib):
+    rng = np.random.default_rng(1)
+    cam = scenes.pinhole_camera(37, 29)
+    img = rng.random((3, 29, 37))
+    L, d, ssim = oracle_lib.loss_ssim(cam, img, img.astype(np.float32).astype(np.float64).astype(np.float32))
+    assert ssim == pytest.approx(1.0, abs=1e-12) or abs(ssim - 1) < 1e-6
+    img32 = img.astype(np.float32)
+    L, d, ssim = oracle_lib.loss_ssim(cam, img32.astype(np.float64), img32)
+    assert abs(ssim - 1.0) < 1e-12 and abs(L) < 1e-12
+
+
+def test_ssim_constant_images_closed_form(oracle_lib):
+    # constant x = a, y = b with zero padding: with m(p) the window mass
+    # inside the image, mu = a m, var_x = a^2 m (1 - m), cov = a b m (1 - m)
+    W, H, a, b = 23, 17, 0.8, 0.3
+    cam = scenes.pinhole_camera(W, H)
+    g = gauss_window()
+    mx = np.array([g[max(0, 5 - p):min(11, 5 + W - p)].sum() for p in range(W)])
+    my = np.array([g[max(0, 5 - p):min(11, 5 + H - p)].sum() for p in range(H)])
+    m = my[:, None] * mx[None, :]
+    C1, C2 = 0.01 ** 2, 0.03 ** 2
+    mu_x, mu_y = a * m, b * m
+    vx, vy, cxy = a * a * m * (1 - m), b * b * m * (1 - m), a * b * m * (1 - m)
+    S = ((2 * mu_x * mu_y + C1) * (2 * cxy + C2)) / ((mu_x ** 2 + mu_y ** 2 + C1) * (vx + vy + C2))
+    L, d, ssim = oracle_lib.loss_ssim(cam, np.full((3, H, W), a), np.full((3, H, W), b, np.float32), lam=0.2)
+    bf = float(np.float32(b))
+    mu_y = bf * m
+    vy, cxy = bf * bf * m * (1 - m), a * bf * m * (1 - m)
+    S = ((2 * mu_x * mu_y + C1) * (2 * cxy + C2)) / ((mu_x ** 2 + mu_y ** 2 + C1) * (vx + vy + C2))
+    assert ssim == pytest.approx(S.mean(), rel=1e-10)
+    assert L == pytest.approx(0.8 * abs(a - bf) + 0.2 * (1 - S.mean()), rel=1e-10)
+
+
+def test_ssim_gradient_finite_differences(oracle_lib):
+    rng = np.random.default_rng(6)
+    W, H = 19, 14
+    cam = scenes.pinhole_camera(W, H)
+    x = rng.random((3, H, W))
+    y = rng.random((3, H, W)).astype(np.float32)
+    L, d, _ = oracle_lib.loss_ssim(cam, x, y)
+    for _ in range(40):
+        c, i, j = rng.integers(3), rng.integers(H), rng.integers(W)
+        h = 1e-6
+        xp, xm = x.copy(), x.copy()
+        xp[c, i, j] += h
+        xm[c, i, j] -= h
+        if np.sign(xp[c, i, j] - y[c, i, j]) != np.sign(xm[c, i, j] - y[c, i, j]):
+            continue
+        fd = (oracle_lib.loss_ssim(cam, xp, y)[0] - oracle_lib.loss_ssim(cam, xm, y)[0]) / (2 * h)
+        assert fd == pytest.approx(d[c, i, j], rel=1e-5, abs=1e-10)
