@@ -1,0 +1,771 @@
+// gs_api.cpp -- the C ABI of libgsmi (declared in include/gs.h): context,
+// allocation accounting, kernel timing, handles, argument checking and the
+// whole-view driver.  Every numeric step runs in the HIP kernels of the .hip
+// files; this file only allocates, launches, synchronises and checks.
+#include <cstdarg>
+#include <cstring>
+#include <algorithm>
+#include <cmath>
+#include <new>
+
+#include "gs_internal.h"
+
+gs_status launch_project_write(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
+                               const uint32_t* flag, const uint32_t* slot);
+
+// ---------------------------------------------------------------------------
+// errors
+
+gs_status gs_fail(gs_ctx* ctx, gs_status st, const char* fmt, ...)
+{
+    if (ctx) {
+        char buf[1024];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof(buf), fmt, ap);
+        va_end(ap);
+        ctx->err = buf;
+    }
+    return st;
+}
+
+// ---------------------------------------------------------------------------
+// memory
+
+void* gs_malloc(gs_ctx* ctx, size_t bytes, int cat, std::vector<GsAlloc>* owner)
+{
+    bytes = (bytes + 255) & ~(size_t)255;
+    if (bytes == 0) bytes = 256;
+    void* p = nullptr;
+    if (ctx->alloc) {
+        p = ctx->alloc(ctx->user, bytes, (void*)ctx->stream);
+    } else if (hipMallocAsync(&p, bytes, ctx->stream) != hipSuccess) {
+        p = nullptr;
+    }
+    if (!p) {
+        gs_fail(ctx, GS_ERR_OOM, "allocation of %zu bytes failed", bytes);
+        return nullptr;
+    }
+    ctx->live += bytes;
+    ctx->live_cat[cat] += bytes;
+    ctx->peak = std::max(ctx->peak, ctx->live);
+    ctx->peak_cat[cat] = std::max(ctx->peak_cat[cat], ctx->live_cat[cat]);
+    ctx->n_alloc += 1;
+    owner->push_back(GsAlloc{p, bytes, cat});
+    return p;
+}
+
+static void release_alloc(gs_ctx* ctx, const GsAlloc& a)
+{
+    if (ctx->free_fn) ctx->free_fn(ctx->user, a.ptr, a.bytes, (void*)ctx->stream);
+    else (void)hipFreeAsync(a.ptr, ctx->stream);
+    ctx->live -= a.bytes;
+    ctx->live_cat[a.cat] -= a.bytes;
+    ctx->n_free += 1;
+}
+
+void gs_free_all(gs_ctx* ctx, std::vector<GsAlloc>* owner)
+{
+    for (const GsAlloc& a : *owner) release_alloc(ctx, a);
+    owner->clear();
+}
+
+void gs_free_one(gs_ctx* ctx, std::vector<GsAlloc>* owner, void* ptr)
+{
+    for (size_t k = 0; k < owner->size(); ++k)
+        if ((*owner)[k].ptr == ptr) {
+            release_alloc(ctx, (*owner)[k]);
+            owner->erase(owner->begin() + (long)k);
+            return;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// timing
+
+static hipEvent_t take_event(gs_ctx* ctx)
+{
+    if (!ctx->event_pool.empty()) {
+        hipEvent_t e = ctx->event_pool.back();
+        ctx->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+GsTimerScope::GsTimerScope(gs_ctx* c, const char* n) : ctx(c), name(n)
+{
+    if (!ctx->timing) return;
+    hipEvent_t s = take_event(ctx);
+    stop = take_event(ctx);
+    if (!s || !stop) {
+        stop = nullptr;
+        return;
+    }
+    (void)hipEventRecord(s, ctx->stream);
+    ctx->timers.push_back(GsTimerRec{name, s, stop});
+}
+
+GsTimerScope::~GsTimerScope()
+{
+    if (stop) (void)hipEventRecord(stop, ctx->stream);
+}
+
+// ---------------------------------------------------------------------------
+// handles
+
+template <typename H>
+static H* new_handle(gs_ctx* ctx, uint32_t magic)
+{
+    H* h = new (std::nothrow) H();
+    if (!h) return nullptr;
+    h->magic = magic;
+    h->ctx = ctx;
+    return h;
+}
+
+static bool handle_ok(const gs_ctx* ctx, const void* h, uint32_t magic)
+{
+    if (!h) return false;
+    const GsHandle* g = static_cast<const GsHandle*>(h);
+    return g->magic == magic && g->ctx == ctx;
+}
+
+static void destroy_handle(gs_ctx* ctx, GsHandle* h)
+{
+    gs_free_all(ctx, &h->allocs);
+    const uint32_t magic = h->magic;
+    h->magic = 0;
+    // delete through the concrete type
+    if (magic == kMagicProj) delete static_cast<gs_proj*>(h);
+    else if (magic == kMagicBins) delete static_cast<gs_bins*>(h);
+    else if (magic == kMagicRaster) delete static_cast<gs_raster*>(h);
+    else delete h;
+}
+
+// ---------------------------------------------------------------------------
+// read-back helper: copy `bytes` device bytes to the pinned buffer and wait
+
+static gs_status readback(gs_ctx* ctx, const void* dev, size_t bytes, void* host)
+{
+    GS_HIP(ctx, hipMemcpyAsync(ctx->pinned, dev, bytes, hipMemcpyDeviceToHost, ctx->stream));
+    GS_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    std::memcpy(host, ctx->pinned, bytes);
+    return GS_OK;
+}
+
+static gs_status check_camera(gs_ctx* ctx, const gs_camera* cam)
+{
+    if (!cam) return gs_fail(ctx, GS_ERR_INVALID_ARG, "camera is NULL");
+    if (cam->width < 1 || cam->height < 1 || cam->width > (1 << 20) || cam->height > (1 << 20))
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "image size %d x %d out of range", cam->width, cam->height);
+    const int64_t tiles = (int64_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
+    if (tiles >= (1ll << 31)) return gs_fail(ctx, GS_ERR_OVERFLOW, "too many tiles");
+    if (!(cam->fx > 0.0f) || !(cam->fy > 0.0f) || !std::isfinite(cam->fx) || !std::isfinite(cam->fy))
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "focal lengths must be positive and finite");
+    return GS_OK;
+}
+
+static gs_status check_params(gs_ctx* ctx, const gs_params* p)
+{
+    if (!p) return gs_fail(ctx, GS_ERR_INVALID_ARG, "params is NULL");
+    if (p->n < 0) return gs_fail(ctx, GS_ERR_INVALID_ARG, "negative Gaussian count");
+    if (p->n >= (1ll << 31)) return gs_fail(ctx, GS_ERR_OVERFLOW, "at most 2^31 - 1 Gaussians");
+    if (p->sh_degree < 0 || p->sh_degree > 3) return gs_fail(ctx, GS_ERR_INVALID_ARG, "sh_degree must be 0..3");
+    if (p->n > 0 && (!p->means || !p->log_scales || !p->quats || !p->opacity_logits || !p->sh))
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "a parameter pointer is NULL");
+    return GS_OK;
+}
+
+extern "C" {
+
+// ---------------------------------------------------------------------------
+// context
+
+gs_status gs_ctx_create(gs_ctx** out, void* stream, gs_alloc_fn alloc, gs_free_fn free_fn, void* user)
+{
+    if (!out) return GS_ERR_INVALID_ARG;
+    *out = nullptr;
+    if ((alloc == nullptr) != (free_fn == nullptr)) return GS_ERR_INVALID_ARG;
+    gs_ctx* c = new (std::nothrow) gs_ctx();
+    if (!c) return GS_ERR_OOM;
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        return GS_ERR_DEVICE;
+    }
+    c->stream = (hipStream_t)stream;
+    c->alloc = alloc;
+    c->free_fn = free_fn;
+    c->user = user;
+    if (hipHostMalloc(&c->pinned, 256, hipHostMallocDefault) != hipSuccess) {
+        delete c;
+        return GS_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, c->device) == hipSuccess) {
+        c->num_cu = prop.multiProcessorCount;
+        c->max_lds = prop.sharedMemPerBlock;
+    }
+    *out = c;
+    return GS_OK;
+}
+
+void gs_ctx_destroy(gs_ctx* ctx)
+{
+    if (!ctx) return;
+    (void)hipStreamSynchronize(ctx->stream);
+    for (auto& t : ctx->timers) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+    }
+    for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
+    if (ctx->pinned) (void)hipHostFree(ctx->pinned);
+    delete ctx;
+}
+
+const char* gs_last_error(const gs_ctx* ctx) { return ctx ? ctx->err.c_str() : "no context"; }
+
+gs_status gs_mem_stats_get(const gs_ctx* ctx, gs_mem_stats* out)
+{
+    if (!ctx || !out) return GS_ERR_INVALID_ARG;
+    out->live_bytes = ctx->live;
+    out->peak_bytes = ctx->peak;
+    for (int k = 0; k < GS_MEM_NCAT; ++k) {
+        out->live_by_cat[k] = ctx->live_cat[k];
+        out->peak_by_cat[k] = ctx->peak_cat[k];
+    }
+    out->n_alloc = ctx->n_alloc;
+    out->n_free = ctx->n_free;
+    return GS_OK;
+}
+
+gs_status gs_mem_reset_peak(gs_ctx* ctx)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    ctx->peak = ctx->live;
+    for (int k = 0; k < GS_MEM_NCAT; ++k) ctx->peak_cat[k] = ctx->live_cat[k];
+    return GS_OK;
+}
+
+gs_status gs_set_timing(gs_ctx* ctx, int32_t on)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    ctx->timing = on != 0;
+    return GS_OK;
+}
+
+gs_status gs_reset_timing(gs_ctx* ctx)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    GS_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    for (auto& t : ctx->timers) {
+        ctx->event_pool.push_back(t.start);
+        ctx->event_pool.push_back(t.stop);
+    }
+    ctx->timers.clear();
+    return GS_OK;
+}
+
+gs_status gs_kernel_time(gs_ctx* ctx, const char* name, double* total_ms, int64_t* launches)
+{
+    if (!ctx || !name || !total_ms || !launches) return GS_ERR_INVALID_ARG;
+    GS_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    double tot = 0.0;
+    int64_t cnt = 0;
+    for (auto& t : ctx->timers)
+        if (std::strcmp(t.name, name) == 0) {
+            float ms = 0.0f;
+            GS_HIP(ctx, hipEventElapsedTime(&ms, t.start, t.stop));
+            tot += ms;
+            cnt += 1;
+        }
+    *total_ms = tot;
+    *launches = cnt;
+    return GS_OK;
+}
+
+gs_cost_model gs_default_cost_model(void)
+{
+    // bytes the library allocates for one leaf (L1 fused):
+    //   per intersection: composite key u64 + sorted slot u32 + merge scratch u64
+    //   per pixel: T_final f32 + last u32 + dL/dout 3 x f32
+    //   per tile: counts i32, cursor u32, offsets u64, 4 L1 partials f64
+    //   constant: scan block sums, allocation rounding, small buffers
+    gs_cost_model c;
+    c.b_isect = 20;
+    c.b_pixel = 20;
+    c.b_tile = 64;
+    c.b_const = 1u << 20;
+    return c;
+}
+
+// ---------------------------------------------------------------------------
+// projection
+
+gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, gs_proj** out, int64_t* n_cand)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (!out || !n_cand) return gs_fail(ctx, GS_ERR_INVALID_ARG, "out / n_cand is NULL");
+    gs_status st;
+    if ((st = check_camera(ctx, cam)) != GS_OK) return st;
+    if ((st = check_params(ctx, params)) != GS_OK) return st;
+    gs_proj* p = new_handle<gs_proj>(ctx, kMagicProj);
+    if (!p) return gs_fail(ctx, GS_ERR_OOM, "host allocation failed");
+    p->n = params->n;
+    p->sh_degree = params->sh_degree;
+    p->W = cam->width;
+    p->H = cam->height;
+    p->TW = (cam->width + 15) / 16;
+    p->TH = (cam->height + 15) / 16;
+    std::vector<GsAlloc> tmp;
+    const int64_t n = params->n;
+    uint32_t* flag = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n, 1), GS_MEM_SCRATCH, &tmp);
+    uint32_t* slot = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n + 1), GS_MEM_SCRATCH, &tmp);
+    uint32_t cnt = 0;
+    if (!flag || !slot) { st = GS_ERR_OOM; goto fail; }
+    if ((st = launch_project(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
+    if ((st = readback(ctx, slot + n, sizeof(uint32_t), &cnt)) != GS_OK) goto fail;
+    p->n_cand = cnt;
+    {
+        const int64_t nc = std::max<int64_t>(cnt, 1);
+        p->ids = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
+        p->rect = (int4*)gs_malloc(ctx, sizeof(int4) * nc, GS_MEM_PROJ, &p->allocs);
+        p->g0 = (float4*)gs_malloc(ctx, sizeof(float4) * nc, GS_MEM_PROJ, &p->allocs);
+        p->g1 = (float4*)gs_malloc(ctx, sizeof(float4) * nc, GS_MEM_PROJ, &p->allocs);
+        p->g2 = (float4*)gs_malloc(ctx, sizeof(float4) * nc, GS_MEM_PROJ, &p->allocs);
+        p->slot_of = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * std::max<int64_t>(n, 1), GS_MEM_PROJ, &p->allocs);
+        if (!p->ids || !p->rect || !p->g0 || !p->g1 || !p->g2 || !p->slot_of) { st = GS_ERR_OOM; goto fail; }
+    }
+    if ((st = launch_project_write(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
+    gs_free_all(ctx, &tmp);
+    *out = p;
+    *n_cand = (int64_t)cnt;
+    return GS_OK;
+fail:
+    gs_free_all(ctx, &tmp);
+    destroy_handle(ctx, p);
+    return st;
+}
+
+// ---------------------------------------------------------------------------
+// planning
+
+gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
+                         const gs_cost_model* cost, int32_t strict, gs_leaf* leaves, int32_t max_leaves,
+                         int32_t* n_leaves)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    gs_status st;
+    if ((st = check_camera(ctx, cam)) != GS_OK) return st;
+    if (!handle_ok(ctx, proj, kMagicProj)) return gs_fail(ctx, GS_ERR_STATE, "invalid projection handle");
+    if (proj->W != cam->width || proj->H != cam->height)
+        return gs_fail(ctx, GS_ERR_STATE, "camera does not match the projection");
+    if (budget_bytes == 0) return gs_fail(ctx, GS_ERR_INVALID_ARG, "budget must be > 0");
+    if (!n_leaves || (max_leaves > 0 && !leaves) || max_leaves < 0)
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "leaves / n_leaves");
+    const gs_cost_model cm = cost ? *cost : gs_default_cost_model();
+    const int64_t T = (int64_t)proj->TW * proj->TH;
+    const int32_t cap = (int32_t)std::min<int64_t>(std::max<int32_t>(max_leaves, 1), T);
+    std::vector<GsAlloc> tmp;
+    uint64_t* sat = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (proj->TW + 1) * (int64_t)(proj->TH + 1),
+                                         GS_MEM_SCRATCH, &tmp);
+    int32_t* diff = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * T, GS_MEM_SCRATCH, &tmp);
+    gs_leaf* ldev = (gs_leaf*)gs_malloc(ctx, sizeof(gs_leaf) * cap, GS_MEM_SCRATCH, &tmp);
+    int32_t* small = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * 2, GS_MEM_SCRATCH, &tmp);
+    int32_t hv[2] = {0, 0};
+    if (!sat || !diff || !ldev || !small) {
+        gs_free_all(ctx, &tmp);
+        return GS_ERR_OOM;
+    }
+    st = launch_plan(ctx, proj, sat, diff, budget_bytes, &cm, ldev, cap, small, small + 1);
+    if (st == GS_OK) st = readback(ctx, small, sizeof(hv), hv);
+    if (st == GS_OK && max_leaves > 0 && hv[0] > 0) {
+        const int32_t nw = std::min(hv[0], max_leaves);
+        hipError_t e = hipMemcpyAsync(leaves, ldev, sizeof(gs_leaf) * nw, hipMemcpyDeviceToHost, ctx->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+        if (e != hipSuccess) st = gs_fail(ctx, GS_ERR_DEVICE, "leaf copy failed: %s", hipGetErrorString(e));
+    }
+    gs_free_all(ctx, &tmp);
+    if (st != GS_OK) return st;
+    *n_leaves = hv[0];
+    if (strict && hv[1]) return gs_fail(ctx, GS_ERR_BUDGET, "a single tile exceeds the budget");
+    return GS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// binning
+
+gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs_tile_rect leaf, gs_bins** out,
+                      int64_t* n_isect)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    gs_status st;
+    if ((st = check_camera(ctx, cam)) != GS_OK) return st;
+    if (!handle_ok(ctx, proj, kMagicProj)) return gs_fail(ctx, GS_ERR_STATE, "invalid projection handle");
+    if (!out || !n_isect) return gs_fail(ctx, GS_ERR_INVALID_ARG, "out / n_isect is NULL");
+    if (leaf.tx0 < 0 || leaf.ty0 < 0 || leaf.tx1 > proj->TW || leaf.ty1 > proj->TH || leaf.tx0 >= leaf.tx1 ||
+        leaf.ty0 >= leaf.ty1)
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "leaf (%d,%d)-(%d,%d) is empty or outside the %d x %d tile grid",
+                       leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, proj->TW, proj->TH);
+    gs_bins* b = new_handle<gs_bins>(ctx, kMagicBins);
+    if (!b) return gs_fail(ctx, GS_ERR_OOM, "host allocation failed");
+    b->proj = proj;
+    b->leaf = leaf;
+    b->TWL = leaf.tx1 - leaf.tx0;
+    b->THL = leaf.ty1 - leaf.ty0;
+    b->n_tiles = (int64_t)b->TWL * b->THL;
+    std::vector<GsAlloc> tmp;
+    uint64_t hv[2] = {0, 0};
+    int32_t* diff = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * b->n_tiles, GS_MEM_RASTER, &tmp);
+    uint64_t* small = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * 2, GS_MEM_SCRATCH, &tmp);
+    b->offsets = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (b->n_tiles + 1), GS_MEM_RASTER, &b->allocs);
+    uint32_t* cursor = nullptr;
+    uint64_t* comp = nullptr;
+    uint64_t* scratch = nullptr;
+    if (!diff || !small || !b->offsets) { st = GS_ERR_OOM; goto fail; }
+    if ((st = launch_fill_u32(ctx, (uint32_t*)diff, 0u, b->n_tiles)) != GS_OK) goto fail;
+    if ((st = launch_rect_diff(ctx, proj, leaf, diff)) != GS_OK) goto fail;
+    if ((st = launch_prefix2d_i32(ctx, diff, b->THL, b->TWL)) != GS_OK) goto fail;
+    if ((st = launch_scan_u32_to_u64(ctx, (const uint32_t*)diff, b->offsets, b->n_tiles)) != GS_OK) goto fail;
+    if ((st = launch_max_segment(ctx, b->offsets, b->n_tiles, small + 1)) != GS_OK) goto fail;
+    if (hipMemcpyAsync(small, b->offsets + b->n_tiles, sizeof(uint64_t), hipMemcpyDeviceToDevice, ctx->stream) !=
+        hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "copy failed"); goto fail; }
+    if ((st = readback(ctx, small, sizeof(hv), hv)) != GS_OK) goto fail;
+    gs_free_one(ctx, &tmp, diff);
+    b->n_isect = (int64_t)hv[0];
+    {
+        const int64_t ni = std::max<int64_t>(b->n_isect, 1);
+        cursor = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * b->n_tiles, GS_MEM_RASTER, &tmp);
+        comp = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * ni, GS_MEM_RASTER, &tmp);
+        b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &b->allocs);
+        if (!cursor || !comp || !b->values) { st = GS_ERR_OOM; goto fail; }
+        if (hv[1] > 8192) {
+            scratch = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * ni, GS_MEM_RASTER, &tmp);
+            if (!scratch) { st = GS_ERR_OOM; goto fail; }
+        }
+    }
+    if ((st = launch_fill_u32(ctx, cursor, 0u, b->n_tiles)) != GS_OK) goto fail;
+    if ((st = launch_emit(ctx, proj, leaf, b->offsets, cursor, comp)) != GS_OK) goto fail;
+    if ((st = launch_sort_tiles(ctx, b->n_tiles, b->offsets, comp, scratch, b->values, (int64_t)hv[1])) != GS_OK)
+        goto fail;
+    gs_free_all(ctx, &tmp);
+    *out = b;
+    *n_isect = b->n_isect;
+    return GS_OK;
+fail:
+    gs_free_all(ctx, &tmp);
+    destroy_handle(ctx, b);
+    return st;
+}
+
+// ---------------------------------------------------------------------------
+// raster
+
+gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                        const float* target, double* loss_accum, float* image_out, gs_raster** out)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    gs_status st;
+    if ((st = check_camera(ctx, cam)) != GS_OK) return st;
+    if (!handle_ok(ctx, proj, kMagicProj)) return gs_fail(ctx, GS_ERR_STATE, "invalid projection handle");
+    if (!handle_ok(ctx, bins, kMagicBins) || bins->proj != proj)
+        return gs_fail(ctx, GS_ERR_STATE, "bins handle does not belong to this projection");
+    if (!out) return gs_fail(ctx, GS_ERR_INVALID_ARG, "out is NULL");
+    if (proj->W != cam->width || proj->H != cam->height)
+        return gs_fail(ctx, GS_ERR_STATE, "camera does not match the projection");
+    gs_raster* r = new_handle<gs_raster>(ctx, kMagicRaster);
+    if (!r) return gs_fail(ctx, GS_ERR_OOM, "host allocation failed");
+    r->bins = bins;
+    r->px0 = bins->leaf.tx0 * 16;
+    r->py0 = bins->leaf.ty0 * 16;
+    r->WL = std::min(bins->leaf.tx1 * 16, cam->width) - r->px0;
+    r->HL = std::min(bins->leaf.ty1 * 16, cam->height) - r->py0;
+    r->n_pix = (int64_t)r->WL * r->HL;
+    r->tfinal = (float*)gs_malloc(ctx, sizeof(float) * r->n_pix, GS_MEM_RASTER, &r->allocs);
+    r->last = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * r->n_pix, GS_MEM_RASTER, &r->allocs);
+    if (target) {
+        r->dldc = (float*)gs_malloc(ctx, sizeof(float) * 3 * r->n_pix, GS_MEM_RASTER, &r->allocs);
+        r->l1_part = (double*)gs_malloc(ctx, sizeof(double) * 4 * bins->n_tiles, GS_MEM_RASTER, &r->allocs);
+    }
+    if (!r->tfinal || !r->last || (target && (!r->dldc || !r->l1_part))) {
+        destroy_handle(ctx, r);
+        return GS_ERR_OOM;
+    }
+    if ((st = launch_raster_fwd(ctx, cam, proj, bins, r, target, image_out, loss_accum)) != GS_OK) {
+        destroy_handle(ctx, r);
+        return st;
+    }
+    *out = r;
+    return GS_OK;
+}
+
+gs_status gs_render_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                        const gs_raster* raster, const float* dl_dimage, float* grad2d)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    gs_status st;
+    if ((st = check_camera(ctx, cam)) != GS_OK) return st;
+    if (!handle_ok(ctx, proj, kMagicProj) || !handle_ok(ctx, bins, kMagicBins) ||
+        !handle_ok(ctx, raster, kMagicRaster) || bins->proj != proj || raster->bins != bins)
+        return gs_fail(ctx, GS_ERR_STATE, "handles do not belong together");
+    if (!grad2d && proj->n_cand > 0) return gs_fail(ctx, GS_ERR_INVALID_ARG, "grad2d is NULL");
+    if (!dl_dimage && !raster->dldc)
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "no dL/dimage given and no L1 target fused in the forward");
+    return launch_raster_bwd(ctx, cam, proj, bins, raster, dl_dimage, grad2d);
+}
+
+gs_status gs_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const gs_proj* proj,
+                         const float* grad2d, float* grad3d)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    gs_status st;
+    if ((st = check_camera(ctx, cam)) != GS_OK) return st;
+    if ((st = check_params(ctx, params)) != GS_OK) return st;
+    if (!handle_ok(ctx, proj, kMagicProj)) return gs_fail(ctx, GS_ERR_STATE, "invalid projection handle");
+    if (params->n != proj->n || params->sh_degree != proj->sh_degree)
+        return gs_fail(ctx, GS_ERR_STATE, "params do not match the projection");
+    if (proj->n_cand > 0 && (!grad2d || !grad3d)) return gs_fail(ctx, GS_ERR_INVALID_ARG, "grad2d / grad3d NULL");
+    return launch_project_bwd(ctx, cam, params, proj, grad2d, grad3d);
+}
+
+// ---------------------------------------------------------------------------
+// extras
+
+gs_status gs_loss_ssim(gs_ctx* ctx, int32_t width, int32_t height, const float* image, const float* target,
+                       float lambda, float* dl_dimage, double* loss, double* ssim)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (width < 1 || height < 1 || !image || !target || !dl_dimage)
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "gs_loss_ssim arguments");
+    const int64_t P = (int64_t)width * height;
+    const int64_t nb = ssim_partial_blocks(width, height);
+    std::vector<GsAlloc> tmp;
+    float* scratch = (float*)gs_malloc(ctx, sizeof(float) * 24 * P, GS_MEM_LOSS, &tmp);
+    double* part = (double*)gs_malloc(ctx, sizeof(double) * (2 * nb + 2), GS_MEM_LOSS, &tmp);
+    if (!scratch || !part) {
+        gs_free_all(ctx, &tmp);
+        return GS_ERR_OOM;
+    }
+    gs_status st = launch_ssim(ctx, width, height, image, target, lambda, dl_dimage, part, nb, scratch);
+    if (st == GS_OK && (loss || ssim)) {
+        st = launch_sum_f64(ctx, part, nb, 2, part + 2 * nb, 0);
+        if (st == GS_OK) st = launch_sum_f64(ctx, part + 1, nb, 2, part + 2 * nb + 1, 0);
+        double hv[2] = {0, 0};
+        if (st == GS_OK) st = readback(ctx, part + 2 * nb, sizeof(hv), hv);
+        if (st == GS_OK) {
+            const double s = hv[0] / (3.0 * (double)P), l1 = hv[1] / (3.0 * (double)P);
+            if (ssim) *ssim = s;
+            if (loss) *loss = (1.0 - lambda) * l1 + lambda * (1.0 - s);
+        }
+    }
+    gs_free_all(ctx, &tmp);
+    return st;
+}
+
+gs_status gs_adam_step(gs_ctx* ctx, const gs_proj* proj, int64_t n, int32_t sh_degree, const gs_param_ptrs* params,
+                       const gs_param_ptrs* m, const gs_param_ptrs* v, const float* grad3d, int32_t step, float lr,
+                       float beta1, float beta2, float eps)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (!handle_ok(ctx, proj, kMagicProj)) return gs_fail(ctx, GS_ERR_STATE, "invalid projection handle");
+    if (n != proj->n || sh_degree != proj->sh_degree) return gs_fail(ctx, GS_ERR_STATE, "sizes do not match");
+    if (!params || !m || !v || step < 1 || (proj->n_cand > 0 && !grad3d))
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "gs_adam_step arguments");
+    return launch_adam(ctx, proj, n, sh_degree, params, m, v, grad3d, step, lr, beta1, beta2, eps);
+}
+
+void gs_release(gs_ctx* ctx, void* handle)
+{
+    if (!ctx || !handle) return;
+    GsHandle* h = static_cast<GsHandle*>(handle);
+    if (h->ctx != ctx || (h->magic != kMagicProj && h->magic != kMagicBins && h->magic != kMagicRaster)) return;
+    destroy_handle(ctx, h);
+}
+
+gs_status gs_export_size(gs_ctx* ctx, const void* handle, int32_t field, size_t* bytes)
+{
+    if (!ctx || !handle || !bytes) return GS_ERR_INVALID_ARG;
+    const GsHandle* h = static_cast<const GsHandle*>(handle);
+    if (h->ctx != ctx) return gs_fail(ctx, GS_ERR_STATE, "handle of another context");
+    if (h->magic == kMagicProj) {
+        const gs_proj* p = static_cast<const gs_proj*>(h);
+        const size_t nc = (size_t)p->n_cand;
+        switch (field) {
+        case GS_PROJ_IDS: case GS_PROJ_DEPTH: case GS_PROJ_RADIUS: case GS_PROJ_OPACITY: case GS_PROJ_FLAGS:
+            *bytes = 4 * nc; return GS_OK;
+        case GS_PROJ_RECT: *bytes = 16 * nc; return GS_OK;
+        case GS_PROJ_XY: *bytes = 8 * nc; return GS_OK;
+        case GS_PROJ_CONIC: case GS_PROJ_RGB: *bytes = 12 * nc; return GS_OK;
+        case GS_PROJ_SLOT_OF: *bytes = 4 * (size_t)p->n; return GS_OK;
+        default: break;
+        }
+    } else if (h->magic == kMagicBins) {
+        const gs_bins* b = static_cast<const gs_bins*>(h);
+        switch (field) {
+        case GS_BINS_OFFSETS: *bytes = 8 * (size_t)(b->n_tiles + 1); return GS_OK;
+        case GS_BINS_VALUES: *bytes = 4 * (size_t)b->n_isect; return GS_OK;
+        case GS_BINS_KEYS: *bytes = 8 * (size_t)b->n_isect; return GS_OK;
+        default: break;
+        }
+    } else if (h->magic == kMagicRaster) {
+        const gs_raster* r = static_cast<const gs_raster*>(h);
+        if (field == GS_RASTER_TFINAL || field == GS_RASTER_LAST) {
+            *bytes = 4 * (size_t)r->n_pix;
+            return GS_OK;
+        }
+    }
+    return gs_fail(ctx, GS_ERR_INVALID_ARG, "field %d does not belong to this handle", field);
+}
+
+gs_status gs_export(gs_ctx* ctx, const void* handle, int32_t field, void* dst, size_t dst_bytes)
+{
+    size_t need = 0;
+    gs_status st = gs_export_size(ctx, handle, field, &need);
+    if (st != GS_OK) return st;
+    if (need == 0) return GS_OK;
+    if (!dst || dst_bytes < need) return gs_fail(ctx, GS_ERR_INVALID_ARG, "destination too small (%zu < %zu)", dst_bytes, need);
+    const GsHandle* h = static_cast<const GsHandle*>(handle);
+    if (h->magic == kMagicProj) return launch_export_proj(ctx, static_cast<const gs_proj*>(h), field, dst);
+    if (h->magic == kMagicBins) {
+        const gs_bins* b = static_cast<const gs_bins*>(h);
+        if (field == GS_BINS_KEYS) return launch_export_keys(ctx, b, (uint64_t*)dst);
+        const void* src = field == GS_BINS_OFFSETS ? (const void*)b->offsets : (const void*)b->values;
+        GS_HIP(ctx, hipMemcpyAsync(dst, src, need, hipMemcpyDeviceToDevice, ctx->stream));
+        return GS_OK;
+    }
+    const gs_raster* r = static_cast<const gs_raster*>(h);
+    const void* src = field == GS_RASTER_TFINAL ? (const void*)r->tfinal : (const void*)r->last;
+    GS_HIP(ctx, hipMemcpyAsync(dst, src, need, hipMemcpyDeviceToDevice, ctx->stream));
+    return GS_OK;
+}
+
+gs_status gs_util_exp(gs_ctx* ctx, const float* x, float* y, int64_t n)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (n < 0 || (n > 0 && (!x || !y))) return gs_fail(ctx, GS_ERR_INVALID_ARG, "gs_util_exp arguments");
+    return launch_exp(ctx, x, y, n);
+}
+
+// ---------------------------------------------------------------------------
+// one whole view
+
+gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
+                        const gs_view_opts* opts, gs_view_result* result)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (!opts || !result || !target) return gs_fail(ctx, GS_ERR_INVALID_ARG, "opts / result / target is NULL");
+    if (opts->loss_kind != 0 && opts->loss_kind != 1) return gs_fail(ctx, GS_ERR_INVALID_ARG, "loss_kind");
+    if (opts->adam_step > 0 && (!opts->params_rw || !opts->adam_m || !opts->adam_v))
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "Adam needs params_rw, adam_m, adam_v");
+    std::memset(result, 0, sizeof(*result));
+    gs_status st;
+    gs_proj* proj = nullptr;
+    int64_t n_cand = 0;
+    const uint64_t live0 = ctx->live;
+    const uint64_t peak_before = ctx->peak;
+    ctx->peak = ctx->live;
+    if ((st = gs_project(ctx, cam, params, &proj, &n_cand)) != GS_OK) return st;
+
+    std::vector<gs_leaf> leaves;
+    const int32_t TW = proj->TW, TH = proj->TH;
+    if (opts->budget_bytes > 0) {
+        int32_t nl = 0;
+        leaves.resize(4096);
+        st = gs_plan_leaves(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, leaves.data(),
+                            (int32_t)leaves.size(), &nl);
+        if (st == GS_OK && nl > (int32_t)leaves.size()) {
+            leaves.resize(nl);
+            st = gs_plan_leaves(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, leaves.data(),
+                                nl, &nl);
+        }
+        if (st != GS_OK) { gs_release(ctx, proj); return st; }
+        leaves.resize(nl);
+    } else {
+        gs_leaf L{};
+        L.tx0 = 0; L.ty0 = 0; L.tx1 = TW; L.ty1 = TH;
+        leaves.push_back(L);
+    }
+    if (opts->loss_kind == 1 && leaves.size() != 1) {
+        gs_release(ctx, proj);
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "the SSIM loss is computed on the full image (budget 0)");
+    }
+    if (opts->leaves_out && opts->max_leaves > 0)
+        std::memcpy(opts->leaves_out, leaves.data(), sizeof(gs_leaf) * std::min<size_t>(leaves.size(), opts->max_leaves));
+
+    const int K = (params->sh_degree + 1) * (params->sh_degree + 1);
+    const int F = 11 + 3 * K;
+    std::vector<GsAlloc> view;
+    const int64_t nc = std::max<int64_t>(n_cand, 1);
+    float* grad2d = (float*)gs_malloc(ctx, sizeof(float) * 9 * nc, GS_MEM_GRAD, &view);
+    double* loss_dev = (double*)gs_malloc(ctx, sizeof(double), GS_MEM_SCRATCH, &view);
+    const int64_t P = (int64_t)cam->width * cam->height;
+    float* image = opts->image_out;
+    float* dl_dimage = nullptr;
+    double loss = 0.0;
+    int64_t isect_total = 0;
+    if (!grad2d || !loss_dev) { st = GS_ERR_OOM; goto done; }
+    if ((st = launch_fill_f32(ctx, grad2d, 0.0f, 9 * nc)) != GS_OK) goto done;
+    if (hipMemsetAsync(loss_dev, 0, sizeof(double), ctx->stream) != hipSuccess) {
+        st = gs_fail(ctx, GS_ERR_DEVICE, "memset failed");
+        goto done;
+    }
+    if (opts->loss_kind == 1) {
+        if (!image) image = (float*)gs_malloc(ctx, sizeof(float) * 3 * P, GS_MEM_LOSS, &view);
+        dl_dimage = (float*)gs_malloc(ctx, sizeof(float) * 3 * P, GS_MEM_LOSS, &view);
+        if (!image || !dl_dimage) { st = GS_ERR_OOM; goto done; }
+    }
+    for (const gs_leaf& L : leaves) {
+        gs_bins* bins = nullptr;
+        gs_raster* ras = nullptr;
+        int64_t ni = 0;
+        gs_tile_rect r{L.tx0, L.ty0, L.tx1, L.ty1};
+        if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
+        isect_total += ni;
+        if (opts->loss_kind == 0) {
+            st = gs_render_fwd(ctx, cam, proj, bins, target, loss_dev, image, &ras);
+            if (st == GS_OK) st = gs_render_bwd(ctx, cam, proj, bins, ras, nullptr, grad2d);
+        } else {
+            st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, &ras);
+            if (st == GS_OK)
+                st = gs_loss_ssim(ctx, cam->width, cam->height, image, target, opts->ssim_lambda, dl_dimage, &loss,
+                                  nullptr);
+            if (st == GS_OK) st = gs_render_bwd(ctx, cam, proj, bins, ras, dl_dimage, grad2d);
+        }
+        gs_release(ctx, ras);
+        gs_release(ctx, bins);
+        if (st != GS_OK) goto done;
+    }
+    {
+        float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * nc, GS_MEM_GRAD, &view);
+        if (!grad3d) { st = GS_ERR_OOM; goto done; }
+        if ((st = gs_project_bwd(ctx, cam, params, proj, grad2d, grad3d)) != GS_OK) goto done;
+        if (opts->grad3d_out && (st = launch_scatter_grad3d(ctx, proj, F, grad3d, opts->grad3d_out)) != GS_OK)
+            goto done;
+        if (opts->adam_step > 0 &&
+            (st = gs_adam_step(ctx, proj, params->n, params->sh_degree, opts->params_rw, opts->adam_m, opts->adam_v,
+                               grad3d, opts->adam_step, opts->lr, opts->beta1, opts->beta2, opts->eps)) != GS_OK)
+            goto done;
+    }
+    if (opts->loss_kind == 0) {
+        double s = 0.0;
+        if ((st = readback(ctx, loss_dev, sizeof(double), &s)) != GS_OK) goto done;
+        loss = s / (3.0 * (double)P);
+    } else if (hipStreamSynchronize(ctx->stream) != hipSuccess) {
+        st = gs_fail(ctx, GS_ERR_DEVICE, "stream synchronisation failed");
+        goto done;
+    }
+    result->loss = loss;
+    result->n_cand = n_cand;
+    result->n_isect = isect_total;
+    result->n_leaves = (int32_t)leaves.size();
+    result->peak_bytes = ctx->peak - live0;
+done:
+    gs_free_all(ctx, &view);
+    gs_release(ctx, proj);
+    ctx->peak = std::max(ctx->peak, peak_before);
+    return st;
+}
+
+}  // extern "C"

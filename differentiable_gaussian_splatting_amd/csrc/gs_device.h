@@ -1,0 +1,180 @@
+// gs_device.h -- device-side helpers for the gfx950 kernels of libgsmi.
+//
+// Float discipline.  Everything on the forward path (projection, binning
+// keys, compositing) is f32 with a fixed operation order: the library is
+// built with -ffp-contract=off, correctly rounded f32 division and square
+// root, and IEEE denormals; an fma is used only where fmaf() is written.
+// This makes every threshold decision (candidate culling, tile rectangles,
+// alpha < 1/255, T < 1e-4) reproducible bit for bit by an independent
+// implementation of the same specification.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gsd {
+
+// ---------------------------------------------------------------------------
+// exp by Cody & Waite argument reduction ("Software Manual for the Elementary
+// Functions", 1980) with a degree-7 Taylor polynomial:
+//   k = rint(x log2 e); r = (x - k ln2_hi) - k ln2_lo; e^r = sum_{n<=7} r^n/n!
+//   (Horner, fma); result = ldexp(p, k).
+// ln2_hi is ln 2 rounded to f32 with its 12 low significand bits cleared, so
+// that k * ln2_hi is exact for |k| < 2^12; ln2_lo = f32(ln 2 - ln2_hi).
+// Within 2 ulp of exp over [-87, 88].  The compositing rule evaluates it at
+// power <= 0 only; callers skip power < -87, where it returns 0 (alpha = 0).
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2Hi = __builtin_bit_cast(
+    float, __builtin_bit_cast(uint32_t, 0.693147180559945309417232121458f) & 0xFFFFF000u);
+constexpr float kLn2Lo = (float)(0.693147180559945309417232121458 - (double)kLn2Hi);
+constexpr float kInvFact2 = 1.0f / 2.0f;
+constexpr float kInvFact3 = 1.0f / 6.0f;
+constexpr float kInvFact4 = 1.0f / 24.0f;
+constexpr float kInvFact5 = 1.0f / 120.0f;
+constexpr float kInvFact6 = 1.0f / 720.0f;
+constexpr float kInvFact7 = 1.0f / 5040.0f;
+
+// core: valid for -87 <= x <= 88.7
+__device__ __forceinline__ float exp_cw_core(float x)
+{
+    const float k = __builtin_rintf(x * kLog2e);
+    float r = __builtin_fmaf(-k, kLn2Hi, x);
+    r = __builtin_fmaf(-k, kLn2Lo, r);
+    float p = kInvFact7;
+    p = __builtin_fmaf(p, r, kInvFact6);
+    p = __builtin_fmaf(p, r, kInvFact5);
+    p = __builtin_fmaf(p, r, kInvFact4);
+    p = __builtin_fmaf(p, r, kInvFact3);
+    p = __builtin_fmaf(p, r, kInvFact2);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)k);
+}
+
+__device__ __forceinline__ float exp_cw(float x)
+{
+    if (x < -87.0f) return 0.0f;
+    if (x > 88.7f) return __builtin_inff();
+    if (x != x) return x;
+    return exp_cw_core(x);
+}
+
+// compositing constants
+constexpr float kAlphaMin = 1.0f / 255.0f;
+constexpr float kAlphaMax = 0.99f;
+constexpr float kTMin = 0.0001f;
+
+// ---------------------------------------------------------------------------
+// Real orthonormal SH basis, degree <= 3, no Condon-Shortley phase, order l
+// then m = -l..l, as polynomials in the unit direction (x, y, z).
+__device__ __forceinline__ void sh_basis(int deg, float x, float y, float z, float* Y)
+{
+    Y[0] = 0.282094791773878143f;
+    if (deg < 1) return;
+    Y[1] = 0.488602511902919921f * y;
+    Y[2] = 0.488602511902919921f * z;
+    Y[3] = 0.488602511902919921f * x;
+    if (deg < 2) return;
+    const float xx = x * x, yy = y * y, zz = z * z;
+    const float xy = x * y, yz = y * z, xz = x * z;
+    Y[4] = 1.09254843059207907f * xy;
+    Y[5] = 1.09254843059207907f * yz;
+    Y[6] = 0.315391565252520050f * ((2.0f * zz - xx) - yy);
+    Y[7] = 1.09254843059207907f * xz;
+    Y[8] = 0.546274215296039535f * (xx - yy);
+    if (deg < 3) return;
+    Y[9] = 0.590043589926643510f * (y * (3.0f * xx - yy));
+    Y[10] = 2.89061144264055405f * (xy * z);
+    Y[11] = 0.457045799464465739f * (y * ((4.0f * zz - xx) - yy));
+    Y[12] = 0.373176332590115391f * (z * ((2.0f * zz - 3.0f * xx) - 3.0f * yy));
+    Y[13] = 0.457045799464465739f * (x * ((4.0f * zz - xx) - yy));
+    Y[14] = 1.44530572132027703f * (z * (xx - yy));
+    Y[15] = 0.590043589926643510f * (x * (xx - 3.0f * yy));
+}
+
+// d Y_k / d(x, y, z) of the polynomials above (k = 0..K-1), D[k][3]
+__device__ __forceinline__ void sh_basis_grad(int deg, float x, float y, float z, float (*D)[3])
+{
+    constexpr float c1 = 0.488602511902919921f, c2a = 1.09254843059207907f,
+                    c2b = 0.315391565252520050f, c2c = 0.546274215296039535f,
+                    c3a = 0.590043589926643510f, c3b = 2.89061144264055405f,
+                    c3c = 0.457045799464465739f, c3d = 0.373176332590115391f,
+                    c3e = 1.44530572132027703f;
+    D[0][0] = D[0][1] = D[0][2] = 0.0f;
+    if (deg < 1) return;
+    D[1][0] = 0.0f; D[1][1] = c1; D[1][2] = 0.0f;
+    D[2][0] = 0.0f; D[2][1] = 0.0f; D[2][2] = c1;
+    D[3][0] = c1; D[3][1] = 0.0f; D[3][2] = 0.0f;
+    if (deg < 2) return;
+    const float xx = x * x, yy = y * y, zz = z * z;
+    D[4][0] = c2a * y; D[4][1] = c2a * x; D[4][2] = 0.0f;
+    D[5][0] = 0.0f; D[5][1] = c2a * z; D[5][2] = c2a * y;
+    D[6][0] = -2.0f * c2b * x; D[6][1] = -2.0f * c2b * y; D[6][2] = 4.0f * c2b * z;
+    D[7][0] = c2a * z; D[7][1] = 0.0f; D[7][2] = c2a * x;
+    D[8][0] = 2.0f * c2c * x; D[8][1] = -2.0f * c2c * y; D[8][2] = 0.0f;
+    if (deg < 3) return;
+    D[9][0] = 6.0f * c3a * x * y; D[9][1] = 3.0f * c3a * (xx - yy); D[9][2] = 0.0f;
+    D[10][0] = c3b * y * z; D[10][1] = c3b * x * z; D[10][2] = c3b * x * y;
+    D[11][0] = -2.0f * c3c * x * y; D[11][1] = c3c * (4.0f * zz - xx - 3.0f * yy); D[11][2] = 8.0f * c3c * y * z;
+    D[12][0] = -6.0f * c3d * x * z; D[12][1] = -6.0f * c3d * y * z; D[12][2] = c3d * (6.0f * zz - 3.0f * xx - 3.0f * yy);
+    D[13][0] = c3c * (4.0f * zz - 3.0f * xx - yy); D[13][1] = -2.0f * c3c * x * y; D[13][2] = 8.0f * c3c * x * z;
+    D[14][0] = 2.0f * c3e * x * z; D[14][1] = -2.0f * c3e * y * z; D[14][2] = c3e * (xx - yy);
+    D[15][0] = 3.0f * c3a * (xx - yy); D[15][1] = -6.0f * c3a * x * y; D[15][2] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// wave64 helpers
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// The compiler may reorder LDS accesses of one wavefront that it believes do
+// not alias; this fence orders them (the hardware keeps a wave's LDS ops in
+// order) without a workgroup barrier.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF, bool BOUND = false>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                  BANK_MASK, BOUND));
+}
+
+// Sum over the 64 lanes; the total is valid in lane 63.
+__device__ __forceinline__ float wave_sum_to_lane63(float v)
+{
+    v += dpp_f<0xB1>(v);              // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);              // quad_perm [2,3,0,1]
+    v += dpp_f<0x124>(v);             // row_ror:4
+    v += dpp_f<0x128>(v);             // row_ror:8
+    v += dpp_f<0x142, 0xA>(v);        // row_bcast:15 into rows 1, 3
+    v += dpp_f<0x143, 0xC>(v);        // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_to_lane63(v)), 63));
+}
+
+__device__ __forceinline__ double wave_sum_d(double v)
+{
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+}  // namespace gsd

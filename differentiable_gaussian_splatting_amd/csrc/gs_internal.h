@@ -1,0 +1,156 @@
+// gs_internal.h -- host-side internals of libgsmi: context, handles,
+// allocation accounting, kernel timing and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/gs.h"
+
+struct GsAlloc {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    int cat = GS_MEM_SCRATCH;
+};
+
+struct GsTimerRec {
+    const char* name;
+    hipEvent_t start, stop;
+};
+
+struct gs_ctx {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    gs_alloc_fn alloc = nullptr;
+    gs_free_fn free_fn = nullptr;
+    void* user = nullptr;
+    std::string err;
+    uint64_t live = 0, peak = 0, n_alloc = 0, n_free = 0;
+    uint64_t live_cat[GS_MEM_NCAT] = {0}, peak_cat[GS_MEM_NCAT] = {0};
+    bool timing = false;
+    std::vector<GsTimerRec> timers;
+    std::vector<hipEvent_t> event_pool;
+    void* pinned = nullptr;        // small pinned host buffer for count read-backs
+    int num_cu = 256;
+    size_t max_lds = 65536;
+};
+
+constexpr uint32_t kMagicProj = 0x9a0c0001u, kMagicBins = 0x9a0c0002u, kMagicRaster = 0x9a0c0003u;
+
+struct GsHandle {
+    uint32_t magic = 0;
+    gs_ctx* ctx = nullptr;
+    std::vector<GsAlloc> allocs;
+};
+
+struct gs_proj : GsHandle {
+    int64_t n = 0, n_cand = 0;
+    int sh_degree = 0;
+    int W = 0, H = 0, TW = 0, TH = 0;
+    uint32_t* ids = nullptr;      // [n_cand] Gaussian id of each slot
+    int4* rect = nullptr;         // [n_cand] tx0, ty0, tx1, ty1
+    float4* g0 = nullptr;         // [n_cand] x, y, -A/2, -B
+    float4* g1 = nullptr;         // [n_cand] -C/2, opacity, r, g
+    float4* g2 = nullptr;         // [n_cand] b, depth, radius, flags (bits)
+    int32_t* slot_of = nullptr;   // [n] slot or -1
+};
+
+struct gs_bins : GsHandle {
+    const gs_proj* proj = nullptr;
+    gs_tile_rect leaf{};
+    int64_t n_tiles = 0, n_isect = 0;
+    int TWL = 0, THL = 0;
+    uint64_t* offsets = nullptr;  // [n_tiles + 1]
+    uint32_t* values = nullptr;   // [n_isect]
+};
+
+struct gs_raster : GsHandle {
+    const gs_bins* bins = nullptr;
+    int64_t n_pix = 0;
+    int px0 = 0, py0 = 0, WL = 0, HL = 0;
+    float* tfinal = nullptr;      // [n_pix]
+    uint32_t* last = nullptr;     // [n_pix]
+    float* dldc = nullptr;        // [3][n_pix] or null
+    double* l1_part = nullptr;    // [n_tiles * 4]
+};
+
+// ---- error plumbing --------------------------------------------------------
+gs_status gs_fail(gs_ctx* ctx, gs_status st, const char* fmt, ...);
+#define GS_HIP(ctx, call)                                                                       \
+    do {                                                                                        \
+        hipError_t e_ = (call);                                                                 \
+        if (e_ != hipSuccess) return gs_fail((ctx), GS_ERR_DEVICE, "%s failed: %s (%s:%d)", #call, \
+                                             hipGetErrorString(e_), __FILE__, __LINE__);         \
+    } while (0)
+
+// ---- memory -----------------------------------------------------------------
+void* gs_malloc(gs_ctx* ctx, size_t bytes, int cat, std::vector<GsAlloc>* owner);
+void gs_free_all(gs_ctx* ctx, std::vector<GsAlloc>* owner);
+void gs_free_one(gs_ctx* ctx, std::vector<GsAlloc>* owner, void* ptr);
+
+// ---- timing -----------------------------------------------------------------
+struct GsTimerScope {
+    gs_ctx* ctx;
+    const char* name;
+    hipEvent_t stop = nullptr;
+    GsTimerScope(gs_ctx* c, const char* n);
+    ~GsTimerScope();
+};
+
+// ---- launchers (defined in the .hip files) ------------------------------------
+// scan.hip: exclusive scans; out has n + 1 entries, out[n] = total.
+gs_status launch_scan_u32_to_u64(gs_ctx* ctx, const uint32_t* in, uint64_t* out, int64_t n);
+gs_status launch_scan_u32_to_u32(gs_ctx* ctx, const uint32_t* in, uint32_t* out, int64_t n);
+gs_status launch_fill_u32(gs_ctx* ctx, uint32_t* p, uint32_t v, int64_t n);
+gs_status launch_fill_f32(gs_ctx* ctx, float* p, float v, int64_t n);
+// 2D inclusive prefix over an int32 grid [rows][cols] (rows, then columns)
+gs_status launch_prefix2d_i32(gs_ctx* ctx, int32_t* grid, int rows, int cols);
+gs_status launch_prefix2d_u64(gs_ctx* ctx, uint64_t* grid, int rows, int cols);
+
+// project.hip
+gs_status launch_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
+                         uint32_t* flag_scratch, uint32_t* slot_scratch);
+gs_status launch_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
+                             const float* grad2d, float* grad3d);
+gs_status launch_export_proj(gs_ctx* ctx, const gs_proj* proj, int field, void* dst);
+gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
+
+// binning.hip
+gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, int32_t* diff);
+gs_status launch_emit(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* offsets,
+                      uint32_t* cursor, uint64_t* comp);
+gs_status launch_sort_tiles(gs_ctx* ctx, int64_t n_tiles, const uint64_t* offsets, uint64_t* comp,
+                            uint64_t* scratch, uint32_t* values, int64_t max_len);
+gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);
+gs_status launch_max_segment(gs_ctx* ctx, const uint64_t* offsets, int64_t n_tiles, uint64_t* out);
+gs_status launch_big_segment_total(gs_ctx* ctx, const uint64_t* offsets, int64_t n_tiles, uint64_t* out);
+
+// raster.hip
+gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                            gs_raster* r, const float* target, float* image_out, double* loss_accum);
+gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                            const gs_raster* r, const float* dl_dimage, float* grad2d);
+
+// planner.hip
+gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, int32_t* diff, uint64_t budget,
+                      const gs_cost_model* cost, gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev,
+                      int32_t* overflow_dev);
+
+// loss.hip
+gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,
+                      float* dl_dimage, double* partials /*[n_blocks*2]*/, int64_t n_blocks,
+                      float* scratch /*[15][3][H][W] */);
+int64_t ssim_partial_blocks(int W, int H);
+gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate);
+
+// adam.hip
+gs_status launch_adam(gs_ctx* ctx, const gs_proj* proj, int64_t n, int sh_degree, const gs_param_ptrs* p,
+                      const gs_param_ptrs* m, const gs_param_ptrs* v, const float* grad3d, int32_t step,
+                      float lr, float b1, float b2, float eps);
+gs_status launch_scatter_grad3d(gs_ctx* ctx, const gs_proj* proj, int F, const float* grad3d, float* dense);
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -1,0 +1,211 @@
+// loss.hip -- deterministic f64 sums and the full-image L1 + SSIM loss with
+// its gradient.
+//
+// SkipGS notes, "loss function": L = (1 - lambda) L1 + lambda (1 - SSIM),
+// lambda = 0.2.  SSIM reading: 11x11 Gaussian window (sigma 1.5, weights
+// summing to 1), K1 = 0.01, K2 = 0.03 on a [0, 1] range, zero padding, mean
+// over channels and pixels.  The window is separable, so each windowed
+// statistic is a horizontal then a vertical 11-tap pass; the gradient pushes
+// the per-pixel partials of SSIM back through the same (symmetric, hence
+// self-adjoint) zero-padded filter.
+#include "gs_device.h"
+#include "gs_internal.h"
+
+namespace {
+
+// one block: out = (accumulate ? out : 0) + sum(in[k * stride]) in a fixed order
+__global__ __launch_bounds__(256) void k_sum_f64(const double* __restrict__ in, int64_t n, int stride,
+                                                 double* __restrict__ out, int accumulate)
+{
+    __shared__ double sh[256];
+    double s = 0.0;
+    for (int64_t k = threadIdx.x; k < n; k += 256) s += in[k * stride];
+    sh[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = (accumulate ? *out : 0.0) + sh[0];
+}
+
+struct Win {
+    float w[11];
+};
+
+constexpr int kSB = 256;
+
+// horizontal pass of the five statistics of each channel:
+// out[(s * 3 + ch) * P + p], s = x, y, x^2, y^2, xy
+__global__ __launch_bounds__(kSB) void k_ssim_h(int W, int H, Win win, const float* __restrict__ x,
+                                                const float* __restrict__ y, float* __restrict__ out)
+{
+    const int64_t P = (int64_t)W * H;
+    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
+    if (k >= 3 * P) return;
+    const int ch = (int)(k / P);
+    const int64_t p = k % P;
+    const int py = (int)(p / W), px = (int)(p % W);
+    const float* xr = x + ch * P + (int64_t)py * W;
+    const float* yr = y + ch * P + (int64_t)py * W;
+    float a = 0.f, b = 0.f, c = 0.f, d = 0.f, e = 0.f;
+#pragma unroll
+    for (int t = 0; t < 11; ++t) {
+        const int q = px + t - 5;
+        if (q < 0 || q >= W) continue;
+        const float wv = win.w[t], xv = xr[q], yv = yr[q];
+        a += wv * xv;
+        b += wv * yv;
+        c += wv * xv * xv;
+        d += wv * yv * yv;
+        e += wv * xv * yv;
+    }
+    out[(0 * 3 + ch) * P + p] = a;
+    out[(1 * 3 + ch) * P + p] = b;
+    out[(2 * 3 + ch) * P + p] = c;
+    out[(3 * 3 + ch) * P + p] = d;
+    out[(4 * 3 + ch) * P + p] = e;
+}
+
+// vertical pass + SSIM map + per-pixel partials dS/d(mu_x), dS/d(E[x^2]),
+// dS/d(E[xy]) into grad[(s * 3 + ch) * P + p]; block partial sums of S and
+// |x - y| into part[2 * block], part[2 * block + 1]
+__global__ __launch_bounds__(kSB) void k_ssim_v(int W, int H, Win win, const float* __restrict__ hs,
+                                                const float* __restrict__ x, const float* __restrict__ y,
+                                                float* __restrict__ grad, double* __restrict__ part)
+{
+    const int64_t P = (int64_t)W * H;
+    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
+    double s_sum = 0.0, l1_sum = 0.0;
+    if (k < 3 * P) {
+        const int ch = (int)(k / P);
+        const int64_t p = k % P;
+        const int py = (int)(p / W), px = (int)(p % W);
+        float st[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 11; ++t) {
+            const int q = py + t - 5;
+            if (q < 0 || q >= H) continue;
+            const float wv = win.w[t];
+#pragma unroll
+            for (int s = 0; s < 5; ++s) st[s] += wv * hs[(s * 3 + ch) * P + (int64_t)q * W + px];
+        }
+        const float C1 = 0.0001f, C2 = 0.0009f;
+        const float mx = st[0], my = st[1];
+        const float sxx = st[2] - mx * mx, syy = st[3] - my * my, sxy = st[4] - mx * my;
+        const float N1 = 2.f * mx * my + C1, N2 = 2.f * sxy + C2;
+        const float D1 = mx * mx + my * my + C1, D2 = sxx + syy + C2;
+        const float iD = 1.0f / (D1 * D2);
+        const float S = N1 * N2 * iD;
+        const float dS_dmx = 2.f * my * N2 * iD - S * 2.f * mx / D1;
+        const float dS_dsxx = -S / D2;
+        const float dS_dsxy = 2.f * N1 * iD;
+        grad[(0 * 3 + ch) * P + p] = dS_dmx - 2.f * mx * dS_dsxx - my * dS_dsxy;
+        grad[(1 * 3 + ch) * P + p] = dS_dsxx;
+        grad[(2 * 3 + ch) * P + p] = dS_dsxy;
+        s_sum = (double)S;
+        l1_sum = fabs((double)x[k] - (double)y[k]);
+    }
+    s_sum = gsd::wave_sum_d(s_sum);
+    l1_sum = gsd::wave_sum_d(l1_sum);
+    __shared__ double sh[2][kSB / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sh[0][wave] = s_sum;
+        sh[1][wave] = l1_sum;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double a = 0.0, b = 0.0;
+        for (int w = 0; w < kSB / 64; ++w) {
+            a += sh[0][w];
+            b += sh[1][w];
+        }
+        part[2 * blockIdx.x] = a;
+        part[2 * blockIdx.x + 1] = b;
+    }
+}
+
+// horizontal pass of the three partial maps (9 maps)
+__global__ __launch_bounds__(kSB) void k_ssim_h2(int W, int H, Win win, const float* __restrict__ in,
+                                                 float* __restrict__ out)
+{
+    const int64_t P = (int64_t)W * H;
+    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
+    if (k >= 9 * P) return;
+    const int64_t m = k / P, p = k % P;
+    const int py = (int)(p / W), px = (int)(p % W);
+    const float* r = in + m * P + (int64_t)py * W;
+    float a = 0.f;
+#pragma unroll
+    for (int t = 0; t < 11; ++t) {
+        const int q = px + t - 5;
+        if (q >= 0 && q < W) a += win.w[t] * r[q];
+    }
+    out[k] = a;
+}
+
+// vertical pass + gradient of the loss w.r.t. the image
+__global__ __launch_bounds__(kSB) void k_ssim_v2(int W, int H, Win win, const float* __restrict__ hs,
+                                                 const float* __restrict__ x, const float* __restrict__ y,
+                                                 float lambda, float inv, float* __restrict__ dl)
+{
+    const int64_t P = (int64_t)W * H;
+    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
+    if (k >= 3 * P) return;
+    const int ch = (int)(k / P);
+    const int64_t p = k % P;
+    const int py = (int)(p / W), px = (int)(p % W);
+    float f[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 11; ++t) {
+        const int q = py + t - 5;
+        if (q < 0 || q >= H) continue;
+        const float wv = win.w[t];
+#pragma unroll
+        for (int s = 0; s < 3; ++s) f[s] += wv * hs[(s * 3 + ch) * P + (int64_t)q * W + px];
+    }
+    const float xv = x[k], yv = y[k];
+    const float dssim = f[0] + 2.f * xv * f[1] + yv * f[2];
+    const float d = xv - yv;
+    const float sg = d > 0.f ? 1.f : (d < 0.f ? -1.f : 0.f);
+    dl[k] = (1.0f - lambda) * sg * inv - lambda * dssim * inv;
+}
+
+}  // namespace
+
+gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate)
+{
+    hipLaunchKernelGGL(k_sum_f64, dim3(1), dim3(256), 0, ctx->stream, in, n, stride, out, accumulate);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+int64_t ssim_partial_blocks(int W, int H) { return ceil_div(3 * (int64_t)W * H, kSB); }
+
+gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,
+                      float* dl_dimage, double* partials, int64_t n_blocks, float* scratch)
+{
+    Win win;
+    double g[11], s = 0.0;
+    for (int i = 0; i < 11; ++i) {
+        g[i] = std::exp(-((i - 5) * (i - 5)) / (2.0 * 1.5 * 1.5));
+        s += g[i];
+    }
+    for (int i = 0; i < 11; ++i) win.w[i] = (float)(g[i] / s);
+    const int64_t P = (int64_t)W * H;
+    float* bufA = scratch;            // 15 maps
+    float* bufB = scratch + 15 * P;   // 9 maps
+    const float inv = (float)(1.0 / (3.0 * (double)P));
+    GsTimerScope ts(ctx, "ssim");
+    hipLaunchKernelGGL(k_ssim_h, dim3((unsigned)ceil_div(3 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, image,
+                       target, bufA);
+    hipLaunchKernelGGL(k_ssim_v, dim3((unsigned)n_blocks), dim3(kSB), 0, ctx->stream, W, H, win, bufA, image, target,
+                       bufB, partials);
+    hipLaunchKernelGGL(k_ssim_h2, dim3((unsigned)ceil_div(9 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, bufB,
+                       bufA);
+    hipLaunchKernelGGL(k_ssim_v2, dim3((unsigned)ceil_div(3 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, bufA,
+                       image, target, lambda, inv, dl_dimage);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}

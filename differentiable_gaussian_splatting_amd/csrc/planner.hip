@@ -1,0 +1,186 @@
+// planner.hip -- load-budgeted leaf planning.
+//
+// BoundedGS page, "01": regions are sized by their actual load, estimated
+// from the overlap count, the pixels and the buffer layout, so dense regions
+// become small and sparse ones large; Fig. 3 B->C: regions over the budget
+// are subdivided further.  Reading: starting from the whole tile grid, a
+// region is kept when est <= budget or it is a single tile; otherwise its
+// longer side (ties: x) is halved at floor(len/2) and both halves are planned
+// in order (depth-first order of the leaves).
+//
+// Per-tile overlap counts come from the same 2D difference array as binning;
+// a summed-area table makes every region's overlap count O(1).  The split
+// recursion runs in one workgroup, level by level: the frontier is kept in
+// depth-first order, and each level replaces every region to be split by its
+// two halves (a workgroup scan gives the output positions), so the final
+// frontier is the depth-first list of leaves.
+#include "gs_device.h"
+#include "gs_internal.h"
+
+namespace {
+
+__global__ void k_counts_to_sat(const int32_t* __restrict__ cnt, int TW, int TH, uint64_t* __restrict__ sat)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t S = TW + 1;
+    if (k >= S * (TH + 1)) return;
+    const int64_t y = k / S, x = k % S;
+    sat[k] = (x == 0 || y == 0) ? 0ull : (uint64_t)(uint32_t)cnt[(y - 1) * TW + (x - 1)];
+}
+
+struct PlanArgs {
+    int W, H, TW, TH;
+    uint64_t budget, bI, bP, bT, b0;
+};
+
+__device__ __forceinline__ uint64_t region_est(const PlanArgs& a, const uint64_t* __restrict__ sat, int4 r)
+{
+    const int64_t S = a.TW + 1;
+    const uint64_t I = sat[(int64_t)r.w * S + r.z] - sat[(int64_t)r.y * S + r.z] - sat[(int64_t)r.w * S + r.x] +
+                       sat[(int64_t)r.y * S + r.x];
+    const int64_t x1 = min<int64_t>((int64_t)r.z * 16, a.W), y1 = min<int64_t>((int64_t)r.w * 16, a.H);
+    const uint64_t P = (uint64_t)(x1 - (int64_t)r.x * 16) * (uint64_t)(y1 - (int64_t)r.y * 16);
+    const uint64_t T = (uint64_t)(r.z - r.x) * (uint64_t)(r.w - r.y);
+    return a.bI * I + a.bP * P + a.bT * T + a.b0;
+}
+
+__device__ __forceinline__ bool region_split(const PlanArgs& a, const uint64_t* __restrict__ sat, int4 r)
+{
+    const bool single = (r.z - r.x) == 1 && (r.w - r.y) == 1;
+    return !single && region_est(a, sat, r) > a.budget;
+}
+
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* tot, uint32_t* sh)
+{
+    // sh: kPlanThreads / 64 entries
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(x, o, 64);
+        if (lane >= o) x += u;
+    }
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+        if (w < wave) before += sh[w];
+        all += sh[w];
+    }
+    __syncthreads();
+    *tot = all;
+    return before + x - v;
+}
+
+// frontier ping-pong in global memory; cap >= number of tiles
+__global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a, const uint64_t* __restrict__ sat,
+                                                       int4* __restrict__ fa, int4* __restrict__ fb, int64_t cap,
+                                                       gs_leaf* __restrict__ leaves, int32_t max_leaves,
+                                                       int32_t* __restrict__ count_out,
+                                                       int32_t* __restrict__ over_out)
+{
+    __shared__ uint32_t sh[kPlanThreads / 64];
+    __shared__ uint32_t s_total, s_any;
+    int4* cur = fa;
+    int4* nxt = fb;
+    if (threadIdx.x == 0) cur[0] = make_int4(0, 0, a.TW, a.TH);
+    uint32_t n = 1;
+    __syncthreads();
+    for (;;) {
+        // one level: every region to split becomes two, in order
+        uint32_t carry = 0;
+        if (threadIdx.x == 0) s_any = 0;
+        __syncthreads();
+        for (uint32_t c0 = 0; c0 < n; c0 += kPlanThreads) {
+            const uint32_t i = c0 + threadIdx.x;
+            int4 r = make_int4(0, 0, 0, 0);
+            bool sp = false;
+            if (i < n) {
+                r = cur[i];
+                sp = region_split(a, sat, r);
+            }
+            const uint32_t w = i < n ? (sp ? 2u : 1u) : 0u;
+            uint32_t tot;
+            const uint32_t pos = carry + block_excl_scan_u32(w, &tot, sh);
+            if (i < n && pos + w <= cap) {
+                if (!sp) {
+                    nxt[pos] = r;
+                } else {
+                    int4 lo = r, hi = r;
+                    const int wdt = r.z - r.x, hgt = r.w - r.y;
+                    if (wdt >= hgt) { lo.z = r.x + wdt / 2; hi.x = lo.z; }
+                    else { lo.w = r.y + hgt / 2; hi.y = lo.w; }
+                    nxt[pos] = lo;
+                    nxt[pos + 1] = hi;
+                    s_any = 1;
+                }
+            }
+            carry += tot;
+            __syncthreads();
+        }
+        const uint32_t any = s_any;
+        n = carry < cap ? carry : (uint32_t)cap;
+        int4* t = cur;
+        cur = nxt;
+        nxt = t;
+        __syncthreads();
+        if (!any) break;
+    }
+    // cur holds the leaves in depth-first order
+    uint32_t over = 0;
+    for (uint32_t i = threadIdx.x; i < n; i += kPlanThreads) {
+        const int4 r = cur[i];
+        const uint64_t e = region_est(a, sat, r);
+        if (e > a.budget) over = 1;
+        if ((int32_t)i < max_leaves) {
+            gs_leaf L;
+            L.tx0 = r.x; L.ty0 = r.y; L.tx1 = r.z; L.ty1 = r.w;
+            L.est_bytes = e;
+            L.over_budget = e > a.budget ? 1 : 0;
+            L.pad = 0;
+            leaves[i] = L;
+        }
+    }
+    if (over) atomicOr(over_out, 1);
+    if (threadIdx.x == 0) *count_out = (int32_t)n;
+}
+
+}  // namespace
+
+gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, int32_t* diff, uint64_t budget,
+                      const gs_cost_model* cost, gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev,
+                      int32_t* over_dev)
+{
+    const int TW = proj->TW, TH = proj->TH;
+    const int64_t T = (int64_t)TW * TH;
+    gs_status st = launch_fill_u32(ctx, (uint32_t*)diff, 0u, T);
+    if (st != GS_OK) return st;
+    gs_tile_rect all{0, 0, TW, TH};
+    if ((st = launch_rect_diff(ctx, proj, all, diff)) != GS_OK) return st;
+    if ((st = launch_prefix2d_i32(ctx, diff, TH, TW)) != GS_OK) return st;
+    const int64_t S = (int64_t)(TW + 1) * (TH + 1);
+    hipLaunchKernelGGL(k_counts_to_sat, dim3((unsigned)ceil_div(S, 256)), dim3(256), 0, ctx->stream, diff, TW, TH, sat);
+    if ((st = launch_prefix2d_u64(ctx, sat, TH + 1, TW + 1)) != GS_OK) return st;
+
+    std::vector<GsAlloc> tmp;
+    int4* fa = (int4*)gs_malloc(ctx, sizeof(int4) * T, GS_MEM_SCRATCH, &tmp);
+    int4* fb = (int4*)gs_malloc(ctx, sizeof(int4) * T, GS_MEM_SCRATCH, &tmp);
+    if (!fa || !fb) {
+        gs_free_all(ctx, &tmp);
+        return GS_ERR_OOM;
+    }
+    PlanArgs a;
+    a.W = proj->W; a.H = proj->H; a.TW = TW; a.TH = TH;
+    a.budget = budget;
+    a.bI = cost->b_isect; a.bP = cost->b_pixel; a.bT = cost->b_tile; a.b0 = cost->b_const;
+    GS_HIP(ctx, hipMemsetAsync(over_dev, 0, sizeof(int32_t), ctx->stream));
+    {
+        GsTimerScope ts(ctx, "plan_split");
+        hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, ctx->stream, a, sat, fa, fb, T, leaves_dev,
+                           max_leaves, count_dev, over_dev);
+    }
+    gs_free_all(ctx, &tmp);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}

@@ -1,0 +1,486 @@
+// project.hip -- EWA projection with candidate compaction, its backward, and
+// inspection exports.
+//
+// BoundedGS page, Fig. 3 C->D->E: projected state and gradients are kept only
+// for candidate Gaussians (those that may take part in the view).  Two passes:
+// (1) per Gaussian, decide candidacy; (2) after an exclusive scan of the
+// decisions (stable, ascending Gaussian id), recompute and write the compact
+// state of each candidate at its slot.  Pass 2 recomputes the geometry rather
+// than staging it for all N Gaussians, so only candidates cost HBM writes.
+#include "gs_device.h"
+#include "gs_internal.h"
+
+namespace {
+
+struct CamDev {
+    float R[9], t[3], cc[3];
+    float fx, fy, cx, cy, near_z, limx, limy;
+    int W, H, TW, TH;
+};
+
+CamDev make_cam(const gs_camera* c)
+{
+    CamDev d;
+    for (int k = 0; k < 9; ++k) d.R[k] = c->R[k];
+    for (int k = 0; k < 3; ++k) d.t[k] = c->t[k];
+    // camera centre -R^T t, summed in row order
+    for (int k = 0; k < 3; ++k) d.cc[k] = -((d.R[k] * d.t[0] + d.R[3 + k] * d.t[1]) + d.R[6 + k] * d.t[2]);
+    d.fx = c->fx; d.fy = c->fy; d.cx = c->cx; d.cy = c->cy; d.near_z = c->near_z;
+    d.limx = 1.3f * ((0.5f * (float)c->width) / c->fx);
+    d.limy = 1.3f * ((0.5f * (float)c->height) / c->fy);
+    d.W = c->width; d.H = c->height;
+    d.TW = (c->width + 15) / 16; d.TH = (c->height + 15) / 16;
+    return d;
+}
+
+struct Proj2D {
+    bool ok;
+    float x, y, A, B, C, r, depth;
+    int tx0, ty0, tx1, ty1;
+    uint32_t flags;
+    float vx, vy, vz;   // mean - camera centre (for the colour direction)
+};
+
+__device__ __forceinline__ float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Geometry of Gaussian i in the specified f32 operation order.
+__device__ __forceinline__ Proj2D project_geom(const CamDev& cam, const float* __restrict__ means,
+                                               const float* __restrict__ log_scales,
+                                               const float* __restrict__ quats, int64_t i)
+{
+    Proj2D o;
+    o.ok = true;
+    o.flags = 0;
+    const float mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
+    const float px = ((cam.R[0] * mx + cam.R[1] * my) + cam.R[2] * mz) + cam.t[0];
+    const float py = ((cam.R[3] * mx + cam.R[4] * my) + cam.R[5] * mz) + cam.t[1];
+    const float pz = ((cam.R[6] * mx + cam.R[7] * my) + cam.R[8] * mz) + cam.t[2];
+    o.depth = pz;
+    o.vx = mx - cam.cc[0];
+    o.vy = my - cam.cc[1];
+    o.vz = mz - cam.cc[2];
+    if (!(pz > cam.near_z)) { o.ok = false; return o; }
+
+    const float s0 = gsd::exp_cw(log_scales[3 * i]);
+    const float s1 = gsd::exp_cw(log_scales[3 * i + 1]);
+    const float s2 = gsd::exp_cw(log_scales[3 * i + 2]);
+    const float4 q = *reinterpret_cast<const float4*>(quats + 4 * i);
+    const float qn = sqrtf(((q.x * q.x + q.y * q.y) + q.z * q.z) + q.w * q.w);
+    const float w = q.x / qn, x = q.y / qn, y = q.z / qn, z = q.w / qn;
+    float Rq[3][3];
+    Rq[0][0] = 1.0f - 2.0f * (y * y + z * z);
+    Rq[0][1] = 2.0f * (x * y - w * z);
+    Rq[0][2] = 2.0f * (x * z + w * y);
+    Rq[1][0] = 2.0f * (x * y + w * z);
+    Rq[1][1] = 1.0f - 2.0f * (x * x + z * z);
+    Rq[1][2] = 2.0f * (y * z - w * x);
+    Rq[2][0] = 2.0f * (x * z - w * y);
+    Rq[2][1] = 2.0f * (y * z + w * x);
+    Rq[2][2] = 1.0f - 2.0f * (x * x + y * y);
+    const float s[3] = {s0, s1, s2};
+    float M[3][3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) M[r][c] = Rq[r][c] * s[c];
+    float Sg[3][3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = r; c < 3; ++c) {
+            Sg[r][c] = (M[r][0] * M[c][0] + M[r][1] * M[c][1]) + M[r][2] * M[c][2];
+            Sg[c][r] = Sg[r][c];
+        }
+    const float u = px / pz, v = py / pz;
+    float ux = u, uy = v;
+    if (ux < -cam.limx) { ux = -cam.limx; o.flags |= 8u; }
+    else if (ux > cam.limx) { ux = cam.limx; o.flags |= 8u; }
+    if (uy < -cam.limy) { uy = -cam.limy; o.flags |= 16u; }
+    else if (uy > cam.limy) { uy = cam.limy; o.flags |= 16u; }
+    const float J00 = cam.fx / pz, J02 = -((cam.fx * ux) / pz);
+    const float J11 = cam.fy / pz, J12 = -((cam.fy * uy) / pz);
+    float T[2][3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        T[0][c] = J00 * cam.R[c] + J02 * cam.R[6 + c];
+        T[1][c] = J11 * cam.R[3 + c] + J12 * cam.R[6 + c];
+    }
+    float U[2][3];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) U[a][c] = (T[a][0] * Sg[0][c] + T[a][1] * Sg[1][c]) + T[a][2] * Sg[2][c];
+    const float s00 = (U[0][0] * T[0][0] + U[0][1] * T[0][1]) + U[0][2] * T[0][2];
+    const float s01 = (U[0][0] * T[1][0] + U[0][1] * T[1][1]) + U[0][2] * T[1][2];
+    const float s11 = (U[1][0] * T[1][0] + U[1][1] * T[1][1]) + U[1][2] * T[1][2];
+    const float a = s00 + 0.3f, b = s01, c = s11 + 0.3f;
+    const float det = a * c - b * b;
+    if (!(det > 0.0f)) { o.ok = false; return o; }
+    o.A = c / det;
+    o.B = -(b / det);
+    o.C = a / det;
+    const float mid = 0.5f * (a + c);
+    float disc = mid * mid - det;
+    disc = disc > 0.1f ? disc : 0.1f;
+    const float lam = mid + sqrtf(disc);
+    o.r = ceilf(3.0f * sqrtf(lam));
+    o.x = cam.fx * u + cam.cx;
+    o.y = cam.fy * v + cam.cy;
+    if (!(isfinite(o.x) && isfinite(o.y) && isfinite(o.A) && isfinite(o.B) && isfinite(o.C) && isfinite(o.r))) {
+        o.ok = false;
+        return o;
+    }
+    o.tx0 = (int)clampf(floorf((o.x - o.r) * 0.0625f), 0.0f, (float)cam.TW);
+    o.tx1 = (int)clampf(floorf((o.x + o.r) * 0.0625f) + 1.0f, 0.0f, (float)cam.TW);
+    o.ty0 = (int)clampf(floorf((o.y - o.r) * 0.0625f), 0.0f, (float)cam.TH);
+    o.ty1 = (int)clampf(floorf((o.y + o.r) * 0.0625f) + 1.0f, 0.0f, (float)cam.TH);
+    if (o.tx0 >= o.tx1 || o.ty0 >= o.ty1) o.ok = false;
+    return o;
+}
+
+__global__ __launch_bounds__(256) void k_project_flags(CamDev cam, int64_t n, const float* __restrict__ means,
+                                                       const float* __restrict__ log_scales,
+                                                       const float* __restrict__ quats, uint32_t* __restrict__ flag)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    flag[i] = project_geom(cam, means, log_scales, quats, i).ok ? 1u : 0u;
+}
+
+__global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, int deg,
+                                                       const float* __restrict__ means,
+                                                       const float* __restrict__ log_scales,
+                                                       const float* __restrict__ quats,
+                                                       const float* __restrict__ logits,
+                                                       const float* __restrict__ sh,
+                                                       const uint32_t* __restrict__ flag,
+                                                       const uint32_t* __restrict__ slot, uint32_t* __restrict__ ids,
+                                                       int4* __restrict__ rect, float4* __restrict__ g0,
+                                                       float4* __restrict__ g1, float4* __restrict__ g2,
+                                                       int32_t* __restrict__ slot_of)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    if (!flag[i]) {
+        slot_of[i] = -1;
+        return;
+    }
+    const uint32_t j = slot[i];
+    slot_of[i] = (int32_t)j;
+    const Proj2D p = project_geom(cam, means, log_scales, quats, i);
+    const float o = 1.0f / (1.0f + gsd::exp_cw(-logits[i]));
+    const float vn = sqrtf((p.vx * p.vx + p.vy * p.vy) + p.vz * p.vz);
+    const float dx = p.vx / vn, dy = p.vy / vn, dz = p.vz / vn;
+    float Y[16];
+    gsd::sh_basis(deg, dx, dy, dz, Y);
+    const int K = (deg + 1) * (deg + 1);
+    const float* shi = sh + (int64_t)3 * K * i;
+    float rgb[3];
+    uint32_t fl = p.flags;
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) {
+        float acc = Y[0] * shi[ch];
+        for (int k = 1; k < K; ++k) acc = acc + Y[k] * shi[3 * k + ch];
+        acc = acc + 0.5f;
+        if (acc < 0.0f) {
+            acc = 0.0f;
+            fl |= (1u << ch);
+        }
+        rgb[ch] = acc;
+    }
+    ids[j] = (uint32_t)i;
+    rect[j] = make_int4(p.tx0, p.ty0, p.tx1, p.ty1);
+    g0[j] = make_float4(p.x, p.y, -0.5f * p.A, -p.B);
+    g1[j] = make_float4(-0.5f * p.C, o, rgb[0], rgb[1]);
+    g2[j] = make_float4(rgb[2], p.depth, p.r, __builtin_bit_cast(float, fl));
+}
+
+// ---------------------------------------------------------------------------
+// Projection backward, one thread per candidate (f32).  Chain rule through
+// each step of the projection, with the forward's clamp decisions (flags).
+__global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand, int deg,
+                                                     const float* __restrict__ means,
+                                                     const float* __restrict__ log_scales,
+                                                     const float* __restrict__ quats,
+                                                     const float* __restrict__ logits, const float* __restrict__ sh,
+                                                     const uint32_t* __restrict__ ids,
+                                                     const float4* __restrict__ g2s,
+                                                     const float* __restrict__ grad2d, float* __restrict__ grad3d)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n_cand) return;
+    const int64_t i = ids[j];
+    const int K = (deg + 1) * (deg + 1);
+    const int F = 11 + 3 * K;
+    const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[j].w);
+    const float* g = grad2d + 9 * j;
+    float* out = grad3d + (int64_t)F * j;
+
+    // forward recomputation
+    const float mu[3] = {means[3 * i], means[3 * i + 1], means[3 * i + 2]};
+    float p[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) p[r] = cam.R[3 * r] * mu[0] + cam.R[3 * r + 1] * mu[1] + cam.R[3 * r + 2] * mu[2] + cam.t[r];
+    const float pz = p[2];
+    float s[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) s[k] = gsd::exp_cw(log_scales[3 * i + k]);
+    const float4 q = *reinterpret_cast<const float4*>(quats + 4 * i);
+    const float qn = sqrtf(q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w);
+    const float w = q.x / qn, x = q.y / qn, y = q.z / qn, z = q.w / qn;
+    float Rq[3][3];
+    Rq[0][0] = 1.0f - 2.0f * (y * y + z * z); Rq[0][1] = 2.0f * (x * y - w * z); Rq[0][2] = 2.0f * (x * z + w * y);
+    Rq[1][0] = 2.0f * (x * y + w * z); Rq[1][1] = 1.0f - 2.0f * (x * x + z * z); Rq[1][2] = 2.0f * (y * z - w * x);
+    Rq[2][0] = 2.0f * (x * z - w * y); Rq[2][1] = 2.0f * (y * z + w * x); Rq[2][2] = 1.0f - 2.0f * (x * x + y * y);
+    float M[3][3], Sg[3][3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) M[r][c] = Rq[r][c] * s[c];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) Sg[r][c] = M[r][0] * M[c][0] + M[r][1] * M[c][1] + M[r][2] * M[c][2];
+    const float u = p[0] / pz, v = p[1] / pz;
+    const bool clx = (fl & 8u) != 0, cly = (fl & 16u) != 0;
+    const float ux = clx ? (u < 0.0f ? -cam.limx : cam.limx) : u;
+    const float uy = cly ? (v < 0.0f ? -cam.limy : cam.limy) : v;
+    const float iz = 1.0f / pz;
+    const float J00 = cam.fx * iz, J02 = -cam.fx * ux * iz, J11 = cam.fy * iz, J12 = -cam.fy * uy * iz;
+    float T[2][3], U[2][3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        T[0][c] = J00 * cam.R[c] + J02 * cam.R[6 + c];
+        T[1][c] = J11 * cam.R[3 + c] + J12 * cam.R[6 + c];
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) U[a][c] = T[a][0] * Sg[0][c] + T[a][1] * Sg[1][c] + T[a][2] * Sg[2][c];
+    const float a = U[0][0] * T[0][0] + U[0][1] * T[0][1] + U[0][2] * T[0][2] + 0.3f;
+    const float b = U[0][0] * T[1][0] + U[0][1] * T[1][1] + U[0][2] * T[1][2];
+    const float c = U[1][0] * T[1][0] + U[1][1] * T[1][1] + U[1][2] * T[1][2] + 0.3f;
+    const float det = a * c - b * b;
+    const float o = 1.0f / (1.0f + gsd::exp_cw(-logits[i]));
+    const float vx = mu[0] - cam.cc[0], vy = mu[1] - cam.cc[1], vz = mu[2] - cam.cc[2];
+    const float vn = sqrtf(vx * vx + vy * vy + vz * vz);
+    const float d[3] = {vx / vn, vy / vn, vz / vn};
+
+    // mean2d = (fx u + cx, fy v + cy)
+    float dp[3];
+    const float du = cam.fx * g[0], dv = cam.fy * g[1];
+    dp[0] = du * iz;
+    dp[1] = dv * iz;
+    dp[2] = -(du * u + dv * v) * iz;
+    // conic = (c, -b, a) / det
+    const float dA = g[2], dB = g[3], dC = g[4];
+    const float idet2 = 1.0f / (det * det);
+    const float da = (-c * c * dA + b * c * dB - b * b * dC) * idet2;
+    const float db = (2.0f * b * c * dA - (a * c + b * b) * dB + 2.0f * a * b * dC) * idet2;
+    const float dc = (-b * b * dA + a * b * dB - a * a * dC) * idet2;
+    // Sigma2 entries (0,0), (0,1), (1,1) = U T^T
+    float dU[2][3], dT[2][3], dSg[3][3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        dU[0][k] = da * T[0][k] + db * T[1][k];
+        dU[1][k] = dc * T[1][k];
+        dT[0][k] = da * U[0][k];
+        dT[1][k] = db * U[0][k] + dc * U[1][k];
+    }
+    // U = T Sigma
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc) dSg[k][cc] = T[0][k] * dU[0][cc] + T[1][k] * dU[1][cc];
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            dT[aa][k] += dU[aa][0] * Sg[k][0] + dU[aa][1] * Sg[k][1] + dU[aa][2] * Sg[k][2];
+    // T = J R
+    float dJ00 = 0.0f, dJ02 = 0.0f, dJ11 = 0.0f, dJ12 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        dJ00 += dT[0][k] * cam.R[k];
+        dJ02 += dT[0][k] * cam.R[6 + k];
+        dJ11 += dT[1][k] * cam.R[3 + k];
+        dJ12 += dT[1][k] * cam.R[6 + k];
+    }
+    const float iz2 = iz * iz;
+    dp[2] += -cam.fx * iz2 * dJ00 + cam.fx * ux * iz2 * dJ02 - cam.fy * iz2 * dJ11 + cam.fy * uy * iz2 * dJ12;
+    const float dux = -cam.fx * iz * dJ02, duy = -cam.fy * iz * dJ12;
+    if (!clx) { dp[0] += dux * iz; dp[2] -= dux * u * iz; }
+    if (!cly) { dp[1] += duy * iz; dp[2] -= duy * v * iz; }
+    // Sigma = M M^T
+    float dM[3][3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc)
+            dM[r][cc] = (dSg[r][0] + dSg[0][r]) * M[0][cc] + (dSg[r][1] + dSg[1][r]) * M[1][cc] +
+                        (dSg[r][2] + dSg[2][r]) * M[2][cc];
+    float dRq[3][3], ds[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc) {
+            dRq[r][cc] = dM[r][cc] * s[cc];
+            ds[cc] += dM[r][cc] * Rq[r][cc];
+        }
+    out[3] = ds[0] * s[0];
+    out[4] = ds[1] * s[1];
+    out[5] = ds[2] * s[2];
+    // rotation of the unit quaternion (w, x, y, z)
+    float gw = 0.0f, gx = 0.0f, gy = 0.0f, gz = 0.0f;
+    gy += -4.0f * y * dRq[0][0]; gz += -4.0f * z * dRq[0][0];
+    gx += 2.0f * y * dRq[0][1]; gy += 2.0f * x * dRq[0][1]; gw += -2.0f * z * dRq[0][1]; gz += -2.0f * w * dRq[0][1];
+    gx += 2.0f * z * dRq[0][2]; gz += 2.0f * x * dRq[0][2]; gw += 2.0f * y * dRq[0][2]; gy += 2.0f * w * dRq[0][2];
+    gx += 2.0f * y * dRq[1][0]; gy += 2.0f * x * dRq[1][0]; gw += 2.0f * z * dRq[1][0]; gz += 2.0f * w * dRq[1][0];
+    gx += -4.0f * x * dRq[1][1]; gz += -4.0f * z * dRq[1][1];
+    gy += 2.0f * z * dRq[1][2]; gz += 2.0f * y * dRq[1][2]; gw += -2.0f * x * dRq[1][2]; gx += -2.0f * w * dRq[1][2];
+    gx += 2.0f * z * dRq[2][0]; gz += 2.0f * x * dRq[2][0]; gw += -2.0f * y * dRq[2][0]; gy += -2.0f * w * dRq[2][0];
+    gy += 2.0f * z * dRq[2][1]; gz += 2.0f * y * dRq[2][1]; gw += 2.0f * x * dRq[2][1]; gx += 2.0f * w * dRq[2][1];
+    gx += -4.0f * x * dRq[2][2]; gy += -4.0f * y * dRq[2][2];
+    const float dot = w * gw + x * gx + y * gy + z * gz;
+    const float iqn = 1.0f / qn;
+    out[6] = (gw - w * dot) * iqn;
+    out[7] = (gx - x * dot) * iqn;
+    out[8] = (gy - y * dot) * iqn;
+    out[9] = (gz - z * dot) * iqn;
+    out[10] = g[5] * o * (1.0f - o);
+    // colour: rgb = 0.5 + sum_k Y_k(d) sh_k, masked where clamped
+    float Y[16], D[16][3];
+    gsd::sh_basis(deg, d[0], d[1], d[2], Y);
+    gsd::sh_basis_grad(deg, d[0], d[1], d[2], D);
+    const float* shi = sh + (int64_t)3 * K * i;
+    float dd0 = 0.0f, dd1 = 0.0f, dd2 = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        float t = 0.0f;
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) {
+            const float gr = (fl & (1u << ch)) ? 0.0f : g[6 + ch];
+            out[11 + 3 * k + ch] = Y[k] * gr;
+            t += shi[3 * k + ch] * gr;
+        }
+        dd0 += t * D[k][0];
+        dd1 += t * D[k][1];
+        dd2 += t * D[k][2];
+    }
+    const float ddot = d[0] * dd0 + d[1] * dd1 + d[2] * dd2;
+    const float ivn = 1.0f / vn;
+    float dmu[3] = {(dd0 - d[0] * ddot) * ivn, (dd1 - d[1] * ddot) * ivn, (dd2 - d[2] * ddot) * ivn};
+#pragma unroll
+    for (int e = 0; e < 3; ++e) dmu[e] += cam.R[e] * dp[0] + cam.R[3 + e] * dp[1] + cam.R[6 + e] * dp[2];
+    out[0] = dmu[0];
+    out[1] = dmu[1];
+    out[2] = dmu[2];
+}
+
+// ---------------------------------------------------------------------------
+__global__ void k_export_proj(int64_t n, int field, const uint32_t* __restrict__ ids, const int4* __restrict__ rect,
+                              const float4* __restrict__ g0, const float4* __restrict__ g1,
+                              const float4* __restrict__ g2, void* __restrict__ dst)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n) return;
+    switch (field) {
+    case GS_PROJ_IDS: ((uint32_t*)dst)[j] = ids[j]; break;
+    case GS_PROJ_RECT: ((int4*)dst)[j] = rect[j]; break;
+    case GS_PROJ_XY: ((float*)dst)[2 * j] = g0[j].x; ((float*)dst)[2 * j + 1] = g0[j].y; break;
+    case GS_PROJ_CONIC:   // stored as -A/2, -B, -C/2: exact rescaling
+        ((float*)dst)[3 * j] = -2.0f * g0[j].z;
+        ((float*)dst)[3 * j + 1] = -g0[j].w;
+        ((float*)dst)[3 * j + 2] = -2.0f * g1[j].x;
+        break;
+    case GS_PROJ_DEPTH: ((float*)dst)[j] = g2[j].y; break;
+    case GS_PROJ_RADIUS: ((float*)dst)[j] = g2[j].z; break;
+    case GS_PROJ_OPACITY: ((float*)dst)[j] = g1[j].y; break;
+    case GS_PROJ_RGB:
+        ((float*)dst)[3 * j] = g1[j].z;
+        ((float*)dst)[3 * j + 1] = g1[j].w;
+        ((float*)dst)[3 * j + 2] = g2[j].x;
+        break;
+    case GS_PROJ_FLAGS: ((uint32_t*)dst)[j] = __builtin_bit_cast(uint32_t, g2[j].w); break;
+    default: break;
+    }
+}
+
+__global__ void k_copy_i32(int64_t n, const int32_t* __restrict__ src, int32_t* __restrict__ dst)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) dst[j] = src[j];
+}
+
+__global__ void k_exp(int64_t n, const float* __restrict__ x, float* __restrict__ y)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) y[j] = gsd::exp_cw(x[j]);
+}
+
+}  // namespace
+
+gs_status launch_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
+                         uint32_t* flag, uint32_t* slot)
+{
+    const CamDev cd = make_cam(cam);
+    const int64_t n = p->n;
+    if (n > 0) {
+        GsTimerScope ts(ctx, "project_flags");
+        hipLaunchKernelGGL(k_project_flags, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, cd, n,
+                           p->means, p->log_scales, p->quats, flag);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return launch_scan_u32_to_u32(ctx, flag, slot, n);
+}
+
+// second half of the projection (after the host read the candidate count)
+gs_status launch_project_write(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
+                               const uint32_t* flag, const uint32_t* slot)
+{
+    const CamDev cd = make_cam(cam);
+    const int64_t n = p->n;
+    if (n > 0) {
+        GsTimerScope ts(ctx, "project_write");
+        hipLaunchKernelGGL(k_project_write, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, cd, n,
+                           p->sh_degree, p->means, p->log_scales, p->quats, p->opacity_logits, p->sh, flag, slot,
+                           proj->ids, proj->rect, proj->g0, proj->g1, proj->g2, proj->slot_of);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
+                             const float* grad2d, float* grad3d)
+{
+    const CamDev cd = make_cam(cam);
+    if (proj->n_cand > 0) {
+        GsTimerScope ts(ctx, "project_bwd");
+        hipLaunchKernelGGL(k_project_bwd, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream, cd,
+                           proj->n_cand, p->sh_degree, p->means, p->log_scales, p->quats, p->opacity_logits, p->sh,
+                           proj->ids, proj->g2, grad2d, grad3d);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_export_proj(gs_ctx* ctx, const gs_proj* proj, int field, void* dst)
+{
+    if (field == GS_PROJ_SLOT_OF) {
+        if (proj->n > 0)
+            hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)ceil_div(proj->n, 256)), dim3(256), 0, ctx->stream,
+                               proj->n, proj->slot_of, (int32_t*)dst);
+    } else if (proj->n_cand > 0) {
+        hipLaunchKernelGGL(k_export_proj, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream,
+                           proj->n_cand, field, proj->ids, proj->rect, proj->g0, proj->g1, proj->g2, dst);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n)
+{
+    if (n > 0)
+        hipLaunchKernelGGL(k_exp, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, x, y);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
