@@ -27,11 +27,17 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
 # 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz: f32 VALU instructions per second,
 # counting one per lane (an fma counts once); packed f32 is not used.
 PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# per (pixel, entry) pair of the raster backward: f32 VALU operations of the
-# specified arithmetic (recompute power/exp/alpha 29, T recovery 6,
-# dL/dalpha 12, the other partials 20, colour-behind update 9)
-OPS_PER_PAIR_BWD = 76
-OPS_PER_PAIR_FWD = 38
+# f32 VALU operations of the specified per-(pixel, entry) arithmetic:
+#   every examined pair: offsets 2, power 5, range test 2, exp 14, alpha with
+#     clamp and threshold 4                                            = 27
+#   an included pair adds, forward: T' 2, stop test 1, weight 1,
+#     colour 3 fma, bookkeeping 1                                      -> 35
+#   backward: T recovery 3, colour partials 4, dL/dalpha 12, colour
+#     behind 3, opacity and exponent partials 9, conic and mean partials 7
+#                                                                      -> 65
+OPS_EXAMINED = 27
+OPS_INCLUDED_FWD = 35
+OPS_INCLUDED_BWD = 65
 
 
 def log(*a):
@@ -111,8 +117,8 @@ def main():
     log(f"[bench] {args.steps} steps in {t_total:.3f}s: {ms_step:.2f} ms/step, loss {r['loss']:.6f}, "
         f"leaves {r['n_leaves']}, isect {r['n_isect']}")
 
-    kernels = ["project_flags", "project_write", "prefix2d", "scan", "rect_diff", "emit", "sort_tiles",
-               "plan_split", "raster_fwd", "raster_bwd", "project_bwd", "adam"]
+    kernels = ["project_flags", "project_write", "prefix2d", "scan", "rect_diff", "bin_count", "emit", "radix",
+               "seg_offsets", "plan_split", "leaf_groups", "raster_fwd", "raster_bwd", "project_bwd", "adam"]
     ktimes = {}
     for name in kernels:
         ms, n = B.gs_kernel_time(ctx, name)
@@ -121,15 +127,31 @@ def main():
     log("[bench] per-step kernel time (ms): " +
         ", ".join(f"{k}={v['total_ms']:.2f}" for k, v in sorted(ktimes.items(), key=lambda kv: -kv[1]['total_ms'])))
 
-    # work counters of the view (untimed): pairs the raster backward walks
-    q_b = count_backward_pairs(B, ctx, cam, params, budget)
-    dom = "raster_bwd"
-    bwd = ktimes.get(dom, dict(total_ms=float("nan"), launches=0, avg_ms=float("nan")))
-    achieved = OPS_PER_PAIR_BWD * q_b / (bwd["total_ms"] * 1e-3) / 1e12   # per-step totals
-    roofline = dict(bound="alu", achieved=round(achieved, 3), peak=round(PEAK_VALU_TOPS, 2), unit="Top/s",
-                    frac=round(achieved / PEAK_VALU_TOPS, 4), traffic=None, kernel=dom,
-                    ops_per_unit=OPS_PER_PAIR_BWD, units_per_step=int(q_b),
-                    avg_launch_ms=round(bwd["avg_ms"], 4), launches_per_step=bwd["launches"])
+    # work counters of the view (untimed pass): pairs examined / included /
+    # revisited by the backward, intersections, candidates
+    wc = count_work(B, ctx, cam, params, budget)
+    work = kernel_work(wc, sc)
+    rooflines = {}
+    for name, (bound, amount, unit_desc) in work.items():
+        kt = ktimes.get(name)
+        if not kt:
+            continue
+        sec = kt["total_ms"] * 1e-3
+        if bound == "alu":
+            ach = amount / sec / 1e12
+            rooflines[name] = dict(bound="alu", achieved=round(ach, 3), peak=round(PEAK_VALU_TOPS, 2), unit="Top/s",
+                                   frac=round(ach / PEAK_VALU_TOPS, 4), work=unit_desc)
+        else:
+            ach = amount / sec / 1e9
+            rooflines[name] = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                                   frac=round(ach / PEAK_HBM_GBS, 4), work=unit_desc)
+    dom = max((k for k in rooflines), key=lambda k: ktimes[k]["total_ms"])
+    roofline = dict(rooflines[dom])
+    roofline.update(traffic=None, kernel=dom, avg_launch_ms=round(ktimes[dom]["avg_ms"], 4),
+                    launches_per_step=ktimes[dom]["launches"])
+    # whole-step HBM fraction: the algorithmic bytes of every stage over the step time
+    step_bytes = sum(a for (b, a, _) in work.values() if b == "hbm") + wc["raster_bytes"]
+    hbm_frac_step = step_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9)
 
     cpu = None
     if args.cpu_baseline:
@@ -160,31 +182,76 @@ def main():
         "n_candidates": r["n_cand"],
         "n_intersections": r["n_isect"],
         "n_leaves": r["n_leaves"],
-        "pairs_backward": int(q_b),
+        "pairs": {"examined": wc["q_f"], "included": wc["q_inc"], "backward": wc["q_b"], "sum_last": wc["sum_last"]},
         "kernel_ms_per_step": {k: round(v["total_ms"], 3) for k, v in ktimes.items()},
         "roofline": roofline,
+        "rooflines_all": rooflines,
+        "step_hbm": {"algorithmic_bytes": int(step_bytes), "frac_of_8TBps": round(hbm_frac_step, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     ctx.close()
 
 
-def count_backward_pairs(B, ctx, cam, params, budget):
-    """Sum over pixels of the list position after the last included entry
-    (the pairs the raster backward revisits), for the view as benchmarked."""
+def count_work(B, ctx, cam, params, budget):
+    """Work counters of the view as benchmarked (untimed): pairs examined by
+    the forward (q_f), pairs included (q_inc), pairs the backward revisits
+    (q_b = sum of last), intersections, candidates, leaves, tiles, pixels."""
     import torch
-    proj, _ = B.gs_project(ctx, cam, params)
+    proj, n_cand = B.gs_project(ctx, cam, params)
     leaves = B.gs_plan_leaves(ctx, cam, proj, budget)
-    total = 0
+    stats = torch.zeros(4, dtype=torch.int64, device=ctx.device)
+    n_isect = 0
+    tiles = 0
+    radix_elems = 4 * n_cand           # the per-view depth sort: 4 passes over the candidates
+    group_entries = 0
+    rects = B.gs_export(ctx, proj, B.PROJ_RECT).cpu().numpy()
     for L in leaves:
-        bins, _ = B.gs_bin_sort(ctx, cam, proj, L)
-        ras = B.gs_render_fwd(ctx, cam, proj, bins)
-        last = B.gs_export(ctx, ras, B.RASTER_LAST)
-        total += int(last.to(torch.int64).sum().item())
+        bins, ni = B.gs_bin_sort(ctx, cam, proj, L)
+        n_isect += ni
+        t_l = (L["tx1"] - L["tx0"]) * (L["ty1"] - L["ty0"])
+        tiles += t_l
+        radix_elems += ni * ((max(1, (t_l - 1).bit_length()) + 7) // 8)
+        group_entries += int(((rects[:, 0] < L["tx1"]) & (rects[:, 2] > L["tx0"]) &
+                               (rects[:, 1] < L["ty1"]) & (rects[:, 3] > L["ty0"])).sum())
+        ras = B.gs_render_fwd(ctx, cam, proj, bins, stats=stats)
         B.gs_release(ctx, ras)
         B.gs_release(ctx, bins)
     B.gs_release(ctx, proj)
-    return total
+    q = stats.cpu().tolist()
+    P = cam.width * cam.height
+    # raster state traffic: fwd writes T_final, last, dL/dout (20 B/px) and
+    # reads the target (12 B/px); bwd reads them back (20 B/px)
+    return dict(q_f=int(q[0]), q_inc=int(q[1]), q_b=int(q[3]), sum_last=int(q[2]), n_isect=int(n_isect),
+                n_cand=int(n_cand),
+                n_leaves=len(leaves), tiles=int(tiles), pixels=P, raster_bytes=52 * P,
+                radix_elems=int(radix_elems), group_entries=int(group_entries))
+
+
+def kernel_work(wc, sc):
+    """Algorithmic work per step of each timed kernel: (bound, amount, description).
+    alu: f32 VALU lane operations; hbm: bytes that must cross HBM."""
+    K = (sc.sh_degree + 1) ** 2
+    F = 11 + 3 * K
+    N, Nc, I, T, L = sc.n, wc["n_cand"], wc["n_isect"], wc["tiles"], wc["n_leaves"]
+    qf, qi, qb = wc["q_f"], wc["q_inc"], wc["q_b"]
+    return {
+        "raster_fwd": ("alu", OPS_EXAMINED * (qf - qi) + OPS_INCLUDED_FWD * qi,
+                       f"{OPS_EXAMINED} ops x examined-only pairs + {OPS_INCLUDED_FWD} x included pairs"),
+        "raster_bwd": ("alu", OPS_EXAMINED * (qb - qi) + OPS_INCLUDED_BWD * qi,
+                       f"{OPS_EXAMINED} ops x revisited-only pairs + {OPS_INCLUDED_BWD} x included pairs"),
+        "radix": ("hbm", 20 * wc["radix_elems"], "per pass and element: read the key twice, the value once, "
+                                                   "write key and value (20 B)"),
+        "emit": ("hbm", 8 * I + 24 * wc["group_entries"], "write 8 B (tile, slot) per intersection; read list, "
+                                                          "rectangle, offset per candidate visit"),
+        "bin_count": ("hbm", 24 * wc["group_entries"], "read list entry and rectangle, write the count"),
+        "seg_offsets": ("hbm", 4 * I + 8 * T, "read sorted tile keys, write tile offsets"),
+        "rect_diff": ("hbm", 16 * Nc + 4 * T, "read rects, touch the count grid"),
+        "project_flags": ("hbm", 40 * N, "read mean, log-scale, quaternion"),
+        "project_write": ("hbm", N * (40 + 4 + 12 * K + 8) + Nc * 68, "read parameters, write compact state"),
+        "project_bwd": ("hbm", Nc * (36 + 48 + 40 + 4 + 12 * K + 4 * F + 4), "read 2D grads, state, params; write 3D grads"),
+        "adam": ("hbm", 24 * N * F + 4 * F * Nc + 4 * N, "read/write params, m, v; read compact grads"),
+    }
 
 
 def cpu_baseline(w, window):

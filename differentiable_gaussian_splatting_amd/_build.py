@@ -10,8 +10,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgsmi.so")
-SOURCES = ["gs_api.cpp", "scan.hip", "project.hip", "binning.hip", "raster.hip", "planner.hip", "loss.hip",
-           "adam.hip"]
+SOURCES = ["gs_api.cpp", "scan.hip", "radix.hip", "project.hip", "binning.hip", "raster.hip", "planner.hip",
+           "loss.hip", "adam.hip"]
 HEADERS = ["gs_device.h", "gs_internal.h"]
 
 # Float discipline of the forward path: no contraction of a*b+c into fma (only

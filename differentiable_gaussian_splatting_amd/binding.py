@@ -125,7 +125,7 @@ def load(path: str = LIB_PATH):
         "gs_project": (st, [vp, P(gs_camera), P(gs_params), P(vp), P(i64)]),
         "gs_plan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, P(i32)]),
         "gs_bin_sort": (st, [vp, P(gs_camera), vp, gs_tile_rect, P(vp), P(i64)]),
-        "gs_render_fwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp, P(vp)]),
+        "gs_render_fwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp, vp, P(vp)]),
         "gs_render_bwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp]),
         "gs_project_bwd": (st, [vp, P(gs_camera), P(gs_params), vp, vp, vp]),
         "gs_loss_ssim": (st, [vp, i32, i32, vp, vp, C.c_float, vp, P(C.c_double), P(C.c_double)]),
@@ -291,10 +291,12 @@ def gs_bin_sort(ctx: Context, cam, proj, leaf):
     return h, int(n.value)
 
 
-def gs_render_fwd(ctx: Context, cam, proj, bins, target=None, loss_accum=None, image_out=None):
+def gs_render_fwd(ctx: Context, cam, proj, bins, target=None, loss_accum=None, image_out=None, stats=None):
+    """stats: optional int64 device tensor [4] accumulating (pairs examined,
+    pairs included, sum of last, pairs the backward revisits)."""
     h = C.c_void_p()
     ctx.check(ctx.lib.gs_render_fwd(ctx.handle, C.byref(camera_struct(cam)), proj, bins, _ptr(target),
-                                    _ptr(loss_accum), _ptr(image_out), C.byref(h)))
+                                    _ptr(loss_accum), _ptr(image_out), _ptr(stats), C.byref(h)))
     return h
 
 

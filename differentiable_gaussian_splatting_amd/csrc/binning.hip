@@ -1,213 +1,151 @@
-// binning.hip -- per-leaf tile-intersection counting, key emission and the
-// (tile, depth, slot) sort.
+// binning.hip -- tile-intersection counting, (tile, depth, slot) ordering of
+// one leaf's intersections, and the candidate orders they start from.
 //
 // BoundedGS page, "01": raster buffers grow with the overlaps of Gaussians
 // and image tiles.  Design (MI355X):
-//   1. counts per tile from a 2D difference array: four integer atomics per
-//      candidate rectangle, then a 2D inclusive prefix (O(N_c + T), exact);
-//   2. exclusive scan of the counts -> u64 tile offsets;
-//   3. emission: every (candidate, tile) pair is bucketed into its tile's
-//      segment through a per-tile atomic cursor, as the 64-bit composite
-//      (depth bits << 32 | slot); candidates whose rectangle covers many tiles
-//      are emitted by a whole wavefront so that one thread never carries a
-//      large rectangle alone;
-//   4. each tile's segment is sorted by the composite (depth, then slot --
-//      unique, so the result does not depend on the emission order): bitonic
-//      networks in LDS for segments that fit, chunk sorts plus merge-path
-//      merges in HBM for longer ones.
-// This replaces a global LSD radix sort over (tile << 32 | depth) keys (6-7
-// passes over all entries) with about two passes.
+//   - once per view the candidates are sorted by depth (stable LSD radix on
+//     the f32 depth bits over slots in ascending order), giving the order
+//     (depth, slot) that every tile list must follow;
+//   - a leaf's candidates are visited in that order; each writes one
+//     (leaf-local tile id, slot) pair per tile of its rectangle inside the
+//     leaf at an offset from an exclusive scan of the per-candidate tile
+//     counts (no atomics; a wavefront shares a wide rectangle so that the
+//     writes stay coalesced);
+//   - a stable radix sort on the tile id alone (ceil(log2 T_L) bits, two
+//     passes for most leaves) then yields each tile's list in (depth, slot)
+//     order, and tile offsets come from the key boundaries.
+// The per-tile counts of a whole grid (for the planner) come from a 2D
+// difference array: four integer atomics per rectangle and a 2D prefix; the
+// cells of the first row and column, which every rectangle clamped at the
+// image border hits, are aggregated in LDS first.
 #include "gs_device.h"
 #include "gs_internal.h"
 
 namespace {
 
-__global__ __launch_bounds__(256) void k_rect_diff(int64_t n, const int4* __restrict__ rect, int ltx0, int lty0,
-                                                   int ltx1, int lty1, int32_t* __restrict__ diff)
+constexpr int kBorderLds = 4096;
+
+__global__ __launch_bounds__(256) void k_rect_diff(int64_t n, const uint32_t* __restrict__ list,
+                                                   const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
+                                                   int lty1, int32_t* __restrict__ diff)
 {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= n) return;
-    const int4 r = rect[j];
+    __shared__ int32_t col0[kBorderLds];   // cells (y, 0)
+    __shared__ int32_t row0[kBorderLds];   // cells (0, x)
     const int TWL = ltx1 - ltx0, THL = lty1 - lty0;
-    const int x0 = max(r.x, ltx0) - ltx0, x1 = min(r.z, ltx1) - ltx0;
-    const int y0 = max(r.y, lty0) - lty0, y1 = min(r.w, lty1) - lty0;
-    if (x0 >= x1 || y0 >= y1) return;
-    atomicAdd(&diff[(int64_t)y0 * TWL + x0], 1);
-    if (x1 < TWL) atomicAdd(&diff[(int64_t)y0 * TWL + x1], -1);
-    if (y1 < THL) atomicAdd(&diff[(int64_t)y1 * TWL + x0], -1);
-    if (x1 < TWL && y1 < THL) atomicAdd(&diff[(int64_t)y1 * TWL + x1], 1);
+    const bool lds = TWL <= kBorderLds && THL <= kBorderLds;
+    if (lds) {
+        for (int k = threadIdx.x; k < THL; k += blockDim.x) col0[k] = 0;
+        for (int k = threadIdx.x; k < TWL; k += blockDim.x) row0[k] = 0;
+        __syncthreads();
+    }
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < n) {
+        const int64_t j = list ? (int64_t)list[k] : k;
+        const int4 r = rect[j];
+        const int x0 = max(r.x, ltx0) - ltx0, x1 = min(r.z, ltx1) - ltx0;
+        const int y0 = max(r.y, lty0) - lty0, y1 = min(r.w, lty1) - lty0;
+        if (x0 < x1 && y0 < y1) {
+            auto add = [&](int y, int x, int v) {
+                if (lds && x == 0) atomicAdd(&col0[y], v);
+                else if (lds && y == 0) atomicAdd(&row0[x], v);
+                else atomicAdd(&diff[(int64_t)y * TWL + x], v);
+            };
+            add(y0, x0, 1);
+            if (x1 < TWL) add(y0, x1, -1);
+            if (y1 < THL) add(y1, x0, -1);
+            if (x1 < TWL && y1 < THL) add(y1, x1, 1);
+        }
+    }
+    if (lds) {
+        __syncthreads();
+        for (int q = threadIdx.x; q < THL; q += blockDim.x)
+            if (col0[q]) atomicAdd(&diff[(int64_t)q * TWL], col0[q]);
+        for (int q = threadIdx.x; q < TWL; q += blockDim.x)
+            if (row0[q]) atomicAdd(&diff[q], row0[q]);
+    }
 }
 
-constexpr int kWideRect = 32;   // rectangles with more tiles are emitted by a whole wave
-
-__device__ __forceinline__ void emit_one(int64_t t, uint64_t comp, const uint64_t* __restrict__ offsets,
-                                         uint32_t* __restrict__ cursor, uint64_t* __restrict__ out)
+// tiles of each listed candidate's rectangle inside the leaf
+__global__ __launch_bounds__(256) void k_count_tiles(int64_t n, const uint32_t* __restrict__ list,
+                                                     const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
+                                                     int lty1, uint32_t* __restrict__ cnt)
 {
-    const uint32_t k = atomicAdd(&cursor[t], 1u);
-    out[offsets[t] + k] = comp;
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const int4 r = rect[list[k]];
+    const int w = min(r.z, ltx1) - max(r.x, ltx0), h = min(r.w, lty1) - max(r.y, lty0);
+    cnt[k] = (w > 0 && h > 0) ? (uint32_t)(w * h) : 0u;
 }
 
-__global__ __launch_bounds__(256) void k_emit(int64_t n, const int4* __restrict__ rect,
-                                              const float4* __restrict__ g2, int ltx0, int lty0, int ltx1,
-                                              int lty1, const uint64_t* __restrict__ offsets,
-                                              uint32_t* __restrict__ cursor, uint64_t* __restrict__ out)
+constexpr int kWideRect = 32;   // rectangles with more tiles are written by a whole wave
+
+// (leaf-local tile, slot) pairs of the listed candidates, in list order and
+// row-major tile order, at eoff[k]
+__global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
+                                                    const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
+                                                    int lty1, const uint64_t* __restrict__ eoff,
+                                                    uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
 {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int lane = gsd::lane_id();
     const int TWL = ltx1 - ltx0;
-    int x0 = 0, x1 = 0, y0 = 0, y1 = 0;
-    uint64_t comp = 0;
-    if (j < n) {
+    int x0 = 0, y0 = 0, w = 0, h = 0;
+    uint32_t j = 0;
+    uint64_t o = 0;
+    if (k < n) {
+        j = list[k];
         const int4 r = rect[j];
-        x0 = max(r.x, ltx0) - ltx0; x1 = min(r.z, ltx1) - ltx0;
-        y0 = max(r.y, lty0) - lty0; y1 = min(r.w, lty1) - lty0;
-        if (x0 >= x1 || y0 >= y1) { x0 = x1 = y0 = y1 = 0; }
-        comp = ((uint64_t)__builtin_bit_cast(uint32_t, g2[j].y) << 32) | (uint64_t)(uint32_t)j;
+        x0 = max(r.x, ltx0) - ltx0;
+        y0 = max(r.y, lty0) - lty0;
+        w = min(r.z, ltx1) - ltx0 - x0;
+        h = min(r.w, lty1) - lty0 - y0;
+        if (w <= 0 || h <= 0) w = h = 0;
+        o = eoff[k];
     }
-    const int w = x1 - x0, h = y1 - y0;
     const bool wide = w * h > kWideRect;
     if (!wide) {
-        for (int ty = y0; ty < y1; ++ty)
-            for (int tx = x0; tx < x1; ++tx) emit_one((int64_t)ty * TWL + tx, comp, offsets, cursor, out);
+        for (int ty = 0; ty < h; ++ty)
+            for (int tx = 0; tx < w; ++tx) {
+                keys[o] = (uint32_t)((y0 + ty) * TWL + x0 + tx);
+                vals[o] = j;
+                ++o;
+            }
     }
-    // wide rectangles: the wave takes them one at a time, lanes stride the tiles
     uint64_t pending = gsd::ballot(wide);
     while (pending) {
         const int src = __builtin_ctzll(pending);
         pending &= pending - 1;
         const int sx0 = __shfl(x0, src, 64), sy0 = __shfl(y0, src, 64);
         const int sw = __shfl(w, src, 64), sh = __shfl(h, src, 64);
-        const uint64_t scomp = __shfl(comp, src, 64);
+        const uint32_t sj = (uint32_t)__shfl((int)j, src, 64);
+        const uint64_t so = __shfl(o, src, 64);
         const int tot = sw * sh;
-        for (int k = lane; k < tot; k += 64) {
-            const int ty = sy0 + k / sw, tx = sx0 + k % sw;
-            emit_one((int64_t)ty * TWL + tx, scomp, offsets, cursor, out);
+        for (int q = lane; q < tot; q += 64) {
+            keys[so + q] = (uint32_t)((sy0 + q / sw) * TWL + sx0 + q % sw);
+            vals[so + q] = sj;
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// per-tile segment sort
-
-template <int CAP>
-__device__ __forceinline__ void bitonic_lds(uint64_t* s, int n2)
+// offsets[s] = first position whose key is >= s, for s in [0, n_seg]; keys
+// sorted ascending, all < n_seg
+__global__ __launch_bounds__(256) void k_seg_offsets(const uint32_t* __restrict__ keys, int64_t n, int64_t n_seg,
+                                                     uint64_t* __restrict__ offsets)
 {
-    for (int k = 2; k <= n2; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = threadIdx.x; i < n2; i += blockDim.x) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const uint64_t a = s[i], b = s[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) {
-                        s[i] = b;
-                        s[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k > n) return;
+    const int64_t prev = k == 0 ? -1 : (int64_t)keys[k - 1];
+    const int64_t cur = k == n ? n_seg : (int64_t)keys[k];
+    for (int64_t s = prev + 1; s <= cur; ++s) offsets[s] = (uint64_t)k;
 }
 
-__device__ __forceinline__ int next_pow2(int v)
+__global__ __launch_bounds__(256) void k_depth_pairs(int64_t n, const float4* __restrict__ g2,
+                                                     uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
 {
-    int p = 1;
-    while (p < v) p <<= 1;
-    return p;
-}
-
-// segments with lo < len <= CAP: one block, bitonic sort in LDS
-template <int CAP>
-__global__ __launch_bounds__(1024) void k_sort_lds(int64_t n_tiles, const uint64_t* __restrict__ offsets, const uint64_t* __restrict__ comp,
-                           uint32_t* __restrict__ values, int lo)
-{
-    __shared__ uint64_t s[CAP];
-    const int64_t t = blockIdx.x;
-    if (t >= n_tiles) return;
-    const uint64_t start = offsets[t];
-    const int64_t len = (int64_t)(offsets[t + 1] - start);
-    if (len <= lo || len > CAP) return;
-    if (len == 1) {
-        if (threadIdx.x == 0) values[start] = (uint32_t)comp[start];
-        return;
-    }
-    const int n2 = next_pow2((int)len);
-    for (int i = threadIdx.x; i < n2; i += blockDim.x) s[i] = i < len ? comp[start + i] : ~0ull;
-    __syncthreads();
-    bitonic_lds<CAP>(s, n2);
-    for (int i = threadIdx.x; i < len; i += blockDim.x) values[start + i] = (uint32_t)s[i];
-}
-
-constexpr int kChunk = 8192;
-
-// segments longer than kChunk: one block sorts kChunk chunks in LDS, then
-// merges runs pairwise (merge path) between comp and scratch
-__global__ __launch_bounds__(1024) void k_sort_big(int64_t n_tiles, const uint64_t* __restrict__ offsets,
-                                                   uint64_t* __restrict__ comp, uint64_t* __restrict__ scratch,
-                                                   uint32_t* __restrict__ values)
-{
-    __shared__ uint64_t s[kChunk];
-    const int64_t t = blockIdx.x;
-    if (t >= n_tiles) return;
-    const uint64_t start = offsets[t];
-    const int64_t len = (int64_t)(offsets[t + 1] - start);
-    if (len <= kChunk) return;
-    uint64_t* src = comp + start;
-    uint64_t* dst = scratch + start;
-    for (int64_t c0 = 0; c0 < len; c0 += kChunk) {
-        const int m = (int)min<int64_t>(kChunk, len - c0);
-        const int n2 = next_pow2(m);
-        for (int i = threadIdx.x; i < n2; i += blockDim.x) s[i] = i < m ? src[c0 + i] : ~0ull;
-        __syncthreads();
-        bitonic_lds<kChunk>(s, n2);
-        for (int i = threadIdx.x; i < m; i += blockDim.x) src[c0 + i] = s[i];
-        __syncthreads();
-    }
-    for (int64_t w = kChunk; w < len; w *= 2) {
-        for (int64_t p0 = 0; p0 < len; p0 += 2 * w) {
-            const uint64_t* A = src + p0;
-            const int64_t la = min<int64_t>(w, len - p0);
-            const uint64_t* B = A + la;
-            const int64_t lb = min<int64_t>(w, len - p0 - la);
-            const int64_t m = la + lb;
-            const int64_t per = (m + blockDim.x - 1) / blockDim.x;
-            const int64_t k0 = (int64_t)threadIdx.x * per;
-            const int64_t k1 = min<int64_t>(m, k0 + per);
-            if (k0 < m) {
-                int64_t lo = max<int64_t>(0, k0 - lb), hi = min<int64_t>(k0, la);
-                while (lo < hi) {
-                    const int64_t mid = (lo + hi) >> 1;
-                    if (A[mid] < B[k0 - 1 - mid]) lo = mid + 1;
-                    else hi = mid;
-                }
-                int64_t i = lo, j = k0 - lo;
-                for (int64_t k = k0; k < k1; ++k) {
-                    const bool takeA = i < la && (j >= lb || A[i] < B[j]);
-                    dst[p0 + k] = takeA ? A[i++] : B[j++];
-                }
-            }
-        }
-        __syncthreads();
-        uint64_t* tmp = src;
-        src = dst;
-        dst = tmp;
-    }
-    for (int64_t i = threadIdx.x; i < len; i += blockDim.x) values[start + i] = (uint32_t)src[i];
-}
-
-__global__ void k_max_segment(const uint64_t* __restrict__ offsets, int64_t n_tiles, uint64_t* __restrict__ out)
-{
-    uint64_t m = 0;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n_tiles; t += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t len = offsets[t + 1] - offsets[t];
-        m = len > m ? len : m;
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t v = __shfl_xor(m, o, 64);
-        m = v > m ? v : m;
-    }
-    if (gsd::lane_id() == 0) atomicMax((unsigned long long*)out, (unsigned long long)m);
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n) return;
+    keys[j] = __builtin_bit_cast(uint32_t, g2[j].y);   // depth > 0: the bits order like the values
+    vals[j] = (uint32_t)j;
 }
 
 __global__ void k_export_keys(int64_t n_tiles, int ltx0, int lty0, int TWL, int TW, const uint64_t* __restrict__ offsets,
@@ -223,52 +161,64 @@ __global__ void k_export_keys(int64_t n_tiles, int ltx0, int lty0, int TWL, int 
 
 }  // namespace
 
-gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, int32_t* diff)
+int bits_for(int64_t n_keys)
 {
-    if (proj->n_cand > 0) {
+    int b = 0;
+    while (b < 40 && (1ll << b) < n_keys) ++b;
+    return b;
+}
+
+gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+                           int64_t n_list, int32_t* diff)
+{
+    const int64_t n = list ? n_list : proj->n_cand;
+    if (n > 0) {
         GsTimerScope ts(ctx, "rect_diff");
-        hipLaunchKernelGGL(k_rect_diff, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream,
-                           proj->n_cand, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, diff);
+        hipLaunchKernelGGL(k_rect_diff, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, list,
+                           proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, diff);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }
 
-gs_status launch_emit(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* offsets,
-                      uint32_t* cursor, uint64_t* comp)
+gs_status launch_count_tiles(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+                             int64_t n_list, uint32_t* cnt)
 {
-    if (proj->n_cand > 0) {
+    if (n_list > 0) {
+        GsTimerScope ts(ctx, "bin_count");
+        hipLaunchKernelGGL(k_count_tiles, dim3((unsigned)ceil_div(n_list, 256)), dim3(256), 0, ctx->stream, n_list,
+                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, cnt);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_emit_pairs(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+                            int64_t n_list, const uint64_t* eoff, uint32_t* keys, uint32_t* vals)
+{
+    if (n_list > 0) {
         GsTimerScope ts(ctx, "emit");
-        hipLaunchKernelGGL(k_emit, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream,
-                           proj->n_cand, proj->rect, proj->g2, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, offsets,
-                           cursor, comp);
+        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div(n_list, 256)), dim3(256), 0, ctx->stream, n_list,
+                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, eoff, keys, vals);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }
 
-gs_status launch_sort_tiles(gs_ctx* ctx, int64_t n_tiles, const uint64_t* offsets, uint64_t* comp,
-                            uint64_t* scratch, uint32_t* values, int64_t max_len)
+gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets)
 {
-    if (n_tiles <= 0 || max_len <= 0) return GS_OK;
-    GsTimerScope ts(ctx, "sort_tiles");
-    const dim3 grid((unsigned)n_tiles);
-    hipLaunchKernelGGL(k_sort_lds<256>, grid, dim3(64), 0, ctx->stream, n_tiles, offsets, comp, values, 0);
-    if (max_len > 256)
-        hipLaunchKernelGGL(k_sort_lds<2048>, grid, dim3(256), 0, ctx->stream, n_tiles, offsets, comp, values, 256);
-    if (max_len > 2048)
-        hipLaunchKernelGGL(k_sort_lds<8192>, grid, dim3(1024), 0, ctx->stream, n_tiles, offsets, comp, values, 2048);
-    if (max_len > kChunk)
-        hipLaunchKernelGGL(k_sort_big, grid, dim3(1024), 0, ctx->stream, n_tiles, offsets, comp, scratch, values);
+    GsTimerScope ts(ctx, "seg_offsets");
+    hipLaunchKernelGGL(k_seg_offsets, dim3((unsigned)ceil_div(n + 1, 256)), dim3(256), 0, ctx->stream, sorted_keys,
+                       n, n_seg, offsets);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }
 
-gs_status launch_max_segment(gs_ctx* ctx, const uint64_t* offsets, int64_t n_tiles, uint64_t* out)
+gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals)
 {
-    GS_HIP(ctx, hipMemsetAsync(out, 0, sizeof(uint64_t), ctx->stream));
-    const int64_t blocks = std::min<int64_t>(std::max<int64_t>(ceil_div(n_tiles, 256), 1), 1024);
-    hipLaunchKernelGGL(k_max_segment, dim3((unsigned)blocks), dim3(256), 0, ctx->stream, offsets, n_tiles, out);
+    if (proj->n_cand > 0)
+        hipLaunchKernelGGL(k_depth_pairs, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream,
+                           proj->n_cand, proj->g2, keys, vals);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

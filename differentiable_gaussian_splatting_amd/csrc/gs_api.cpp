@@ -136,6 +136,7 @@ static bool handle_ok(const gs_ctx* ctx, const void* h, uint32_t magic)
 static void destroy_handle(gs_ctx* ctx, GsHandle* h)
 {
     gs_free_all(ctx, &h->allocs);
+    if (h->magic == kMagicProj) gs_free_all(ctx, &static_cast<gs_proj*>(h)->plan_allocs);
     const uint32_t magic = h->magic;
     h->magic = 0;
     // delete through the concrete type
@@ -177,6 +178,86 @@ static gs_status check_params(gs_ctx* ctx, const gs_params* p)
     if (p->n > 0 && (!p->means || !p->log_scales || !p->quats || !p->opacity_logits || !p->sh))
         return gs_fail(ctx, GS_ERR_INVALID_ARG, "a parameter pointer is NULL");
     return GS_OK;
+}
+
+// leaf -> candidate groups of a plan (leaves on the device), attached to
+// proj; every group keeps the candidates' (depth, slot) order
+static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ldev, int32_t nl)
+{
+    gs_free_all(ctx, &proj->plan_allocs);
+    proj->plan.clear();
+    proj->plan_off.clear();
+    proj->plan_cands = nullptr;
+    const int64_t T = (int64_t)proj->TW * proj->TH;
+    const int64_t nc = proj->n_cand;
+    std::vector<GsAlloc> tmp;
+    gs_status st = GS_OK;
+    std::vector<gs_leaf> plan(nl);
+    std::vector<uint64_t> hoff(nl + 1, 0);
+    uint64_t G = 0;
+    bool second = false;
+    uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
+    uint64_t* segoff = nullptr;
+    hipError_t e;
+    int32_t* lot = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * T, GS_MEM_SCRATCH, &tmp);
+    uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(nc, 1), GS_MEM_SCRATCH, &tmp);
+    uint64_t* goff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nc + 1), GS_MEM_SCRATCH, &tmp);
+    if (!lot || !cnt || !goff) { st = GS_ERR_OOM; goto out; }
+    if ((st = launch_leaf_map(ctx, ldev, nl, proj->TW, lot)) != GS_OK) goto out;
+    if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
+    if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
+    if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;
+    k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
+    k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
+    v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
+    v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
+    segoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
+    if (!k0 || !k1 || !v0 || !v1 || !segoff) { st = GS_ERR_OOM; goto out; }
+    if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, goff, k0, v0)) != GS_OK) goto out;
+    if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
+    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, segoff)) != GS_OK) goto out;
+    e = hipMemcpyAsync(hoff.data(), segoff, sizeof(uint64_t) * (nl + 1), hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(plan.data(), ldev, sizeof(gs_leaf) * nl, hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
+    gs_free_one(ctx, &proj->plan_allocs, second ? v0 : v1);
+    proj->plan_cands = second ? v1 : v0;
+    proj->plan.swap(plan);
+    proj->plan_off.swap(hoff);
+out:
+    gs_free_all(ctx, &tmp);
+    if (st != GS_OK) {
+        gs_free_all(ctx, &proj->plan_allocs);
+        proj->plan_cands = nullptr;
+        proj->plan.clear();
+        proj->plan_off.clear();
+    }
+    return st;
+}
+
+// The candidate group of a planned leaf, or (nullptr, 0) when the leaf is
+// not part of the plan.  *isect gets the leaf's intersection count when the
+// plan's estimate determines it (est = bI I + bP P + bT T + b0, bI > 0), else -1.
+static const uint32_t* plan_group(const gs_proj* proj, gs_tile_rect leaf, int64_t* n, int64_t* isect)
+{
+    *n = 0;
+    *isect = -1;
+    if (!proj->plan_cands) return nullptr;
+    for (size_t k = 0; k < proj->plan.size(); ++k) {
+        const gs_leaf& L = proj->plan[k];
+        if (L.tx0 == leaf.tx0 && L.ty0 == leaf.ty0 && L.tx1 == leaf.tx1 && L.ty1 == leaf.ty1) {
+            *n = (int64_t)(proj->plan_off[k + 1] - proj->plan_off[k]);
+            const gs_cost_model& c = proj->plan_cost;
+            const uint64_t P = (uint64_t)(std::min(L.tx1 * 16, proj->W) - L.tx0 * 16) *
+                               (uint64_t)(std::min(L.ty1 * 16, proj->H) - L.ty0 * 16);
+            const uint64_t T = (uint64_t)(L.tx1 - L.tx0) * (uint64_t)(L.ty1 - L.ty0);
+            const uint64_t rest = c.b_pixel * P + c.b_tile * T + c.b_const;
+            if (c.b_isect > 0 && L.est_bytes >= rest && (L.est_bytes - rest) % c.b_isect == 0)
+                *isect = (int64_t)((L.est_bytes - rest) / c.b_isect);
+            return proj->plan_cands + proj->plan_off[k];
+        }
+    }
+    return nullptr;
 }
 
 extern "C" {
@@ -339,6 +420,21 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
         if (!p->ids || !p->rect || !p->g0 || !p->g1 || !p->g2 || !p->slot_of) { st = GS_ERR_OOM; goto fail; }
     }
     if ((st = launch_project_write(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
+    {
+        // candidates in (depth, slot) order: stable radix sort of the depth
+        // bits over slots in ascending order
+        const int64_t nc = std::max<int64_t>(cnt, 1);
+        uint32_t* k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &tmp);
+        uint32_t* k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &tmp);
+        uint32_t* v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
+        uint32_t* v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
+        bool second = false;
+        if (!k0 || !k1 || !v0 || !v1) { st = GS_ERR_OOM; goto fail; }
+        if ((st = launch_depth_pairs(ctx, p, k0, v0)) != GS_OK) goto fail;
+        if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)cnt, 32, &second)) != GS_OK) goto fail;
+        gs_free_one(ctx, &p->allocs, second ? v0 : v1);
+        p->order = second ? v1 : v0;
+    }
     gs_free_all(ctx, &tmp);
     *out = p;
     *n_cand = (int64_t)cnt;
@@ -387,6 +483,12 @@ gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj,
         if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
         if (e != hipSuccess) st = gs_fail(ctx, GS_ERR_DEVICE, "leaf copy failed: %s", hipGetErrorString(e));
     }
+    // Attach the leaf -> candidate groups of this plan to the projection, so
+    // that gs_bin_sort of a planned leaf visits only the candidates meeting it.
+    if (st == GS_OK && hv[0] > 0 && hv[0] <= cap) {
+        st = build_plan_groups(ctx, const_cast<gs_proj*>(proj), ldev, hv[0]);
+        const_cast<gs_proj*>(proj)->plan_cost = cm;
+    }
     gs_free_all(ctx, &tmp);
     if (st != GS_OK) return st;
     *n_leaves = hv[0];
@@ -417,39 +519,48 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     b->THL = leaf.ty1 - leaf.ty0;
     b->n_tiles = (int64_t)b->TWL * b->THL;
     std::vector<GsAlloc> tmp;
-    uint64_t hv[2] = {0, 0};
-    int32_t* diff = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * b->n_tiles, GS_MEM_RASTER, &tmp);
-    uint64_t* small = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * 2, GS_MEM_SCRATCH, &tmp);
-    b->offsets = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (b->n_tiles + 1), GS_MEM_RASTER, &b->allocs);
-    uint32_t* cursor = nullptr;
-    uint64_t* comp = nullptr;
-    uint64_t* scratch = nullptr;
-    if (!diff || !small || !b->offsets) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_fill_u32(ctx, (uint32_t*)diff, 0u, b->n_tiles)) != GS_OK) goto fail;
-    if ((st = launch_rect_diff(ctx, proj, leaf, diff)) != GS_OK) goto fail;
-    if ((st = launch_prefix2d_i32(ctx, diff, b->THL, b->TWL)) != GS_OK) goto fail;
-    if ((st = launch_scan_u32_to_u64(ctx, (const uint32_t*)diff, b->offsets, b->n_tiles)) != GS_OK) goto fail;
-    if ((st = launch_max_segment(ctx, b->offsets, b->n_tiles, small + 1)) != GS_OK) goto fail;
-    if (hipMemcpyAsync(small, b->offsets + b->n_tiles, sizeof(uint64_t), hipMemcpyDeviceToDevice, ctx->stream) !=
-        hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "copy failed"); goto fail; }
-    if ((st = readback(ctx, small, sizeof(hv), hv)) != GS_OK) goto fail;
-    gs_free_one(ctx, &tmp, diff);
-    b->n_isect = (int64_t)hv[0];
-    {
-        const int64_t ni = std::max<int64_t>(b->n_isect, 1);
-        cursor = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * b->n_tiles, GS_MEM_RASTER, &tmp);
-        comp = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * ni, GS_MEM_RASTER, &tmp);
-        b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &b->allocs);
-        if (!cursor || !comp || !b->values) { st = GS_ERR_OOM; goto fail; }
-        if (hv[1] > 8192) {
-            scratch = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * ni, GS_MEM_RASTER, &tmp);
-            if (!scratch) { st = GS_ERR_OOM; goto fail; }
-        }
+    uint64_t I = 0;
+    bool second = false;
+    int64_t n_list = 0, known = -1;
+    const uint32_t* list = plan_group(proj, leaf, &n_list, &known);
+    if (!list) {               // not a planned leaf: visit every candidate
+        list = proj->order;
+        n_list = proj->n_cand;
     }
-    if ((st = launch_fill_u32(ctx, cursor, 0u, b->n_tiles)) != GS_OK) goto fail;
-    if ((st = launch_emit(ctx, proj, leaf, b->offsets, cursor, comp)) != GS_OK) goto fail;
-    if ((st = launch_sort_tiles(ctx, b->n_tiles, b->offsets, comp, scratch, b->values, (int64_t)hv[1])) != GS_OK)
+    uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
+    uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n_list, 1), GS_MEM_RASTER, &tmp);
+    uint64_t* eoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (n_list + 1), GS_MEM_RASTER, &tmp);
+    if (!cnt || !eoff) { st = GS_ERR_OOM; goto fail; }
+    if ((st = launch_count_tiles(ctx, proj, leaf, list, n_list, cnt)) != GS_OK) goto fail;
+    if ((st = launch_scan_u32_to_u64(ctx, cnt, eoff, n_list)) != GS_OK) goto fail;
+    if (known >= 0) {
+        I = (uint64_t)known;    // from the plan's summed-area table: no read-back
+    } else if ((st = readback(ctx, eoff + n_list, sizeof(uint64_t), &I)) != GS_OK) {
         goto fail;
+    }
+    if (I >= (1ull << 32)) { st = gs_fail(ctx, GS_ERR_OVERFLOW, "leaf has %llu >= 2^32 intersections", (unsigned long long)I); goto fail; }
+    b->n_isect = (int64_t)I;
+    {
+        const uint64_t ni = std::max<uint64_t>(I, 1);
+        k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &tmp);
+        v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &b->allocs);
+        if (!k0 || !v0) { st = GS_ERR_OOM; goto fail; }
+    }
+    if ((st = launch_emit_pairs(ctx, proj, leaf, list, n_list, eoff, k0, v0)) != GS_OK) goto fail;
+    gs_free_one(ctx, &tmp, cnt);
+    gs_free_one(ctx, &tmp, eoff);
+    {
+        const uint64_t ni = std::max<uint64_t>(I, 1);
+        k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &tmp);
+        v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &b->allocs);
+        if (!k1 || !v1) { st = GS_ERR_OOM; goto fail; }
+    }
+    if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)I, bits_for(b->n_tiles), &second)) != GS_OK) goto fail;
+    b->offsets = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (b->n_tiles + 1), GS_MEM_RASTER, &b->allocs);
+    if (!b->offsets) { st = GS_ERR_OOM; goto fail; }
+    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)I, b->n_tiles, b->offsets)) != GS_OK) goto fail;
+    gs_free_one(ctx, &b->allocs, second ? v0 : v1);
+    b->values = second ? v1 : v0;
     gs_free_all(ctx, &tmp);
     *out = b;
     *n_isect = b->n_isect;
@@ -464,7 +575,8 @@ fail:
 // raster
 
 gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                        const float* target, double* loss_accum, float* image_out, gs_raster** out)
+                        const float* target, double* loss_accum, float* image_out, uint64_t* stats,
+                        gs_raster** out)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     gs_status st;
@@ -493,7 +605,7 @@ gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, 
         destroy_handle(ctx, r);
         return GS_ERR_OOM;
     }
-    if ((st = launch_raster_fwd(ctx, cam, proj, bins, r, target, image_out, loss_accum)) != GS_OK) {
+    if ((st = launch_raster_fwd(ctx, cam, proj, bins, r, target, image_out, loss_accum, stats)) != GS_OK) {
         destroy_handle(ctx, r);
         return st;
     }
@@ -724,10 +836,10 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
         isect_total += ni;
         if (opts->loss_kind == 0) {
-            st = gs_render_fwd(ctx, cam, proj, bins, target, loss_dev, image, &ras);
+            st = gs_render_fwd(ctx, cam, proj, bins, target, loss_dev, image, nullptr, &ras);
             if (st == GS_OK) st = gs_render_bwd(ctx, cam, proj, bins, ras, nullptr, grad2d);
         } else {
-            st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, &ras);
+            st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, nullptr, &ras);
             if (st == GS_OK)
                 st = gs_loss_ssim(ctx, cam->width, cam->height, image, target, opts->ssim_lambda, dl_dimage, &loss,
                                   nullptr);

@@ -57,6 +57,14 @@ struct gs_proj : GsHandle {
     float4* g1 = nullptr;         // [n_cand] -C/2, opacity, r, g
     float4* g2 = nullptr;         // [n_cand] b, depth, radius, flags (bits)
     int32_t* slot_of = nullptr;   // [n] slot or -1
+    uint32_t* order = nullptr;    // [n_cand] slots sorted by (depth, slot)
+    // leaf plan of the view (set by gs_plan_leaves): the candidates whose
+    // rectangle meets each leaf, so that binning a leaf visits only those
+    std::vector<gs_leaf> plan;
+    std::vector<uint64_t> plan_off;   // host copy of the group offsets [plan.size() + 1]
+    uint32_t* plan_cands = nullptr;   // device [plan_off.back()] candidate slots, depth order per group
+    std::vector<GsAlloc> plan_allocs;
+    gs_cost_model plan_cost{};        // cost model the plan was made with
 };
 
 struct gs_bins : GsHandle {
@@ -120,18 +128,26 @@ gs_status launch_export_proj(gs_ctx* ctx, const gs_proj* proj, int field, void* 
 gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
 
 // binning.hip
-gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, int32_t* diff);
-gs_status launch_emit(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* offsets,
-                      uint32_t* cursor, uint64_t* comp);
-gs_status launch_sort_tiles(gs_ctx* ctx, int64_t n_tiles, const uint64_t* offsets, uint64_t* comp,
-                            uint64_t* scratch, uint32_t* values, int64_t max_len);
+// list: candidate slots to visit (NULL: all n_cand), n_list entries
+gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+                           int64_t n_list, int32_t* diff);
+gs_status launch_count_tiles(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+                             int64_t n_list, uint32_t* cnt);
+gs_status launch_emit_pairs(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+                            int64_t n_list, const uint64_t* eoff, uint32_t* keys, uint32_t* vals);
+gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets);
+gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
 gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);
-gs_status launch_max_segment(gs_ctx* ctx, const uint64_t* offsets, int64_t n_tiles, uint64_t* out);
-gs_status launch_big_segment_total(gs_ctx* ctx, const uint64_t* offsets, int64_t n_tiles, uint64_t* out);
+int bits_for(int64_t n_keys);
+
+// radix.hip: stable sort of (u32 key, u32 value) pairs on the low key_bits bits
+gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n,
+                            int key_bits, bool* in_second);
 
 // raster.hip
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                            gs_raster* r, const float* target, float* image_out, double* loss_accum);
+                            gs_raster* r, const float* target, float* image_out, double* loss_accum,
+                            uint64_t* stats);
 gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
                             const gs_raster* r, const float* dl_dimage, float* grad2d);
 
@@ -139,6 +155,11 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
 gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, int32_t* diff, uint64_t budget,
                       const gs_cost_model* cost, gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev,
                       int32_t* overflow_dev);
+
+// leaf -> candidate groups (planner.hip)
+gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot);
+gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
+                            const int32_t* lot, uint32_t* cnt, const uint64_t* off, uint32_t* keys, uint32_t* vals);
 
 // loss.hip
 gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,

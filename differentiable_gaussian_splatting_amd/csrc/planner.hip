@@ -157,7 +157,7 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, int32_t* 
     gs_status st = launch_fill_u32(ctx, (uint32_t*)diff, 0u, T);
     if (st != GS_OK) return st;
     gs_tile_rect all{0, 0, TW, TH};
-    if ((st = launch_rect_diff(ctx, proj, all, diff)) != GS_OK) return st;
+    if ((st = launch_rect_diff(ctx, proj, all, nullptr, 0, diff)) != GS_OK) return st;
     if ((st = launch_prefix2d_i32(ctx, diff, TH, TW)) != GS_OK) return st;
     const int64_t S = (int64_t)(TW + 1) * (TH + 1);
     hipLaunchKernelGGL(k_counts_to_sat, dim3((unsigned)ceil_div(S, 256)), dim3(256), 0, ctx->stream, diff, TW, TH, sat);
@@ -181,6 +181,95 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, int32_t* 
                            max_leaves, count_dev, over_dev);
     }
     gs_free_all(ctx, &tmp);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// leaf -> candidate groups.  Binning a leaf only needs the candidates whose
+// rectangle meets it, in depth order.  The candidates are visited in depth
+// order; each emits (leaf, slot) for every leaf it meets -- one leaf when its
+// four rectangle corners share a leaf (leaves are rectangles), otherwise every
+// leaf its rectangle meets -- and a stable radix sort on the leaf id groups
+// them with the depth order kept inside each group.
+
+namespace {
+
+__global__ void k_leaf_map(const gs_leaf* __restrict__ leaves, int TW, int32_t* __restrict__ lot)
+{
+    const gs_leaf L = leaves[blockIdx.x];
+    const int w = L.tx1 - L.tx0;
+    const int64_t tot = (int64_t)w * (L.ty1 - L.ty0);
+    for (int64_t k = threadIdx.x; k < tot; k += blockDim.x)
+        lot[(int64_t)(L.ty0 + k / w) * TW + (L.tx0 + k % w)] = (int32_t)blockIdx.x;
+}
+
+__device__ __forceinline__ bool rect_meets(int4 r, const gs_leaf& L)
+{
+    return r.x < L.tx1 && L.tx0 < r.z && r.y < L.ty1 && L.ty0 < r.w;
+}
+
+// EMIT = false: number of leaves met; true: write the (leaf, slot) pairs
+template <bool EMIT>
+__global__ __launch_bounds__(256) void k_leaf_pairs(int64_t n, const uint32_t* __restrict__ order,
+                                                    const int4* __restrict__ rect,
+                                                    const gs_leaf* __restrict__ leaves, int nl,
+                                                    const int32_t* __restrict__ lot, int TW,
+                                                    uint32_t* __restrict__ cnt, const uint64_t* __restrict__ off,
+                                                    uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const uint32_t j = order[k];
+    const int4 r = rect[j];
+    const int a = lot[(int64_t)r.y * TW + r.x], b = lot[(int64_t)r.y * TW + r.z - 1];
+    const int c = lot[(int64_t)(r.w - 1) * TW + r.x], d = lot[(int64_t)(r.w - 1) * TW + r.z - 1];
+    if (a == b && a == c && a == d) {
+        if (EMIT) {
+            keys[off[k]] = (uint32_t)a;
+            vals[off[k]] = j;
+        } else {
+            cnt[k] = 1u;
+        }
+        return;
+    }
+    uint64_t o = EMIT ? off[k] : 0;
+    uint32_t m = 0;
+    for (int L = 0; L < nl; ++L)
+        if (rect_meets(r, leaves[L])) {
+            if (EMIT) {
+                keys[o] = (uint32_t)L;
+                vals[o] = j;
+                ++o;
+            }
+            ++m;
+        }
+    if (!EMIT) cnt[k] = m;
+}
+
+}  // namespace
+
+gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot)
+{
+    if (n_leaves > 0)
+        hipLaunchKernelGGL(k_leaf_map, dim3((unsigned)n_leaves), dim3(256), 0, ctx->stream, leaves_dev, TW, lot);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
+                            const int32_t* lot, uint32_t* cnt, const uint64_t* off, uint32_t* keys, uint32_t* vals)
+{
+    const int64_t n = proj->n_cand;
+    if (n > 0) {
+        GsTimerScope ts(ctx, "leaf_groups");
+        if (!off)
+            hipLaunchKernelGGL(k_leaf_pairs<false>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n,
+                               proj->order, proj->rect, leaves_dev, n_leaves, lot, proj->TW, cnt, off, keys, vals);
+        else
+            hipLaunchKernelGGL(k_leaf_pairs<true>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n,
+                               proj->order, proj->rect, leaves_dev, n_leaves, lot, proj->TW, cnt, off, keys, vals);
+    }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -1,0 +1,176 @@
+// radix.hip -- stable LSD radix sort of (u32 key, u32 value) pairs.
+//
+// Each pass takes 8 key bits (fewer on the last pass): a per-block digit
+// histogram (LDS atomics), an exclusive scan of the digit-major histogram
+// (digit * n_blocks + block), and a stable scatter.  The scatter ranks a
+// block's elements in element order: 256 elements per round, a wavefront
+// finds the lanes holding the same digit with one ballot per digit bit
+// (lane rank = popcount of same-digit lanes below it), per-wave digit counts
+// go through LDS, and a running per-digit base carries the order across
+// rounds.  Stable passes make the result sorted by the whole key with ties in
+// input order.
+#include "gs_device.h"
+#include "gs_internal.h"
+
+namespace {
+
+constexpr int kRB = 256;      // threads per block
+constexpr int kRItems = 8;    // rounds (elements per thread)
+constexpr int kRTile = kRB * kRItems;
+constexpr int kRadix = 256;
+
+__global__ __launch_bounds__(kRB) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n, int shift,
+                                                    uint32_t mask, uint32_t* __restrict__ hist, int64_t nb)
+{
+    __shared__ uint32_t h[kRadix];
+    for (int d = threadIdx.x; d < kRadix; d += kRB) h[d] = 0u;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kRTile;
+    for (int k = threadIdx.x; k < kRTile; k += kRB) {
+        const int64_t i = base + k;
+        if (i < n) atomicAdd(&h[(keys[i] >> shift) & mask], 1u);
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < kRadix; d += kRB) hist[(int64_t)d * nb + blockIdx.x] = h[d];
+}
+
+__device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(x, o, 64);
+        if (lane >= o) x += u;
+    }
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += sh[w];
+    __syncthreads();
+    return before + x - v;
+}
+
+// Stable scatter of one block's kRTile elements: (1) local ranks in element
+// order, (2) the block's elements placed digit-sorted in LDS, (3) written out
+// digit run by digit run, so that consecutive lanes write consecutive
+// addresses.
+__global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restrict__ kin,
+                                                       const uint32_t* __restrict__ vin, int64_t n, int shift,
+                                                       int bits, const uint32_t* __restrict__ hscan, int64_t nb,
+                                                       uint32_t* __restrict__ kout, uint32_t* __restrict__ vout)
+{
+    __shared__ uint32_t run[kRadix];
+    __shared__ uint32_t lstart[kRadix];
+    __shared__ uint32_t gbase[kRadix];
+    __shared__ uint32_t wh[kRB / 64][kRadix];
+    __shared__ uint32_t sk[kRTile];
+    __shared__ uint32_t sv[kRTile];
+    __shared__ uint32_t scan_sh[kRB / 64];
+    const uint32_t mask = (1u << bits) - 1u;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int d = threadIdx.x; d < kRadix; d += kRB) {
+        run[d] = 0u;
+        gbase[d] = hscan[(int64_t)d * nb + blockIdx.x];
+    }
+    const int64_t base = (int64_t)blockIdx.x * kRTile;
+    uint32_t kk[kRItems], vv[kRItems], ll[kRItems], dd[kRItems];
+#pragma unroll
+    for (int r = 0; r < kRItems; ++r) {
+        for (int q = threadIdx.x; q < (kRB / 64) * kRadix; q += kRB) (&wh[0][0])[q] = 0u;
+        const int64_t i = base + (int64_t)r * kRB + threadIdx.x;
+        const bool valid = i < n;
+        uint32_t key = 0, val = 0, d = 0;
+        if (valid) {
+            key = kin[i];
+            val = vin[i];
+            d = (key >> shift) & mask;
+        }
+        uint64_t peers = gsd::ballot(valid);
+        for (int b = 0; b < bits; ++b) {
+            const uint64_t bb = gsd::ballot(valid && ((d >> b) & 1u));
+            peers &= ((d >> b) & 1u) ? bb : ~bb;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & lt);
+        __syncthreads();
+        if (valid && rank == 0) wh[wave][d] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        uint32_t loc = run[d] + rank;
+        for (int w = 0; w < wave; ++w) loc += wh[w][d];
+        kk[r] = key;
+        vv[r] = val;
+        dd[r] = valid ? d : 0xFFFFFFFFu;
+        ll[r] = loc;
+        __syncthreads();
+        for (int q = threadIdx.x; q < kRadix; q += kRB) {
+            uint32_t s = 0;
+            for (int w = 0; w < kRB / 64; ++w) s += wh[w][q];
+            run[q] += s;
+        }
+        __syncthreads();
+    }
+    // local start of every digit run (kRadix == kRB: one digit per thread)
+    lstart[threadIdx.x] = block_excl_scan256(run[threadIdx.x], scan_sh);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRItems; ++r)
+        if (dd[r] != 0xFFFFFFFFu) {
+            const uint32_t pos = lstart[dd[r]] + ll[r];
+            sk[pos] = kk[r];
+            sv[pos] = vv[r];
+        }
+    __syncthreads();
+    const int nvalid = (int)min<int64_t>(kRTile, n - base);
+    for (int q = threadIdx.x; q < nvalid; q += kRB) {
+        const uint32_t key = sk[q];
+        const uint32_t d = (key >> shift) & mask;
+        const uint32_t o = gbase[d] + (uint32_t)q - lstart[d];
+        kout[o] = key;
+        vout[o] = sv[q];
+    }
+}
+
+}  // namespace
+
+// Sorts n pairs by the low key_bits bits of the keys (stable).  k0/v0 hold the
+// input; k1/v1 are scratch of the same size.  *in_second is set when the
+// sorted result ends in (k1, v1).  Offsets of one pass fit u32: n < 2^32.
+gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n,
+                            int key_bits, bool* in_second)
+{
+    *in_second = false;
+    if (n <= 1 || key_bits <= 0) return GS_OK;
+    if (n >= (1ll << 32)) return gs_fail(ctx, GS_ERR_OVERFLOW, "radix sort of %lld >= 2^32 pairs", (long long)n);
+    const int64_t nb = ceil_div(n, kRTile);
+    std::vector<GsAlloc> tmp;
+    uint32_t* hist = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * kRadix * nb, GS_MEM_SCRATCH, &tmp);
+    uint32_t* hscan = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (kRadix * nb + 1), GS_MEM_SCRATCH, &tmp);
+    if (!hist || !hscan) {
+        gs_free_all(ctx, &tmp);
+        return GS_ERR_OOM;
+    }
+    gs_status st = GS_OK;
+    uint32_t *ki = k0, *vi = v0, *ko = k1, *vo = v1;
+    for (int shift = 0; shift < key_bits && st == GS_OK; shift += 8) {
+        const int bits = std::min(8, key_bits - shift);
+        {
+            GsTimerScope ts(ctx, "radix");
+            hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, n, shift,
+                               (1u << bits) - 1u, hist, nb);
+        }
+        st = launch_scan_u32_to_u32(ctx, hist, hscan, kRadix * nb);
+        if (st != GS_OK) break;
+        {
+            GsTimerScope ts(ctx, "radix");
+            hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n, shift,
+                               bits, hscan, nb, ko, vo);
+        }
+        std::swap(ki, ko);
+        std::swap(vi, vo);
+        *in_second = !*in_second;
+    }
+    gs_free_all(ctx, &tmp);
+    if (st != GS_OK) return st;
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}

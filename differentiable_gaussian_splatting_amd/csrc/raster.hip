@@ -3,10 +3,18 @@
 // Layout (MI355X, wave64): one workgroup of 4 wavefronts per 16x16 tile, each
 // wavefront owning an independent 8x8 sub-tile (lane = pixel).  A wavefront
 // stages a batch of 64 list entries in its own LDS slice (lane i gathers entry
-// i's 9 floats), then every lane walks the batch with wave-uniform LDS reads
-// (broadcast, no bank conflicts).  No workgroup barrier is used: wavefronts of
-// one tile finish independently, and a wavefront leaves as soon as a ballot
-// shows that every one of its pixels has stopped.
+// i), then every lane walks the batch with wave-uniform LDS reads (broadcast,
+// free of bank conflicts).  No workgroup barrier is used: the wavefronts of a
+// tile finish independently, and one leaves as soon as a ballot shows that all
+// of its pixels have stopped.
+//
+// Sub-tile culling: while staging, lane i also decides whether entry i can
+// reach alpha >= 1/255 anywhere in the wavefront's 8x8 box of pixel centres:
+// the minimum of the quadratic form q = A dx^2 + 2B dx dy + C dy^2 over the
+// box (0 if the centre is inside, else the least of four clamped edge minima)
+// is compared with 2 ln(255 o), with a margin that covers the f32 rounding of
+// both q and the per-pixel exponent.  An entry is dropped only when every
+// pixel of the box would skip it, so the per-pixel decisions are unchanged.
 //
 // Forward (SkipGS notes, "loss function": transmittance accumulation; the
 // pages give no formulas, this is the standard compositing rule):
@@ -20,9 +28,10 @@
 // Backward (BoundedGS Fig. 3 A->B; SkipGS notes: atomic accumulation): per
 // pixel the included entries are revisited back to front from the last one,
 // with T recovered as T' / (1 - alpha) and the colour behind accumulated as S;
-//   dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha))
-// and the 9 partials of an entry are summed over the wavefront (DPP) before a
-// single lane-parallel atomic add of the 9 values.
+//   dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha)).
+// The 9 partials of an entry are summed over the wavefront by a transposed
+// reduction (each step halves the lanes per value while pairing values, with
+// the gfx950 lane-swap instructions and DPP) and written by one 9-lane atomic.
 #include "gs_device.h"
 #include "gs_internal.h"
 
@@ -50,8 +59,38 @@ struct Staged {        // one wavefront's staged batch
     float4 a[64];      // x, y, -A/2, -B
     float4 b[64];      // -C/2, opacity, r, g
     float c[64];       // b
+    uint32_t slot[64];
 };
 
+// true when no pixel centre of the box [bx0, bx0+7] x [by0, by0+7] can
+// include the entry (alpha < 1/255 everywhere)
+__device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by0)
+{
+    const float o = b.y;
+    if (!(o * 255.0f >= 1.0f)) return true;     // alpha <= o < 1/255
+    const float A = -2.0f * a.z, B = -a.w, C = -2.0f * b.x;
+    const float dx0 = bx0 - a.x, dx1 = dx0 + 7.0f;
+    const float dy0 = by0 - a.y, dy1 = dy0 + 7.0f;
+    if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) return false;
+    float qmin = __builtin_inff();
+    {
+        const float iC = 1.0f / C, iA = 1.0f / A;
+        float X = dx0, t = fminf(fmaxf(-B * X * iC, dy0), dy1);
+        qmin = fminf(qmin, A * X * X + 2.0f * B * X * t + C * t * t);
+        X = dx1; t = fminf(fmaxf(-B * X * iC, dy0), dy1);
+        qmin = fminf(qmin, A * X * X + 2.0f * B * X * t + C * t * t);
+        float Y = dy0, s = fminf(fmaxf(-B * Y * iA, dx0), dx1);
+        qmin = fminf(qmin, C * Y * Y + 2.0f * B * Y * s + A * s * s);
+        Y = dy1; s = fminf(fmaxf(-B * Y * iA, dx0), dx1);
+        qmin = fminf(qmin, C * Y * Y + 2.0f * B * Y * s + A * s * s);
+    }
+    const float Xm = fmaxf(fabsf(dx0), fabsf(dx1)), Ym = fmaxf(fabsf(dy0), fabsf(dy1));
+    const float S = fabsf(A) * Xm * Xm + 2.0f * fabsf(B) * Xm * Ym + fabsf(C) * Ym * Ym;
+    const float thr = 2.0f * __logf(255.0f * o);
+    return qmin - (0.02f + 1e-3f * qmin + 1e-5f * S) > thr;
+}
+
+template <bool STATS>
 __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* __restrict__ offsets,
                                                     const uint32_t* __restrict__ values,
                                                     const float4* __restrict__ g0, const float4* __restrict__ g1,
@@ -59,35 +98,43 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
                                                     const float* __restrict__ target, float inv_norm,
                                                     float* __restrict__ image, float* __restrict__ tfinal,
                                                     uint32_t* __restrict__ last, float* __restrict__ dldc,
-                                                    double* __restrict__ l1_part)
+                                                    double* __restrict__ l1_part,
+                                                    unsigned long long* __restrict__ stats)
 {
     __shared__ Staged st[4];
     const int lt = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tx = g.ltx0 + lt % g.TWL, ty = g.lty0 + lt / g.TWL;
-    const int px = tx * 16 + (wave & 1) * 8 + (lane & 7);
-    const int py = ty * 16 + (wave >> 1) * 8 + (lane >> 3);
+    const int sx0 = tx * 16 + (wave & 1) * 8, sy0 = ty * 16 + (wave >> 1) * 8;
+    const int px = sx0 + (lane & 7), py = sy0 + (lane >> 3);
     const bool inside = px < g.W && py < g.H;
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
+    const float bx0 = (float)sx0 + 0.5f, by0 = (float)sy0 + 0.5f;
     const uint64_t start = offsets[lt], end = offsets[lt + 1];
     Staged& S = st[wave];
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
-    uint32_t lastn = 0;
+    uint32_t lastn = 0, n_eval = 0, n_inc = 0, ev_at_last = 0;
     bool done = !inside;
     for (uint64_t base = start; base < end; base += 64) {
         if (gsd::ballot(!done) == 0) break;
         const uint64_t e = base + lane;
+        bool keep = false;
         if (e < end) {
             const uint32_t s = values[e];
-            S.a[lane] = g0[s];
-            S.b[lane] = g1[s];
+            const float4 a = g0[s], b = g1[s];
+            S.a[lane] = a;
+            S.b[lane] = b;
             S.c[lane] = g2[s].x;
+            keep = !cull_box(a, b, bx0, by0);
         }
+        uint64_t mask = gsd::ballot(keep);
         gsd::wave_sync();
-        const int cnt = (int)min<uint64_t>(64, end - base);
         if (!done) {
-            for (int j = 0; j < cnt; ++j) {
+            while (mask) {
+                const int j = __builtin_ctzll(mask);
+                mask &= mask - 1;
+                if (STATS) ++n_eval;
                 const float4 a = S.a[j];
                 const float4 b = S.b[j];
                 const float dx = pxc - a.x, dy = pyc - a.y;
@@ -112,6 +159,10 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
                 C2 = __builtin_fmaf(S.c[j], w, C2);
                 T = Tn;
                 lastn = (uint32_t)(base - start) + (uint32_t)j + 1u;
+                if (STATS) {
+                    ++n_inc;
+                    ev_at_last = n_eval;
+                }
             }
         }
         gsd::wave_sync();
@@ -145,6 +196,81 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
         l1 = gsd::wave_sum_d(l1);
         if (lane == 0) l1_part[(int64_t)lt * 4 + wave] = l1;
     }
+    if (STATS) {
+        // [0] pairs examined, [1] pairs included, [2] sum of last, [3] pairs
+        // the backward revisits (examined up to the last included entry)
+        const double a0 = gsd::wave_sum_d((double)n_eval), a1 = gsd::wave_sum_d((double)n_inc);
+        const double a2 = gsd::wave_sum_d((double)(inside ? lastn : 0u));
+        const double a3 = gsd::wave_sum_d((double)ev_at_last);
+        if (lane == 0) {
+            atomicAdd(&stats[0], (unsigned long long)a0);
+            atomicAdd(&stats[1], (unsigned long long)a1);
+            atomicAdd(&stats[2], (unsigned long long)a2);
+            atomicAdd(&stats[3], (unsigned long long)a3);
+        }
+    }
+}
+
+// ---- transposed wave reduction of 9 values --------------------------------
+__device__ __forceinline__ uint32_t fb(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bf(uint32_t v) { return __builtin_bit_cast(float, v); }
+
+// x, y -> x + y where the first 32 lanes hold the value of x and the last 32
+// that of y (each summed over lanes l and l +- 32)
+__device__ __forceinline__ float pair32(float x, float y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(fb(x), fb(y), false, false);
+    return bf(r[0]) + bf(r[1]);
+}
+
+// per 32-lane half: rows 0/2 of the result carry x, rows 1/3 carry y (each
+// summed over the two rows of the half)
+__device__ __forceinline__ float pair16(float x, float y)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(fb(x), fb(y), false, false);
+    return bf(r[0]) + bf(r[1]);
+}
+
+// within each 16-lane row: lanes 0-7 carry x, lanes 8-15 carry y
+__device__ __forceinline__ float pair8(float x, float y, int lane)
+{
+    const bool hi = (lane & 8) != 0;
+    const float send = hi ? x : y, keep = hi ? y : x;
+    return keep + gsd::dpp_f<0x140>(send);   // row_mirror
+}
+
+// within each 8-lane group: lanes 0-3 carry x, lanes 4-7 carry y
+__device__ __forceinline__ float pair4(float x, float y, int lane)
+{
+    const bool hi = (lane & 4) != 0;
+    const float send = hi ? x : y, keep = hi ? y : x;
+    return keep + gsd::dpp_f<0x141>(send);   // row_half_mirror
+}
+
+// Sums p[0..8] over the wavefront.  On return the full sum of value v is in
+// the first lane of quad q (lane 4q) with v = bitreverse3(q / 2) for even q
+// and v = 8 for q = 1; *vidx gets that v, or -1 for lanes that hold none.
+__device__ __forceinline__ float wave_reduce9(const float* p, int lane, int* vidx)
+{
+    const float a0 = pair32(p[0], p[1]), a1 = pair32(p[2], p[3]), a2 = pair32(p[4], p[5]);
+    const float a3 = pair32(p[6], p[7]), a4 = pair32(p[8], 0.0f);
+    const float b0 = pair16(a0, a1), b1 = pair16(a2, a3), b2 = pair16(a4, 0.0f);
+    const float c0 = pair8(b0, b1, lane), c1 = pair8(b2, 0.0f, lane);
+    float d = pair4(c0, c1, lane);
+    d += gsd::dpp_f<0x4E>(d);   // quad_perm [2,3,0,1]
+    d += gsd::dpp_f<0xB1>(d);   // quad_perm [1,0,3,2]
+    const int q = lane >> 2;
+    int v = -1;
+    if ((lane & 3) == 0) {
+        if ((q & 1) == 0) {
+            const int k = q >> 1;
+            v = ((k & 1) << 2) | (k & 2) | ((k >> 2) & 1);
+        } else if (q == 1) {
+            v = 8;
+        }
+    }
+    *vidx = v;
+    return d;
 }
 
 __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* __restrict__ offsets,
@@ -158,14 +284,14 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
                                                     float* __restrict__ grad2d)
 {
     __shared__ Staged st[4];
-    __shared__ uint32_t slot_s[4][64];
     const int lt = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tx = g.ltx0 + lt % g.TWL, ty = g.lty0 + lt / g.TWL;
-    const int px = tx * 16 + (wave & 1) * 8 + (lane & 7);
-    const int py = ty * 16 + (wave >> 1) * 8 + (lane >> 3);
+    const int sx0 = tx * 16 + (wave & 1) * 8, sy0 = ty * 16 + (wave >> 1) * 8;
+    const int px = sx0 + (lane & 7), py = sy0 + (lane >> 3);
     const bool inside = px < g.W && py < g.H;
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
+    const float bx0 = (float)sx0 + 0.5f, by0 = (float)sy0 + 0.5f;
     const uint64_t start = offsets[lt];
     Staged& S = st[wave];
 
@@ -193,18 +319,23 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
     for (int64_t hi = maxl; hi > 0; hi -= 64) {
         const int64_t lo = hi > 64 ? hi - 64 : 0;
         const int cnt = (int)(hi - lo);
+        bool keep = false;
         if (lane < cnt) {
             const uint32_t s = values[start + lo + lane];
-            slot_s[wave][lane] = s;
-            S.a[lane] = g0[s];
-            S.b[lane] = g1[s];
+            const float4 a = g0[s], b = g1[s];
+            S.slot[lane] = s;
+            S.a[lane] = a;
+            S.b[lane] = b;
             S.c[lane] = g2[s].x;
+            keep = !cull_box(a, b, bx0, by0);
         }
+        uint64_t mask = gsd::ballot(keep);
         gsd::wave_sync();
-        for (int j = cnt - 1; j >= 0; --j) {
+        while (mask) {
+            const int j = 63 - __builtin_clzll(mask);
+            mask &= ~(1ull << j);
             const uint32_t n = (uint32_t)(lo + j);
-            float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f, p4 = 0.0f, p5 = 0.0f, p6 = 0.0f, p7 = 0.0f,
-                  p8 = 0.0f;
+            float p[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             bool contrib = false;
             if (n < lst) {
                 const float4 a = S.a[j];
@@ -227,9 +358,9 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
                         const float rom = __builtin_amdgcn_rcpf(om);
                         T = T * rom;                      // T before this entry
                         const float w = alpha * T;
-                        p6 = gr0 * w;
-                        p7 = gr1 * w;
-                        p8 = gr2 * w;
+                        p[6] = gr0 * w;
+                        p[7] = gr1 * w;
+                        p[8] = gr2 * w;
                         const float dal = gr0 * (b.z * T - S0 * rom) + gr1 * (b.w * T - S1 * rom) +
                                           gr2 * (cb * T - S2 * rom);
                         S0 = __builtin_fmaf(b.z, w, S0);
@@ -237,31 +368,21 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
                         S2 = __builtin_fmaf(cb, w, S2);
                         if (!clamped) {
                             const float dpw = dal * av;   // d alpha / d power = o G
-                            p5 = dal * G;
+                            p[5] = dal * G;
                             // A = -2 a.z, B = -a.w, C = -2 b.x
-                            p2 = -0.5f * dx * dx * dpw;
-                            p3 = -dx * dy * dpw;
-                            p4 = -0.5f * dy * dy * dpw;
-                            p0 = (-2.0f * a.z * dx - a.w * dy) * dpw;
-                            p1 = (-2.0f * b.x * dy - a.w * dx) * dpw;
+                            p[2] = -0.5f * dx * dx * dpw;
+                            p[3] = -dx * dy * dpw;
+                            p[4] = -0.5f * dy * dy * dpw;
+                            p[0] = (-2.0f * a.z * dx - a.w * dy) * dpw;
+                            p[1] = (-2.0f * b.x * dy - a.w * dx) * dpw;
                         }
                     }
                 }
             }
             if (gsd::ballot(contrib) == 0) continue;
-            const float r0 = gsd::wave_sum(p0), r1 = gsd::wave_sum(p1), r2 = gsd::wave_sum(p2);
-            const float r3 = gsd::wave_sum(p3), r4 = gsd::wave_sum(p4), r5 = gsd::wave_sum(p5);
-            const float r6 = gsd::wave_sum(p6), r7 = gsd::wave_sum(p7), r8 = gsd::wave_sum(p8);
-            float mine = r0;
-            mine = lane == 1 ? r1 : mine;
-            mine = lane == 2 ? r2 : mine;
-            mine = lane == 3 ? r3 : mine;
-            mine = lane == 4 ? r4 : mine;
-            mine = lane == 5 ? r5 : mine;
-            mine = lane == 6 ? r6 : mine;
-            mine = lane == 7 ? r7 : mine;
-            mine = lane == 8 ? r8 : mine;
-            if (lane < 9) unsafeAtomicAdd(&grad2d[(int64_t)slot_s[wave][j] * 9 + lane], mine);
+            int v;
+            const float r = wave_reduce9(p, lane, &v);
+            if (v >= 0) unsafeAtomicAdd(&grad2d[(int64_t)S.slot[j] * 9 + v], r);
         }
         gsd::wave_sync();
     }
@@ -270,15 +391,23 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
 }  // namespace
 
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                            gs_raster* r, const float* target, float* image_out, double* loss_accum)
+                            gs_raster* r, const float* target, float* image_out, double* loss_accum,
+                            uint64_t* stats)
 {
     const LeafGeom g = make_geom(cam, bins, r);
     const float inv_norm = (float)(1.0 / (3.0 * (double)cam->width * (double)cam->height));
     if (bins->n_tiles > 0) {
         GsTimerScope ts(ctx, "raster_fwd");
-        hipLaunchKernelGGL(k_raster_fwd, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g, bins->offsets,
-                           bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2], target,
-                           inv_norm, image_out, r->tfinal, r->last, r->dldc, r->l1_part);
+        if (stats)
+            hipLaunchKernelGGL(k_raster_fwd<true>, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g,
+                               bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
+                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->dldc, r->l1_part,
+                               (unsigned long long*)stats);
+        else
+            hipLaunchKernelGGL(k_raster_fwd<false>, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g,
+                               bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
+                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->dldc, r->l1_part,
+                               nullptr);
     }
     GS_HIP(ctx, hipGetLastError());
     if (target && loss_accum) return launch_sum_f64(ctx, r->l1_part, bins->n_tiles * 4, 1, loss_accum, 1);

@@ -173,7 +173,10 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
  * summed-area table -> starting from the whole tile grid, a region is kept
  * when its estimate <= budget_bytes or it is a single tile, otherwise its
  * longer side (ties: x) is halved at floor(len/2); leaves are returned in
- * depth-first order (first half first).  cost: NULL = default.
+ * depth-first order (first half first).  The plan (with, for each leaf, the
+ * candidates whose rectangle meets it) is attached to `proj`, so that
+ * gs_bin_sort of a planned leaf visits only those candidates; a new plan
+ * replaces it.  cost: NULL = default.
  * leaves: host array of max_leaves entries; *n_leaves (host) = number of
  * leaves (entries beyond max_leaves are counted, not written; call again
  * with a larger array).  strict != 0: GS_ERR_BUDGET if any single tile
@@ -204,10 +207,15 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
  * is fused: sum |out - target| over the leaf is added to *loss_accum
  * (device, one double, may be NULL) and dL/dout = sgn(out - target)/(3WH)
  * is kept in the raster handle for gs_render_bwd.  image_out: device full
- * image [3][H][W] or NULL; the leaf's pixels are written.  *out: new handle.
+ * image [3][H][W] or NULL; the leaf's pixels are written.  stats: device
+ * u64 [4] or NULL; when given, [0] the (pixel, entry) pairs examined, [1]
+ * the pairs included, [2] the sum over pixels of the list position after the
+ * last included entry, [3] the pairs gs_render_bwd revisits, are added to it
+ * (a separately compiled, slightly slower kernel).  *out: new handle.
  * Asynchronous. */
 gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                        const float* target, double* loss_accum, float* image_out, gs_raster** out);
+                        const float* target, double* loss_accum, float* image_out, uint64_t* stats,
+                        gs_raster** out);
 
 /* Raster backward of one leaf, accumulated into grad2d.  BoundedGS Fig. 3
  * A->B (rasterization backward collects the projected attributes'
