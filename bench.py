@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-adam", action="store_true")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-window", type=int, default=384, help="side (pixels) of the oracle's sampled window")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (a known-traffic kernel for counter scaling)")
     return ap.parse_args()
 
 
@@ -86,6 +88,13 @@ def main():
     target = torch.from_numpy(w.target).to(dev)
     torch.cuda.synchronize()
     P = cam.width * cam.height
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib * MIB // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+        del src, dst
 
     def step(k):
         adam = None if args.no_adam else dict(step=k, params=params, m=m, v=v, lr=1e-3)

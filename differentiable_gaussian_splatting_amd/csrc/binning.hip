@@ -77,66 +77,95 @@ __global__ __launch_bounds__(256) void k_count_tiles(int64_t n, const uint32_t* 
     cnt[k] = (w > 0 && h > 0) ? (uint32_t)(w * h) : 0u;
 }
 
-constexpr int kWideRect = 32;   // rectangles with more tiles are written by a whole wave
+constexpr int kOB = 256;     // threads of an emission block
+constexpr int kOE = 4096;    // outputs of an emission block
+
+__device__ __forceinline__ int64_t last_le(const uint64_t* __restrict__ a, int64_t n, uint64_t v)
+{
+    // largest k in [0, n) with a[k] <= v (a non-decreasing, a[0] <= v)
+    int64_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (a[mid] <= v) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
 
 // (leaf-local tile, slot) pairs of the listed candidates, in list order and
-// row-major tile order, at eoff[k]
-__global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
+// row-major tile order within a rectangle.  eoff is the exclusive scan of the
+// per-candidate tile counts (n + 1 entries).  Each block writes a fixed range
+// of kOE consecutive outputs, so the writes are coalesced whatever the
+// rectangle sizes; the candidate of an output is found by binary search in an
+// LDS copy of the block's part of eoff (or in eoff itself when that part is
+// too long, which only long runs of empty candidates cause).
+__global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
                                                     const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
-                                                    int lty1, const uint64_t* __restrict__ eoff,
+                                                    int lty1, const uint64_t* __restrict__ eoff, uint64_t total,
                                                     uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int lane = gsd::lane_id();
+    __shared__ uint64_t se[kOE + 1];
+    __shared__ int64_t s_c0, s_m;
+    const uint64_t o0 = (uint64_t)blockIdx.x * kOE;
+    const uint64_t o1 = min<uint64_t>(total, o0 + kOE);
+    if (o0 >= o1) return;
+    if (threadIdx.x == 0) {
+        const int64_t c0 = last_le(eoff, n + 1, o0);
+        const int64_t c1 = last_le(eoff, n + 1, o1 - 1);
+        s_c0 = c0;
+        s_m = c1 - c0 + 1;
+    }
+    __syncthreads();
+    const int64_t c0 = s_c0, m = s_m;
+    const bool in_lds = m <= kOE + 1;
+    if (in_lds)
+        for (int64_t k = threadIdx.x; k < m; k += kOB) se[k] = eoff[c0 + k];
+    __syncthreads();
     const int TWL = ltx1 - ltx0;
-    int x0 = 0, y0 = 0, w = 0, h = 0;
-    uint32_t j = 0;
-    uint64_t o = 0;
-    if (k < n) {
-        j = list[k];
-        const int4 r = rect[j];
-        x0 = max(r.x, ltx0) - ltx0;
-        y0 = max(r.y, lty0) - lty0;
-        w = min(r.z, ltx1) - ltx0 - x0;
-        h = min(r.w, lty1) - lty0 - y0;
-        if (w <= 0 || h <= 0) w = h = 0;
-        o = eoff[k];
-    }
-    const bool wide = w * h > kWideRect;
-    if (!wide) {
-        for (int ty = 0; ty < h; ++ty)
-            for (int tx = 0; tx < w; ++tx) {
-                keys[o] = (uint32_t)((y0 + ty) * TWL + x0 + tx);
-                vals[o] = j;
-                ++o;
-            }
-    }
-    uint64_t pending = gsd::ballot(wide);
-    while (pending) {
-        const int src = __builtin_ctzll(pending);
-        pending &= pending - 1;
-        const int sx0 = __shfl(x0, src, 64), sy0 = __shfl(y0, src, 64);
-        const int sw = __shfl(w, src, 64), sh = __shfl(h, src, 64);
-        const uint32_t sj = (uint32_t)__shfl((int)j, src, 64);
-        const uint64_t so = __shfl(o, src, 64);
-        const int tot = sw * sh;
-        for (int q = lane; q < tot; q += 64) {
-            keys[so + q] = (uint32_t)((sy0 + q / sw) * TWL + sx0 + q % sw);
-            vals[so + q] = sj;
+    for (uint64_t o = o0 + threadIdx.x; o < o1; o += kOB) {
+        int64_t c;
+        uint64_t start;
+        if (in_lds) {
+            const int64_t k = last_le(se, m, o);
+            c = c0 + k;
+            start = se[k];
+        } else {
+            c = c0 + last_le(eoff + c0, m, o);
+            start = eoff[c];
         }
+        const uint32_t j = list[c];
+        const int4 r = rect[j];
+        const int x0 = max(r.x, ltx0) - ltx0, y0 = max(r.y, lty0) - lty0;
+        const int w = min(r.z, ltx1) - ltx0 - x0;
+        const uint32_t t = (uint32_t)(o - start);
+        keys[o] = (uint32_t)((y0 + (int)(t / (uint32_t)w)) * TWL + x0 + (int)(t % (uint32_t)w));
+        vals[o] = j;
     }
 }
 
 // offsets[s] = first position whose key is >= s, for s in [0, n_seg]; keys
-// sorted ascending, all < n_seg
+// sorted ascending, all < n_seg.  Four keys per thread.
 __global__ __launch_bounds__(256) void k_seg_offsets(const uint32_t* __restrict__ keys, int64_t n, int64_t n_seg,
                                                      uint64_t* __restrict__ offsets)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k > n) return;
-    const int64_t prev = k == 0 ? -1 : (int64_t)keys[k - 1];
-    const int64_t cur = k == n ? n_seg : (int64_t)keys[k];
-    for (int64_t s = prev + 1; s <= cur; ++s) offsets[s] = (uint64_t)k;
+    const int64_t k0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (k0 > n) return;
+    int64_t prev = k0 == 0 ? -1 : (int64_t)keys[k0 - 1];
+    uint32_t cur4[4];
+    if (k0 + 4 <= n && (k0 & 3) == 0) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + k0);
+        cur4[0] = v.x; cur4[1] = v.y; cur4[2] = v.z; cur4[3] = v.w;
+    } else {
+        for (int q = 0; q < 4; ++q) cur4[q] = k0 + q < n ? keys[k0 + q] : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t k = k0 + q;
+        if (k > n) break;
+        const int64_t cur = k == n ? n_seg : (int64_t)cur4[q];
+        for (int64_t s = prev + 1; s <= cur; ++s) offsets[s] = (uint64_t)k;
+        prev = cur;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_depth_pairs(int64_t n, const float4* __restrict__ g2,
@@ -194,12 +223,12 @@ gs_status launch_count_tiles(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf
 }
 
 gs_status launch_emit_pairs(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
-                            int64_t n_list, const uint64_t* eoff, uint32_t* keys, uint32_t* vals)
+                            int64_t n_list, const uint64_t* eoff, uint64_t total, uint32_t* keys, uint32_t* vals)
 {
-    if (n_list > 0) {
+    if (n_list > 0 && total > 0) {
         GsTimerScope ts(ctx, "emit");
-        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div(n_list, 256)), dim3(256), 0, ctx->stream, n_list,
-                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, eoff, keys, vals);
+        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div((int64_t)total, kOE)), dim3(kOB), 0, ctx->stream,
+                           n_list, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, eoff, total, keys, vals);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
@@ -208,8 +237,8 @@ gs_status launch_emit_pairs(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets)
 {
     GsTimerScope ts(ctx, "seg_offsets");
-    hipLaunchKernelGGL(k_seg_offsets, dim3((unsigned)ceil_div(n + 1, 256)), dim3(256), 0, ctx->stream, sorted_keys,
-                       n, n_seg, offsets);
+    hipLaunchKernelGGL(k_seg_offsets, dim3((unsigned)ceil_div(ceil_div(n + 1, 4), 256)), dim3(256), 0, ctx->stream,
+                       sorted_keys, n, n_seg, offsets);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -369,15 +369,20 @@ gs_status gs_kernel_time(gs_ctx* ctx, const char* name, double* total_ms, int64_
 
 gs_cost_model gs_default_cost_model(void)
 {
-    // bytes the library allocates for one leaf (L1 fused):
-    //   per intersection: composite key u64 + sorted slot u32 + merge scratch u64
-    //   per pixel: T_final f32 + last u32 + dL/dout 3 x f32
-    //   per tile: counts i32, cursor u32, offsets u64, 4 L1 partials f64
+    // bytes the library allocates for one leaf (L1 fused), peak of binning
+    // and rasterization together:
+    //   per intersection: tile keys u32 x 2 and slots u32 x 2 (radix sort
+    //     ping-pong; one slot array is kept), radix histograms and their scan
+    //     (2 x 256 u32 per 2048 entries), and the per-candidate tile counts
+    //     u32 + emission offsets u64 (at most one candidate per intersection)
+    //     which are freed before the sort buffers peak -> 17 B
+    //   per pixel: T_final f32 + last u32 + L1 signs u8 -> 9 B
+    //   per tile: offsets u64 + 4 L1 partials f64 -> 40 B
     //   constant: scan block sums, allocation rounding, small buffers
     gs_cost_model c;
-    c.b_isect = 20;
-    c.b_pixel = 20;
-    c.b_tile = 64;
+    c.b_isect = 17;
+    c.b_pixel = 9;
+    c.b_tile = 40;
     c.b_const = 1u << 20;
     return c;
 }
@@ -533,6 +538,7 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     if (!cnt || !eoff) { st = GS_ERR_OOM; goto fail; }
     if ((st = launch_count_tiles(ctx, proj, leaf, list, n_list, cnt)) != GS_OK) goto fail;
     if ((st = launch_scan_u32_to_u64(ctx, cnt, eoff, n_list)) != GS_OK) goto fail;
+    gs_free_one(ctx, &tmp, cnt);   // stream-ordered: the scan has consumed it
     if (known >= 0) {
         I = (uint64_t)known;    // from the plan's summed-area table: no read-back
     } else if ((st = readback(ctx, eoff + n_list, sizeof(uint64_t), &I)) != GS_OK) {
@@ -546,8 +552,7 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &b->allocs);
         if (!k0 || !v0) { st = GS_ERR_OOM; goto fail; }
     }
-    if ((st = launch_emit_pairs(ctx, proj, leaf, list, n_list, eoff, k0, v0)) != GS_OK) goto fail;
-    gs_free_one(ctx, &tmp, cnt);
+    if ((st = launch_emit_pairs(ctx, proj, leaf, list, n_list, eoff, I, k0, v0)) != GS_OK) goto fail;
     gs_free_one(ctx, &tmp, eoff);
     {
         const uint64_t ni = std::max<uint64_t>(I, 1);
@@ -598,10 +603,10 @@ gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, 
     r->tfinal = (float*)gs_malloc(ctx, sizeof(float) * r->n_pix, GS_MEM_RASTER, &r->allocs);
     r->last = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * r->n_pix, GS_MEM_RASTER, &r->allocs);
     if (target) {
-        r->dldc = (float*)gs_malloc(ctx, sizeof(float) * 3 * r->n_pix, GS_MEM_RASTER, &r->allocs);
+        r->sgn = (uint8_t*)gs_malloc(ctx, r->n_pix, GS_MEM_RASTER, &r->allocs);
         r->l1_part = (double*)gs_malloc(ctx, sizeof(double) * 4 * bins->n_tiles, GS_MEM_RASTER, &r->allocs);
     }
-    if (!r->tfinal || !r->last || (target && (!r->dldc || !r->l1_part))) {
+    if (!r->tfinal || !r->last || (target && (!r->sgn || !r->l1_part))) {
         destroy_handle(ctx, r);
         return GS_ERR_OOM;
     }
@@ -623,7 +628,7 @@ gs_status gs_render_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, 
         !handle_ok(ctx, raster, kMagicRaster) || bins->proj != proj || raster->bins != bins)
         return gs_fail(ctx, GS_ERR_STATE, "handles do not belong together");
     if (!grad2d && proj->n_cand > 0) return gs_fail(ctx, GS_ERR_INVALID_ARG, "grad2d is NULL");
-    if (!dl_dimage && !raster->dldc)
+    if (!dl_dimage && !raster->sgn)
         return gs_fail(ctx, GS_ERR_INVALID_ARG, "no dL/dimage given and no L1 target fused in the forward");
     return launch_raster_bwd(ctx, cam, proj, bins, raster, dl_dimage, grad2d);
 }

@@ -82,7 +82,7 @@ struct gs_raster : GsHandle {
     int px0 = 0, py0 = 0, WL = 0, HL = 0;
     float* tfinal = nullptr;      // [n_pix]
     uint32_t* last = nullptr;     // [n_pix]
-    float* dldc = nullptr;        // [3][n_pix] or null
+    uint8_t* sgn = nullptr;       // [n_pix] L1 residual signs (2 bits per channel) or null
     double* l1_part = nullptr;    // [n_tiles * 4]
 };
 
@@ -134,7 +134,7 @@ gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, 
 gs_status launch_count_tiles(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                              int64_t n_list, uint32_t* cnt);
 gs_status launch_emit_pairs(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
-                            int64_t n_list, const uint64_t* eoff, uint32_t* keys, uint32_t* vals);
+                            int64_t n_list, const uint64_t* eoff, uint64_t total, uint32_t* keys, uint32_t* vals);
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets);
 gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
 gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);

@@ -29,6 +29,23 @@ __global__ __launch_bounds__(256) void k_sum_f64(const double* __restrict__ in, 
     if (threadIdx.x == 0) *out = (accumulate ? *out : 0.0) + sh[0];
 }
 
+// block b: part[b] = sum of in[k * stride] for k in [b * per, (b + 1) * per)
+__global__ __launch_bounds__(256) void k_sum_chunks(const double* __restrict__ in, int64_t n, int stride, int64_t per,
+                                                    double* __restrict__ part)
+{
+    __shared__ double sh[256];
+    const int64_t k0 = (int64_t)blockIdx.x * per, k1 = min<int64_t>(n, k0 + per);
+    double s = 0.0;
+    for (int64_t k = k0 + threadIdx.x; k < k1; k += 256) s += in[k * stride];
+    sh[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
+}
+
 struct Win {
     float w[11];
 };
@@ -176,7 +193,22 @@ __global__ __launch_bounds__(kSB) void k_ssim_v2(int W, int H, Win win, const fl
 
 gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate)
 {
-    hipLaunchKernelGGL(k_sum_f64, dim3(1), dim3(256), 0, ctx->stream, in, n, stride, out, accumulate);
+    // two stages for long inputs: up to 256 blocks each sum a contiguous
+    // chunk (fixed order), then one block sums the chunk sums
+    constexpr int64_t kChunk = 4096;
+    if (n <= kChunk) {
+        hipLaunchKernelGGL(k_sum_f64, dim3(1), dim3(256), 0, ctx->stream, in, n, stride, out, accumulate);
+        GS_HIP(ctx, hipGetLastError());
+        return GS_OK;
+    }
+    const int64_t nb = std::min<int64_t>(256, ceil_div(n, kChunk));
+    const int64_t per = ceil_div(n, nb);
+    std::vector<GsAlloc> tmp;
+    double* part = (double*)gs_malloc(ctx, sizeof(double) * nb, GS_MEM_SCRATCH, &tmp);
+    if (!part) return GS_ERR_OOM;
+    hipLaunchKernelGGL(k_sum_chunks, dim3((unsigned)nb), dim3(256), 0, ctx->stream, in, n, stride, per, part);
+    hipLaunchKernelGGL(k_sum_f64, dim3(1), dim3(256), 0, ctx->stream, part, nb, 1, out, accumulate);
+    gs_free_all(ctx, &tmp);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -147,8 +147,12 @@ __global__ __launch_bounds__(256) void k_project_flags(CamDev cam, int64_t n, co
     flag[i] = project_geom(cam, means, log_scales, quats, i).ok ? 1u : 0u;
 }
 
-__global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, int deg,
-                                                       const float* __restrict__ means,
+// Compact state of every candidate.  A wavefront covers 64 consecutive
+// Gaussians; their SH rows are contiguous, so the wave stages them in LDS with
+// coalesced loads (row stride 3K + 1 floats keeps the per-lane row reads free
+// of bank conflicts) before each lane evaluates its colour.
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, const float* __restrict__ means,
                                                        const float* __restrict__ log_scales,
                                                        const float* __restrict__ quats,
                                                        const float* __restrict__ logits,
@@ -159,7 +163,20 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, in
                                                        float4* __restrict__ g1, float4* __restrict__ g2,
                                                        int32_t* __restrict__ slot_of)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    constexpr int RS = 3 * K + 1;
+    __shared__ float shs[4][64 * RS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t w0 = (int64_t)blockIdx.x * blockDim.x + wave * 64;
+    const int64_t i = w0 + lane;
+    float* S = shs[wave];
+    {
+        const int64_t lim = (n - w0) * 3 * K;   // floats of this wave's rows that exist
+        const float* src = sh + w0 * 3 * K;
+        for (int q = lane; q < 64 * 3 * K; q += 64)
+            if (q < lim) S[(q / (3 * K)) * RS + q % (3 * K)] = src[q];
+    }
+    gsd::wave_sync();
     if (i >= n) return;
     if (!flag[i]) {
         slot_of[i] = -1;
@@ -172,14 +189,14 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, in
     const float vn = sqrtf((p.vx * p.vx + p.vy * p.vy) + p.vz * p.vz);
     const float dx = p.vx / vn, dy = p.vy / vn, dz = p.vz / vn;
     float Y[16];
-    gsd::sh_basis(deg, dx, dy, dz, Y);
-    const int K = (deg + 1) * (deg + 1);
-    const float* shi = sh + (int64_t)3 * K * i;
+    gsd::sh_basis(DEG, dx, dy, dz, Y);
+    const float* shi = S + lane * RS;
     float rgb[3];
     uint32_t fl = p.flags;
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch) {
         float acc = Y[0] * shi[ch];
+#pragma unroll
         for (int k = 1; k < K; ++k) acc = acc + Y[k] * shi[3 * k + ch];
         acc = acc + 0.5f;
         if (acc < 0.0f) {
@@ -198,7 +215,8 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, in
 // ---------------------------------------------------------------------------
 // Projection backward, one thread per candidate (f32).  Chain rule through
 // each step of the projection, with the forward's clamp decisions (flags).
-__global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand, int deg,
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand,
                                                      const float* __restrict__ means,
                                                      const float* __restrict__ log_scales,
                                                      const float* __restrict__ quats,
@@ -207,14 +225,20 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand,
                                                      const float4* __restrict__ g2s,
                                                      const float* __restrict__ grad2d, float* __restrict__ grad3d)
 {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= n_cand) return;
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    constexpr int F = 11 + 3 * K;
+    // the wave's 64 output rows are contiguous in grad3d: stage them in LDS
+    // (odd row stride) and write them out coalesced at the end
+    constexpr int RS = F | 1;
+    __shared__ float outs[4][64 * RS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t w0 = (int64_t)blockIdx.x * blockDim.x + wave * 64;
+    const int64_t j = w0 + lane;
+    float* out = outs[wave] + lane * RS;
+    if (j < n_cand) {
     const int64_t i = ids[j];
-    const int K = (deg + 1) * (deg + 1);
-    const int F = 11 + 3 * K;
     const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[j].w);
     const float* g = grad2d + 9 * j;
-    float* out = grad3d + (int64_t)F * j;
 
     // forward recomputation
     const float mu[3] = {means[3 * i], means[3 * i + 1], means[3 * i + 2]};
@@ -350,10 +374,11 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand,
     out[10] = g[5] * o * (1.0f - o);
     // colour: rgb = 0.5 + sum_k Y_k(d) sh_k, masked where clamped
     float Y[16], D[16][3];
-    gsd::sh_basis(deg, d[0], d[1], d[2], Y);
-    gsd::sh_basis_grad(deg, d[0], d[1], d[2], D);
+    gsd::sh_basis(DEG, d[0], d[1], d[2], Y);
+    gsd::sh_basis_grad(DEG, d[0], d[1], d[2], D);
     const float* shi = sh + (int64_t)3 * K * i;
     float dd0 = 0.0f, dd1 = 0.0f, dd2 = 0.0f;
+#pragma unroll
     for (int k = 0; k < K; ++k) {
         float t = 0.0f;
 #pragma unroll
@@ -374,6 +399,14 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand,
     out[0] = dmu[0];
     out[1] = dmu[1];
     out[2] = dmu[2];
+    }
+    gsd::wave_sync();
+    const int64_t rows = n_cand - w0 < 64 ? n_cand - w0 : 64;
+    if (rows > 0) {
+        float* dst = grad3d + w0 * F;
+        const float* src = outs[wave];
+        for (int q = lane; q < rows * F; q += 64) dst[q] = src[(q / F) * RS + q % F];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -441,9 +474,17 @@ gs_status launch_project_write(gs_ctx* ctx, const gs_camera* cam, const gs_param
     const int64_t n = p->n;
     if (n > 0) {
         GsTimerScope ts(ctx, "project_write");
-        hipLaunchKernelGGL(k_project_write, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, cd, n,
-                           p->sh_degree, p->means, p->log_scales, p->quats, p->opacity_logits, p->sh, flag, slot,
-                           proj->ids, proj->rect, proj->g0, proj->g1, proj->g2, proj->slot_of);
+        const dim3 grid((unsigned)ceil_div(n, 256));
+#define GS_PW(D) hipLaunchKernelGGL(k_project_write<D>, grid, dim3(256), 0, ctx->stream, cd, n, p->means, \
+                                    p->log_scales, p->quats, p->opacity_logits, p->sh, flag, slot, proj->ids, \
+                                    proj->rect, proj->g0, proj->g1, proj->g2, proj->slot_of)
+        switch (p->sh_degree) {
+        case 0: GS_PW(0); break;
+        case 1: GS_PW(1); break;
+        case 2: GS_PW(2); break;
+        default: GS_PW(3); break;
+        }
+#undef GS_PW
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
@@ -455,9 +496,17 @@ gs_status launch_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params*
     const CamDev cd = make_cam(cam);
     if (proj->n_cand > 0) {
         GsTimerScope ts(ctx, "project_bwd");
-        hipLaunchKernelGGL(k_project_bwd, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream, cd,
-                           proj->n_cand, p->sh_degree, p->means, p->log_scales, p->quats, p->opacity_logits, p->sh,
-                           proj->ids, proj->g2, grad2d, grad3d);
+        const dim3 grid((unsigned)ceil_div(proj->n_cand, 256));
+#define GS_PB(D) hipLaunchKernelGGL(k_project_bwd<D>, grid, dim3(256), 0, ctx->stream, cd, proj->n_cand, p->means, \
+                                    p->log_scales, p->quats, p->opacity_logits, p->sh, proj->ids, proj->g2, grad2d, \
+                                    grad3d)
+        switch (p->sh_degree) {
+        case 0: GS_PB(0); break;
+        case 1: GS_PB(1); break;
+        case 2: GS_PB(2); break;
+        default: GS_PB(3); break;
+        }
+#undef GS_PB
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;

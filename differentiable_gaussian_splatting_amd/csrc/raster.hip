@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
                                                     const float4* __restrict__ g2, float bg0, float bg1, float bg2,
                                                     const float* __restrict__ target, float inv_norm,
                                                     float* __restrict__ image, float* __restrict__ tfinal,
-                                                    uint32_t* __restrict__ last, float* __restrict__ dldc,
+                                                    uint32_t* __restrict__ last, uint8_t* __restrict__ sgn,
                                                     double* __restrict__ l1_part,
                                                     unsigned long long* __restrict__ stats)
 {
@@ -186,9 +186,11 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
         if (target) {
             const float t0 = target[gi], t1 = target[P + gi], t2 = target[2 * P + gi];
             const float d0 = o0 - t0, d1 = o1 - t1, d2 = o2 - t2;   // sign exact in f32
-            dldc[lp] = d0 > 0.0f ? inv_norm : (d0 < 0.0f ? -inv_norm : 0.0f);
-            dldc[g.PL + lp] = d1 > 0.0f ? inv_norm : (d1 < 0.0f ? -inv_norm : 0.0f);
-            dldc[2 * g.PL + lp] = d2 > 0.0f ? inv_norm : (d2 < 0.0f ? -inv_norm : 0.0f);
+            // dL/dout = sgn(out - target) / (3WH): 2 bits per channel, 1 = +, 2 = -
+            const uint32_t c0 = d0 > 0.0f ? 1u : (d0 < 0.0f ? 2u : 0u);
+            const uint32_t c1 = d1 > 0.0f ? 1u : (d1 < 0.0f ? 2u : 0u);
+            const uint32_t c2 = d2 > 0.0f ? 1u : (d2 < 0.0f ? 2u : 0u);
+            sgn[lp] = (uint8_t)(c0 | (c1 << 2) | (c2 << 4));
             l1 = fabs((double)o0 - (double)t0) + fabs((double)o1 - (double)t1) + fabs((double)o2 - (double)t2);
         }
     }
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
                                                     const float4* __restrict__ g2, float bg0, float bg1, float bg2,
                                                     const float* __restrict__ tfinal,
                                                     const uint32_t* __restrict__ last,
-                                                    const float* __restrict__ dldc,
+                                                    const uint8_t* __restrict__ sgn, float inv_norm,
                                                     const float* __restrict__ dl_dimage,
                                                     float* __restrict__ grad2d)
 {
@@ -308,9 +310,11 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
             gr1 = dl_dimage[P + gi];
             gr2 = dl_dimage[2 * P + gi];
         } else {
-            gr0 = dldc[lp];
-            gr1 = dldc[g.PL + lp];
-            gr2 = dldc[2 * g.PL + lp];
+            const uint32_t c = sgn[lp];
+            auto dec = [&](uint32_t code) { return code == 1u ? inv_norm : (code == 2u ? -inv_norm : 0.0f); };
+            gr0 = dec(c & 3u);
+            gr1 = dec((c >> 2) & 3u);
+            gr2 = dec((c >> 4) & 3u);
         }
     }
     float S0 = T * bg0, S1 = T * bg1, S2 = T * bg2;
@@ -401,12 +405,12 @@ gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
         if (stats)
             hipLaunchKernelGGL(k_raster_fwd<true>, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g,
                                bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
-                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->dldc, r->l1_part,
+                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->sgn, r->l1_part,
                                (unsigned long long*)stats);
         else
             hipLaunchKernelGGL(k_raster_fwd<false>, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g,
                                bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
-                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->dldc, r->l1_part,
+                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->sgn, r->l1_part,
                                nullptr);
     }
     GS_HIP(ctx, hipGetLastError());
@@ -418,11 +422,12 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
                             const gs_raster* r, const float* dl_dimage, float* grad2d)
 {
     const LeafGeom g = make_geom(cam, bins, r);
+    const float inv_norm = (float)(1.0 / (3.0 * (double)cam->width * (double)cam->height));
     if (bins->n_tiles > 0) {
         GsTimerScope ts(ctx, "raster_bwd");
         hipLaunchKernelGGL(k_raster_bwd, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g, bins->offsets,
                            bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
-                           r->tfinal, r->last, r->dldc, dl_dimage, grad2d);
+                           r->tfinal, r->last, r->sgn, inv_norm, dl_dimage, grad2d);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;

@@ -239,7 +239,7 @@ def project_bwd(cam, scene, cand, flags, slot_of, grad2d):
     return grad3d
 
 
-DEFAULT_COST = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
+DEFAULT_COST = dict(b_isect=17, b_pixel=9, b_tile=40, b_const=1 << 20)
 
 
 def cost_struct(cost=None) -> Cost_c:
