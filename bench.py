@@ -127,7 +127,7 @@ def main():
         f"leaves {r['n_leaves']}, isect {r['n_isect']}")
 
     kernels = ["project_flags", "project_write", "prefix2d", "scan", "rect_diff", "bin_count", "emit", "radix",
-               "seg_offsets", "plan_split", "leaf_groups", "raster_fwd", "raster_bwd", "project_bwd", "adam"]
+               "seg_offsets", "fine", "plan_split", "leaf_groups", "raster_fwd", "raster_bwd", "project_bwd", "adam"]
     ktimes = {}
     for name in kernels:
         ms, n = B.gs_kernel_time(ctx, name)
@@ -190,6 +190,7 @@ def main():
         "peak_working_set_torch_gib": round(torch_peak / 2 ** 30, 4),
         "n_candidates": r["n_cand"],
         "n_intersections": r["n_isect"],
+        "n_coarse_pairs": wc["cells"],
         "n_leaves": r["n_leaves"],
         "pairs": {"examined": wc["q_f"], "included": wc["q_inc"], "backward": wc["q_b"], "sum_last": wc["sum_last"]},
         "kernel_ms_per_step": {k: round(v["total_ms"], 3) for k, v in ktimes.items()},
@@ -214,15 +215,27 @@ def count_work(B, ctx, cam, params, budget):
     tiles = 0
     radix_elems = 4 * n_cand           # the per-view depth sort: 4 passes over the candidates
     group_entries = 0
-    rects = B.gs_export(ctx, proj, B.PROJ_RECT).cpu().numpy()
+    cells = 0                          # coarse (super-tile of 8 x 8 tiles, candidate) pairs
+    supers = 0
+    rects = B.gs_export(ctx, proj, B.PROJ_RECT).cpu().numpy().astype(np.int64)
     for L in leaves:
         bins, ni = B.gs_bin_sort(ctx, cam, proj, L)
         n_isect += ni
         t_l = (L["tx1"] - L["tx0"]) * (L["ty1"] - L["ty0"])
         tiles += t_l
-        radix_elems += ni * ((max(1, (t_l - 1).bit_length()) + 7) // 8)
-        group_entries += int(((rects[:, 0] < L["tx1"]) & (rects[:, 2] > L["tx0"]) &
-                               (rects[:, 1] < L["ty1"]) & (rects[:, 3] > L["ty0"])).sum())
+        meet = ((rects[:, 0] < L["tx1"]) & (rects[:, 2] > L["tx0"]) &
+                (rects[:, 1] < L["ty1"]) & (rects[:, 3] > L["ty0"]))
+        r = rects[meet]
+        x0 = np.maximum(r[:, 0], L["tx0"]) - L["tx0"]
+        x1 = np.minimum(r[:, 2], L["tx1"]) - L["tx0"]
+        y0 = np.maximum(r[:, 1], L["ty0"]) - L["ty0"]
+        y1 = np.minimum(r[:, 3], L["ty1"]) - L["ty0"]
+        c_l = int((((x1 - 1) >> 3) - (x0 >> 3) + 1) @ (((y1 - 1) >> 3) - (y0 >> 3) + 1))
+        s_l = ((L["tx1"] - L["tx0"] + 7) // 8) * ((L["ty1"] - L["ty0"] + 7) // 8)
+        cells += c_l
+        supers += s_l
+        radix_elems += c_l * ((max(1, (s_l - 1).bit_length()) + 7) // 8) if s_l > 1 else 0
+        group_entries += int(meet.sum())
         ras = B.gs_render_fwd(ctx, cam, proj, bins, stats=stats)
         B.gs_release(ctx, ras)
         B.gs_release(ctx, bins)
@@ -234,7 +247,8 @@ def count_work(B, ctx, cam, params, budget):
     return dict(q_f=int(q[0]), q_inc=int(q[1]), q_b=int(q[3]), sum_last=int(q[2]), n_isect=int(n_isect),
                 n_cand=int(n_cand),
                 n_leaves=len(leaves), tiles=int(tiles), pixels=P, raster_bytes=52 * P,
-                radix_elems=int(radix_elems), group_entries=int(group_entries))
+                radix_elems=int(radix_elems), group_entries=int(group_entries), cells=int(cells),
+                supers=int(supers))
 
 
 def kernel_work(wc, sc):
@@ -243,6 +257,7 @@ def kernel_work(wc, sc):
     K = (sc.sh_degree + 1) ** 2
     F = 11 + 3 * K
     N, Nc, I, T, L = sc.n, wc["n_cand"], wc["n_isect"], wc["tiles"], wc["n_leaves"]
+    C = wc["cells"]
     qf, qi, qb = wc["q_f"], wc["q_inc"], wc["q_b"]
     return {
         "raster_fwd": ("alu", OPS_EXAMINED * (qf - qi) + OPS_INCLUDED_FWD * qi,
@@ -251,10 +266,13 @@ def kernel_work(wc, sc):
                        f"{OPS_EXAMINED} ops x revisited-only pairs + {OPS_INCLUDED_BWD} x included pairs"),
         "radix": ("hbm", 20 * wc["radix_elems"], "per pass and element: read the key twice, the value once, "
                                                    "write key and value (20 B)"),
-        "emit": ("hbm", 8 * I + 24 * wc["group_entries"], "write 8 B (tile, slot) per intersection; read list, "
-                                                          "rectangle, offset per candidate visit"),
-        "bin_count": ("hbm", 24 * wc["group_entries"], "read list entry and rectangle, write the count"),
-        "seg_offsets": ("hbm", 4 * I + 8 * T, "read sorted tile keys, write tile offsets"),
+        "emit": ("hbm", 8 * C + 28 * wc["group_entries"], "write 8 B (super-tile, slot) per coarse pair; read "
+                                                           "list entry, rectangle, offset per candidate visit"),
+        "bin_count": ("hbm", 24 * wc["group_entries"] + 8 * T, "read list entry and rectangle, write the count; "
+                                                             "gather the leaf's tile counts"),
+        "seg_offsets": ("hbm", 4 * C + 8 * wc["supers"], "read sorted super-tile keys, write group offsets"),
+        "fine": ("hbm", 4 * I + 20 * C + 8 * T, "read each coarse entry and its rectangle, the tile offsets; "
+                                                "write one slot per intersection"),
         "rect_diff": ("hbm", 16 * Nc + 4 * T, "read rects, touch the count grid"),
         "project_flags": ("hbm", 40 * N, "read mean, log-scale, quaternion"),
         "project_write": ("hbm", N * (40 + 4 + 12 * K + 8) + Nc * 68, "read parameters, write compact state"),

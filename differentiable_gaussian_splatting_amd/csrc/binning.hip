@@ -1,23 +1,28 @@
-// binning.hip -- tile-intersection counting, (tile, depth, slot) ordering of
-// one leaf's intersections, and the candidate orders they start from.
+// binning.hip -- tile-intersection counting and the (tile, depth, slot)
+// ordered lists of one leaf.
 //
 // BoundedGS page, "01": raster buffers grow with the overlaps of Gaussians
-// and image tiles.  Design (MI355X):
+// and image tiles.  Design (MI355X), two levels:
 //   - once per view the candidates are sorted by depth (stable LSD radix on
 //     the f32 depth bits over slots in ascending order), giving the order
-//     (depth, slot) that every tile list must follow;
-//   - a leaf's candidates are visited in that order; each writes one
-//     (leaf-local tile id, slot) pair per tile of its rectangle inside the
-//     leaf at an offset from an exclusive scan of the per-candidate tile
-//     counts (no atomics; a wavefront shares a wide rectangle so that the
-//     writes stay coalesced);
-//   - a stable radix sort on the tile id alone (ceil(log2 T_L) bits, two
-//     passes for most leaves) then yields each tile's list in (depth, slot)
-//     order, and tile offsets come from the key boundaries.
-// The per-tile counts of a whole grid (for the planner) come from a 2D
-// difference array: four integer atomics per rectangle and a 2D prefix; the
-// cells of the first row and column, which every rectangle clamped at the
-// image border hits, are aggregated in LDS first.
+//     (depth, slot) that every tile list must follow, and the per-tile
+//     candidate counts of the whole grid come from a 2D difference array
+//     (four integer atomics per rectangle, the first row and column
+//     aggregated in LDS) and a 2D prefix;
+//   - a leaf's tile offsets are the exclusive scan of those counts over the
+//     leaf's tiles (row-major inside the leaf);
+//   - coarse level: the leaf is cut into super-tiles of 8 x 8 tiles; the
+//     leaf's candidates, in depth order, emit one (super-tile, slot) pair per
+//     super-tile their rectangle meets (load-balanced, coalesced writes at
+//     offsets from an exclusive scan), and a stable radix sort on the
+//     super-tile id groups them with the depth order kept;
+//   - fine level: one workgroup per super-tile, each wavefront owning 2 x 8
+//     of its tiles, walks the super-tile's group 64 entries at a time; for
+//     each tile a ballot over the 64 rectangles gives the entries that cover
+//     it, which are appended in order at the tile's offset (the rank of an
+//     entry is the number of set ballot bits below its lane).
+// Every tile list therefore comes out in (depth, slot) order, and the number
+// of entries written to a tile equals its count from the difference array.
 #include "gs_device.h"
 #include "gs_internal.h"
 
@@ -65,16 +70,46 @@ __global__ __launch_bounds__(256) void k_rect_diff(int64_t n, const uint32_t* __
     }
 }
 
-// tiles of each listed candidate's rectangle inside the leaf
-__global__ __launch_bounds__(256) void k_count_tiles(int64_t n, const uint32_t* __restrict__ list,
+// Cells of the leaf's grid of 2^sh x 2^sh tiles (aligned to the leaf origin)
+// that the rectangle r meets: origin (cx0, cy0) and extent (w, h) in cells;
+// w = h = 0 when r misses the leaf.
+struct Cells {
+    int cx0, cy0, w, h;
+};
+
+__device__ __forceinline__ Cells leaf_cells(int4 r, int ltx0, int lty0, int ltx1, int lty1, int sh)
+{
+    const int x0 = max(r.x, ltx0) - ltx0, x1 = min(r.z, ltx1) - ltx0;
+    const int y0 = max(r.y, lty0) - lty0, y1 = min(r.w, lty1) - lty0;
+    Cells c{0, 0, 0, 0};
+    if (x0 < x1 && y0 < y1) {
+        c.cx0 = x0 >> sh;
+        c.cy0 = y0 >> sh;
+        c.w = ((x1 - 1) >> sh) - c.cx0 + 1;
+        c.h = ((y1 - 1) >> sh) - c.cy0 + 1;
+    }
+    return c;
+}
+
+// super-tiles of the leaf that each listed candidate's rectangle meets
+__global__ __launch_bounds__(256) void k_count_cells(int64_t n, const uint32_t* __restrict__ list,
                                                      const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
-                                                     int lty1, uint32_t* __restrict__ cnt)
+                                                     int lty1, int sh, uint32_t* __restrict__ cnt)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
-    const int4 r = rect[list[k]];
-    const int w = min(r.z, ltx1) - max(r.x, ltx0), h = min(r.w, lty1) - max(r.y, lty0);
-    cnt[k] = (w > 0 && h > 0) ? (uint32_t)(w * h) : 0u;
+    const Cells c = leaf_cells(rect[list[k]], ltx0, lty0, ltx1, lty1, sh);
+    cnt[k] = (uint32_t)(c.w * c.h);
+}
+
+// per-tile counts of the leaf, row-major inside the leaf, gathered from the
+// counts of the whole grid
+__global__ __launch_bounds__(256) void k_leaf_counts(const int32_t* __restrict__ grid, int TW, int ltx0, int lty0,
+                                                     int TWL, int64_t n_tiles, uint32_t* __restrict__ out)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_tiles) return;
+    out[t] = (uint32_t)grid[(int64_t)(lty0 + t / TWL) * TW + ltx0 + t % TWL];
 }
 
 constexpr int kOB = 256;     // threads of an emission block
@@ -92,17 +127,18 @@ __device__ __forceinline__ int64_t last_le(const uint64_t* __restrict__ a, int64
     return lo;
 }
 
-// (leaf-local tile, slot) pairs of the listed candidates, in list order and
-// row-major tile order within a rectangle.  eoff is the exclusive scan of the
-// per-candidate tile counts (n + 1 entries).  Each block writes a fixed range
+// (super-tile, slot) pairs of the listed candidates, in list order and
+// row-major super-tile order within a rectangle.  eoff is the exclusive scan
+// of the per-candidate super-tile counts (n + 1 entries).  Each block writes a fixed range
 // of kOE consecutive outputs, so the writes are coalesced whatever the
 // rectangle sizes; the candidate of an output is found by binary search in an
 // LDS copy of the block's part of eoff (or in eoff itself when that part is
 // too long, which only long runs of empty candidates cause).
 __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
                                                     const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
-                                                    int lty1, const uint64_t* __restrict__ eoff, uint64_t total,
-                                                    uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
+                                                    int lty1, int sh, int SW, const uint64_t* __restrict__ eoff,
+                                                    uint64_t total, uint32_t* __restrict__ keys,
+                                                    uint32_t* __restrict__ vals)
 {
     __shared__ uint64_t se[kOE + 1];
     __shared__ int64_t s_c0, s_m;
@@ -121,7 +157,6 @@ __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* _
     if (in_lds)
         for (int64_t k = threadIdx.x; k < m; k += kOB) se[k] = eoff[c0 + k];
     __syncthreads();
-    const int TWL = ltx1 - ltx0;
     for (uint64_t o = o0 + threadIdx.x; o < o1; o += kOB) {
         int64_t c;
         uint64_t start;
@@ -134,12 +169,135 @@ __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* _
             start = eoff[c];
         }
         const uint32_t j = list[c];
-        const int4 r = rect[j];
-        const int x0 = max(r.x, ltx0) - ltx0, y0 = max(r.y, lty0) - lty0;
-        const int w = min(r.z, ltx1) - ltx0 - x0;
+        const Cells cl = leaf_cells(rect[j], ltx0, lty0, ltx1, lty1, sh);
         const uint32_t t = (uint32_t)(o - start);
-        keys[o] = (uint32_t)((y0 + (int)(t / (uint32_t)w)) * TWL + x0 + (int)(t % (uint32_t)w));
+        keys[o] = (uint32_t)((cl.cy0 + (int)(t / (uint32_t)cl.w)) * SW + cl.cx0 + (int)(t % (uint32_t)cl.w));
         vals[o] = j;
+    }
+}
+
+// Fine level.  A super-tile's group (slots in depth order) is cut into
+// segments of kSeg entries; a work item is one segment, processed by one
+// workgroup whose wavefront w owns tile rows 2w and 2w + 1 of the super-tile
+// (8 x 8 tiles at leaf-local tile (sx << 3, sy << 3)).  Three passes keep the
+// work balanced however long a group is:
+//   count: per item and tile, the entries of the segment that cover the tile;
+//   scan:  per tile, those counts become the write positions of the items in
+//          segment order, starting at the tile's offset;
+//   write: each item appends its covering entries at its positions.
+// A segment is walked 64 entries at a time: a ballot over the 64 rectangles
+// per tile gives the covering entries, and the rank of an entry is the number
+// of set bits below its lane.
+constexpr int kSuperShift = 3;
+constexpr int kSeg = 512;
+
+struct FineItem {
+    int sc;            // super-tile
+    uint64_t b, e;     // segment [b, e) of the group array
+    int64_t item;      // work item index
+};
+
+// item -> (super-tile, segment); false for the surplus items of the grid
+__device__ __forceinline__ bool fine_item(const uint64_t* __restrict__ soff, const uint32_t* __restrict__ ioff,
+                                          int n_super, FineItem& it)
+{
+    const uint32_t i = blockIdx.x;
+    if (i >= ioff[n_super]) return false;
+    int lo = 0, hi = n_super - 1;            // last super-tile with ioff <= i
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ioff[mid] <= i) lo = mid;
+        else hi = mid - 1;
+    }
+    it.sc = lo;
+    it.item = i;
+    it.b = soff[lo] + (uint64_t)(i - ioff[lo]) * kSeg;
+    it.e = min<uint64_t>(soff[lo + 1], it.b + kSeg);
+    return true;
+}
+
+template <bool WRITE>
+__global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int THL, int SW, int n_super,
+                                              const uint64_t* __restrict__ soff, const uint32_t* __restrict__ ioff,
+                                              const uint32_t* __restrict__ group, const int4* __restrict__ rect,
+                                              uint64_t* __restrict__ pos, uint64_t n_values,
+                                              uint32_t* __restrict__ values)
+{
+    FineItem it;
+    if (!fine_item(soff, ioff, n_super, it)) return;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int lx0 = (it.sc % SW) << kSuperShift, ly0 = ((it.sc / SW) << kSuperShift) + 2 * wave;
+    if (ly0 >= THL) return;
+    const int nx = min(8, TWL - lx0), ny = min(2, THL - ly0);
+    const int gx0 = ltx0 + lx0, gy0 = lty0 + ly0;
+    uint64_t* wp = pos + it.item * 64 + wave * 16;   // this wave's 16 tiles of the item
+    uint64_t cur[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cur[q] = WRITE ? wp[q] : 0;
+    const uint64_t b = it.b, e = it.e;
+    uint32_t s_c = 0, s_n = 0;
+    int4 r_c = make_int4(0, 0, 0, 0);
+    if (b + lane < e) s_c = group[b + lane];
+    if (b + lane < e) r_c = rect[s_c];
+    if (b + 64 + lane < e) s_n = group[b + 64 + lane];
+    for (uint64_t k = b; k < e; k += 64) {
+        int4 r_n = make_int4(0, 0, 0, 0);
+        uint32_t s_nn = 0;
+        if (k + 64 + lane < e) r_n = rect[s_n];
+        if (k + 128 + lane < e) s_nn = group[k + 128 + lane];
+        const bool ok = k + lane < e;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int c = q & 7, rr = q >> 3;
+            if (c >= nx || rr >= ny) continue;
+            const int gx = gx0 + c, gy = gy0 + rr;
+            const bool cov = ok && r_c.x <= gx && gx < r_c.z && r_c.y <= gy && gy < r_c.w;
+            const uint64_t m = gsd::ballot(cov);
+            if (WRITE && cov) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                const uint64_t p = cur[q] + below;
+                if (p < n_values) values[p] = s_c;   // always true when the counts agree
+            }
+            cur[q] += (uint64_t)__builtin_popcountll(m);
+        }
+        s_c = s_n;
+        r_c = r_n;
+        s_n = s_nn;
+    }
+    if (!WRITE && lane < 16) {
+        uint64_t v = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (lane == q) v = cur[q];
+        wp[lane] = v;
+    }
+}
+
+// segments per super-tile
+__global__ __launch_bounds__(256) void k_fine_segs(const uint64_t* __restrict__ soff, int n_super,
+                                                   uint32_t* __restrict__ nseg)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < n_super) nseg[s] = (uint32_t)((soff[s + 1] - soff[s] + kSeg - 1) / kSeg);
+}
+
+// per (super-tile, tile): item counts -> write positions, in item order
+__global__ __launch_bounds__(256) void k_fine_scan(int TWL, int THL, int SW, int n_super,
+                                                   const uint32_t* __restrict__ ioff, const uint64_t* __restrict__ toff,
+                                                   uint64_t* __restrict__ pos)
+{
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= (int64_t)n_super * 64) return;
+    const int sc = (int)(g >> 6), j = (int)(g & 63);
+    const int lx = ((sc % SW) << kSuperShift) + (j & 7), ly = ((sc / SW) << kSuperShift) + (j >> 3);
+    if (lx >= TWL || ly >= THL) return;
+    uint64_t p = toff[(int64_t)ly * TWL + lx];
+    for (uint32_t i = ioff[sc]; i < ioff[sc + 1]; ++i) {
+        const uint64_t c = pos[(int64_t)i * 64 + j];
+        pos[(int64_t)i * 64 + j] = p;
+        p += c;
     }
 }
 
@@ -190,6 +348,11 @@ __global__ void k_export_keys(int64_t n_tiles, int ltx0, int lty0, int TWL, int 
 
 }  // namespace
 
+int super_cols(gs_tile_rect leaf) { return (leaf.tx1 - leaf.tx0 + (1 << kSuperShift) - 1) >> kSuperShift; }
+int super_rows(gs_tile_rect leaf) { return (leaf.ty1 - leaf.ty0 + (1 << kSuperShift) - 1) >> kSuperShift; }
+int64_t super_cells(gs_tile_rect leaf) { return (int64_t)super_cols(leaf) * super_rows(leaf); }
+int super_shift() { return kSuperShift; }
+
 int bits_for(int64_t n_keys)
 {
     int b = 0;
@@ -210,26 +373,71 @@ gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, 
     return GS_OK;
 }
 
-gs_status launch_count_tiles(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+gs_status launch_count_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                              int64_t n_list, uint32_t* cnt)
 {
     if (n_list > 0) {
         GsTimerScope ts(ctx, "bin_count");
-        hipLaunchKernelGGL(k_count_tiles, dim3((unsigned)ceil_div(n_list, 256)), dim3(256), 0, ctx->stream, n_list,
-                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, cnt);
+        hipLaunchKernelGGL(k_count_cells, dim3((unsigned)ceil_div(n_list, 256)), dim3(256), 0, ctx->stream, n_list,
+                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift, cnt);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }
 
-gs_status launch_emit_pairs(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+gs_status launch_leaf_counts(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, uint32_t* out)
+{
+    const int TWL = leaf.tx1 - leaf.tx0;
+    const int64_t n = (int64_t)TWL * (leaf.ty1 - leaf.ty0);
+    if (n > 0) {
+        GsTimerScope ts(ctx, "bin_count");
+        hipLaunchKernelGGL(k_leaf_counts, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream,
+                           proj->tile_cnt, proj->TW, leaf.tx0, leaf.ty0, TWL, n, out);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                             int64_t n_list, const uint64_t* eoff, uint64_t total, uint32_t* keys, uint32_t* vals)
 {
     if (n_list > 0 && total > 0) {
         GsTimerScope ts(ctx, "emit");
         hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div((int64_t)total, kOE)), dim3(kOB), 0, ctx->stream,
-                           n_list, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, eoff, total, keys, vals);
+                           n_list, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift,
+                           super_cols(leaf), eoff, total, keys, vals);
     }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells)
+{
+    return super_cells(leaf) + (int64_t)((n_cells + kSeg - 1) / kSeg);
+}
+
+gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
+                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* nseg,
+                            uint32_t* ioff, uint64_t* pos, uint64_t n_values, uint32_t* values)
+{
+    const int n_super = (int)super_cells(leaf);
+    const int64_t items = fine_items_bound(leaf, n_cells);
+    if (n_super <= 0 || n_cells == 0) return GS_OK;
+    const int TWL = leaf.tx1 - leaf.tx0, THL = leaf.ty1 - leaf.ty0, SW = super_cols(leaf);
+    {
+        GsTimerScope ts(ctx, "fine");
+        hipLaunchKernelGGL(k_fine_segs, dim3((unsigned)ceil_div(n_super, 256)), dim3(256), 0, ctx->stream, soff,
+                           n_super, nseg);
+    }
+    gs_status st = launch_scan_u32_to_u32(ctx, nseg, ioff, n_super);
+    if (st != GS_OK) return st;
+    GsTimerScope ts(ctx, "fine");
+    hipLaunchKernelGGL(k_fine<false>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
+                       SW, n_super, soff, ioff, group, proj->rect, pos, n_values, values);
+    hipLaunchKernelGGL(k_fine_scan, dim3((unsigned)ceil_div((int64_t)n_super * 64, 256)), dim3(256), 0, ctx->stream,
+                       TWL, THL, SW, n_super, ioff, toff, pos);
+    hipLaunchKernelGGL(k_fine<true>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
+                       SW, n_super, soff, ioff, group, proj->rect, pos, n_values, values);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -182,19 +182,36 @@ static gs_status check_params(gs_ctx* ctx, const gs_params* p)
 
 // leaf -> candidate groups of a plan (leaves on the device), attached to
 // proj; every group keeps the candidates' (depth, slot) order
+// Candidates per tile of the whole grid, made once per projection.
+static gs_status ensure_tile_counts(gs_ctx* ctx, gs_proj* proj)
+{
+    if (proj->tile_cnt) return GS_OK;
+    int32_t* g = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * (int64_t)proj->TW * proj->TH, GS_MEM_PROJ, &proj->allocs);
+    if (!g) return GS_ERR_OOM;
+    const gs_status st = launch_tile_counts(ctx, proj, g);
+    if (st != GS_OK) {
+        gs_free_one(ctx, &proj->allocs, g);
+        return st;
+    }
+    proj->tile_cnt = g;
+    return GS_OK;
+}
+
 static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ldev, int32_t nl)
 {
     gs_free_all(ctx, &proj->plan_allocs);
     proj->plan.clear();
     proj->plan_off.clear();
+    proj->plan_cells.clear();
     proj->plan_cands = nullptr;
     const int64_t T = (int64_t)proj->TW * proj->TH;
     const int64_t nc = proj->n_cand;
     std::vector<GsAlloc> tmp;
     gs_status st = GS_OK;
     std::vector<gs_leaf> plan(nl);
-    std::vector<uint64_t> hoff(nl + 1, 0);
+    std::vector<uint64_t> hoff(nl + 1, 0), hcells(nl, 0);
     uint64_t G = 0;
+    uint64_t* cells = nullptr;
     bool second = false;
     uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
     uint64_t* segoff = nullptr;
@@ -212,11 +229,17 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
     v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
     segoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
-    if (!k0 || !k1 || !v0 || !v1 || !segoff) { st = GS_ERR_OOM; goto out; }
+    cells = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * nl, GS_MEM_SCRATCH, &tmp);
+    if (!k0 || !k1 || !v0 || !v1 || !segoff || !cells) { st = GS_ERR_OOM; goto out; }
+    if ((st = launch_fill_u32(ctx, (uint32_t*)cells, 0u, 2 * (int64_t)nl)) != GS_OK) goto out;
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, goff, k0, v0)) != GS_OK) goto out;
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
     if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, segoff)) != GS_OK) goto out;
+    if ((st = launch_leaf_cells(ctx, proj, ldev, (int64_t)G, second ? k1 : k0, second ? v1 : v0, cells)) != GS_OK)
+        goto out;
     e = hipMemcpyAsync(hoff.data(), segoff, sizeof(uint64_t) * (nl + 1), hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(hcells.data(), cells, sizeof(uint64_t) * nl, hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess) e = hipMemcpyAsync(plan.data(), ldev, sizeof(gs_leaf) * nl, hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
@@ -224,6 +247,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     proj->plan_cands = second ? v1 : v0;
     proj->plan.swap(plan);
     proj->plan_off.swap(hoff);
+    proj->plan_cells.swap(hcells);
 out:
     gs_free_all(ctx, &tmp);
     if (st != GS_OK) {
@@ -231,22 +255,27 @@ out:
         proj->plan_cands = nullptr;
         proj->plan.clear();
         proj->plan_off.clear();
+        proj->plan_cells.clear();
     }
     return st;
 }
 
 // The candidate group of a planned leaf, or (nullptr, 0) when the leaf is
 // not part of the plan.  *isect gets the leaf's intersection count when the
-// plan's estimate determines it (est = bI I + bP P + bT T + b0, bI > 0), else -1.
-static const uint32_t* plan_group(const gs_proj* proj, gs_tile_rect leaf, int64_t* n, int64_t* isect)
+// plan's estimate determines it (est = bI I + bP P + bT T + b0, bI > 0), else
+// -1; *cells the number of its coarse (super-tile, candidate) pairs.
+static const uint32_t* plan_group(const gs_proj* proj, gs_tile_rect leaf, int64_t* n, int64_t* isect,
+                                  int64_t* cells)
 {
     *n = 0;
     *isect = -1;
+    *cells = -1;
     if (!proj->plan_cands) return nullptr;
     for (size_t k = 0; k < proj->plan.size(); ++k) {
         const gs_leaf& L = proj->plan[k];
         if (L.tx0 == leaf.tx0 && L.ty0 == leaf.ty0 && L.tx1 == leaf.tx1 && L.ty1 == leaf.ty1) {
             *n = (int64_t)(proj->plan_off[k + 1] - proj->plan_off[k]);
+            *cells = (int64_t)proj->plan_cells[k];
             const gs_cost_model& c = proj->plan_cost;
             const uint64_t P = (uint64_t)(std::min(L.tx1 * 16, proj->W) - L.tx0 * 16) *
                                (uint64_t)(std::min(L.ty1 * 16, proj->H) - L.ty0 * 16);
@@ -470,17 +499,17 @@ gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj,
     const int64_t T = (int64_t)proj->TW * proj->TH;
     const int32_t cap = (int32_t)std::min<int64_t>(std::max<int32_t>(max_leaves, 1), T);
     std::vector<GsAlloc> tmp;
+    if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) return st;
     uint64_t* sat = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (proj->TW + 1) * (int64_t)(proj->TH + 1),
                                          GS_MEM_SCRATCH, &tmp);
-    int32_t* diff = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * T, GS_MEM_SCRATCH, &tmp);
     gs_leaf* ldev = (gs_leaf*)gs_malloc(ctx, sizeof(gs_leaf) * cap, GS_MEM_SCRATCH, &tmp);
     int32_t* small = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * 2, GS_MEM_SCRATCH, &tmp);
     int32_t hv[2] = {0, 0};
-    if (!sat || !diff || !ldev || !small) {
+    if (!sat || !ldev || !small) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
-    st = launch_plan(ctx, proj, sat, diff, budget_bytes, &cm, ldev, cap, small, small + 1);
+    st = launch_plan(ctx, proj, sat, budget_bytes, &cm, ldev, cap, small, small + 1);
     if (st == GS_OK) st = readback(ctx, small, sizeof(hv), hv);
     if (st == GS_OK && max_leaves > 0 && hv[0] > 0) {
         const int32_t nw = std::min(hv[0], max_leaves);
@@ -524,48 +553,81 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     b->THL = leaf.ty1 - leaf.ty0;
     b->n_tiles = (int64_t)b->TWL * b->THL;
     std::vector<GsAlloc> tmp;
-    uint64_t I = 0;
+    uint64_t I = 0, C = 0;
     bool second = false;
-    int64_t n_list = 0, known = -1;
-    const uint32_t* list = plan_group(proj, leaf, &n_list, &known);
+    int64_t n_list = 0, known = -1, known_cells = -1;
+    const int64_t n_super = super_cells(leaf);
+    uint32_t *cnt = nullptr, *lc = nullptr, *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
+    uint64_t *eoff = nullptr, *soff = nullptr;
+    const uint32_t* list = plan_group(proj, leaf, &n_list, &known, &known_cells);
     if (!list) {               // not a planned leaf: visit every candidate
         list = proj->order;
         n_list = proj->n_cand;
     }
-    uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
-    uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n_list, 1), GS_MEM_RASTER, &tmp);
-    uint64_t* eoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (n_list + 1), GS_MEM_RASTER, &tmp);
+    if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) goto fail;
+    // tile offsets: exclusive scan of the leaf's per-tile counts
+    b->offsets = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (b->n_tiles + 1), GS_MEM_RASTER, &b->allocs);
+    lc = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * b->n_tiles, GS_MEM_RASTER, &tmp);
+    if (!b->offsets || !lc) { st = GS_ERR_OOM; goto fail; }
+    if ((st = launch_leaf_counts(ctx, proj, leaf, lc)) != GS_OK) goto fail;
+    if ((st = launch_scan_u32_to_u64(ctx, lc, b->offsets, b->n_tiles)) != GS_OK) goto fail;
+    gs_free_one(ctx, &tmp, lc);
+    // coarse level: (super-tile, slot) pairs, grouped by a stable sort
+    cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n_list, 1), GS_MEM_RASTER, &tmp);
+    eoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (n_list + 1), GS_MEM_RASTER, &tmp);
     if (!cnt || !eoff) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_count_tiles(ctx, proj, leaf, list, n_list, cnt)) != GS_OK) goto fail;
+    if ((st = launch_count_cells(ctx, proj, leaf, list, n_list, cnt)) != GS_OK) goto fail;
     if ((st = launch_scan_u32_to_u64(ctx, cnt, eoff, n_list)) != GS_OK) goto fail;
     gs_free_one(ctx, &tmp, cnt);   // stream-ordered: the scan has consumed it
-    if (known >= 0) {
-        I = (uint64_t)known;    // from the plan's summed-area table: no read-back
-    } else if ((st = readback(ctx, eoff + n_list, sizeof(uint64_t), &I)) != GS_OK) {
+    if (known >= 0 && known_cells >= 0) {
+        I = (uint64_t)known;       // from the plan: no read-back
+        C = (uint64_t)known_cells;
+    } else {
+        uint64_t hv[2] = {0, 0};
+        if ((st = readback(ctx, b->offsets + b->n_tiles, sizeof(uint64_t), &hv[0])) != GS_OK) goto fail;
+        if ((st = readback(ctx, eoff + n_list, sizeof(uint64_t), &hv[1])) != GS_OK) goto fail;
+        I = hv[0];
+        C = hv[1];
+    }
+    if (I >= (1ull << 32) || C >= (1ull << 32)) {
+        st = gs_fail(ctx, GS_ERR_OVERFLOW, "leaf has %llu intersections / %llu super-tile pairs (limit 2^32)",
+                     (unsigned long long)I, (unsigned long long)C);
         goto fail;
     }
-    if (I >= (1ull << 32)) { st = gs_fail(ctx, GS_ERR_OVERFLOW, "leaf has %llu >= 2^32 intersections", (unsigned long long)I); goto fail; }
     b->n_isect = (int64_t)I;
     {
-        const uint64_t ni = std::max<uint64_t>(I, 1);
-        k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &tmp);
-        v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &b->allocs);
+        const uint64_t nc = std::max<uint64_t>(C, 1);
+        k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
+        v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
         if (!k0 || !v0) { st = GS_ERR_OOM; goto fail; }
     }
-    if ((st = launch_emit_pairs(ctx, proj, leaf, list, n_list, eoff, I, k0, v0)) != GS_OK) goto fail;
+    if ((st = launch_emit_cells(ctx, proj, leaf, list, n_list, eoff, C, k0, v0)) != GS_OK) goto fail;
     gs_free_one(ctx, &tmp, eoff);
     {
-        const uint64_t ni = std::max<uint64_t>(I, 1);
-        k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &tmp);
-        v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * ni, GS_MEM_RASTER, &b->allocs);
+        const uint64_t nc = std::max<uint64_t>(C, 1);
+        k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
+        v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
         if (!k1 || !v1) { st = GS_ERR_OOM; goto fail; }
     }
-    if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)I, bits_for(b->n_tiles), &second)) != GS_OK) goto fail;
-    b->offsets = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (b->n_tiles + 1), GS_MEM_RASTER, &b->allocs);
-    if (!b->offsets) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)I, b->n_tiles, b->offsets)) != GS_OK) goto fail;
-    gs_free_one(ctx, &b->allocs, second ? v0 : v1);
-    b->values = second ? v1 : v0;
+    if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)C, bits_for(n_super), &second)) != GS_OK) goto fail;
+    soff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (n_super + 1), GS_MEM_RASTER, &tmp);
+    if (!soff) { st = GS_ERR_OOM; goto fail; }
+    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)C, n_super, soff)) != GS_OK) goto fail;
+    gs_free_one(ctx, &tmp, second ? k1 : k0);
+    gs_free_one(ctx, &tmp, second ? k0 : k1);
+    gs_free_one(ctx, &tmp, second ? v0 : v1);
+    // fine level: per-tile lists at the tile offsets
+    {
+        const int64_t items = fine_items_bound(leaf, C);
+        b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(I, 1), GS_MEM_RASTER, &b->allocs);
+        uint32_t* nseg = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * n_super, GS_MEM_RASTER, &tmp);
+        uint32_t* ioff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n_super + 1), GS_MEM_RASTER, &tmp);
+        uint64_t* pos = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * 64 * items, GS_MEM_RASTER, &tmp);
+        if (!b->values || !nseg || !ioff || !pos) { st = GS_ERR_OOM; goto fail; }
+        if ((st = launch_fine_lists(ctx, proj, leaf, soff, second ? v1 : v0, C, b->offsets, nseg, ioff, pos, I,
+                                    b->values)) != GS_OK)
+            goto fail;
+    }
     gs_free_all(ctx, &tmp);
     *out = b;
     *n_isect = b->n_isect;

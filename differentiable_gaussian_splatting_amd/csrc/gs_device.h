@@ -166,6 +166,12 @@ __device__ __forceinline__ double wave_sum_d(double v)
     return v;
 }
 
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) v += (uint64_t)__shfl_xor((unsigned long long)v, o, 64);
+    return v;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     for (int o = 32; o > 0; o >>= 1) {

@@ -58,10 +58,12 @@ struct gs_proj : GsHandle {
     float4* g2 = nullptr;         // [n_cand] b, depth, radius, flags (bits)
     int32_t* slot_of = nullptr;   // [n] slot or -1
     uint32_t* order = nullptr;    // [n_cand] slots sorted by (depth, slot)
+    int32_t* tile_cnt = nullptr;  // [TH][TW] candidates per tile (made on first use)
     // leaf plan of the view (set by gs_plan_leaves): the candidates whose
     // rectangle meets each leaf, so that binning a leaf visits only those
     std::vector<gs_leaf> plan;
     std::vector<uint64_t> plan_off;   // host copy of the group offsets [plan.size() + 1]
+    std::vector<uint64_t> plan_cells; // per leaf: (super-tile, candidate) pairs of its coarse level
     uint32_t* plan_cands = nullptr;   // device [plan_off.back()] candidate slots, depth order per group
     std::vector<GsAlloc> plan_allocs;
     gs_cost_model plan_cost{};        // cost model the plan was made with
@@ -131,10 +133,27 @@ gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
 // list: candidate slots to visit (NULL: all n_cand), n_list entries
 gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                            int64_t n_list, int32_t* diff);
-gs_status launch_count_tiles(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+// super-tiles (8 x 8 tiles, aligned to the leaf origin) of a leaf
+int super_cols(gs_tile_rect leaf);
+int super_rows(gs_tile_rect leaf);
+int64_t super_cells(gs_tile_rect leaf);
+int super_shift();
+// per listed candidate: super-tiles of the leaf its rectangle meets
+gs_status launch_count_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                              int64_t n_list, uint32_t* cnt);
-gs_status launch_emit_pairs(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
+// per-tile candidate counts of the leaf (row-major in the leaf) from proj->tile_cnt
+gs_status launch_leaf_counts(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, uint32_t* out);
+// (super-tile, slot) pairs at the offsets eoff (exclusive scan of the counts)
+gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                             int64_t n_list, const uint64_t* eoff, uint64_t total, uint32_t* keys, uint32_t* vals);
+// per-tile lists from the super-tile groups (soff: group offsets, toff: tile offsets)
+// Work items of the fine level (segments of the super-tile groups), an upper
+// bound for n_cells coarse pairs; scratch: nseg u32 [n_super], ioff u32
+// [n_super + 1], pos u64 [items * 64]
+int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells);
+gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
+                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* nseg,
+                            uint32_t* ioff, uint64_t* pos, uint64_t n_values, uint32_t* values);
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets);
 gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
 gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);
@@ -152,14 +171,19 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
                             const gs_raster* r, const float* dl_dimage, float* grad2d);
 
 // planner.hip
-gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, int32_t* diff, uint64_t budget,
-                      const gs_cost_model* cost, gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev,
-                      int32_t* overflow_dev);
+// candidates per tile of the whole grid ([TH][TW], from the rectangles)
+gs_status launch_tile_counts(gs_ctx* ctx, const gs_proj* proj, int32_t* grid);
+// leaf plan from proj->tile_cnt
+gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t budget, const gs_cost_model* cost,
+                      gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev, int32_t* overflow_dev);
 
 // leaf -> candidate groups (planner.hip)
 gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot);
 gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
                             const int32_t* lot, uint32_t* cnt, const uint64_t* off, uint32_t* keys, uint32_t* vals);
+// cells[L] += coarse (super-tile, candidate) pairs of the grouped entries (leaf_of sorted)
+gs_status launch_leaf_cells(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int64_t n,
+                            const uint32_t* leaf_of, const uint32_t* slot, uint64_t* cells);
 
 // loss.hip
 gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,

@@ -148,17 +148,23 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a, const uint64_
 
 }  // namespace
 
-gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, int32_t* diff, uint64_t budget,
-                      const gs_cost_model* cost, gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev,
-                      int32_t* over_dev)
+gs_status launch_tile_counts(gs_ctx* ctx, const gs_proj* proj, int32_t* grid)
+{
+    const int TW = proj->TW, TH = proj->TH;
+    gs_status st = launch_fill_u32(ctx, (uint32_t*)grid, 0u, (int64_t)TW * TH);
+    if (st != GS_OK) return st;
+    gs_tile_rect all{0, 0, TW, TH};
+    if ((st = launch_rect_diff(ctx, proj, all, nullptr, 0, grid)) != GS_OK) return st;
+    return launch_prefix2d_i32(ctx, grid, TH, TW);
+}
+
+gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t budget, const gs_cost_model* cost,
+                      gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev, int32_t* over_dev)
 {
     const int TW = proj->TW, TH = proj->TH;
     const int64_t T = (int64_t)TW * TH;
-    gs_status st = launch_fill_u32(ctx, (uint32_t*)diff, 0u, T);
-    if (st != GS_OK) return st;
-    gs_tile_rect all{0, 0, TW, TH};
-    if ((st = launch_rect_diff(ctx, proj, all, nullptr, 0, diff)) != GS_OK) return st;
-    if ((st = launch_prefix2d_i32(ctx, diff, TH, TW)) != GS_OK) return st;
+    const int32_t* diff = proj->tile_cnt;
+    gs_status st = GS_OK;
     const int64_t S = (int64_t)(TW + 1) * (TH + 1);
     hipLaunchKernelGGL(k_counts_to_sat, dim3((unsigned)ceil_div(S, 256)), dim3(256), 0, ctx->stream, diff, TW, TH, sat);
     if ((st = launch_prefix2d_u64(ctx, sat, TH + 1, TW + 1)) != GS_OK) return st;
@@ -247,7 +253,50 @@ __global__ __launch_bounds__(256) void k_leaf_pairs(int64_t n, const uint32_t* _
     if (!EMIT) cnt[k] = m;
 }
 
+// per leaf: the (super-tile, candidate) pairs of its coarse level, summed
+// over the grouped (leaf, slot) entries (sorted by leaf, so a wavefront's
+// entries nearly always share one leaf and add with one atomic)
+__global__ __launch_bounds__(256) void k_leaf_cells(int64_t n, const uint32_t* __restrict__ leaf_of,
+                                                    const uint32_t* __restrict__ slot, const int4* __restrict__ rect,
+                                                    const gs_leaf* __restrict__ leaves, int sh,
+                                                    unsigned long long* __restrict__ cells)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool ok = k < n;
+    uint32_t L = 0;
+    uint64_t c = 0;
+    if (ok) {
+        L = leaf_of[k];
+        const gs_leaf lf = leaves[L];
+        const int4 r = rect[slot[k]];
+        const int x0 = max(r.x, lf.tx0) - lf.tx0, x1 = min(r.z, lf.tx1) - lf.tx0;
+        const int y0 = max(r.y, lf.ty0) - lf.ty0, y1 = min(r.w, lf.ty1) - lf.ty0;
+        if (x0 < x1 && y0 < y1)
+            c = (uint64_t)(((x1 - 1) >> sh) - (x0 >> sh) + 1) * (uint64_t)(((y1 - 1) >> sh) - (y0 >> sh) + 1);
+    }
+    const uint32_t L0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)L);
+    const bool same = gsd::ballot(ok && L != L0) == 0;
+    if (same) {
+        const uint64_t tot = gsd::wave_sum_u64(c);
+        if (gsd::lane_id() == 0 && tot) atomicAdd(&cells[L0], (unsigned long long)tot);
+    } else if (ok && c) {
+        atomicAdd(&cells[L], (unsigned long long)c);
+    }
+}
+
 }  // namespace
+
+gs_status launch_leaf_cells(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int64_t n,
+                            const uint32_t* leaf_of, const uint32_t* slot, uint64_t* cells)
+{
+    if (n > 0) {
+        GsTimerScope ts(ctx, "leaf_groups");
+        hipLaunchKernelGGL(k_leaf_cells, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, leaf_of,
+                           slot, proj->rect, leaves_dev, super_shift(), (unsigned long long*)cells);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
 
 gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot)
 {
