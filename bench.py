@@ -156,7 +156,8 @@ def main():
                                    frac=round(ach / PEAK_HBM_GBS, 4), work=unit_desc)
     dom = max((k for k in rooflines), key=lambda k: ktimes[k]["total_ms"])
     roofline = dict(rooflines[dom])
-    roofline.update(traffic=None, kernel=dom, avg_launch_ms=round(ktimes[dom]["avg_ms"], 4),
+    roofline.update(traffic=measured_traffic(args.workload, dom), traffic_unit="HBM bytes per launch (counters)",
+                    kernel=dom, avg_launch_ms=round(ktimes[dom]["avg_ms"], 4),
                     launches_per_step=ktimes[dom]["launches"])
     # whole-step HBM fraction: the algorithmic bytes of every stage over the step time
     step_bytes = sum(a for (b, a, _) in work.values() if b == "hbm") + wc["raster_bytes"]
@@ -279,6 +280,35 @@ def kernel_work(wc, sc):
         "project_bwd": ("hbm", Nc * (36 + 48 + 40 + 4 + 12 * K + 4 * F + 4), "read 2D grads, state, params; write 3D grads"),
         "adam": ("hbm", 24 * N * F + 4 * F * Nc + 4 * N, "read/write params, m, v; read compact grads"),
     }
+
+
+RASTER_SOURCES = ("differentiable_gaussian_splatting_amd/csrc/raster.hip",
+                  "differentiable_gaussian_splatting_amd/csrc/gs_device.h")
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of a raster kernel from the committed counter
+    summary (calibrated FETCH_SIZE + WRITE_SIZE), or None when there is none
+    for this workload or the kernel sources have changed since it was taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"raster_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in RASTER_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    for line in open(path):
+        parts = line.split()
+        if not parts or parts[0].startswith("#"):
+            continue
+        fields[parts[0]] = parts[1:]
+    if fields.get("source_sha256_16", [None])[0] != h.hexdigest()[:16] or kernel not in fields:
+        return None
+    kv = fields[kernel]
+    return int(dict(zip(kv[0::2], kv[1::2]))["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, window):
