@@ -55,11 +55,10 @@ LeafGeom make_geom(const gs_camera* cam, const gs_bins* b, const gs_raster* r)
     return g;
 }
 
-struct Staged {        // one wavefront's staged batch
-    float4 a[64];      // x, y, -A/2, -B
-    float4 b[64];      // -C/2, opacity, r, g
-    float c[64];       // b
-    uint32_t slot[64];
+struct Staged {        // one wavefront's staged batch (entry j at byte 16 j of each array,
+    float4 a[64];      // so one address register serves all three reads)
+    float4 b[64];      // x, y, -A/2, -B | -C/2, opacity, r, g
+    float4 c[64];      // b, slot (bits), -, -
 };
 
 // true when no pixel centre of the box [bx0, bx0+7] x [by0, by0+7] can
@@ -115,9 +114,9 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
     uint32_t lastn = 0, n_eval = 0, n_inc = 0, ev_at_last = 0;
-    bool done = !inside;
+    bool active = inside;
     for (uint64_t base = start; base < end; base += 64) {
-        if (gsd::ballot(!done) == 0) break;
+        if (gsd::ballot(active) == 0) break;
         const uint64_t e = base + lane;
         bool keep = false;
         if (e < end) {
@@ -125,45 +124,50 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
             const float4 a = g0[s], b = g1[s];
             S.a[lane] = a;
             S.b[lane] = b;
-            S.c[lane] = g2[s].x;
+            S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
             keep = !cull_box(a, b, bx0, by0);
         }
         uint64_t mask = gsd::ballot(keep);
         gsd::wave_sync();
-        if (!done) {
-            while (mask) {
-                const int j = __builtin_ctzll(mask);
-                mask &= mask - 1;
-                if (STATS) ++n_eval;
-                const float4 a = S.a[j];
-                const float4 b = S.b[j];
-                const float dx = pxc - a.x, dy = pyc - a.y;
-                float t = a.w * dy;
-                t = __builtin_fmaf(a.z, dx, t);
-                float u = b.x * dy;
-                u = u * dy;
-                const float power = __builtin_fmaf(t, dx, u);
-                if (power > 0.0f || power < -87.0f) continue;
-                const float G = gsd::exp_cw_core(power);
-                const float av = b.y * G;
-                const float alpha = av > gsd::kAlphaMax ? gsd::kAlphaMax : av;
-                if (alpha < gsd::kAlphaMin) continue;
-                const float Tn = T * (1.0f - alpha);
-                if (Tn < gsd::kTMin) {
-                    done = true;
-                    break;
-                }
-                const float w = alpha * T;
-                C0 = __builtin_fmaf(b.z, w, C0);
-                C1 = __builtin_fmaf(b.w, w, C1);
-                C2 = __builtin_fmaf(S.c[j], w, C2);
-                T = Tn;
-                lastn = (uint32_t)(base - start) + (uint32_t)j + 1u;
-                if (STATS) {
-                    ++n_inc;
-                    ev_at_last = n_eval;
-                }
+        const uint32_t n0 = (uint32_t)(base - start) + 1u;
+        // Branch-free over the lanes: every lane evaluates the entry and the
+        // per-lane decisions become selects, so the wavefront issues one
+        // straight run of instructions per entry.  A lane's values for an
+        // entry it includes are computed in exactly the order given above.
+        while (mask) {
+            const int j = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const float4 a = S.a[j];
+            const float4 b = S.b[j];
+            const float dx = pxc - a.x, dy = pyc - a.y;
+            float t = a.w * dy;
+            t = __builtin_fmaf(a.z, dx, t);
+            float u = b.x * dy;
+            u = u * dy;
+            const float power = __builtin_fmaf(t, dx, u);
+            const bool pok = !(power > 0.0f || power < -87.0f);
+            // exp of the clamped exponent: equal to exp(power) on every lane
+            // that can include the entry, finite on the others
+            const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
+            const float av = b.y * G;
+            const float alpha = av > gsd::kAlphaMax ? gsd::kAlphaMax : av;
+            const bool inc = active && pok && !(alpha < gsd::kAlphaMin);
+            const float ae = inc ? alpha : 0.0f;
+            const float Tn = T * (1.0f - ae);
+            const bool stop = inc && Tn < gsd::kTMin;
+            const bool contrib = inc && !stop;
+            if (STATS) {
+                n_eval += active ? 1u : 0u;
+                n_inc += contrib ? 1u : 0u;
+                ev_at_last = contrib ? n_eval : ev_at_last;
             }
+            active = active && !stop;
+            const float w = contrib ? ae * T : 0.0f;   // fma(x, 0, C) = C exactly
+            C0 = __builtin_fmaf(b.z, w, C0);
+            C1 = __builtin_fmaf(b.w, w, C1);
+            C2 = __builtin_fmaf(S.c[j].x, w, C2);
+            T = contrib ? Tn : T;
+            lastn = contrib ? n0 + (uint32_t)j : lastn;
         }
         gsd::wave_sync();
     }
@@ -317,7 +321,9 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
             gr2 = dec((c >> 4) & 3u);
         }
     }
-    float S0 = T * bg0, S1 = T * bg1, S2 = T * bg2;
+    // GS = sum_ch dL/dout_ch * (colour behind the current entry, ch); it
+    // starts as the background seen through T_final
+    float GS = T * (gr0 * bg0 + gr1 * bg1 + gr2 * bg2);
     const uint32_t maxl = gsd::wave_max_u32(lst);
 
     for (int64_t hi = maxl; hi > 0; hi -= 64) {
@@ -327,66 +333,66 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
         if (lane < cnt) {
             const uint32_t s = values[start + lo + lane];
             const float4 a = g0[s], b = g1[s];
-            S.slot[lane] = s;
             S.a[lane] = a;
             S.b[lane] = b;
-            S.c[lane] = g2[s].x;
+            S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
             keep = !cull_box(a, b, bx0, by0);
         }
         uint64_t mask = gsd::ballot(keep);
         gsd::wave_sync();
+        // Branch-free over the lanes, as in the forward: the inclusion of an
+        // entry is re-derived with the forward's exact f32 operations, and the
+        // partials of lanes that do not include it are zero.
         while (mask) {
             const int j = 63 - __builtin_clzll(mask);
             mask &= ~(1ull << j);
             const uint32_t n = (uint32_t)(lo + j);
-            float p[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            bool contrib = false;
-            if (n < lst) {
-                const float4 a = S.a[j];
-                const float4 b = S.b[j];
-                const float cb = S.c[j];
-                const float dx = pxc - a.x, dy = pyc - a.y;
-                float t = a.w * dy;
-                t = __builtin_fmaf(a.z, dx, t);
-                float u = b.x * dy;
-                u = u * dy;
-                const float power = __builtin_fmaf(t, dx, u);
-                if (!(power > 0.0f || power < -87.0f)) {
-                    const float G = gsd::exp_cw_core(power);
-                    const float av = b.y * G;
-                    const bool clamped = av > gsd::kAlphaMax;
-                    const float alpha = clamped ? gsd::kAlphaMax : av;
-                    if (!(alpha < gsd::kAlphaMin)) {
-                        contrib = true;
-                        const float om = 1.0f - alpha;
-                        const float rom = __builtin_amdgcn_rcpf(om);
-                        T = T * rom;                      // T before this entry
-                        const float w = alpha * T;
-                        p[6] = gr0 * w;
-                        p[7] = gr1 * w;
-                        p[8] = gr2 * w;
-                        const float dal = gr0 * (b.z * T - S0 * rom) + gr1 * (b.w * T - S1 * rom) +
-                                          gr2 * (cb * T - S2 * rom);
-                        S0 = __builtin_fmaf(b.z, w, S0);
-                        S1 = __builtin_fmaf(b.w, w, S1);
-                        S2 = __builtin_fmaf(cb, w, S2);
-                        if (!clamped) {
-                            const float dpw = dal * av;   // d alpha / d power = o G
-                            p[5] = dal * G;
-                            // A = -2 a.z, B = -a.w, C = -2 b.x
-                            p[2] = -0.5f * dx * dx * dpw;
-                            p[3] = -dx * dy * dpw;
-                            p[4] = -0.5f * dy * dy * dpw;
-                            p[0] = (-2.0f * a.z * dx - a.w * dy) * dpw;
-                            p[1] = (-2.0f * b.x * dy - a.w * dx) * dpw;
-                        }
-                    }
-                }
-            }
+            const float4 a = S.a[j];
+            const float4 b = S.b[j];
+            const float2 cs = *reinterpret_cast<const float2*>(&S.c[j]);
+            const float cb = cs.x;
+            const float dx = pxc - a.x, dy = pyc - a.y;
+            float t = a.w * dy;
+            t = __builtin_fmaf(a.z, dx, t);
+            const float u1 = b.x * dy;
+            const float u = u1 * dy;
+            const float power = __builtin_fmaf(t, dx, u);
+            const bool pok = !(power > 0.0f || power < -87.0f);
+            const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
+            const float av = b.y * G;
+            const bool clamped = av > gsd::kAlphaMax;
+            const float alpha = clamped ? gsd::kAlphaMax : av;
+            const bool contrib = n < lst && pok && !(alpha < gsd::kAlphaMin);
             if (gsd::ballot(contrib) == 0) continue;
+            // T before this entry = T after it / (1 - alpha)
+            const float rom = contrib ? __builtin_amdgcn_rcpf(1.0f - alpha) : 1.0f;
+            T = T * rom;
+            const float w = contrib ? alpha * T : 0.0f;
+            // dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha))
+            const float grgb = __builtin_fmaf(gr2, cb, __builtin_fmaf(gr1, b.w, gr0 * b.z));
+            const float dal = contrib ? __builtin_fmaf(T, grgb, -(rom * GS)) : 0.0f;
+            GS = __builtin_fmaf(grgb, w, GS);
+            float p[9];
+            p[6] = gr0 * w;
+            p[7] = gr1 * w;
+            p[8] = gr2 * w;
+            // through alpha = o G (zero when alpha is clamped)
+            p[5] = clamped ? 0.0f : dal * G;
+            const float ndpw = clamped ? 0.0f : -(dal * av);   // -dL/dpower
+            // power = -(A dx^2 + C dy^2)/2 - B dx dy with A = -2 a.z, B = -a.w,
+            // C = -2 b.x, dx = px - x, dy = py - y:
+            //   dL/dx = (A dx + B dy) dL/dpower = (a.z dx + t) (-dL/dpower)
+            //   dL/dy = (C dy + B dx) dL/dpower = (2 b.x dy + a.w dx) (-dL/dpower)
+            //   dL/dA = -dx^2/2 dL/dpower, dL/dB = -dx dy dL/dpower, dL/dC = -dy^2/2 dL/dpower
+            p[0] = __builtin_fmaf(a.z, dx, t) * ndpw;
+            p[1] = __builtin_fmaf(a.w, dx, u1 + u1) * ndpw;
+            const float h = 0.5f * ndpw;
+            p[2] = (dx * h) * dx;
+            p[3] = (dx * ndpw) * dy;
+            p[4] = (dy * h) * dy;
             int v;
             const float r = wave_reduce9(p, lane, &v);
-            if (v >= 0) unsafeAtomicAdd(&grad2d[(int64_t)S.slot[j] * 9 + v], r);
+            if (v >= 0) unsafeAtomicAdd(&grad2d[(int64_t)__builtin_bit_cast(uint32_t, cs.y) * 9 + v], r);
         }
         gsd::wave_sync();
     }
