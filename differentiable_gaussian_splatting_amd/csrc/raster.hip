@@ -279,6 +279,22 @@ __device__ __forceinline__ float wave_reduce9(const float* p, int lane, int* vid
     return d;
 }
 
+// Backward, one workgroup per tile.  The four wavefronts walk the tile's
+// list together, 64 entries per batch from the last entry any pixel of the
+// tile included: the batch is staged once in LDS (16 entries per wavefront),
+// each wavefront culls it against its own 8 x 8 box and reduces the 9
+// partials of each entry over its lanes into an LDS row, and after a barrier
+// the 256 threads add the four rows of each (entry, value) and issue one
+// atomic add per nonzero sum -- a quarter of the atomics of per-wavefront
+// adds.  Staging and partial rows are double-buffered, so a batch costs two
+// workgroup barriers: one after staging, one before the sums.
+struct BwdShared {
+    Staged st[2];
+    float4 red[2][64 * 9];               // [entry * 9 + value] -> the 4 wavefronts' sums
+    unsigned long long wmask[2][4];      // entries each wavefront wrote in the batch
+    uint32_t maxl[4];
+};
+
 __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* __restrict__ offsets,
                                                     const uint32_t* __restrict__ values,
                                                     const float4* __restrict__ g0, const float4* __restrict__ g1,
@@ -289,9 +305,10 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
                                                     const float* __restrict__ dl_dimage,
                                                     float* __restrict__ grad2d)
 {
-    __shared__ Staged st[4];
+    __shared__ BwdShared sh;
     const int lt = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int tx = g.ltx0 + lt % g.TWL, ty = g.lty0 + lt / g.TWL;
     const int sx0 = tx * 16 + (wave & 1) * 8, sy0 = ty * 16 + (wave >> 1) * 8;
     const int px = sx0 + (lane & 7), py = sy0 + (lane >> 3);
@@ -299,7 +316,6 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
     const float bx0 = (float)sx0 + 0.5f, by0 = (float)sy0 + 0.5f;
     const uint64_t start = offsets[lt];
-    Staged& S = st[wave];
 
     float T = 1.0f, gr0 = 0.0f, gr1 = 0.0f, gr2 = 0.0f;
     uint32_t lst = 0;
@@ -324,22 +340,35 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
     // GS = sum_ch dL/dout_ch * (colour behind the current entry, ch); it
     // starts as the background seen through T_final
     float GS = T * (gr0 * bg0 + gr1 * bg1 + gr2 * bg2);
-    const uint32_t maxl = gsd::wave_max_u32(lst);
+    {
+        const uint32_t m = gsd::wave_max_u32(lst);
+        if (lane == 0) sh.maxl[wave] = m;
+    }
+    __syncthreads();
+    const int64_t maxl = (int64_t)max(max(sh.maxl[0], sh.maxl[1]), max(sh.maxl[2], sh.maxl[3]));
 
-    for (int64_t hi = maxl; hi > 0; hi -= 64) {
+    // stage entries [lo, hi) of the tile's list into buffer b (16 per wavefront)
+    auto stage = [&](int b, int64_t hi) {
+        const int64_t lo = hi > 64 ? hi - 64 : 0;
+        const int e = wave * 16 + lane;
+        if (lane < 16 && lo + e < hi) {
+            const uint32_t s = values[start + lo + e];
+            sh.st[b].a[e] = g0[s];
+            sh.st[b].b[e] = g1[s];
+            sh.st[b].c[e] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
+        }
+    };
+    if (maxl > 0) stage(0, maxl);
+    int b = 0;
+    for (int64_t hi = maxl; hi > 0; hi -= 64, b ^= 1) {
         const int64_t lo = hi > 64 ? hi - 64 : 0;
         const int cnt = (int)(hi - lo);
+        __syncthreads();                       // batch staged; previous sums done
+        Staged& S = sh.st[b];
         bool keep = false;
-        if (lane < cnt) {
-            const uint32_t s = values[start + lo + lane];
-            const float4 a = g0[s], b = g1[s];
-            S.a[lane] = a;
-            S.b[lane] = b;
-            S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
-            keep = !cull_box(a, b, bx0, by0);
-        }
+        if (lane < cnt) keep = !cull_box(S.a[lane], S.b[lane], bx0, by0);
         uint64_t mask = gsd::ballot(keep);
-        gsd::wave_sync();
+        uint64_t wrote = 0;
         // Branch-free over the lanes, as in the forward: the inclusion of an
         // entry is re-derived with the forward's exact f32 operations, and the
         // partials of lanes that do not include it are zero.
@@ -348,18 +377,17 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
             mask &= ~(1ull << j);
             const uint32_t n = (uint32_t)(lo + j);
             const float4 a = S.a[j];
-            const float4 b = S.b[j];
-            const float2 cs = *reinterpret_cast<const float2*>(&S.c[j]);
-            const float cb = cs.x;
+            const float4 bb = S.b[j];
+            const float cb = S.c[j].x;
             const float dx = pxc - a.x, dy = pyc - a.y;
             float t = a.w * dy;
             t = __builtin_fmaf(a.z, dx, t);
-            const float u1 = b.x * dy;
+            const float u1 = bb.x * dy;
             const float u = u1 * dy;
             const float power = __builtin_fmaf(t, dx, u);
             const bool pok = !(power > 0.0f || power < -87.0f);
             const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
-            const float av = b.y * G;
+            const float av = bb.y * G;
             const bool clamped = av > gsd::kAlphaMax;
             const float alpha = clamped ? gsd::kAlphaMax : av;
             const bool contrib = n < lst && pok && !(alpha < gsd::kAlphaMin);
@@ -369,7 +397,7 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
             T = T * rom;
             const float w = contrib ? alpha * T : 0.0f;
             // dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha))
-            const float grgb = __builtin_fmaf(gr2, cb, __builtin_fmaf(gr1, b.w, gr0 * b.z));
+            const float grgb = __builtin_fmaf(gr2, cb, __builtin_fmaf(gr1, bb.w, gr0 * bb.z));
             const float dal = contrib ? __builtin_fmaf(T, grgb, -(rom * GS)) : 0.0f;
             GS = __builtin_fmaf(grgb, w, GS);
             float p[9];
@@ -392,9 +420,31 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
             p[4] = (dy * h) * dy;
             int v;
             const float r = wave_reduce9(p, lane, &v);
-            if (v >= 0) unsafeAtomicAdd(&grad2d[(int64_t)__builtin_bit_cast(uint32_t, cs.y) * 9 + v], r);
+            if (v >= 0) {
+                float* row = reinterpret_cast<float*>(&sh.red[b][j * 9 + v]);
+                row[wave] = r;
+            }
+            wrote |= 1ull << j;
         }
-        gsd::wave_sync();
+        if (lane == 0) sh.wmask[b][wave] = wrote;
+        __syncthreads();                       // rows of the batch written
+        // sums of the four rows, one atomic per nonzero (entry, value)
+        const unsigned long long m0 = sh.wmask[b][0], m1 = sh.wmask[b][1];
+        const unsigned long long m2 = sh.wmask[b][2], m3 = sh.wmask[b][3];
+        for (int o = tid; o < cnt * 9; o += 256) {
+            const int j = o / 9;
+            const float4 q = sh.red[b][o];
+            float sum = 0.0f;
+            sum += ((m0 >> j) & 1ull) ? q.x : 0.0f;
+            sum += ((m1 >> j) & 1ull) ? q.y : 0.0f;
+            sum += ((m2 >> j) & 1ull) ? q.z : 0.0f;
+            sum += ((m3 >> j) & 1ull) ? q.w : 0.0f;
+            if (sum != 0.0f) {
+                const uint32_t slot = __builtin_bit_cast(uint32_t, S.c[j].y);
+                unsafeAtomicAdd(&grad2d[(int64_t)slot * 9 + (o - j * 9)], sum);
+            }
+        }
+        if (hi - 64 > 0) stage(b ^ 1, hi - 64);
     }
 }
 
