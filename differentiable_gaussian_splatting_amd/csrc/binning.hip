@@ -112,65 +112,37 @@ __global__ __launch_bounds__(256) void k_leaf_counts(const int32_t* __restrict__
     out[t] = (uint32_t)grid[(int64_t)(lty0 + t / TWL) * TW + ltx0 + t % TWL];
 }
 
-constexpr int kOB = 256;     // threads of an emission block
-constexpr int kOE = 4096;    // outputs of an emission block
-
-__device__ __forceinline__ int64_t last_le(const uint64_t* __restrict__ a, int64_t n, uint64_t v)
-{
-    // largest k in [0, n) with a[k] <= v (a non-decreasing, a[0] <= v)
-    int64_t lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (a[mid] <= v) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
+constexpr int kOB = 256;     // threads (and candidates) of an emission block
 
 // (super-tile, slot) pairs of the listed candidates, in list order and
-// row-major super-tile order within a rectangle.  eoff is the exclusive scan
-// of the per-candidate super-tile counts (n + 1 entries).  Each block writes a fixed range
-// of kOE consecutive outputs, so the writes are coalesced whatever the
-// rectangle sizes; the candidate of an output is found by binary search in an
-// LDS copy of the block's part of eoff (or in eoff itself when that part is
-// too long, which only long runs of empty candidates cause).
+// row-major super-tile order within a rectangle.  eoff[k] - ebase is the
+// first output of candidate k (exclusive scan of the per-candidate super-tile
+// counts, n + 1 entries).  Block = kOB consecutive candidates: their outputs
+// form one contiguous range, which the block's threads write at consecutive
+// positions (coalesced), each finding its candidate by binary search in an
+// LDS copy of the block's offsets.
 __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
                                                     const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
-                                                    int lty1, int sh, int SW, const uint64_t* __restrict__ eoff,
-                                                    uint64_t total, uint32_t* __restrict__ keys,
+                                                    int lty1, int sh, int SW, const uint32_t* __restrict__ eoff,
+                                                    uint32_t ebase, uint32_t* __restrict__ keys,
                                                     uint32_t* __restrict__ vals)
 {
-    __shared__ uint64_t se[kOE + 1];
-    __shared__ int64_t s_c0, s_m;
-    const uint64_t o0 = (uint64_t)blockIdx.x * kOE;
-    const uint64_t o1 = min<uint64_t>(total, o0 + kOE);
-    if (o0 >= o1) return;
-    if (threadIdx.x == 0) {
-        const int64_t c0 = last_le(eoff, n + 1, o0);
-        const int64_t c1 = last_le(eoff, n + 1, o1 - 1);
-        s_c0 = c0;
-        s_m = c1 - c0 + 1;
-    }
+    __shared__ uint32_t se[kOB + 1];
+    const int64_t c0 = (int64_t)blockIdx.x * kOB;
+    const int m = (int)min<int64_t>(kOB, n - c0);
+    for (int k = threadIdx.x; k <= m; k += kOB) se[k] = eoff[c0 + k] - ebase;
     __syncthreads();
-    const int64_t c0 = s_c0, m = s_m;
-    const bool in_lds = m <= kOE + 1;
-    if (in_lds)
-        for (int64_t k = threadIdx.x; k < m; k += kOB) se[k] = eoff[c0 + k];
-    __syncthreads();
-    for (uint64_t o = o0 + threadIdx.x; o < o1; o += kOB) {
-        int64_t c;
-        uint64_t start;
-        if (in_lds) {
-            const int64_t k = last_le(se, m, o);
-            c = c0 + k;
-            start = se[k];
-        } else {
-            c = c0 + last_le(eoff + c0, m, o);
-            start = eoff[c];
+    const uint32_t o0 = se[0], o1 = se[m];
+    for (uint32_t o = o0 + threadIdx.x; o < o1; o += kOB) {
+        int lo = 0, hi = m - 1;                 // last k with se[k] <= o
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (se[mid] <= o) lo = mid;
+            else hi = mid - 1;
         }
-        const uint32_t j = list[c];
+        const uint32_t j = list[c0 + lo];
         const Cells cl = leaf_cells(rect[j], ltx0, lty0, ltx1, lty1, sh);
-        const uint32_t t = (uint32_t)(o - start);
+        const uint32_t t = o - se[lo];
         keys[o] = (uint32_t)((cl.cy0 + (int)(t / (uint32_t)cl.w)) * SW + cl.cx0 + (int)(t % (uint32_t)cl.w));
         vals[o] = j;
     }
@@ -199,32 +171,28 @@ struct FineItem {
 
 // item -> (super-tile, segment); false for the surplus items of the grid
 __device__ __forceinline__ bool fine_item(const uint64_t* __restrict__ soff, const uint32_t* __restrict__ ioff,
-                                          int n_super, FineItem& it)
+                                          const uint32_t* __restrict__ item_sc, int n_super, FineItem& it)
 {
     const uint32_t i = blockIdx.x;
     if (i >= ioff[n_super]) return false;
-    int lo = 0, hi = n_super - 1;            // last super-tile with ioff <= i
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (ioff[mid] <= i) lo = mid;
-        else hi = mid - 1;
-    }
-    it.sc = lo;
+    const int sc = (int)item_sc[i];
+    it.sc = sc;
     it.item = i;
-    it.b = soff[lo] + (uint64_t)(i - ioff[lo]) * kSeg;
-    it.e = min<uint64_t>(soff[lo + 1], it.b + kSeg);
+    it.b = soff[sc] + (uint64_t)(i - ioff[sc]) * kSeg;
+    it.e = min<uint64_t>(soff[sc + 1], it.b + kSeg);
     return true;
 }
 
 template <bool WRITE>
 __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int THL, int SW, int n_super,
                                               const uint64_t* __restrict__ soff, const uint32_t* __restrict__ ioff,
+                                              const uint32_t* __restrict__ item_sc,
                                               const uint32_t* __restrict__ group, const int4* __restrict__ rect,
                                               uint64_t* __restrict__ pos, uint64_t n_values,
                                               uint32_t* __restrict__ values)
 {
     FineItem it;
-    if (!fine_item(soff, ioff, n_super, it)) return;
+    if (!fine_item(soff, ioff, item_sc, n_super, it)) return;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int lx0 = (it.sc % SW) << kSuperShift, ly0 = ((it.sc / SW) << kSuperShift) + 2 * wave;
@@ -275,12 +243,38 @@ __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int T
     }
 }
 
-// segments per super-tile
-__global__ __launch_bounds__(256) void k_fine_segs(const uint64_t* __restrict__ soff, int n_super,
-                                                   uint32_t* __restrict__ nseg)
+// One workgroup: segments per super-tile, their exclusive scan ioff
+// [n_super + 1] and the item -> super-tile map.
+__global__ __launch_bounds__(1024) void k_fine_items(const uint64_t* __restrict__ soff, int n_super,
+                                                     uint32_t* __restrict__ ioff, uint32_t* __restrict__ item_sc)
 {
-    const int s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s < n_super) nseg[s] = (uint32_t)((soff[s + 1] - soff[s] + kSeg - 1) / kSeg);
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t carry;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int s0 = 0; s0 < n_super; s0 += 1024) {
+        const int s = s0 + tid;
+        const uint32_t ns = s < n_super ? (uint32_t)((soff[s + 1] - soff[s] + kSeg - 1) / kSeg) : 0u;
+        uint32_t x = ns;                       // inclusive wave scan
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t u = __shfl_up(x, o, 64);
+            if (lane >= o) x += u;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        uint32_t before = carry;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        const uint32_t first = before + x - ns;
+        if (s < n_super) {
+            ioff[s] = first;
+            for (uint32_t q = 0; q < ns; ++q) item_sc[first + q] = (uint32_t)s;
+        }
+        __syncthreads();
+        if (tid == 1023) carry = first + ns;
+        __syncthreads();
+    }
+    if (tid == 0) ioff[n_super] = carry;
 }
 
 // per (super-tile, tile): item counts -> write positions, in item order
@@ -399,13 +393,14 @@ gs_status launch_leaf_counts(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf
 }
 
 gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
-                            int64_t n_list, const uint64_t* eoff, uint64_t total, uint32_t* keys, uint32_t* vals)
+                            int64_t n_list, const uint32_t* eoff, uint32_t ebase, uint64_t total, uint32_t* keys,
+                            uint32_t* vals)
 {
     if (n_list > 0 && total > 0) {
         GsTimerScope ts(ctx, "emit");
-        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div((int64_t)total, kOE)), dim3(kOB), 0, ctx->stream,
-                           n_list, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift,
-                           super_cols(leaf), eoff, total, keys, vals);
+        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div(n_list, kOB)), dim3(kOB), 0, ctx->stream, n_list,
+                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift, super_cols(leaf),
+                           eoff, ebase, keys, vals);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
@@ -417,27 +412,21 @@ int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells)
 }
 
 gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
-                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* nseg,
+                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* item_sc,
                             uint32_t* ioff, uint64_t* pos, uint64_t n_values, uint32_t* values)
 {
     const int n_super = (int)super_cells(leaf);
     const int64_t items = fine_items_bound(leaf, n_cells);
     if (n_super <= 0 || n_cells == 0) return GS_OK;
     const int TWL = leaf.tx1 - leaf.tx0, THL = leaf.ty1 - leaf.ty0, SW = super_cols(leaf);
-    {
-        GsTimerScope ts(ctx, "fine");
-        hipLaunchKernelGGL(k_fine_segs, dim3((unsigned)ceil_div(n_super, 256)), dim3(256), 0, ctx->stream, soff,
-                           n_super, nseg);
-    }
-    gs_status st = launch_scan_u32_to_u32(ctx, nseg, ioff, n_super);
-    if (st != GS_OK) return st;
     GsTimerScope ts(ctx, "fine");
+    hipLaunchKernelGGL(k_fine_items, dim3(1), dim3(1024), 0, ctx->stream, soff, n_super, ioff, item_sc);
     hipLaunchKernelGGL(k_fine<false>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                       SW, n_super, soff, ioff, group, proj->rect, pos, n_values, values);
+                       SW, n_super, soff, ioff, item_sc, group, proj->rect, pos, n_values, values);
     hipLaunchKernelGGL(k_fine_scan, dim3((unsigned)ceil_div((int64_t)n_super * 64, 256)), dim3(256), 0, ctx->stream,
                        TWL, THL, SW, n_super, ioff, toff, pos);
     hipLaunchKernelGGL(k_fine<true>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                       SW, n_super, soff, ioff, group, proj->rect, pos, n_values, values);
+                       SW, n_super, soff, ioff, item_sc, group, proj->rect, pos, n_values, values);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

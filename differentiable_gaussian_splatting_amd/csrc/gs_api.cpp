@@ -136,7 +136,10 @@ static bool handle_ok(const gs_ctx* ctx, const void* h, uint32_t magic)
 static void destroy_handle(gs_ctx* ctx, GsHandle* h)
 {
     gs_free_all(ctx, &h->allocs);
-    if (h->magic == kMagicProj) gs_free_all(ctx, &static_cast<gs_proj*>(h)->plan_allocs);
+    if (h->magic == kMagicProj) {
+        gs_free_all(ctx, &static_cast<gs_proj*>(h)->plan_allocs);
+        gs_free_all(ctx, &static_cast<gs_proj*>(h)->plan_retired);
+    }
     const uint32_t magic = h->magic;
     h->magic = 0;
     // delete through the concrete type
@@ -197,96 +200,142 @@ static gs_status ensure_tile_counts(gs_ctx* ctx, gs_proj* proj)
     return GS_OK;
 }
 
-static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ldev, int32_t nl)
+static void clear_plan(gs_ctx* ctx, gs_proj* proj, bool retire)
 {
-    gs_free_all(ctx, &proj->plan_allocs);
+    // bins of an earlier plan may still point at its tile offsets: keep its
+    // memory until the projection is released
+    if (retire)
+        for (auto& a : proj->plan_allocs) proj->plan_retired.push_back(a);
+    else
+        gs_free_all(ctx, &proj->plan_allocs);
+    proj->plan_allocs.clear();
     proj->plan.clear();
     proj->plan_off.clear();
     proj->plan_cells.clear();
+    proj->plan_cbase.clear();
+    proj->plan_tbase.clear();
     proj->plan_cands = nullptr;
+    proj->plan_coff = nullptr;
+    proj->plan_toff = nullptr;
+}
+
+// Groups the candidates by planned leaf and precomputes, for the whole view,
+// what binning a planned leaf needs besides its own kernels: the leaf's
+// candidates in depth order, the offsets of their coarse pairs and the leaf's
+// tile offsets.
+static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ldev, int32_t nl)
+{
+    clear_plan(ctx, proj, true);
     const int64_t T = (int64_t)proj->TW * proj->TH;
     const int64_t nc = proj->n_cand;
     std::vector<GsAlloc> tmp;
     gs_status st = GS_OK;
     std::vector<gs_leaf> plan(nl);
-    std::vector<uint64_t> hoff(nl + 1, 0), hcells(nl, 0);
+    std::vector<uint64_t> hoff(nl + 1, 0), hcells(nl, 0), tbase(nl + 1, 0);
+    std::vector<uint32_t> hlc(2 * (size_t)nl, 0), cbase(nl, 0);
     uint64_t G = 0;
-    uint64_t* cells = nullptr;
     bool second = false;
-    uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
-    uint64_t* segoff = nullptr;
+    uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr, *ccnt = nullptr, *coff = nullptr;
+    uint32_t* lcells = nullptr;
+    uint64_t *segoff = nullptr, *dtbase = nullptr, *toff = nullptr;
     hipError_t e;
     int32_t* lot = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * T, GS_MEM_SCRATCH, &tmp);
     uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(nc, 1), GS_MEM_SCRATCH, &tmp);
     uint64_t* goff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nc + 1), GS_MEM_SCRATCH, &tmp);
     if (!lot || !cnt || !goff) { st = GS_ERR_OOM; goto out; }
+    e = hipMemcpyAsync(plan.data(), ldev, sizeof(gs_leaf) * nl, hipMemcpyDeviceToHost, ctx->stream);
+    if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
     if ((st = launch_leaf_map(ctx, ldev, nl, proj->TW, lot)) != GS_OK) goto out;
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
     if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
-    if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;
+    if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;   // also completes the plan copy
+    for (int32_t L = 0; L < nl; ++L)
+        tbase[L + 1] = tbase[L] + (uint64_t)(plan[L].tx1 - plan[L].tx0) * (uint64_t)(plan[L].ty1 - plan[L].ty0) + 1;
     k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
     v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
     segoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
-    cells = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * nl, GS_MEM_SCRATCH, &tmp);
-    if (!k0 || !k1 || !v0 || !v1 || !segoff || !cells) { st = GS_ERR_OOM; goto out; }
-    if ((st = launch_fill_u32(ctx, (uint32_t*)cells, 0u, 2 * (int64_t)nl)) != GS_OK) goto out;
+    ccnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
+    coff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (G + 1), GS_MEM_PROJ, &proj->plan_allocs);
+    lcells = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * 2 * nl, GS_MEM_SCRATCH, &tmp);
+    dtbase = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
+    toff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
+    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !lcells || !dtbase || !toff) {
+        st = GS_ERR_OOM;
+        goto out;
+    }
+    e = hipMemcpyAsync(dtbase, tbase.data(), sizeof(uint64_t) * (nl + 1), hipMemcpyHostToDevice, ctx->stream);
+    if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, goff, k0, v0)) != GS_OK) goto out;
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
     if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, segoff)) != GS_OK) goto out;
-    if ((st = launch_leaf_cells(ctx, proj, ldev, (int64_t)G, second ? k1 : k0, second ? v1 : v0, cells)) != GS_OK)
+    if ((st = launch_plan_offsets(ctx, proj, ldev, nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0, segoff, ccnt,
+                                  coff, lcells, dtbase, toff)) != GS_OK)
         goto out;
     e = hipMemcpyAsync(hoff.data(), segoff, sizeof(uint64_t) * (nl + 1), hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess)
-        e = hipMemcpyAsync(hcells.data(), cells, sizeof(uint64_t) * nl, hipMemcpyDeviceToHost, ctx->stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(plan.data(), ldev, sizeof(gs_leaf) * nl, hipMemcpyDeviceToHost, ctx->stream);
+        e = hipMemcpyAsync(hlc.data(), lcells, sizeof(uint32_t) * 2 * nl, hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
+    for (int32_t L = 0; L < nl; ++L) {
+        cbase[L] = hlc[2 * (size_t)L];
+        hcells[L] = hlc[2 * (size_t)L + 1];
+    }
     gs_free_one(ctx, &proj->plan_allocs, second ? v0 : v1);
     proj->plan_cands = second ? v1 : v0;
+    proj->plan_coff = coff;
+    proj->plan_toff = toff;
     proj->plan.swap(plan);
     proj->plan_off.swap(hoff);
     proj->plan_cells.swap(hcells);
+    proj->plan_cbase.swap(cbase);
+    proj->plan_tbase.swap(tbase);
 out:
     gs_free_all(ctx, &tmp);
-    if (st != GS_OK) {
-        gs_free_all(ctx, &proj->plan_allocs);
-        proj->plan_cands = nullptr;
-        proj->plan.clear();
-        proj->plan_off.clear();
-        proj->plan_cells.clear();
-    }
+    if (st != GS_OK) clear_plan(ctx, proj, false);
     return st;
 }
 
-// The candidate group of a planned leaf, or (nullptr, 0) when the leaf is
-// not part of the plan.  *isect gets the leaf's intersection count when the
-// plan's estimate determines it (est = bI I + bP P + bT T + b0, bI > 0), else
-// -1; *cells the number of its coarse (super-tile, candidate) pairs.
-static const uint32_t* plan_group(const gs_proj* proj, gs_tile_rect leaf, int64_t* n, int64_t* isect,
-                                  int64_t* cells)
+// What binning a leaf of the current plan can take from it; found = false
+// when the leaf is not part of the plan.
+struct PlanLeaf {
+    bool found = false;
+    const uint32_t* list = nullptr;   // candidates meeting the leaf, depth order
+    int64_t n = 0;
+    int64_t isect = -1;               // from the plan's estimate, or -1
+    int64_t cells = 0;                // coarse pairs
+    const uint32_t* eoff = nullptr;   // their offsets (subtract ebase)
+    uint32_t ebase = 0;
+    uint64_t* toff = nullptr;         // tile offsets [T_L + 1]
+};
+
+static PlanLeaf plan_leaf(const gs_proj* proj, gs_tile_rect leaf)
 {
-    *n = 0;
-    *isect = -1;
-    *cells = -1;
-    if (!proj->plan_cands) return nullptr;
+    PlanLeaf r;
+    if (!proj->plan_cands) return r;
     for (size_t k = 0; k < proj->plan.size(); ++k) {
         const gs_leaf& L = proj->plan[k];
         if (L.tx0 == leaf.tx0 && L.ty0 == leaf.ty0 && L.tx1 == leaf.tx1 && L.ty1 == leaf.ty1) {
-            *n = (int64_t)(proj->plan_off[k + 1] - proj->plan_off[k]);
-            *cells = (int64_t)proj->plan_cells[k];
+            r.found = true;
+            r.list = proj->plan_cands + proj->plan_off[k];
+            r.n = (int64_t)(proj->plan_off[k + 1] - proj->plan_off[k]);
+            r.cells = (int64_t)proj->plan_cells[k];
+            r.eoff = proj->plan_coff + proj->plan_off[k];
+            r.ebase = proj->plan_cbase[k];
+            r.toff = proj->plan_toff + proj->plan_tbase[k];
+            // est = bI I + bP P + bT T + b0 determines I when bI > 0
             const gs_cost_model& c = proj->plan_cost;
             const uint64_t P = (uint64_t)(std::min(L.tx1 * 16, proj->W) - L.tx0 * 16) *
                                (uint64_t)(std::min(L.ty1 * 16, proj->H) - L.ty0 * 16);
             const uint64_t T = (uint64_t)(L.tx1 - L.tx0) * (uint64_t)(L.ty1 - L.ty0);
             const uint64_t rest = c.b_pixel * P + c.b_tile * T + c.b_const;
             if (c.b_isect > 0 && L.est_bytes >= rest && (L.est_bytes - rest) % c.b_isect == 0)
-                *isect = (int64_t)((L.est_bytes - rest) / c.b_isect);
-            return proj->plan_cands + proj->plan_off[k];
+                r.isect = (int64_t)((L.est_bytes - rest) / c.b_isect);
+            return r;
         }
     }
-    return nullptr;
+    return r;
 }
 
 extern "C" {
@@ -555,39 +604,43 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     std::vector<GsAlloc> tmp;
     uint64_t I = 0, C = 0;
     bool second = false;
-    int64_t n_list = 0, known = -1, known_cells = -1;
     const int64_t n_super = super_cells(leaf);
     uint32_t *cnt = nullptr, *lc = nullptr, *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
-    uint64_t *eoff = nullptr, *soff = nullptr;
-    const uint32_t* list = plan_group(proj, leaf, &n_list, &known, &known_cells);
-    if (!list) {               // not a planned leaf: visit every candidate
-        list = proj->order;
-        n_list = proj->n_cand;
-    }
-    if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) goto fail;
-    // tile offsets: exclusive scan of the leaf's per-tile counts
-    b->offsets = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (b->n_tiles + 1), GS_MEM_RASTER, &b->allocs);
-    lc = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * b->n_tiles, GS_MEM_RASTER, &tmp);
-    if (!b->offsets || !lc) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_leaf_counts(ctx, proj, leaf, lc)) != GS_OK) goto fail;
-    if ((st = launch_scan_u32_to_u64(ctx, lc, b->offsets, b->n_tiles)) != GS_OK) goto fail;
-    gs_free_one(ctx, &tmp, lc);
-    // coarse level: (super-tile, slot) pairs, grouped by a stable sort
-    cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n_list, 1), GS_MEM_RASTER, &tmp);
-    eoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (n_list + 1), GS_MEM_RASTER, &tmp);
-    if (!cnt || !eoff) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_count_cells(ctx, proj, leaf, list, n_list, cnt)) != GS_OK) goto fail;
-    if ((st = launch_scan_u32_to_u64(ctx, cnt, eoff, n_list)) != GS_OK) goto fail;
-    gs_free_one(ctx, &tmp, cnt);   // stream-ordered: the scan has consumed it
-    if (known >= 0 && known_cells >= 0) {
-        I = (uint64_t)known;       // from the plan: no read-back
-        C = (uint64_t)known_cells;
+    uint32_t* eoff_own = nullptr;
+    uint64_t* soff = nullptr;
+    const PlanLeaf pl = plan_leaf(proj, leaf);
+    const uint32_t* list = pl.found ? pl.list : proj->order;   // not planned: every candidate
+    const int64_t n_list = pl.found ? pl.n : proj->n_cand;
+    const uint32_t* eoff = pl.eoff;
+    const uint32_t ebase = pl.ebase;
+    if (pl.found) {
+        b->offsets = pl.toff;      // the plan's memory (kept until the projection is released)
+        C = (uint64_t)pl.cells;
     } else {
-        uint64_t hv[2] = {0, 0};
-        if ((st = readback(ctx, b->offsets + b->n_tiles, sizeof(uint64_t), &hv[0])) != GS_OK) goto fail;
-        if ((st = readback(ctx, eoff + n_list, sizeof(uint64_t), &hv[1])) != GS_OK) goto fail;
-        I = hv[0];
-        C = hv[1];
+        if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) goto fail;
+        // tile offsets: exclusive scan of the leaf's per-tile counts
+        b->offsets = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (b->n_tiles + 1), GS_MEM_RASTER, &b->allocs);
+        lc = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * b->n_tiles, GS_MEM_RASTER, &tmp);
+        if (!b->offsets || !lc) { st = GS_ERR_OOM; goto fail; }
+        if ((st = launch_leaf_counts(ctx, proj, leaf, lc)) != GS_OK) goto fail;
+        if ((st = launch_scan_u32_to_u64(ctx, lc, b->offsets, b->n_tiles)) != GS_OK) goto fail;
+        gs_free_one(ctx, &tmp, lc);
+        // coarse pair offsets of the listed candidates
+        cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n_list, 1), GS_MEM_RASTER, &tmp);
+        eoff_own = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n_list + 1), GS_MEM_RASTER, &tmp);
+        if (!cnt || !eoff_own) { st = GS_ERR_OOM; goto fail; }
+        if ((st = launch_count_cells(ctx, proj, leaf, list, n_list, cnt)) != GS_OK) goto fail;
+        if ((st = launch_scan_u32_to_u32(ctx, cnt, eoff_own, n_list)) != GS_OK) goto fail;
+        gs_free_one(ctx, &tmp, cnt);   // stream-ordered: the scan has consumed it
+        eoff = eoff_own;
+        uint32_t hc = 0;
+        if ((st = readback(ctx, eoff_own + n_list, sizeof(uint32_t), &hc)) != GS_OK) goto fail;
+        C = hc;
+    }
+    if (pl.found && pl.isect >= 0) {
+        I = (uint64_t)pl.isect;    // from the plan's summed-area table: no read-back
+    } else if ((st = readback(ctx, b->offsets + b->n_tiles, sizeof(uint64_t), &I)) != GS_OK) {
+        goto fail;
     }
     if (I >= (1ull << 32) || C >= (1ull << 32)) {
         st = gs_fail(ctx, GS_ERR_OVERFLOW, "leaf has %llu intersections / %llu super-tile pairs (limit 2^32)",
@@ -601,8 +654,8 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
         if (!k0 || !v0) { st = GS_ERR_OOM; goto fail; }
     }
-    if ((st = launch_emit_cells(ctx, proj, leaf, list, n_list, eoff, C, k0, v0)) != GS_OK) goto fail;
-    gs_free_one(ctx, &tmp, eoff);
+    if ((st = launch_emit_cells(ctx, proj, leaf, list, n_list, eoff, ebase, C, k0, v0)) != GS_OK) goto fail;
+    if (eoff_own) gs_free_one(ctx, &tmp, eoff_own);
     {
         const uint64_t nc = std::max<uint64_t>(C, 1);
         k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
@@ -620,11 +673,11 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     {
         const int64_t items = fine_items_bound(leaf, C);
         b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(I, 1), GS_MEM_RASTER, &b->allocs);
-        uint32_t* nseg = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * n_super, GS_MEM_RASTER, &tmp);
+        uint32_t* item_sc = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * items, GS_MEM_RASTER, &tmp);
         uint32_t* ioff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n_super + 1), GS_MEM_RASTER, &tmp);
         uint64_t* pos = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * 64 * items, GS_MEM_RASTER, &tmp);
-        if (!b->values || !nseg || !ioff || !pos) { st = GS_ERR_OOM; goto fail; }
-        if ((st = launch_fine_lists(ctx, proj, leaf, soff, second ? v1 : v0, C, b->offsets, nseg, ioff, pos, I,
+        if (!b->values || !item_sc || !ioff || !pos) { st = GS_ERR_OOM; goto fail; }
+        if ((st = launch_fine_lists(ctx, proj, leaf, soff, second ? v1 : v0, C, b->offsets, item_sc, ioff, pos, I,
                                     b->values)) != GS_OK)
             goto fail;
     }

@@ -64,6 +64,11 @@ struct gs_proj : GsHandle {
     std::vector<gs_leaf> plan;
     std::vector<uint64_t> plan_off;   // host copy of the group offsets [plan.size() + 1]
     std::vector<uint64_t> plan_cells; // per leaf: (super-tile, candidate) pairs of its coarse level
+    std::vector<uint32_t> plan_cbase; // per leaf: value of plan_coff at its first group entry
+    std::vector<uint64_t> plan_tbase; // per leaf: start of its tile offsets in plan_toff
+    uint32_t* plan_coff = nullptr;    // device [entries + 1] scan of the entries' coarse pair counts
+    uint64_t* plan_toff = nullptr;    // device: per leaf, its tile offsets [T_L + 1]
+    std::vector<GsAlloc> plan_retired; // earlier plans (bins may still point into them)
     uint32_t* plan_cands = nullptr;   // device [plan_off.back()] candidate slots, depth order per group
     std::vector<GsAlloc> plan_allocs;
     gs_cost_model plan_cost{};        // cost model the plan was made with
@@ -143,16 +148,17 @@ gs_status launch_count_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf
                              int64_t n_list, uint32_t* cnt);
 // per-tile candidate counts of the leaf (row-major in the leaf) from proj->tile_cnt
 gs_status launch_leaf_counts(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, uint32_t* out);
-// (super-tile, slot) pairs at the offsets eoff (exclusive scan of the counts)
+// (super-tile, slot) pairs at the offsets eoff - ebase (exclusive scan of the counts)
 gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
-                            int64_t n_list, const uint64_t* eoff, uint64_t total, uint32_t* keys, uint32_t* vals);
+                            int64_t n_list, const uint32_t* eoff, uint32_t ebase, uint64_t total, uint32_t* keys,
+                            uint32_t* vals);
 // per-tile lists from the super-tile groups (soff: group offsets, toff: tile offsets)
 // Work items of the fine level (segments of the super-tile groups), an upper
-// bound for n_cells coarse pairs; scratch: nseg u32 [n_super], ioff u32
+// bound for n_cells coarse pairs; scratch: item_sc u32 [items], ioff u32
 // [n_super + 1], pos u64 [items * 64]
 int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells);
 gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
-                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* nseg,
+                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* item_sc,
                             uint32_t* ioff, uint64_t* pos, uint64_t n_values, uint32_t* values);
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets);
 gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
@@ -181,9 +187,14 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
 gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot);
 gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
                             const int32_t* lot, uint32_t* cnt, const uint64_t* off, uint32_t* keys, uint32_t* vals);
-// cells[L] += coarse (super-tile, candidate) pairs of the grouped entries (leaf_of sorted)
-gs_status launch_leaf_cells(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int64_t n,
-                            const uint32_t* leaf_of, const uint32_t* slot, uint64_t* cells);
+// Per-view offsets of a plan: per grouped entry (sorted by leaf) its coarse
+// pair count and their exclusive scan (u32, modulo 2^32), per leaf the scan
+// value at its first entry and its pair count (leaf_cells [2 * n_leaves]),
+// and per leaf the exclusive scan of its tile counts at toff + toff_base[L].
+gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
+                              int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
+                              const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
+                              uint32_t* leaf_cells, const uint64_t* toff_base, uint64_t* toff);
 
 // loss.hip
 gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,

@@ -253,46 +253,90 @@ __global__ __launch_bounds__(256) void k_leaf_pairs(int64_t n, const uint32_t* _
     if (!EMIT) cnt[k] = m;
 }
 
-// per leaf: the (super-tile, candidate) pairs of its coarse level, summed
-// over the grouped (leaf, slot) entries (sorted by leaf, so a wavefront's
-// entries nearly always share one leaf and add with one atomic)
-__global__ __launch_bounds__(256) void k_leaf_cells(int64_t n, const uint32_t* __restrict__ leaf_of,
-                                                    const uint32_t* __restrict__ slot, const int4* __restrict__ rect,
-                                                    const gs_leaf* __restrict__ leaves, int sh,
-                                                    unsigned long long* __restrict__ cells)
+// per grouped (leaf, slot) entry: the super-tiles of its leaf that the
+// rectangle meets (the entry's coarse pairs)
+__global__ __launch_bounds__(256) void k_group_cells(int64_t n, const uint32_t* __restrict__ leaf_of,
+                                                     const uint32_t* __restrict__ slot, const int4* __restrict__ rect,
+                                                     const gs_leaf* __restrict__ leaves, int sh,
+                                                     uint32_t* __restrict__ cnt)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool ok = k < n;
-    uint32_t L = 0;
-    uint64_t c = 0;
-    if (ok) {
-        L = leaf_of[k];
-        const gs_leaf lf = leaves[L];
-        const int4 r = rect[slot[k]];
-        const int x0 = max(r.x, lf.tx0) - lf.tx0, x1 = min(r.z, lf.tx1) - lf.tx0;
-        const int y0 = max(r.y, lf.ty0) - lf.ty0, y1 = min(r.w, lf.ty1) - lf.ty0;
-        if (x0 < x1 && y0 < y1)
-            c = (uint64_t)(((x1 - 1) >> sh) - (x0 >> sh) + 1) * (uint64_t)(((y1 - 1) >> sh) - (y0 >> sh) + 1);
+    if (k >= n) return;
+    const gs_leaf lf = leaves[leaf_of[k]];
+    const int4 r = rect[slot[k]];
+    const int x0 = max(r.x, lf.tx0) - lf.tx0, x1 = min(r.z, lf.tx1) - lf.tx0;
+    const int y0 = max(r.y, lf.ty0) - lf.ty0, y1 = min(r.w, lf.ty1) - lf.ty0;
+    uint32_t c = 0;
+    if (x0 < x1 && y0 < y1)
+        c = (uint32_t)((((x1 - 1) >> sh) - (x0 >> sh) + 1) * (((y1 - 1) >> sh) - (y0 >> sh) + 1));
+    cnt[k] = c;
+}
+
+// per leaf: the scan value at its first entry and its number of coarse pairs
+// (u32 arithmetic modulo 2^32: exact for any leaf with fewer than 2^32 pairs)
+__global__ void k_leaf_cell_bounds(int nl, const uint64_t* __restrict__ goff, const uint32_t* __restrict__ coff,
+                                   uint32_t* __restrict__ out)
+{
+    const int L = blockIdx.x * blockDim.x + threadIdx.x;
+    if (L >= nl) return;
+    const uint32_t a = coff[goff[L]], b = coff[goff[L + 1]];
+    out[2 * L] = a;
+    out[2 * L + 1] = b - a;
+}
+
+// per leaf (one workgroup): exclusive scan of its tiles' candidate counts in
+// leaf-local row-major order, written at out + base[L] (T_L + 1 entries)
+__global__ __launch_bounds__(1024) void k_leaf_toff(const gs_leaf* __restrict__ leaves,
+                                                    const int32_t* __restrict__ tile_cnt, int TW,
+                                                    const uint64_t* __restrict__ base, uint64_t* __restrict__ out)
+{
+    __shared__ uint64_t wsum[16];
+    __shared__ uint64_t carry;
+    const gs_leaf lf = leaves[blockIdx.x];
+    const int TWL = lf.tx1 - lf.tx0;
+    const int64_t n = (int64_t)TWL * (lf.ty1 - lf.ty0);
+    uint64_t* o = out + base[blockIdx.x];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int64_t t0 = 0; t0 < n; t0 += 1024) {
+        const int64_t t = t0 + tid;
+        const uint64_t c = t < n ? (uint64_t)tile_cnt[(int64_t)(lf.ty0 + t / TWL) * TW + lf.tx0 + t % TWL] : 0ull;
+        uint64_t x = c;
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t u = __shfl_up((unsigned long long)x, d, 64);
+            if (lane >= d) x += u;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        uint64_t before = carry;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        if (t < n) o[t] = before + x - c;
+        __syncthreads();
+        if (tid == 1023) carry = before + x;
+        __syncthreads();
     }
-    const uint32_t L0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)L);
-    const bool same = gsd::ballot(ok && L != L0) == 0;
-    if (same) {
-        const uint64_t tot = gsd::wave_sum_u64(c);
-        if (gsd::lane_id() == 0 && tot) atomicAdd(&cells[L0], (unsigned long long)tot);
-    } else if (ok && c) {
-        atomicAdd(&cells[L], (unsigned long long)c);
-    }
+    if (tid == 0) o[n] = carry;
 }
 
 }  // namespace
 
-gs_status launch_leaf_cells(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int64_t n,
-                            const uint32_t* leaf_of, const uint32_t* slot, uint64_t* cells)
+gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
+                              int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
+                              const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
+                              uint32_t* leaf_cells, const uint64_t* toff_base, uint64_t* toff)
 {
-    if (n > 0) {
-        GsTimerScope ts(ctx, "leaf_groups");
-        hipLaunchKernelGGL(k_leaf_cells, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, leaf_of,
-                           slot, proj->rect, leaves_dev, super_shift(), (unsigned long long*)cells);
+    GsTimerScope ts(ctx, "leaf_groups");
+    if (n_entries > 0)
+        hipLaunchKernelGGL(k_group_cells, dim3((unsigned)ceil_div(n_entries, 256)), dim3(256), 0, ctx->stream,
+                           n_entries, leaf_of, slot, proj->rect, leaves_dev, super_shift(), cell_cnt);
+    gs_status st = launch_scan_u32_to_u32(ctx, cell_cnt, cell_off, n_entries);
+    if (st != GS_OK) return st;
+    if (n_leaves > 0) {
+        hipLaunchKernelGGL(k_leaf_cell_bounds, dim3((unsigned)ceil_div(n_leaves, 256)), dim3(256), 0, ctx->stream,
+                           n_leaves, group_off, cell_off, leaf_cells);
+        hipLaunchKernelGGL(k_leaf_toff, dim3((unsigned)n_leaves), dim3(1024), 0, ctx->stream, leaves_dev,
+                           proj->tile_cnt, proj->TW, toff_base, toff);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
