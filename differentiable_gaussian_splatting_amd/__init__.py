@@ -9,10 +9,10 @@ layer over it that uses PyTorch only for device memory and streams, and
 from . import scenes
 from .binding import (Context, DeviceScene, GsError, like_scene, load, gs_project, gs_plan_leaves, gs_bin_sort,
                       gs_render_fwd, gs_render_bwd, gs_project_bwd, gs_loss_ssim, gs_adam_step, gs_release,
-                      gs_export, gs_util_exp, gs_train_view, gs_set_timing, gs_reset_timing, gs_kernel_time,
-                      gs_default_cost_model)
+                      gs_export, gs_util_exp, gs_train_view, gs_set_timing, gs_set_timing_only, gs_reset_timing,
+                      gs_kernel_time,                       gs_default_cost_model)
 
 __all__ = ["scenes", "Context", "DeviceScene", "GsError", "like_scene", "load", "gs_project", "gs_plan_leaves",
            "gs_bin_sort", "gs_render_fwd", "gs_render_bwd", "gs_project_bwd", "gs_loss_ssim", "gs_adam_step",
-           "gs_release", "gs_export", "gs_util_exp", "gs_train_view", "gs_set_timing", "gs_reset_timing",
-           "gs_kernel_time", "gs_default_cost_model"]
+           "gs_release", "gs_export", "gs_util_exp", "gs_train_view", "gs_set_timing", "gs_set_timing_only",
+           "gs_reset_timing", "gs_kernel_time", "gs_default_cost_model"]

@@ -121,6 +121,7 @@ def load(path: str = LIB_PATH):
         "gs_set_timing": (st, [vp, i32]),
         "gs_kernel_time": (st, [vp, C.c_char_p, P(C.c_double), P(i64)]),
         "gs_reset_timing": (st, [vp]),
+        "gs_set_timing_only": (st, [vp, C.c_char_p]),
         "gs_default_cost_model": (gs_cost_model, []),
         "gs_project": (st, [vp, P(gs_camera), P(gs_params), P(vp), P(i64)]),
         "gs_plan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, P(i32)]),
@@ -362,6 +363,10 @@ def gs_util_exp(ctx: Context, x):
 
 def gs_set_timing(ctx: Context, on: bool):
     ctx.check(ctx.lib.gs_set_timing(ctx.handle, int(on)))
+
+
+def gs_set_timing_only(ctx: Context, name):
+    ctx.check(ctx.lib.gs_set_timing_only(ctx.handle, None if name is None else name.encode()))
 
 
 def gs_reset_timing(ctx: Context):

@@ -98,6 +98,7 @@ static hipEvent_t take_event(gs_ctx* ctx)
 GsTimerScope::GsTimerScope(gs_ctx* c, const char* n) : ctx(c), name(n)
 {
     if (!ctx->timing) return;
+    if (!ctx->timing_only.empty() && ctx->timing_only != name) return;
     hipEvent_t s = take_event(ctx);
     stop = take_event(ctx);
     if (!s || !stop) {
@@ -412,6 +413,13 @@ gs_status gs_set_timing(gs_ctx* ctx, int32_t on)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     ctx->timing = on != 0;
+    return GS_OK;
+}
+
+gs_status gs_set_timing_only(gs_ctx* ctx, const char* name)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    ctx->timing_only = name ? name : "";
     return GS_OK;
 }
 

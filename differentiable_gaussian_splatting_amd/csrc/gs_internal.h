@@ -32,6 +32,7 @@ struct gs_ctx {
     uint64_t live = 0, peak = 0, n_alloc = 0, n_free = 0;
     uint64_t live_cat[GS_MEM_NCAT] = {0}, peak_cat[GS_MEM_NCAT] = {0};
     bool timing = false;
+    std::string timing_only;       // time only kernels of this name (empty: all)
     std::vector<GsTimerRec> timers;
     std::vector<hipEvent_t> event_pool;
     void* pinned = nullptr;        // small pinned host buffer for count read-backs

@@ -150,6 +150,9 @@ gs_status gs_set_timing(gs_ctx* ctx, int32_t on);
  * total milliseconds and number of launches (synchronises). */
 gs_status gs_kernel_time(gs_ctx* ctx, const char* name, double* total_ms, int64_t* launches);
 gs_status gs_reset_timing(gs_ctx* ctx);
+/* Restrict timing to the kernels timed under `name` (NULL: all kernels), so
+ * that a measured run carries events around one kernel only. */
+gs_status gs_set_timing_only(gs_ctx* ctx, const char* name);
 gs_cost_model gs_default_cost_model(void);
 
 /* ---- the six calls of one view ----------------------------------------- */
