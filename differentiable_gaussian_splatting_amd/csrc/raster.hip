@@ -392,32 +392,37 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
             const float alpha = clamped ? gsd::kAlphaMax : av;
             const bool contrib = n < lst && pok && !(alpha < gsd::kAlphaMin);
             if (gsd::ballot(contrib) == 0) continue;
+            // alpha of the lanes that include the entry, 0 on the others: then
+            // T / (1 - 0) = T and w = 0 leave those lanes' state unchanged
+            const float ae = contrib ? alpha : 0.0f;
             // T before this entry = T after it / (1 - alpha)
-            const float rom = contrib ? __builtin_amdgcn_rcpf(1.0f - alpha) : 1.0f;
+            const float rom = __builtin_amdgcn_rcpf(1.0f - ae);
             T = T * rom;
-            const float w = contrib ? alpha * T : 0.0f;
+            const float w = ae * T;
             // dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha))
             const float grgb = __builtin_fmaf(gr2, cb, __builtin_fmaf(gr1, bb.w, gr0 * bb.z));
-            const float dal = contrib ? __builtin_fmaf(T, grgb, -(rom * GS)) : 0.0f;
+            const float dal0 = __builtin_fmaf(T, grgb, -(rom * GS));
             GS = __builtin_fmaf(grgb, w, GS);
             float p[9];
             p[6] = gr0 * w;
             p[7] = gr1 * w;
             p[8] = gr2 * w;
-            // through alpha = o G (zero when alpha is clamped)
-            p[5] = clamped ? 0.0f : dal * G;
-            const float ndpw = clamped ? 0.0f : -(dal * av);   // -dL/dpower
+            // through alpha = o G, zero where alpha is clamped or not included
+            const float dal = (contrib && !clamped) ? dal0 : 0.0f;
+            p[5] = dal * G;
+            const float ndpw = -(dal * av);   // -dL/dpower
             // power = -(A dx^2 + C dy^2)/2 - B dx dy with A = -2 a.z, B = -a.w,
-            // C = -2 b.x, dx = px - x, dy = py - y:
-            //   dL/dx = (A dx + B dy) dL/dpower = (a.z dx + t) (-dL/dpower)
-            //   dL/dy = (C dy + B dx) dL/dpower = (2 b.x dy + a.w dx) (-dL/dpower)
-            //   dL/dA = -dx^2/2 dL/dpower, dL/dB = -dx dy dL/dpower, dL/dC = -dy^2/2 dL/dpower
-            p[0] = __builtin_fmaf(a.z, dx, t) * ndpw;
-            p[1] = __builtin_fmaf(a.w, dx, u1 + u1) * ndpw;
-            const float h = 0.5f * ndpw;
-            p[2] = (dx * h) * dx;
-            p[3] = (dx * ndpw) * dy;
-            p[4] = (dy * h) * dy;
+            // C = -2 b.x, dx = px - x, dy = py - y, so with q = -dL/dpower
+            //   dL/dx = (A dx + B dy) dL/dpower = 2 a.z (q dx) + a.w (q dy)
+            //   dL/dy = (C dy + B dx) dL/dpower = 2 b.x (q dy) + a.w (q dx)
+            //   dL/dA = (q dx dx)/2, dL/dB = q dx dy, dL/dC = (q dy dy)/2.
+            // The five moments q dx, q dy, q dx dx, q dx dy, q dy dy are summed
+            // over the pixels and turned into the five partials once per entry.
+            p[0] = ndpw * dx;
+            p[1] = ndpw * dy;
+            p[2] = p[0] * dx;
+            p[3] = p[0] * dy;
+            p[4] = p[1] * dy;
             int v;
             const float r = wave_reduce9(p, lane, &v);
             if (v >= 0) {
@@ -431,17 +436,28 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
         // sums of the four rows, one atomic per nonzero (entry, value)
         const unsigned long long m0 = sh.wmask[b][0], m1 = sh.wmask[b][1];
         const unsigned long long m2 = sh.wmask[b][2], m3 = sh.wmask[b][3];
-        for (int o = tid; o < cnt * 9; o += 256) {
-            const int j = o / 9;
+        auto row_sum = [&](int o, int j) {
             const float4 q = sh.red[b][o];
             float sum = 0.0f;
             sum += ((m0 >> j) & 1ull) ? q.x : 0.0f;
             sum += ((m1 >> j) & 1ull) ? q.y : 0.0f;
             sum += ((m2 >> j) & 1ull) ? q.z : 0.0f;
             sum += ((m3 >> j) & 1ull) ? q.w : 0.0f;
+            return sum;
+        };
+        for (int o = tid; o < cnt * 9; o += 256) {
+            const int j = o / 9, v = o - j * 9;
+            float sum = row_sum(o, j);
+            if (v < 5) {
+                // moments -> partials of the mean and the conic
+                const float4 a = S.a[j];
+                if (v == 0) sum = 2.0f * a.z * sum + a.w * row_sum(o + 1, j);
+                else if (v == 1) sum = 2.0f * S.b[j].x * sum + a.w * row_sum(o - 1, j);
+                else if (v != 3) sum = 0.5f * sum;
+            }
             if (sum != 0.0f) {
                 const uint32_t slot = __builtin_bit_cast(uint32_t, S.c[j].y);
-                unsafeAtomicAdd(&grad2d[(int64_t)slot * 9 + (o - j * 9)], sum);
+                unsafeAtomicAdd(&grad2d[(int64_t)slot * 9 + v], sum);
             }
         }
         if (hi - 64 > 0) stage(b ^ 1, hi - 64);
