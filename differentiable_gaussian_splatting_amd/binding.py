@@ -81,7 +81,7 @@ class gs_view_opts(C.Structure):
                 ("eps", C.c_float), ("strict_budget", C.c_int32), ("max_leaves", C.c_int32),
                 ("leaves_out", C.c_void_p), ("cost", C.c_void_p), ("image_out", C.c_void_p),
                 ("grad3d_out", C.c_void_p), ("params_rw", C.c_void_p), ("adam_m", C.c_void_p),
-                ("adam_v", C.c_void_p)]
+                ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64)]
 
 
 class gs_view_result(C.Structure):
@@ -387,7 +387,7 @@ def gs_default_cost_model():
 def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0, loss="l1", lam=0.2,
                   adam=None, image_out=None, grad3d_out=None, strict=False, cost=None, max_leaves=0):
     """One whole view in the library (see gs_train_view in include/gs.h).
-    adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps)."""
+    adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk)."""
     o = gs_view_opts()
     o.budget_bytes = int(budget_bytes)
     o.loss_kind = 0 if loss == "l1" else 1
@@ -405,6 +405,7 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
         o.adam_step = int(adam["step"])
         o.lr, o.beta1, o.beta2, o.eps = (float(adam.get(k, d)) for k, d in
                                          (("lr", 1e-3), ("beta1", 0.9), ("beta2", 0.999), ("eps", 1e-15)))
+        o.adam_chunk = int(adam.get("chunk", 0))
         pr, pm, pv = adam["params"].ptrs(), adam["m"].ptrs(), adam["v"].ptrs()
         keep += [pr, pm, pv]
         o.params_rw, o.adam_m, o.adam_v = (C.cast(C.pointer(x), C.c_void_p) for x in (pr, pm, pv))

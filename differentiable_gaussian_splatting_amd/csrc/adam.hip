@@ -15,24 +15,32 @@ struct AdamArgs {
     float lr, b1, b2, eps, bc1, bc2;
 };
 
-// group of `width` consecutive values per Gaussian at column `col0` of grad3d
-__global__ __launch_bounds__(256) void k_adam_group(int64_t n, int width, int col0, int F,
+// Group of `width` consecutive values per Gaussian at column `col0` of the
+// compact gradient rows of slots [s0, s1) (row s - s0 in grad3d).  Covers the
+// Gaussians [g0, g1) whose candidates are exactly those slots: g0 = 0 or the
+// Gaussian of slot s0, g1 = N or the Gaussian of slot s1 (slots are in
+// ascending Gaussian order).  Grid-stride, since g0 and g1 are read here.
+__global__ __launch_bounds__(256) void k_adam_group(int64_t n, int64_t n_cand, const uint32_t* __restrict__ ids,
+                                                    int64_t s0, int64_t s1, int width, int col0, int F,
                                                     const int32_t* __restrict__ slot_of,
                                                     const float* __restrict__ grad3d, float* __restrict__ p,
                                                     float* __restrict__ m, float* __restrict__ v, AdamArgs a)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= n * width) return;
-    const int64_t i = k / width;
-    const int c = (int)(k - i * width);
-    const int32_t s = slot_of[i];
-    const float g = s >= 0 ? grad3d[(int64_t)s * F + col0 + c] : 0.0f;
-    const float mk = a.b1 * m[k] + (1.0f - a.b1) * g;
-    const float vk = a.b2 * v[k] + (1.0f - a.b2) * g * g;
-    m[k] = mk;
-    v[k] = vk;
-    const float mh = mk / a.bc1, vh = vk / a.bc2;
-    p[k] = p[k] - a.lr * mh / (sqrtf(vh) + a.eps);
+    const int64_t g0 = s0 == 0 ? 0 : (int64_t)ids[s0];
+    const int64_t g1 = s1 >= n_cand ? n : (int64_t)ids[s1];
+    for (int64_t k = g0 * width + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < g1 * width;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = k / width;
+        const int c = (int)(k - i * width);
+        const int32_t s = slot_of[i];
+        const float g = s >= 0 ? grad3d[(int64_t)(s - s0) * F + col0 + c] : 0.0f;
+        const float mk = a.b1 * m[k] + (1.0f - a.b1) * g;
+        const float vk = a.b2 * v[k] + (1.0f - a.b2) * g * g;
+        m[k] = mk;
+        v[k] = vk;
+        const float mh = mk / a.bc1, vh = vk / a.bc2;
+        p[k] = p[k] - a.lr * mh / (sqrtf(vh) + a.eps);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_scatter(int64_t n, int F, const int32_t* __restrict__ slot_of,
@@ -49,8 +57,8 @@ __global__ __launch_bounds__(256) void k_scatter(int64_t n, int F, const int32_t
 }  // namespace
 
 gs_status launch_adam(gs_ctx* ctx, const gs_proj* proj, int64_t n, int sh_degree, const gs_param_ptrs* p,
-                      const gs_param_ptrs* m, const gs_param_ptrs* v, const float* grad3d, int32_t step, float lr,
-                      float b1, float b2, float eps)
+                      const gs_param_ptrs* m, const gs_param_ptrs* v, const float* grad3d, int64_t s0, int64_t s1,
+                      int32_t step, float lr, float b1, float b2, float eps)
 {
     const int K = (sh_degree + 1) * (sh_degree + 1);
     const int F = 11 + 3 * K;
@@ -66,9 +74,14 @@ gs_status launch_adam(gs_ctx* ctx, const gs_proj* proj, int64_t n, int sh_degree
         {p->sh, m->sh, v->sh, 3 * K, 11}};
     if (n <= 0) return GS_OK;
     GsTimerScope ts(ctx, "adam");
-    for (const G& g : groups)
-        hipLaunchKernelGGL(k_adam_group, dim3((unsigned)ceil_div(n * g.width, 256)), dim3(256), 0, ctx->stream, n,
-                           g.width, g.col0, F, proj->slot_of, grad3d, g.p, g.m, g.v, a);
+    // enough threads for the Gaussians of the slot range (about its share of
+    // all Gaussians), at most 8 per compute unit and wavefront slot
+    const int64_t share = proj->n_cand > 0 ? ceil_div(n * (s1 - s0), proj->n_cand) : n;
+    for (const G& g : groups) {
+        const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(share * g.width, 256), 8192));
+        hipLaunchKernelGGL(k_adam_group, dim3((unsigned)blocks), dim3(256), 0, ctx->stream, n, proj->n_cand,
+                           proj->ids, s0, s1, g.width, g.col0, F, proj->slot_of, grad3d, g.p, g.m, g.v, a);
+    }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -153,6 +153,9 @@ static void destroy_handle(gs_ctx* ctx, GsHandle* h)
 // ---------------------------------------------------------------------------
 // read-back helper: copy `bytes` device bytes to the pinned buffer and wait
 
+// candidate slots per projection-backward + Adam chunk of gs_train_view
+constexpr int64_t kAdamChunkSlots = 512 * 1024;
+
 static gs_status readback(gs_ctx* ctx, const void* dev, size_t bytes, void* host)
 {
     GS_HIP(ctx, hipMemcpyAsync(ctx->pinned, dev, bytes, hipMemcpyDeviceToHost, ctx->stream));
@@ -767,7 +770,7 @@ gs_status gs_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* par
     if (params->n != proj->n || params->sh_degree != proj->sh_degree)
         return gs_fail(ctx, GS_ERR_STATE, "params do not match the projection");
     if (proj->n_cand > 0 && (!grad2d || !grad3d)) return gs_fail(ctx, GS_ERR_INVALID_ARG, "grad2d / grad3d NULL");
-    return launch_project_bwd(ctx, cam, params, proj, grad2d, grad3d);
+    return launch_project_bwd(ctx, cam, params, proj, grad2d, 0, proj->n_cand, grad3d);
 }
 
 // ---------------------------------------------------------------------------
@@ -813,7 +816,7 @@ gs_status gs_adam_step(gs_ctx* ctx, const gs_proj* proj, int64_t n, int32_t sh_d
     if (n != proj->n || sh_degree != proj->sh_degree) return gs_fail(ctx, GS_ERR_STATE, "sizes do not match");
     if (!params || !m || !v || step < 1 || (proj->n_cand > 0 && !grad3d))
         return gs_fail(ctx, GS_ERR_INVALID_ARG, "gs_adam_step arguments");
-    return launch_adam(ctx, proj, n, sh_degree, params, m, v, grad3d, step, lr, beta1, beta2, eps);
+    return launch_adam(ctx, proj, n, sh_degree, params, m, v, grad3d, 0, proj->n_cand, step, lr, beta1, beta2, eps);
 }
 
 void gs_release(gs_ctx* ctx, void* handle)
@@ -977,7 +980,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         gs_release(ctx, bins);
         if (st != GS_OK) goto done;
     }
-    {
+    if (opts->grad3d_out || opts->adam_step <= 0) {
         float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * nc, GS_MEM_GRAD, &view);
         if (!grad3d) { st = GS_ERR_OOM; goto done; }
         if ((st = gs_project_bwd(ctx, cam, params, proj, grad2d, grad3d)) != GS_OK) goto done;
@@ -987,6 +990,27 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
             (st = gs_adam_step(ctx, proj, params->n, params->sh_degree, opts->params_rw, opts->adam_m, opts->adam_v,
                                grad3d, opts->adam_step, opts->lr, opts->beta1, opts->beta2, opts->eps)) != GS_OK)
             goto done;
+    } else {
+        // Projection backward and Adam in chunks of candidate slots: the
+        // compact gradient rows of one chunk at a time (121 MB at SH3), each
+        // chunk's Gaussians updated right after; same result as the whole
+        // [n_cand][F] buffer followed by one Adam step.
+        if (!opts->params_rw || !opts->adam_m || !opts->adam_v) {
+            st = gs_fail(ctx, GS_ERR_INVALID_ARG, "Adam parameters / moments NULL");
+            goto done;
+        }
+        const int64_t want = opts->adam_chunk > 0 ? opts->adam_chunk : kAdamChunkSlots;
+        const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(nc, want));
+        float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * chunk, GS_MEM_GRAD, &view);
+        if (!grad3d) { st = GS_ERR_OOM; goto done; }
+        for (int64_t s0 = 0; s0 < std::max<int64_t>(nc, 1); s0 += chunk) {
+            const int64_t s1 = std::min<int64_t>(nc, s0 + chunk);
+            if ((st = launch_project_bwd(ctx, cam, params, proj, grad2d, s0, s1, grad3d)) != GS_OK) goto done;
+            if ((st = launch_adam(ctx, proj, params->n, params->sh_degree, opts->params_rw, opts->adam_m,
+                                  opts->adam_v, grad3d, s0, s1, opts->adam_step, opts->lr, opts->beta1, opts->beta2,
+                                  opts->eps)) != GS_OK)
+                goto done;
+        }
     }
     if (opts->loss_kind == 0) {
         double s = 0.0;

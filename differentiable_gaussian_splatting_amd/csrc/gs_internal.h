@@ -130,8 +130,9 @@ gs_status launch_prefix2d_u64(gs_ctx* ctx, uint64_t* grid, int rows, int cols);
 // project.hip
 gs_status launch_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
                          uint32_t* flag_scratch, uint32_t* slot_scratch);
+// compact gradient rows of slots [s0, s1) into grad3d (row s - s0)
 gs_status launch_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
-                             const float* grad2d, float* grad3d);
+                             const float* grad2d, int64_t s0, int64_t s1, float* grad3d);
 gs_status launch_export_proj(gs_ctx* ctx, const gs_proj* proj, int field, void* dst);
 gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
 
@@ -205,9 +206,11 @@ int64_t ssim_partial_blocks(int W, int H);
 gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate);
 
 // adam.hip
+// Adam over the Gaussians whose candidates are the slots [s0, s1), with their
+// gradient rows in grad3d (row s - s0); [0, n_cand) covers every Gaussian
 gs_status launch_adam(gs_ctx* ctx, const gs_proj* proj, int64_t n, int sh_degree, const gs_param_ptrs* p,
-                      const gs_param_ptrs* m, const gs_param_ptrs* v, const float* grad3d, int32_t step,
-                      float lr, float b1, float b2, float eps);
+                      const gs_param_ptrs* m, const gs_param_ptrs* v, const float* grad3d, int64_t s0, int64_t s1,
+                      int32_t step, float lr, float b1, float b2, float eps);
 gs_status launch_scatter_grad3d(gs_ctx* ctx, const gs_proj* proj, int F, const float* grad3d, float* dense);
 
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

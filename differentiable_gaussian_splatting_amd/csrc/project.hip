@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, co
 // Projection backward, one thread per candidate (f32).  Chain rule through
 // each step of the projection, with the forward's clamp decisions (flags).
 template <int DEG>
-__global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand,
+__global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int64_t s_end,
                                                      const float* __restrict__ means,
                                                      const float* __restrict__ log_scales,
                                                      const float* __restrict__ quats,
@@ -232,10 +232,10 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand,
     constexpr int RS = F | 1;
     __shared__ float outs[4][64 * RS];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t w0 = (int64_t)blockIdx.x * blockDim.x + wave * 64;
+    const int64_t w0 = s0 + (int64_t)blockIdx.x * blockDim.x + wave * 64;   // slots [s0, s_end)
     const int64_t j = w0 + lane;
     float* out = outs[wave] + lane * RS;
-    if (j < n_cand) {
+    if (j < s_end) {
     const int64_t i = ids[j];
     const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[j].w);
     const float* g = grad2d + 9 * j;
@@ -401,9 +401,9 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t n_cand,
     out[2] = dmu[2];
     }
     gsd::wave_sync();
-    const int64_t rows = n_cand - w0 < 64 ? n_cand - w0 : 64;
+    const int64_t rows = s_end - w0 < 64 ? s_end - w0 : 64;
     if (rows > 0) {
-        float* dst = grad3d + w0 * F;
+        float* dst = grad3d + (w0 - s0) * F;   // row j - s0
         const float* src = outs[wave];
         for (int q = lane; q < rows * F; q += 64) dst[q] = src[(q / F) * RS + q % F];
     }
@@ -491,13 +491,13 @@ gs_status launch_project_write(gs_ctx* ctx, const gs_camera* cam, const gs_param
 }
 
 gs_status launch_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
-                             const float* grad2d, float* grad3d)
+                             const float* grad2d, int64_t s0, int64_t s1, float* grad3d)
 {
     const CamDev cd = make_cam(cam);
-    if (proj->n_cand > 0) {
+    if (s1 > s0) {
         GsTimerScope ts(ctx, "project_bwd");
-        const dim3 grid((unsigned)ceil_div(proj->n_cand, 256));
-#define GS_PB(D) hipLaunchKernelGGL(k_project_bwd<D>, grid, dim3(256), 0, ctx->stream, cd, proj->n_cand, p->means, \
+        const dim3 grid((unsigned)ceil_div(s1 - s0, 256));
+#define GS_PB(D) hipLaunchKernelGGL(k_project_bwd<D>, grid, dim3(256), 0, ctx->stream, cd, s0, s1, p->means, \
                                     p->log_scales, p->quats, p->opacity_logits, p->sh, proj->ids, proj->g2, grad2d, \
                                     grad3d)
         switch (p->sh_degree) {

@@ -309,6 +309,10 @@ typedef struct {
     gs_param_ptrs* params_rw;    /* required when adam_step >= 1 (in/out)      */
     gs_param_ptrs* adam_m;
     gs_param_ptrs* adam_v;
+    int64_t adam_chunk;          /* with Adam and no grad3d_out: candidate     */
+                                 /* slots per projection-backward + Adam chunk */
+                                 /* (0: 524288), which bounds the compact      */
+                                 /* gradient buffer to adam_chunk x F floats   */
 } gs_view_opts;
 
 typedef struct {
@@ -322,7 +326,9 @@ typedef struct {
  * (gs_bin_sort, gs_render_fwd, loss, gs_render_bwd, release) ->
  * gs_project_bwd -> optional gs_adam_step; the 2D gradients of all leaves are
  * summed in one buffer before the single projection backward (BoundedGS
- * page "01", Fig. 3, Fig. 5 conclusion).  target: device [3][H][W].
+ * page "01", Fig. 3, Fig. 5 conclusion).  With Adam and no grad3d_out the
+ * projection backward and the update run chunk by chunk of candidate slots
+ * (same result, a smaller gradient buffer).  target: device [3][H][W].
  * Synchronises. */
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result);

@@ -169,6 +169,37 @@ def test_adam_step_matches_oracle(ctx):
         assert rel_l2(got - p0, p - p0) <= 1e-3, name
 
 
+@pytest.mark.parametrize("chunk", [700, 0])
+def test_train_view_chunked_update_matches_oracle(ctx, chunk):
+    """gs_train_view with Adam and no dense gradient output runs the projection
+    backward and the update chunk by chunk of candidate slots (700: several
+    chunks and a ragged last one; 0: the default, one chunk here)."""
+    import torch
+    w = scenes.make_workload("c2_hd", n=5000, width=200, height=150, posed=True, seed=108)
+    o = oracle.train_view(w.camera, w.scene, w.target)
+    assert o["n_cand"] > 2 * 700
+    rng = np.random.default_rng(1)
+    m0 = [rng.normal(0, 1e-3, size=t.shape) for t in w.scene.arrays()]
+    v0 = [rng.uniform(0, 1e-6, size=t.shape) for t in w.scene.arrays()]
+    ds = B.DeviceScene(w.scene, ctx.device)
+    m, v = B.like_scene(ds), B.like_scene(ds)
+    for dst, src in zip(m.tensors(), m0):
+        dst.copy_(torch.from_numpy(src.astype(np.float32)))
+    for dst, src in zip(v.tensors(), v0):
+        dst.copy_(torch.from_numpy(src.astype(np.float32)))
+    target = torch.from_numpy(w.target).to(ctx.device)
+    r = B.gs_train_view(ctx, w.camera, ds, target, adam=dict(step=3, params=ds, m=m, v=v, chunk=chunk))
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    groups = grad3d_groups(o["grad3d"], 3)
+    for k, (t, name) in enumerate(zip(ds.tensors(), ["means", "log_scales", "quats", "logits", "sh"])):
+        p0 = w.scene.arrays()[k].astype(np.float64)
+        p, mm, vv = oracle.adam(groups[name].reshape(p0.shape), p0, m0[k].astype(np.float32),
+                                v0[k].astype(np.float32), step=3)
+        got = t.cpu().numpy().astype(np.float64)
+        say(f"  {name:10s} update rel L2 {rel_l2(got - p0, p - p0):.2e}")
+        assert rel_l2(got - p0, p - p0) <= 1e-3, name
+
+
 @pytest.mark.parametrize("case", ["empty", "all_culled", "one_pixel", "ragged", "huge", "dense_tile"])
 def test_edge_cases(ctx, case):
     rng = np.random.default_rng(200)
@@ -187,7 +218,7 @@ def test_edge_cases(ctx, case):
         w.scene.log_scales[:5] = 1.5          # rectangles covering the whole grid (wave-wide emission)
         w.scene.logits[:5] = -3.0
     else:
-        # one tile receives far more than 8192 entries (the HBM merge-sort path)
+        # one tile receives far more than 8192 entries (a long list split into many fine segments)
         n = 12000
         w = scenes.make_workload("c1_small", n=n, width=96, height=64, seed=203)
         w.scene.means[:, 0] = rng.uniform(-0.05, 0.05, n)
