@@ -234,7 +234,8 @@ def count_work(B, ctx, cam, params, budget):
     (q_b = sum of last), intersections, candidates, leaves, tiles, pixels."""
     import torch
     proj, n_cand = B.gs_project(ctx, cam, params)
-    leaves = B.gs_plan_leaves(ctx, cam, proj, budget)
+    leaves = (B.gs_plan_leaves(ctx, cam, proj, budget) if budget > 0 else
+              [dict(tx0=0, ty0=0, tx1=cam.tiles_x, ty1=cam.tiles_y)])
     stats = torch.zeros(4, dtype=torch.int64, device=ctx.device)
     n_isect = 0
     tiles = 0
@@ -251,12 +252,13 @@ def count_work(B, ctx, cam, params, budget):
         meet = ((rects[:, 0] < L["tx1"]) & (rects[:, 2] > L["tx0"]) &
                 (rects[:, 1] < L["ty1"]) & (rects[:, 3] > L["ty0"]))
         r = rects[meet]
-        x0 = np.maximum(r[:, 0], L["tx0"]) - L["tx0"]
-        x1 = np.minimum(r[:, 2], L["tx1"]) - L["tx0"]
-        y0 = np.maximum(r[:, 1], L["ty0"]) - L["ty0"]
-        y1 = np.minimum(r[:, 3], L["ty1"]) - L["ty0"]
+        # image-aligned super-cells of 8 x 8 tiles met inside the leaf
+        x0 = np.maximum(r[:, 0], L["tx0"])
+        x1 = np.minimum(r[:, 2], L["tx1"])
+        y0 = np.maximum(r[:, 1], L["ty0"])
+        y1 = np.minimum(r[:, 3], L["ty1"])
         c_l = int((((x1 - 1) >> 3) - (x0 >> 3) + 1) @ (((y1 - 1) >> 3) - (y0 >> 3) + 1))
-        s_l = ((L["tx1"] - L["tx0"] + 7) // 8) * ((L["ty1"] - L["ty0"] + 7) // 8)
+        s_l = (((L["tx1"] - 1) >> 3) - (L["tx0"] >> 3) + 1) * (((L["ty1"] - 1) >> 3) - (L["ty0"] >> 3) + 1)
         cells += c_l
         supers += s_l
         radix_elems += c_l * ((max(1, (s_l - 1).bit_length()) + 7) // 8) if s_l > 1 else 0

@@ -67,7 +67,13 @@ class gs_leaf(C.Structure):
 
 
 class gs_cost_model(C.Structure):
-    _fields_ = [("b_isect", C.c_uint64), ("b_pixel", C.c_uint64), ("b_tile", C.c_uint64), ("b_const", C.c_uint64)]
+    _fields_ = [("b_isect", C.c_uint64), ("b_pixel", C.c_uint64), ("b_tile", C.c_uint64), ("b_const", C.c_uint64),
+                ("b_cell", C.c_uint64)]
+
+
+def cost_struct(cost):
+    """gs_cost_model from a dict; a cost given without b_cell has no super-cell term."""
+    return gs_cost_model(cost["b_isect"], cost["b_pixel"], cost["b_tile"], cost["b_const"], cost.get("b_cell", 0))
 
 
 class gs_mem_stats(C.Structure):
@@ -269,7 +275,7 @@ def gs_project(ctx: Context, cam, params: DeviceScene):
 def gs_plan_leaves(ctx: Context, cam, proj, budget_bytes: int, cost=None, strict=False, max_leaves=4096):
     cs = None
     if cost is not None:
-        cs = gs_cost_model(cost["b_isect"], cost["b_pixel"], cost["b_tile"], cost["b_const"])
+        cs = cost_struct(cost)
     n = C.c_int32()
     while True:
         arr = (gs_leaf * max_leaves)()
@@ -381,7 +387,7 @@ def gs_kernel_time(ctx: Context, name: str):
 
 def gs_default_cost_model():
     c = load().gs_default_cost_model()
-    return dict(b_isect=c.b_isect, b_pixel=c.b_pixel, b_tile=c.b_tile, b_const=c.b_const)
+    return dict(b_isect=c.b_isect, b_pixel=c.b_pixel, b_tile=c.b_tile, b_const=c.b_const, b_cell=c.b_cell)
 
 
 def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0, loss="l1", lam=0.2,
@@ -395,7 +401,7 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     leaves_arr = (gs_leaf * max(max_leaves, 1))()
     o.max_leaves = int(max_leaves)
     o.leaves_out = C.cast(leaves_arr, C.c_void_p) if max_leaves else None
-    cs = gs_cost_model(cost["b_isect"], cost["b_pixel"], cost["b_tile"], cost["b_const"]) if cost else None
+    cs = cost_struct(cost) if cost else None
     o.cost = C.cast(C.pointer(cs), C.c_void_p) if cs is not None else None
     o.image_out = image_out.data_ptr() if image_out is not None else None
     o.grad3d_out = grad3d_out.data_ptr() if grad3d_out is not None else None

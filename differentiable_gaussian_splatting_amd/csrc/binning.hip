@@ -11,9 +11,10 @@
 //     aggregated in LDS) and a 2D prefix;
 //   - a leaf's tile offsets are the exclusive scan of those counts over the
 //     leaf's tiles (row-major inside the leaf);
-//   - coarse level: the leaf is cut into super-tiles of 8 x 8 tiles; the
-//     leaf's candidates, in depth order, emit one (super-tile, slot) pair per
-//     super-tile their rectangle meets (load-balanced, coalesced writes at
+//   - coarse level: the leaf is covered by the image-aligned super-tiles of
+//     8 x 8 tiles that meet it (those on its border are partial); the leaf's
+//     candidates, in depth order, emit one (super-tile, slot) pair per
+//     super-tile their rectangle meets inside the leaf (load-balanced, coalesced writes at
 //     offsets from an exclusive scan), and a stable radix sort on the
 //     super-tile id groups them with the depth order kept;
 //   - fine level: one workgroup per super-tile, each wavefront owning 2 x 8
@@ -70,23 +71,23 @@ __global__ __launch_bounds__(256) void k_rect_diff(int64_t n, const uint32_t* __
     }
 }
 
-// Cells of the leaf's grid of 2^sh x 2^sh tiles (aligned to the leaf origin)
-// that the rectangle r meets: origin (cx0, cy0) and extent (w, h) in cells;
-// w = h = 0 when r misses the leaf.
+// Super-cells (image-aligned blocks of 2^sh x 2^sh tiles) that the rectangle
+// r meets inside the leaf: first cell (cx0, cy0) relative to the leaf's first
+// super-cell, and extent (w, h); w = h = 0 when r misses the leaf.
 struct Cells {
     int cx0, cy0, w, h;
 };
 
 __device__ __forceinline__ Cells leaf_cells(int4 r, int ltx0, int lty0, int ltx1, int lty1, int sh)
 {
-    const int x0 = max(r.x, ltx0) - ltx0, x1 = min(r.z, ltx1) - ltx0;
-    const int y0 = max(r.y, lty0) - lty0, y1 = min(r.w, lty1) - lty0;
+    const int x0 = max(r.x, ltx0), x1 = min(r.z, ltx1);
+    const int y0 = max(r.y, lty0), y1 = min(r.w, lty1);
     Cells c{0, 0, 0, 0};
     if (x0 < x1 && y0 < y1) {
-        c.cx0 = x0 >> sh;
-        c.cy0 = y0 >> sh;
-        c.w = ((x1 - 1) >> sh) - c.cx0 + 1;
-        c.h = ((y1 - 1) >> sh) - c.cy0 + 1;
+        c.cx0 = (x0 >> sh) - (ltx0 >> sh);
+        c.cy0 = (y0 >> sh) - (lty0 >> sh);
+        c.w = ((x1 - 1) >> sh) - (x0 >> sh) + 1;
+        c.h = ((y1 - 1) >> sh) - (y0 >> sh) + 1;
     }
     return c;
 }
@@ -188,21 +189,22 @@ __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int T
                                               const uint64_t* __restrict__ soff, const uint32_t* __restrict__ ioff,
                                               const uint32_t* __restrict__ item_sc,
                                               const uint32_t* __restrict__ group, const int4* __restrict__ rect,
-                                              uint64_t* __restrict__ pos, uint64_t n_values,
+                                              uint32_t* __restrict__ pos, uint64_t n_values,
                                               uint32_t* __restrict__ values)
 {
     FineItem it;
     if (!fine_item(soff, ioff, item_sc, n_super, it)) return;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int lx0 = (it.sc % SW) << kSuperShift, ly0 = ((it.sc / SW) << kSuperShift) + 2 * wave;
-    if (ly0 >= THL) return;
-    const int nx = min(8, TWL - lx0), ny = min(2, THL - ly0);
-    const int gx0 = ltx0 + lx0, gy0 = lty0 + ly0;
-    uint64_t* wp = pos + it.item * 64 + wave * 16;   // this wave's 16 tiles of the item
-    uint64_t cur[16];
+    // global tile coordinates of this wave's 2 x 8 tiles of the super-tile;
+    // tiles outside the leaf (super-tiles straddling its border) are skipped
+    const int gx0 = (((ltx0 >> kSuperShift) + it.sc % SW) << kSuperShift);
+    const int gy0 = (((lty0 >> kSuperShift) + it.sc / SW) << kSuperShift) + 2 * wave;
+    if (gy0 >= lty0 + THL || gy0 + 2 <= lty0) return;
+    uint32_t* wp = pos + it.item * 64 + wave * 16;   // this wave's 16 tiles of the item
+    uint32_t cur[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) cur[q] = WRITE ? wp[q] : 0;
+    for (int q = 0; q < 16; ++q) cur[q] = WRITE ? wp[q] : 0u;
     const uint64_t b = it.b, e = it.e;
     uint32_t s_c = 0, s_n = 0;
     int4 r_c = make_int4(0, 0, 0, 0);
@@ -217,25 +219,24 @@ __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int T
         const bool ok = k + lane < e;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const int c = q & 7, rr = q >> 3;
-            if (c >= nx || rr >= ny) continue;
-            const int gx = gx0 + c, gy = gy0 + rr;
+            const int gx = gx0 + (q & 7), gy = gy0 + (q >> 3);
+            if (gx < ltx0 || gx >= ltx0 + TWL || gy < lty0 || gy >= lty0 + THL) continue;
             const bool cov = ok && r_c.x <= gx && gx < r_c.z && r_c.y <= gy && gy < r_c.w;
             const uint64_t m = gsd::ballot(cov);
             if (WRITE && cov) {
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                const uint64_t p = cur[q] + below;
+                const uint32_t p = cur[q] + below;
                 if (p < n_values) values[p] = s_c;   // always true when the counts agree
             }
-            cur[q] += (uint64_t)__builtin_popcountll(m);
+            cur[q] += (uint32_t)__builtin_popcountll(m);
         }
         s_c = s_n;
         r_c = r_n;
         s_n = s_nn;
     }
     if (!WRITE && lane < 16) {
-        uint64_t v = 0;
+        uint32_t v = 0;
 #pragma unroll
         for (int q = 0; q < 16; ++q)
             if (lane == q) v = cur[q];
@@ -278,18 +279,20 @@ __global__ __launch_bounds__(1024) void k_fine_items(const uint64_t* __restrict_
 }
 
 // per (super-tile, tile): item counts -> write positions, in item order
-__global__ __launch_bounds__(256) void k_fine_scan(int TWL, int THL, int SW, int n_super,
-                                                   const uint32_t* __restrict__ ioff, const uint64_t* __restrict__ toff,
-                                                   uint64_t* __restrict__ pos)
+// (positions inside the leaf's slot array, < 2^32)
+__global__ __launch_bounds__(256) void k_fine_scan(int ltx0, int lty0, int TWL, int THL, int SW, int n_super,
+                                                   const uint32_t* __restrict__ ioff,
+                                                   const uint64_t* __restrict__ toff, uint32_t* __restrict__ pos)
 {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= (int64_t)n_super * 64) return;
     const int sc = (int)(g >> 6), j = (int)(g & 63);
-    const int lx = ((sc % SW) << kSuperShift) + (j & 7), ly = ((sc / SW) << kSuperShift) + (j >> 3);
-    if (lx >= TWL || ly >= THL) return;
-    uint64_t p = toff[(int64_t)ly * TWL + lx];
+    const int gx = (((ltx0 >> kSuperShift) + sc % SW) << kSuperShift) + (j & 7);
+    const int gy = (((lty0 >> kSuperShift) + sc / SW) << kSuperShift) + (j >> 3);
+    if (gx < ltx0 || gx >= ltx0 + TWL || gy < lty0 || gy >= lty0 + THL) return;
+    uint32_t p = (uint32_t)toff[(int64_t)(gy - lty0) * TWL + (gx - ltx0)];
     for (uint32_t i = ioff[sc]; i < ioff[sc + 1]; ++i) {
-        const uint64_t c = pos[(int64_t)i * 64 + j];
+        const uint32_t c = pos[(int64_t)i * 64 + j];
         pos[(int64_t)i * 64 + j] = p;
         p += c;
     }
@@ -342,8 +345,8 @@ __global__ void k_export_keys(int64_t n_tiles, int ltx0, int lty0, int TWL, int 
 
 }  // namespace
 
-int super_cols(gs_tile_rect leaf) { return (leaf.tx1 - leaf.tx0 + (1 << kSuperShift) - 1) >> kSuperShift; }
-int super_rows(gs_tile_rect leaf) { return (leaf.ty1 - leaf.ty0 + (1 << kSuperShift) - 1) >> kSuperShift; }
+int super_cols(gs_tile_rect leaf) { return ((leaf.tx1 - 1) >> kSuperShift) - (leaf.tx0 >> kSuperShift) + 1; }
+int super_rows(gs_tile_rect leaf) { return ((leaf.ty1 - 1) >> kSuperShift) - (leaf.ty0 >> kSuperShift) + 1; }
 int64_t super_cells(gs_tile_rect leaf) { return (int64_t)super_cols(leaf) * super_rows(leaf); }
 int super_shift() { return kSuperShift; }
 
@@ -413,7 +416,7 @@ int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells)
 
 gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
                             const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* item_sc,
-                            uint32_t* ioff, uint64_t* pos, uint64_t n_values, uint32_t* values)
+                            uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values)
 {
     const int n_super = (int)super_cells(leaf);
     const int64_t items = fine_items_bound(leaf, n_cells);
@@ -424,7 +427,7 @@ gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
     hipLaunchKernelGGL(k_fine<false>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
                        SW, n_super, soff, ioff, item_sc, group, proj->rect, pos, n_values, values);
     hipLaunchKernelGGL(k_fine_scan, dim3((unsigned)ceil_div((int64_t)n_super * 64, 256)), dim3(256), 0, ctx->stream,
-                       TWL, THL, SW, n_super, ioff, toff, pos);
+                       leaf.tx0, leaf.ty0, TWL, THL, SW, n_super, ioff, toff, pos);
     hipLaunchKernelGGL(k_fine<true>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
                        SW, n_super, soff, ioff, item_sc, group, proj->rect, pos, n_values, values);
     GS_HIP(ctx, hipGetLastError());

@@ -218,6 +218,7 @@ static void clear_plan(gs_ctx* ctx, gs_proj* proj, bool retire)
     proj->plan_cells.clear();
     proj->plan_cbase.clear();
     proj->plan_tbase.clear();
+    proj->plan_isect.clear();
     proj->plan_cands = nullptr;
     proj->plan_coff = nullptr;
     proj->plan_toff = nullptr;
@@ -237,6 +238,8 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     std::vector<gs_leaf> plan(nl);
     std::vector<uint64_t> hoff(nl + 1, 0), hcells(nl, 0), tbase(nl + 1, 0);
     std::vector<uint32_t> hlc(2 * (size_t)nl, 0), cbase(nl, 0);
+    std::vector<uint64_t> hisect(nl, 0);
+    uint64_t* lisect = nullptr;
     uint64_t G = 0;
     bool second = false;
     uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr, *ccnt = nullptr, *coff = nullptr;
@@ -263,9 +266,10 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     ccnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     coff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (G + 1), GS_MEM_PROJ, &proj->plan_allocs);
     lcells = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * 2 * nl, GS_MEM_SCRATCH, &tmp);
+    lisect = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * nl, GS_MEM_SCRATCH, &tmp);
     dtbase = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
     toff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
-    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !lcells || !dtbase || !toff) {
+    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !lcells || !lisect || !dtbase || !toff) {
         st = GS_ERR_OOM;
         goto out;
     }
@@ -275,11 +279,13 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
     if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, segoff)) != GS_OK) goto out;
     if ((st = launch_plan_offsets(ctx, proj, ldev, nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0, segoff, ccnt,
-                                  coff, lcells, dtbase, toff)) != GS_OK)
+                                  coff, lcells, lisect, dtbase, toff)) != GS_OK)
         goto out;
     e = hipMemcpyAsync(hoff.data(), segoff, sizeof(uint64_t) * (nl + 1), hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(hlc.data(), lcells, sizeof(uint32_t) * 2 * nl, hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(hisect.data(), lisect, sizeof(uint64_t) * nl, hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
     for (int32_t L = 0; L < nl; ++L) {
@@ -295,6 +301,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     proj->plan_cells.swap(hcells);
     proj->plan_cbase.swap(cbase);
     proj->plan_tbase.swap(tbase);
+    proj->plan_isect.swap(hisect);
 out:
     gs_free_all(ctx, &tmp);
     if (st != GS_OK) clear_plan(ctx, proj, false);
@@ -307,7 +314,7 @@ struct PlanLeaf {
     bool found = false;
     const uint32_t* list = nullptr;   // candidates meeting the leaf, depth order
     int64_t n = 0;
-    int64_t isect = -1;               // from the plan's estimate, or -1
+    int64_t isect = -1;               // from the plan's tile offsets
     int64_t cells = 0;                // coarse pairs
     const uint32_t* eoff = nullptr;   // their offsets (subtract ebase)
     uint32_t ebase = 0;
@@ -328,14 +335,7 @@ static PlanLeaf plan_leaf(const gs_proj* proj, gs_tile_rect leaf)
             r.eoff = proj->plan_coff + proj->plan_off[k];
             r.ebase = proj->plan_cbase[k];
             r.toff = proj->plan_toff + proj->plan_tbase[k];
-            // est = bI I + bP P + bT T + b0 determines I when bI > 0
-            const gs_cost_model& c = proj->plan_cost;
-            const uint64_t P = (uint64_t)(std::min(L.tx1 * 16, proj->W) - L.tx0 * 16) *
-                               (uint64_t)(std::min(L.ty1 * 16, proj->H) - L.ty0 * 16);
-            const uint64_t T = (uint64_t)(L.tx1 - L.tx0) * (uint64_t)(L.ty1 - L.ty0);
-            const uint64_t rest = c.b_pixel * P + c.b_tile * T + c.b_const;
-            if (c.b_isect > 0 && L.est_bytes >= rest && (L.est_bytes - rest) % c.b_isect == 0)
-                r.isect = (int64_t)((L.est_bytes - rest) / c.b_isect);
+            r.isect = (int64_t)proj->plan_isect[k];
             return r;
         }
     }
@@ -458,20 +458,23 @@ gs_status gs_kernel_time(gs_ctx* ctx, const char* name, double* total_ms, int64_
 
 gs_cost_model gs_default_cost_model(void)
 {
-    // bytes the library allocates for one leaf (L1 fused), peak of binning
-    // and rasterization together:
-    //   per intersection: tile keys u32 x 2 and slots u32 x 2 (radix sort
-    //     ping-pong; one slot array is kept), radix histograms and their scan
-    //     (2 x 256 u32 per 2048 entries), and the per-candidate tile counts
-    //     u32 + emission offsets u64 (at most one candidate per intersection)
-    //     which are freed before the sort buffers peak -> 17 B
-    //   per pixel: T_final f32 + last u32 + L1 signs u8 -> 9 B
-    //   per tile: offsets u64 + 4 L1 partials f64 -> 40 B
-    //   constant: scan block sums, allocation rounding, small buffers
+    // Upper bounds of the bytes the library allocates for a planned leaf (L1
+    // fused), each phase bounded by the sum of the terms:
+    //   coarse sort of the C coarse pairs (C <= Cb): keys u32 x 2 and slots
+    //     u32 x 2 (ping-pong) + histograms and their scan (2 x 256 u32 per
+    //     2048 pairs) -> 17 B per pair;
+    //   fine lists: slots u32 per intersection, the grouped slots u32 per
+    //     pair, per work item (at most one per super-tile, so per tile, plus
+    //     one per 512 pairs) 64 u32 positions, its super-tile and offsets
+    //     -> 4 B per intersection, 5 B per pair, 272 B per tile;
+    //   rasterization: the slots, T_final f32 + last u32 + L1 signs u8 per
+    //     pixel, 4 f64 L1 partials per tile -> 4 B, 9 B, 32 B;
+    //   constant: scan block sums, allocation rounding, small buffers.
     gs_cost_model c;
-    c.b_isect = 17;
+    c.b_isect = 4;
+    c.b_cell = 17;
     c.b_pixel = 9;
-    c.b_tile = 40;
+    c.b_tile = 320;
     c.b_const = 1u << 20;
     return c;
 }
@@ -649,7 +652,7 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         C = hc;
     }
     if (pl.found && pl.isect >= 0) {
-        I = (uint64_t)pl.isect;    // from the plan's summed-area table: no read-back
+        I = (uint64_t)pl.isect;    // read back with the plan: no synchronisation here
     } else if ((st = readback(ctx, b->offsets + b->n_tiles, sizeof(uint64_t), &I)) != GS_OK) {
         goto fail;
     }
@@ -686,7 +689,7 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(I, 1), GS_MEM_RASTER, &b->allocs);
         uint32_t* item_sc = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * items, GS_MEM_RASTER, &tmp);
         uint32_t* ioff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n_super + 1), GS_MEM_RASTER, &tmp);
-        uint64_t* pos = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * 64 * items, GS_MEM_RASTER, &tmp);
+        uint32_t* pos = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * 64 * items, GS_MEM_RASTER, &tmp);
         if (!b->values || !item_sc || !ioff || !pos) { st = GS_ERR_OOM; goto fail; }
         if ((st = launch_fine_lists(ctx, proj, leaf, soff, second ? v1 : v0, C, b->offsets, item_sc, ioff, pos, I,
                                     b->values)) != GS_OK)

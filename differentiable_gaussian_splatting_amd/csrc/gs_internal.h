@@ -67,6 +67,7 @@ struct gs_proj : GsHandle {
     std::vector<uint64_t> plan_cells; // per leaf: (super-tile, candidate) pairs of its coarse level
     std::vector<uint32_t> plan_cbase; // per leaf: value of plan_coff at its first group entry
     std::vector<uint64_t> plan_tbase; // per leaf: start of its tile offsets in plan_toff
+    std::vector<uint64_t> plan_isect; // per leaf: intersections
     uint32_t* plan_coff = nullptr;    // device [entries + 1] scan of the entries' coarse pair counts
     uint64_t* plan_toff = nullptr;    // device: per leaf, its tile offsets [T_L + 1]
     std::vector<GsAlloc> plan_retired; // earlier plans (bins may still point into them)
@@ -140,7 +141,7 @@ gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
 // list: candidate slots to visit (NULL: all n_cand), n_list entries
 gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                            int64_t n_list, int32_t* diff);
-// super-tiles (8 x 8 tiles, aligned to the leaf origin) of a leaf
+// super-tiles (8 x 8 tiles, aligned to the image) meeting a leaf
 int super_cols(gs_tile_rect leaf);
 int super_rows(gs_tile_rect leaf);
 int64_t super_cells(gs_tile_rect leaf);
@@ -157,11 +158,11 @@ gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
 // per-tile lists from the super-tile groups (soff: group offsets, toff: tile offsets)
 // Work items of the fine level (segments of the super-tile groups), an upper
 // bound for n_cells coarse pairs; scratch: item_sc u32 [items], ioff u32
-// [n_super + 1], pos u64 [items * 64]
+// [n_super + 1], pos u32 [items * 64]
 int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells);
 gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
                             const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* item_sc,
-                            uint32_t* ioff, uint64_t* pos, uint64_t n_values, uint32_t* values);
+                            uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values);
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets);
 gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
 gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);
@@ -196,7 +197,7 @@ gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* lea
 gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
                               int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
                               const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
-                              uint32_t* leaf_cells, const uint64_t* toff_base, uint64_t* toff);
+                              uint32_t* leaf_cells, uint64_t* leaf_isect, const uint64_t* toff_base, uint64_t* toff);
 
 // loss.hip
 gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,

@@ -8,8 +8,13 @@
 // longer side (ties: x) is halved at floor(len/2) and both halves are planned
 // in order (depth-first order of the leaves).
 //
-// Per-tile overlap counts come from the same 2D difference array as binning;
-// a summed-area table makes every region's overlap count O(1).  The split
+// Reading of the load estimate (the library's own allocation bounds):
+//   est = bI I + bC Cb + bP P + bT T + b0
+// with I the region's Gaussian-tile overlaps and Cb the (candidate,
+// super-cell) pairs over the image-aligned 8 x 8-tile super-cells the region
+// meets -- an upper bound of the coarse pairs its binning sorts.  Per-tile
+// and per-super-cell counts come from 2D difference arrays; summed-area
+// tables make every region's I and Cb O(1).  The split
 // recursion runs in one workgroup, level by level: the frontier is kept in
 // depth-first order, and each level replaces every region to be split by its
 // two halves (a workgroup scan gives the output positions), so the final
@@ -29,25 +34,71 @@ __global__ void k_counts_to_sat(const int32_t* __restrict__ cnt, int TW, int TH,
 }
 
 struct PlanArgs {
-    int W, H, TW, TH;
-    uint64_t budget, bI, bP, bT, b0;
+    int W, H, TW, TH, SW;
+    uint64_t budget, bI, bP, bT, b0, bC;
+    const uint64_t* sat;     // (TH + 1) x (TW + 1), tile counts
+    const uint64_t* sat8;    // (SH + 1) x (SW + 1), super-cell counts
 };
 
-__device__ __forceinline__ uint64_t region_est(const PlanArgs& a, const uint64_t* __restrict__ sat, int4 r)
+__device__ __forceinline__ uint64_t sat_rect(const uint64_t* __restrict__ sat, int64_t S, int x0, int y0, int x1,
+                                             int y1)
 {
-    const int64_t S = a.TW + 1;
-    const uint64_t I = sat[(int64_t)r.w * S + r.z] - sat[(int64_t)r.y * S + r.z] - sat[(int64_t)r.w * S + r.x] +
-                       sat[(int64_t)r.y * S + r.x];
+    return sat[(int64_t)y1 * S + x1] - sat[(int64_t)y0 * S + x1] - sat[(int64_t)y1 * S + x0] +
+           sat[(int64_t)y0 * S + x0];
+}
+
+__device__ __forceinline__ uint64_t region_est(const PlanArgs& a, int4 r)
+{
+    const uint64_t I = sat_rect(a.sat, a.TW + 1, r.x, r.y, r.z, r.w);
+    const uint64_t Cb = sat_rect(a.sat8, a.SW + 1, r.x >> 3, r.y >> 3, ((r.z - 1) >> 3) + 1, ((r.w - 1) >> 3) + 1);
     const int64_t x1 = min<int64_t>((int64_t)r.z * 16, a.W), y1 = min<int64_t>((int64_t)r.w * 16, a.H);
     const uint64_t P = (uint64_t)(x1 - (int64_t)r.x * 16) * (uint64_t)(y1 - (int64_t)r.y * 16);
     const uint64_t T = (uint64_t)(r.z - r.x) * (uint64_t)(r.w - r.y);
-    return a.bI * I + a.bP * P + a.bT * T + a.b0;
+    return a.bI * I + a.bC * Cb + a.bP * P + a.bT * T + a.b0;
 }
 
-__device__ __forceinline__ bool region_split(const PlanArgs& a, const uint64_t* __restrict__ sat, int4 r)
+__device__ __forceinline__ bool region_split(const PlanArgs& a, int4 r)
 {
     const bool single = (r.z - r.x) == 1 && (r.w - r.y) == 1;
-    return !single && region_est(a, sat, r) > a.budget;
+    return !single && region_est(a, r) > a.budget;
+}
+
+// Difference array of the candidates' super-cell rectangles on the
+// [SH][SW] grid (add its 2D prefix for the counts).  A block takes
+// kCellBlock candidates into an LDS copy of the grid, then adds its nonzero
+// cells to the global grid: far fewer global atomics on the few cells.
+constexpr int kCellBlock = 8192;
+constexpr int kCellLds = 16384;    // cells of the LDS copy (64 KB)
+
+__global__ __launch_bounds__(256) void k_cell_diff(int64_t n, const int4* __restrict__ rect, int SW, int SH,
+                                                   int32_t* __restrict__ diff)
+{
+    extern __shared__ int32_t hd[];
+    const int64_t cells = (int64_t)SW * SH;
+    const bool lds = cells <= kCellLds;
+    if (lds) {
+        for (int64_t k = threadIdx.x; k < cells; k += blockDim.x) hd[k] = 0;
+        __syncthreads();
+    }
+    const int64_t c0 = (int64_t)blockIdx.x * kCellBlock;
+    for (int64_t k = c0 + threadIdx.x; k < min<int64_t>(n, c0 + kCellBlock); k += blockDim.x) {
+        const int4 r = rect[k];
+        if (!(r.x < r.z && r.y < r.w)) continue;
+        const int x0 = r.x >> 3, y0 = r.y >> 3, x1 = ((r.z - 1) >> 3) + 1, y1 = ((r.w - 1) >> 3) + 1;
+        auto add = [&](int y, int x, int v) {
+            if (lds) atomicAdd(&hd[(int64_t)y * SW + x], v);
+            else atomicAdd(&diff[(int64_t)y * SW + x], v);
+        };
+        add(y0, x0, 1);
+        if (x1 < SW) add(y0, x1, -1);
+        if (y1 < SH) add(y1, x0, -1);
+        if (x1 < SW && y1 < SH) add(y1, x1, 1);
+    }
+    if (lds) {
+        __syncthreads();
+        for (int64_t k = threadIdx.x; k < cells; k += blockDim.x)
+            if (hd[k]) atomicAdd(&diff[k], hd[k]);
+    }
 }
 
 constexpr int kPlanThreads = 1024;
@@ -74,7 +125,7 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* to
 }
 
 // frontier ping-pong in global memory; cap >= number of tiles
-__global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a, const uint64_t* __restrict__ sat,
+__global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a,
                                                        int4* __restrict__ fa, int4* __restrict__ fb, int64_t cap,
                                                        gs_leaf* __restrict__ leaves, int32_t max_leaves,
                                                        int32_t* __restrict__ count_out,
@@ -98,7 +149,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a, const uint64_
             bool sp = false;
             if (i < n) {
                 r = cur[i];
-                sp = region_split(a, sat, r);
+                sp = region_split(a, r);
             }
             const uint32_t w = i < n ? (sp ? 2u : 1u) : 0u;
             uint32_t tot;
@@ -131,7 +182,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a, const uint64_
     uint32_t over = 0;
     for (uint32_t i = threadIdx.x; i < n; i += kPlanThreads) {
         const int4 r = cur[i];
-        const uint64_t e = region_est(a, sat, r);
+        const uint64_t e = region_est(a, r);
         if (e > a.budget) over = 1;
         if ((int32_t)i < max_leaves) {
             gs_leaf L;
@@ -162,29 +213,56 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
                       gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev, int32_t* over_dev)
 {
     const int TW = proj->TW, TH = proj->TH;
+    const int SW = (TW + 7) >> 3, SH = (TH + 7) >> 3;
     const int64_t T = (int64_t)TW * TH;
     const int32_t* diff = proj->tile_cnt;
-    gs_status st = GS_OK;
     const int64_t S = (int64_t)(TW + 1) * (TH + 1);
     hipLaunchKernelGGL(k_counts_to_sat, dim3((unsigned)ceil_div(S, 256)), dim3(256), 0, ctx->stream, diff, TW, TH, sat);
-    if ((st = launch_prefix2d_u64(ctx, sat, TH + 1, TW + 1)) != GS_OK) return st;
+    gs_status st = launch_prefix2d_u64(ctx, sat, TH + 1, TW + 1);
+    if (st != GS_OK) return st;
 
     std::vector<GsAlloc> tmp;
     int4* fa = (int4*)gs_malloc(ctx, sizeof(int4) * T, GS_MEM_SCRATCH, &tmp);
     int4* fb = (int4*)gs_malloc(ctx, sizeof(int4) * T, GS_MEM_SCRATCH, &tmp);
-    if (!fa || !fb) {
+    int32_t* cgrid = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * SW * SH, GS_MEM_SCRATCH, &tmp);
+    uint64_t* sat8 = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (SW + 1) * (SH + 1), GS_MEM_SCRATCH, &tmp);
+    if (!fa || !fb || !cgrid || !sat8) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
+    // candidates per image-aligned super-cell of 8 x 8 tiles, and their table
+    if ((st = launch_fill_u32(ctx, (uint32_t*)cgrid, 0u, (int64_t)SW * SH)) != GS_OK) {
+        gs_free_all(ctx, &tmp);
+        return st;
+    }
+    if (proj->n_cand > 0) {
+        GsTimerScope ts(ctx, "rect_diff");
+        const size_t lds = (int64_t)SW * SH <= kCellLds ? sizeof(int32_t) * SW * SH : 0;
+        hipLaunchKernelGGL(k_cell_diff, dim3((unsigned)ceil_div(proj->n_cand, kCellBlock)), dim3(256), lds,
+                           ctx->stream, proj->n_cand, proj->rect, SW, SH, cgrid);
+    }
+    if ((st = launch_prefix2d_i32(ctx, cgrid, SH, SW)) != GS_OK) {
+        gs_free_all(ctx, &tmp);
+        return st;
+    }
+    const int64_t S8 = (int64_t)(SW + 1) * (SH + 1);
+    hipLaunchKernelGGL(k_counts_to_sat, dim3((unsigned)ceil_div(S8, 256)), dim3(256), 0, ctx->stream, cgrid, SW, SH,
+                       sat8);
+    if ((st = launch_prefix2d_u64(ctx, sat8, SH + 1, SW + 1)) != GS_OK) {
+        gs_free_all(ctx, &tmp);
+        return st;
+    }
     PlanArgs a;
-    a.W = proj->W; a.H = proj->H; a.TW = TW; a.TH = TH;
+    a.W = proj->W; a.H = proj->H; a.TW = TW; a.TH = TH; a.SW = SW;
     a.budget = budget;
-    a.bI = cost->b_isect; a.bP = cost->b_pixel; a.bT = cost->b_tile; a.b0 = cost->b_const;
+    a.bI = cost->b_isect; a.bP = cost->b_pixel; a.bT = cost->b_tile; a.b0 = cost->b_const; a.bC = cost->b_cell;
+    a.sat = sat;
+    a.sat8 = sat8;
     GS_HIP(ctx, hipMemsetAsync(over_dev, 0, sizeof(int32_t), ctx->stream));
     {
         GsTimerScope ts(ctx, "plan_split");
-        hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, ctx->stream, a, sat, fa, fb, T, leaves_dev,
-                           max_leaves, count_dev, over_dev);
+        hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, ctx->stream, a, fa, fb, T, leaves_dev, max_leaves,
+                           count_dev, over_dev);
     }
     gs_free_all(ctx, &tmp);
     GS_HIP(ctx, hipGetLastError());
@@ -264,8 +342,9 @@ __global__ __launch_bounds__(256) void k_group_cells(int64_t n, const uint32_t* 
     if (k >= n) return;
     const gs_leaf lf = leaves[leaf_of[k]];
     const int4 r = rect[slot[k]];
-    const int x0 = max(r.x, lf.tx0) - lf.tx0, x1 = min(r.z, lf.tx1) - lf.tx0;
-    const int y0 = max(r.y, lf.ty0) - lf.ty0, y1 = min(r.w, lf.ty1) - lf.ty0;
+    // image-aligned super-cells that the rectangle meets inside the leaf
+    const int x0 = max(r.x, lf.tx0), x1 = min(r.z, lf.tx1);
+    const int y0 = max(r.y, lf.ty0), y1 = min(r.w, lf.ty1);
     uint32_t c = 0;
     if (x0 < x1 && y0 < y1)
         c = (uint32_t)((((x1 - 1) >> sh) - (x0 >> sh) + 1) * (((y1 - 1) >> sh) - (y0 >> sh) + 1));
@@ -273,15 +352,20 @@ __global__ __launch_bounds__(256) void k_group_cells(int64_t n, const uint32_t* 
 }
 
 // per leaf: the scan value at its first entry and its number of coarse pairs
-// (u32 arithmetic modulo 2^32: exact for any leaf with fewer than 2^32 pairs)
+// (u32 arithmetic modulo 2^32: exact for any leaf with fewer than 2^32
+// pairs), and its intersections (the last of its tile offsets)
 __global__ void k_leaf_cell_bounds(int nl, const uint64_t* __restrict__ goff, const uint32_t* __restrict__ coff,
-                                   uint32_t* __restrict__ out)
+                                   const gs_leaf* __restrict__ leaves, const uint64_t* __restrict__ toff_base,
+                                   const uint64_t* __restrict__ toff, uint32_t* __restrict__ out,
+                                   uint64_t* __restrict__ isect)
 {
     const int L = blockIdx.x * blockDim.x + threadIdx.x;
     if (L >= nl) return;
     const uint32_t a = coff[goff[L]], b = coff[goff[L + 1]];
     out[2 * L] = a;
     out[2 * L + 1] = b - a;
+    const gs_leaf lf = leaves[L];
+    isect[L] = toff[toff_base[L] + (uint64_t)(lf.tx1 - lf.tx0) * (uint64_t)(lf.ty1 - lf.ty0)];
 }
 
 // per leaf (one workgroup): exclusive scan of its tiles' candidate counts in
@@ -324,7 +408,7 @@ __global__ __launch_bounds__(1024) void k_leaf_toff(const gs_leaf* __restrict__ 
 gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
                               int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
                               const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
-                              uint32_t* leaf_cells, const uint64_t* toff_base, uint64_t* toff)
+                              uint32_t* leaf_cells, uint64_t* leaf_isect, const uint64_t* toff_base, uint64_t* toff)
 {
     GsTimerScope ts(ctx, "leaf_groups");
     if (n_entries > 0)
@@ -333,10 +417,10 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
     gs_status st = launch_scan_u32_to_u32(ctx, cell_cnt, cell_off, n_entries);
     if (st != GS_OK) return st;
     if (n_leaves > 0) {
-        hipLaunchKernelGGL(k_leaf_cell_bounds, dim3((unsigned)ceil_div(n_leaves, 256)), dim3(256), 0, ctx->stream,
-                           n_leaves, group_off, cell_off, leaf_cells);
         hipLaunchKernelGGL(k_leaf_toff, dim3((unsigned)n_leaves), dim3(1024), 0, ctx->stream, leaves_dev,
                            proj->tile_cnt, proj->TW, toff_base, toff);
+        hipLaunchKernelGGL(k_leaf_cell_bounds, dim3((unsigned)ceil_div(n_leaves, 256)), dim3(256), 0, ctx->stream,
+                           n_leaves, group_off, cell_off, leaves_dev, toff_base, toff, leaf_cells, leaf_isect);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;

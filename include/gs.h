@@ -117,12 +117,16 @@ typedef struct {
     int32_t pad;
 } gs_leaf;
 
-/* Leaf load model: est = b_isect * I + b_pixel * P + b_tile * T + b_const,
- * I = Gaussian-tile overlaps of the leaf, P = its pixels inside the image,
- * T = its tiles.  gs_default_cost_model() returns the library's own
+/* Leaf load model:
+ *   est = b_isect * I + b_cell * Cb + b_pixel * P + b_tile * T + b_const,
+ * I = Gaussian-tile overlaps of the leaf, Cb = (candidate, super-cell) pairs
+ * over the image-aligned super-cells of 8 x 8 tiles that the leaf meets (a
+ * candidate meets a super-cell when its tile rectangle does; an upper bound
+ * of the coarse pairs the leaf's binning sorts), P = its pixels inside the
+ * image, T = its tiles.  gs_default_cost_model() returns the library's own
  * allocation sizes, which make est an upper bound of the bytes that
- * gs_bin_sort + gs_render_fwd allocate for that leaf (L1 loss inline). */
-typedef struct { uint64_t b_isect, b_pixel, b_tile, b_const; } gs_cost_model;
+ * gs_bin_sort + gs_render_fwd allocate for a planned leaf (L1 loss inline). */
+typedef struct { uint64_t b_isect, b_pixel, b_tile, b_const, b_cell; } gs_cost_model;
 
 enum { GS_MEM_PROJ = 0, GS_MEM_RASTER = 1, GS_MEM_GRAD = 2, GS_MEM_LOSS = 3, GS_MEM_SCRATCH = 4,
        GS_MEM_NCAT = 5 };

@@ -47,7 +47,7 @@ class Leaf_c(C.Structure):
 
 class Cost_c(C.Structure):
     _fields_ = [("b_isect", C.c_uint64), ("b_pixel", C.c_uint64), ("b_tile", C.c_uint64),
-                ("b_const", C.c_uint64)]
+                ("b_const", C.c_uint64), ("b_cell", C.c_uint64)]
 
 
 FLAG_CLAMP_R, FLAG_CLAMP_G, FLAG_CLAMP_B, FLAG_CLAMP_UX, FLAG_CLAMP_UY = 1, 2, 4, 8, 16
@@ -93,7 +93,7 @@ def _declare(L):
     L.gso_plan_leaves.restype = i32
     L.gso_plan_leaves.argtypes = [i32, i32, i64, vp, u64, C.POINTER(Cost_c), vp, i32, vp]
     L.gso_leaf_estimate.restype = u64
-    L.gso_leaf_estimate.argtypes = [i32, i32, Rect_c, u64, C.POINTER(Cost_c)]
+    L.gso_leaf_estimate.argtypes = [i32, i32, Rect_c, u64, u64, C.POINTER(Cost_c)]
     L.gso_adam.argtypes = [i64, vp, vp, vp, vp, i32, dbl, dbl, dbl, dbl]
 
 
@@ -239,12 +239,13 @@ def project_bwd(cam, scene, cand, flags, slot_of, grad2d):
     return grad3d
 
 
-DEFAULT_COST = dict(b_isect=17, b_pixel=9, b_tile=40, b_const=1 << 20)
+DEFAULT_COST = dict(b_isect=4, b_cell=17, b_pixel=9, b_tile=320, b_const=1 << 20)
 
 
 def cost_struct(cost=None) -> Cost_c:
-    c = dict(DEFAULT_COST, **(cost or {}))
-    return Cost_c(c["b_isect"], c["b_pixel"], c["b_tile"], c["b_const"])
+    """A cost given without b_cell has no super-cell term."""
+    c = dict(DEFAULT_COST) if cost is None else dict(dict(b_cell=0), **cost)
+    return Cost_c(c["b_isect"], c["b_pixel"], c["b_tile"], c["b_const"], c["b_cell"])
 
 
 def plan_leaves(cam, rect_c, budget, cost=None, with_sat=False):
@@ -262,9 +263,9 @@ def plan_leaves(cam, rect_c, budget, cost=None, with_sat=False):
     return (leaves, sat) if with_sat else leaves
 
 
-def leaf_estimate(cam, r: Rect_c, n_isect, cost=None):
+def leaf_estimate(cam, r: Rect_c, n_isect, cost=None, n_cells=0):
     cs = cost_struct(cost)
-    return int(lib().gso_leaf_estimate(cam.width, cam.height, r, int(n_isect), C.byref(cs)))
+    return int(lib().gso_leaf_estimate(cam.width, cam.height, r, int(n_isect), int(n_cells), C.byref(cs)))
 
 
 def adam(grad, param, m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-15):

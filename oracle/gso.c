@@ -612,39 +612,46 @@ void gso_project_bwd(const gso_camera* cam, int64_t n, int deg,
  * actual load, estimated from overlap counts, pixels and buffer layout, so
  * that dense regions become smaller; Fig. 3 B->C: regions over the budget
  * are subdivided further.  Reading: load estimate
- *   est = bI * I + bP * P + bT * T + b0
- * (I = Gaussian-tile overlaps in the region, P = its pixels inside the
- * image, T = its tiles); a region is kept when est <= budget or it is one
- * tile, otherwise its longer side (in tiles, ties -> x) is halved at
- * floor(len/2) and the halves are planned in order.                       */
-uint64_t gso_leaf_estimate(int32_t W, int32_t H, gso_rect r, uint64_t n_isect, const gso_cost* cost)
+ *   est = bI * I + bC * Cb + bP * P + bT * T + b0
+ * (I = Gaussian-tile overlaps in the region, Cb = pairs (candidate,
+ * super-cell) over the image-aligned 8x8-tile super-cells the region meets,
+ * where a candidate meets a super-cell when its tile rectangle does,
+ * P = the region's pixels inside the image, T = its tiles); a region is kept
+ * when est <= budget or it is one tile, otherwise its longer side (in tiles,
+ * ties -> x) is halved at floor(len/2) and the halves are planned in order. */
+uint64_t gso_leaf_estimate(int32_t W, int32_t H, gso_rect r, uint64_t n_isect, uint64_t n_cells,
+                           const gso_cost* cost)
 {
     const int64_t x1 = (int64_t)r.tx1 * 16 < W ? (int64_t)r.tx1 * 16 : W;
     const int64_t y1 = (int64_t)r.ty1 * 16 < H ? (int64_t)r.ty1 * 16 : H;
     const uint64_t P = (uint64_t)(x1 - (int64_t)r.tx0 * 16) * (uint64_t)(y1 - (int64_t)r.ty0 * 16);
     const uint64_t T = (uint64_t)(r.tx1 - r.tx0) * (uint64_t)(r.ty1 - r.ty0);
-    return cost->b_isect * n_isect + cost->b_pixel * P + cost->b_tile * T + cost->b_const;
+    return cost->b_isect * n_isect + cost->b_cell * n_cells + cost->b_pixel * P + cost->b_tile * T +
+           cost->b_const;
 }
 
 typedef struct {
-    int32_t W, H, TW;
-    const uint64_t* sat;
+    int32_t W, H, TW, SW;
+    const uint64_t* sat;    /* (TH+1) x (TW+1), tile counts */
+    const uint64_t* sat8;   /* (SH+1) x (SW+1), super-cell counts */
     uint64_t budget;
     const gso_cost* cost;
     gso_leaf* out;
     int32_t max_leaves, count;
 } plan_ctx;
 
-static uint64_t sat_sum(const plan_ctx* pc, gso_rect r)
+static uint64_t rect_sum(const uint64_t* sat, int64_t S, int32_t x0, int32_t y0, int32_t x1, int32_t y1)
 {
-    const int64_t S = pc->TW + 1;
-    return pc->sat[(int64_t)r.ty1 * S + r.tx1] - pc->sat[(int64_t)r.ty0 * S + r.tx1]
-           - pc->sat[(int64_t)r.ty1 * S + r.tx0] + pc->sat[(int64_t)r.ty0 * S + r.tx0];
+    return sat[(int64_t)y1 * S + x1] - sat[(int64_t)y0 * S + x1] - sat[(int64_t)y1 * S + x0] +
+           sat[(int64_t)y0 * S + x0];
 }
 
 static void plan_rec(plan_ctx* pc, gso_rect r)
 {
-    const uint64_t est = gso_leaf_estimate(pc->W, pc->H, r, sat_sum(pc, r), pc->cost);
+    const uint64_t I = rect_sum(pc->sat, pc->TW + 1, r.tx0, r.ty0, r.tx1, r.ty1);
+    const uint64_t Cb = rect_sum(pc->sat8, pc->SW + 1, r.tx0 / 8, r.ty0 / 8, (r.tx1 - 1) / 8 + 1,
+                                 (r.ty1 - 1) / 8 + 1);
+    const uint64_t est = gso_leaf_estimate(pc->W, pc->H, r, I, Cb, pc->cost);
     const int32_t w = r.tx1 - r.tx0, h = r.ty1 - r.ty0;
     if (est <= pc->budget || (w == 1 && h == 1)) {
         if (pc->count < pc->max_leaves) {
@@ -664,28 +671,43 @@ static void plan_rec(plan_ctx* pc, gso_rect r)
     plan_rec(pc, b);
 }
 
+/* summed-area table (rows+1) x (cols+1) of a count grid rows x cols */
+static void make_sat(const uint64_t* cnt, int32_t rows, int32_t cols, uint64_t* sat)
+{
+    const int64_t S = cols + 1;
+    for (int64_t k = 0; k < S * (rows + 1); ++k) sat[k] = 0;
+    for (int32_t y = 0; y < rows; ++y)
+        for (int32_t x = 0; x < cols; ++x)
+            sat[(int64_t)(y + 1) * S + x + 1] = cnt[(int64_t)y * cols + x] + sat[(int64_t)y * S + x + 1]
+                                                + sat[(int64_t)(y + 1) * S + x] - sat[(int64_t)y * S + x];
+}
+
 int32_t gso_plan_leaves(int32_t W, int32_t H, int64_t n_cand, const int32_t* rect,
                         uint64_t budget, const gso_cost* cost, gso_leaf* out,
                         int32_t max_leaves, uint64_t* sat_out)
 {
     const int32_t TW = (W + 15) / 16, TH = (H + 15) / 16;
-    const int64_t S = TW + 1;
+    const int32_t SW = (TW + 7) / 8, SH = (TH + 7) / 8;
     uint64_t* cnt = (uint64_t*)calloc((size_t)TW * TH, sizeof(uint64_t));
-    uint64_t* sat = sat_out ? sat_out : (uint64_t*)malloc(sizeof(uint64_t) * S * (TH + 1));
+    uint64_t* cnt8 = (uint64_t*)calloc((size_t)SW * SH, sizeof(uint64_t));
+    uint64_t* sat = sat_out ? sat_out : (uint64_t*)malloc(sizeof(uint64_t) * (TW + 1) * (TH + 1));
+    uint64_t* sat8 = (uint64_t*)malloc(sizeof(uint64_t) * (SW + 1) * (SH + 1));
     for (int64_t j = 0; j < n_cand; ++j) {
         const int32_t* r = rect + 4 * j;
         for (int32_t ty = r[1]; ty < r[3]; ++ty)
             for (int32_t tx = r[0]; tx < r[2]; ++tx) cnt[(int64_t)ty * TW + tx] += 1;
+        if (r[0] < r[2] && r[1] < r[3])
+            for (int32_t sy = r[1] / 8; sy <= (r[3] - 1) / 8; ++sy)
+                for (int32_t sx = r[0] / 8; sx <= (r[2] - 1) / 8; ++sx) cnt8[(int64_t)sy * SW + sx] += 1;
     }
-    for (int64_t k = 0; k < S * (TH + 1); ++k) sat[k] = 0;
-    for (int32_t ty = 0; ty < TH; ++ty)
-        for (int32_t tx = 0; tx < TW; ++tx)
-            sat[(int64_t)(ty + 1) * S + tx + 1] = cnt[(int64_t)ty * TW + tx] + sat[(int64_t)ty * S + tx + 1]
-                                                  + sat[(int64_t)(ty + 1) * S + tx] - sat[(int64_t)ty * S + tx];
-    plan_ctx pc = {W, H, TW, sat, budget, cost, out, max_leaves, 0};
+    make_sat(cnt, TH, TW, sat);
+    make_sat(cnt8, SH, SW, sat8);
+    plan_ctx pc = {W, H, TW, SW, sat, sat8, budget, cost, out, max_leaves, 0};
     gso_rect all = {0, 0, TW, TH};
     plan_rec(&pc, all);
     free(cnt);
+    free(cnt8);
+    free(sat8);
     if (!sat_out) free(sat);
     return pc.count;
 }

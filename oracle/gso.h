@@ -67,8 +67,10 @@ typedef struct {
     int32_t pad;
 } gso_leaf;
 
-typedef struct {          /* leaf load model: bytes = bI*I + bP*P + bT*T + b0 */
+typedef struct {          /* leaf load model: bytes = bI*I + bP*P + bT*T + b0 + bC*Cb */
     uint64_t b_isect, b_pixel, b_tile, b_const;
+    uint64_t b_cell;      /* per candidate-(8x8-tile super-cell) pair of the region, counted
+                             over the image-aligned super-cells the region meets */
 } gso_cost;
 
 /* flag bits written by the projection */
@@ -150,15 +152,18 @@ void gso_project_bwd(const gso_camera* cam, int64_t n, int sh_degree,
                      const uint8_t* cand, const uint32_t* flags, const int64_t* slot_of,
                      const double* grad2d, double* grad3d);
 
-/* Leaf planner: per-tile counts from candidate rects, summed-area table,
- * recursive bisection of the longer side until est <= budget or one tile.
- * Leaves are written in depth-first order; returns their number (entries
- * beyond max_leaves are counted but not written).  sat (nullable) gets the
- * (TH+1) x (TW+1) table. */
+/* Leaf planner: per-tile counts and per-super-cell counts (8x8 tiles,
+ * image-aligned) from candidate rects, their summed-area tables, recursive
+ * bisection of the longer side until est <= budget or one tile.  Leaves are
+ * written in depth-first order; returns their number (entries beyond
+ * max_leaves are counted but not written).  sat (nullable) gets the
+ * (TH+1) x (TW+1) table of the tile counts. */
 int32_t gso_plan_leaves(int32_t W, int32_t H, int64_t n_cand, const int32_t* rect,
                         uint64_t budget, const gso_cost* cost, gso_leaf* out,
                         int32_t max_leaves, uint64_t* sat);
-uint64_t gso_leaf_estimate(int32_t W, int32_t H, gso_rect r, uint64_t n_isect,
+/* est of a region with n_isect overlaps and n_cells candidate-super-cell
+ * pairs over the super-cells it meets */
+uint64_t gso_leaf_estimate(int32_t W, int32_t H, gso_rect r, uint64_t n_isect, uint64_t n_cells,
                            const gso_cost* cost);
 
 /* Adam, elementwise in f64: m, v, param updated in place. */

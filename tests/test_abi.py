@@ -25,12 +25,13 @@ def test_the_six_calls_and_binding_names():
 
 def test_default_cost_model_is_an_upper_bound_of_allocations():
     c = dgs.gs_default_cost_model()   # a pure host function: no device needed
-    # per intersection, at the peak of binning: tile keys u32 x 2 and slots
-    # u32 x 2 (radix ping-pong) + 256 u32 histogram bins and their scan per
-    # 2048 entries; earlier, emission holds only keys + slots + a u64 offset
-    # per candidate (at most one candidate per intersection)
-    assert c["b_isect"] >= max(16 + 2 * 256 * 4 / 2048, 8 + 8)
+    # per coarse pair: keys u32 x 2 and slots u32 x 2 (radix ping-pong) + 256
+    # u32 histogram bins and their scan per 2048 pairs
+    assert c["b_cell"] >= 16 + 2 * 256 * 4 / 2048
+    # per intersection: the sorted slot u32
+    assert c["b_isect"] >= 4
     # per pixel: T_final f32 + last u32 + packed L1 signs u8
     assert c["b_pixel"] >= 4 + 4 + 1
-    # per tile: u64 offset + 4 f64 L1 partials
-    assert c["b_tile"] >= 8 + 32
+    # per tile: 4 f64 L1 partials; fine work items (at most one per tile
+    # beyond one per 512 pairs) with 64 u32 positions, super-tile id and offsets
+    assert c["b_tile"] >= 32 + 64 * 4 + 4 + 12

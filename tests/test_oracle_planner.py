@@ -1,14 +1,15 @@
 """Pins of the oracle's leaf planner: the leaves partition the tile grid, fit
 the budget unless they are a single tile, their overlap counts equal the
 binning's brute-force counts, and the plan is the depth-first result of the
-halving rule (re-derived here with brute-force per-tile counts)."""
+halving rule (re-derived here with brute-force per-tile counts and
+candidate-super-cell pairs)."""
 import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
 from differentiable_gaussian_splatting_amd import scenes
 
-COST = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=4096)
+COST = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=4096, b_cell=7)
 
 
 def brute_counts(rect_c, TW, TH):
@@ -18,16 +19,29 @@ def brute_counts(rect_c, TW, TH):
     return cnt
 
 
-def replan(cnt, W, H, budget):
-    """The halving rule, with the overlap count of a region taken by brute force."""
+def brute_cells(rect_c, TW, TH):
+    """Candidates meeting each image-aligned super-cell of 8 x 8 tiles."""
+    SW, SH = (TW + 7) // 8, (TH + 7) // 8
+    cnt = np.zeros((SH, SW), np.int64)
+    for x0, y0, x1, y1 in rect_c:
+        if x0 < x1 and y0 < y1:
+            cnt[y0 // 8:(y1 - 1) // 8 + 1, x0 // 8:(x1 - 1) // 8 + 1] += 1
+    return cnt
+
+
+def replan(cnt, W, H, budget, cells=None):
+    """The halving rule, with the overlap count of a region taken by brute
+    force, and its candidate-super-cell pairs over the super-cells it meets."""
     out = []
 
     def est(r):
         tx0, ty0, tx1, ty1 = r
         I = int(cnt[ty0:ty1, tx0:tx1].sum())
+        Cb = int(cells[ty0 // 8:(ty1 - 1) // 8 + 1, tx0 // 8:(tx1 - 1) // 8 + 1].sum()) if cells is not None else 0
         P = (min(tx1 * 16, W) - tx0 * 16) * (min(ty1 * 16, H) - ty0 * 16)
         T = (tx1 - tx0) * (ty1 - ty0)
-        return COST["b_isect"] * I + COST["b_pixel"] * P + COST["b_tile"] * T + COST["b_const"]
+        return (COST["b_isect"] * I + COST["b_cell"] * Cb + COST["b_pixel"] * P + COST["b_tile"] * T +
+                COST["b_const"])
 
     def rec(r):
         tx0, ty0, tx1, ty1 = r
@@ -65,7 +79,7 @@ def test_planner_partition_budget_and_rule(oracle_lib, budget):
     assert (cover == 1).all()
     cnt = brute_counts(rect_c, TW, TH)
     assert int(sat[-1, -1]) == int(cnt.sum())
-    expect = replan(cnt, cam.width, cam.height, budget)
+    expect = replan(cnt, cam.width, cam.height, budget, brute_cells(rect_c, TW, TH))
     got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in leaves]
     assert got == expect
     # a leaf's estimate uses the same overlap count the binning produces
@@ -73,7 +87,9 @@ def test_planner_partition_budget_and_rule(oracle_lib, budget):
         b = oracle_lib.bin_leaf(TW, oracle_lib.rect(L["tx0"], L["ty0"], L["tx1"], L["ty1"]),
                                 rect_c, p["depth"][p["cand"]])
         r = oracle_lib.rect(L["tx0"], L["ty0"], L["tx1"], L["ty1"])
-        assert oracle_lib.leaf_estimate(cam, r, b["n_isect"], COST) == L["est_bytes"]
+        cb = int(brute_cells(rect_c, TW, TH)[L["ty0"] // 8:(L["ty1"] - 1) // 8 + 1,
+                                              L["tx0"] // 8:(L["tx1"] - 1) // 8 + 1].sum())
+        assert oracle_lib.leaf_estimate(cam, r, b["n_isect"], COST, n_cells=cb) == L["est_bytes"]
 
 
 @settings(max_examples=60, deadline=None)
@@ -88,4 +104,28 @@ def test_planner_random_rects(oracle_lib, W, H, n, budget, seed):
     rect_c = np.stack([x0, y0, x1, y1], 1).astype(np.int32).reshape(-1, 4)
     leaves = oracle_lib.plan_leaves(cam, rect_c, budget, COST)
     got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in leaves]
-    assert got == replan(brute_counts(rect_c, TW, TH), W, H, budget)
+    assert got == replan(brute_counts(rect_c, TW, TH), W, H, budget, brute_cells(rect_c, TW, TH))
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(1, 90), st.integers(1, 70), st.integers(0, 40), st.integers(0, 2**31 - 1))
+def test_super_cell_count_bounds_the_coarse_pairs(W8, H8, n, seed):
+    """The planner's super-cell term Cb of a region is at least the number of
+    (candidate, super-cell) pairs met inside the region, whatever the region:
+    the estimate stays an upper bound of the coarse sort of any leaf."""
+    rng = np.random.default_rng(seed)
+    TW, TH = W8, H8
+    x0 = rng.integers(0, TW, n); x1 = np.minimum(TW, x0 + 1 + rng.integers(0, TW, n))
+    y0 = rng.integers(0, TH, n); y1 = np.minimum(TH, y0 + 1 + rng.integers(0, TH, n))
+    rect_c = np.stack([x0, y0, x1, y1], 1).astype(np.int32).reshape(-1, 4)
+    cells = brute_cells(rect_c, TW, TH)
+    for _ in range(10):
+        lx0 = int(rng.integers(0, TW)); lx1 = int(rng.integers(lx0 + 1, TW + 1))
+        ly0 = int(rng.integers(0, TH)); ly1 = int(rng.integers(ly0 + 1, TH + 1))
+        cb = int(cells[ly0 // 8:(ly1 - 1) // 8 + 1, lx0 // 8:(lx1 - 1) // 8 + 1].sum())
+        pairs = 0
+        for a0, b0, a1, b1 in rect_c:
+            ix0, ix1, iy0, iy1 = max(a0, lx0), min(a1, lx1), max(b0, ly0), min(b1, ly1)
+            if ix0 < ix1 and iy0 < iy1:
+                pairs += ((ix1 - 1) // 8 - ix0 // 8 + 1) * ((iy1 - 1) // 8 - iy0 // 8 + 1)
+        assert pairs <= cb
