@@ -178,7 +178,8 @@ def main():
             rooflines[name] = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                                    frac=round(ach / PEAK_HBM_GBS, 4), work=unit_desc)
     roofline = dict(rooflines[dom])
-    roofline.update(traffic=measured_traffic(args.workload, dom), traffic_unit="HBM bytes per launch (counters)",
+    roofline.update(traffic=measured_traffic(args.workload, dom, wc["n_leaves"]),
+                    traffic_unit="HBM bytes per launch (counters)",
                     kernel=dom, avg_launch_ms=round(dom_live["avg_ms"], 4), launches_per_step=dom_live["launches"],
                     timing="HIP events around this kernel's launches inside the timed steps")
     # whole-step HBM fraction: the algorithmic bytes of every stage over the step time
@@ -312,10 +313,11 @@ RASTER_SOURCES = ("differentiable_gaussian_splatting_amd/csrc/raster.hip",
                   "differentiable_gaussian_splatting_amd/csrc/gs_device.h")
 
 
-def measured_traffic(workload, kernel):
+def measured_traffic(workload, kernel, n_leaves):
     """HBM bytes per launch of a raster kernel from the committed counter
     summary (calibrated FETCH_SIZE + WRITE_SIZE), or None when there is none
-    for this workload or the kernel sources have changed since it was taken."""
+    for this workload and leaf count, or the kernel sources have changed since
+    it was taken."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"raster_traffic_{workload}.txt")
@@ -332,6 +334,8 @@ def measured_traffic(workload, kernel):
             continue
         fields[parts[0]] = parts[1:]
     if fields.get("source_sha256_16", [None])[0] != h.hexdigest()[:16] or kernel not in fields:
+        return None
+    if int(fields.get("n_leaves", ["-1"])[0]) != int(n_leaves):
         return None
     kv = fields[kernel]
     return int(dict(zip(kv[0::2], kv[1::2]))["traffic_bytes_per_launch"])
