@@ -71,6 +71,39 @@ __global__ __launch_bounds__(256) void k_rect_diff(int64_t n, const uint32_t* __
     }
 }
 
+// The same difference array for a grid that fits in LDS (few tiles, so
+// heavily contended cells): a block takes kDiffBlock rectangles into an LDS
+// copy of the whole grid and then adds its nonzero cells to the global grid.
+constexpr int kDiffBlock = 8192;
+constexpr int kDiffLds = 16384;    // cells (64 KB)
+
+__global__ __launch_bounds__(256) void k_rect_diff_lds(int64_t n, const uint32_t* __restrict__ list,
+                                                       const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
+                                                       int lty1, int32_t* __restrict__ diff)
+{
+    extern __shared__ int32_t hd[];
+    const int TWL = ltx1 - ltx0, THL = lty1 - lty0;
+    const int64_t cells = (int64_t)TWL * THL;
+    for (int64_t k = threadIdx.x; k < cells; k += blockDim.x) hd[k] = 0;
+    __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.x * kDiffBlock;
+    for (int64_t k = c0 + threadIdx.x; k < min<int64_t>(n, c0 + kDiffBlock); k += blockDim.x) {
+        const int64_t j = list ? (int64_t)list[k] : k;
+        const int4 r = rect[j];
+        const int x0 = max(r.x, ltx0) - ltx0, x1 = min(r.z, ltx1) - ltx0;
+        const int y0 = max(r.y, lty0) - lty0, y1 = min(r.w, lty1) - lty0;
+        if (x0 < x1 && y0 < y1) {
+            atomicAdd(&hd[(int64_t)y0 * TWL + x0], 1);
+            if (x1 < TWL) atomicAdd(&hd[(int64_t)y0 * TWL + x1], -1);
+            if (y1 < THL) atomicAdd(&hd[(int64_t)y1 * TWL + x0], -1);
+            if (x1 < TWL && y1 < THL) atomicAdd(&hd[(int64_t)y1 * TWL + x1], 1);
+        }
+    }
+    __syncthreads();
+    for (int64_t k = threadIdx.x; k < cells; k += blockDim.x)
+        if (hd[k]) atomicAdd(&diff[k], hd[k]);
+}
+
 // Super-cells (image-aligned blocks of 2^sh x 2^sh tiles) that the rectangle
 // r meets inside the leaf: first cell (cx0, cy0) relative to the leaf's first
 // super-cell, and extent (w, h); w = h = 0 when r misses the leaf.
@@ -361,10 +394,16 @@ gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, 
                            int64_t n_list, int32_t* diff)
 {
     const int64_t n = list ? n_list : proj->n_cand;
+    const int64_t cells = (int64_t)(leaf.tx1 - leaf.tx0) * (leaf.ty1 - leaf.ty0);
     if (n > 0) {
         GsTimerScope ts(ctx, "rect_diff");
-        hipLaunchKernelGGL(k_rect_diff, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, list,
-                           proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, diff);
+        if (cells <= kDiffLds)
+            hipLaunchKernelGGL(k_rect_diff_lds, dim3((unsigned)ceil_div(n, kDiffBlock)), dim3(256),
+                               sizeof(int32_t) * cells, ctx->stream, n, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1,
+                               leaf.ty1, diff);
+        else
+            hipLaunchKernelGGL(k_rect_diff, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, list,
+                               proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, diff);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;

@@ -145,9 +145,10 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
             float u = b.x * dy;
             u = u * dy;
             const float power = __builtin_fmaf(t, dx, u);
-            const bool pok = !(power > 0.0f || power < -87.0f);
-            // exp of the clamped exponent: equal to exp(power) on every lane
-            // that can include the entry, finite on the others
+            // exp of the exponent clamped into [-87, 0]: exp(power) on every
+            // lane that can include the entry (below -87 the exp is 0 and
+            // alpha < 1/255; at -87 o exp(-87) < 1/255 too), finite on the others
+            const bool pok = !(power > 0.0f);
             const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
             const float av = b.y * G;
             const float alpha = av > gsd::kAlphaMax ? gsd::kAlphaMax : av;
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
             const float u1 = bb.x * dy;
             const float u = u1 * dy;
             const float power = __builtin_fmaf(t, dx, u);
-            const bool pok = !(power > 0.0f || power < -87.0f);
+            const bool pok = !(power > 0.0f);   // power < -87: alpha < 1/255 (as in the forward)
             const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
             const float av = bb.y * G;
             const bool clamped = av > gsd::kAlphaMax;
