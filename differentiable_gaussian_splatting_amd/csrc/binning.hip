@@ -151,10 +151,11 @@ constexpr int kOB = 256;     // threads (and candidates) of an emission block
 // (super-tile, slot) pairs of the listed candidates, in list order and
 // row-major super-tile order within a rectangle.  eoff[k] - ebase is the
 // first output of candidate k (exclusive scan of the per-candidate super-tile
-// counts, n + 1 entries).  Block = kOB consecutive candidates: their outputs
-// form one contiguous range, which the block's threads write at consecutive
-// positions (coalesced), each finding its candidate by binary search in an
-// LDS copy of the block's offsets.
+// counts, n + 1 entries).  Block = kOB consecutive candidates: their slots,
+// super-cell ranges and offsets are staged in LDS in one round of loads;
+// their outputs form one contiguous range, which the block's threads write
+// at consecutive positions (coalesced), each finding its candidate by binary
+// search in the LDS offsets.
 __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
                                                     const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
                                                     int lty1, int sh, int SW, const uint32_t* __restrict__ eoff,
@@ -162,9 +163,17 @@ __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* _
                                                     uint32_t* __restrict__ vals)
 {
     __shared__ uint32_t se[kOB + 1];
+    __shared__ uint32_t sj[kOB];
+    __shared__ int4 sc[kOB];       // cx0, cy0, w, h of each candidate's super-cells
     const int64_t c0 = (int64_t)blockIdx.x * kOB;
     const int m = (int)min<int64_t>(kOB, n - c0);
     for (int k = threadIdx.x; k <= m; k += kOB) se[k] = eoff[c0 + k] - ebase;
+    if ((int)threadIdx.x < m) {
+        const uint32_t j = list[c0 + threadIdx.x];
+        const Cells cl = leaf_cells(rect[j], ltx0, lty0, ltx1, lty1, sh);
+        sj[threadIdx.x] = j;
+        sc[threadIdx.x] = make_int4(cl.cx0, cl.cy0, cl.w, cl.h);
+    }
     __syncthreads();
     const uint32_t o0 = se[0], o1 = se[m];
     for (uint32_t o = o0 + threadIdx.x; o < o1; o += kOB) {
@@ -174,11 +183,11 @@ __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* _
             if (se[mid] <= o) lo = mid;
             else hi = mid - 1;
         }
-        const uint32_t j = list[c0 + lo];
-        const Cells cl = leaf_cells(rect[j], ltx0, lty0, ltx1, lty1, sh);
+        const int4 cl = sc[lo];
         const uint32_t t = o - se[lo];
-        keys[o] = (uint32_t)((cl.cy0 + (int)(t / (uint32_t)cl.w)) * SW + cl.cx0 + (int)(t % (uint32_t)cl.w));
-        vals[o] = j;
+        const uint32_t ty = t / (uint32_t)cl.z;
+        keys[o] = (uint32_t)((cl.y + (int)ty) * SW + cl.x + (int)(t - ty * (uint32_t)cl.z));
+        vals[o] = sj[lo];
     }
 }
 
