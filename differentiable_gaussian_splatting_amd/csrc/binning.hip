@@ -147,6 +147,10 @@ __global__ __launch_bounds__(256) void k_leaf_counts(const int32_t* __restrict__
 }
 
 constexpr int kOB = 256;     // threads (and candidates) of an emission block
+// coarse key: bits [0, kCellBits) the leaf's super-tile, above them the
+// entry's rectangle inside that super-tile (x0, x1 - 1, y0, y1 - 1 in its
+// 8 x 8 local tiles, 3 bits each), carried through the sort for the fine level
+constexpr int kCellBits = 20;
 
 // (super-tile, slot) pairs of the listed candidates, in list order and
 // row-major super-tile order within a rectangle.  eoff[k] - ebase is the
@@ -165,14 +169,17 @@ __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* _
     __shared__ uint32_t se[kOB + 1];
     __shared__ uint32_t sj[kOB];
     __shared__ int4 sc[kOB];       // cx0, cy0, w, h of each candidate's super-cells
+    __shared__ int4 sr[kOB];       // its rectangle clipped to the leaf
     const int64_t c0 = (int64_t)blockIdx.x * kOB;
     const int m = (int)min<int64_t>(kOB, n - c0);
     for (int k = threadIdx.x; k <= m; k += kOB) se[k] = eoff[c0 + k] - ebase;
     if ((int)threadIdx.x < m) {
         const uint32_t j = list[c0 + threadIdx.x];
-        const Cells cl = leaf_cells(rect[j], ltx0, lty0, ltx1, lty1, sh);
+        const int4 r = rect[j];
+        const Cells cl = leaf_cells(r, ltx0, lty0, ltx1, lty1, sh);
         sj[threadIdx.x] = j;
         sc[threadIdx.x] = make_int4(cl.cx0, cl.cy0, cl.w, cl.h);
+        sr[threadIdx.x] = make_int4(max(r.x, ltx0), max(r.y, lty0), min(r.z, ltx1), min(r.w, lty1));
     }
     __syncthreads();
     const uint32_t o0 = se[0], o1 = se[m];
@@ -186,7 +193,13 @@ __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* _
         const int4 cl = sc[lo];
         const uint32_t t = o - se[lo];
         const uint32_t ty = t / (uint32_t)cl.z;
-        keys[o] = (uint32_t)((cl.y + (int)ty) * SW + cl.x + (int)(t - ty * (uint32_t)cl.z));
+        const int cx = cl.x + (int)(t - ty * (uint32_t)cl.z), cy = cl.y + (int)ty;
+        // the rectangle inside this super-tile (and the leaf), in its local tiles
+        const int4 r = sr[lo];
+        const int bx = ((ltx0 >> sh) + cx) << sh, by = ((lty0 >> sh) + cy) << sh;
+        const uint32_t x0 = (uint32_t)(max(r.x, bx) - bx), x1 = (uint32_t)(min(r.z, bx + 8) - bx);
+        const uint32_t y0 = (uint32_t)(max(r.y, by) - by), y1 = (uint32_t)(min(r.w, by + 8) - by);
+        keys[o] = ((x0 | ((x1 - 1u) << 3) | (y0 << 6) | ((y1 - 1u) << 9)) << kCellBits) | (uint32_t)(cy * SW + cx);
         vals[o] = sj[lo];
     }
 }
@@ -200,9 +213,10 @@ __global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* _
 //   scan:  per tile, those counts become the write positions of the items in
 //          segment order, starting at the tile's offset;
 //   write: each item appends its covering entries at its positions.
-// A segment is walked 64 entries at a time: a ballot over the 64 rectangles
-// per tile gives the covering entries, and the rank of an entry is the number
-// of set bits below its lane.
+// A segment is walked 64 entries at a time: a ballot per tile over the 64
+// entries' rectangles (carried in their sort keys, local to the super-tile)
+// gives the covering entries, and the rank of an entry is the number of set
+// bits below its lane.
 constexpr int kSuperShift = 3;
 constexpr int kSeg = 512;
 
@@ -230,7 +244,7 @@ template <bool WRITE>
 __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int THL, int SW, int n_super,
                                               const uint64_t* __restrict__ soff, const uint32_t* __restrict__ ioff,
                                               const uint32_t* __restrict__ item_sc,
-                                              const uint32_t* __restrict__ group, const int4* __restrict__ rect,
+                                              const uint32_t* __restrict__ group, const uint32_t* __restrict__ gkey,
                                               uint32_t* __restrict__ pos, uint64_t n_values,
                                               uint32_t* __restrict__ values)
 {
@@ -248,34 +262,38 @@ __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int T
 #pragma unroll
     for (int q = 0; q < 16; ++q) cur[q] = WRITE ? wp[q] : 0u;
     const uint64_t b = it.b, e = it.e;
-    uint32_t s_c = 0, s_n = 0;
-    int4 r_c = make_int4(0, 0, 0, 0);
-    if (b + lane < e) s_c = group[b + lane];
-    if (b + lane < e) r_c = rect[s_c];
-    if (b + 64 + lane < e) s_n = group[b + 64 + lane];
+    // this wave's tiles in the super-tile: columns 0-7, rows 2w and 2w + 1
+    const uint32_t row0 = 2u * (uint32_t)wave;
+    uint32_t sl_n = 0, key_n = 0;          // the next chunk's entry, loaded one chunk ahead
+    if (b + lane < e) {
+        sl_n = group[b + lane];
+        key_n = gkey[b + lane];
+    }
     for (uint64_t k = b; k < e; k += 64) {
-        int4 r_n = make_int4(0, 0, 0, 0);
-        uint32_t s_nn = 0;
-        if (k + 64 + lane < e) r_n = rect[s_n];
-        if (k + 128 + lane < e) s_nn = group[k + 128 + lane];
         const bool ok = k + lane < e;
+        const uint32_t sl = sl_n, lr = key_n >> kCellBits;
+        if (k + 64 + lane < e) {
+            sl_n = group[k + 64 + lane];
+            key_n = gkey[k + 64 + lane];
+        }
+        const uint32_t x0 = lr & 7u, x1 = ((lr >> 3) & 7u) + 1u;
+        const uint32_t y0 = (lr >> 6) & 7u, y1 = ((lr >> 9) & 7u) + 1u;
+        const bool r0 = ok && y0 <= row0 && row0 < y1, r1 = ok && y0 <= row0 + 1u && row0 + 1u < y1;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const int gx = gx0 + (q & 7), gy = gy0 + (q >> 3);
-            if (gx < ltx0 || gx >= ltx0 + TWL || gy < lty0 || gy >= lty0 + THL) continue;
-            const bool cov = ok && r_c.x <= gx && gx < r_c.z && r_c.y <= gy && gy < r_c.w;
+            const uint32_t c = (uint32_t)(q & 7);
+            // a rectangle clipped to the leaf covers no tile outside it
+            const bool cov = ((q >> 3) ? r1 : r0) && x0 <= c && c < x1;
             const uint64_t m = gsd::ballot(cov);
+            if (m == 0) continue;
             if (WRITE && cov) {
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
                 const uint32_t p = cur[q] + below;
-                if (p < n_values) values[p] = s_c;   // always true when the counts agree
+                if (p < n_values) values[p] = sl;   // always true when the counts agree
             }
             cur[q] += (uint32_t)__builtin_popcountll(m);
         }
-        s_c = s_n;
-        r_c = r_n;
-        s_n = s_nn;
     }
     if (!WRITE && lane < 16) {
         uint32_t v = 0;
@@ -340,20 +358,21 @@ __global__ __launch_bounds__(256) void k_fine_scan(int ltx0, int lty0, int TWL, 
     }
 }
 
-// offsets[s] = first position whose key is >= s, for s in [0, n_seg]; keys
-// sorted ascending, all < n_seg.  Four keys per thread.
+// offsets[s] = first position whose key (& kmask) is >= s, for s in
+// [0, n_seg]; keys sorted ascending by key & kmask, all < n_seg.  Four keys
+// per thread.
 __global__ __launch_bounds__(256) void k_seg_offsets(const uint32_t* __restrict__ keys, int64_t n, int64_t n_seg,
-                                                     uint64_t* __restrict__ offsets)
+                                                     uint32_t kmask, uint64_t* __restrict__ offsets)
 {
     const int64_t k0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (k0 > n) return;
-    int64_t prev = k0 == 0 ? -1 : (int64_t)keys[k0 - 1];
+    int64_t prev = k0 == 0 ? -1 : (int64_t)(keys[k0 - 1] & kmask);
     uint32_t cur4[4];
     if (k0 + 4 <= n && (k0 & 3) == 0) {
         const uint4 v = *reinterpret_cast<const uint4*>(keys + k0);
-        cur4[0] = v.x; cur4[1] = v.y; cur4[2] = v.z; cur4[3] = v.w;
+        cur4[0] = v.x & kmask; cur4[1] = v.y & kmask; cur4[2] = v.z & kmask; cur4[3] = v.w & kmask;
     } else {
-        for (int q = 0; q < 4; ++q) cur4[q] = k0 + q < n ? keys[k0 + q] : 0u;
+        for (int q = 0; q < 4; ++q) cur4[q] = k0 + q < n ? keys[k0 + q] & kmask : 0u;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -391,6 +410,8 @@ int super_cols(gs_tile_rect leaf) { return ((leaf.tx1 - 1) >> kSuperShift) - (le
 int super_rows(gs_tile_rect leaf) { return ((leaf.ty1 - 1) >> kSuperShift) - (leaf.ty0 >> kSuperShift) + 1; }
 int64_t super_cells(gs_tile_rect leaf) { return (int64_t)super_cols(leaf) * super_rows(leaf); }
 int super_shift() { return kSuperShift; }
+uint32_t super_key_mask() { return (1u << kCellBits) - 1u; }
+int64_t super_cells_max() { return (int64_t)1 << kCellBits; }
 
 int bits_for(int64_t n_keys)
 {
@@ -463,8 +484,8 @@ int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells)
 }
 
 gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
-                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* item_sc,
-                            uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values)
+                            const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint64_t* toff,
+                            uint32_t* item_sc, uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values)
 {
     const int n_super = (int)super_cells(leaf);
     const int64_t items = fine_items_bound(leaf, n_cells);
@@ -473,20 +494,21 @@ gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
     GsTimerScope ts(ctx, "fine");
     hipLaunchKernelGGL(k_fine_items, dim3(1), dim3(1024), 0, ctx->stream, soff, n_super, ioff, item_sc);
     hipLaunchKernelGGL(k_fine<false>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                       SW, n_super, soff, ioff, item_sc, group, proj->rect, pos, n_values, values);
+                       SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
     hipLaunchKernelGGL(k_fine_scan, dim3((unsigned)ceil_div((int64_t)n_super * 64, 256)), dim3(256), 0, ctx->stream,
                        leaf.tx0, leaf.ty0, TWL, THL, SW, n_super, ioff, toff, pos);
     hipLaunchKernelGGL(k_fine<true>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                       SW, n_super, soff, ioff, item_sc, group, proj->rect, pos, n_values, values);
+                       SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }
 
-gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets)
+gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint32_t kmask,
+                             uint64_t* offsets)
 {
     GsTimerScope ts(ctx, "seg_offsets");
     hipLaunchKernelGGL(k_seg_offsets, dim3((unsigned)ceil_div(ceil_div(n + 1, 4), 256)), dim3(256), 0, ctx->stream,
-                       sorted_keys, n, n_seg, offsets);
+                       sorted_keys, n, n_seg, kmask, offsets);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -277,7 +277,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, goff, k0, v0)) != GS_OK) goto out;
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
-    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, segoff)) != GS_OK) goto out;
+    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, 0xFFFFFFFFu, segoff)) != GS_OK) goto out;
     if ((st = launch_plan_offsets(ctx, proj, ldev, nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0, segoff, ccnt,
                                   coff, lcells, lisect, dtbase, toff)) != GS_OK)
         goto out;
@@ -619,6 +619,11 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     uint64_t I = 0, C = 0;
     bool second = false;
     const int64_t n_super = super_cells(leaf);
+    if (n_super >= super_cells_max()) {
+        destroy_handle(ctx, b);
+        return gs_fail(ctx, GS_ERR_OVERFLOW, "leaf meets %lld super-tiles (limit %lld)", (long long)n_super,
+                       (long long)super_cells_max());
+    }
     uint32_t *cnt = nullptr, *lc = nullptr, *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
     uint32_t* eoff_own = nullptr;
     uint64_t* soff = nullptr;
@@ -679,9 +684,9 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)C, bits_for(n_super), &second)) != GS_OK) goto fail;
     soff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (n_super + 1), GS_MEM_RASTER, &tmp);
     if (!soff) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)C, n_super, soff)) != GS_OK) goto fail;
-    gs_free_one(ctx, &tmp, second ? k1 : k0);
-    gs_free_one(ctx, &tmp, second ? k0 : k1);
+    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)C, n_super, super_key_mask(), soff)) != GS_OK)
+        goto fail;
+    gs_free_one(ctx, &tmp, second ? k0 : k1);     // the sorted keys stay for the fine level
     gs_free_one(ctx, &tmp, second ? v0 : v1);
     // fine level: per-tile lists at the tile offsets
     {
@@ -691,8 +696,8 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         uint32_t* ioff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n_super + 1), GS_MEM_RASTER, &tmp);
         uint32_t* pos = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * 64 * items, GS_MEM_RASTER, &tmp);
         if (!b->values || !item_sc || !ioff || !pos) { st = GS_ERR_OOM; goto fail; }
-        if ((st = launch_fine_lists(ctx, proj, leaf, soff, second ? v1 : v0, C, b->offsets, item_sc, ioff, pos, I,
-                                    b->values)) != GS_OK)
+        if ((st = launch_fine_lists(ctx, proj, leaf, soff, second ? v1 : v0, second ? k1 : k0, C, b->offsets, item_sc,
+                                    ioff, pos, I, b->values)) != GS_OK)
             goto fail;
     }
     gs_free_all(ctx, &tmp);

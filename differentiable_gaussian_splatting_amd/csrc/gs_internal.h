@@ -146,6 +146,8 @@ int super_cols(gs_tile_rect leaf);
 int super_rows(gs_tile_rect leaf);
 int64_t super_cells(gs_tile_rect leaf);
 int super_shift();
+uint32_t super_key_mask();      // bits of a coarse key that hold the super-tile
+int64_t super_cells_max();      // super-tiles a leaf may have
 // per listed candidate: super-tiles of the leaf its rectangle meets
 gs_status launch_count_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                              int64_t n_list, uint32_t* cnt);
@@ -160,10 +162,13 @@ gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
 // bound for n_cells coarse pairs; scratch: item_sc u32 [items], ioff u32
 // [n_super + 1], pos u32 [items * 64]
 int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells);
+// group: slots by super-tile; gkey: their sorted coarse keys (super-tile id
+// and the rectangle inside the super-tile)
 gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
-                            const uint32_t* group, uint64_t n_cells, const uint64_t* toff, uint32_t* item_sc,
-                            uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values);
-gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint64_t* offsets);
+                            const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint64_t* toff,
+                            uint32_t* item_sc, uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values);
+gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint32_t kmask,
+                             uint64_t* offsets);
 gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
 gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);
 int bits_for(int64_t n_keys);
