@@ -1,8 +1,9 @@
 // radix.hip -- stable LSD radix sort of (u32 key, u32 value) pairs.
 //
-// Each pass takes 8 key bits (fewer on the last pass): a per-block digit
-// histogram (LDS atomics), an exclusive scan of the digit-major histogram
-// (digit * n_blocks + block), and a stable scatter.  The scatter ranks a
+// Each pass takes 8 key bits (fewer on the last pass), or a single pass takes
+// up to 10 bits: a per-block digit histogram (LDS atomics), an exclusive scan
+// of the digit-major histogram (digit * n_blocks + block), and a stable
+// scatter.  The scatter ranks a
 // block's elements in element order: 256 elements per round, a wavefront
 // finds the lanes holding the same digit with one ballot per digit bit
 // (lane rank = popcount of same-digit lanes below it), per-wave digit counts
@@ -17,8 +18,8 @@ namespace {
 constexpr int kRB = 256;      // threads per block
 constexpr int kRItems = 8;    // rounds (elements per thread)
 constexpr int kRTile = kRB * kRItems;
-constexpr int kRadix = 256;
 
+template <int kRadix>
 __global__ __launch_bounds__(kRB) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n, int shift,
                                                     uint32_t mask, uint32_t* __restrict__ hist, int64_t nb)
 {
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(kRB) void k_radix_hist(const uint32_t* __restrict__
         if (i < n) atomicAdd(&h[(keys[i] >> shift) & mask], 1u);
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < kRadix; d += kRB) hist[(int64_t)d * nb + blockIdx.x] = h[d];
+    for (int d = threadIdx.x; d <= (int)mask; d += kRB) hist[(int64_t)d * nb + blockIdx.x] = h[d];
 }
 
 __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* sh)
@@ -54,6 +55,7 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* sh)
 // order, (2) the block's elements placed digit-sorted in LDS, (3) written out
 // digit run by digit run, so that consecutive lanes write consecutive
 // addresses.
+template <int kRadix>
 __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restrict__ kin,
                                                        const uint32_t* __restrict__ vin, int64_t n, int shift,
                                                        int bits, const uint32_t* __restrict__ hscan, int64_t nb,
@@ -109,8 +111,20 @@ __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restric
         }
         __syncthreads();
     }
-    // local start of every digit run (kRadix == kRB: one digit per thread)
-    lstart[threadIdx.x] = block_excl_scan256(run[threadIdx.x], scan_sh);
+    // local start of every digit run (each thread scans kRadix / kRB
+    // consecutive digits)
+    {
+        constexpr int P = kRadix / kRB;
+        uint32_t part = 0;
+#pragma unroll
+        for (int q = 0; q < P; ++q) part += run[threadIdx.x * P + q];
+        uint32_t at = block_excl_scan256(part, scan_sh);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            lstart[threadIdx.x * P + q] = at;
+            at += run[threadIdx.x * P + q];
+        }
+    }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kRItems; ++r)
@@ -142,28 +156,42 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
     if (n <= 1 || key_bits <= 0) return GS_OK;
     if (n >= (1ll << 32)) return gs_fail(ctx, GS_ERR_OVERFLOW, "radix sort of %lld >= 2^32 pairs", (long long)n);
     const int64_t nb = ceil_div(n, kRTile);
+    // up to 10 bits in one pass, else 8-bit passes
+    const bool wide = key_bits <= 10;
+    const int radix = wide ? 1024 : 256;
     std::vector<GsAlloc> tmp;
-    uint32_t* hist = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * kRadix * nb, GS_MEM_SCRATCH, &tmp);
-    uint32_t* hscan = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (kRadix * nb + 1), GS_MEM_SCRATCH, &tmp);
+    uint32_t* hist = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix * nb, GS_MEM_SCRATCH, &tmp);
+    uint32_t* hscan = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (radix * nb + 1), GS_MEM_SCRATCH, &tmp);
     if (!hist || !hscan) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
     gs_status st = GS_OK;
     uint32_t *ki = k0, *vi = v0, *ko = k1, *vo = v1;
-    for (int shift = 0; shift < key_bits && st == GS_OK; shift += 8) {
-        const int bits = std::min(8, key_bits - shift);
+    const int step = wide ? key_bits : 8;
+    for (int shift = 0; shift < key_bits && st == GS_OK; shift += step) {
+        const int bits = std::min(step, key_bits - shift);
+        const uint32_t mask = (1u << bits) - 1u;
         {
             GsTimerScope ts(ctx, "radix");
-            hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, n, shift,
-                               (1u << bits) - 1u, hist, nb);
+            if (wide)
+                hipLaunchKernelGGL(k_radix_hist<1024>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, n, shift,
+                                   mask, hist, nb);
+            else
+                hipLaunchKernelGGL(k_radix_hist<256>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, n, shift,
+                                   mask, hist, nb);
         }
-        st = launch_scan_u32_to_u32(ctx, hist, hscan, kRadix * nb);
+        // the digit-major histogram rows of the digits that occur
+        st = launch_scan_u32_to_u32(ctx, hist, hscan, (int64_t)(mask + 1u) * nb);
         if (st != GS_OK) break;
         {
             GsTimerScope ts(ctx, "radix");
-            hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n, shift,
-                               bits, hscan, nb, ko, vo);
+            if (wide)
+                hipLaunchKernelGGL(k_radix_scatter<1024>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n,
+                                   shift, bits, hscan, nb, ko, vo);
+            else
+                hipLaunchKernelGGL(k_radix_scatter<256>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n,
+                                   shift, bits, hscan, nb, ko, vo);
         }
         std::swap(ki, ko);
         std::swap(vi, vo);
