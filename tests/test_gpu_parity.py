@@ -197,7 +197,10 @@ def test_train_view_chunked_update_matches_oracle(ctx, chunk):
                                 v0[k].astype(np.float32), step=3)
         got = t.cpu().numpy().astype(np.float64)
         say(f"  {name:10s} update rel L2 {rel_l2(got - p0, p - p0):.2e}")
-        assert rel_l2(got - p0, p - p0) <= 1e-3, name
+        # each update within 1e-3 of the oracle's, beside the rounding of the
+        # stored f32 parameter (its ulp is ~2e-6 at the means' depth of ~20)
+        ulp = np.spacing(np.abs(p).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - p) <= 1e-3 * np.abs(p - p0) + 2 * ulp), name
 
 
 @pytest.mark.parametrize("case", ["empty", "all_culled", "one_pixel", "ragged", "huge", "dense_tile"])
