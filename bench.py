@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--budget-mib", type=float, default=384.0)
     ap.add_argument("--no-adam", action="store_true")
     ap.add_argument("--cpu-baseline", type=int, default=1)
-    ap.add_argument("--cpu-window", type=int, default=384, help="side (pixels) of the oracle's sampled window")
+    ap.add_argument("--cpu-window", type=int, default=768,
+                    help="side (pixels) of the window the oracle rasterizes for the CPU baseline")
     ap.add_argument("--attr-steps", type=int, default=2,
                     help="steps of the per-kernel attribution pass (events around every kernel)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
