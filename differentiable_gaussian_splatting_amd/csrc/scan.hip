@@ -159,17 +159,29 @@ __global__ __launch_bounds__(256) void k_row_prefix(T* __restrict__ g, int rows,
     }
 }
 
-// inclusive prefix down each column: one thread per column
+// inclusive prefix down each column: a block takes 32 columns, its 32
+// wavefront-halves each a chunk of rows (consecutive lanes on consecutive
+// columns); chunk sums, then each chunk re-walked with the sums above it
 template <typename T>
-__global__ __launch_bounds__(256) void k_col_prefix(T* __restrict__ g, int rows, int cols)
+__global__ __launch_bounds__(1024) void k_col_prefix(T* __restrict__ g, int rows, int cols)
 {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= cols) return;
+    __shared__ T part[32][33];
+    const int cx = threadIdx.x & 31, ck = threadIdx.x >> 5;
+    const int c = blockIdx.x * 32 + cx;
+    const int R = (rows + 31) / 32;
+    const int r0 = min(rows, ck * R), r1 = min(rows, r0 + R);
+    T s = 0;
+    if (c < cols)
+        for (int r = r0; r < r1; ++r) s += g[(int64_t)r * cols + c];
+    part[ck][cx] = s;
+    __syncthreads();
     T acc = 0;
-    for (int r = 0; r < rows; ++r) {
-        acc += g[(int64_t)r * cols + c];
-        g[(int64_t)r * cols + c] = acc;
-    }
+    for (int k = 0; k < ck; ++k) acc += part[k][cx];
+    if (c < cols)
+        for (int r = r0; r < r1; ++r) {
+            acc += g[(int64_t)r * cols + c];
+            g[(int64_t)r * cols + c] = acc;
+        }
 }
 
 template <typename T>
@@ -179,7 +191,7 @@ gs_status prefix2d_impl(gs_ctx* ctx, T* g, int rows, int cols)
     GsTimerScope ts(ctx, "prefix2d");
     hipLaunchKernelGGL((k_row_prefix<T>), dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, ctx->stream, g, rows,
                        cols);
-    hipLaunchKernelGGL((k_col_prefix<T>), dim3((unsigned)ceil_div(cols, 256)), dim3(256), 0, ctx->stream, g, rows,
+    hipLaunchKernelGGL((k_col_prefix<T>), dim3((unsigned)ceil_div(cols, 32)), dim3(1024), 0, ctx->stream, g, rows,
                        cols);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
