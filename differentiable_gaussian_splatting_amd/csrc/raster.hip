@@ -1,12 +1,14 @@
 // raster.hip -- per-leaf forward compositing and its reverse-order backward.
 //
-// Layout (MI355X, wave64): one workgroup of 4 wavefronts per 16x16 tile, each
-// wavefront owning an independent 8x8 sub-tile (lane = pixel).  A wavefront
-// stages a batch of 64 list entries in its own LDS slice (lane i gathers entry
-// i), then every lane walks the batch with wave-uniform LDS reads (broadcast,
-// free of bank conflicts).  No workgroup barrier is used: the wavefronts of a
-// tile finish independently, and one leaves as soon as a ballot shows that all
-// of its pixels have stopped.
+// Layout (MI355X, wave64).  Forward: one workgroup of 4 wavefronts per 16x16
+// tile, each wavefront owning an independent 8x8 sub-tile (lane = pixel).
+// Backward: one wavefront per 16x16 tile (lane = one pixel in each of the four
+// 8x8 quadrants), four tiles per workgroup.  A wavefront stages a batch of 64
+// list entries in its own LDS slice (lane i gathers entry i), then every lane
+// walks the batch with wave-uniform LDS reads (broadcast, free of bank
+// conflicts).  No workgroup barrier is used: wavefronts finish independently,
+// and a forward wavefront leaves as soon as a ballot shows that all of its
+// pixels have stopped.
 //
 // Sub-tile culling: while staging, lane i also decides whether entry i can
 // reach alpha >= 1/255 anywhere in the wavefront's 8x8 box of pixel centres:
@@ -61,32 +63,58 @@ struct Staged {        // one wavefront's staged batch (entry j at byte 16 j of 
     float4 c[64];      // b, slot (bits), -, -
 };
 
+// Per-entry part of the sub-tile cull: the conic, the reciprocals of its
+// diagonal and the threshold 2 ln(255 o), shared by every box the entry is
+// tested against.
+struct CullPrep {
+    float x, y, A, B, C, iA, iC, thr;
+    bool faint;   // o < 1/255: alpha <= o stays below 1/255 everywhere
+};
+
+__device__ __forceinline__ CullPrep cull_prep(float4 a, float4 b)
+{
+    CullPrep p;
+    const float o = b.y;
+    p.faint = !(o * 255.0f >= 1.0f);
+    p.x = a.x;
+    p.y = a.y;
+    p.A = -2.0f * a.z;
+    p.B = -a.w;
+    p.C = -2.0f * b.x;
+    p.iC = 1.0f / p.C;
+    p.iA = 1.0f / p.A;
+    p.thr = 2.0f * __logf(255.0f * o);
+    return p;
+}
+
 // true when no pixel centre of the box [bx0, bx0+7] x [by0, by0+7] can
 // include the entry (alpha < 1/255 everywhere)
-__device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by0)
+__device__ __forceinline__ bool cull_test(const CullPrep& p, float bx0, float by0)
 {
-    const float o = b.y;
-    if (!(o * 255.0f >= 1.0f)) return true;     // alpha <= o < 1/255
-    const float A = -2.0f * a.z, B = -a.w, C = -2.0f * b.x;
-    const float dx0 = bx0 - a.x, dx1 = dx0 + 7.0f;
-    const float dy0 = by0 - a.y, dy1 = dy0 + 7.0f;
+    if (p.faint) return true;
+    const float A = p.A, B = p.B, C = p.C;
+    const float dx0 = bx0 - p.x, dx1 = dx0 + 7.0f;
+    const float dy0 = by0 - p.y, dy1 = dy0 + 7.0f;
     if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) return false;
     float qmin = __builtin_inff();
     {
-        const float iC = 1.0f / C, iA = 1.0f / A;
-        float X = dx0, t = fminf(fmaxf(-B * X * iC, dy0), dy1);
+        float X = dx0, t = fminf(fmaxf(-B * X * p.iC, dy0), dy1);
         qmin = fminf(qmin, A * X * X + 2.0f * B * X * t + C * t * t);
-        X = dx1; t = fminf(fmaxf(-B * X * iC, dy0), dy1);
+        X = dx1; t = fminf(fmaxf(-B * X * p.iC, dy0), dy1);
         qmin = fminf(qmin, A * X * X + 2.0f * B * X * t + C * t * t);
-        float Y = dy0, s = fminf(fmaxf(-B * Y * iA, dx0), dx1);
+        float Y = dy0, s = fminf(fmaxf(-B * Y * p.iA, dx0), dx1);
         qmin = fminf(qmin, C * Y * Y + 2.0f * B * Y * s + A * s * s);
-        Y = dy1; s = fminf(fmaxf(-B * Y * iA, dx0), dx1);
+        Y = dy1; s = fminf(fmaxf(-B * Y * p.iA, dx0), dx1);
         qmin = fminf(qmin, C * Y * Y + 2.0f * B * Y * s + A * s * s);
     }
     const float Xm = fmaxf(fabsf(dx0), fabsf(dx1)), Ym = fmaxf(fabsf(dy0), fabsf(dy1));
     const float S = fabsf(A) * Xm * Xm + 2.0f * fabsf(B) * Xm * Ym + fabsf(C) * Ym * Ym;
-    const float thr = 2.0f * __logf(255.0f * o);
-    return qmin - (0.02f + 1e-3f * qmin + 1e-5f * S) > thr;
+    return qmin - (0.02f + 1e-3f * qmin + 1e-5f * S) > p.thr;
+}
+
+__device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by0)
+{
+    return cull_test(cull_prep(a, b), bx0, by0);
 }
 
 template <bool STATS>
@@ -280,23 +308,22 @@ __device__ __forceinline__ float wave_reduce9(const float* p, int lane, int* vid
     return d;
 }
 
-// Backward, one workgroup per tile.  The four wavefronts walk the tile's
-// list together, 64 entries per batch from the last entry any pixel of the
-// tile included: the batch is staged once in LDS (16 entries per wavefront),
-// each wavefront culls it against its own 8 x 8 box and reduces the 9
-// partials of each entry over its lanes into an LDS row, and after a barrier
-// the 256 threads add the four rows of each (entry, value) and issue one
-// atomic add per nonzero sum -- a quarter of the atomics of per-wavefront
-// adds.  Staging and partial rows are double-buffered, so a batch costs two
-// workgroup barriers: one after staging, one before the sums.
-struct BwdShared {
-    Staged st[2];
-    float4 red[2][64 * 9];               // [entry * 9 + value] -> the 4 wavefronts' sums
-    unsigned long long wmask[2][4];      // entries each wavefront wrote in the batch
-    uint32_t maxl[4];
-};
-
-__global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* __restrict__ offsets,
+// Backward, one wavefront per 16 x 16 tile, four tiles per workgroup and no
+// workgroup barrier.  Lane l owns pixel l (x = l % 8, y = l / 8) of each 8 x 8
+// quadrant k of the tile (k & 1: right half, k >> 1: bottom half).  The
+// wavefront walks the tile's list back to front from the last entry any of its
+// pixels included, 64 entries per batch staged in its own LDS slice; lane i
+// gathers entry i and sets bit k of the entry's quadrant mask when the entry
+// precedes the last entry included in quadrant k and survives the cull
+// against quadrant k's box.  Per entry, the quadrants of the mask are
+// evaluated in turn (one wave-uniform branch each, skipped when none of the
+// quadrant's pixels includes the entry); the partials of a lane's four pixels
+// are summed in registers, the moments become the partials of the mean and
+// the conic, and one transposed reduction over the wavefront and one 9-lane
+// atomic add follow.  Entries that reach a tile mostly cover all of its
+// quadrants, so a tile-wide reduction replaces up to four per-quadrant ones.
+__global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
+                                                    const uint64_t* __restrict__ offsets,
                                                     const uint32_t* __restrict__ values,
                                                     const float4* __restrict__ g0, const float4* __restrict__ g1,
                                                     const float4* __restrict__ g2, float bg0, float bg1, float bg2,
@@ -306,162 +333,153 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, const uint64_t* 
                                                     const float* __restrict__ dl_dimage,
                                                     float* __restrict__ grad2d)
 {
-    __shared__ BwdShared sh;
-    const int lt = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int tx = g.ltx0 + lt % g.TWL, ty = g.lty0 + lt / g.TWL;
-    const int sx0 = tx * 16 + (wave & 1) * 8, sy0 = ty * 16 + (wave >> 1) * 8;
-    const int px = sx0 + (lane & 7), py = sy0 + (lane >> 3);
-    const bool inside = px < g.W && py < g.H;
-    const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
-    const float bx0 = (float)sx0 + 0.5f, by0 = (float)sy0 + 0.5f;
+    __shared__ Staged st[4];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t lt = (int64_t)blockIdx.x * 4 + wave;
+    if (lt >= n_tiles) return;
+    Staged& S = st[wave];
+    const int tx = g.ltx0 + (int)(lt % g.TWL), ty = g.lty0 + (int)(lt / g.TWL);
+    const int qx = lane & 7, qy = lane >> 3;
+    float pxc[2], pyc[2], bx[2], by[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        pxc[h] = (float)(tx * 16 + h * 8 + qx) + 0.5f;
+        pyc[h] = (float)(ty * 16 + h * 8 + qy) + 0.5f;
+        bx[h] = (float)(tx * 16 + h * 8) + 0.5f;
+        by[h] = (float)(ty * 16 + h * 8) + 0.5f;
+    }
     const uint64_t start = offsets[lt];
 
-    float T = 1.0f, gr0 = 0.0f, gr1 = 0.0f, gr2 = 0.0f;
-    uint32_t lst = 0;
-    if (inside) {
-        const int64_t lp = (int64_t)(py - g.py0) * g.WL + (px - g.px0);
-        T = tfinal[lp];
-        lst = last[lp];
-        if (dl_dimage) {
-            const int64_t P = (int64_t)g.W * g.H;
-            const int64_t gi = (int64_t)py * g.W + px;
-            gr0 = dl_dimage[gi];
-            gr1 = dl_dimage[P + gi];
-            gr2 = dl_dimage[2 * P + gi];
-        } else {
-            const uint32_t c = sgn[lp];
-            auto dec = [&](uint32_t code) { return code == 1u ? inv_norm : (code == 2u ? -inv_norm : 0.0f); };
-            gr0 = dec(c & 3u);
-            gr1 = dec((c >> 2) & 3u);
-            gr2 = dec((c >> 4) & 3u);
+    // per quadrant k: transmittance after the last included entry, dL/dout,
+    // GS = sum_ch dL/dout_ch * (colour behind the current entry, ch), which
+    // starts as the background seen through T_final, and the last entry
+    float T[4], GS[4], gr0[4], gr1[4], gr2[4];
+    uint32_t lst[4], mq[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int px = tx * 16 + (k & 1) * 8 + qx, py = ty * 16 + (k >> 1) * 8 + qy;
+        T[k] = 1.0f;
+        gr0[k] = gr1[k] = gr2[k] = 0.0f;
+        lst[k] = 0;
+        if (px < g.W && py < g.H) {
+            const int64_t lp = (int64_t)(py - g.py0) * g.WL + (px - g.px0);
+            T[k] = tfinal[lp];
+            lst[k] = last[lp];
+            if (dl_dimage) {
+                const int64_t P = (int64_t)g.W * g.H;
+                const int64_t gi = (int64_t)py * g.W + px;
+                gr0[k] = dl_dimage[gi];
+                gr1[k] = dl_dimage[P + gi];
+                gr2[k] = dl_dimage[2 * P + gi];
+            } else {
+                const uint32_t c = sgn[lp];
+                auto dec = [&](uint32_t code) { return code == 1u ? inv_norm : (code == 2u ? -inv_norm : 0.0f); };
+                gr0[k] = dec(c & 3u);
+                gr1[k] = dec((c >> 2) & 3u);
+                gr2[k] = dec((c >> 4) & 3u);
+            }
         }
+        GS[k] = T[k] * (gr0[k] * bg0 + gr1[k] * bg1 + gr2[k] * bg2);
+        mq[k] = __builtin_amdgcn_readfirstlane(gsd::wave_max_u32(lst[k]));
     }
-    // GS = sum_ch dL/dout_ch * (colour behind the current entry, ch); it
-    // starts as the background seen through T_final
-    float GS = T * (gr0 * bg0 + gr1 * bg1 + gr2 * bg2);
-    {
-        const uint32_t m = gsd::wave_max_u32(lst);
-        if (lane == 0) sh.maxl[wave] = m;
-    }
-    __syncthreads();
-    const int64_t maxl = (int64_t)max(max(sh.maxl[0], sh.maxl[1]), max(sh.maxl[2], sh.maxl[3]));
+    const uint32_t maxl = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
 
-    // stage entries [lo, hi) of the tile's list into buffer b (16 per wavefront)
-    auto stage = [&](int b, int64_t hi) {
-        const int64_t lo = hi > 64 ? hi - 64 : 0;
-        const int e = wave * 16 + lane;
-        if (lane < 16 && lo + e < hi) {
-            const uint32_t s = values[start + lo + e];
-            sh.st[b].a[e] = g0[s];
-            sh.st[b].b[e] = g1[s];
-            sh.st[b].c[e] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
-        }
-    };
-    if (maxl > 0) stage(0, maxl);
-    int b = 0;
-    for (int64_t hi = maxl; hi > 0; hi -= 64, b ^= 1) {
+    for (int64_t hi = maxl; hi > 0; hi -= 64) {
         const int64_t lo = hi > 64 ? hi - 64 : 0;
         const int cnt = (int)(hi - lo);
-        __syncthreads();                       // batch staged; previous sums done
-        Staged& S = sh.st[b];
-        bool keep = false;
-        if (lane < cnt) keep = !cull_box(S.a[lane], S.b[lane], bx0, by0);
-        uint64_t mask = gsd::ballot(keep);
-        uint64_t wrote = 0;
-        // Branch-free over the lanes, as in the forward: the inclusion of an
-        // entry is re-derived with the forward's exact f32 operations, and the
-        // partials of lanes that do not include it are zero.
+        uint32_t qb = 0;
+        if (lane < cnt) {
+            const uint32_t s = values[start + lo + lane];
+            const float4 a = g0[s], b = g1[s];
+            S.a[lane] = a;
+            S.b[lane] = b;
+            S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
+            const uint32_t n = (uint32_t)(lo + lane);
+            const CullPrep cp = cull_prep(a, b);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (n < mq[k] && !cull_test(cp, bx[k & 1], by[k >> 1])) qb |= 1u << k;
+        }
+        gsd::wave_sync();
+        uint64_t mask = gsd::ballot(qb != 0);
         while (mask) {
             const int j = 63 - __builtin_clzll(mask);
             mask &= ~(1ull << j);
+            const uint32_t qm = __builtin_amdgcn_readlane(qb, j);
             const uint32_t n = (uint32_t)(lo + j);
             const float4 a = S.a[j];
             const float4 bb = S.b[j];
-            const float cb = S.c[j].x;
-            const float dx = pxc - a.x, dy = pyc - a.y;
-            float t = a.w * dy;
-            t = __builtin_fmaf(a.z, dx, t);
-            const float u1 = bb.x * dy;
-            const float u = u1 * dy;
-            const float power = __builtin_fmaf(t, dx, u);
-            const bool pok = !(power > 0.0f);   // power < -87: alpha < 1/255 (as in the forward)
-            const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
-            const float av = bb.y * G;
-            const bool clamped = av > gsd::kAlphaMax;
-            const float alpha = clamped ? gsd::kAlphaMax : av;
-            const bool contrib = n < lst && pok && !(alpha < gsd::kAlphaMin);
-            if (gsd::ballot(contrib) == 0) continue;
-            // alpha of the lanes that include the entry, 0 on the others: then
-            // T / (1 - 0) = T and w = 0 leave those lanes' state unchanged
-            const float ae = contrib ? alpha : 0.0f;
-            // T before this entry = T after it / (1 - alpha)
-            const float rom = __builtin_amdgcn_rcpf(1.0f - ae);
-            T = T * rom;
-            const float w = ae * T;
-            // dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha))
-            const float grgb = __builtin_fmaf(gr2, cb, __builtin_fmaf(gr1, bb.w, gr0 * bb.z));
-            const float dal0 = __builtin_fmaf(T, grgb, -(rom * GS));
-            GS = __builtin_fmaf(grgb, w, GS);
+            const float4 cs = S.c[j];
             float p[9];
-            p[6] = gr0 * w;
-            p[7] = gr1 * w;
-            p[8] = gr2 * w;
-            // through alpha = o G, zero where alpha is clamped or not included
-            const float dal = (contrib && !clamped) ? dal0 : 0.0f;
-            p[5] = dal * G;
-            const float ndpw = -(dal * av);   // -dL/dpower
-            // power = -(A dx^2 + C dy^2)/2 - B dx dy with A = -2 a.z, B = -a.w,
-            // C = -2 b.x, dx = px - x, dy = py - y, so with q = -dL/dpower
-            //   dL/dx = (A dx + B dy) dL/dpower = 2 a.z (q dx) + a.w (q dy)
-            //   dL/dy = (C dy + B dx) dL/dpower = 2 b.x (q dy) + a.w (q dx)
-            //   dL/dA = (q dx dx)/2, dL/dB = q dx dy, dL/dC = (q dy dy)/2.
-            // The five moments q dx, q dy, q dx dx, q dx dy, q dy dy are summed
-            // over the pixels and turned into the five partials once per entry.
-            p[0] = ndpw * dx;
-            p[1] = ndpw * dy;
-            p[2] = p[0] * dx;
-            p[3] = p[0] * dy;
-            p[4] = p[1] * dy;
+#pragma unroll
+            for (int v = 0; v < 9; ++v) p[v] = 0.0f;
+            bool any = false;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (!((qm >> k) & 1u)) continue;
+                // Branch-free over the lanes, as in the forward: the inclusion
+                // is re-derived with the forward's exact f32 operations, and
+                // lanes that do not include the entry add zero partials.
+                const float dx = pxc[k & 1] - a.x, dy = pyc[k >> 1] - a.y;
+                float t = a.w * dy;
+                t = __builtin_fmaf(a.z, dx, t);
+                const float u1 = bb.x * dy;
+                const float u = u1 * dy;
+                const float power = __builtin_fmaf(t, dx, u);
+                const bool pok = !(power > 0.0f);   // power < -87: alpha < 1/255 (as in the forward)
+                const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
+                const float av = bb.y * G;
+                const bool clamped = av > gsd::kAlphaMax;
+                const float alpha = clamped ? gsd::kAlphaMax : av;
+                const bool contrib = n < lst[k] && pok && !(alpha < gsd::kAlphaMin);
+                if (gsd::ballot(contrib) == 0) continue;
+                any = true;
+                // alpha of the lanes that include the entry, 0 on the others:
+                // T / (1 - 0) = T and w = 0 leave those lanes' state unchanged
+                const float ae = contrib ? alpha : 0.0f;
+                // T before this entry = T after it / (1 - alpha)
+                const float rom = __builtin_amdgcn_rcpf(1.0f - ae);
+                T[k] = T[k] * rom;
+                const float w = ae * T[k];
+                // dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha))
+                const float grgb = __builtin_fmaf(gr2[k], cs.x, __builtin_fmaf(gr1[k], bb.w, gr0[k] * bb.z));
+                const float dal0 = __builtin_fmaf(T[k], grgb, -(rom * GS[k]));
+                GS[k] = __builtin_fmaf(grgb, w, GS[k]);
+                p[6] = __builtin_fmaf(gr0[k], w, p[6]);
+                p[7] = __builtin_fmaf(gr1[k], w, p[7]);
+                p[8] = __builtin_fmaf(gr2[k], w, p[8]);
+                // through alpha = o G, zero where alpha is clamped or not included
+                const float dal = (contrib && !clamped) ? dal0 : 0.0f;
+                p[5] = __builtin_fmaf(dal, G, p[5]);
+                // power = -(A dx^2 + C dy^2)/2 - B dx dy with A = -2 a.z,
+                // B = -a.w, C = -2 bb.x, dx = px - x, dy = py - y; with
+                // q = -dL/dpower the five moments q dx, q dy, q dx dx,
+                // q dx dy, q dy dy are summed here and give, once per entry,
+                //   dL/dx = (A dx + B dy) dL/dpower = 2 a.z (q dx) + a.w (q dy)
+                //   dL/dy = (C dy + B dx) dL/dpower = 2 bb.x (q dy) + a.w (q dx)
+                //   dL/dA = (q dx dx)/2, dL/dB = q dx dy, dL/dC = (q dy dy)/2.
+                const float q = -(dal * av);
+                const float qdx = q * dx, qdy = q * dy;
+                p[0] += qdx;
+                p[1] += qdy;
+                p[2] = __builtin_fmaf(qdx, dx, p[2]);
+                p[3] = __builtin_fmaf(qdx, dy, p[3]);
+                p[4] = __builtin_fmaf(qdy, dy, p[4]);
+            }
+            if (!any) continue;
+            const float m0 = p[0], m1 = p[1];
+            p[0] = 2.0f * a.z * m0 + a.w * m1;
+            p[1] = 2.0f * bb.x * m1 + a.w * m0;
+            p[2] = 0.5f * p[2];
+            p[4] = 0.5f * p[4];
             int v;
             const float r = wave_reduce9(p, lane, &v);
-            if (v >= 0) {
-                float* row = reinterpret_cast<float*>(&sh.red[b][j * 9 + v]);
-                row[wave] = r;
-            }
-            wrote |= 1ull << j;
-        }
-        if (lane == 0) sh.wmask[b][wave] = wrote;
-        __syncthreads();                       // rows of the batch written
-        // sums of the four rows, one atomic per nonzero (entry, value)
-        const unsigned long long m0 = sh.wmask[b][0], m1 = sh.wmask[b][1];
-        const unsigned long long m2 = sh.wmask[b][2], m3 = sh.wmask[b][3];
-        auto row_sum = [&](int o, int j) {
-            const float4 q = sh.red[b][o];
-            float sum = 0.0f;
-            sum += ((m0 >> j) & 1ull) ? q.x : 0.0f;
-            sum += ((m1 >> j) & 1ull) ? q.y : 0.0f;
-            sum += ((m2 >> j) & 1ull) ? q.z : 0.0f;
-            sum += ((m3 >> j) & 1ull) ? q.w : 0.0f;
-            return sum;
-        };
-        for (int o = tid; o < cnt * 9; o += 256) {
-            const int j = o / 9, v = o - j * 9;
-            float sum = row_sum(o, j);
-            if (v < 5) {
-                // moments -> partials of the mean and the conic
-                const float4 a = S.a[j];
-                if (v == 0) sum = 2.0f * a.z * sum + a.w * row_sum(o + 1, j);
-                else if (v == 1) sum = 2.0f * S.b[j].x * sum + a.w * row_sum(o - 1, j);
-                else if (v != 3) sum = 0.5f * sum;
-            }
-            if (sum != 0.0f) {
-                const uint32_t slot = __builtin_bit_cast(uint32_t, S.c[j].y);
-                unsafeAtomicAdd(&grad2d[(int64_t)slot * 9 + v], sum);
+            if (v >= 0 && r != 0.0f) {
+                const uint32_t slot = __builtin_bit_cast(uint32_t, cs.y);
+                unsafeAtomicAdd(&grad2d[(int64_t)slot * 9 + v], r);
             }
         }
-        if (hi - 64 > 0) stage(b ^ 1, hi - 64);
+        gsd::wave_sync();
     }
 }
 
@@ -498,8 +516,9 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
     const float inv_norm = (float)(1.0 / (3.0 * (double)cam->width * (double)cam->height));
     if (bins->n_tiles > 0) {
         GsTimerScope ts(ctx, "raster_bwd");
-        hipLaunchKernelGGL(k_raster_bwd, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g, bins->offsets,
-                           bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
+        const int64_t nt = bins->n_tiles;
+        hipLaunchKernelGGL(k_raster_bwd, dim3((unsigned)((nt + 3) / 4)), dim3(256), 0, ctx->stream, g, nt,
+                           bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
                            r->tfinal, r->last, r->sgn, inv_norm, dl_dimage, grad2d);
     }
     GS_HIP(ctx, hipGetLastError());
