@@ -7,8 +7,10 @@
 //     the f32 depth bits over slots in ascending order), giving the order
 //     (depth, slot) that every tile list must follow, and the per-tile
 //     candidate counts of the whole grid come from a 2D difference array
-//     (four integer atomics per rectangle, the first row and column
-//     aggregated in LDS) and a 2D prefix;
+//     and a 2D prefix.  The difference array is built one row at a time
+//     without global atomics: the rectangles' corners are bucketed by row
+//     (per-block row counts, their scan, a scatter), then one workgroup per
+//     row adds its corners in LDS and writes the row;
 //   - a leaf's tile offsets are the exclusive scan of those counts over the
 //     leaf's tiles (row-major inside the leaf);
 //   - coarse level: the leaf is covered by the image-aligned super-tiles of
@@ -69,6 +71,95 @@ __global__ __launch_bounds__(256) void k_rect_diff(int64_t n, const uint32_t* __
         for (int q = threadIdx.x; q < TWL; q += blockDim.x)
             if (row0[q]) atomicAdd(&diff[q], row0[q]);
     }
+}
+
+// ---- difference array by rows, without global atomics -------------------
+// Scattered integer atomics on device memory are slow (each one a separate
+// memory-side operation), so the corners of the rectangles (+1 at (y0, x0)
+// and (y1, x1), -1 at (y0, x1) and (y1, x0), those on the far edge dropped)
+// are bucketed by grid row instead: per-block row counts (kRowRects
+// rectangles per block), an exclusive scan of them in row-major order (row,
+// block), a scatter of one u32 record per corner (x << 1 | negative) to its
+// row's bucket, and one workgroup per row that adds its records into an LDS
+// copy of the row and writes the row.
+constexpr int kRowRects = 4096;    // rectangles per block of the bucketing passes
+constexpr int kRowsMax = 8192;     // grid rows (LDS counters of the bucketing passes)
+constexpr int kRowCellsMax = 16384; // grid columns (LDS row of the summing pass)
+
+template <typename Fn>
+__device__ __forceinline__ void leaf_corners(int4 r, int ltx0, int lty0, int ltx1, int lty1, Fn&& fn)
+{
+    const int TWL = ltx1 - ltx0, THL = lty1 - lty0;
+    const int x0 = max(r.x, ltx0) - ltx0, x1 = min(r.z, ltx1) - ltx0;
+    const int y0 = max(r.y, lty0) - lty0, y1 = min(r.w, lty1) - lty0;
+    if (!(x0 < x1 && y0 < y1)) return;
+    fn(y0, x0, 0u);
+    if (x1 < TWL) fn(y0, x1, 1u);
+    if (y1 < THL) {
+        fn(y1, x0, 1u);
+        if (x1 < TWL) fn(y1, x1, 0u);
+    }
+}
+
+// hist[row * nblk + block] = corners of the block's rectangles in that row
+__global__ __launch_bounds__(256) void k_row_hist(int64_t n, const int4* __restrict__ rect, int ltx0, int lty0,
+                                                  int ltx1, int lty1, uint32_t* __restrict__ hist)
+{
+    __shared__ uint32_t cnt[kRowsMax];
+    const int THL = lty1 - lty0;
+    for (int y = threadIdx.x; y < THL; y += blockDim.x) cnt[y] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kRowRects;
+    const int64_t lim = min<int64_t>(n - base, kRowRects);
+    for (int k = threadIdx.x; k < lim; k += blockDim.x)
+        leaf_corners(rect[base + k], ltx0, lty0, ltx1, lty1, [&](int y, int, uint32_t) { atomicAdd(&cnt[y], 1u); });
+    __syncthreads();
+    for (int y = threadIdx.x; y < THL; y += blockDim.x) hist[(int64_t)y * gridDim.x + blockIdx.x] = cnt[y];
+}
+
+// the same blocks write their corner records at the scanned offsets
+__global__ __launch_bounds__(256) void k_row_scatter(int64_t n, const int4* __restrict__ rect, int ltx0, int lty0,
+                                                     int ltx1, int lty1, const uint32_t* __restrict__ off,
+                                                     uint32_t* __restrict__ rec)
+{
+    __shared__ uint32_t pos[kRowsMax];
+    const int THL = lty1 - lty0;
+    for (int y = threadIdx.x; y < THL; y += blockDim.x) pos[y] = off[(int64_t)y * gridDim.x + blockIdx.x];
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kRowRects;
+    const int64_t lim = min<int64_t>(n - base, kRowRects);
+    for (int k = threadIdx.x; k < lim; k += blockDim.x)
+        leaf_corners(rect[base + k], ltx0, lty0, ltx1, lty1, [&](int y, int x, uint32_t neg) {
+            rec[atomicAdd(&pos[y], 1u)] = ((uint32_t)x << 1) | neg;
+        });
+}
+
+// one workgroup per row: its records [off[row * nblk], off[(row + 1) * nblk])
+__global__ __launch_bounds__(256) void k_row_sum(const uint32_t* __restrict__ off, int nblk,
+                                                 const uint32_t* __restrict__ rec, int TWL,
+                                                 int32_t* __restrict__ diff)
+{
+    extern __shared__ int32_t row[];
+    const int y = blockIdx.x;
+    for (int x = threadIdx.x; x < TWL; x += blockDim.x) row[x] = 0;
+    __syncthreads();
+    const int64_t r0 = off[(int64_t)y * nblk], r1 = off[(int64_t)(y + 1) * nblk];
+    constexpr int U = 8;   // independent loads in flight per thread
+    const int64_t B = blockDim.x;
+    int64_t k = r0 + threadIdx.x;
+    for (; k + (U - 1) * B < r1; k += U * B) {
+        uint32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = rec[k + u * B];
+#pragma unroll
+        for (int u = 0; u < U; ++u) atomicAdd(&row[v[u] >> 1], (v[u] & 1u) ? -1 : 1);
+    }
+    for (; k < r1; k += B) {
+        const uint32_t v = rec[k];
+        atomicAdd(&row[v >> 1], (v & 1u) ? -1 : 1);
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < TWL; x += blockDim.x) diff[(int64_t)y * TWL + x] = row[x];
 }
 
 // The same difference array for a grid that fits in LDS (few tiles, so
@@ -427,11 +518,35 @@ gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, 
     const int64_t cells = (int64_t)(leaf.tx1 - leaf.tx0) * (leaf.ty1 - leaf.ty0);
     if (n > 0) {
         GsTimerScope ts(ctx, "rect_diff");
-        if (cells <= kDiffLds)
+        const int TWL = leaf.tx1 - leaf.tx0, THL = leaf.ty1 - leaf.ty0;
+        if (cells <= kDiffLds) {
             hipLaunchKernelGGL(k_rect_diff_lds, dim3((unsigned)ceil_div(n, kDiffBlock)), dim3(256),
                                sizeof(int32_t) * cells, ctx->stream, n, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1,
                                leaf.ty1, diff);
-        else
+        } else if (!list && TWL <= kRowCellsMax && THL <= kRowsMax && n < (int64_t)1 << 30) {
+            // by rows: every cell of the grid is written
+            const int64_t nblk = ceil_div(n, kRowRects);
+            const int64_t nh = nblk * THL;
+            std::vector<GsAlloc> tmp;
+            uint32_t* hist = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nh, GS_MEM_SCRATCH, &tmp);
+            uint32_t* off = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (nh + 1), GS_MEM_SCRATCH, &tmp);
+            uint32_t* rec = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * 4 * n, GS_MEM_SCRATCH, &tmp);
+            if (!hist || !off || !rec) {
+                gs_free_all(ctx, &tmp);
+                return GS_ERR_OOM;
+            }
+            hipLaunchKernelGGL(k_row_hist, dim3((unsigned)nblk), dim3(256), 0, ctx->stream, n, proj->rect, leaf.tx0,
+                               leaf.ty0, leaf.tx1, leaf.ty1, hist);
+            gs_status st = launch_scan_u32_to_u32(ctx, hist, off, nh);
+            if (st == GS_OK) {
+                hipLaunchKernelGGL(k_row_scatter, dim3((unsigned)nblk), dim3(256), 0, ctx->stream, n, proj->rect,
+                                   leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, off, rec);
+                hipLaunchKernelGGL(k_row_sum, dim3((unsigned)THL), dim3(256), sizeof(int32_t) * TWL, ctx->stream, off,
+                                   (int)nblk, rec, TWL, diff);
+            }
+            gs_free_all(ctx, &tmp);
+            if (st != GS_OK) return st;
+        } else
             hipLaunchKernelGGL(k_rect_diff, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, list,
                                proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, diff);
     }
