@@ -110,7 +110,8 @@ def main():
         log(f"[bench] warmup step {k}: loss {r['loss']:.6f} cand {r['n_cand']} isect {r['n_isect']} "
             f"leaves {r['n_leaves']}")
     kernels = ["project_flags", "project_write", "prefix2d", "scan", "rect_diff", "bin_count", "emit", "radix",
-               "seg_offsets", "fine", "plan_split", "leaf_groups", "raster_fwd", "raster_bwd", "project_bwd", "adam"]
+               "seg_offsets", "fine", "plan_split", "leaf_groups", "raster_fwd", "raster_bwd", "project_bwd", "adam",
+               "bwd_adam"]
 
     def kernel_times(n_steps, names):
         out = {}
@@ -284,7 +285,7 @@ def count_work(B, ctx, cam, params, budget):
 
 
 KERNEL_WORK_NAMES = ("raster_fwd", "raster_bwd", "radix", "emit", "bin_count", "seg_offsets", "fine", "rect_diff",
-                     "project_flags", "project_write", "project_bwd", "adam")
+                     "project_flags", "project_write", "project_bwd", "adam", "bwd_adam")
 
 
 def kernel_work(wc, sc):
@@ -314,6 +315,8 @@ def kernel_work(wc, sc):
         "project_write": ("hbm", N * (40 + 4 + 12 * K + 8) + Nc * 68, "read parameters, write compact state"),
         "project_bwd": ("hbm", Nc * (36 + 48 + 40 + 4 + 12 * K + 4 * F + 4), "read 2D grads, state, params; write 3D grads"),
         "adam": ("hbm", 24 * N * F + 4 * F * Nc + 4 * N, "read/write params, m, v; read compact grads"),
+        "bwd_adam": ("hbm", 24 * N * F + 52 * Nc + 4 * N, "read/write params, m, v once; read the candidates' 2D "
+                                                         "grads and flags, the slot map"),
     }
 
 

@@ -11,67 +11,95 @@
 
 namespace {
 
-struct AdamArgs {
-    float lr_t, b1, b2, eps, inv_bc2;   // lr_t = lr / (1 - b1^t), inv_bc2 = 1 / (1 - b2^t)
+using gsd::AdamArgs;
+using gsd::adam_one;
+
+// The five parameter groups in one launch: blocks [bend[q-1], bend[q]) update
+// group q (means, log-scales, quaternions, opacity logits, SH; W values per
+// Gaussian, W a compile-time constant).  Each group covers the Gaussians
+// [g0, g1) whose candidates are exactly the slots [s0, s1) of the compact
+// gradient rows (row s - s0 of grad3d, the group's values from column col0):
+// g0 = 0 or the Gaussian of slot s0, g1 = N or the Gaussian of slot s1 (slots
+// are in ascending Gaussian order), read on the device, hence grid-stride
+// loops.  The flat value range [g0 W, g1 W) is walked as aligned float4s
+// (arrays 16-byte aligned, checked by the launcher; otherwise one value per
+// thread), with at most three single values at each end.  Indices are 32-bit
+// (N W < 2^32, checked by the launcher).
+struct AdamGroup {
+    float* p;
+    float* m;
+    float* v;
+    int col0;
+    bool vec;
 };
 
-// m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2,
-// p -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
-// (hardware reciprocal and square root, 1 ulp)
-__device__ __forceinline__ void adam_one(float g, float& p, float& m, float& v, const AdamArgs& a)
-{
-    m = a.b1 * m + (1.0f - a.b1) * g;
-    v = a.b2 * v + (1.0f - a.b2) * g * g;
-    p = p - a.lr_t * m * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(v * a.inv_bc2) + a.eps);
-}
+struct AdamJob {
+    AdamGroup grp[5];
+    int bend[5];   // cumulative block counts
+};
 
-// Group of `width` consecutive values per Gaussian at column `col0` of the
-// compact gradient rows of slots [s0, s1) (row s - s0 in grad3d).  Covers the
-// Gaussians [g0, g1) whose candidates are exactly those slots: g0 = 0 or the
-// Gaussian of slot s0, g1 = N or the Gaussian of slot s1 (slots are in
-// ascending Gaussian order).  Grid-stride, since g0 and g1 are read here.
-// Indices are 32-bit (n * width < 2^32, checked by the launcher).  vec: the
-// arrays are 16-byte aligned and width is a multiple of 4, so each thread
-// takes an aligned float4 of one Gaussian's values.
-__global__ __launch_bounds__(256) void k_adam_group(uint32_t n, int64_t n_cand, const uint32_t* __restrict__ ids,
-                                                    int64_t s0, int64_t s1, uint32_t width, int col0, int F,
-                                                    const int32_t* __restrict__ slot_of,
-                                                    const float* __restrict__ grad3d, float* __restrict__ p,
-                                                    float* __restrict__ m, float* __restrict__ v, AdamArgs a,
-                                                    bool vec)
+template <int W>
+__device__ __forceinline__ void adam_group(const AdamGroup& gr, int blk, int nblk, uint32_t g0, uint32_t g1,
+                                           int64_t s0, int F, const int32_t* __restrict__ slot_of,
+                                           const float* __restrict__ grad3d, const AdamArgs& a)
 {
-    const uint32_t g0 = s0 == 0 ? 0u : ids[s0];
-    const uint32_t g1 = s1 >= n_cand ? n : ids[s1];
-    const uint32_t e0 = g0 * width, e1 = g1 * width;
-    const uint32_t stride = gridDim.x * blockDim.x;
-    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (!vec) {
-        for (uint32_t k = e0 + t; k < e1; k += stride) {
-            const uint32_t i = k / width;
-            const int32_t s = slot_of[i];
-            const float g = s >= 0 ? grad3d[(int64_t)(s - s0) * F + col0 + (k - i * width)] : 0.0f;
-            adam_one(g, p[k], m[k], v[k], a);
-        }
+    const uint32_t e0 = g0 * (uint32_t)W, e1 = g1 * (uint32_t)W;
+    const uint32_t t = (uint32_t)blk * blockDim.x + threadIdx.x;
+    const uint32_t stride = (uint32_t)nblk * blockDim.x;
+    auto grad = [&](uint32_t k) {
+        const uint32_t i = k / (uint32_t)W;
+        const int32_t s = slot_of[i];
+        return s >= 0 ? grad3d[(int64_t)(s - s0) * F + gr.col0 + (k - i * (uint32_t)W)] : 0.0f;
+    };
+    auto one = [&](uint32_t k) {
+        float p = gr.p[k], m = gr.m[k], v = gr.v[k];
+        adam_one(grad(k), p, m, v, a);
+        gr.p[k] = p;
+        gr.m[k] = m;
+        gr.v[k] = v;
+    };
+    if (!gr.vec) {
+        for (uint32_t k = e0 + t; k < e1; k += stride) one(k);
         return;
     }
-    for (uint32_t k = e0 + 4 * t; k < e1; k += 4 * stride) {
-        const uint32_t i = k / width;
-        const int32_t s = slot_of[i];
-        float4 gg = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (s >= 0) {
-            const float* gr = grad3d + (int64_t)(s - s0) * F + col0 + (k - i * width);
-            gg = make_float4(gr[0], gr[1], gr[2], gr[3]);
-        }
-        float4 pp = *reinterpret_cast<const float4*>(p + k);
-        float4 mm = *reinterpret_cast<const float4*>(m + k);
-        float4 vv = *reinterpret_cast<const float4*>(v + k);
-        adam_one(gg.x, pp.x, mm.x, vv.x, a);
-        adam_one(gg.y, pp.y, mm.y, vv.y, a);
-        adam_one(gg.z, pp.z, mm.z, vv.z, a);
-        adam_one(gg.w, pp.w, mm.w, vv.w, a);
-        *reinterpret_cast<float4*>(p + k) = pp;
-        *reinterpret_cast<float4*>(m + k) = mm;
-        *reinterpret_cast<float4*>(v + k) = vv;
+    const uint32_t a0 = min((e0 + 3u) & ~3u, e1);
+    const uint32_t a1 = max(a0, e1 & ~3u);
+    if (t < a0 - e0) one(e0 + t);
+    if (t < e1 - a1) one(a1 + t);
+    for (uint32_t k = a0 + 4u * t; k < a1; k += 4u * stride) {
+        float4 pp = *reinterpret_cast<const float4*>(gr.p + k);
+        float4 mm = *reinterpret_cast<const float4*>(gr.m + k);
+        float4 vv = *reinterpret_cast<const float4*>(gr.v + k);
+        const float q0 = grad(k), q1 = grad(k + 1), q2 = grad(k + 2), q3 = grad(k + 3);
+        adam_one(q0, pp.x, mm.x, vv.x, a);
+        adam_one(q1, pp.y, mm.y, vv.y, a);
+        adam_one(q2, pp.z, mm.z, vv.z, a);
+        adam_one(q3, pp.w, mm.w, vv.w, a);
+        *reinterpret_cast<float4*>(gr.p + k) = pp;
+        *reinterpret_cast<float4*>(gr.m + k) = mm;
+        *reinterpret_cast<float4*>(gr.v + k) = vv;
+    }
+}
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_adam(uint32_t n, int64_t n_cand, const uint32_t* __restrict__ ids,
+                                              int64_t s0, int64_t s1, const int32_t* __restrict__ slot_of,
+                                              const float* __restrict__ grad3d, AdamJob job, AdamArgs a)
+{
+    constexpr int F = 11 + 3 * (DEG + 1) * (DEG + 1);
+    const uint32_t g0 = s0 == 0 ? 0u : ids[s0];
+    const uint32_t g1 = s1 >= n_cand ? n : ids[s1];
+    const int b = blockIdx.x;
+    int q = 0;
+    while (q < 4 && b >= job.bend[q]) ++q;
+    const int lo = q == 0 ? 0 : job.bend[q - 1];
+    const int blk = b - lo, nblk = job.bend[q] - lo;
+    switch (q) {
+    case 0: adam_group<3>(job.grp[0], blk, nblk, g0, g1, s0, F, slot_of, grad3d, a); break;
+    case 1: adam_group<3>(job.grp[1], blk, nblk, g0, g1, s0, F, slot_of, grad3d, a); break;
+    case 2: adam_group<4>(job.grp[2], blk, nblk, g0, g1, s0, F, slot_of, grad3d, a); break;
+    case 3: adam_group<1>(job.grp[3], blk, nblk, g0, g1, s0, F, slot_of, grad3d, a); break;
+    default: adam_group<F - 11>(job.grp[4], blk, nblk, g0, g1, s0, F, slot_of, grad3d, a); break;
     }
 }
 
@@ -93,31 +121,36 @@ gs_status launch_adam(gs_ctx* ctx, const gs_proj* proj, int64_t n, int sh_degree
                       int32_t step, float lr, float b1, float b2, float eps)
 {
     const int K = (sh_degree + 1) * (sh_degree + 1);
-    const int F = 11 + 3 * K;
-    AdamArgs a;
-    a.b1 = b1; a.b2 = b2; a.eps = eps;
-    a.lr_t = (float)((double)lr / (1.0 - std::pow((double)b1, (double)step)));
-    a.inv_bc2 = (float)(1.0 / (1.0 - std::pow((double)b2, (double)step)));
-    struct G { float* p; float* m; float* v; int width, col0; } groups[5] = {
-        {p->means, m->means, v->means, 3, 0},
-        {p->log_scales, m->log_scales, v->log_scales, 3, 3},
-        {p->quats, m->quats, v->quats, 4, 6},
-        {p->opacity_logits, m->opacity_logits, v->opacity_logits, 1, 10},
-        {p->sh, m->sh, v->sh, 3 * K, 11}};
+    const AdamArgs a = gsd::adam_args(step, lr, b1, b2, eps);
+    const int width[5] = {3, 3, 4, 1, 3 * K};
+    float* const pp[5] = {p->means, p->log_scales, p->quats, p->opacity_logits, p->sh};
+    float* const mp[5] = {m->means, m->log_scales, m->quats, m->opacity_logits, m->sh};
+    float* const vp[5] = {v->means, v->log_scales, v->quats, v->opacity_logits, v->sh};
+    const int col0[5] = {0, 3, 6, 10, 11};
     if (n <= 0) return GS_OK;
     if ((uint64_t)n * (uint64_t)(3 * K) >= (1ull << 32))
         return gs_fail(ctx, GS_ERR_OVERFLOW, "Adam over %lld Gaussians x %d values exceeds 2^32", (long long)n, 3 * K);
     GsTimerScope ts(ctx, "adam");
-    // enough threads for the Gaussians of the slot range (about its share of
-    // all Gaussians), at most 8 per compute unit and wavefront slot
+    // blocks per group for the Gaussians of the slot range (about its share
+    // of all Gaussians): about four float4s per thread, at most 4096 blocks
     const int64_t share = proj->n_cand > 0 ? ceil_div(n * (s1 - s0), proj->n_cand) : n;
-    for (const G& g : groups) {
-        const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(share * g.width, 1024), 8192));
-        const bool vec = g.width % 4 == 0 && (((uintptr_t)g.p | (uintptr_t)g.m | (uintptr_t)g.v) & 15u) == 0;
-        hipLaunchKernelGGL(k_adam_group, dim3((unsigned)blocks), dim3(256), 0, ctx->stream, (uint32_t)n,
-                           proj->n_cand, proj->ids, s0, s1, (uint32_t)g.width, g.col0, F, proj->slot_of, grad3d,
-                           g.p, g.m, g.v, a, vec);
+    AdamJob job;
+    int total = 0;
+    for (int q = 0; q < 5; ++q) {
+        job.grp[q] = AdamGroup{pp[q], mp[q], vp[q], col0[q],
+                               (((uintptr_t)pp[q] | (uintptr_t)mp[q] | (uintptr_t)vp[q]) & 15u) == 0};
+        total += (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(share * width[q], 4 * 4 * 256), 4096));
+        job.bend[q] = total;
     }
+#define GS_ADAM(D) hipLaunchKernelGGL(k_adam<D>, dim3((unsigned)total), dim3(256), 0, ctx->stream, (uint32_t)n, \
+                                      proj->n_cand, proj->ids, s0, s1, proj->slot_of, grad3d, job, a)
+    switch (sh_degree) {
+    case 0: GS_ADAM(0); break;
+    case 1: GS_ADAM(1); break;
+    case 2: GS_ADAM(2); break;
+    default: GS_ADAM(3); break;
+    }
+#undef GS_ADAM
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -153,9 +153,6 @@ static void destroy_handle(gs_ctx* ctx, GsHandle* h)
 // ---------------------------------------------------------------------------
 // read-back helper: copy `bytes` device bytes to the pinned buffer and wait
 
-// candidate slots per projection-backward + Adam chunk of gs_train_view
-constexpr int64_t kAdamChunkSlots = 512 * 1024;
-
 static gs_status readback(gs_ctx* ctx, const void* dev, size_t bytes, void* host)
 {
     GS_HIP(ctx, hipMemcpyAsync(ctx->pinned, dev, bytes, hipMemcpyDeviceToHost, ctx->stream));
@@ -998,17 +995,25 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
             (st = gs_adam_step(ctx, proj, params->n, params->sh_degree, opts->params_rw, opts->adam_m, opts->adam_v,
                                grad3d, opts->adam_step, opts->lr, opts->beta1, opts->beta2, opts->eps)) != GS_OK)
             goto done;
+    } else if (opts->adam_chunk <= 0) {
+        // projection backward fused with the update over all Gaussians
+        if (!opts->params_rw || !opts->adam_m || !opts->adam_v) {
+            st = gs_fail(ctx, GS_ERR_INVALID_ARG, "Adam parameters / moments NULL");
+            goto done;
+        }
+        if ((st = launch_bwd_adam(ctx, cam, params, proj, grad2d, opts->params_rw, opts->adam_m, opts->adam_v,
+                                  opts->adam_step, opts->lr, opts->beta1, opts->beta2, opts->eps)) != GS_OK)
+            goto done;
     } else {
         // Projection backward and Adam in chunks of candidate slots: the
-        // compact gradient rows of one chunk at a time (121 MB at SH3), each
-        // chunk's Gaussians updated right after; same result as the whole
+        // compact gradient rows of one chunk at a time, each chunk's
+        // Gaussians updated right after; same result as the whole
         // [n_cand][F] buffer followed by one Adam step.
         if (!opts->params_rw || !opts->adam_m || !opts->adam_v) {
             st = gs_fail(ctx, GS_ERR_INVALID_ARG, "Adam parameters / moments NULL");
             goto done;
         }
-        const int64_t want = opts->adam_chunk > 0 ? opts->adam_chunk : kAdamChunkSlots;
-        const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(nc, want));
+        const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(nc, opts->adam_chunk));
         float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * chunk, GS_MEM_GRAD, &view);
         if (!grad3d) { st = GS_ERR_OOM; goto done; }
         for (int64_t s0 = 0; s0 < std::max<int64_t>(nc, 1); s0 += chunk) {

@@ -10,6 +10,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 #include <stdint.h>
 
 namespace gsd {
@@ -120,6 +122,34 @@ __device__ __forceinline__ void sh_basis_grad(int deg, float x, float y, float z
     D[13][0] = c3c * (4.0f * zz - 3.0f * xx - yy); D[13][1] = -2.0f * c3c * x * y; D[13][2] = 8.0f * c3c * x * z;
     D[14][0] = 2.0f * c3e * x * z; D[14][1] = -2.0f * c3e * y * z; D[14][2] = c3e * (xx - yy);
     D[15][0] = 3.0f * c3a * (xx - yy); D[15][1] = -6.0f * c3a * x * y; D[15][2] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Adam (SkipGS notes, "loss function"): one step of one value.
+struct AdamArgs {
+    float lr_t, b1, b2, eps, inv_bc2;   // lr_t = lr / (1 - b1^t), inv_bc2 = 1 / (1 - b2^t)
+};
+
+// m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2,
+// p -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+// (hardware reciprocal and square root, 1 ulp)
+__device__ __forceinline__ void adam_one(float g, float& p, float& m, float& v, const AdamArgs& a)
+{
+    m = a.b1 * m + (1.0f - a.b1) * g;
+    v = a.b2 * v + (1.0f - a.b2) * g * g;
+    p = p - a.lr_t * m * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(v * a.inv_bc2) + a.eps);
+}
+
+// the step-t constants (bias corrections in f64, rounded once)
+inline AdamArgs adam_args(int32_t step, float lr, float b1, float b2, float eps)
+{
+    AdamArgs a;
+    a.b1 = b1;
+    a.b2 = b2;
+    a.eps = eps;
+    a.lr_t = (float)((double)lr / (1.0 - std::pow((double)b1, (double)step)));
+    a.inv_bc2 = (float)(1.0 / (1.0 - std::pow((double)b2, (double)step)));
+    return a;
 }
 
 // ---------------------------------------------------------------------------

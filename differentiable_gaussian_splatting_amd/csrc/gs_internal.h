@@ -218,5 +218,11 @@ gs_status launch_adam(gs_ctx* ctx, const gs_proj* proj, int64_t n, int sh_degree
                       const gs_param_ptrs* m, const gs_param_ptrs* v, const float* grad3d, int64_t s0, int64_t s1,
                       int32_t step, float lr, float b1, float b2, float eps);
 gs_status launch_scatter_grad3d(gs_ctx* ctx, const gs_proj* proj, int F, const float* grad3d, float* dense);
+// projection backward of the candidates fused with one Adam step over all N
+// Gaussians (no gradient array); p: the parameters the backward reads, pr /
+// m / v: the parameters and moments Adam updates (pr may equal p's arrays)
+gs_status launch_bwd_adam(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
+                          const float* grad2d, const gs_param_ptrs* pr, const gs_param_ptrs* m, const gs_param_ptrs* v,
+                          int32_t step, float lr, float b1, float b2, float eps);
 
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -213,33 +213,20 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, co
 }
 
 // ---------------------------------------------------------------------------
-// Projection backward, one thread per candidate (f32).  Chain rule through
-// each step of the projection, with the forward's clamp decisions (flags).
+// Projection backward of one candidate, Gaussian i (f32): the chain rule
+// through each step of the projection, with the forward's clamp decisions
+// (flags fl).  g: the candidate's 9 screen-space partials (mean2d, conic,
+// opacity, colour).  shi: its 3K SH coefficients (device memory or LDS).
+// Out: geo[0..10] = dL/d(mean, log-scale, quaternion, opacity logit), Y[0..K-1]
+// = the SH basis at the view direction and grm[3] = dL/drgb, zero where the
+// forward clamped the channel; dL/dsh[k][c] = Y[k] grm[c].
 template <int DEG>
-__global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int64_t s_end,
-                                                     const float* __restrict__ means,
-                                                     const float* __restrict__ log_scales,
-                                                     const float* __restrict__ quats,
-                                                     const float* __restrict__ logits, const float* __restrict__ sh,
-                                                     const uint32_t* __restrict__ ids,
-                                                     const float4* __restrict__ g2s,
-                                                     const float* __restrict__ grad2d, float* __restrict__ grad3d)
+__device__ __forceinline__ void proj_bwd_one(const CamDev& cam, int64_t i, uint32_t fl, const float* g,
+                                             const float* __restrict__ means, const float* __restrict__ log_scales,
+                                             const float* __restrict__ quats, const float* __restrict__ logits,
+                                             const float* shi, float* geo, float* Y, float* grm)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    constexpr int F = 11 + 3 * K;
-    // the wave's 64 output rows are contiguous in grad3d: stage them in LDS
-    // (odd row stride) and write them out coalesced at the end
-    constexpr int RS = F | 1;
-    __shared__ float outs[4][64 * RS];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t w0 = s0 + (int64_t)blockIdx.x * blockDim.x + wave * 64;   // slots [s0, s_end)
-    const int64_t j = w0 + lane;
-    float* out = outs[wave] + lane * RS;
-    if (j < s_end) {
-    const int64_t i = ids[j];
-    const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[j].w);
-    const float* g = grad2d + 9 * j;
-
     // forward recomputation
     const float mu[3] = {means[3 * i], means[3 * i + 1], means[3 * i + 2]};
     float p[3];
@@ -351,9 +338,9 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int
             dRq[r][cc] = dM[r][cc] * s[cc];
             ds[cc] += dM[r][cc] * Rq[r][cc];
         }
-    out[3] = ds[0] * s[0];
-    out[4] = ds[1] * s[1];
-    out[5] = ds[2] * s[2];
+    geo[3] = ds[0] * s[0];
+    geo[4] = ds[1] * s[1];
+    geo[5] = ds[2] * s[2];
     // rotation of the unit quaternion (w, x, y, z)
     float gw = 0.0f, gx = 0.0f, gy = 0.0f, gz = 0.0f;
     gy += -4.0f * y * dRq[0][0]; gz += -4.0f * z * dRq[0][0];
@@ -367,26 +354,23 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int
     gx += -4.0f * x * dRq[2][2]; gy += -4.0f * y * dRq[2][2];
     const float dot = w * gw + x * gx + y * gy + z * gz;
     const float iqn = 1.0f / qn;
-    out[6] = (gw - w * dot) * iqn;
-    out[7] = (gx - x * dot) * iqn;
-    out[8] = (gy - y * dot) * iqn;
-    out[9] = (gz - z * dot) * iqn;
-    out[10] = g[5] * o * (1.0f - o);
+    geo[6] = (gw - w * dot) * iqn;
+    geo[7] = (gx - x * dot) * iqn;
+    geo[8] = (gy - y * dot) * iqn;
+    geo[9] = (gz - z * dot) * iqn;
+    geo[10] = g[5] * o * (1.0f - o);
     // colour: rgb = 0.5 + sum_k Y_k(d) sh_k, masked where clamped
-    float Y[16], D[16][3];
+    float D[16][3];
     gsd::sh_basis(DEG, d[0], d[1], d[2], Y);
     gsd::sh_basis_grad(DEG, d[0], d[1], d[2], D);
-    const float* shi = sh + (int64_t)3 * K * i;
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) grm[ch] = (fl & (1u << ch)) ? 0.0f : g[6 + ch];
     float dd0 = 0.0f, dd1 = 0.0f, dd2 = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         float t = 0.0f;
 #pragma unroll
-        for (int ch = 0; ch < 3; ++ch) {
-            const float gr = (fl & (1u << ch)) ? 0.0f : g[6 + ch];
-            out[11 + 3 * k + ch] = Y[k] * gr;
-            t += shi[3 * k + ch] * gr;
-        }
+        for (int ch = 0; ch < 3; ++ch) t += shi[3 * k + ch] * grm[ch];
         dd0 += t * D[k][0];
         dd1 += t * D[k][1];
         dd2 += t * D[k][2];
@@ -396,9 +380,43 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int
     float dmu[3] = {(dd0 - d[0] * ddot) * ivn, (dd1 - d[1] * ddot) * ivn, (dd2 - d[2] * ddot) * ivn};
 #pragma unroll
     for (int e = 0; e < 3; ++e) dmu[e] += cam.R[e] * dp[0] + cam.R[3 + e] * dp[1] + cam.R[6 + e] * dp[2];
-    out[0] = dmu[0];
-    out[1] = dmu[1];
-    out[2] = dmu[2];
+    geo[0] = dmu[0];
+    geo[1] = dmu[1];
+    geo[2] = dmu[2];
+}
+
+// Projection backward, one thread per candidate slot in [s0, s_end); row
+// j - s0 of grad3d gets the candidate's F partials.
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int64_t s_end,
+                                                     const float* __restrict__ means,
+                                                     const float* __restrict__ log_scales,
+                                                     const float* __restrict__ quats,
+                                                     const float* __restrict__ logits, const float* __restrict__ sh,
+                                                     const uint32_t* __restrict__ ids,
+                                                     const float4* __restrict__ g2s,
+                                                     const float* __restrict__ grad2d, float* __restrict__ grad3d)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    constexpr int F = 11 + 3 * K;
+    // the wave's 64 output rows are contiguous in grad3d: stage them in LDS
+    // (odd row stride) and write them out coalesced at the end
+    constexpr int RS = F | 1;
+    __shared__ float outs[4][64 * RS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t w0 = s0 + (int64_t)blockIdx.x * blockDim.x + wave * 64;   // slots [s0, s_end)
+    const int64_t j = w0 + lane;
+    float* out = outs[wave] + lane * RS;
+    if (j < s_end) {
+        const int64_t i = ids[j];
+        const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[j].w);
+        float Y[16], grm[3];
+        proj_bwd_one<DEG>(cam, i, fl, grad2d + 9 * j, means, log_scales, quats, logits, sh + (int64_t)3 * K * i, out,
+                          Y, grm);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) out[11 + 3 * k + ch] = Y[k] * grm[ch];
     }
     gsd::wave_sync();
     const int64_t rows = s_end - w0 < 64 ? s_end - w0 : 64;
@@ -407,6 +425,141 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int
         const float* src = outs[wave];
         for (int q = lane; q < rows * F; q += 64) dst[q] = src[(q / F) * RS + q % F];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Projection backward fused with the Adam step, over all N Gaussians (one
+// Adam step per view over the summed gradient, BoundedGS page, "01"; SkipGS
+// notes, "loss function": Adam; Gaussians that are not candidates of the view
+// get a zero gradient).  A wavefront takes 64 consecutive Gaussians:
+//   1. their SH rows are staged in LDS with coalesced loads;
+//   2. each lane runs the projection backward of its Gaussian if it is a
+//      candidate (SH coefficients from LDS), giving its 11 geometric partials
+//      and the factors Y[k], dL/drgb[c] of its SH partials Y[k] dL/drgb[c];
+//   3. the factors replace the staged rows in LDS, and the lane updates its
+//      Gaussian's 11 geometric values;
+//   4. the wavefront updates its 64 SH rows as aligned float4s (the rows of
+//      64 Gaussians start on a 256-byte boundary), each value's partial
+//      formed from the two LDS factors.
+// No gradient array is written, and each parameter and moment crosses HBM
+// once each way.  The backward reads the parameters through `means` ... `sh`
+// and Adam updates `pw`; the two may be the same arrays (a Gaussian's values
+// are read by its own wavefront before that wavefront writes them).
+struct AdamPtrs {
+    float* p[5];   // means, log-scales, quaternions, opacity logits, SH
+    float* m[5];
+    float* v[5];
+    bool vec;      // every array 16-byte aligned
+};
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_bwd_adam(CamDev cam, int64_t n, const float* __restrict__ means,
+                                                  const float* __restrict__ log_scales,
+                                                  const float* __restrict__ quats, const float* __restrict__ logits,
+                                                  const float* __restrict__ sh, const int32_t* __restrict__ slot_of,
+                                                  const float4* __restrict__ g2s, const float* __restrict__ grad2d,
+                                                  AdamPtrs pw, gsd::AdamArgs a)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    constexpr int W = 3 * K;    // SH values per Gaussian
+    constexpr int RS = W + 1;   // LDS row of a staged SH row (odd stride: per-lane rows without bank conflicts)
+    constexpr int RT = K + 3;   // LDS row of the SH partial factors: Y[0..K-1], dL/drgb[0..2]
+    __shared__ float shs[4][64 * RS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t w0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
+    if (w0 >= n) return;
+    const int mw = (int)(n - w0 < 64 ? n - w0 : 64);   // Gaussians of this wavefront
+    const int64_t i = w0 + lane;
+    const bool live = lane < mw;
+    float* S = shs[wave];
+    {
+        const float* src = sh + w0 * W;
+        for (int q = lane; q < mw * W; q += 64) S[(q / W) * RS + q % W] = src[q];
+    }
+    gsd::wave_sync();
+    float geo[11], Y[16], grm[3];
+#pragma unroll
+    for (int k = 0; k < 11; ++k) geo[k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) Y[k] = 0.0f;
+    grm[0] = grm[1] = grm[2] = 0.0f;
+    const int32_t s = live ? slot_of[i] : -1;
+    if (s >= 0) {
+        const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[s].w);
+        proj_bwd_one<DEG>(cam, i, fl, grad2d + 9 * (int64_t)s, means, log_scales, quats, logits, S + lane * RS, geo,
+                          Y, grm);
+    }
+    gsd::wave_sync();   // every lane has read its staged row
+    float* Tf = S;
+#pragma unroll
+    for (int k = 0; k < K; ++k) Tf[lane * RT + k] = Y[k];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) Tf[lane * RT + K + c] = grm[c];
+    gsd::wave_sync();
+    if (live) {
+        auto upd = [&](int q, int64_t k, float g) {
+            float pp = pw.p[q][k], mm = pw.m[q][k], vv = pw.v[q][k];
+            gsd::adam_one(g, pp, mm, vv, a);
+            pw.p[q][k] = pp;
+            pw.m[q][k] = mm;
+            pw.v[q][k] = vv;
+        };
+#pragma unroll
+        for (int c = 0; c < 3; ++c) upd(0, 3 * i + c, geo[c]);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) upd(1, 3 * i + c, geo[3 + c]);
+        if (pw.vec) {
+            float4 pp = reinterpret_cast<const float4*>(pw.p[2])[i];
+            float4 mm = reinterpret_cast<const float4*>(pw.m[2])[i];
+            float4 vv = reinterpret_cast<const float4*>(pw.v[2])[i];
+            gsd::adam_one(geo[6], pp.x, mm.x, vv.x, a);
+            gsd::adam_one(geo[7], pp.y, mm.y, vv.y, a);
+            gsd::adam_one(geo[8], pp.z, mm.z, vv.z, a);
+            gsd::adam_one(geo[9], pp.w, mm.w, vv.w, a);
+            reinterpret_cast<float4*>(pw.p[2])[i] = pp;
+            reinterpret_cast<float4*>(pw.m[2])[i] = mm;
+            reinterpret_cast<float4*>(pw.v[2])[i] = vv;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) upd(2, 4 * i + c, geo[6 + c]);
+        }
+        upd(3, i, geo[10]);
+    }
+    // SH values [w0 W, (w0 + mw) W) of the wavefront
+    const int nv = mw * W;
+    float* P = pw.p[4] + w0 * W;
+    float* M = pw.m[4] + w0 * W;
+    float* V = pw.v[4] + w0 * W;
+    auto shg = [&](int q) {   // partial of value q of the wavefront's rows
+        const int gl = q / W, r = q - gl * W;
+        const int k = r / 3, c = r - 3 * k;
+        return Tf[gl * RT + k] * Tf[gl * RT + K + c];
+    };
+    auto one = [&](int q) {
+        float pp = P[q], mm = M[q], vv = V[q];
+        gsd::adam_one(shg(q), pp, mm, vv, a);
+        P[q] = pp;
+        M[q] = mm;
+        V[q] = vv;
+    };
+    if (!pw.vec) {
+        for (int q = lane; q < nv; q += 64) one(q);
+        return;
+    }
+    for (int q = 4 * lane; q + 3 < nv; q += 256) {
+        float4 pp = *reinterpret_cast<const float4*>(P + q);
+        float4 mm = *reinterpret_cast<const float4*>(M + q);
+        float4 vv = *reinterpret_cast<const float4*>(V + q);
+        gsd::adam_one(shg(q), pp.x, mm.x, vv.x, a);
+        gsd::adam_one(shg(q + 1), pp.y, mm.y, vv.y, a);
+        gsd::adam_one(shg(q + 2), pp.z, mm.z, vv.z, a);
+        gsd::adam_one(shg(q + 3), pp.w, mm.w, vv.w, a);
+        *reinterpret_cast<float4*>(P + q) = pp;
+        *reinterpret_cast<float4*>(M + q) = mm;
+        *reinterpret_cast<float4*>(V + q) = vv;
+    }
+    const int q0 = nv & ~3;
+    if (lane < nv - q0) one(q0 + lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,6 +639,42 @@ gs_status launch_project_write(gs_ctx* ctx, const gs_camera* cam, const gs_param
         }
 #undef GS_PW
     }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_bwd_adam(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
+                          const float* grad2d, const gs_param_ptrs* pr, const gs_param_ptrs* m, const gs_param_ptrs* v,
+                          int32_t step, float lr, float b1, float b2, float eps)
+{
+    const CamDev cd = make_cam(cam);
+    const int64_t n = p->n;
+    if (n <= 0) return GS_OK;
+    AdamPtrs pw;
+    const gs_param_ptrs* src[3] = {pr, m, v};
+    float** dst[3] = {pw.p, pw.m, pw.v};
+    uintptr_t bits = 0;
+    for (int t = 0; t < 3; ++t) {
+        dst[t][0] = src[t]->means;
+        dst[t][1] = src[t]->log_scales;
+        dst[t][2] = src[t]->quats;
+        dst[t][3] = src[t]->opacity_logits;
+        dst[t][4] = src[t]->sh;
+        for (int q = 0; q < 5; ++q) bits |= (uintptr_t)dst[t][q];
+    }
+    pw.vec = (bits & 15u) == 0;
+    const gsd::AdamArgs a = gsd::adam_args(step, lr, b1, b2, eps);
+    GsTimerScope ts(ctx, "bwd_adam");
+    const dim3 grid((unsigned)ceil_div(n, 256));
+#define GS_BA(D) hipLaunchKernelGGL(k_bwd_adam<D>, grid, dim3(256), 0, ctx->stream, cd, n, p->means, p->log_scales, \
+                                    p->quats, p->opacity_logits, p->sh, proj->slot_of, proj->g2, grad2d, pw, a)
+    switch (p->sh_degree) {
+    case 0: GS_BA(0); break;
+    case 1: GS_BA(1); break;
+    case 2: GS_BA(2); break;
+    default: GS_BA(3); break;
+    }
+#undef GS_BA
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -180,7 +180,7 @@ MIB = 1 << 20
 
 def make_workload(name: str, seed: int | None = None, n: int | None = None,
                   width: int | None = None, height: int | None = None,
-                  posed: bool = False) -> Workload:
+                  posed: bool = False, sh_degree: int | None = None) -> Workload:
     """Workloads by name, with optional size overrides (parity tests shrink
     them while keeping the generator and its structure):
 
@@ -190,6 +190,8 @@ def make_workload(name: str, seed: int | None = None, n: int | None = None,
       c4_plane5k   6M ground plane + 8 clusters, SH3, 5000x3300, 384 MiB leaves
       c5_plane16k  6M same generator, 16000x10560, 384 MiB leaves, one Adam step
       c5_plane16k_12m  12M, same
+
+    sh_degree overrides the SH degree of the box scenes (c1_small, c2_hd).
     """
     table = {
         "c1_small": dict(seed=1, n=2000, w=128, h=128, loss="l1", budgets=()),
@@ -210,11 +212,14 @@ def make_workload(name: str, seed: int | None = None, n: int | None = None,
     w = spec["w"] if width is None else width
     h = spec["h"] if height is None else height
     rng = np.random.default_rng(seed)
+    if sh_degree is not None and name not in ("c1_small", "c2_hd"):
+        raise ValueError(f"sh_degree override applies to c1_small and c2_hd only, not {name!r}")
     if name == "c1_small":
-        scene = uniform_box_scene(rng, n, half=1.0, depth=4.0, log_mu=-3.0, log_sd=0.5, deg=0)
+        scene = uniform_box_scene(rng, n, half=1.0, depth=4.0, log_mu=-3.0, log_sd=0.5,
+                                  deg=0 if sh_degree is None else sh_degree)
     elif name == "c2_hd":
-        scene = uniform_box_scene(rng, n, half=5.0, depth=20.0, log_mu=-4.0, log_sd=0.7, deg=3,
-                                  sh0_uniform=False)
+        scene = uniform_box_scene(rng, n, half=5.0, depth=20.0, log_mu=-4.0, log_sd=0.7,
+                                  deg=3 if sh_degree is None else sh_degree, sh0_uniform=False)
     elif name == "c3_gmm4k":
         scene = gmm_scene(rng, n)
     else:

@@ -313,10 +313,11 @@ typedef struct {
     gs_param_ptrs* params_rw;    /* required when adam_step >= 1 (in/out)      */
     gs_param_ptrs* adam_m;
     gs_param_ptrs* adam_v;
-    int64_t adam_chunk;          /* with Adam and no grad3d_out: candidate     */
-                                 /* slots per projection-backward + Adam chunk */
-                                 /* (0: 524288), which bounds the compact      */
-                                 /* gradient buffer to adam_chunk x F floats   */
+    int64_t adam_chunk;          /* with Adam and no grad3d_out: 0 fuses the   */
+                                 /* projection backward with the update (no    */
+                                 /* gradient array); > 0 runs them as two      */
+                                 /* kernels per chunk of that many candidate   */
+                                 /* slots (gradient buffer adam_chunk x F)     */
 } gs_view_opts;
 
 typedef struct {
@@ -331,9 +332,10 @@ typedef struct {
  * gs_project_bwd -> optional gs_adam_step; the 2D gradients of all leaves are
  * summed in one buffer before the single projection backward (BoundedGS
  * page "01", Fig. 3, Fig. 5 conclusion).  With Adam and no grad3d_out the
- * projection backward and the update run chunk by chunk of candidate slots
- * (same result, a smaller gradient buffer).  target: device [3][H][W].
- * Synchronises. */
+ * projection backward and the update run as one fused pass over the
+ * Gaussians (adam_chunk 0), or chunk by chunk of candidate slots; both give
+ * the result of gs_project_bwd followed by gs_adam_step.  target: device
+ * [3][H][W].  Synchronises. */
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result);
 

@@ -169,13 +169,14 @@ def test_adam_step_matches_oracle(ctx):
         assert rel_l2(got - p0, p - p0) <= 1e-3, name
 
 
-@pytest.mark.parametrize("chunk", [700, 0])
-def test_train_view_chunked_update_matches_oracle(ctx, chunk):
-    """gs_train_view with Adam and no dense gradient output runs the projection
-    backward and the update chunk by chunk of candidate slots (700: several
-    chunks and a ragged last one; 0: the default, one chunk here)."""
+@pytest.mark.parametrize("chunk,deg", [(700, 3), (0, 3), (0, 1), (0, 0)])
+def test_train_view_chunked_update_matches_oracle(ctx, chunk, deg):
+    """gs_train_view with Adam and no dense gradient output: chunk 0 (the
+    default) fuses the projection backward with the update over all
+    Gaussians; chunk 700 runs them chunk by chunk of candidate slots (several
+    chunks and a ragged last one).  N = 5000 leaves a ragged last wavefront."""
     import torch
-    w = scenes.make_workload("c2_hd", n=5000, width=200, height=150, posed=True, seed=108)
+    w = scenes.make_workload("c2_hd", n=5000, width=200, height=150, posed=True, seed=108, sh_degree=deg)
     o = oracle.train_view(w.camera, w.scene, w.target)
     assert o["n_cand"] > 2 * 700
     rng = np.random.default_rng(1)
@@ -190,7 +191,7 @@ def test_train_view_chunked_update_matches_oracle(ctx, chunk):
     target = torch.from_numpy(w.target).to(ctx.device)
     r = B.gs_train_view(ctx, w.camera, ds, target, adam=dict(step=3, params=ds, m=m, v=v, chunk=chunk))
     assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
-    groups = grad3d_groups(o["grad3d"], 3)
+    groups = grad3d_groups(o["grad3d"], deg)
     for k, (t, name) in enumerate(zip(ds.tensors(), ["means", "log_scales", "quats", "logits", "sh"])):
         p0 = w.scene.arrays()[k].astype(np.float64)
         p, mm, vv = oracle.adam(groups[name].reshape(p0.shape), p0, m0[k].astype(np.float32),
