@@ -53,12 +53,15 @@ __device__ __forceinline__ float exp_cw_core(float x)
     return __builtin_ldexpf(p, (int)k);
 }
 
+// exp_cw_core of x inside [-87, 88.7]; 0 below, inf above, NaN kept.  The
+// special cases are selects, not branches, so that loads around a call are
+// not held back by control flow.
 __device__ __forceinline__ float exp_cw(float x)
 {
-    if (x < -87.0f) return 0.0f;
-    if (x > 88.7f) return __builtin_inff();
-    if (x != x) return x;
-    return exp_cw_core(x);
+    float r = exp_cw_core(__builtin_amdgcn_fmed3f(x, -87.0f, 88.7f));
+    r = x < -87.0f ? 0.0f : r;
+    r = x > 88.7f ? __builtin_inff() : r;
+    return x != x ? x : r;
 }
 
 // compositing constants
@@ -122,6 +125,44 @@ __device__ __forceinline__ void sh_basis_grad(int deg, float x, float y, float z
     D[13][0] = c3c * (4.0f * zz - 3.0f * xx - yy); D[13][1] = -2.0f * c3c * x * y; D[13][2] = 8.0f * c3c * x * z;
     D[14][0] = 2.0f * c3e * x * z; D[14][1] = -2.0f * c3e * y * z; D[14][2] = c3e * (xx - yy);
     D[15][0] = 3.0f * c3a * (xx - yy); D[15][1] = -6.0f * c3a * x * y; D[15][2] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging of the rows of W floats of a wavefront's mw (<= 64) consecutive
+// items (src: the first item's row) into rows of stride RS.  With `aligned`
+// (src 16-byte aligned) every lane issues all of its float4 loads before the
+// first LDS store, so the loads are in flight together.
+template <int W, int RS>
+__device__ __forceinline__ void stage_rows(float* S, const float* __restrict__ src, int mw, int lane, bool aligned)
+{
+    const int nv = mw * W;
+    if (!aligned) {
+        for (int q = lane; q < nv; q += 64) S[(q / W) * RS + q % W] = src[q];
+        return;
+    }
+    constexpr int NQ = (16 * W + 63) / 64;   // float4s per lane
+    float t[NQ][4];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        const int q = 4 * (lane + 64 * r);
+        if (q + 3 < nv) {
+            const float4 v = *reinterpret_cast<const float4*>(src + q);
+            t[r][0] = v.x;
+            t[r][1] = v.y;
+            t[r][2] = v.z;
+            t[r][3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[r][e] = q + e < nv ? src[q + e] : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        const int q = 4 * (lane + 64 * r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (q + e < nv) S[((q + e) / W) * RS + (q + e) % W] = t[r][e];
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -43,15 +43,34 @@ struct Proj2D {
 
 __device__ __forceinline__ float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Geometry of Gaussian i in the specified f32 operation order.
-__device__ __forceinline__ Proj2D project_geom(const CamDev& cam, const float* __restrict__ means,
-                                               const float* __restrict__ log_scales,
-                                               const float* __restrict__ quats, int64_t i)
+// The inputs of one Gaussian's projection, loaded together (no load waits on
+// an earlier decision).
+struct GaussIn {
+    float mx, my, mz, l0, l1, l2;
+    float4 q;
+};
+
+__device__ __forceinline__ GaussIn load_gauss(const float* __restrict__ means, const float* __restrict__ log_scales,
+                                              const float* __restrict__ quats, int64_t i)
+{
+    GaussIn g;
+    g.mx = means[3 * i];
+    g.my = means[3 * i + 1];
+    g.mz = means[3 * i + 2];
+    g.l0 = log_scales[3 * i];
+    g.l1 = log_scales[3 * i + 1];
+    g.l2 = log_scales[3 * i + 2];
+    g.q = *reinterpret_cast<const float4*>(quats + 4 * i);
+    return g;
+}
+
+// Geometry of one Gaussian in the specified f32 operation order.
+__device__ __forceinline__ Proj2D project_geom(const CamDev& cam, const GaussIn& gi)
 {
     Proj2D o;
     o.ok = true;
     o.flags = 0;
-    const float mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
+    const float mx = gi.mx, my = gi.my, mz = gi.mz;
     const float px = ((cam.R[0] * mx + cam.R[1] * my) + cam.R[2] * mz) + cam.t[0];
     const float py = ((cam.R[3] * mx + cam.R[4] * my) + cam.R[5] * mz) + cam.t[1];
     const float pz = ((cam.R[6] * mx + cam.R[7] * my) + cam.R[8] * mz) + cam.t[2];
@@ -61,10 +80,10 @@ __device__ __forceinline__ Proj2D project_geom(const CamDev& cam, const float* _
     o.vz = mz - cam.cc[2];
     if (!(pz > cam.near_z)) { o.ok = false; return o; }
 
-    const float s0 = gsd::exp_cw(log_scales[3 * i]);
-    const float s1 = gsd::exp_cw(log_scales[3 * i + 1]);
-    const float s2 = gsd::exp_cw(log_scales[3 * i + 2]);
-    const float4 q = *reinterpret_cast<const float4*>(quats + 4 * i);
+    const float s0 = gsd::exp_cw(gi.l0);
+    const float s1 = gsd::exp_cw(gi.l1);
+    const float s2 = gsd::exp_cw(gi.l2);
+    const float4 q = gi.q;
     const float qn = sqrtf(((q.x * q.x + q.y * q.y) + q.z * q.z) + q.w * q.w);
     const float w = q.x / qn, x = q.y / qn, y = q.z / qn, z = q.w / qn;
     float Rq[3][3];
@@ -144,7 +163,7 @@ __global__ __launch_bounds__(256) void k_project_flags(CamDev cam, int64_t n, co
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    flag[i] = project_geom(cam, means, log_scales, quats, i).ok ? 1u : 0u;
+    flag[i] = project_geom(cam, load_gauss(means, log_scales, quats, i)).ok ? 1u : 0u;
 }
 
 // Compact state of every candidate.  A wavefront covers 64 consecutive
@@ -156,7 +175,7 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, co
                                                        const float* __restrict__ log_scales,
                                                        const float* __restrict__ quats,
                                                        const float* __restrict__ logits,
-                                                       const float* __restrict__ sh,
+                                                       const float* __restrict__ sh, bool sh_aligned,
                                                        const uint32_t* __restrict__ flag,
                                                        const uint32_t* __restrict__ slot, uint32_t* __restrict__ ids,
                                                        int4* __restrict__ rect, float4* __restrict__ g0,
@@ -170,22 +189,28 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, co
     const int64_t w0 = (int64_t)blockIdx.x * blockDim.x + wave * 64;
     const int64_t i = w0 + lane;
     float* S = shs[wave];
-    {
-        const int64_t lim = (n - w0) * 3 * K;   // floats of this wave's rows that exist
-        const float* src = sh + w0 * 3 * K;
-        for (int q = lane; q < 64 * 3 * K; q += 64)
-            if (q < lim) S[(q / (3 * K)) * RS + q % (3 * K)] = src[q];
+    // every input of the lane's Gaussian is requested before the SH rows are
+    // staged, so that all loads of the wavefront are in flight together
+    const bool live = i < n;
+    GaussIn gi{};
+    uint32_t cand = 0, j = 0;
+    float logit = 0.0f;
+    if (live) {
+        gi = load_gauss(means, log_scales, quats, i);
+        cand = flag[i];
+        j = slot[i];
+        logit = logits[i];
     }
+    if (w0 < n) gsd::stage_rows<3 * K, RS>(S, sh + w0 * 3 * K, (int)(n - w0 < 64 ? n - w0 : 64), lane, sh_aligned);
     gsd::wave_sync();
-    if (i >= n) return;
-    if (!flag[i]) {
+    if (!live) return;
+    if (!cand) {
         slot_of[i] = -1;
         return;
     }
-    const uint32_t j = slot[i];
     slot_of[i] = (int32_t)j;
-    const Proj2D p = project_geom(cam, means, log_scales, quats, i);
-    const float o = 1.0f / (1.0f + gsd::exp_cw(-logits[i]));
+    const Proj2D p = project_geom(cam, gi);
+    const float o = 1.0f / (1.0f + gsd::exp_cw(-logit));
     const float vn = sqrtf((p.vx * p.vx + p.vy * p.vy) + p.vz * p.vz);
     const float dx = p.vx / vn, dy = p.vy / vn, dz = p.vz / vn;
     float Y[16];
@@ -221,22 +246,21 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, co
 // = the SH basis at the view direction and grm[3] = dL/drgb, zero where the
 // forward clamped the channel; dL/dsh[k][c] = Y[k] grm[c].
 template <int DEG>
-__device__ __forceinline__ void proj_bwd_one(const CamDev& cam, int64_t i, uint32_t fl, const float* g,
-                                             const float* __restrict__ means, const float* __restrict__ log_scales,
-                                             const float* __restrict__ quats, const float* __restrict__ logits,
-                                             const float* shi, float* geo, float* Y, float* grm)
+__device__ __forceinline__ void proj_bwd_one(const CamDev& cam, const GaussIn& gi, float logit, uint32_t fl,
+                                             const float* g, const float* shi, float* geo, float* Y, float* grm)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     // forward recomputation
-    const float mu[3] = {means[3 * i], means[3 * i + 1], means[3 * i + 2]};
+    const float mu[3] = {gi.mx, gi.my, gi.mz};
     float p[3];
 #pragma unroll
     for (int r = 0; r < 3; ++r) p[r] = cam.R[3 * r] * mu[0] + cam.R[3 * r + 1] * mu[1] + cam.R[3 * r + 2] * mu[2] + cam.t[r];
     const float pz = p[2];
     float s[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) s[k] = gsd::exp_cw(log_scales[3 * i + k]);
-    const float4 q = *reinterpret_cast<const float4*>(quats + 4 * i);
+    s[0] = gsd::exp_cw(gi.l0);
+    s[1] = gsd::exp_cw(gi.l1);
+    s[2] = gsd::exp_cw(gi.l2);
+    const float4 q = gi.q;
     const float qn = sqrtf(q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w);
     const float w = q.x / qn, x = q.y / qn, y = q.z / qn, z = q.w / qn;
     float Rq[3][3];
@@ -272,7 +296,7 @@ __device__ __forceinline__ void proj_bwd_one(const CamDev& cam, int64_t i, uint3
     const float b = U[0][0] * T[1][0] + U[0][1] * T[1][1] + U[0][2] * T[1][2];
     const float c = U[1][0] * T[1][0] + U[1][1] * T[1][1] + U[1][2] * T[1][2] + 0.3f;
     const float det = a * c - b * b;
-    const float o = 1.0f / (1.0f + gsd::exp_cw(-logits[i]));
+    const float o = 1.0f / (1.0f + gsd::exp_cw(-logit));
     const float vx = mu[0] - cam.cc[0], vy = mu[1] - cam.cc[1], vz = mu[2] - cam.cc[2];
     const float vn = sqrtf(vx * vx + vy * vy + vz * vz);
     const float d[3] = {vx / vn, vy / vn, vz / vn};
@@ -411,8 +435,8 @@ __global__ __launch_bounds__(256) void k_project_bwd(CamDev cam, int64_t s0, int
         const int64_t i = ids[j];
         const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[j].w);
         float Y[16], grm[3];
-        proj_bwd_one<DEG>(cam, i, fl, grad2d + 9 * j, means, log_scales, quats, logits, sh + (int64_t)3 * K * i, out,
-                          Y, grm);
+        proj_bwd_one<DEG>(cam, load_gauss(means, log_scales, quats, i), logits[i], fl, grad2d + 9 * j,
+                          sh + (int64_t)3 * K * i, out, Y, grm);
 #pragma unroll
         for (int k = 0; k < K; ++k)
 #pragma unroll
@@ -456,7 +480,8 @@ template <int DEG>
 __global__ __launch_bounds__(256) void k_bwd_adam(CamDev cam, int64_t n, const float* __restrict__ means,
                                                   const float* __restrict__ log_scales,
                                                   const float* __restrict__ quats, const float* __restrict__ logits,
-                                                  const float* __restrict__ sh, const int32_t* __restrict__ slot_of,
+                                                  const float* __restrict__ sh, bool sh_aligned,
+                                                  const int32_t* __restrict__ slot_of,
                                                   const float4* __restrict__ g2s, const float* __restrict__ grad2d,
                                                   AdamPtrs pw, gsd::AdamArgs a)
 {
@@ -472,10 +497,16 @@ __global__ __launch_bounds__(256) void k_bwd_adam(CamDev cam, int64_t n, const f
     const int64_t i = w0 + lane;
     const bool live = lane < mw;
     float* S = shs[wave];
-    {
-        const float* src = sh + w0 * W;
-        for (int q = lane; q < mw * W; q += 64) S[(q / W) * RS + q % W] = src[q];
+    // the lane's slot and projection inputs are requested before the SH rows
+    // are staged, so that these loads are in flight together
+    GaussIn gi{};
+    float logit = 0.0f;
+    const int32_t s = live ? slot_of[i] : -1;
+    if (live) {
+        gi = load_gauss(means, log_scales, quats, i);
+        logit = logits[i];
     }
+    gsd::stage_rows<W, RS>(S, sh + w0 * W, mw, lane, sh_aligned);
     gsd::wave_sync();
     float geo[11], Y[16], grm[3];
 #pragma unroll
@@ -483,11 +514,9 @@ __global__ __launch_bounds__(256) void k_bwd_adam(CamDev cam, int64_t n, const f
 #pragma unroll
     for (int k = 0; k < 16; ++k) Y[k] = 0.0f;
     grm[0] = grm[1] = grm[2] = 0.0f;
-    const int32_t s = live ? slot_of[i] : -1;
     if (s >= 0) {
         const uint32_t fl = __builtin_bit_cast(uint32_t, g2s[s].w);
-        proj_bwd_one<DEG>(cam, i, fl, grad2d + 9 * (int64_t)s, means, log_scales, quats, logits, S + lane * RS, geo,
-                          Y, grm);
+        proj_bwd_one<DEG>(cam, gi, logit, fl, grad2d + 9 * (int64_t)s, S + lane * RS, geo, Y, grm);
     }
     gsd::wave_sync();   // every lane has read its staged row
     float* Tf = S;
@@ -497,33 +526,27 @@ __global__ __launch_bounds__(256) void k_bwd_adam(CamDev cam, int64_t n, const f
     for (int c = 0; c < 3; ++c) Tf[lane * RT + K + c] = grm[c];
     gsd::wave_sync();
     if (live) {
-        auto upd = [&](int q, int64_t k, float g) {
-            float pp = pw.p[q][k], mm = pw.m[q][k], vv = pw.v[q][k];
-            gsd::adam_one(g, pp, mm, vv, a);
-            pw.p[q][k] = pp;
-            pw.m[q][k] = mm;
-            pw.v[q][k] = vv;
-        };
+        // the 11 geometric values: all loads, then the updates, then the stores
+        constexpr int off[11] = {0, 1, 2, 0, 1, 2, 0, 1, 2, 3, 0};
+        constexpr int grp[11] = {0, 0, 0, 1, 1, 1, 2, 2, 2, 2, 3};
+        constexpr int wid[4] = {3, 3, 4, 1};
+        float pp[11], mm[11], vv[11];
 #pragma unroll
-        for (int c = 0; c < 3; ++c) upd(0, 3 * i + c, geo[c]);
-#pragma unroll
-        for (int c = 0; c < 3; ++c) upd(1, 3 * i + c, geo[3 + c]);
-        if (pw.vec) {
-            float4 pp = reinterpret_cast<const float4*>(pw.p[2])[i];
-            float4 mm = reinterpret_cast<const float4*>(pw.m[2])[i];
-            float4 vv = reinterpret_cast<const float4*>(pw.v[2])[i];
-            gsd::adam_one(geo[6], pp.x, mm.x, vv.x, a);
-            gsd::adam_one(geo[7], pp.y, mm.y, vv.y, a);
-            gsd::adam_one(geo[8], pp.z, mm.z, vv.z, a);
-            gsd::adam_one(geo[9], pp.w, mm.w, vv.w, a);
-            reinterpret_cast<float4*>(pw.p[2])[i] = pp;
-            reinterpret_cast<float4*>(pw.m[2])[i] = mm;
-            reinterpret_cast<float4*>(pw.v[2])[i] = vv;
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) upd(2, 4 * i + c, geo[6 + c]);
+        for (int k = 0; k < 11; ++k) {
+            const int64_t e = wid[grp[k]] * i + off[k];
+            pp[k] = pw.p[grp[k]][e];
+            mm[k] = pw.m[grp[k]][e];
+            vv[k] = pw.v[grp[k]][e];
         }
-        upd(3, i, geo[10]);
+#pragma unroll
+        for (int k = 0; k < 11; ++k) gsd::adam_one(geo[k], pp[k], mm[k], vv[k], a);
+#pragma unroll
+        for (int k = 0; k < 11; ++k) {
+            const int64_t e = wid[grp[k]] * i + off[k];
+            pw.p[grp[k]][e] = pp[k];
+            pw.m[grp[k]][e] = mm[k];
+            pw.v[grp[k]][e] = vv[k];
+        }
     }
     // SH values [w0 W, (w0 + mw) W) of the wavefront
     const int nv = mw * W;
@@ -535,31 +558,56 @@ __global__ __launch_bounds__(256) void k_bwd_adam(CamDev cam, int64_t n, const f
         const int k = r / 3, c = r - 3 * k;
         return Tf[gl * RT + k] * Tf[gl * RT + K + c];
     };
-    auto one = [&](int q) {
-        float pp = P[q], mm = M[q], vv = V[q];
-        gsd::adam_one(shg(q), pp, mm, vv, a);
-        P[q] = pp;
-        M[q] = mm;
-        V[q] = vv;
-    };
     if (!pw.vec) {
-        for (int q = lane; q < nv; q += 64) one(q);
+        for (int q = lane; q < nv; q += 64) {
+            float p1 = P[q], m1 = M[q], v1 = V[q];
+            gsd::adam_one(shg(q), p1, m1, v1, a);
+            P[q] = p1;
+            M[q] = m1;
+            V[q] = v1;
+        }
         return;
     }
-    for (int q = 4 * lane; q + 3 < nv; q += 256) {
-        float4 pp = *reinterpret_cast<const float4*>(P + q);
-        float4 mm = *reinterpret_cast<const float4*>(M + q);
-        float4 vv = *reinterpret_cast<const float4*>(V + q);
-        gsd::adam_one(shg(q), pp.x, mm.x, vv.x, a);
-        gsd::adam_one(shg(q + 1), pp.y, mm.y, vv.y, a);
-        gsd::adam_one(shg(q + 2), pp.z, mm.z, vv.z, a);
-        gsd::adam_one(shg(q + 3), pp.w, mm.w, vv.w, a);
-        *reinterpret_cast<float4*>(P + q) = pp;
-        *reinterpret_cast<float4*>(M + q) = mm;
-        *reinterpret_cast<float4*>(V + q) = vv;
+    // float4 q4 = lane + 64 r of the rows (16-byte aligned: 64 rows start on a
+    // 256-byte boundary), B of them loaded before any is updated
+    constexpr int NQ = (16 * W + 63) / 64;
+    constexpr int B = 4;
+#pragma unroll
+    for (int r0 = 0; r0 < NQ; r0 += B) {
+        float4 p4[B], m4[B], v4[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int q = 4 * (lane + 64 * (r0 + b));
+            if (r0 + b < NQ && q + 3 < nv) {
+                p4[b] = *reinterpret_cast<const float4*>(P + q);
+                m4[b] = *reinterpret_cast<const float4*>(M + q);
+                v4[b] = *reinterpret_cast<const float4*>(V + q);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int q = 4 * (lane + 64 * (r0 + b));
+            if (r0 + b < NQ && q + 3 < nv) {
+                gsd::adam_one(shg(q), p4[b].x, m4[b].x, v4[b].x, a);
+                gsd::adam_one(shg(q + 1), p4[b].y, m4[b].y, v4[b].y, a);
+                gsd::adam_one(shg(q + 2), p4[b].z, m4[b].z, v4[b].z, a);
+                gsd::adam_one(shg(q + 3), p4[b].w, m4[b].w, v4[b].w, a);
+                *reinterpret_cast<float4*>(P + q) = p4[b];
+                *reinterpret_cast<float4*>(M + q) = m4[b];
+                *reinterpret_cast<float4*>(V + q) = v4[b];
+            }
+        }
     }
+    // a last partial float4 (rows of a ragged last wavefront)
     const int q0 = nv & ~3;
-    if (lane < nv - q0) one(q0 + lane);
+    if (lane < nv - q0) {
+        const int q = q0 + lane;
+        float p1 = P[q], m1 = M[q], v1 = V[q];
+        gsd::adam_one(shg(q), p1, m1, v1, a);
+        P[q] = p1;
+        M[q] = m1;
+        V[q] = v1;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -628,8 +676,9 @@ gs_status launch_project_write(gs_ctx* ctx, const gs_camera* cam, const gs_param
     if (n > 0) {
         GsTimerScope ts(ctx, "project_write");
         const dim3 grid((unsigned)ceil_div(n, 256));
+        const bool sh_aligned = ((uintptr_t)p->sh & 15u) == 0;
 #define GS_PW(D) hipLaunchKernelGGL(k_project_write<D>, grid, dim3(256), 0, ctx->stream, cd, n, p->means, \
-                                    p->log_scales, p->quats, p->opacity_logits, p->sh, flag, slot, proj->ids, \
+                                    p->log_scales, p->quats, p->opacity_logits, p->sh, sh_aligned, flag, slot, proj->ids, \
                                     proj->rect, proj->g0, proj->g1, proj->g2, proj->slot_of)
         switch (p->sh_degree) {
         case 0: GS_PW(0); break;
@@ -666,8 +715,10 @@ gs_status launch_bwd_adam(gs_ctx* ctx, const gs_camera* cam, const gs_params* p,
     const gsd::AdamArgs a = gsd::adam_args(step, lr, b1, b2, eps);
     GsTimerScope ts(ctx, "bwd_adam");
     const dim3 grid((unsigned)ceil_div(n, 256));
+    const bool sh_aligned = ((uintptr_t)p->sh & 15u) == 0;
 #define GS_BA(D) hipLaunchKernelGGL(k_bwd_adam<D>, grid, dim3(256), 0, ctx->stream, cd, n, p->means, p->log_scales, \
-                                    p->quats, p->opacity_logits, p->sh, proj->slot_of, proj->g2, grad2d, pw, a)
+                                    p->quats, p->opacity_logits, p->sh, sh_aligned, proj->slot_of, proj->g2, grad2d, \
+                                    pw, a)
     switch (p->sh_degree) {
     case 0: GS_BA(0); break;
     case 1: GS_BA(1); break;
