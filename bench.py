@@ -32,12 +32,15 @@ PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 #     clamp and threshold 4                                            = 27
 #   an included pair adds, forward: T' 2, stop test 1, weight 1,
 #     colour 3 fma, bookkeeping 1                                      -> 35
-#   backward: T recovery 3, colour partials 4, dL/dalpha 12, colour
-#     behind 3, opacity and exponent partials 9, conic and mean partials 7
-#                                                                      -> 65
+#   backward: T recovery 3 (1 - alpha, reciprocal, product), weight 1,
+#     colour dot dL/dout 3, dL/dalpha 2, colour behind 1, colour partials
+#     3, clamp decision 1, opacity partial 1, -dL/dpower 1, the five
+#     power moments q dx, q dy, q dx^2, q dx dy, q dy^2 accumulated 7
+#     (the mean and conic partials follow from the moments once per
+#     entry, not per pixel)                                            -> 50
 OPS_EXAMINED = 27
 OPS_INCLUDED_FWD = 35
-OPS_INCLUDED_BWD = 65
+OPS_INCLUDED_BWD = 50
 
 
 def log(*a):

@@ -331,7 +331,7 @@ __device__ __forceinline__ bool fine_item(const uint64_t* __restrict__ soff, con
     return true;
 }
 
-template <bool WRITE>
+template <bool WRITE, bool BUF>
 __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int THL, int SW, int n_super,
                                               const uint64_t* __restrict__ soff, const uint32_t* __restrict__ ioff,
                                               const uint32_t* __restrict__ item_sc,
@@ -348,12 +348,17 @@ __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int T
     const int gx0 = (((ltx0 >> kSuperShift) + it.sc % SW) << kSuperShift);
     const int gy0 = (((lty0 >> kSuperShift) + it.sc / SW) << kSuperShift) + 2 * wave;
     if (gy0 >= lty0 + THL || gy0 + 2 <= lty0) return;
+    (void)gx0;
     uint32_t* wp = pos + it.item * 64 + wave * 16;   // this wave's 16 tiles of the item
+    // BUF: the slot array as a raw buffer of n_values u32 (byte offsets are
+    // 32-bit: fewer than 2^30 entries), else plain stores
+    const __amdgpu_buffer_rsrc_t vbuf =
+        __builtin_amdgcn_make_buffer_rsrc(values, (short)0, (int)(uint32_t)(BUF ? n_values * 4u : 0u), 0x00020000);
+    // running position (write) or count (count pass) of each tile, uniform
     uint32_t cur[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) cur[q] = WRITE ? wp[q] : 0u;
+    for (int q = 0; q < 16; ++q) cur[q] = WRITE ? __builtin_amdgcn_readfirstlane(wp[q]) : 0u;
     const uint64_t b = it.b, e = it.e;
-    // this wave's tiles in the super-tile: columns 0-7, rows 2w and 2w + 1
     const uint32_t row0 = 2u * (uint32_t)wave;
     uint32_t sl_n = 0, key_n = 0;          // the next chunk's entry, loaded one chunk ahead
     if (b + lane < e) {
@@ -367,21 +372,31 @@ __global__ __launch_bounds__(256) void k_fine(int ltx0, int lty0, int TWL, int T
             sl_n = group[k + 64 + lane];
             key_n = gkey[k + 64 + lane];
         }
+        // the entry covers tile (c, r) of the super-tile iff x0 <= c < x1 and
+        // y0 <= r < y1: bit q of `bits` (q = 8 (r - row0) + c) marks the
+        // wave's tiles it covers, and one ballot per tile tests a bit
         const uint32_t x0 = lr & 7u, x1 = ((lr >> 3) & 7u) + 1u;
         const uint32_t y0 = (lr >> 6) & 7u, y1 = ((lr >> 9) & 7u) + 1u;
-        const bool r0 = ok && y0 <= row0 && row0 < y1, r1 = ok && y0 <= row0 + 1u && row0 + 1u < y1;
+        const uint32_t cols = (0xFFu >> (8u - x1)) & (0xFFu << x0);
+        const bool r0 = ok && y0 <= row0 && row0 < y1;
+        const bool r1 = ok && y0 <= row0 + 1u && row0 + 1u < y1;
+        const uint32_t bits = (r0 ? cols : 0u) | (r1 ? cols << 8 : 0u);
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const uint32_t c = (uint32_t)(q & 7);
-            // a rectangle clipped to the leaf covers no tile outside it
-            const bool cov = ((q >> 3) ? r1 : r0) && x0 <= c && c < x1;
+            const bool cov = (bits & (1u << q)) != 0u;
             const uint64_t m = gsd::ballot(cov);
-            if (m == 0) continue;
-            if (WRITE && cov) {
+            if (WRITE) {
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
                 const uint32_t p = cur[q] + below;
-                if (p < n_values) values[p] = sl;   // always true when the counts agree
+                if (BUF) {
+                    // lanes that do not cover the tile get an offset past the
+                    // buffer's end, and the hardware drops those stores (so
+                    // would it any position >= n_values)
+                    __builtin_amdgcn_raw_buffer_store_b32(sl, vbuf, (int)(cov ? p * 4u : 0xFFFFFFFFu), 0, 0);
+                } else if (cov && p < n_values) {
+                    values[p] = sl;   // always true when the counts agree
+                }
             }
             cur[q] += (uint32_t)__builtin_popcountll(m);
         }
@@ -608,12 +623,16 @@ gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
     const int TWL = leaf.tx1 - leaf.tx0, THL = leaf.ty1 - leaf.ty0, SW = super_cols(leaf);
     GsTimerScope ts(ctx, "fine");
     hipLaunchKernelGGL(k_fine_items, dim3(1), dim3(1024), 0, ctx->stream, soff, n_super, ioff, item_sc);
-    hipLaunchKernelGGL(k_fine<false>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                       SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
+    hipLaunchKernelGGL((k_fine<false, false>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0,
+                       TWL, THL, SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
     hipLaunchKernelGGL(k_fine_scan, dim3((unsigned)ceil_div((int64_t)n_super * 64, 256)), dim3(256), 0, ctx->stream,
                        leaf.tx0, leaf.ty0, TWL, THL, SW, n_super, ioff, toff, pos);
-    hipLaunchKernelGGL(k_fine<true>, dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                       SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
+    if (n_values < (1ull << 30))
+        hipLaunchKernelGGL((k_fine<true, true>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
+                           SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
+    else
+        hipLaunchKernelGGL((k_fine<true, false>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
+                           SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

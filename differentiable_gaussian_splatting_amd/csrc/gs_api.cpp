@@ -710,9 +710,13 @@ fail:
 // ---------------------------------------------------------------------------
 // raster
 
-gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                        const float* target, double* loss_accum, float* image_out, uint64_t* stats,
-                        gs_raster** out)
+// gs_render_fwd with an optional caller-owned destination for the per-tile
+// L1 partials (l1_dst, 4 doubles per tile of the leaf): then the partials are
+// left there for the caller to sum once for several leaves, and loss_accum is
+// not touched.
+static gs_status render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                            const float* target, double* loss_accum, float* image_out, uint64_t* stats,
+                            double* l1_dst, gs_raster** out)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     gs_status st;
@@ -735,18 +739,27 @@ gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, 
     r->last = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * r->n_pix, GS_MEM_RASTER, &r->allocs);
     if (target) {
         r->sgn = (uint8_t*)gs_malloc(ctx, r->n_pix, GS_MEM_RASTER, &r->allocs);
-        r->l1_part = (double*)gs_malloc(ctx, sizeof(double) * 4 * bins->n_tiles, GS_MEM_RASTER, &r->allocs);
+        r->l1_part = l1_dst ? l1_dst
+                            : (double*)gs_malloc(ctx, sizeof(double) * 4 * bins->n_tiles, GS_MEM_RASTER, &r->allocs);
     }
     if (!r->tfinal || !r->last || (target && (!r->sgn || !r->l1_part))) {
         destroy_handle(ctx, r);
         return GS_ERR_OOM;
     }
-    if ((st = launch_raster_fwd(ctx, cam, proj, bins, r, target, image_out, loss_accum, stats)) != GS_OK) {
+    if ((st = launch_raster_fwd(ctx, cam, proj, bins, r, target, image_out, l1_dst ? nullptr : loss_accum,
+                                stats)) != GS_OK) {
         destroy_handle(ctx, r);
         return st;
     }
     *out = r;
     return GS_OK;
+}
+
+gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                        const float* target, double* loss_accum, float* image_out, uint64_t* stats,
+                        gs_raster** out)
+{
+    return render_fwd(ctx, cam, proj, bins, target, loss_accum, image_out, stats, nullptr, out);
 }
 
 gs_status gs_render_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
@@ -953,7 +966,13 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     float* dl_dimage = nullptr;
     double loss = 0.0;
     int64_t isect_total = 0;
-    if (!grad2d || !loss_dev) { st = GS_ERR_OOM; goto done; }
+    // L1: the per-tile partials of every leaf side by side, summed once
+    int64_t l1_n = 0, l1_off = 0;
+    for (const gs_leaf& L : leaves) l1_n += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
+    double* l1_view = opts->loss_kind == 0 && l1_n > 0
+                          ? (double*)gs_malloc(ctx, sizeof(double) * l1_n, GS_MEM_LOSS, &view)
+                          : nullptr;
+    if (!grad2d || !loss_dev || (opts->loss_kind == 0 && l1_n > 0 && !l1_view)) { st = GS_ERR_OOM; goto done; }
     if ((st = launch_fill_f32(ctx, grad2d, 0.0f, 9 * nc)) != GS_OK) goto done;
     if (hipMemsetAsync(loss_dev, 0, sizeof(double), ctx->stream) != hipSuccess) {
         st = gs_fail(ctx, GS_ERR_DEVICE, "memset failed");
@@ -972,7 +991,8 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
         isect_total += ni;
         if (opts->loss_kind == 0) {
-            st = gs_render_fwd(ctx, cam, proj, bins, target, loss_dev, image, nullptr, &ras);
+            st = render_fwd(ctx, cam, proj, bins, target, loss_dev, image, nullptr, l1_view + l1_off, &ras);
+            l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
             if (st == GS_OK) st = gs_render_bwd(ctx, cam, proj, bins, ras, nullptr, grad2d);
         } else {
             st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, nullptr, &ras);
@@ -1027,6 +1047,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     }
     if (opts->loss_kind == 0) {
         double s = 0.0;
+        if (l1_off > 0 && (st = launch_sum_f64(ctx, l1_view, l1_off, 1, loss_dev, 1)) != GS_OK) goto done;
         if ((st = readback(ctx, loss_dev, sizeof(double), &s)) != GS_OK) goto done;
         loss = s / (3.0 * (double)P);
     } else if (hipStreamSynchronize(ctx->stream) != hipSuccess) {

@@ -178,11 +178,12 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
             // alpha < 1/255; at -87 o exp(-87) < 1/255 too), finite on the others
             const bool pok = !(power > 0.0f);
             const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
-            const float av = b.y * G;
-            const float alpha = av > gsd::kAlphaMax ? gsd::kAlphaMax : av;
+            // o and G are finite, so min gives the clamp exactly
+            const float alpha = fminf(b.y * G, gsd::kAlphaMax);
             const bool inc = active && pok && !(alpha < gsd::kAlphaMin);
-            const float ae = inc ? alpha : 0.0f;
-            const float Tn = T * (1.0f - ae);
+            // T' and the weight of a lane that includes the entry (the other
+            // lanes keep their state through the selects below)
+            const float Tn = T * (1.0f - alpha);
             const bool stop = inc && Tn < gsd::kTMin;
             const bool contrib = inc && !stop;
             if (STATS) {
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
                 ev_at_last = contrib ? n_eval : ev_at_last;
             }
             active = active && !stop;
-            const float w = contrib ? ae * T : 0.0f;   // fma(x, 0, C) = C exactly
+            const float w = contrib ? alpha * T : 0.0f;   // fma(x, 0, C) = C exactly
             C0 = __builtin_fmaf(b.z, w, C0);
             C1 = __builtin_fmaf(b.w, w, C1);
             C2 = __builtin_fmaf(S.c[j].x, w, C2);
