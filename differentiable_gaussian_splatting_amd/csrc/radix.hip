@@ -27,10 +27,15 @@ __global__ __launch_bounds__(kRB) void k_radix_hist(const uint32_t* __restrict__
     for (int d = threadIdx.x; d < kRadix; d += kRB) h[d] = 0u;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kRTile;
-    for (int k = threadIdx.x; k < kRTile; k += kRB) {
-        const int64_t i = base + k;
-        if (i < n) atomicAdd(&h[(keys[i] >> shift) & mask], 1u);
+    uint32_t kk[kRItems];   // all of the thread's keys requested before the first count
+#pragma unroll
+    for (int r = 0; r < kRItems; ++r) {
+        const int64_t i = base + (int64_t)r * kRB + threadIdx.x;
+        kk[r] = i < n ? keys[i] : 0u;
     }
+#pragma unroll
+    for (int r = 0; r < kRItems; ++r)
+        if (base + (int64_t)r * kRB + threadIdx.x < n) atomicAdd(&h[(kk[r] >> shift) & mask], 1u);
     __syncthreads();
     for (int d = threadIdx.x; d <= (int)mask; d += kRB) hist[(int64_t)d * nb + blockIdx.x] = h[d];
 }
@@ -54,7 +59,13 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* sh)
 // Stable scatter of one block's kRTile elements: (1) local ranks in element
 // order, (2) the block's elements placed digit-sorted in LDS, (3) written out
 // digit run by digit run, so that consecutive lanes write consecutive
-// addresses.
+// addresses.  Ranks, round by round (kRB elements each): a wavefront's lanes
+// with equal digits are found with one ballot per digit bit; the first lane
+// of each such group records the group size in wh[wave][digit] tagged with
+// the round (entries with another tag count as zero, so wh is cleared only
+// once), and after the round the group sizes are added to run[digit] with one
+// LDS atomic per (wavefront, digit).  Two barriers per round: one after the
+// tagged sizes are written, one after every lane has read run[].
 template <int kRadix>
 __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restrict__ kin,
                                                        const uint32_t* __restrict__ vin, int64_t n, int shift,
@@ -64,7 +75,7 @@ __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restric
     __shared__ uint32_t run[kRadix];
     __shared__ uint32_t lstart[kRadix];
     __shared__ uint32_t gbase[kRadix];
-    __shared__ uint32_t wh[kRB / 64][kRadix];
+    __shared__ uint32_t wh[kRB / 64][kRadix];   // (round + 1) << 16 | group size
     __shared__ uint32_t sk[kRTile];
     __shared__ uint32_t sv[kRTile];
     __shared__ uint32_t scan_sh[kRB / 64];
@@ -75,42 +86,44 @@ __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restric
         run[d] = 0u;
         gbase[d] = hscan[(int64_t)d * nb + blockIdx.x];
     }
+    for (int q = threadIdx.x; q < (kRB / 64) * kRadix; q += kRB) (&wh[0][0])[q] = 0u;
+    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kRTile;
     uint32_t kk[kRItems], vv[kRItems], ll[kRItems], dd[kRItems];
+    // every element of the thread is requested before the first round
 #pragma unroll
     for (int r = 0; r < kRItems; ++r) {
-        for (int q = threadIdx.x; q < (kRB / 64) * kRadix; q += kRB) (&wh[0][0])[q] = 0u;
+        const int64_t i = base + (int64_t)r * kRB + threadIdx.x;
+        kk[r] = i < n ? kin[i] : 0u;
+        vv[r] = i < n ? vin[i] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kRItems; ++r) {
         const int64_t i = base + (int64_t)r * kRB + threadIdx.x;
         const bool valid = i < n;
-        uint32_t key = 0, val = 0, d = 0;
-        if (valid) {
-            key = kin[i];
-            val = vin[i];
-            d = (key >> shift) & mask;
-        }
+        const uint32_t key = kk[r];
+        const uint32_t d = valid ? (key >> shift) & mask : 0u;
         uint64_t peers = gsd::ballot(valid);
         for (int b = 0; b < bits; ++b) {
             const uint64_t bb = gsd::ballot(valid && ((d >> b) & 1u));
             peers &= ((d >> b) & 1u) ? bb : ~bb;
         }
         const uint32_t rank = (uint32_t)__popcll(peers & lt);
-        __syncthreads();
-        if (valid && rank == 0) wh[wave][d] = (uint32_t)__popcll(peers);
-        __syncthreads();
+        const uint32_t size = (uint32_t)__popcll(peers);
+        const uint32_t tag = (uint32_t)(r + 1) << 16;
+        if (valid && rank == 0) wh[wave][d] = tag | size;
+        __syncthreads();                       // tagged group sizes of the round written
         uint32_t loc = run[d] + rank;
-        for (int w = 0; w < wave; ++w) loc += wh[w][d];
-        kk[r] = key;
-        vv[r] = val;
+        for (int w = 0; w < wave; ++w) {
+            const uint32_t t = wh[w][d];
+            loc += (t & 0xFFFF0000u) == tag ? (t & 0xFFFFu) : 0u;
+        }
         dd[r] = valid ? d : 0xFFFFFFFFu;
         ll[r] = loc;
-        __syncthreads();
-        for (int q = threadIdx.x; q < kRadix; q += kRB) {
-            uint32_t s = 0;
-            for (int w = 0; w < kRB / 64; ++w) s += wh[w][q];
-            run[q] += s;
-        }
-        __syncthreads();
+        __syncthreads();                       // every lane has read run[] for the round
+        if (valid && rank == 0) atomicAdd(&run[d], size);
     }
+    __syncthreads();
     // local start of every digit run (each thread scans kRadix / kRB
     // consecutive digits)
     {
