@@ -237,7 +237,6 @@ __global__ __launch_bounds__(256) void k_leaf_counts(const int32_t* __restrict__
     out[t] = (uint32_t)grid[(int64_t)(lty0 + t / TWL) * TW + ltx0 + t % TWL];
 }
 
-constexpr int kOB = 256;     // threads (and candidates) of an emission block
 // coarse key: bits [0, kCellBits) the leaf's super-tile, above them the
 // entry's rectangle inside that super-tile (x0, x1 - 1, y0, y1 - 1 in its
 // 8 x 8 local tiles, 3 bits each), carried through the sort for the fine level
@@ -246,52 +245,158 @@ constexpr int kCellBits = 20;
 // (super-tile, slot) pairs of the listed candidates, in list order and
 // row-major super-tile order within a rectangle.  eoff[k] - ebase is the
 // first output of candidate k (exclusive scan of the per-candidate super-tile
-// counts, n + 1 entries).  Block = kOB consecutive candidates: their slots,
-// super-cell ranges and offsets are staged in LDS in one round of loads;
-// their outputs form one contiguous range, which the block's threads write
-// at consecutive positions (coalesced), each finding its candidate by binary
-// search in the LDS offsets.
-__global__ __launch_bounds__(kOB) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
+// counts, n + 1 entries, ascending).  A block writes kEO consecutive outputs,
+// so that one candidate with many super-tiles does not hold up a block:
+//   - its first candidate (the last k with eoff[k] - ebase <= first output)
+//     comes from a 256-ary search over eoff, three rounds of loads for up to
+//     2^24 candidates;
+//   - the candidates from there on are staged in LDS (every listed candidate
+//     meets the leaf, so at most kEO + 1 of them overlap the block's outputs);
+//   - each candidate whose outputs start inside the block marks that
+//     position with its index, and a prefix maximum over the positions gives
+//     every output its candidate;
+//   - thread t writes outputs 4t .. 4t + 3 of the block.
+// The super-cell row of output t of a candidate spanning w columns is t / w,
+// from the f32 reciprocal of w with one correction (t < 2^23).  Outputs past
+// the staged candidates (only if some candidate had no output) fall back to a
+// binary search in eoff.
+constexpr int kEO = 1024;          // outputs per emission block (4 per thread)
+
+__device__ __forceinline__ int wave_prefix_max(int v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v = max(v, u);
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
                                                     const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
                                                     int lty1, int sh, int SW, const uint32_t* __restrict__ eoff,
-                                                    uint32_t ebase, uint32_t* __restrict__ keys,
+                                                    uint32_t ebase, uint32_t total, uint32_t* __restrict__ keys,
                                                     uint32_t* __restrict__ vals)
 {
-    __shared__ uint32_t se[kOB + 1];
-    __shared__ uint32_t sj[kOB];
-    __shared__ int4 sc[kOB];       // cx0, cy0, w, h of each candidate's super-cells
-    __shared__ int4 sr[kOB];       // its rectangle clipped to the leaf
-    const int64_t c0 = (int64_t)blockIdx.x * kOB;
-    const int m = (int)min<int64_t>(kOB, n - c0);
-    for (int k = threadIdx.x; k <= m; k += kOB) se[k] = eoff[c0 + k] - ebase;
-    if ((int)threadIdx.x < m) {
-        const uint32_t j = list[c0 + threadIdx.x];
+    __shared__ uint32_t se[kEO + 2];
+    __shared__ uint32_t sj[kEO + 1];
+    __shared__ int4 sc[kEO + 1];       // cx0, cy0, w, h of each staged candidate's super-cells
+    __shared__ int4 sr[kEO + 1];       // its rectangle clipped to the leaf
+    __shared__ float srw[kEO + 1];     // 1 / w
+    __shared__ int owner[kEO];         // candidate whose outputs start at this position, else -1
+    __shared__ int wred[4];
+    __shared__ int64_t s_lo;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t ob = blockIdx.x * (uint32_t)kEO;
+    const uint32_t oe = min(ob + (uint32_t)kEO, total);
+    // ---- first candidate: 256-ary search for the last k with eoff[k] - ebase <= ob
+    int64_t lo = 0, len = n;
+    while (len > 1) {
+        const int64_t st = (len + 255) / 256;
+        const int64_t idx = lo + (int64_t)tid * st;
+        const bool le = idx < lo + len && eoff[idx] - ebase <= ob;
+        const uint64_t bm = gsd::ballot(le);
+        if (lane == 0) wred[wave] = __popcll(bm);
+        __syncthreads();
+        const int64_t cnt = (int64_t)wred[0] + wred[1] + wred[2] + wred[3];   // >= 1: eoff[lo] - ebase <= ob
+        __syncthreads();
+        const int64_t nlo = lo + (cnt - 1) * st;
+        len = min(st, lo + len - nlo);
+        lo = nlo;
+    }
+    if (tid == 0) s_lo = lo;
+    __syncthreads();
+    const int64_t k0 = s_lo;
+    const int ns = (int)min<int64_t>(kEO + 1, n - k0);   // staged candidates
+    for (int i = tid; i <= ns; i += 256) se[i] = eoff[k0 + i] - ebase;
+    for (int i = tid; i < ns; i += 256) {
+        const uint32_t j = list[k0 + i];
         const int4 r = rect[j];
         const Cells cl = leaf_cells(r, ltx0, lty0, ltx1, lty1, sh);
-        sj[threadIdx.x] = j;
-        sc[threadIdx.x] = make_int4(cl.cx0, cl.cy0, cl.w, cl.h);
-        sr[threadIdx.x] = make_int4(max(r.x, ltx0), max(r.y, lty0), min(r.z, ltx1), min(r.w, lty1));
+        sj[i] = j;
+        sc[i] = make_int4(cl.cx0, cl.cy0, cl.w, cl.h);
+        sr[i] = make_int4(max(r.x, ltx0), max(r.y, lty0), min(r.z, ltx1), min(r.w, lty1));
+        srw[i] = 1.0f / (float)max(cl.w, 1);
+    }
+    for (int i = tid; i < kEO; i += 256) owner[i] = -1;
+    __syncthreads();
+    for (int i = tid; i < ns; i += 256) {
+        const uint32_t a = se[i], b = se[i + 1];
+        if (b > a && a >= ob && a < oe) owner[a - ob] = i;
     }
     __syncthreads();
-    const uint32_t o0 = se[0], o1 = se[m];
-    for (uint32_t o = o0 + threadIdx.x; o < o1; o += kOB) {
-        int lo = 0, hi = m - 1;                 // last k with se[k] <= o
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (se[mid] <= o) lo = mid;
-            else hi = mid - 1;
+    // prefix maximum over positions 4 tid .. 4 tid + 3, then over the threads
+    int om[4];
+    int run = 0;   // staged candidate 0 starts at or before ob
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        run = max(run, owner[4 * tid + q]);
+        om[q] = run;
+    }
+    const int inc = wave_prefix_max(run, lane);
+    int exc = __shfl_up(inc, 1, 64);
+    if (lane == 0) exc = 0;
+    if (lane == 63) wred[wave] = inc;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) exc = max(exc, wred[w]);
+    const uint32_t end_staged = se[ns];
+    uint32_t kq[4], vq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t o = ob + 4u * (uint32_t)tid + (uint32_t)q;
+        kq[q] = 0u;
+        vq[q] = 0u;
+        if (o >= oe) continue;
+        int v = max(om[q], exc);
+        int4 cl, r;
+        uint32_t t, j;
+        float rw;
+        if (o < end_staged) {
+            cl = sc[v];
+            r = sr[v];
+            t = o - se[v];
+            j = sj[v];
+            rw = srw[v];
+        } else {
+            // past the staged candidates: the last k with eoff[k] - ebase <= o
+            int64_t a = k0, b = n - 1;
+            while (a < b) {
+                const int64_t mid = (a + b + 1) >> 1;
+                if (eoff[mid] - ebase <= o) a = mid;
+                else b = mid - 1;
+            }
+            j = list[a];
+            const int4 rr = rect[j];
+            const Cells c = leaf_cells(rr, ltx0, lty0, ltx1, lty1, sh);
+            cl = make_int4(c.cx0, c.cy0, c.w, c.h);
+            r = make_int4(max(rr.x, ltx0), max(rr.y, lty0), min(rr.z, ltx1), min(rr.w, lty1));
+            t = o - (eoff[a] - ebase);
+            rw = 1.0f / (float)max(c.w, 1);
         }
-        const int4 cl = sc[lo];
-        const uint32_t t = o - se[lo];
-        const uint32_t ty = t / (uint32_t)cl.z;
-        const int cx = cl.x + (int)(t - ty * (uint32_t)cl.z), cy = cl.y + (int)ty;
+        const uint32_t wd = (uint32_t)cl.z;
+        uint32_t ty = (uint32_t)((float)t * rw);
+        int32_t rem = (int32_t)(t - ty * wd);
+        if (rem < 0) { ty -= 1u; rem += (int32_t)wd; }
+        else if (rem >= (int32_t)wd) { ty += 1u; rem -= (int32_t)wd; }
+        const int cx = cl.x + rem, cy = cl.y + (int)ty;
         // the rectangle inside this super-tile (and the leaf), in its local tiles
-        const int4 r = sr[lo];
         const int bx = ((ltx0 >> sh) + cx) << sh, by = ((lty0 >> sh) + cy) << sh;
         const uint32_t x0 = (uint32_t)(max(r.x, bx) - bx), x1 = (uint32_t)(min(r.z, bx + 8) - bx);
         const uint32_t y0 = (uint32_t)(max(r.y, by) - by), y1 = (uint32_t)(min(r.w, by + 8) - by);
-        keys[o] = ((x0 | ((x1 - 1u) << 3) | (y0 << 6) | ((y1 - 1u) << 9)) << kCellBits) | (uint32_t)(cy * SW + cx);
-        vals[o] = sj[lo];
+        kq[q] = ((x0 | ((x1 - 1u) << 3) | (y0 << 6) | ((y1 - 1u) << 9)) << kCellBits) | (uint32_t)(cy * SW + cx);
+        vq[q] = j;
+    }
+    const uint32_t o4 = ob + 4u * (uint32_t)tid;
+    if (o4 + 3u < oe) {
+        *reinterpret_cast<uint4*>(keys + o4) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+        *reinterpret_cast<uint4*>(vals + o4) = make_uint4(vq[0], vq[1], vq[2], vq[3]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (o4 + (uint32_t)q < oe) {
+                keys[o4 + q] = kq[q];
+                vals[o4 + q] = vq[q];
+            }
     }
 }
 
@@ -600,9 +705,9 @@ gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
 {
     if (n_list > 0 && total > 0) {
         GsTimerScope ts(ctx, "emit");
-        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div(n_list, kOB)), dim3(kOB), 0, ctx->stream, n_list,
-                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift, super_cols(leaf),
-                           eoff, ebase, keys, vals);
+        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div((int64_t)total, kEO)), dim3(256), 0, ctx->stream,
+                           n_list, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift,
+                           super_cols(leaf), eoff, ebase, (uint32_t)total, keys, vals);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
