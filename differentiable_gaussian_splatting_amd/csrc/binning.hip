@@ -250,8 +250,10 @@ constexpr int kCellBits = 20;
 //   - its first candidate (the last k with eoff[k] - ebase <= first output)
 //     comes from a 256-ary search over eoff, three rounds of loads for up to
 //     2^24 candidates;
-//   - the candidates from there on are staged in LDS (every listed candidate
-//     meets the leaf, so at most kEO + 1 of them overlap the block's outputs);
+//   - the offsets of the next kEO + 1 candidates are loaded (every listed
+//     candidate meets the leaf, so no more can overlap the block's outputs),
+//     and the slots and rectangles of those that start before the block's
+//     last output are gathered into LDS;
 //   - each candidate whose outputs start inside the block marks that
 //     position with its index, and a prefix maximum over the positions gives
 //     every output its candidate;
@@ -307,8 +309,19 @@ __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* _
     if (tid == 0) s_lo = lo;
     __syncthreads();
     const int64_t k0 = s_lo;
-    const int ns = (int)min<int64_t>(kEO + 1, n - k0);   // staged candidates
-    for (int i = tid; i <= ns; i += 256) se[i] = eoff[k0 + i] - ebase;
+    const int nmax = (int)min<int64_t>(kEO + 1, n - k0);
+    for (int i = tid; i <= nmax; i += 256) se[i] = eoff[k0 + i] - ebase;
+    __syncthreads();
+    // stage only the candidates that start before the block's last output
+    {
+        int c = 0;
+        for (int i = tid; i < nmax; i += 256) c += se[i] < oe ? 1 : 0;
+        c = (int)gsd::wave_sum_u64((uint64_t)c);
+        if (lane == 0) wred[wave] = c;
+    }
+    __syncthreads();
+    const int ns = wred[0] + wred[1] + wred[2] + wred[3];   // >= 1
+    __syncthreads();
     for (int i = tid; i < ns; i += 256) {
         const uint32_t j = list[k0 + i];
         const int4 r = rect[j];
