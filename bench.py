@@ -31,7 +31,7 @@ PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 #   every examined pair: offsets 2, power 5, range test 2, exp 14, alpha with
 #     clamp and threshold 4                                            = 27
 #   an included pair adds, forward: T' 2, stop test 1, weight 1,
-#     colour 3 fma, bookkeeping 1                                      -> 35
+#     colour 3 fma                                                     -> 34
 #   backward: T recovery 3 (1 - alpha, reciprocal, product), weight 1,
 #     colour dot dL/dout 3, dL/dalpha 2, colour behind 1, colour partials
 #     3, clamp decision 1, opacity partial 1, -dL/dpower 1, the five
@@ -39,7 +39,7 @@ PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 #     (the mean and conic partials follow from the moments once per
 #     entry, not per pixel)                                            -> 50
 OPS_EXAMINED = 27
-OPS_INCLUDED_FWD = 35
+OPS_INCLUDED_FWD = 34
 OPS_INCLUDED_BWD = 50
 
 
@@ -240,7 +240,7 @@ def main():
 def count_work(B, ctx, cam, params, budget):
     """Work counters of the view as benchmarked (untimed): pairs examined by
     the forward (q_f), pairs included (q_inc), pairs the backward revisits
-    (q_b = sum of last), intersections, candidates, leaves, tiles, pixels."""
+    (q_b: those examined), intersections, candidates, leaves, tiles, pixels."""
     import torch
     proj, n_cand = B.gs_project(ctx, cam, params)
     leaves = (B.gs_plan_leaves(ctx, cam, proj, budget) if budget > 0 else

@@ -28,8 +28,10 @@
 //   C = fma(rgb, alpha T, C); T = T'
 //   out = fma(T, bg, C)
 // Backward (BoundedGS Fig. 3 A->B; SkipGS notes: atomic accumulation): per
-// pixel the included entries are revisited back to front from the last one,
-// with T recovered as T' / (1 - alpha) and the colour behind accumulated as S;
+// pixel the included entries are revisited back to front, starting at the end
+// of the pixel's forward walk (the position of the entry before which it
+// stopped, else the list length: no entry from there on is included), with T
+// recovered as T' / (1 - alpha) and the colour behind accumulated as S;
 //   dL/dalpha = sum_ch g_ch (rgb_ch T - S_ch / (1 - alpha)).
 // The 9 partials of an entry are summed over the wavefront by a transposed
 // reduction (each step halves the lanes per value while pairing values, with
@@ -141,7 +143,10 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
     Staged& S = st[wave];
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
-    uint32_t lastn = 0, n_eval = 0, n_inc = 0, ev_at_last = 0;
+    // end of the pixel's walk: the list position of the entry before which
+    // compositing stopped, else the list length (no entry at or after it is
+    // included, so the backward revisits the entries before it)
+    uint32_t lastn = (uint32_t)(end - start), n_eval = 0, n_inc = 0;
     bool active = inside;
     for (uint64_t base = start; base < end; base += 64) {
         if (gsd::ballot(active) == 0) break;
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
         }
         uint64_t mask = gsd::ballot(keep);
         gsd::wave_sync();
-        const uint32_t n0 = (uint32_t)(base - start) + 1u;
+        const uint32_t n0 = (uint32_t)(base - start);
         // Branch-free over the lanes: every lane evaluates the entry and the
         // per-lane decisions become selects, so the wavefront issues one
         // straight run of instructions per entry.  A lane's values for an
@@ -189,7 +194,6 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
             if (STATS) {
                 n_eval += active ? 1u : 0u;
                 n_inc += contrib ? 1u : 0u;
-                ev_at_last = contrib ? n_eval : ev_at_last;
             }
             active = active && !stop;
             const float w = contrib ? alpha * T : 0.0f;   // fma(x, 0, C) = C exactly
@@ -197,7 +201,14 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
             C1 = __builtin_fmaf(b.w, w, C1);
             C2 = __builtin_fmaf(S.c[j].x, w, C2);
             T = contrib ? Tn : T;
-            lastn = contrib ? n0 + (uint32_t)j : lastn;
+            // a lane stops once per list: the stopping lanes record the
+            // position under an exec mask that is empty on almost every entry
+            // (scalar instructions only then; the empty volatile asm keeps the
+            // compiler from turning the branch into a select on every entry)
+            if (stop) {
+                asm volatile("");
+                lastn = n0 + (uint32_t)j;
+            }
         }
         gsd::wave_sync();
     }
@@ -234,10 +245,11 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
     }
     if (STATS) {
         // [0] pairs examined, [1] pairs included, [2] sum of last, [3] pairs
-        // the backward revisits (examined up to the last included entry)
+        // the backward revisits (those the forward examined: the backward
+        // walks each pixel's list from the end of its forward walk)
         const double a0 = gsd::wave_sum_d((double)n_eval), a1 = gsd::wave_sum_d((double)n_inc);
         const double a2 = gsd::wave_sum_d((double)(inside ? lastn : 0u));
-        const double a3 = gsd::wave_sum_d((double)ev_at_last);
+        const double a3 = gsd::wave_sum_d((double)n_eval);
         if (lane == 0) {
             atomicAdd(&stats[0], (unsigned long long)a0);
             atomicAdd(&stats[1], (unsigned long long)a1);
@@ -312,10 +324,10 @@ __device__ __forceinline__ float wave_reduce9(const float* p, int lane, int* vid
 // Backward, one wavefront per 16 x 16 tile, four tiles per workgroup and no
 // workgroup barrier.  Lane l owns pixel l (x = l % 8, y = l / 8) of each 8 x 8
 // quadrant k of the tile (k & 1: right half, k >> 1: bottom half).  The
-// wavefront walks the tile's list back to front from the last entry any of its
-// pixels included, 64 entries per batch staged in its own LDS slice; lane i
-// gathers entry i and sets bit k of the entry's quadrant mask when the entry
-// precedes the last entry included in quadrant k and survives the cull
+// wavefront walks the tile's list back to front from the furthest end of its
+// pixels' forward walks, 64 entries per batch staged in its own LDS slice;
+// lane i gathers entry i and sets bit k of the entry's quadrant mask when the
+// entry precedes the end of some forward walk in quadrant k and survives the cull
 // against quadrant k's box.  Per entry, the quadrants of the mask are
 // evaluated in turn (one wave-uniform branch each, skipped when none of the
 // quadrant's pixels includes the entry); the partials of a lane's four pixels
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
 
     // per quadrant k: transmittance after the last included entry, dL/dout,
     // GS = sum_ch dL/dout_ch * (colour behind the current entry, ch), which
-    // starts as the background seen through T_final, and the last entry
+    // starts as the background seen through T_final, and the end of the walk
     float T[4], GS[4], gr0[4], gr1[4], gr2[4];
     uint32_t lst[4], mq[4];
 #pragma unroll

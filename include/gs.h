@@ -208,16 +208,18 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
  * the backward.  Per pixel, front to back over its tile's list:
  * alpha = min(0.99, opacity * exp(power)); entries with power > 0 or
  * alpha < 1/255 are skipped; compositing stops before an entry that would
- * take T below 1e-4; out = C + T bg.  Keeps T_final and the list position
- * after the last included entry per pixel.
+ * take T below 1e-4; out = C + T bg.  Keeps, per pixel, T_final and the
+ * end of its walk over the list: the position of the entry before which
+ * compositing stopped, else the list length (no entry from there on is
+ * included; the backward starts there).
  * target: device full image [3][H][W] or NULL.  With a target the L1 term
  * is fused: sum |out - target| over the leaf is added to *loss_accum
  * (device, one double, may be NULL) and dL/dout = sgn(out - target)/(3WH)
  * is kept in the raster handle for gs_render_bwd.  image_out: device full
  * image [3][H][W] or NULL; the leaf's pixels are written.  stats: device
  * u64 [4] or NULL; when given, [0] the (pixel, entry) pairs examined, [1]
- * the pairs included, [2] the sum over pixels of the list position after the
- * last included entry, [3] the pairs gs_render_bwd revisits, are added to it
+ * the pairs included, [2] the sum over pixels of the end of the walk, [3]
+ * the pairs gs_render_bwd revisits (those examined), are added to it
  * (a separately compiled, slightly slower kernel).  *out: new handle.
  * Asynchronous. */
 gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
