@@ -575,7 +575,21 @@ __global__ __launch_bounds__(256) void k_fine_scan(int ltx0, int lty0, int TWL, 
     const int gy = (((lty0 >> kSuperShift) + sc / SW) << kSuperShift) + (j >> 3);
     if (gx < ltx0 || gx >= ltx0 + TWL || gy < lty0 || gy >= lty0 + THL) return;
     uint32_t p = (uint32_t)toff[(int64_t)(gy - lty0) * TWL + (gx - ltx0)];
-    for (uint32_t i = ioff[sc]; i < ioff[sc + 1]; ++i) {
+    // eight items' counts are loaded before their positions are written, so
+    // the loads do not wait on each other
+    uint32_t i = ioff[sc];
+    const uint32_t ie = ioff[sc + 1];
+    for (; i + 8u <= ie; i += 8u) {
+        uint32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = pos[(int64_t)(i + u) * 64 + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            pos[(int64_t)(i + u) * 64 + j] = p;
+            p += c[u];
+        }
+    }
+    for (; i < ie; ++i) {
         const uint32_t c = pos[(int64_t)i * 64 + j];
         pos[(int64_t)i * 64 + j] = p;
         p += c;

@@ -369,38 +369,57 @@ __global__ void k_leaf_cell_bounds(int nl, const uint64_t* __restrict__ goff, co
 }
 
 // per leaf (one workgroup): exclusive scan of its tiles' candidate counts in
-// leaf-local row-major order, written at out + base[L] (T_L + 1 entries)
+// leaf-local row-major order, written at out + base[L] (T_L + 1 entries).
+// Wavefront w owns a contiguous segment of the leaf's tiles, read in
+// coalesced chunks of 64: it sums the segment (four chunks' loads in flight
+// at a time), one scan over the 16 segment sums gives each segment's offset,
+// and a second walk scans chunk by chunk (wave scan plus a carry) and writes.
+__device__ __forceinline__ uint64_t leaf_tile_count(const int32_t* __restrict__ tile_cnt, int TW, const gs_leaf& lf,
+                                                    int TWL, int64_t t, int64_t t1)
+{
+    return t < t1 ? (uint64_t)tile_cnt[(int64_t)(lf.ty0 + t / TWL) * TW + lf.tx0 + t % TWL] : 0ull;
+}
+
 __global__ __launch_bounds__(1024) void k_leaf_toff(const gs_leaf* __restrict__ leaves,
                                                     const int32_t* __restrict__ tile_cnt, int TW,
                                                     const uint64_t* __restrict__ base, uint64_t* __restrict__ out)
 {
     __shared__ uint64_t wsum[16];
-    __shared__ uint64_t carry;
     const gs_leaf lf = leaves[blockIdx.x];
     const int TWL = lf.tx1 - lf.tx0;
     const int64_t n = (int64_t)TWL * (lf.ty1 - lf.ty0);
     uint64_t* o = out + base[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) carry = 0;
+    const int64_t seg = ((n + 15) / 16 + 63) / 64 * 64;   // tiles per wavefront, a multiple of 64
+    const int64_t t0 = min(n, (int64_t)wave * seg), t1 = min(n, t0 + seg);
+    uint64_t s = 0;
+    for (int64_t c = t0; c < t1; c += 256) {
+        const uint64_t a0 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + lane, t1);
+        const uint64_t a1 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + 64 + lane, t1);
+        const uint64_t a2 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + 128 + lane, t1);
+        const uint64_t a3 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + 192 + lane, t1);
+        s += (a0 + a1) + (a2 + a3);
+    }
+    s = gsd::wave_sum_u64(s);
+    if (lane == 0) wsum[wave] = s;
     __syncthreads();
-    for (int64_t t0 = 0; t0 < n; t0 += 1024) {
-        const int64_t t = t0 + tid;
-        const uint64_t c = t < n ? (uint64_t)tile_cnt[(int64_t)(lf.ty0 + t / TWL) * TW + lf.tx0 + t % TWL] : 0ull;
-        uint64_t x = c;
+    uint64_t carry = 0;
+    for (int w = 0; w < wave; ++w) carry += wsum[w];
+    for (int64_t c = t0; c < t1; c += 64) {
+        const uint64_t v = leaf_tile_count(tile_cnt, TW, lf, TWL, c + lane, t1);
+        uint64_t x = v;
         for (int d = 1; d < 64; d <<= 1) {
             const uint64_t u = __shfl_up((unsigned long long)x, d, 64);
             if (lane >= d) x += u;
         }
-        if (lane == 63) wsum[wave] = x;
-        __syncthreads();
-        uint64_t before = carry;
-        for (int w = 0; w < wave; ++w) before += wsum[w];
-        if (t < n) o[t] = before + x - c;
-        __syncthreads();
-        if (tid == 1023) carry = before + x;
-        __syncthreads();
+        if (c + lane < t1) o[c + lane] = carry + x - v;
+        carry += __shfl((unsigned long long)x, 63, 64);
     }
-    if (tid == 0) o[n] = carry;
+    if (tid == 0) {
+        uint64_t tot = 0;
+        for (int w = 0; w < 16; ++w) tot += wsum[w];
+        o[n] = tot;
+    }
 }
 
 }  // namespace
