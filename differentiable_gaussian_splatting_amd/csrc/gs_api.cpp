@@ -678,11 +678,18 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
         if (!k1 || !v1) { st = GS_ERR_OOM; goto fail; }
     }
-    if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)C, bits_for(n_super), &second)) != GS_OK) goto fail;
     soff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (n_super + 1), GS_MEM_RASTER, &tmp);
     if (!soff) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)C, n_super, super_key_mask(), soff)) != GS_OK)
-        goto fail;
+    {
+        // a single-pass sort writes the super-tile group offsets itself
+        bool have_soff = false;
+        if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)C, bits_for(n_super), &second, soff, n_super,
+                                    &have_soff)) != GS_OK)
+            goto fail;
+        if (!have_soff &&
+            (st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)C, n_super, super_key_mask(), soff)) != GS_OK)
+            goto fail;
+    }
     gs_free_one(ctx, &tmp, second ? k0 : k1);     // the sorted keys stay for the fine level
     gs_free_one(ctx, &tmp, second ? v0 : v1);
     // fine level: per-tile lists at the tile offsets

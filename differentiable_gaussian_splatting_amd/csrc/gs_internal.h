@@ -175,7 +175,8 @@ int bits_for(int64_t n_keys);
 
 // radix.hip: stable sort of (u32 key, u32 value) pairs on the low key_bits bits
 gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n,
-                            int key_bits, bool* in_second);
+                            int key_bits, bool* in_second, uint64_t* digit_off = nullptr, int64_t n_seg = 0,
+                            bool* off_written = nullptr);
 
 // raster.hip
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,

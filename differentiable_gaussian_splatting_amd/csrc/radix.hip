@@ -70,7 +70,8 @@ template <int kRadix>
 __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restrict__ kin,
                                                        const uint32_t* __restrict__ vin, int64_t n, int shift,
                                                        int bits, const uint32_t* __restrict__ hscan, int64_t nb,
-                                                       uint32_t* __restrict__ kout, uint32_t* __restrict__ vout)
+                                                       uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
+                                                       uint64_t* __restrict__ digit_off, int n_seg)
 {
     __shared__ uint32_t run[kRadix];
     __shared__ uint32_t lstart[kRadix];
@@ -86,6 +87,10 @@ __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restric
         run[d] = 0u;
         gbase[d] = hscan[(int64_t)d * nb + blockIdx.x];
     }
+    // a single pass over keys < n_seg: where each digit's run starts in the
+    // output (the scan at block 0), and the total
+    if (digit_off && blockIdx.x == 0)
+        for (int d = threadIdx.x; d <= n_seg; d += kRB) digit_off[d] = hscan[(int64_t)d * nb];
     for (int q = threadIdx.x; q < (kRB / 64) * kRadix; q += kRB) (&wh[0][0])[q] = 0u;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kRTile;
@@ -162,10 +167,15 @@ __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restric
 // Sorts n pairs by the low key_bits bits of the keys (stable).  k0/v0 hold the
 // input; k1/v1 are scratch of the same size.  *in_second is set when the
 // sorted result ends in (k1, v1).  Offsets of one pass fit u32: n < 2^32.
+// digit_off (optional, n_seg + 1 entries): when the sort takes a single pass
+// and every key's low bits are < n_seg, the first output position of each
+// value s in [0, n_seg) and the total are written there, and *off_written is
+// set.
 gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n,
-                            int key_bits, bool* in_second)
+                            int key_bits, bool* in_second, uint64_t* digit_off, int64_t n_seg, bool* off_written)
 {
     *in_second = false;
+    if (off_written) *off_written = false;
     if (n <= 1 || key_bits <= 0) return GS_OK;
     if (n >= (1ll << 32)) return gs_fail(ctx, GS_ERR_OVERFLOW, "radix sort of %lld >= 2^32 pairs", (long long)n);
     const int64_t nb = ceil_div(n, kRTile);
@@ -182,6 +192,7 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
     gs_status st = GS_OK;
     uint32_t *ki = k0, *vi = v0, *ko = k1, *vo = v1;
     const int step = wide ? key_bits : 8;
+    const bool want_off = digit_off && off_written && wide && n_seg >= 0 && n_seg <= radix;
     for (int shift = 0; shift < key_bits && st == GS_OK; shift += step) {
         const int bits = std::min(step, key_bits - shift);
         const uint32_t mask = (1u << bits) - 1u;
@@ -201,10 +212,10 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
             GsTimerScope ts(ctx, "radix");
             if (wide)
                 hipLaunchKernelGGL(k_radix_scatter<1024>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n,
-                                   shift, bits, hscan, nb, ko, vo);
+                                   shift, bits, hscan, nb, ko, vo, want_off ? digit_off : nullptr, (int)n_seg);
             else
                 hipLaunchKernelGGL(k_radix_scatter<256>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n,
-                                   shift, bits, hscan, nb, ko, vo);
+                                   shift, bits, hscan, nb, ko, vo, nullptr, 0);
         }
         std::swap(ki, ko);
         std::swap(vi, vo);
@@ -213,5 +224,6 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
     gs_free_all(ctx, &tmp);
     if (st != GS_OK) return st;
     GS_HIP(ctx, hipGetLastError());
+    if (want_off) *off_written = true;
     return GS_OK;
 }
