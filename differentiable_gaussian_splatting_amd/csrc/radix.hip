@@ -1,9 +1,10 @@
 // radix.hip -- stable LSD radix sort of (u32 key, u32 value) pairs.
 //
 // Each pass takes 8 key bits (fewer on the last pass), or a single pass takes
-// up to 10 bits: a per-block digit histogram (LDS atomics), an exclusive scan
-// of the digit-major histogram (digit * n_blocks + block), and a stable
-// scatter.  The scatter ranks a
+// up to 10 bits: a per-block digit histogram (LDS atomics) laid out
+// digit-major (digit * n_blocks + block), an exclusive scan of each digit's
+// row with its total (one workgroup per digit), and a stable scatter, whose
+// blocks add the scan of the digit totals.  The scatter ranks a
 // block's elements in element order: 256 elements per round, a wavefront
 // finds the lanes holding the same digit with one ballot per digit bit
 // (lane rank = popcount of same-digit lanes below it), per-wave digit counts
@@ -56,6 +57,43 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* sh)
     return before + x - v;
 }
 
+// Per digit (one workgroup): exclusive scan of its row of per-block counts
+// (the histogram is digit-major, so a row is contiguous), in place, and the
+// digit's total.  Each wavefront owns a quarter of the row: it sums it in
+// coalesced chunks, then rescans it chunk by chunk with a carry.
+__global__ __launch_bounds__(256) void k_radix_digit_scan(uint32_t* __restrict__ hist, int64_t nb,
+                                                          uint32_t* __restrict__ dtot)
+{
+    __shared__ uint32_t wsum[4];
+    uint32_t* row = hist + (int64_t)blockIdx.x * nb;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t seg = ((nb + 3) / 4 + 63) / 64 * 64;
+    const int64_t t0 = min(nb, (int64_t)wave * seg), t1 = min(nb, t0 + seg);
+    uint64_t s = 0;
+    for (int64_t c = t0; c < t1; c += 256) {
+        uint32_t a[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = c + 64 * u + lane < t1 ? row[c + 64 * u + lane] : 0u;
+        s += (uint64_t)a[0] + a[1] + a[2] + a[3];
+    }
+    s = gsd::wave_sum_u64(s);
+    if (lane == 0) wsum[wave] = (uint32_t)s;
+    __syncthreads();
+    uint32_t carry = 0;
+    for (int w = 0; w < wave; ++w) carry += wsum[w];
+    for (int64_t c = t0; c < t1; c += 64) {
+        const uint32_t v = c + lane < t1 ? row[c + lane] : 0u;
+        uint32_t x = v;
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t u = (uint32_t)__shfl_up((int)x, d, 64);
+            if (lane >= d) x += u;
+        }
+        if (c + lane < t1) row[c + lane] = carry + x - v;
+        carry += (uint32_t)__shfl((int)x, 63, 64);
+    }
+    if (threadIdx.x == 0) dtot[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
 // Stable scatter of one block's kRTile elements: (1) local ranks in element
 // order, (2) the block's elements placed digit-sorted in LDS, (3) written out
 // digit run by digit run, so that consecutive lanes write consecutive
@@ -69,7 +107,8 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* sh)
 template <int kRadix>
 __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restrict__ kin,
                                                        const uint32_t* __restrict__ vin, int64_t n, int shift,
-                                                       int bits, const uint32_t* __restrict__ hscan, int64_t nb,
+                                                       int bits, const uint32_t* __restrict__ hpre,
+                                                       const uint32_t* __restrict__ dtot, int64_t nb,
                                                        uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                        uint64_t* __restrict__ digit_off, int n_seg)
 {
@@ -83,14 +122,31 @@ __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restric
     const uint32_t mask = (1u << bits) - 1u;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint64_t lt = (1ull << lane) - 1ull;
-    for (int d = threadIdx.x; d < kRadix; d += kRB) {
-        run[d] = 0u;
-        gbase[d] = hscan[(int64_t)d * nb + blockIdx.x];
+    for (int d = threadIdx.x; d < kRadix; d += kRB) run[d] = 0u;
+    // output base of each digit for this block: the digit's start (exclusive
+    // scan of the digit totals; digits above the mask are empty) plus the
+    // earlier blocks' count of it.  A single pass over keys < n_seg also
+    // reports where each digit's run starts, and the total.
+    {
+        constexpr int P = kRadix / kRB;
+        uint32_t t[P];
+        uint32_t part = 0;
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int d = threadIdx.x * P + q;
+            t[q] = (uint32_t)d <= mask ? dtot[d] : 0u;
+            part += t[q];
+        }
+        uint32_t at = block_excl_scan256(part, scan_sh);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int d = threadIdx.x * P + q;
+            gbase[d] = at + ((uint32_t)d <= mask ? hpre[(int64_t)d * nb + blockIdx.x] : 0u);
+            if (digit_off && blockIdx.x == 0 && d < n_seg) digit_off[d] = at;
+            at += t[q];
+        }
+        if (digit_off && blockIdx.x == 0 && threadIdx.x == 0) digit_off[n_seg] = (uint64_t)n;
     }
-    // a single pass over keys < n_seg: where each digit's run starts in the
-    // output (the scan at block 0), and the total
-    if (digit_off && blockIdx.x == 0)
-        for (int d = threadIdx.x; d <= n_seg; d += kRB) digit_off[d] = hscan[(int64_t)d * nb];
     for (int q = threadIdx.x; q < (kRB / 64) * kRadix; q += kRB) (&wh[0][0])[q] = 0u;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kRTile;
@@ -184,8 +240,8 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
     const int radix = wide ? 1024 : 256;
     std::vector<GsAlloc> tmp;
     uint32_t* hist = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix * nb, GS_MEM_SCRATCH, &tmp);
-    uint32_t* hscan = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (radix * nb + 1), GS_MEM_SCRATCH, &tmp);
-    if (!hist || !hscan) {
+    uint32_t* dtot = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix, GS_MEM_SCRATCH, &tmp);
+    if (!hist || !dtot) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
@@ -205,17 +261,20 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
                 hipLaunchKernelGGL(k_radix_hist<256>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, n, shift,
                                    mask, hist, nb);
         }
-        // the digit-major histogram rows of the digits that occur
-        st = launch_scan_u32_to_u32(ctx, hist, hscan, (int64_t)(mask + 1u) * nb);
-        if (st != GS_OK) break;
+        {
+            // per digit that can occur: its row of block counts scanned in
+            // place, and its total
+            GsTimerScope ts(ctx, "radix");
+            hipLaunchKernelGGL(k_radix_digit_scan, dim3(mask + 1u), dim3(256), 0, ctx->stream, hist, nb, dtot);
+        }
         {
             GsTimerScope ts(ctx, "radix");
             if (wide)
                 hipLaunchKernelGGL(k_radix_scatter<1024>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n,
-                                   shift, bits, hscan, nb, ko, vo, want_off ? digit_off : nullptr, (int)n_seg);
+                                   shift, bits, hist, dtot, nb, ko, vo, want_off ? digit_off : nullptr, (int)n_seg);
             else
                 hipLaunchKernelGGL(k_radix_scatter<256>, dim3((unsigned)nb), dim3(kRB), 0, ctx->stream, ki, vi, n,
-                                   shift, bits, hscan, nb, ko, vo, nullptr, 0);
+                                   shift, bits, hist, dtot, nb, ko, vo, nullptr, 0);
         }
         std::swap(ki, ko);
         std::swap(vi, vo);
