@@ -227,7 +227,9 @@ def main():
         "pairs": {"examined": wc["q_f"], "included": wc["q_inc"], "backward": wc["q_b"], "sum_last": wc["sum_last"]},
         "kernel_ms_per_step": {k: round(v["total_ms"], 3) for k, v in ktimes.items()},
         "kernel_ms_note": "HIP events around every kernel in a separate attribution pass of "
-                          f"{args.attr_steps} steps before the timed steps",
+                          f"{args.attr_steps} steps before the timed steps, with the leaves binned in "
+                          "series (the timed steps bin each next leaf on a second stream during the "
+                          "current leaf's raster, so their step time is less than this sum)",
         "roofline": roofline,
         "rooflines_all": rooflines,
         "step_hbm": {"algorithmic_bytes": int(step_bytes), "frac_of_8TBps": round(hbm_frac_step, 4)},

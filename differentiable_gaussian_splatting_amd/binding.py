@@ -174,7 +174,8 @@ class Context:
 
         def _alloc(user, nbytes, strm):
             try:
-                return torch.cuda.caching_allocator_alloc(int(nbytes), dev_index, raw_stream)
+                # stream-ordered on the stream the library allocates for
+                return torch.cuda.caching_allocator_alloc(int(nbytes), dev_index, strm if strm else raw_stream)
             except Exception:   # the library turns NULL into GS_ERR_OOM
                 traceback.print_exc()
                 return None

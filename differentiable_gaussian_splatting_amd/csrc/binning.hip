@@ -745,10 +745,13 @@ int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells)
     return super_cells(leaf) + (int64_t)((n_cells + kSeg - 1) / kSeg);
 }
 
-gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
-                            const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint64_t* toff,
-                            uint32_t* item_sc, uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values)
+// items, their per-tile counts and the write positions (everything of the
+// fine level before the slot array is written)
+gs_status launch_fine_prepare(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
+                              const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint64_t* toff,
+                              uint32_t* item_sc, uint32_t* ioff, uint32_t* pos)
 {
+    (void)proj;
     const int n_super = (int)super_cells(leaf);
     const int64_t items = fine_items_bound(leaf, n_cells);
     if (n_super <= 0 || n_cells == 0) return GS_OK;
@@ -756,17 +759,41 @@ gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
     GsTimerScope ts(ctx, "fine");
     hipLaunchKernelGGL(k_fine_items, dim3(1), dim3(1024), 0, ctx->stream, soff, n_super, ioff, item_sc);
     hipLaunchKernelGGL((k_fine<false, false>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0,
-                       TWL, THL, SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
+                       TWL, THL, SW, n_super, soff, ioff, item_sc, group, gkey, pos, 0ull, nullptr);
     hipLaunchKernelGGL(k_fine_scan, dim3((unsigned)ceil_div((int64_t)n_super * 64, 256)), dim3(256), 0, ctx->stream,
                        leaf.tx0, leaf.ty0, TWL, THL, SW, n_super, ioff, toff, pos);
-    if (n_values < (1ull << 30))
-        hipLaunchKernelGGL((k_fine<true, true>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                           SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
-    else
-        hipLaunchKernelGGL((k_fine<true, false>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0, TWL, THL,
-                           SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
+}
+
+// the slot array from the prepared items and positions
+gs_status launch_fine_write(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
+                            const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint32_t* item_sc,
+                            const uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values)
+{
+    (void)proj;
+    const int n_super = (int)super_cells(leaf);
+    const int64_t items = fine_items_bound(leaf, n_cells);
+    if (n_super <= 0 || n_cells == 0) return GS_OK;
+    const int TWL = leaf.tx1 - leaf.tx0, THL = leaf.ty1 - leaf.ty0, SW = super_cols(leaf);
+    GsTimerScope ts(ctx, "fine");
+    if (n_values < (1ull << 30))
+        hipLaunchKernelGGL((k_fine<true, true>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0, leaf.ty0,
+                           TWL, THL, SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
+    else
+        hipLaunchKernelGGL((k_fine<true, false>), dim3((unsigned)items), dim3(256), 0, ctx->stream, leaf.tx0,
+                           leaf.ty0, TWL, THL, SW, n_super, soff, ioff, item_sc, group, gkey, pos, n_values, values);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
+                            const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint64_t* toff,
+                            uint32_t* item_sc, uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values)
+{
+    gs_status st = launch_fine_prepare(ctx, proj, leaf, soff, group, gkey, n_cells, toff, item_sc, ioff, pos);
+    if (st != GS_OK) return st;
+    return launch_fine_write(ctx, proj, leaf, soff, group, gkey, n_cells, item_sc, ioff, pos, n_values, values);
 }
 
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint32_t kmask,

@@ -376,6 +376,13 @@ void gs_ctx_destroy(gs_ctx* ctx)
 {
     if (!ctx) return;
     (void)hipStreamSynchronize(ctx->stream);
+    if (ctx->side) {
+        (void)hipStreamSynchronize(ctx->side);
+        (void)hipStreamDestroy(ctx->side);
+    }
+    if (ctx->ev_alloc) (void)hipEventDestroy(ctx->ev_alloc);
+    for (hipEvent_t e : ctx->ev_done)
+        if (e) (void)hipEventDestroy(e);
     for (auto& t : ctx->timers) {
         (void)hipEventDestroy(t.start);
         (void)hipEventDestroy(t.stop);
@@ -592,6 +599,133 @@ gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj,
 
 // ---------------------------------------------------------------------------
 // binning
+
+// ---------------------------------------------------------------------------
+// Binning of a planned leaf in two stages, so that gs_train_view can bin the
+// next leaf on a second stream while the current one is rendered:
+//   coarse_alloc (main stream): every buffer the first stage needs;
+//   coarse_launch (any stream, allocates nothing): emission, the coarse sort,
+//     the super-tile group offsets, the fine items, counts and positions;
+//   fine_finish (main stream): the slot array, the bins handle, and the
+//     release of the stage's buffers.
+// The same kernels and launch shapes as gs_bin_sort.
+struct CoarseBins {
+    gs_tile_rect leaf{};
+    PlanLeaf pl{};
+    int64_t n_super = 0, items = 0;
+    uint64_t C = 0, I = 0;
+    uint32_t *k0 = nullptr, *v0 = nullptr, *k1 = nullptr, *v1 = nullptr;
+    uint32_t *item_sc = nullptr, *ioff = nullptr, *pos = nullptr, *scratch = nullptr;
+    uint64_t* soff = nullptr;
+    bool second = false;
+    std::vector<GsAlloc> allocs;
+};
+
+static bool leaf_pipelinable(const gs_proj* proj, gs_tile_rect leaf)
+{
+    const PlanLeaf pl = plan_leaf(proj, leaf);
+    return pl.found && pl.isect >= 0 && super_cells(leaf) < super_cells_max() && (uint64_t)pl.isect < (1ull << 32) &&
+           (uint64_t)pl.cells < (1ull << 32);
+}
+
+static gs_status coarse_alloc(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, CoarseBins* cb)
+{
+    cb->leaf = leaf;
+    cb->pl = plan_leaf(proj, leaf);
+    cb->n_super = super_cells(leaf);
+    cb->C = (uint64_t)cb->pl.cells;
+    cb->I = (uint64_t)cb->pl.isect;
+    cb->items = fine_items_bound(leaf, cb->C);
+    const uint64_t nc = std::max<uint64_t>(cb->C, 1);
+    auto get = [&](size_t bytes) { return gs_malloc(ctx, bytes, GS_MEM_RASTER, &cb->allocs); };
+    cb->k0 = (uint32_t*)get(sizeof(uint32_t) * nc);
+    cb->v0 = (uint32_t*)get(sizeof(uint32_t) * nc);
+    cb->k1 = (uint32_t*)get(sizeof(uint32_t) * nc);
+    cb->v1 = (uint32_t*)get(sizeof(uint32_t) * nc);
+    cb->soff = (uint64_t*)get(sizeof(uint64_t) * (cb->n_super + 1));
+    cb->item_sc = (uint32_t*)get(sizeof(uint32_t) * cb->items);
+    cb->ioff = (uint32_t*)get(sizeof(uint32_t) * (cb->n_super + 1));
+    cb->pos = (uint32_t*)get(sizeof(uint32_t) * 64 * cb->items);
+    cb->scratch = (uint32_t*)get(sizeof(uint32_t) * radix_scratch_words((int64_t)cb->C));
+    if (!cb->k0 || !cb->v0 || !cb->k1 || !cb->v1 || !cb->soff || !cb->item_sc || !cb->ioff || !cb->pos ||
+        !cb->scratch) {
+        gs_free_all(ctx, &cb->allocs);
+        return GS_ERR_OOM;
+    }
+    return GS_OK;
+}
+
+static gs_status coarse_launch(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb)
+{
+    gs_status st = launch_emit_cells(ctx, proj, cb->leaf, cb->pl.list, cb->pl.n, cb->pl.eoff, cb->pl.ebase, cb->C,
+                                     cb->k0, cb->v0);
+    if (st != GS_OK) return st;
+    bool have_soff = false;
+    if ((st = launch_radix_sort(ctx, cb->k0, cb->v0, cb->k1, cb->v1, (int64_t)cb->C, bits_for(cb->n_super),
+                                &cb->second, cb->soff, cb->n_super, &have_soff, cb->scratch)) != GS_OK)
+        return st;
+    const uint32_t* gkey = cb->second ? cb->k1 : cb->k0;
+    const uint32_t* group = cb->second ? cb->v1 : cb->v0;
+    if (!have_soff &&
+        (st = launch_seg_offsets(ctx, gkey, (int64_t)cb->C, cb->n_super, super_key_mask(), cb->soff)) != GS_OK)
+        return st;
+    return launch_fine_prepare(ctx, proj, cb->leaf, cb->soff, group, gkey, cb->C, cb->pl.toff, cb->item_sc, cb->ioff,
+                               cb->pos);
+}
+
+static gs_status fine_finish(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb, gs_bins** out)
+{
+    gs_bins* b = new_handle<gs_bins>(ctx, kMagicBins);
+    if (!b) {
+        gs_free_all(ctx, &cb->allocs);
+        return gs_fail(ctx, GS_ERR_OOM, "host allocation failed");
+    }
+    b->proj = proj;
+    b->leaf = cb->leaf;
+    b->TWL = cb->leaf.tx1 - cb->leaf.tx0;
+    b->THL = cb->leaf.ty1 - cb->leaf.ty0;
+    b->n_tiles = (int64_t)b->TWL * b->THL;
+    b->offsets = cb->pl.toff;
+    b->n_isect = (int64_t)cb->I;
+    b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(cb->I, 1), GS_MEM_RASTER, &b->allocs);
+    gs_status st = b->values ? GS_OK : GS_ERR_OOM;
+    if (st == GS_OK)
+        st = launch_fine_write(ctx, proj, cb->leaf, cb->soff, cb->second ? cb->v1 : cb->v0,
+                               cb->second ? cb->k1 : cb->k0, cb->C, cb->item_sc, cb->ioff, cb->pos, cb->I, b->values);
+    gs_free_all(ctx, &cb->allocs);   // stream-ordered after the write
+    if (st != GS_OK) {
+        destroy_handle(ctx, b);
+        return st;
+    }
+    *out = b;
+    return GS_OK;
+}
+
+// the side stream and its events, made on first use
+static gs_status ensure_side(gs_ctx* ctx)
+{
+    if (ctx->side) return GS_OK;
+    GS_HIP(ctx, hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_alloc, hipEventDisableTiming));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[0], hipEventDisableTiming));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[1], hipEventDisableTiming));
+    return GS_OK;
+}
+
+// stage one of leaf cb on the side stream, after everything the main stream
+// has queued so far (its buffers may reuse memory the main stream freed)
+static gs_status coarse_on_side(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb, hipEvent_t done)
+{
+    GS_HIP(ctx, hipEventRecord(ctx->ev_alloc, ctx->stream));
+    GS_HIP(ctx, hipStreamWaitEvent(ctx->side, ctx->ev_alloc, 0));
+    hipStream_t main = ctx->stream;
+    ctx->stream = ctx->side;
+    const gs_status st = coarse_launch(ctx, proj, cb);
+    ctx->stream = main;
+    if (st != GS_OK) return st;
+    GS_HIP(ctx, hipEventRecord(done, ctx->side));
+    return GS_OK;
+}
 
 gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs_tile_rect leaf, gs_bins** out,
                       int64_t* n_isect)
@@ -979,7 +1113,20 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     double* l1_view = opts->loss_kind == 0 && l1_n > 0
                           ? (double*)gs_malloc(ctx, sizeof(double) * l1_n, GS_MEM_LOSS, &view)
                           : nullptr;
+    // Binning of a leaf runs on a second stream while the previous leaf is
+    // rendered, when every leaf is planned (no host read-back in binning)
+    // (not while every kernel is timed: the per-kernel times would then
+    // include the waits of kernels sharing the GPU)
+    CoarseBins cbs[2];
+    bool pipe = leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
+    for (const gs_leaf& L : leaves) pipe = pipe && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
     if (!grad2d || !loss_dev || (opts->loss_kind == 0 && l1_n > 0 && !l1_view)) { st = GS_ERR_OOM; goto done; }
+    if (pipe) {
+        const gs_leaf& L = leaves[0];
+        if ((st = ensure_side(ctx)) != GS_OK) goto done;
+        if ((st = coarse_alloc(ctx, proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, &cbs[0])) != GS_OK) goto done;
+        if ((st = coarse_on_side(ctx, proj, &cbs[0], ctx->ev_done[0])) != GS_OK) goto done;
+    }
     if ((st = launch_fill_f32(ctx, grad2d, 0.0f, 9 * nc)) != GS_OK) goto done;
     if (hipMemsetAsync(loss_dev, 0, sizeof(double), ctx->stream) != hipSuccess) {
         st = gs_fail(ctx, GS_ERR_DEVICE, "memset failed");
@@ -990,12 +1137,35 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         dl_dimage = (float*)gs_malloc(ctx, sizeof(float) * 3 * P, GS_MEM_LOSS, &view);
         if (!image || !dl_dimage) { st = GS_ERR_OOM; goto done; }
     }
-    for (const gs_leaf& L : leaves) {
+    for (size_t li = 0; li < leaves.size(); ++li) {
+        const gs_leaf& L = leaves[li];
         gs_bins* bins = nullptr;
         gs_raster* ras = nullptr;
         int64_t ni = 0;
         gs_tile_rect r{L.tx0, L.ty0, L.tx1, L.ty1};
-        if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
+        if (pipe) {
+            // this leaf's first stage is done on the side stream; its slot
+            // array is written here, and the next leaf's first stage starts
+            // on the side stream behind everything queued so far
+            if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
+                st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
+                goto done;
+            }
+            if ((st = fine_finish(ctx, proj, &cbs[li & 1], &bins)) != GS_OK) goto done;
+            ni = bins->n_isect;
+            if (li + 1 < leaves.size()) {
+                const gs_leaf& N = leaves[li + 1];
+                CoarseBins& nx = cbs[(li + 1) & 1];
+                if ((st = coarse_alloc(ctx, proj, gs_tile_rect{N.tx0, N.ty0, N.tx1, N.ty1}, &nx)) == GS_OK)
+                    st = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
+                if (st != GS_OK) {
+                    gs_release(ctx, bins);
+                    goto done;
+                }
+            }
+        } else if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) {
+            goto done;
+        }
         isect_total += ni;
         if (opts->loss_kind == 0) {
             st = render_fwd(ctx, cam, proj, bins, target, loss_dev, image, nullptr, l1_view + l1_off, &ras);
@@ -1067,6 +1237,11 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     result->n_leaves = (int32_t)leaves.size();
     result->peak_bytes = ctx->peak - live0;
 done:
+    if (pipe) {
+        // nothing may be freed while the side stream could still use it
+        (void)hipStreamSynchronize(ctx->side);
+        for (CoarseBins& cb : cbs) gs_free_all(ctx, &cb.allocs);
+    }
     gs_free_all(ctx, &view);
     gs_release(ctx, proj);
     ctx->peak = std::max(ctx->peak, peak_before);

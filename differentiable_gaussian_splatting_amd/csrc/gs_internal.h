@@ -36,6 +36,10 @@ struct gs_ctx {
     std::vector<GsTimerRec> timers;
     std::vector<hipEvent_t> event_pool;
     void* pinned = nullptr;        // small pinned host buffer for count read-backs
+    // second stream (default priority, non-blocking) on which gs_train_view
+    // bins the next leaf while the current one is rendered, and its events
+    hipStream_t side = nullptr;
+    hipEvent_t ev_alloc = nullptr, ev_done[2] = {nullptr, nullptr};
     int num_cu = 256;
     size_t max_lds = 65536;
 };
@@ -167,6 +171,14 @@ int64_t fine_items_bound(gs_tile_rect leaf, uint64_t n_cells);
 gs_status launch_fine_lists(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
                             const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint64_t* toff,
                             uint32_t* item_sc, uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values);
+// the two halves of launch_fine_lists: items, counts and write positions;
+// then the slot array
+gs_status launch_fine_prepare(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
+                              const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint64_t* toff,
+                              uint32_t* item_sc, uint32_t* ioff, uint32_t* pos);
+gs_status launch_fine_write(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint64_t* soff,
+                            const uint32_t* group, const uint32_t* gkey, uint64_t n_cells, const uint32_t* item_sc,
+                            const uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values);
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint32_t kmask,
                              uint64_t* offsets);
 gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
@@ -176,7 +188,8 @@ int bits_for(int64_t n_keys);
 // radix.hip: stable sort of (u32 key, u32 value) pairs on the low key_bits bits
 gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n,
                             int key_bits, bool* in_second, uint64_t* digit_off = nullptr, int64_t n_seg = 0,
-                            bool* off_written = nullptr);
+                            bool* off_written = nullptr, uint32_t* scratch = nullptr);
+int64_t radix_scratch_words(int64_t n);
 
 // raster.hip
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,

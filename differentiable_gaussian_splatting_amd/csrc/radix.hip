@@ -226,9 +226,16 @@ __global__ __launch_bounds__(kRB) void k_radix_scatter(const uint32_t* __restric
 // digit_off (optional, n_seg + 1 entries): when the sort takes a single pass
 // and every key's low bits are < n_seg, the first output position of each
 // value s in [0, n_seg) and the total are written there, and *off_written is
-// set.
+// set.  scratch (optional, radix_scratch_words(n) u32): the histogram and
+// digit totals; without it the sort allocates them on ctx->stream.
+int64_t radix_scratch_words(int64_t n)
+{
+    return 1024 * ceil_div(std::max<int64_t>(n, 1), kRTile) + 1024;
+}
+
 gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int64_t n,
-                            int key_bits, bool* in_second, uint64_t* digit_off, int64_t n_seg, bool* off_written)
+                            int key_bits, bool* in_second, uint64_t* digit_off, int64_t n_seg, bool* off_written,
+                            uint32_t* scratch)
 {
     *in_second = false;
     if (off_written) *off_written = false;
@@ -239,8 +246,10 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
     const bool wide = key_bits <= 10;
     const int radix = wide ? 1024 : 256;
     std::vector<GsAlloc> tmp;
-    uint32_t* hist = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix * nb, GS_MEM_SCRATCH, &tmp);
-    uint32_t* dtot = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix, GS_MEM_SCRATCH, &tmp);
+    uint32_t* hist = scratch ? scratch
+                             : (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix * nb, GS_MEM_SCRATCH, &tmp);
+    uint32_t* dtot = scratch ? scratch + 1024 * nb
+                             : (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix, GS_MEM_SCRATCH, &tmp);
     if (!hist || !dtot) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;

@@ -336,7 +336,11 @@ typedef struct {
  * page "01", Fig. 3, Fig. 5 conclusion).  With Adam and no grad3d_out the
  * projection backward and the update run as one fused pass over the
  * Gaussians (adam_chunk 0), or chunk by chunk of candidate slots; both give
- * the result of gs_project_bwd followed by gs_adam_step.  target: device
+ * the result of gs_project_bwd followed by gs_adam_step.  With more than
+ * one planned leaf, the binning of each next leaf up to its slot array runs
+ * on a second stream of the library (default priority, created on first use)
+ * while the current leaf is rendered, ordered by events; not while every
+ * kernel is timed (gs_set_timing on, no gs_set_timing_only).  target: device
  * [3][H][W].  Synchronises. */
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result);

@@ -139,6 +139,58 @@ def test_train_view_entry_point(ctx):
     assert r["n_cand"] == o["n_cand"] and r["n_isect"] == o["n_isect"]
 
 
+@pytest.mark.parametrize("seed,budget", [(109, 2_500_000), (110, 1_400_000)])
+def test_train_view_leaves_pipelined(ctx, seed, budget):
+    """gs_train_view over several planned leaves bins each next leaf on a
+    second stream while the current one is rendered: loss, image, leaves,
+    intersections and every 3D gradient group against the oracle's leaf mode,
+    and the fused update against the oracle's Adam step."""
+    import torch
+    w = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, seed=seed)
+    cost = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
+    ds = B.DeviceScene(w.scene, ctx.device)
+    target = torch.from_numpy(w.target).to(ctx.device)
+    K = (w.scene.sh_degree + 1) ** 2
+    g3 = torch.zeros((w.scene.n, 11 + 3 * K), dtype=torch.float32, device=ctx.device)
+    img = torch.zeros((3, w.camera.height, w.camera.width), dtype=torch.float32, device=ctx.device)
+    r = B.gs_train_view(ctx, w.camera, ds, target, budget_bytes=budget, cost=cost, image_out=img, grad3d_out=g3,
+                        max_leaves=64)
+    o = oracle.train_view(w.camera, w.scene, w.target, budget=budget, cost=cost)
+    say(f"case seed {seed} budget {budget}: {r['n_leaves']} leaves")
+    assert r["n_leaves"] == len(o["leaves"]) and r["n_leaves"] > 2
+    got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in r["leaves"]]
+    assert got == [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in o["leaves"]]
+    assert r["n_isect"] == o["n_isect"]
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    assert np.abs(img.cpu().numpy() - o["image"]).max() <= IMG_TOL
+    gg, og = grad3d_groups(g3.cpu().numpy(), 3), grad3d_groups(o["grad3d"], 3)
+    for name in gg:
+        e = rel_l2(gg[name], og[name])
+        say(f"  grad3d {name:10s} rel L2 {e:.2e}")
+        assert e <= GRAD_TOL, name
+    # the same view with the fused update
+    rng = np.random.default_rng(seed)
+    m0 = [rng.normal(0, 1e-3, size=t.shape) for t in w.scene.arrays()]
+    v0 = [rng.uniform(0, 1e-6, size=t.shape) for t in w.scene.arrays()]
+    ds2 = B.DeviceScene(w.scene, ctx.device)
+    m, v = B.like_scene(ds2), B.like_scene(ds2)
+    for dst, src in zip(m.tensors(), m0):
+        dst.copy_(torch.from_numpy(src.astype(np.float32)))
+    for dst, src in zip(v.tensors(), v0):
+        dst.copy_(torch.from_numpy(src.astype(np.float32)))
+    r2 = B.gs_train_view(ctx, w.camera, ds2, target, budget_bytes=budget, cost=cost,
+                         adam=dict(step=2, params=ds2, m=m, v=v))
+    assert abs(r2["loss"] - o["loss"]) <= LOSS_TOL
+    groups = grad3d_groups(o["grad3d"], 3)
+    for k, (t, name) in enumerate(zip(ds2.tensors(), ["means", "log_scales", "quats", "logits", "sh"])):
+        p0 = w.scene.arrays()[k].astype(np.float64)
+        p, mm, vv = oracle.adam(groups[name].reshape(p0.shape), p0, m0[k].astype(np.float32),
+                                v0[k].astype(np.float32), step=2)
+        got = t.cpu().numpy().astype(np.float64)
+        ulp = np.spacing(np.abs(p).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - p) <= 1e-3 * np.abs(p - p0) + 2 * ulp), name
+
+
 def test_adam_step_matches_oracle(ctx):
     import torch
     w = scenes.make_workload("c2_hd", n=5000, width=200, height=150, posed=True, seed=107)
