@@ -139,14 +139,25 @@ def test_train_view_entry_point(ctx):
     assert r["n_cand"] == o["n_cand"] and r["n_isect"] == o["n_isect"]
 
 
-@pytest.mark.parametrize("seed,budget", [(109, 2_500_000), (110, 1_400_000)])
-def test_train_view_leaves_pipelined(ctx, seed, budget):
+@pytest.mark.parametrize("seed,budget,corner", [(109, 2_500_000, False), (110, 1_400_000, False),
+                                               (111, 1_400_000, True)])
+def test_train_view_leaves_pipelined(ctx, seed, budget, corner):
     """gs_train_view over several planned leaves bins each next leaf on a
     second stream while the current one is rendered: loss, image, leaves,
     intersections and every 3D gradient group against the oracle's leaf mode,
-    and the fused update against the oracle's Adam step."""
+    and the fused update against the oracle's Adam step.  In the corner case
+    every centre projects into the top-left ninth of the image, so the leaves
+    planned over the rest of it hold few or no intersections."""
     import torch
     w = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, seed=seed)
+    if corner:
+        c, sc = w.camera, w.scene
+        pc = sc.means.astype(np.float64) @ c.R.T.astype(np.float64) + c.t
+        u = c.fx * pc[:, 0] / pc[:, 2] + c.cx
+        v = c.fy * pc[:, 1] / pc[:, 2] + c.cy
+        keep = (pc[:, 2] > 1.0) & (u < c.width / 3) & (v < c.height / 3)
+        assert keep.sum() > 500
+        w.scene = scenes.Scene(*(a[keep] for a in sc.arrays()), sh_degree=sc.sh_degree)
     cost = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
     ds = B.DeviceScene(w.scene, ctx.device)
     target = torch.from_numpy(w.target).to(ctx.device)
@@ -155,9 +166,13 @@ def test_train_view_leaves_pipelined(ctx, seed, budget):
     img = torch.zeros((3, w.camera.height, w.camera.width), dtype=torch.float32, device=ctx.device)
     r = B.gs_train_view(ctx, w.camera, ds, target, budget_bytes=budget, cost=cost, image_out=img, grad3d_out=g3,
                         max_leaves=64)
-    o = oracle.train_view(w.camera, w.scene, w.target, budget=budget, cost=cost)
-    say(f"case seed {seed} budget {budget}: {r['n_leaves']} leaves")
+    o = oracle.train_view(w.camera, w.scene, w.target, budget=budget, cost=cost, keep_bins=corner)
+    say(f"case seed {seed} budget {budget} corner {corner}: {r['n_leaves']} leaves")
     assert r["n_leaves"] == len(o["leaves"]) and r["n_leaves"] > 2
+    if corner:
+        per_leaf = [b["n_isect"] for b in o["bins"]]
+        say(f"  intersections per leaf {per_leaf}")
+        assert min(per_leaf) == 0 and max(per_leaf) > 0
     got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in r["leaves"]]
     assert got == [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in o["leaves"]]
     assert r["n_isect"] == o["n_isect"]
