@@ -71,6 +71,7 @@ def _declare(L):
     L.gso_exp_cw.restype = C.c_float
     L.gso_exp_cw.argtypes = [C.c_float]
     L.gso_exp_cw_array.argtypes = [vp, vp, i64]
+    L.gso_exp_falloff_array.argtypes = [vp, vp, i64]
     L.gso_sh_basis_f32.argtypes = [C.c_int, vp, vp, i64]
     L.gso_sh_basis_f64.argtypes = [C.c_int, vp, vp, i64]
     proj = [C.POINTER(Camera_c), i64, C.c_int] + [vp] * 5 + [vp] * 9
@@ -129,6 +130,14 @@ def exp_cw(x):
     x = _c(x, np.float32)
     y = np.empty_like(x)
     lib().gso_exp_cw_array(_p(x), _p(y), x.size)
+    return y
+
+
+def exp_falloff(x):
+    """exp of the Gaussian falloff as the f32 compositing pass takes it."""
+    x = _c(x, np.float32)
+    y = np.empty_like(x)
+    lib().gso_exp_falloff_array(_p(x), _p(y), x.size)
     return y
 
 

@@ -73,12 +73,54 @@ void gso_exp_cw_array(const float* x, float* y, int64_t n)
     for (int64_t i = 0; i < n; ++i) y[i] = gso_exp_cw(x[i]);
 }
 
+/* exp_falloff: the f32 exp of the Gaussian falloff in alpha = min(0.99,
+ * o exp(power)).  Since o <= 1, alpha >= 1/255 needs power > -ln 255 = -5.54,
+ * so the argument is first clamped into [-6, 0]: below -6 every pixel skips
+ * the entry whatever the value (o exp(-6) < 1/255), above 0 the entry is
+ * skipped before exp is taken.  On [-6, 0]:
+ *   k = x log2 e rounded once to the nearest integer (ties to even), taken
+ *       from t = fma(x, log2 e, 1.5 * 2^23): at that magnitude the f32 ulp is
+ *       1, so t - 1.5 * 2^23 is exactly that integer;
+ *   r = fma(-k, ln2, x) with ln 2 rounded to f32 (|k| <= 9 keeps the error of
+ *       the one-constant reduction below 2e-8);
+ *   e^r by the degree-7 Taylor polynomial in Horner form (fma), 1/n! in f32;
+ *   result ldexp(p, k).
+ * Within 1 ulp of exp on [-6, 0].  NaN gives an unspecified value.        */
+float gso_exp_falloff(float x)
+{
+    static int init = 0;
+    static float c[8];
+    if (!init) {
+        double fact = 1.0;
+        for (int k = 0; k < 8; ++k) {
+            if (k > 0) fact *= k;
+            c[k] = (float)(1.0 / fact);
+        }
+        init = 1;
+    }
+    if (x < -6.0f) x = -6.0f;
+    if (x > 0.0f) x = 0.0f;
+    const float magic = 12582912.0f;                        /* 1.5 * 2^23 */
+    const float t = fmaf(x, 1.44269504088896340736f, magic);
+    const float k = t - magic;
+    const float r = fmaf(-k, (float)0.693147180559945309417232121458, x);
+    float p = c[7];
+    for (int i = 6; i >= 0; --i) p = fmaf(p, r, c[i]);
+    return ldexpf(p, (int)k);
+}
+
+void gso_exp_falloff_array(const float* x, float* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = gso_exp_falloff(x[i]);
+}
+
 /* ---------------------------------------------------------------------- */
 /* The REAL-generic forward arithmetic, compiled in f32 and in f64.        */
 #define SFX(name) name##_f32
 #define REAL float
 #define LIT(x) x##f
 #define EXPF(x) gso_exp_cw(x)
+#define EXP_FALLOFF(x) gso_exp_falloff(x)
 #define SQRTF(x) sqrtf(x)
 #define CEILF(x) ceilf(x)
 #define FLOORF(x) floorf(x)
@@ -89,6 +131,7 @@ void gso_exp_cw_array(const float* x, float* y, int64_t n)
 #undef REAL
 #undef LIT
 #undef EXPF
+#undef EXP_FALLOFF
 #undef SQRTF
 #undef CEILF
 #undef FLOORF
@@ -98,6 +141,7 @@ void gso_exp_cw_array(const float* x, float* y, int64_t n)
 #define REAL double
 #define LIT(x) x
 #define EXPF(x) exp(x)
+#define EXP_FALLOFF(x) exp(x)
 #define SQRTF(x) sqrt(x)
 #define CEILF(x) ceil(x)
 #define FLOORF(x) floor(x)
@@ -107,6 +151,7 @@ void gso_exp_cw_array(const float* x, float* y, int64_t n)
 #undef REAL
 #undef LIT
 #undef EXPF
+#undef EXP_FALLOFF
 #undef SQRTF
 #undef CEILF
 #undef FLOORF

@@ -83,6 +83,10 @@ typedef struct {          /* leaf load model: bytes = bI*I + bP*P + bT*T + b0 + 
 /* exp by Cody-Waite reduction + degree-7 Taylor/Horner (f32, as specified) */
 float gso_exp_cw(float x);
 void  gso_exp_cw_array(const float* x, float* y, int64_t n);
+/* exp of the Gaussian falloff in alpha (f32 pass of the rasterizer): the
+ * argument clamped into [-6, 0], one-constant reduction, degree-7 Taylor */
+float gso_exp_falloff(float x);
+void  gso_exp_falloff_array(const float* x, float* y, int64_t n);
 /* real orthonormal SH basis (no Condon-Shortley phase), order l then m=-l..l */
 void  gso_sh_basis_f32(int deg, const float* dirs, float* Y, int64_t n);
 void  gso_sh_basis_f64(int deg, const double* dirs, double* Y, int64_t n);

@@ -22,6 +22,31 @@ def test_exp_cw_within_2ulp_of_libm(oracle_lib):
     assert ulp_diff(y, ref).max() <= 2.0
 
 
+def test_exp_falloff_within_1ulp_of_libm(oracle_lib):
+    # a dense sweep of [-6, 0] plus every f32 in three windows: around 0, around
+    # a rounding boundary of k (x log2 e = -0.5) and at the bottom of the range
+    x = np.linspace(-6.0, 0.0, 3_000_001, dtype=np.float32)
+    wins = []
+    for c in (np.float32(-1e-6), np.float32(-0.5 / 1.4426950408889634), np.float32(-5.9999)):
+        u = c.view(np.uint32)
+        wins.append(np.arange(u - 200_000, u + 200_000, dtype=np.uint32).view(np.float32))
+    x = np.concatenate([x] + wins)
+    x = x[(x >= -6.0) & (x <= 0.0)]
+    y = oracle_lib.exp_falloff(x)
+    assert ulp_diff(y, np.exp(x.astype(np.float64))).max() <= 1.0
+
+
+def test_exp_falloff_clamp_keeps_every_skip_decision(oracle_lib):
+    y = oracle_lib.exp_falloff(np.array([0.0, -0.0, 0.5, 1e30, -6.0, -6.5, -87.0, -1e30], np.float32))
+    assert y[0] == 1.0 and y[1] == 1.0 and y[2] == 1.0 and y[3] == 1.0
+    assert y[5] == y[4] and y[6] == y[4] and y[7] == y[4]
+    # below -6 the value stands in for exp(x) < exp(-6): any opacity <= 1 times
+    # it stays under the 1/255 threshold, so the entry is skipped either way,
+    # while the largest power that can be included (-ln 255) is inside the range
+    assert np.float32(1.0) * y[4] < np.float32(1.0) / np.float32(255.0)
+    assert -np.log(255.0) > -6.0
+
+
 def test_exp_cw_special_values(oracle_lib):
     x = np.array([0.0, -0.0, -87.5, -1e30, 89.0, np.inf, -np.inf, 1.0], np.float32)
     y = oracle_lib.exp_cw(x)
