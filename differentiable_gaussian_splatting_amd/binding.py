@@ -142,6 +142,7 @@ def load(path: str = LIB_PATH):
         "gs_export": (st, [vp, vp, i32, vp, C.c_size_t]),
         "gs_export_size": (st, [vp, vp, i32, P(C.c_size_t)]),
         "gs_util_exp": (st, [vp, vp, vp, i64]),
+        "gs_util_exp_falloff": (st, [vp, vp, vp, i64]),
         "gs_train_view": (st, [vp, P(gs_camera), P(gs_params), vp, P(gs_view_opts), P(gs_view_result)]),
     }
     for name, (res, args) in sig.items():
@@ -365,6 +366,12 @@ def gs_export(ctx: Context, handle, field: int):
 def gs_util_exp(ctx: Context, x):
     y = x.new_empty(x.shape)
     ctx.check(ctx.lib.gs_util_exp(ctx.handle, _ptr(x), _ptr(y), x.numel()))
+    return y
+
+
+def gs_util_exp_falloff(ctx: Context, x):
+    y = x.new_empty(x.shape)
+    ctx.check(ctx.lib.gs_util_exp_falloff(ctx.handle, _ptr(x), _ptr(y), x.numel()))
     return y
 
 

@@ -1047,7 +1047,14 @@ gs_status gs_util_exp(gs_ctx* ctx, const float* x, float* y, int64_t n)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     if (n < 0 || (n > 0 && (!x || !y))) return gs_fail(ctx, GS_ERR_INVALID_ARG, "gs_util_exp arguments");
-    return launch_exp(ctx, x, y, n);
+    return launch_exp(ctx, x, y, n, false);
+}
+
+gs_status gs_util_exp_falloff(gs_ctx* ctx, const float* x, float* y, int64_t n)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (n < 0 || (n > 0 && (!x || !y))) return gs_fail(ctx, GS_ERR_INVALID_ARG, "gs_util_exp_falloff arguments");
+    return launch_exp(ctx, x, y, n, true);
 }
 
 // ---------------------------------------------------------------------------

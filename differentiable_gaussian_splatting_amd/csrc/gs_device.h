@@ -23,8 +23,7 @@ namespace gsd {
 //   (Horner, fma); result = ldexp(p, k).
 // ln2_hi is ln 2 rounded to f32 with its 12 low significand bits cleared, so
 // that k * ln2_hi is exact for |k| < 2^12; ln2_lo = f32(ln 2 - ln2_hi).
-// Within 2 ulp of exp over [-87, 88].  The compositing rule evaluates it at
-// power <= 0 only; callers skip power < -87, where it returns 0 (alpha = 0).
+// Within 2 ulp of exp over [-87, 88].
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2Hi = __builtin_bit_cast(
     float, __builtin_bit_cast(uint32_t, 0.693147180559945309417232121458f) & 0xFFFFF000u);
@@ -51,6 +50,53 @@ __device__ __forceinline__ float exp_cw_core(float x)
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
     return __builtin_ldexpf(p, (int)k);
+}
+
+// exp of the Gaussian falloff, for the rasterizer's alpha.  The argument is
+// clamped into [-6, 0] first: an entry is included only where
+// o exp(power) >= 1/255 with o <= 1, i.e. power > -ln 255 = -5.54, so below -6
+// every lane skips the entry whatever value is returned, and above 0 the
+// caller skips it too.  On [-6, 0], k is in [-9, 0], which allows
+//   t = fma(x, log2 e, 1.5 2^23)   (the sum's ulp is 1: t - 1.5 2^23 is x log2 e
+//                                  rounded to the nearest integer k, ties to even)
+//   r = fma(-k, ln2, x)            (one f32 ln 2: |k (ln2 - ln2_f32)| < 2e-8)
+//   e^r by the degree-7 Taylor polynomial (Horner, fma)
+//   result = p 2^k, formed by adding k to p's exponent field: the low 9 bits of
+//   t's pattern above the significand are those of 1.5 2^23, so (bits(t) << 23)
+//   is k << 23 modulo 2^32, and p 2^k stays normal.
+// Within 1 ulp of exp over [-6, 0] (every f32 there checked against libm).
+// The rasterizer tests the range itself (falloff_in_range) and calls the core
+// unclamped: lanes outside the range skip the entry, so their value is unused.
+constexpr float kLn2F = 0.693147180559945309417232121458f;
+constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
+__device__ __forceinline__ float exp_falloff_core(float x)
+{
+    const float t = __builtin_fmaf(x, kLog2e, kRoundMagic);
+    const float k = t - kRoundMagic;
+    const float r = __builtin_fmaf(-k, kLn2F, x);
+    float p = kInvFact7;
+    p = __builtin_fmaf(p, r, kInvFact6);
+    p = __builtin_fmaf(p, r, kInvFact5);
+    p = __builtin_fmaf(p, r, kInvFact4);
+    p = __builtin_fmaf(p, r, kInvFact3);
+    p = __builtin_fmaf(p, r, kInvFact2);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, t) << 23) + __builtin_bit_cast(uint32_t, p));
+}
+
+__device__ __forceinline__ float exp_falloff(float x)
+{
+    return exp_falloff_core(__builtin_amdgcn_fmed3f(x, -6.0f, 0.0f));
+}
+
+// -6 <= x <= 0 (NaN: false) in one unsigned compare: 0 - x maps both zeros to
+// +0 and keeps the order, and the patterns of +0 .. 6 are 0 .. 0x40C00000
+// while negative numbers and NaN lie above.  An entry at power < -6 has
+// alpha <= exp(-6) < 1/255 and is skipped, as at power > 0.
+__device__ __forceinline__ bool falloff_in_range(float x)
+{
+    return __builtin_bit_cast(uint32_t, 0.0f - x) <= 0x40C00000u;
 }
 
 // exp_cw_core of x inside [-87, 88.7]; 0 below, inf above, NaN kept.  The

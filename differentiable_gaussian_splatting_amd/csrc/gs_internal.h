@@ -139,7 +139,7 @@ gs_status launch_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, 
 gs_status launch_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
                              const float* grad2d, int64_t s0, int64_t s1, float* grad3d);
 gs_status launch_export_proj(gs_ctx* ctx, const gs_proj* proj, int field, void* dst);
-gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
+gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n, bool falloff);
 
 // binning.hip
 // list: candidate slots to visit (NULL: all n_cand), n_list entries

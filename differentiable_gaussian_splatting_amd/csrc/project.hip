@@ -651,6 +651,12 @@ __global__ void k_exp(int64_t n, const float* __restrict__ x, float* __restrict_
     if (j < n) y[j] = gsd::exp_cw(x[j]);
 }
 
+__global__ void k_exp_falloff(int64_t n, const float* __restrict__ x, float* __restrict__ y)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) y[j] = gsd::exp_falloff(x[j]);
+}
+
 }  // namespace
 
 gs_status launch_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
@@ -766,10 +772,11 @@ gs_status launch_export_proj(gs_ctx* ctx, const gs_proj* proj, int field, void* 
     return GS_OK;
 }
 
-gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n)
+gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n, bool falloff)
 {
     if (n > 0)
-        hipLaunchKernelGGL(k_exp, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, x, y);
+        hipLaunchKernelGGL(falloff ? k_exp_falloff : k_exp, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0,
+                           ctx->stream, n, x, y);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -22,8 +22,9 @@
 // pages give no formulas, this is the standard compositing rule):
 //   power = -0.5 (A dx^2 + C dy^2) - B dx dy, evaluated as
 //           fma(fma(-A/2, dx, -B dy), dx, (-C/2 dy) dy)
-//   skip if power > 0 (or < -87, where exp gives 0 and alpha < 1/255)
-//   alpha = min(0.99, o exp(power)); skip if alpha < 1/255
+//   skip if power > 0
+//   alpha = min(0.99, o E(power)); skip if alpha < 1/255, where E is exp on
+//           [-6, 0] and E(-6) below it (alpha < 1/255 there either way)
 //   T' = T (1 - alpha); stop before the entry if T' < 1e-4
 //   C = fma(rgb, alpha T, C); T = T'
 //   out = fma(T, bg, C)
@@ -150,26 +151,34 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
     bool active = inside;
     for (uint64_t base = start; base < end; base += 64) {
         if (gsd::ballot(active) == 0) break;
+        // lane i gathers entry i and tests it against the sub-tile; the kept
+        // entries are packed to the front of the wavefront's LDS slice in list
+        // order, each with its list position
         const uint64_t e = base + lane;
         bool keep = false;
+        float4 a, b;
+        float c = 0.0f;
         if (e < end) {
             const uint32_t s = values[e];
-            const float4 a = g0[s], b = g1[s];
-            S.a[lane] = a;
-            S.b[lane] = b;
-            S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
+            a = g0[s];
+            b = g1[s];
+            c = g2[s].x;
             keep = !cull_box(a, b, bx0, by0);
         }
-        uint64_t mask = gsd::ballot(keep);
+        const uint64_t km = gsd::ballot(keep);
+        if (keep) {
+            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+            S.a[pos] = a;
+            S.b[pos] = b;
+            S.c[pos] = make_float4(c, __builtin_bit_cast(float, (uint32_t)(base - start) + (uint32_t)lane), 0.0f, 0.0f);
+        }
+        const int nk = __builtin_popcountll(km);
         gsd::wave_sync();
-        const uint32_t n0 = (uint32_t)(base - start);
-        // Branch-free over the lanes: every lane evaluates the entry and the
-        // per-lane decisions become selects, so the wavefront issues one
-        // straight run of instructions per entry.  A lane's values for an
+        // Every lane evaluates every kept entry; the per-lane decisions (skip,
+        // stop, include) become lane masks, and the updates of a lane that
+        // includes the entry run under that mask.  A lane's values for an
         // entry it includes are computed in exactly the order given above.
-        while (mask) {
-            const int j = __builtin_ctzll(mask);
-            mask &= mask - 1;
+        for (int j = 0; j < nk; ++j) {
             const float4 a = S.a[j];
             const float4 b = S.b[j];
             const float dx = pxc - a.x, dy = pyc - a.y;
@@ -178,16 +187,12 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
             float u = b.x * dy;
             u = u * dy;
             const float power = __builtin_fmaf(t, dx, u);
-            // exp of the exponent clamped into [-87, 0]: exp(power) on every
-            // lane that can include the entry (below -87 the exp is 0 and
-            // alpha < 1/255; at -87 o exp(-87) < 1/255 too), finite on the others
-            const bool pok = !(power > 0.0f);
-            const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
-            // o and G are finite, so min gives the clamp exactly
+            // -6 <= power <= 0: outside, alpha < 1/255 or power > 0, and the
+            // exp's value (unclamped, so arbitrary) is unused
+            const bool pok = gsd::falloff_in_range(power);
+            const float G = gsd::exp_falloff_core(power);
             const float alpha = fminf(b.y * G, gsd::kAlphaMax);
             const bool inc = active && pok && !(alpha < gsd::kAlphaMin);
-            // T' and the weight of a lane that includes the entry (the other
-            // lanes keep their state through the selects below)
             const float Tn = T * (1.0f - alpha);
             const bool stop = inc && Tn < gsd::kTMin;
             const bool contrib = inc && !stop;
@@ -196,18 +201,21 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
                 n_inc += contrib ? 1u : 0u;
             }
             active = active && !stop;
-            const float w = contrib ? alpha * T : 0.0f;   // fma(x, 0, C) = C exactly
-            C0 = __builtin_fmaf(b.z, w, C0);
-            C1 = __builtin_fmaf(b.w, w, C1);
-            C2 = __builtin_fmaf(S.c[j].x, w, C2);
-            T = contrib ? Tn : T;
-            // a lane stops once per list: the stopping lanes record the
-            // position under an exec mask that is empty on almost every entry
-            // (scalar instructions only then; the empty volatile asm keeps the
-            // compiler from turning the branch into a select on every entry)
+            // the empty volatile asm keeps the compiler from turning these
+            // branches into selects on every lane
+            if (contrib) {
+                asm volatile("");
+                const float w = alpha * T;
+                C0 = __builtin_fmaf(b.z, w, C0);
+                C1 = __builtin_fmaf(b.w, w, C1);
+                C2 = __builtin_fmaf(S.c[j].x, w, C2);
+                T = Tn;
+            }
+            // a lane stops once per list: the end of its walk is the stopping
+            // entry's list position
             if (stop) {
                 asm volatile("");
-                lastn = n0 + (uint32_t)j;
+                lastn = __builtin_bit_cast(uint32_t, S.c[j].y);
             }
         }
         gsd::wave_sync();
@@ -439,8 +447,8 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
                 const float u1 = bb.x * dy;
                 const float u = u1 * dy;
                 const float power = __builtin_fmaf(t, dx, u);
-                const bool pok = !(power > 0.0f);   // power < -87: alpha < 1/255 (as in the forward)
-                const float G = gsd::exp_cw_core(__builtin_amdgcn_fmed3f(power, -87.0f, 0.0f));
+                const bool pok = !(power > 0.0f);
+                const float G = gsd::exp_falloff(power);
                 const float av = bb.y * G;
                 const bool clamped = av > gsd::kAlphaMax;
                 const float alpha = clamped ? gsd::kAlphaMax : av;

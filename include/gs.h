@@ -293,9 +293,20 @@ gs_status gs_export(gs_ctx* ctx, const void* handle, int32_t field, void* dst, s
 /* Size in bytes of a field (host). */
 gs_status gs_export_size(gs_ctx* ctx, const void* handle, int32_t field, size_t* bytes);
 
-/* The f32 exp used by the rasterizer (Cody-Waite reduction + degree-7 Taylor
- * polynomial), on n device floats; for bit-exactness checks. */
+/* The f32 exp of the projection (scales, sigmoid of the opacity logit):
+ * Cody-Waite reduction + degree-7 Taylor polynomial, 0 below -87, +inf above
+ * 88.7; on n device floats, for bit-exactness checks. */
 gs_status gs_util_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
+
+/* The f32 exp of the Gaussian falloff in the compositing alpha of
+ * gs_render_fwd (SkipGS notes, "loss function": transmittance accumulation;
+ * alpha = min(0.99, o exp(power))): the argument is clamped into [-6, 0] (below -6,
+ * alpha < 1/255 for every opacity, so the entry is skipped whichever value is
+ * used), then one-constant Cody-Waite reduction and the degree-7 Taylor
+ * polynomial; within 1 ulp of exp on [-6, 0].  On n finite device floats
+ * (NaN gives an unspecified value), for bit-exactness checks.  Errors:
+ * GS_ERR_INVALID_ARG for n < 0 or null pointers with n > 0. */
+gs_status gs_util_exp_falloff(gs_ctx* ctx, const float* x, float* y, int64_t n);
 
 /* ---- one whole view ---------------------------------------------------- */
 

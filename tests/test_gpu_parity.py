@@ -86,6 +86,16 @@ def test_exp_bitwise(ctx):
     assert np.array_equal(bits(y), bits(oracle.exp_cw(x)))
 
 
+def test_exp_falloff_bitwise(ctx):
+    import torch
+    x = np.concatenate([np.linspace(-7.0, 0.5, 1_000_001, dtype=np.float32),
+                        np.arange(0x80000000, 0x80000000 + 100_000, dtype=np.uint32).view(np.float32),
+                        np.array([0.0, -0.0, -6.0, -87.5, -1e30, 89.0, np.inf, -np.inf], np.float32)])
+    xg = torch.from_numpy(x).to(ctx.device)
+    y = B.gs_util_exp_falloff(ctx, xg).cpu().numpy()
+    assert np.array_equal(bits(y), bits(oracle.exp_falloff(x)))
+
+
 @pytest.mark.parametrize("name,kw,budget", [
     ("c1_small", dict(), None),
     ("c1_small", dict(posed=True, seed=101), None),
