@@ -24,9 +24,13 @@ sys.path.insert(0, ROOT)
 
 MIB = 1 << 20
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
-# 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz: f32 VALU instructions per second,
-# counting one per lane (an fma counts once); packed f32 is not used.
-PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# f32 VALU lane operations per second (an fma counts once): 256 CUs x 4 SIMD
+# x 32 lanes x 2.4 GHz = 78.6 T, i.e. the published 157.3 TFLOP/s f32 vector
+# rate.  gfx950 issues f32 add / mul / fma whose operands are VGPRs or inline
+# constants at that rate without packed instructions (a wave64 instruction
+# every 2 cycles per SIMD, measured); compares, min / max / med3, selects,
+# conversions, shifts and instructions reading an SGPR take 4 cycles.
+PEAK_VALU_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 # f32 VALU operations of the specified per-(pixel, entry) arithmetic:
 #   every examined pair: offsets 2, power 5, range test 2, exp 14, alpha with
 #     clamp and threshold 4                                            = 27
@@ -113,8 +117,8 @@ def main():
         log(f"[bench] warmup step {k}: loss {r['loss']:.6f} cand {r['n_cand']} isect {r['n_isect']} "
             f"leaves {r['n_leaves']}")
     kernels = ["project_flags", "project_write", "prefix2d", "scan", "rect_diff", "bin_count", "emit", "radix",
-               "seg_offsets", "fine", "plan_split", "leaf_groups", "raster_fwd", "raster_bwd", "project_bwd", "adam",
-               "bwd_adam"]
+               "seg_offsets", "fine", "plan_split", "leaf_groups", "raster_fwd", "raster_bwd", "raster_fused", "tile_order",
+               "project_bwd", "adam", "bwd_adam"]
 
     def kernel_times(n_steps, names):
         out = {}
@@ -280,16 +284,16 @@ def count_work(B, ctx, cam, params, budget):
     B.gs_release(ctx, proj)
     q = stats.cpu().tolist()
     P = cam.width * cam.height
-    # raster state traffic: fwd writes T_final, last, dL/dout (20 B/px) and
-    # reads the target (12 B/px); bwd reads them back (20 B/px)
+    # raster traffic per pixel: the fused forward + L1 + backward keeps the
+    # per-pixel state in registers and reads the target (12 B/px)
     return dict(q_f=int(q[0]), q_inc=int(q[1]), q_b=int(q[3]), sum_last=int(q[2]), n_isect=int(n_isect),
                 n_cand=int(n_cand),
-                n_leaves=len(leaves), tiles=int(tiles), pixels=P, raster_bytes=52 * P,
+                n_leaves=len(leaves), tiles=int(tiles), pixels=P, raster_bytes=12 * P,
                 radix_elems=int(radix_elems), group_entries=int(group_entries), cells=int(cells),
                 supers=int(supers))
 
 
-KERNEL_WORK_NAMES = ("raster_fwd", "raster_bwd", "radix", "emit", "bin_count", "seg_offsets", "fine", "rect_diff",
+KERNEL_WORK_NAMES = ("raster_fwd", "raster_bwd", "raster_fused", "radix", "emit", "bin_count", "seg_offsets", "fine", "rect_diff",
                      "project_flags", "project_write", "project_bwd", "adam", "bwd_adam")
 
 
@@ -306,6 +310,10 @@ def kernel_work(wc, sc):
                        f"{OPS_EXAMINED} ops x examined-only pairs + {OPS_INCLUDED_FWD} x included pairs"),
         "raster_bwd": ("alu", OPS_EXAMINED * (qb - qi) + OPS_INCLUDED_BWD * qi,
                        f"{OPS_EXAMINED} ops x revisited-only pairs + {OPS_INCLUDED_BWD} x included pairs"),
+        "raster_fused": ("alu", OPS_EXAMINED * (qf - qi) + OPS_INCLUDED_FWD * qi
+                         + OPS_EXAMINED * (qb - qi) + OPS_INCLUDED_BWD * qi,
+                         f"forward ({OPS_EXAMINED} ops x examined-only pairs + {OPS_INCLUDED_FWD} x included pairs) "
+                         f"+ backward ({OPS_EXAMINED} x revisited-only + {OPS_INCLUDED_BWD} x included)"),
         "radix": ("hbm", 20 * wc["radix_elems"], "per pass and element: read the key twice, the value once, "
                                                    "write key and value (20 B)"),
         "emit": ("hbm", 8 * C + 28 * wc["group_entries"], "write 8 B (super-tile, slot) per coarse pair; read "

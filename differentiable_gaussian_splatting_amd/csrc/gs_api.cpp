@@ -219,6 +219,7 @@ static void clear_plan(gs_ctx* ctx, gs_proj* proj, bool retire)
     proj->plan_cands = nullptr;
     proj->plan_coff = nullptr;
     proj->plan_toff = nullptr;
+    proj->plan_order = nullptr;
 }
 
 // Groups the candidates by planned leaf and precomputes, for the whole view,
@@ -242,6 +243,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr, *ccnt = nullptr, *coff = nullptr;
     uint32_t* lcells = nullptr;
     uint64_t *segoff = nullptr, *dtbase = nullptr, *toff = nullptr;
+    uint32_t* torder = nullptr;
     hipError_t e;
     int32_t* lot = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * T, GS_MEM_SCRATCH, &tmp);
     uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(nc, 1), GS_MEM_SCRATCH, &tmp);
@@ -266,7 +268,8 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     lisect = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * nl, GS_MEM_SCRATCH, &tmp);
     dtbase = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
     toff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
-    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !lcells || !lisect || !dtbase || !toff) {
+    torder = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
+    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !lcells || !lisect || !dtbase || !toff || !torder) {
         st = GS_ERR_OOM;
         goto out;
     }
@@ -278,6 +281,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     if ((st = launch_plan_offsets(ctx, proj, ldev, nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0, segoff, ccnt,
                                   coff, lcells, lisect, dtbase, toff)) != GS_OK)
         goto out;
+    if ((st = launch_tile_order_sets(ctx, nl, dtbase, toff, torder)) != GS_OK) goto out;
     e = hipMemcpyAsync(hoff.data(), segoff, sizeof(uint64_t) * (nl + 1), hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(hlc.data(), lcells, sizeof(uint32_t) * 2 * nl, hipMemcpyDeviceToHost, ctx->stream);
@@ -293,6 +297,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     proj->plan_cands = second ? v1 : v0;
     proj->plan_coff = coff;
     proj->plan_toff = toff;
+    proj->plan_order = torder;
     proj->plan.swap(plan);
     proj->plan_off.swap(hoff);
     proj->plan_cells.swap(hcells);
@@ -316,6 +321,7 @@ struct PlanLeaf {
     const uint32_t* eoff = nullptr;   // their offsets (subtract ebase)
     uint32_t ebase = 0;
     uint64_t* toff = nullptr;         // tile offsets [T_L + 1]
+    const uint32_t* order = nullptr;  // tiles longest list first [T_L]
 };
 
 static PlanLeaf plan_leaf(const gs_proj* proj, gs_tile_rect leaf)
@@ -332,6 +338,7 @@ static PlanLeaf plan_leaf(const gs_proj* proj, gs_tile_rect leaf)
             r.eoff = proj->plan_coff + proj->plan_off[k];
             r.ebase = proj->plan_cbase[k];
             r.toff = proj->plan_toff + proj->plan_tbase[k];
+            r.order = proj->plan_order + proj->plan_tbase[k];
             r.isect = (int64_t)proj->plan_isect[k];
             return r;
         }
@@ -686,6 +693,7 @@ static gs_status fine_finish(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb, g
     b->THL = cb->leaf.ty1 - cb->leaf.ty0;
     b->n_tiles = (int64_t)b->TWL * b->THL;
     b->offsets = cb->pl.toff;
+    b->order = cb->pl.order;
     b->n_isect = (int64_t)cb->I;
     b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(cb->I, 1), GS_MEM_RASTER, &b->allocs);
     gs_status st = b->values ? GS_OK : GS_ERR_OOM;
@@ -765,6 +773,7 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     const uint32_t ebase = pl.ebase;
     if (pl.found) {
         b->offsets = pl.toff;      // the plan's memory (kept until the projection is released)
+        b->order = pl.order;
         C = (uint64_t)pl.cells;
     } else {
         if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) goto fail;
@@ -1175,9 +1184,10 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         }
         isect_total += ni;
         if (opts->loss_kind == 0) {
-            st = render_fwd(ctx, cam, proj, bins, target, loss_dev, image, nullptr, l1_view + l1_off, &ras);
+            // L1: each pixel's loss gradient is its own residual sign, so the
+            // forward, the loss and the backward of a tile run in one wavefront
+            st = launch_raster_fused(ctx, cam, proj, bins, target, image, l1_view + l1_off, grad2d);
             l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
-            if (st == GS_OK) st = gs_render_bwd(ctx, cam, proj, bins, ras, nullptr, grad2d);
         } else {
             st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, nullptr, &ras);
             if (st == GS_OK)

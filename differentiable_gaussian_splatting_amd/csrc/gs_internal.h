@@ -74,6 +74,7 @@ struct gs_proj : GsHandle {
     std::vector<uint64_t> plan_isect; // per leaf: intersections
     uint32_t* plan_coff = nullptr;    // device [entries + 1] scan of the entries' coarse pair counts
     uint64_t* plan_toff = nullptr;    // device: per leaf, its tile offsets [T_L + 1]
+    uint32_t* plan_order = nullptr;   // device: per leaf at plan_tbase, its tiles longest list first [T_L]
     std::vector<GsAlloc> plan_retired; // earlier plans (bins may still point into them)
     uint32_t* plan_cands = nullptr;   // device [plan_off.back()] candidate slots, depth order per group
     std::vector<GsAlloc> plan_allocs;
@@ -87,6 +88,7 @@ struct gs_bins : GsHandle {
     int TWL = 0, THL = 0;
     uint64_t* offsets = nullptr;  // [n_tiles + 1]
     uint32_t* values = nullptr;   // [n_isect]
+    const uint32_t* order = nullptr;   // [n_tiles] launch order of the fused raster (plan memory) or null
 };
 
 struct gs_raster : GsHandle {
@@ -195,6 +197,14 @@ int64_t radix_scratch_words(int64_t n);
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
                             gs_raster* r, const float* target, float* image_out, double* loss_accum,
                             uint64_t* stats);
+// forward + L1 + backward of one leaf in one launch (no per-pixel state in
+// memory); l1_part receives 4 doubles per tile of the leaf
+gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                              const float* target, float* image_out, double* l1_part, float* grad2d);
+// tiles of each of n_sets offset arrays (set L at base[L], base[L + 1] - base[L]
+// - 1 tiles) in the fused raster's launch order, written at the same bases
+gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const uint64_t* base, const uint64_t* offsets,
+                                 uint32_t* order);
 gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
                             const gs_raster* r, const float* dl_dimage, float* grad2d);
 

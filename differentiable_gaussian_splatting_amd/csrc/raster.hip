@@ -120,6 +120,54 @@ __device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by
     return cull_test(cull_prep(a, b), bx0, by0);
 }
 
+// One kept entry j of the staged batch at one pixel of the forward walk.
+// Every lane evaluates the entry; the per-lane decisions (skip, stop,
+// include) become lane masks, and the updates of a lane that includes the
+// entry run under that mask.  A lane's values for an entry it includes are
+// computed in exactly the order given above.
+template <bool STATS>
+__device__ __forceinline__ void fwd_step(const Staged& S, int j, const float4 a, const float4 b, float pxc, float pyc,
+                                         float& T, float& C0, float& C1, float& C2, bool& active, uint32_t& lastn,
+                                         uint32_t& n_eval, uint32_t& n_inc)
+{
+    const float dx = pxc - a.x, dy = pyc - a.y;
+    float t = a.w * dy;
+    t = __builtin_fmaf(a.z, dx, t);
+    float u = b.x * dy;
+    u = u * dy;
+    const float power = __builtin_fmaf(t, dx, u);
+    // -6 <= power <= 0: outside, alpha < 1/255 or power > 0, and the exp's
+    // value (unclamped, so arbitrary) is unused
+    const bool pok = gsd::falloff_in_range(power);
+    const float G = gsd::exp_falloff_core(power);
+    const float alpha = fminf(b.y * G, gsd::kAlphaMax);
+    const bool inc = active && pok && !(alpha < gsd::kAlphaMin);
+    const float Tn = T * (1.0f - alpha);
+    const bool stop = inc && Tn < gsd::kTMin;
+    const bool contrib = inc && !stop;
+    if (STATS) {
+        n_eval += active ? 1u : 0u;
+        n_inc += contrib ? 1u : 0u;
+    }
+    active = active && !stop;
+    // the empty volatile asm keeps the compiler from turning these branches
+    // into selects on every lane
+    if (contrib) {
+        asm volatile("");
+        const float w = alpha * T;
+        C0 = __builtin_fmaf(b.z, w, C0);
+        C1 = __builtin_fmaf(b.w, w, C1);
+        C2 = __builtin_fmaf(S.c[j].x, w, C2);
+        T = Tn;
+    }
+    // a lane stops once per list: the end of its walk is the stopping entry's
+    // list position
+    if (stop) {
+        asm volatile("");
+        lastn = __builtin_bit_cast(uint32_t, S.c[j].y);
+    }
+}
+
 template <bool STATS>
 __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* __restrict__ offsets,
                                                     const uint32_t* __restrict__ values,
@@ -174,50 +222,8 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
         }
         const int nk = __builtin_popcountll(km);
         gsd::wave_sync();
-        // Every lane evaluates every kept entry; the per-lane decisions (skip,
-        // stop, include) become lane masks, and the updates of a lane that
-        // includes the entry run under that mask.  A lane's values for an
-        // entry it includes are computed in exactly the order given above.
-        for (int j = 0; j < nk; ++j) {
-            const float4 a = S.a[j];
-            const float4 b = S.b[j];
-            const float dx = pxc - a.x, dy = pyc - a.y;
-            float t = a.w * dy;
-            t = __builtin_fmaf(a.z, dx, t);
-            float u = b.x * dy;
-            u = u * dy;
-            const float power = __builtin_fmaf(t, dx, u);
-            // -6 <= power <= 0: outside, alpha < 1/255 or power > 0, and the
-            // exp's value (unclamped, so arbitrary) is unused
-            const bool pok = gsd::falloff_in_range(power);
-            const float G = gsd::exp_falloff_core(power);
-            const float alpha = fminf(b.y * G, gsd::kAlphaMax);
-            const bool inc = active && pok && !(alpha < gsd::kAlphaMin);
-            const float Tn = T * (1.0f - alpha);
-            const bool stop = inc && Tn < gsd::kTMin;
-            const bool contrib = inc && !stop;
-            if (STATS) {
-                n_eval += active ? 1u : 0u;
-                n_inc += contrib ? 1u : 0u;
-            }
-            active = active && !stop;
-            // the empty volatile asm keeps the compiler from turning these
-            // branches into selects on every lane
-            if (contrib) {
-                asm volatile("");
-                const float w = alpha * T;
-                C0 = __builtin_fmaf(b.z, w, C0);
-                C1 = __builtin_fmaf(b.w, w, C1);
-                C2 = __builtin_fmaf(S.c[j].x, w, C2);
-                T = Tn;
-            }
-            // a lane stops once per list: the end of its walk is the stopping
-            // entry's list position
-            if (stop) {
-                asm volatile("");
-                lastn = __builtin_bit_cast(uint32_t, S.c[j].y);
-            }
-        }
+        for (int j = 0; j < nk; ++j)
+            fwd_step<STATS>(S, j, S.a[j], S.b[j], pxc, pyc, T, C0, C1, C2, active, lastn, n_eval, n_inc);
         gsd::wave_sync();
     }
 
@@ -329,80 +335,17 @@ __device__ __forceinline__ float wave_reduce9(const float* p, int lane, int* vid
     return d;
 }
 
-// Backward, one wavefront per 16 x 16 tile, four tiles per workgroup and no
-// workgroup barrier.  Lane l owns pixel l (x = l % 8, y = l / 8) of each 8 x 8
-// quadrant k of the tile (k & 1: right half, k >> 1: bottom half).  The
-// wavefront walks the tile's list back to front from the furthest end of its
-// pixels' forward walks, 64 entries per batch staged in its own LDS slice;
-// lane i gathers entry i and sets bit k of the entry's quadrant mask when the
-// entry precedes the end of some forward walk in quadrant k and survives the cull
-// against quadrant k's box.  Per entry, the quadrants of the mask are
-// evaluated in turn (one wave-uniform branch each, skipped when none of the
-// quadrant's pixels includes the entry); the partials of a lane's four pixels
-// are summed in registers, the moments become the partials of the mean and
-// the conic, and one transposed reduction over the wavefront and one 9-lane
-// atomic add follow.  Entries that reach a tile mostly cover all of its
-// quadrants, so a tile-wide reduction replaces up to four per-quadrant ones.
-__global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
-                                                    const uint64_t* __restrict__ offsets,
-                                                    const uint32_t* __restrict__ values,
-                                                    const float4* __restrict__ g0, const float4* __restrict__ g1,
-                                                    const float4* __restrict__ g2, float bg0, float bg1, float bg2,
-                                                    const float* __restrict__ tfinal,
-                                                    const uint32_t* __restrict__ last,
-                                                    const uint8_t* __restrict__ sgn, float inv_norm,
-                                                    const float* __restrict__ dl_dimage,
-                                                    float* __restrict__ grad2d)
+// The backward walk of one tile by one wavefront (see k_raster_bwd): T, GS,
+// the dL/dout factors gr0..gr2 and the walk ends lst of the lane's pixel in
+// each quadrant, mq the largest end in each quadrant.
+__device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, const float (&pxc)[2],
+                                         const float (&pyc)[2], const float (&bx)[2], const float (&by)[2],
+                                         float (&T)[4], float (&GS)[4], const float (&gr0)[4],
+                                         const float (&gr1)[4], const float (&gr2)[4], const uint32_t (&lst)[4],
+                                         const uint32_t (&mq)[4], const uint32_t* __restrict__ values,
+                                         const float4* __restrict__ g0, const float4* __restrict__ g1,
+                                         const float4* __restrict__ g2, float* __restrict__ grad2d)
 {
-    __shared__ Staged st[4];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t lt = (int64_t)blockIdx.x * 4 + wave;
-    if (lt >= n_tiles) return;
-    Staged& S = st[wave];
-    const int tx = g.ltx0 + (int)(lt % g.TWL), ty = g.lty0 + (int)(lt / g.TWL);
-    const int qx = lane & 7, qy = lane >> 3;
-    float pxc[2], pyc[2], bx[2], by[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        pxc[h] = (float)(tx * 16 + h * 8 + qx) + 0.5f;
-        pyc[h] = (float)(ty * 16 + h * 8 + qy) + 0.5f;
-        bx[h] = (float)(tx * 16 + h * 8) + 0.5f;
-        by[h] = (float)(ty * 16 + h * 8) + 0.5f;
-    }
-    const uint64_t start = offsets[lt];
-
-    // per quadrant k: transmittance after the last included entry, dL/dout,
-    // GS = sum_ch dL/dout_ch * (colour behind the current entry, ch), which
-    // starts as the background seen through T_final, and the end of the walk
-    float T[4], GS[4], gr0[4], gr1[4], gr2[4];
-    uint32_t lst[4], mq[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int px = tx * 16 + (k & 1) * 8 + qx, py = ty * 16 + (k >> 1) * 8 + qy;
-        T[k] = 1.0f;
-        gr0[k] = gr1[k] = gr2[k] = 0.0f;
-        lst[k] = 0;
-        if (px < g.W && py < g.H) {
-            const int64_t lp = (int64_t)(py - g.py0) * g.WL + (px - g.px0);
-            T[k] = tfinal[lp];
-            lst[k] = last[lp];
-            if (dl_dimage) {
-                const int64_t P = (int64_t)g.W * g.H;
-                const int64_t gi = (int64_t)py * g.W + px;
-                gr0[k] = dl_dimage[gi];
-                gr1[k] = dl_dimage[P + gi];
-                gr2[k] = dl_dimage[2 * P + gi];
-            } else {
-                const uint32_t c = sgn[lp];
-                auto dec = [&](uint32_t code) { return code == 1u ? inv_norm : (code == 2u ? -inv_norm : 0.0f); };
-                gr0[k] = dec(c & 3u);
-                gr1[k] = dec((c >> 2) & 3u);
-                gr2[k] = dec((c >> 4) & 3u);
-            }
-        }
-        GS[k] = T[k] * (gr0[k] * bg0 + gr1[k] * bg1 + gr2[k] * bg2);
-        mq[k] = __builtin_amdgcn_readfirstlane(gsd::wave_max_u32(lst[k]));
-    }
     const uint32_t maxl = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
 
     for (int64_t hi = maxl; hi > 0; hi -= 64) {
@@ -504,6 +447,292 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
     }
 }
 
+// Backward, one wavefront per 16 x 16 tile, four tiles per workgroup and no
+// workgroup barrier.  Lane l owns pixel l (x = l % 8, y = l / 8) of each 8 x 8
+// quadrant k of the tile (k & 1: right half, k >> 1: bottom half).  The
+// wavefront walks the tile's list back to front from the furthest end of its
+// pixels' forward walks, 64 entries per batch staged in its own LDS slice;
+// lane i gathers entry i and sets bit k of the entry's quadrant mask when the
+// entry precedes the end of some forward walk in quadrant k and survives the cull
+// against quadrant k's box.  Per entry, the quadrants of the mask are
+// evaluated in turn (one wave-uniform branch each, skipped when none of the
+// quadrant's pixels includes the entry); the partials of a lane's four pixels
+// are summed in registers, the moments become the partials of the mean and
+// the conic, and one transposed reduction over the wavefront and one 9-lane
+// atomic add follow.  Entries that reach a tile mostly cover all of its
+// quadrants, so a tile-wide reduction replaces up to four per-quadrant ones.
+__global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
+                                                    const uint64_t* __restrict__ offsets,
+                                                    const uint32_t* __restrict__ values,
+                                                    const float4* __restrict__ g0, const float4* __restrict__ g1,
+                                                    const float4* __restrict__ g2, float bg0, float bg1, float bg2,
+                                                    const float* __restrict__ tfinal,
+                                                    const uint32_t* __restrict__ last,
+                                                    const uint8_t* __restrict__ sgn, float inv_norm,
+                                                    const float* __restrict__ dl_dimage,
+                                                    float* __restrict__ grad2d)
+{
+    __shared__ Staged st[4];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t lt = (int64_t)blockIdx.x * 4 + wave;
+    if (lt >= n_tiles) return;
+    Staged& S = st[wave];
+    const int tx = g.ltx0 + (int)(lt % g.TWL), ty = g.lty0 + (int)(lt / g.TWL);
+    const int qx = lane & 7, qy = lane >> 3;
+    float pxc[2], pyc[2], bx[2], by[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        pxc[h] = (float)(tx * 16 + h * 8 + qx) + 0.5f;
+        pyc[h] = (float)(ty * 16 + h * 8 + qy) + 0.5f;
+        bx[h] = (float)(tx * 16 + h * 8) + 0.5f;
+        by[h] = (float)(ty * 16 + h * 8) + 0.5f;
+    }
+    const uint64_t start = offsets[lt];
+
+    // per quadrant k: transmittance after the last included entry, dL/dout,
+    // GS = sum_ch dL/dout_ch * (colour behind the current entry, ch), which
+    // starts as the background seen through T_final, and the end of the walk
+    float T[4], GS[4], gr0[4], gr1[4], gr2[4];
+    uint32_t lst[4], mq[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int px = tx * 16 + (k & 1) * 8 + qx, py = ty * 16 + (k >> 1) * 8 + qy;
+        T[k] = 1.0f;
+        gr0[k] = gr1[k] = gr2[k] = 0.0f;
+        lst[k] = 0;
+        if (px < g.W && py < g.H) {
+            const int64_t lp = (int64_t)(py - g.py0) * g.WL + (px - g.px0);
+            T[k] = tfinal[lp];
+            lst[k] = last[lp];
+            if (dl_dimage) {
+                const int64_t P = (int64_t)g.W * g.H;
+                const int64_t gi = (int64_t)py * g.W + px;
+                gr0[k] = dl_dimage[gi];
+                gr1[k] = dl_dimage[P + gi];
+                gr2[k] = dl_dimage[2 * P + gi];
+            } else {
+                const uint32_t c = sgn[lp];
+                auto dec = [&](uint32_t code) { return code == 1u ? inv_norm : (code == 2u ? -inv_norm : 0.0f); };
+                gr0[k] = dec(c & 3u);
+                gr1[k] = dec((c >> 2) & 3u);
+                gr2[k] = dec((c >> 4) & 3u);
+            }
+        }
+        GS[k] = T[k] * (gr0[k] * bg0 + gr1[k] * bg1 + gr2[k] * bg2);
+        mq[k] = __builtin_amdgcn_readfirstlane(gsd::wave_max_u32(lst[k]));
+    }
+    bwd_walk(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d);
+}
+
+
+// Forward, L1 loss and backward of one tile in one wavefront, for views
+// whose loss gradient at a pixel depends on that pixel alone (L1): the
+// per-pixel state the backward needs (T_final, the end of the walk, the
+// residual signs) stays in registers instead of going through memory, and
+// each tile's list is gathered and culled once for its four quadrants.
+// Lane l owns pixel l of each 8 x 8 quadrant, as in the backward.  Forward:
+// 64 entries per batch; lane i gathers entry i and marks the quadrants (with
+// a pixel still compositing) whose box it can reach; the kept entries are
+// packed in LDS with their list position and quadrant mask, and each is
+// composited into the pixels of its quadrants (fwd_step, the same operations
+// as k_raster_fwd).  The image, the L1 partial of the tile and dL/dout =
+// sgn(out - target) / (3WH) follow, then the backward walk (bwd_walk).
+// One wavefront per workgroup: a tile's wavefront frees its slot the moment
+// it ends, instead of waiting for the other tiles of a shared workgroup.
+constexpr int kFusedWaves = 1;
+__global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, int64_t n_tiles,
+                                                      const uint64_t* __restrict__ offsets,
+                                                      const uint32_t* __restrict__ values,
+                                                      const float4* __restrict__ g0, const float4* __restrict__ g1,
+                                                      const float4* __restrict__ g2, float bg0, float bg1, float bg2,
+                                                      const float* __restrict__ target, float inv_norm,
+                                                      float* __restrict__ image, double* __restrict__ l1_part,
+                                                      float* __restrict__ grad2d, const uint32_t* __restrict__ order)
+{
+    __shared__ Staged st[kFusedWaves];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * kFusedWaves + wave;
+    if (w >= n_tiles) return;
+    const int64_t lt = order[w];
+    Staged& S = st[wave];
+    const int tx = g.ltx0 + (int)(lt % g.TWL), ty = g.lty0 + (int)(lt / g.TWL);
+    const int qx = lane & 7, qy = lane >> 3;
+    float pxc[2], pyc[2], bx[2], by[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        pxc[h] = (float)(tx * 16 + h * 8 + qx) + 0.5f;
+        pyc[h] = (float)(ty * 16 + h * 8 + qy) + 0.5f;
+        bx[h] = (float)(tx * 16 + h * 8) + 0.5f;
+        by[h] = (float)(ty * 16 + h * 8) + 0.5f;
+    }
+    const uint64_t start = offsets[lt], end = offsets[lt + 1];
+
+    // ---- forward over the four quadrants
+    float T[4], C0[4], C1[4], C2[4];
+    uint32_t lst[4];
+    bool act[4], inside[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int px = tx * 16 + (k & 1) * 8 + qx, py = ty * 16 + (k >> 1) * 8 + qy;
+        inside[k] = px < g.W && py < g.H;
+        act[k] = inside[k];
+        T[k] = 1.0f;
+        C0[k] = C1[k] = C2[k] = 0.0f;
+        lst[k] = (uint32_t)(end - start);
+    }
+    uint32_t n_eval = 0, n_inc = 0;   // unused (no statistics here)
+    for (uint64_t base = start; base < end; base += 64) {
+        uint32_t aq = 0;   // quadrants with a pixel still compositing
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (gsd::ballot(act[k]) != 0) aq |= 1u << k;
+        if (aq == 0) break;
+        const uint64_t e = base + lane;
+        uint32_t qb = 0;
+        float4 a, b;
+        float c = 0.0f;
+        if (e < end) {
+            const uint32_t s = values[e];
+            a = g0[s];
+            b = g1[s];
+            c = g2[s].x;
+            const CullPrep cp = cull_prep(a, b);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (((aq >> k) & 1u) && !cull_test(cp, bx[k & 1], by[k >> 1])) qb |= 1u << k;
+        }
+        const uint64_t km = gsd::ballot(qb != 0);
+        if (qb != 0) {
+            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+            S.a[pos] = a;
+            S.b[pos] = b;
+            S.c[pos] = make_float4(c, __builtin_bit_cast(float, (uint32_t)(base - start) + (uint32_t)lane),
+                                   __builtin_bit_cast(float, qb), 0.0f);
+        }
+        const int nk = __builtin_popcountll(km);
+        gsd::wave_sync();
+        for (int j = 0; j < nk; ++j) {
+            const float4 ea = S.a[j];
+            const float4 eb = S.b[j];
+            const uint32_t qm = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, S.c[j].z));
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if ((qm >> k) & 1u)
+                    fwd_step<false>(S, j, ea, eb, pxc[k & 1], pyc[k >> 1], T[k], C0[k], C1[k], C2[k], act[k], lst[k],
+                                    n_eval, n_inc);
+        }
+        gsd::wave_sync();
+    }
+
+    // ---- image, L1 and dL/dout
+    float GS[4], gr0[4], gr1[4], gr2[4];
+    uint32_t mq[4];
+    double l1 = 0.0;
+    const int64_t P = (int64_t)g.W * g.H;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        gr0[k] = gr1[k] = gr2[k] = 0.0f;
+        if (inside[k]) {
+            const int px = tx * 16 + (k & 1) * 8 + qx, py = ty * 16 + (k >> 1) * 8 + qy;
+            const float o0 = __builtin_fmaf(T[k], bg0, C0[k]);
+            const float o1 = __builtin_fmaf(T[k], bg1, C1[k]);
+            const float o2 = __builtin_fmaf(T[k], bg2, C2[k]);
+            const int64_t gi = (int64_t)py * g.W + px;
+            if (image) {
+                image[gi] = o0;
+                image[P + gi] = o1;
+                image[2 * P + gi] = o2;
+            }
+            const float t0 = target[gi], t1 = target[P + gi], t2 = target[2 * P + gi];
+            const float d0 = o0 - t0, d1 = o1 - t1, d2 = o2 - t2;   // sign exact in f32
+            gr0[k] = d0 > 0.0f ? inv_norm : (d0 < 0.0f ? -inv_norm : 0.0f);
+            gr1[k] = d1 > 0.0f ? inv_norm : (d1 < 0.0f ? -inv_norm : 0.0f);
+            gr2[k] = d2 > 0.0f ? inv_norm : (d2 < 0.0f ? -inv_norm : 0.0f);
+            l1 += fabs((double)o0 - (double)t0) + fabs((double)o1 - (double)t1) + fabs((double)o2 - (double)t2);
+        } else {
+            lst[k] = 0;   // outside the image: no entry is revisited
+        }
+        GS[k] = T[k] * (gr0[k] * bg0 + gr1[k] * bg1 + gr2[k] * bg2);
+        mq[k] = __builtin_amdgcn_readfirstlane(gsd::wave_max_u32(lst[k]));
+    }
+    l1 = gsd::wave_sum_d(l1);
+    if (lane < 4) l1_part[lt * 4 + lane] = lane == 0 ? l1 : 0.0;
+
+    // ---- backward
+    bwd_walk(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d);
+}
+
+
+// ---- launch order of the fused kernel's tiles -------------------------------
+// A wavefront's work grows with its tile's list, and the lists of one leaf
+// differ by orders of magnitude, so the tiles are launched longest first
+// (bucketed by half octaves of the list length; order inside a bucket
+// unspecified): the last wavefronts of the launch are then short ones.
+__device__ __forceinline__ int len_bucket(uint64_t len)
+{
+    if (len < 2) return (int)len;
+    const int msb = 63 - __builtin_clzll(len);
+    return 2 * msb + (int)((len >> (msb - 1)) & 1u);   // 2 .. 127 for len < 2^64
+}
+
+// Lanes with b >= 0 add themselves to ctr[b] (one LDS atomic per distinct b
+// in the wavefront); each gets its rank among all adds to its counter.
+__device__ __forceinline__ uint32_t wave_bucket_add(int b, uint32_t* ctr, int lane)
+{
+    uint32_t slot = 0;
+    uint64_t pending = gsd::ballot(b >= 0);
+    while (pending) {
+        const int leader = __builtin_ctzll(pending);
+        const int bl = __builtin_amdgcn_readlane(b, leader);
+        const uint64_t grp = gsd::ballot(b == bl);
+        uint32_t old = 0;
+        if (lane == leader) old = atomicAdd(&ctr[bl], (uint32_t)__builtin_popcountll(grp));
+        old = __builtin_amdgcn_readlane(old, leader);
+        if (b == bl)
+            slot = old + __builtin_amdgcn_mbcnt_hi((uint32_t)(grp >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)grp, 0u));
+        pending &= ~grp;
+    }
+    return slot;
+}
+
+// Workgroup L orders the tiles of list set L: its offsets start at
+// offsets + base[L] and its order goes to order + base[L], with
+// base[L + 1] - base[L] - 1 tiles (base = null: one set of n tiles at 0).
+__global__ __launch_bounds__(1024) void k_tile_order(int64_t n1, const uint64_t* __restrict__ base,
+                                                     const uint64_t* __restrict__ offsets0,
+                                                     uint32_t* __restrict__ order0)
+{
+    __shared__ uint32_t ctr[128];
+    const uint64_t b0 = base ? base[blockIdx.x] : 0;
+    const int64_t n = base ? (int64_t)(base[blockIdx.x + 1] - b0) - 1 : n1;
+    const uint64_t* __restrict__ offsets = offsets0 + b0;
+    uint32_t* __restrict__ order = order0 + b0;
+    const int t = threadIdx.x, lane = t & 63;
+    if (t < 128) ctr[t] = 0;
+    __syncthreads();
+    for (int64_t i0 = 0; i0 < n; i0 += 1024) {
+        const int64_t i = i0 + t;
+        const int b = i < n ? len_bucket(offsets[i + 1] - offsets[i]) : -1;
+        (void)wave_bucket_add(b, ctr, lane);
+    }
+    __syncthreads();
+    if (t == 0) {   // exclusive prefix, longest bucket first
+        uint32_t run = 0;
+        for (int b = 127; b >= 0; --b) {
+            const uint32_t c = ctr[b];
+            ctr[b] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int64_t i0 = 0; i0 < n; i0 += 1024) {
+        const int64_t i = i0 + t;
+        const int b = i < n ? len_bucket(offsets[i + 1] - offsets[i]) : -1;
+        const uint32_t pos = wave_bucket_add(b, ctr, lane);
+        if (b >= 0) order[pos] = (uint32_t)i;
+    }
+}
+
 }  // namespace
 
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
@@ -541,6 +770,56 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
         hipLaunchKernelGGL(k_raster_bwd, dim3((unsigned)((nt + 3) / 4)), dim3(256), 0, ctx->stream, g, nt,
                            bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
                            r->tfinal, r->last, r->sgn, inv_norm, dl_dimage, grad2d);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                              const float* target, float* image_out, double* l1_part, float* grad2d)
+{
+    LeafGeom g;
+    g.W = cam->width;
+    g.H = cam->height;
+    g.ltx0 = bins->leaf.tx0;
+    g.lty0 = bins->leaf.ty0;
+    g.TWL = bins->TWL;
+    g.px0 = bins->leaf.tx0 * 16;
+    g.py0 = bins->leaf.ty0 * 16;
+    g.WL = std::min(bins->leaf.tx1 * 16, cam->width) - g.px0;
+    g.PL = (int64_t)g.WL * (std::min(bins->leaf.ty1 * 16, cam->height) - g.py0);
+    const float inv_norm = (float)(1.0 / (3.0 * (double)cam->width * (double)cam->height));
+    if (bins->n_tiles > 0) {
+        const int64_t nt = bins->n_tiles;
+        std::vector<GsAlloc> tmp;
+        const uint32_t* order = bins->order;   // from the plan
+        if (!order) {
+            uint32_t* o = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nt, GS_MEM_RASTER, &tmp);
+            if (!o) return GS_ERR_OOM;
+            GsTimerScope ts(ctx, "tile_order");
+            hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, ctx->stream, nt, nullptr, bins->offsets, o);
+            order = o;
+        }
+        {
+            GsTimerScope ts(ctx, "raster_fused");
+            hipLaunchKernelGGL(k_raster_fused, dim3((unsigned)ceil_div(nt, kFusedWaves)), dim3(64 * kFusedWaves), 0,
+                               ctx->stream, g, nt,
+                               bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
+                               cam->bg[2], target, inv_norm, image_out, l1_part, grad2d, order);
+        }
+        gs_free_all(ctx, &tmp);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const uint64_t* base, const uint64_t* offsets,
+                                 uint32_t* order)
+{
+    if (n_sets > 0) {
+        GsTimerScope ts(ctx, "tile_order");
+        hipLaunchKernelGGL(k_tile_order, dim3((unsigned)n_sets), dim3(1024), 0, ctx->stream, (int64_t)0, base, offsets,
+                           order);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
