@@ -93,6 +93,8 @@ def _declare(L):
     L.gso_project_bwd.argtypes = [C.POINTER(Camera_c), i64, C.c_int] + [vp] * 5 + [vp] * 5
     L.gso_plan_leaves.restype = i32
     L.gso_plan_leaves.argtypes = [i32, i32, i64, vp, u64, C.POINTER(Cost_c), vp, i32, vp]
+    L.gso_replan_leaves.restype = i32
+    L.gso_replan_leaves.argtypes = [i32, i32, i64, vp, u64, C.POINTER(Cost_c), vp, i32, vp, i32, vp]
     L.gso_leaf_estimate.restype = u64
     L.gso_leaf_estimate.argtypes = [i32, i32, Rect_c, u64, u64, C.POINTER(Cost_c)]
     L.gso_adam.argtypes = [i64, vp, vp, vp, vp, i32, dbl, dbl, dbl, dbl]
@@ -257,16 +259,23 @@ def cost_struct(cost=None) -> Cost_c:
     return Cost_c(c["b_isect"], c["b_pixel"], c["b_tile"], c["b_const"], c["b_cell"])
 
 
-def plan_leaves(cam, rect_c, budget, cost=None, with_sat=False):
+def plan_leaves(cam, rect_c, budget, cost=None, with_sat=False, roots=None):
+    """Leaf plan of the candidates' tile rectangles; with roots (cached leaves,
+    dicts with tx0..ty1) the re-check of that layout instead of a fresh plan."""
     W, H = cam.width, cam.height
     TW, TH = (W + 15) // 16, (H + 15) // 16
     rect_c = _c(rect_c, np.int32)
     cs = cost_struct(cost)
     sat = np.zeros((TH + 1, TW + 1), np.uint64) if with_sat else None
-    n = lib().gso_plan_leaves(W, H, rect_c.shape[0], _p(rect_c), int(budget), C.byref(cs), None, 0, None)
+    if roots is None:
+        rr, nr = None, 0
+    else:
+        rr = (Rect_c * max(len(roots), 1))(*[Rect_c(r["tx0"], r["ty0"], r["tx1"], r["ty1"]) for r in roots])
+        rr, nr = C.cast(rr, C.c_void_p), len(roots)
+    n = lib().gso_replan_leaves(W, H, rect_c.shape[0], _p(rect_c), int(budget), C.byref(cs), rr, nr, None, 0, None)
     out = (Leaf_c * max(n, 1))()
-    lib().gso_plan_leaves(W, H, rect_c.shape[0], _p(rect_c), int(budget), C.byref(cs),
-                          C.cast(out, C.c_void_p), n, _p(sat))
+    lib().gso_replan_leaves(W, H, rect_c.shape[0], _p(rect_c), int(budget), C.byref(cs), rr, nr,
+                            C.cast(out, C.c_void_p), n, _p(sat))
     leaves = [dict(tx0=o.tx0, ty0=o.ty0, tx1=o.tx1, ty1=o.ty1, est_bytes=int(o.est_bytes),
                    over_budget=bool(o.over_budget)) for o in out[:n]]
     return (leaves, sat) if with_sat else leaves

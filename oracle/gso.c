@@ -731,6 +731,19 @@ int32_t gso_plan_leaves(int32_t W, int32_t H, int64_t n_cand, const int32_t* rec
                         uint64_t budget, const gso_cost* cost, gso_leaf* out,
                         int32_t max_leaves, uint64_t* sat_out)
 {
+    return gso_replan_leaves(W, H, n_cand, rect, budget, cost, NULL, 0, out, max_leaves, sat_out);
+}
+
+/* The re-check of a cached layout before it is executed (BoundedGS "02 /
+ * method": the region plan is checked against the current load before a
+ * view runs).  Reading: each cached leaf, in the given order, is kept when
+ * its estimate under the current candidates is within the budget and is
+ * otherwise split by the same rule as a fresh plan; leaves are never merged.
+ * roots = NULL: the whole tile grid, i.e. a fresh plan. */
+int32_t gso_replan_leaves(int32_t W, int32_t H, int64_t n_cand, const int32_t* rect,
+                          uint64_t budget, const gso_cost* cost, const gso_rect* roots,
+                          int32_t n_roots, gso_leaf* out, int32_t max_leaves, uint64_t* sat_out)
+{
     const int32_t TW = (W + 15) / 16, TH = (H + 15) / 16;
     const int32_t SW = (TW + 7) / 8, SH = (TH + 7) / 8;
     uint64_t* cnt = (uint64_t*)calloc((size_t)TW * TH, sizeof(uint64_t));
@@ -748,8 +761,12 @@ int32_t gso_plan_leaves(int32_t W, int32_t H, int64_t n_cand, const int32_t* rec
     make_sat(cnt, TH, TW, sat);
     make_sat(cnt8, SH, SW, sat8);
     plan_ctx pc = {W, H, TW, SW, sat, sat8, budget, cost, out, max_leaves, 0};
-    gso_rect all = {0, 0, TW, TH};
-    plan_rec(&pc, all);
+    if (roots) {
+        for (int32_t k = 0; k < n_roots; ++k) plan_rec(&pc, roots[k]);
+    } else {
+        gso_rect all = {0, 0, TW, TH};
+        plan_rec(&pc, all);
+    }
     free(cnt);
     free(cnt8);
     free(sat8);

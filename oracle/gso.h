@@ -165,6 +165,12 @@ void gso_project_bwd(const gso_camera* cam, int64_t n, int sh_degree,
 int32_t gso_plan_leaves(int32_t W, int32_t H, int64_t n_cand, const int32_t* rect,
                         uint64_t budget, const gso_cost* cost, gso_leaf* out,
                         int32_t max_leaves, uint64_t* sat);
+/* The same bisection started from cached leaves (roots, in order) instead of
+ * the whole grid: a root within the budget is kept, one over it is split;
+ * leaves are never merged.  roots = NULL: a fresh plan. */
+int32_t gso_replan_leaves(int32_t W, int32_t H, int64_t n_cand, const int32_t* rect,
+                          uint64_t budget, const gso_cost* cost, const gso_rect* roots,
+                          int32_t n_roots, gso_leaf* out, int32_t max_leaves, uint64_t* sat_out);
 /* est of a region with n_isect overlaps and n_cells candidate-super-cell
  * pairs over the super-cells it meets */
 uint64_t gso_leaf_estimate(int32_t W, int32_t H, gso_rect r, uint64_t n_isect, uint64_t n_cells,

@@ -29,9 +29,10 @@ def brute_cells(rect_c, TW, TH):
     return cnt
 
 
-def replan(cnt, W, H, budget, cells=None):
+def replan(cnt, W, H, budget, cells=None, roots=None):
     """The halving rule, with the overlap count of a region taken by brute
-    force, and its candidate-super-cell pairs over the super-cells it meets."""
+    force, and its candidate-super-cell pairs over the super-cells it meets;
+    started from the whole grid, or from each of the given regions in turn."""
     out = []
 
     def est(r):
@@ -57,7 +58,8 @@ def replan(cnt, W, H, budget, cells=None):
             m = ty0 + h // 2
             rec((tx0, ty0, tx1, m)); rec((tx0, m, tx1, ty1))
 
-    rec((0, 0, cnt.shape[1], cnt.shape[0]))
+    for r in (roots if roots is not None else [(0, 0, cnt.shape[1], cnt.shape[0])]):
+        rec(tuple(r))
     return out
 
 
@@ -129,3 +131,39 @@ def test_super_cell_count_bounds_the_coarse_pairs(W8, H8, n, seed):
             if ix0 < ix1 and iy0 < iy1:
                 pairs += ((ix1 - 1) // 8 - ix0 // 8 + 1) * ((iy1 - 1) // 8 - iy0 // 8 + 1)
         assert pairs <= cb
+
+
+@pytest.mark.parametrize("budget_a,budget_b", [(400_000, 400_000), (400_000, 120_000), (90_000, 1_000_000)])
+def test_recheck_of_a_cached_layout(oracle_lib, budget_a, budget_b):
+    """A layout planned for one view and re-checked for another (moved
+    camera, other budget): every cached leaf within the new budget is kept
+    as it is, the others are split by the halving rule from that leaf, and the
+    result still partitions the grid.  Re-checking a fresh plan against its own
+    view and budget returns it unchanged."""
+    wa = scenes.make_workload("c3_gmm4k", n=20_000, width=400, height=250, posed=True, seed=301)
+    wb = scenes.make_workload("c3_gmm4k", n=20_000, width=400, height=250, posed=True, seed=302)
+    cam = wa.camera
+    pa = oracle_lib.project(wa.camera, wa.scene, "f32")
+    rect_a = pa["rect"][pa["cand"]]
+    cached = oracle_lib.plan_leaves(cam, rect_a, budget_a, COST)
+    same = oracle_lib.plan_leaves(cam, rect_a, budget_a, COST, roots=cached)
+    assert [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in same] == \
+        [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in cached]
+    pb = oracle_lib.project(wb.camera, wb.scene, "f32")
+    rect_b = pb["rect"][pb["cand"]]
+    TW, TH = cam.tiles_x, cam.tiles_y
+    got = oracle_lib.plan_leaves(wb.camera, rect_b, budget_b, COST, roots=cached)
+    roots = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in cached]
+    expect = replan(brute_counts(rect_b, TW, TH), cam.width, cam.height, budget_b,
+                    brute_cells(rect_b, TW, TH), roots=roots)
+    assert [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in got] == expect
+    cover = np.zeros((TH, TW), np.int64)
+    for L in got:
+        cover[L["ty0"]:L["ty1"], L["tx0"]:L["tx1"]] += 1
+    assert (cover == 1).all()
+    kept = {r for r in roots} & {(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in got}
+    for L in got:
+        if (L["tx0"], L["ty0"], L["tx1"], L["ty1"]) in kept:
+            assert L["est_bytes"] <= budget_b or L["over_budget"]
+    if budget_b >= budget_a:
+        assert len(got) <= len(cached) or len(kept) < len(roots)
