@@ -67,6 +67,9 @@ def parse():
                     help="side (pixels) of the window the oracle rasterizes for the CPU baseline")
     ap.add_argument("--attr-steps", type=int, default=2,
                     help="steps of the per-kernel attribution pass (events around every kernel)")
+    ap.add_argument("--cached-layout", action="store_true",
+                    help="second-round views: every step after the first re-checks the first step's leaf layout "
+                         "against the current model instead of planning afresh")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (a known-traffic kernel for counter scaling)")
     return ap.parse_args()
@@ -106,9 +109,18 @@ def main():
         log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
         del src, dst
 
+    layout = []
+
     def step(k):
         adam = None if args.no_adam else dict(step=k, params=params, m=m, v=v, lr=1e-3)
-        return B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam)
+        if not args.cached_layout:
+            return B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam)
+        # the first step plans and returns its layout; later steps re-check it
+        r = B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam,
+                            max_leaves=0 if layout else 65536, leaves_in=layout or None)
+        if not layout:
+            layout.extend(r["leaves"])
+        return r
 
     k = 0
     for _ in range(args.warmup):
@@ -218,7 +230,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {sc.n} Gaussians SH{sc.sh_degree}, {cam.width}x{cam.height}, "
                                f"leaf budget {args.budget_mib:g} MiB, L1, leaf grads summed, "
-                               + ("one Adam step per view" if not args.no_adam else "no update"),
+                               + ("one Adam step per view" if not args.no_adam else "no update")
+                               + (", cached leaf layout re-checked per view" if args.cached_layout else ""),
                    "n_gaussians": sc.n, "width": cam.width, "height": cam.height,
                    "leaf_budget_mib": args.budget_mib, "parallelism": "single GPU"},
         "gaussians_per_s": round(sc.n / (ms_step * 1e-3), 1),

@@ -87,7 +87,8 @@ class gs_view_opts(C.Structure):
                 ("eps", C.c_float), ("strict_budget", C.c_int32), ("max_leaves", C.c_int32),
                 ("leaves_out", C.c_void_p), ("cost", C.c_void_p), ("image_out", C.c_void_p),
                 ("grad3d_out", C.c_void_p), ("params_rw", C.c_void_p), ("adam_m", C.c_void_p),
-                ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64)]
+                ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64), ("leaves_in", C.c_void_p),
+                ("n_leaves_in", C.c_int32), ("pad_in", C.c_int32)]
 
 
 class gs_view_result(C.Structure):
@@ -131,6 +132,7 @@ def load(path: str = LIB_PATH):
         "gs_default_cost_model": (gs_cost_model, []),
         "gs_project": (st, [vp, P(gs_camera), P(gs_params), P(vp), P(i64)]),
         "gs_plan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, P(i32)]),
+        "gs_replan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, vp, i32, P(i32)]),
         "gs_bin_sort": (st, [vp, P(gs_camera), vp, gs_tile_rect, P(vp), P(i64)]),
         "gs_render_fwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp, vp, P(vp)]),
         "gs_render_bwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp]),
@@ -291,6 +293,30 @@ def gs_plan_leaves(ctx: Context, cam, proj, budget_bytes: int, cost=None, strict
                  over_budget=bool(a.over_budget)) for a in arr[:n.value]]
 
 
+def _leaf_array(leaves):
+    arr = (gs_leaf * max(len(leaves), 1))()
+    for k, L in enumerate(leaves):
+        arr[k].tx0, arr[k].ty0, arr[k].tx1, arr[k].ty1 = L["tx0"], L["ty0"], L["tx1"], L["ty1"]
+    return arr
+
+
+def gs_replan_leaves(ctx: Context, cam, proj, budget_bytes: int, cached, cost=None, strict=False, max_leaves=4096):
+    cs = cost_struct(cost) if cost is not None else None
+    src = _leaf_array(cached)
+    n = C.c_int32()
+    while True:
+        arr = (gs_leaf * max_leaves)()
+        ctx.check(ctx.lib.gs_replan_leaves(ctx.handle, C.byref(camera_struct(cam)), proj, int(budget_bytes),
+                                           C.byref(cs) if cs is not None else None, int(strict),
+                                           C.cast(src, C.c_void_p), len(cached), C.cast(arr, C.c_void_p),
+                                           max_leaves, C.byref(n)))
+        if n.value <= max_leaves:
+            break
+        max_leaves = n.value
+    return [dict(tx0=a.tx0, ty0=a.ty0, tx1=a.tx1, ty1=a.ty1, est_bytes=int(a.est_bytes),
+                 over_budget=bool(a.over_budget)) for a in arr[:n.value]]
+
+
 def gs_bin_sort(ctx: Context, cam, proj, leaf):
     h = C.c_void_p()
     n = C.c_int64()
@@ -399,10 +425,16 @@ def gs_default_cost_model():
 
 
 def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0, loss="l1", lam=0.2,
-                  adam=None, image_out=None, grad3d_out=None, strict=False, cost=None, max_leaves=0):
+                  adam=None, image_out=None, grad3d_out=None, strict=False, cost=None, max_leaves=0,
+                  leaves_in=None):
     """One whole view in the library (see gs_train_view in include/gs.h).
-    adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk)."""
+    adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk).
+    leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh."""
     o = gs_view_opts()
+    src = _leaf_array(leaves_in) if leaves_in else None
+    if leaves_in:
+        o.leaves_in = C.cast(src, C.c_void_p)
+        o.n_leaves_in = len(leaves_in)
     o.budget_bytes = int(budget_bytes)
     o.loss_kind = 0 if loss == "l1" else 1
     o.ssim_lambda = float(lam)

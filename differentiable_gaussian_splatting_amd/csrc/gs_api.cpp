@@ -556,9 +556,12 @@ fail:
 // ---------------------------------------------------------------------------
 // planning
 
-gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
-                         const gs_cost_model* cost, int32_t strict, gs_leaf* leaves, int32_t max_leaves,
-                         int32_t* n_leaves)
+// A fresh plan (roots null) or the re-check of a cached layout: roots (host)
+// must tile the grid exactly; each is kept when within the budget and split
+// by the halving rule otherwise.
+static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
+                           const gs_cost_model* cost, int32_t strict, const gs_leaf* roots, int32_t n_roots,
+                           gs_leaf* leaves, int32_t max_leaves, int32_t* n_leaves)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     gs_status st;
@@ -572,18 +575,45 @@ gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj,
     const gs_cost_model cm = cost ? *cost : gs_default_cost_model();
     const int64_t T = (int64_t)proj->TW * proj->TH;
     const int32_t cap = (int32_t)std::min<int64_t>(std::max<int32_t>(max_leaves, 1), T);
+    if (n_roots > 0) {
+        // the cached leaves must cover every tile of the grid exactly once
+        if (!roots || n_roots > T) return gs_fail(ctx, GS_ERR_INVALID_ARG, "cached leaves: %d for %lld tiles",
+                                                  (int)n_roots, (long long)T);
+        std::vector<uint8_t> cover((size_t)T, 0);
+        for (int32_t k = 0; k < n_roots; ++k) {
+            const gs_leaf& R = roots[k];
+            if (R.tx0 < 0 || R.ty0 < 0 || R.tx1 > proj->TW || R.ty1 > proj->TH || R.tx0 >= R.tx1 || R.ty0 >= R.ty1)
+                return gs_fail(ctx, GS_ERR_INVALID_ARG, "cached leaf %d outside the tile grid or empty", (int)k);
+            for (int32_t ty = R.ty0; ty < R.ty1; ++ty)
+                for (int32_t tx = R.tx0; tx < R.tx1; ++tx) {
+                    uint8_t& c = cover[(size_t)ty * proj->TW + tx];
+                    if (c) return gs_fail(ctx, GS_ERR_INVALID_ARG, "cached leaves overlap at tile (%d, %d)", tx, ty);
+                    c = 1;
+                }
+        }
+        for (size_t t = 0; t < cover.size(); ++t)
+            if (!cover[t]) return gs_fail(ctx, GS_ERR_INVALID_ARG, "cached leaves leave tile %zu uncovered", t);
+    }
     std::vector<GsAlloc> tmp;
     if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) return st;
     uint64_t* sat = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (proj->TW + 1) * (int64_t)(proj->TH + 1),
                                          GS_MEM_SCRATCH, &tmp);
     gs_leaf* ldev = (gs_leaf*)gs_malloc(ctx, sizeof(gs_leaf) * cap, GS_MEM_SCRATCH, &tmp);
     int32_t* small = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * 2, GS_MEM_SCRATCH, &tmp);
+    gs_leaf* rdev = n_roots > 0 ? (gs_leaf*)gs_malloc(ctx, sizeof(gs_leaf) * n_roots, GS_MEM_SCRATCH, &tmp) : nullptr;
     int32_t hv[2] = {0, 0};
-    if (!sat || !ldev || !small) {
+    if (!sat || !ldev || !small || (n_roots > 0 && !rdev)) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
-    st = launch_plan(ctx, proj, sat, budget_bytes, &cm, ldev, cap, small, small + 1);
+    if (n_roots > 0) {
+        const hipError_t e = hipMemcpyAsync(rdev, roots, sizeof(gs_leaf) * n_roots, hipMemcpyHostToDevice, ctx->stream);
+        if (e != hipSuccess) {
+            gs_free_all(ctx, &tmp);
+            return gs_fail(ctx, GS_ERR_DEVICE, "cached leaf copy failed: %s", hipGetErrorString(e));
+        }
+    }
+    st = launch_plan(ctx, proj, sat, budget_bytes, &cm, rdev, n_roots, ldev, cap, small, small + 1);
     if (st == GS_OK) st = readback(ctx, small, sizeof(hv), hv);
     if (st == GS_OK && max_leaves > 0 && hv[0] > 0) {
         const int32_t nw = std::min(hv[0], max_leaves);
@@ -602,6 +632,22 @@ gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj,
     *n_leaves = hv[0];
     if (strict && hv[1]) return gs_fail(ctx, GS_ERR_BUDGET, "a single tile exceeds the budget");
     return GS_OK;
+}
+
+gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
+                         const gs_cost_model* cost, int32_t strict, gs_leaf* leaves, int32_t max_leaves,
+                         int32_t* n_leaves)
+{
+    return plan_impl(ctx, cam, proj, budget_bytes, cost, strict, nullptr, 0, leaves, max_leaves, n_leaves);
+}
+
+gs_status gs_replan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
+                           const gs_cost_model* cost, int32_t strict, const gs_leaf* cached, int32_t n_cached,
+                           gs_leaf* leaves, int32_t max_leaves, int32_t* n_leaves)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (!cached || n_cached < 1) return gs_fail(ctx, GS_ERR_INVALID_ARG, "no cached leaves");
+    return plan_impl(ctx, cam, proj, budget_bytes, cost, strict, cached, n_cached, leaves, max_leaves, n_leaves);
 }
 
 // ---------------------------------------------------------------------------
@@ -1089,14 +1135,17 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     std::vector<gs_leaf> leaves;
     const int32_t TW = proj->TW, TH = proj->TH;
     if (opts->budget_bytes > 0) {
+        // a fresh plan, or the re-check of the caller's cached layout
+        const gs_leaf* roots = opts->n_leaves_in > 0 ? opts->leaves_in : nullptr;
+        const int32_t nr = opts->n_leaves_in > 0 ? opts->n_leaves_in : 0;
         int32_t nl = 0;
         leaves.resize(4096);
-        st = gs_plan_leaves(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, leaves.data(),
-                            (int32_t)leaves.size(), &nl);
+        st = plan_impl(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, roots, nr, leaves.data(),
+                       (int32_t)leaves.size(), &nl);
         if (st == GS_OK && nl > (int32_t)leaves.size()) {
             leaves.resize(nl);
-            st = gs_plan_leaves(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, leaves.data(),
-                                nl, &nl);
+            st = plan_impl(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, roots, nr,
+                           leaves.data(), nl, &nl);
         }
         if (st != GS_OK) { gs_release(ctx, proj); return st; }
         leaves.resize(nl);

@@ -213,7 +213,8 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
 gs_status launch_tile_counts(gs_ctx* ctx, const gs_proj* proj, int32_t* grid);
 // leaf plan from proj->tile_cnt
 gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t budget, const gs_cost_model* cost,
-                      gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev, int32_t* overflow_dev);
+                      const gs_leaf* roots_dev, int32_t n_roots, gs_leaf* leaves_dev, int32_t max_leaves,
+                      int32_t* count_dev, int32_t* over_dev);
 
 // leaf -> candidate groups (planner.hip)
 gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot);

@@ -124,9 +124,13 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* to
     return before + x - v;
 }
 
-// frontier ping-pong in global memory; cap >= number of tiles
+// frontier ping-pong in global memory; cap >= number of tiles.  The frontier
+// starts as the whole grid, or as the given roots (a cached layout to
+// re-check, in order); each level splits every region over the budget in
+// place, so the leaves come out depth-first per root, roots in order.
 __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a,
                                                        int4* __restrict__ fa, int4* __restrict__ fb, int64_t cap,
+                                                       const gs_leaf* __restrict__ roots, int32_t n_roots,
                                                        gs_leaf* __restrict__ leaves, int32_t max_leaves,
                                                        int32_t* __restrict__ count_out,
                                                        int32_t* __restrict__ over_out)
@@ -135,8 +139,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a,
     __shared__ uint32_t s_total, s_any;
     int4* cur = fa;
     int4* nxt = fb;
-    if (threadIdx.x == 0) cur[0] = make_int4(0, 0, a.TW, a.TH);
     uint32_t n = 1;
+    if (n_roots > 0) {
+        for (int32_t i = threadIdx.x; i < n_roots; i += kPlanThreads)
+            cur[i] = make_int4(roots[i].tx0, roots[i].ty0, roots[i].tx1, roots[i].ty1);
+        n = (uint32_t)n_roots;
+    } else if (threadIdx.x == 0) {
+        cur[0] = make_int4(0, 0, a.TW, a.TH);
+    }
     __syncthreads();
     for (;;) {
         // one level: every region to split becomes two, in order
@@ -210,7 +220,8 @@ gs_status launch_tile_counts(gs_ctx* ctx, const gs_proj* proj, int32_t* grid)
 }
 
 gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t budget, const gs_cost_model* cost,
-                      gs_leaf* leaves_dev, int32_t max_leaves, int32_t* count_dev, int32_t* over_dev)
+                      const gs_leaf* roots_dev, int32_t n_roots, gs_leaf* leaves_dev, int32_t max_leaves,
+                      int32_t* count_dev, int32_t* over_dev)
 {
     const int TW = proj->TW, TH = proj->TH;
     const int SW = (TW + 7) >> 3, SH = (TH + 7) >> 3;
@@ -261,8 +272,8 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
     GS_HIP(ctx, hipMemsetAsync(over_dev, 0, sizeof(int32_t), ctx->stream));
     {
         GsTimerScope ts(ctx, "plan_split");
-        hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, ctx->stream, a, fa, fb, T, leaves_dev, max_leaves,
-                           count_dev, over_dev);
+        hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, ctx->stream, a, fa, fb, T, roots_dev, n_roots,
+                           leaves_dev, max_leaves, count_dev, over_dev);
     }
     gs_free_all(ctx, &tmp);
     GS_HIP(ctx, hipGetLastError());

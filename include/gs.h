@@ -192,6 +192,19 @@ gs_status gs_plan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj,
                          const gs_cost_model* cost, int32_t strict, gs_leaf* leaves, int32_t max_leaves,
                          int32_t* n_leaves);
 
+/* Re-check of a cached leaf layout before it is executed (BoundedGS page,
+ * "02 / method": a region plan is checked against the current load before
+ * it runs), e.g. the leaves of this view from an earlier round after the
+ * model has changed.  cached (host, n_cached >= 1) must tile the tile grid
+ * exactly (else GS_ERR_INVALID_ARG).  Each cached leaf, in order, is kept as
+ * it is when its estimate under proj's candidates is within budget_bytes and
+ * is otherwise split by the halving rule of gs_plan_leaves (depth-first);
+ * leaves are never merged.  Output, errors, strict mode and the plan groups
+ * attached to proj as for gs_plan_leaves.  Synchronises. */
+gs_status gs_replan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
+                           const gs_cost_model* cost, int32_t strict, const gs_leaf* cached, int32_t n_cached,
+                           gs_leaf* leaves, int32_t max_leaves, int32_t* n_leaves);
+
 /* Binning of one leaf (tile rectangle inside the grid).  BoundedGS page,
  * "01": raster buffers grow with the overlaps of Gaussians and image tiles.
  * One entry per (candidate, tile of its rectangle inside the leaf), sorted by
@@ -331,6 +344,10 @@ typedef struct {
                                  /* gradient array); > 0 runs them as two      */
                                  /* kernels per chunk of that many candidate   */
                                  /* slots (gradient buffer adam_chunk x F)     */
+    const gs_leaf* leaves_in;    /* host, nullable: a cached layout (e.g. this */
+    int32_t n_leaves_in;         /* view's leaves_out of an earlier round) to  */
+    int32_t pad_in;              /* re-check instead of planning afresh (as    */
+                                 /* gs_replan_leaves); with budget_bytes > 0   */
 } gs_view_opts;
 
 typedef struct {

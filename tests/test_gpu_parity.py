@@ -325,3 +325,80 @@ def test_isotropic_rotation_gradient_is_negligible(ctx):
     g = run_gpu_view(ctx, w, keep_bins=False)
     gg = grad3d_groups(g["grad3d"], 0)
     assert np.linalg.norm(gg["quats"]) <= 1e-4 * np.linalg.norm(gg["log_scales"])
+
+
+def _rects(leaves):
+    return [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"], L["over_budget"]) for L in leaves]
+
+
+@pytest.mark.parametrize("budget_b", [1_400_000, 700_000, 4_000_000])
+def test_replan_cached_layout_matches_oracle(ctx, budget_b):
+    """A layout planned on one view, re-checked on another (moved camera,
+    other budget) through gs_replan_leaves: the same leaves and estimates as
+    the oracle's re-check, bit for bit."""
+    cost = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
+    wa = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, posed=True, seed=121)
+    wb = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, posed=True, seed=122)
+    da = B.DeviceScene(wa.scene, ctx.device)
+    pa, _ = B.gs_project(ctx, wa.camera, da)
+    cached = B.gs_plan_leaves(ctx, wa.camera, pa, 1_400_000, cost=cost)
+    B.gs_release(ctx, pa)
+    db = B.DeviceScene(wb.scene, ctx.device)
+    pb, _ = B.gs_project(ctx, wb.camera, db)
+    got = B.gs_replan_leaves(ctx, wb.camera, pb, budget_b, cached, cost=cost)
+    B.gs_release(ctx, pb)
+    o32 = oracle.project(wb.camera, wb.scene, "f32")
+    rect_c = o32["rect"][o32["cand"]]
+    expect = oracle.plan_leaves(wb.camera, rect_c, budget_b, cost, roots=cached)
+    say(f"cached {len(cached)} leaves -> {len(got)} at budget {budget_b}")
+    assert len(cached) > 2
+    assert _rects(got) == _rects(expect)
+
+
+def test_train_view_with_cached_layout(ctx):
+    """Round 1 of a view returns its layout; round 2 (another view of the
+    sequence) re-checks that layout instead of planning afresh: loss, image,
+    leaves and every gradient group against the oracle's view over the
+    oracle's re-check of the same layout."""
+    import torch
+    cost = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
+    budget = 1_400_000
+    wa = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, posed=True, seed=123)
+    wb = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, posed=True, seed=124)
+    da = B.DeviceScene(wa.scene, ctx.device)
+    ra = B.gs_train_view(ctx, wa.camera, da, torch.from_numpy(wa.target).to(ctx.device), budget_bytes=budget,
+                         cost=cost, max_leaves=256)
+    cached = ra["leaves"]
+    db = B.DeviceScene(wb.scene, ctx.device)
+    K = (wb.scene.sh_degree + 1) ** 2
+    g3 = torch.zeros((wb.scene.n, 11 + 3 * K), dtype=torch.float32, device=ctx.device)
+    img = torch.zeros((3, wb.camera.height, wb.camera.width), dtype=torch.float32, device=ctx.device)
+    rb = B.gs_train_view(ctx, wb.camera, db, torch.from_numpy(wb.target).to(ctx.device), budget_bytes=budget,
+                         cost=cost, max_leaves=256, leaves_in=cached, image_out=img, grad3d_out=g3)
+    o32 = oracle.project(wb.camera, wb.scene, "f32")
+    leaves = oracle.plan_leaves(wb.camera, o32["rect"][o32["cand"]], budget, cost, roots=cached)
+    o = oracle.train_view(wb.camera, wb.scene, wb.target, leaves=leaves, cost=cost)
+    say(f"round 2: {len(cached)} cached leaves -> {rb['n_leaves']}")
+    assert _rects(rb["leaves"]) == _rects(leaves)
+    assert abs(rb["loss"] - o["loss"]) <= LOSS_TOL
+    assert np.abs(img.cpu().numpy() - o["image"]).max() <= IMG_TOL
+    gg, og = grad3d_groups(g3.cpu().numpy(), 3), grad3d_groups(o["grad3d"], 3)
+    for name in gg:
+        assert rel_l2(gg[name], og[name]) <= GRAD_TOL, name
+
+
+def test_replan_rejects_a_layout_that_does_not_tile_the_grid(ctx):
+    w = scenes.make_workload("c1_small", n=300, width=96, height=64, seed=125)
+    d = B.DeviceScene(w.scene, ctx.device)
+    p, _ = B.gs_project(ctx, w.camera, d)
+    TW, TH = w.camera.tiles_x, w.camera.tiles_y
+    bad = [[dict(tx0=0, ty0=0, tx1=TW, ty1=TH), dict(tx0=0, ty0=0, tx1=1, ty1=1)],   # overlap
+           [dict(tx0=0, ty0=0, tx1=TW - 1, ty1=TH)],                                  # a column uncovered
+           [dict(tx0=0, ty0=0, tx1=TW + 1, ty1=TH)]]                                  # outside the grid
+    for layout in bad:
+        with pytest.raises(B.GsError) as ei:
+            B.gs_replan_leaves(ctx, w.camera, p, 1 << 30, layout)
+        assert B.STATUS_NAMES[ei.value.status] == "GS_ERR_INVALID_ARG"
+    ok = B.gs_replan_leaves(ctx, w.camera, p, 1 << 30, [dict(tx0=0, ty0=0, tx1=TW, ty1=TH)])
+    assert [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in ok] == [(0, 0, TW, TH)]
+    B.gs_release(ctx, p)
