@@ -67,6 +67,12 @@ def parse():
                     help="side (pixels) of the window the oracle rasterizes for the CPU baseline")
     ap.add_argument("--attr-steps", type=int, default=2,
                     help="steps of the per-kernel attribution pass (events around every kernel)")
+    ap.add_argument("--layout", default="auto",
+                    help="auto: load-budgeted leaves; grid:N: a fixed N x N block layout rendered as given "
+                         "(the fixed-block baselines)")
+    ap.add_argument("--per-block-update", action="store_true",
+                    help="with --layout grid:N: one Adam step after every block (each block a view of its own: "
+                         "projection, binning, raster, backward and update), instead of one per view")
     ap.add_argument("--cached-layout", action="store_true",
                     help="second-round views: every step after the first re-checks the first step's leaf layout "
                          "against the current model instead of planning afresh")
@@ -110,8 +116,33 @@ def main():
         del src, dst
 
     layout = []
+    grid = None
+    if args.layout.startswith("grid:"):
+        nb = int(args.layout.split(":")[1])
+        grid = B.gs_grid_leaves(B.load(), cam.tiles_x, cam.tiles_y, nb, nb)
+    upd = [0]   # Adam steps taken
 
     def step(k):
+        if grid is not None:
+            if not args.per_block_update:
+                upd[0] += 1
+                adam = None if args.no_adam else dict(step=upd[0], params=params, m=m, v=v, lr=1e-3)
+                return B.gs_train_view(ctx, cam, params, target, budget_bytes=0, loss=w.loss, adam=adam,
+                                       leaves_in=grid)
+            tot = None
+            for blk in grid:
+                upd[0] += 1
+                adam = None if args.no_adam else dict(step=upd[0], params=params, m=m, v=v, lr=1e-3)
+                r = B.gs_train_view(ctx, cam, params, target, budget_bytes=0, loss=w.loss, adam=adam,
+                                    leaves_in=[blk], partial=True)
+                if tot is None:
+                    tot = dict(r)
+                else:
+                    tot["loss"] += r["loss"]
+                    tot["n_isect"] += r["n_isect"]
+                    tot["n_leaves"] += r["n_leaves"]
+                    tot["peak_bytes"] = max(tot["peak_bytes"], r["peak_bytes"])
+            return tot
         adam = None if args.no_adam else dict(step=k, params=params, m=m, v=v, lr=1e-3)
         if not args.cached_layout:
             return B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam)
@@ -229,11 +260,16 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {sc.n} Gaussians SH{sc.sh_degree}, {cam.width}x{cam.height}, "
-                               f"leaf budget {args.budget_mib:g} MiB, L1, leaf grads summed, "
-                               + ("one Adam step per view" if not args.no_adam else "no update")
-                               + (", cached leaf layout re-checked per view" if args.cached_layout else ""),
+                               + (f"fixed {args.layout[5:]}x{args.layout[5:]} blocks, L1, "
+                                  + ("one Adam step per block" if args.per_block_update
+                                     else "block grads summed, one Adam step per view")
+                                  if grid else
+                                  f"leaf budget {args.budget_mib:g} MiB, L1, leaf grads summed, "
+                                  + ("one Adam step per view" if not args.no_adam else "no update")
+                                  + (", cached leaf layout re-checked per view" if args.cached_layout else "")),
                    "n_gaussians": sc.n, "width": cam.width, "height": cam.height,
-                   "leaf_budget_mib": args.budget_mib, "parallelism": "single GPU"},
+                   "leaf_budget_mib": None if grid else args.budget_mib, "layout": args.layout,
+                   "parallelism": "single GPU"},
         "gaussians_per_s": round(sc.n / (ms_step * 1e-3), 1),
         "peak_working_set_gib": round(r["peak_bytes"] / 2 ** 30, 4),
         "peak_working_set_torch_gib": round(torch_peak / 2 ** 30, 4),

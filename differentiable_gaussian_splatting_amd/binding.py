@@ -88,7 +88,7 @@ class gs_view_opts(C.Structure):
                 ("leaves_out", C.c_void_p), ("cost", C.c_void_p), ("image_out", C.c_void_p),
                 ("grad3d_out", C.c_void_p), ("params_rw", C.c_void_p), ("adam_m", C.c_void_p),
                 ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64), ("leaves_in", C.c_void_p),
-                ("n_leaves_in", C.c_int32), ("pad_in", C.c_int32)]
+                ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32)]
 
 
 class gs_view_result(C.Structure):
@@ -133,6 +133,7 @@ def load(path: str = LIB_PATH):
         "gs_project": (st, [vp, P(gs_camera), P(gs_params), P(vp), P(i64)]),
         "gs_plan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, P(i32)]),
         "gs_replan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, vp, i32, P(i32)]),
+        "gs_grid_leaves": (st, [i32, i32, i32, i32, vp]),
         "gs_bin_sort": (st, [vp, P(gs_camera), vp, gs_tile_rect, P(vp), P(i64)]),
         "gs_render_fwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp, vp, P(vp)]),
         "gs_render_bwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp]),
@@ -317,6 +318,16 @@ def gs_replan_leaves(ctx: Context, cam, proj, budget_bytes: int, cached, cost=No
                  over_budget=bool(a.over_budget)) for a in arr[:n.value]]
 
 
+def gs_grid_leaves(lib, tiles_x: int, tiles_y: int, nx: int, ny: int):
+    """Fixed nx x ny block layout of the tile grid (host only; lib = the loaded library)."""
+    arr = (gs_leaf * max(nx * ny, 1))()
+    stv = lib.gs_grid_leaves(int(tiles_x), int(tiles_y), int(nx), int(ny), C.cast(arr, C.c_void_p))
+    if stv != GS_OK:
+        raise GsError(stv, "gs_grid_leaves")
+    return [dict(tx0=a.tx0, ty0=a.ty0, tx1=a.tx1, ty1=a.ty1, est_bytes=0, over_budget=False)
+            for a in arr[:nx * ny]]
+
+
 def gs_bin_sort(ctx: Context, cam, proj, leaf):
     h = C.c_void_p()
     n = C.c_int64()
@@ -426,7 +437,7 @@ def gs_default_cost_model():
 
 def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0, loss="l1", lam=0.2,
                   adam=None, image_out=None, grad3d_out=None, strict=False, cost=None, max_leaves=0,
-                  leaves_in=None):
+                  leaves_in=None, partial=False):
     """One whole view in the library (see gs_train_view in include/gs.h).
     adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk).
     leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh."""
@@ -435,6 +446,7 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     if leaves_in:
         o.leaves_in = C.cast(src, C.c_void_p)
         o.n_leaves_in = len(leaves_in)
+        o.leaves_in_partial = int(bool(partial))
     o.budget_bytes = int(budget_bytes)
     o.loss_kind = 0 if loss == "l1" else 1
     o.ssim_lambda = float(lam)

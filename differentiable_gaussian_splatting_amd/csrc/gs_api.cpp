@@ -251,7 +251,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     if (!lot || !cnt || !goff) { st = GS_ERR_OOM; goto out; }
     e = hipMemcpyAsync(plan.data(), ldev, sizeof(gs_leaf) * nl, hipMemcpyDeviceToHost, ctx->stream);
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
-    if ((st = launch_leaf_map(ctx, ldev, nl, proj->TW, lot)) != GS_OK) goto out;
+    if ((st = launch_leaf_map(ctx, ldev, nl, proj->TW, proj->TH, lot)) != GS_OK) goto out;
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
     if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
     if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;   // also completes the plan copy
@@ -557,11 +557,11 @@ fail:
 // planning
 
 // A fresh plan (roots null) or the re-check of a cached layout: roots (host)
-// must tile the grid exactly; each is kept when within the budget and split
-// by the halving rule otherwise.
+// must tile the grid exactly (partial: must not overlap); each is kept when
+// within the budget and split by the halving rule otherwise.
 static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
                            const gs_cost_model* cost, int32_t strict, const gs_leaf* roots, int32_t n_roots,
-                           gs_leaf* leaves, int32_t max_leaves, int32_t* n_leaves)
+                           gs_leaf* leaves, int32_t max_leaves, int32_t* n_leaves, bool partial = false)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     gs_status st;
@@ -591,7 +591,7 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
                     c = 1;
                 }
         }
-        for (size_t t = 0; t < cover.size(); ++t)
+        for (size_t t = 0; t < cover.size() && !partial; ++t)
             if (!cover[t]) return gs_fail(ctx, GS_ERR_INVALID_ARG, "cached leaves leave tile %zu uncovered", t);
     }
     std::vector<GsAlloc> tmp;
@@ -631,6 +631,22 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
     if (st != GS_OK) return st;
     *n_leaves = hv[0];
     if (strict && hv[1]) return gs_fail(ctx, GS_ERR_BUDGET, "a single tile exceeds the budget");
+    return GS_OK;
+}
+
+gs_status gs_grid_leaves(int32_t tiles_x, int32_t tiles_y, int32_t nx, int32_t ny, gs_leaf* out)
+{
+    if (!out || tiles_x < 1 || tiles_y < 1 || nx < 1 || ny < 1 || nx > tiles_x || ny > tiles_y)
+        return GS_ERR_INVALID_ARG;
+    for (int32_t j = 0; j < ny; ++j)
+        for (int32_t i = 0; i < nx; ++i) {
+            gs_leaf& L = out[(size_t)j * nx + i];
+            L = gs_leaf{};
+            L.tx0 = (int32_t)((int64_t)i * tiles_x / nx);
+            L.tx1 = (int32_t)((int64_t)(i + 1) * tiles_x / nx);
+            L.ty0 = (int32_t)((int64_t)j * tiles_y / ny);
+            L.ty1 = (int32_t)((int64_t)(j + 1) * tiles_y / ny);
+        }
     return GS_OK;
 }
 
@@ -1134,18 +1150,21 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
 
     std::vector<gs_leaf> leaves;
     const int32_t TW = proj->TW, TH = proj->TH;
-    if (opts->budget_bytes > 0) {
-        // a fresh plan, or the re-check of the caller's cached layout
+    if (opts->budget_bytes > 0 || opts->n_leaves_in > 0) {
+        // a fresh plan, the re-check of the caller's cached layout, or (budget
+        // 0) the caller's layout as it is
         const gs_leaf* roots = opts->n_leaves_in > 0 ? opts->leaves_in : nullptr;
         const int32_t nr = opts->n_leaves_in > 0 ? opts->n_leaves_in : 0;
+        const uint64_t budget = opts->budget_bytes > 0 ? opts->budget_bytes : ~0ull;
+        const bool partial = nr > 0 && opts->leaves_in_partial != 0;
         int32_t nl = 0;
         leaves.resize(4096);
-        st = plan_impl(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, roots, nr, leaves.data(),
-                       (int32_t)leaves.size(), &nl);
+        st = plan_impl(ctx, cam, proj, budget, opts->cost, opts->strict_budget, roots, nr, leaves.data(),
+                       (int32_t)leaves.size(), &nl, partial);
         if (st == GS_OK && nl > (int32_t)leaves.size()) {
             leaves.resize(nl);
-            st = plan_impl(ctx, cam, proj, opts->budget_bytes, opts->cost, opts->strict_budget, roots, nr,
-                           leaves.data(), nl, &nl);
+            st = plan_impl(ctx, cam, proj, budget, opts->cost, opts->strict_budget, roots, nr, leaves.data(), nl,
+                           &nl, partial);
         }
         if (st != GS_OK) { gs_release(ctx, proj); return st; }
         leaves.resize(nl);
@@ -1154,9 +1173,9 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         L.tx0 = 0; L.ty0 = 0; L.tx1 = TW; L.ty1 = TH;
         leaves.push_back(L);
     }
-    if (opts->loss_kind == 1 && leaves.size() != 1) {
+    if (opts->loss_kind == 1 && (leaves.size() != 1 || (opts->n_leaves_in > 0 && opts->leaves_in_partial))) {
         gs_release(ctx, proj);
-        return gs_fail(ctx, GS_ERR_INVALID_ARG, "the SSIM loss is computed on the full image (budget 0)");
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "the SSIM loss is computed on the full image (one leaf)");
     }
     if (opts->leaves_out && opts->max_leaves > 0)
         std::memcpy(opts->leaves_out, leaves.data(), sizeof(gs_leaf) * std::min<size_t>(leaves.size(), opts->max_leaves));

@@ -217,7 +217,7 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
                       int32_t* count_dev, int32_t* over_dev);
 
 // leaf -> candidate groups (planner.hip)
-gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot);
+gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int TH, int32_t* lot);
 gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
                             const int32_t* lot, uint32_t* cnt, const uint64_t* off, uint32_t* keys, uint32_t* vals);
 // Per-view offsets of a plan: per grouped entry (sorted by leaf) its coarse

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void k_leaf_pairs(int64_t n, const uint32_t* _
     const int4 r = rect[j];
     const int a = lot[(int64_t)r.y * TW + r.x], b = lot[(int64_t)r.y * TW + r.z - 1];
     const int c = lot[(int64_t)(r.w - 1) * TW + r.x], d = lot[(int64_t)(r.w - 1) * TW + r.z - 1];
-    if (a == b && a == c && a == d) {
+    if (a >= 0 && a == b && a == c && a == d) {   // the four corners in one leaf: the rectangle inside it
         if (EMIT) {
             keys[off[k]] = (uint32_t)a;
             vals[off[k]] = j;
@@ -456,8 +456,11 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
     return GS_OK;
 }
 
-gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int32_t* lot)
+gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int TH, int32_t* lot)
 {
+    // -1 on tiles no leaf covers (a layout that renders part of the view)
+    gs_status st = launch_fill_u32(ctx, (uint32_t*)lot, 0xFFFFFFFFu, (int64_t)TW * TH);
+    if (st != GS_OK) return st;
     if (n_leaves > 0)
         hipLaunchKernelGGL(k_leaf_map, dim3((unsigned)n_leaves), dim3(256), 0, ctx->stream, leaves_dev, TW, lot);
     GS_HIP(ctx, hipGetLastError());

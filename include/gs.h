@@ -174,6 +174,16 @@ gs_cost_model gs_default_cost_model(void);
 gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, gs_proj** out,
                      int64_t* n_cand);
 
+/* A fixed grid layout, the fixed-block baselines of BoundedGS "03 /
+ * results" (Fig. 5: blocks 2K pixels wide; Fig. 6: 1 x 1, 2 x 2, 4 x 4):
+ * nx x ny blocks of the tiles_x x tiles_y tile grid; block (i, j) spans tiles
+ * [floor(i tiles_x / nx), floor((i + 1) tiles_x / nx)) x [floor(j tiles_y /
+ * ny), floor((j + 1) tiles_y / ny)) and is written at out[j nx + i] (host,
+ * nx * ny entries; est_bytes 0).  Host only, no context.  Errors:
+ * GS_ERR_INVALID_ARG unless out != NULL, 1 <= nx <= tiles_x and
+ * 1 <= ny <= tiles_y. */
+gs_status gs_grid_leaves(int32_t tiles_x, int32_t tiles_y, int32_t nx, int32_t ny, gs_leaf* out);
+
 /* Leaf planning.  BoundedGS page, "01": regions sized by load estimated from
  * overlap counts, pixels and buffer layout; Fig. 3 B->C: regions over the
  * budget are subdivided.  Per-tile overlap counts of all candidates ->
@@ -344,10 +354,16 @@ typedef struct {
                                  /* gradient array); > 0 runs them as two      */
                                  /* kernels per chunk of that many candidate   */
                                  /* slots (gradient buffer adam_chunk x F)     */
-    const gs_leaf* leaves_in;    /* host, nullable: a cached layout (e.g. this */
-    int32_t n_leaves_in;         /* view's leaves_out of an earlier round) to  */
-    int32_t pad_in;              /* re-check instead of planning afresh (as    */
-                                 /* gs_replan_leaves); with budget_bytes > 0   */
+    const gs_leaf* leaves_in;    /* host, nullable: a layout to use instead of */
+    int32_t n_leaves_in;         /* planning afresh.  budget_bytes > 0: it is  */
+                                 /* re-checked as by gs_replan_leaves (e.g.    */
+                                 /* this view's leaves_out of an earlier       */
+                                 /* round); budget_bytes = 0: it is rendered   */
+                                 /* as given (e.g. a gs_grid_leaves layout)    */
+    int32_t leaves_in_partial;   /* 1: leaves_in need not cover the grid (no   */
+                                 /* overlaps): only those leaves are rendered, */
+                                 /* loss and gradients are those of their      */
+                                 /* pixels (normaliser still 1/(3WH)); L1 only */
 } gs_view_opts;
 
 typedef struct {

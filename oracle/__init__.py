@@ -281,6 +281,14 @@ def plan_leaves(cam, rect_c, budget, cost=None, with_sat=False, roots=None):
     return (leaves, sat) if with_sat else leaves
 
 
+def grid_leaves(TW, TH, nx, ny):
+    """The fixed-block layout: nx x ny blocks of the tile grid, row by row;
+    block (i, j) covers tiles [i TW // nx, (i + 1) TW // nx) x [j TH // ny,
+    (j + 1) TH // ny) (BoundedGS "03 / results", Fig. 5 and 6)."""
+    return [dict(tx0=i * TW // nx, ty0=j * TH // ny, tx1=(i + 1) * TW // nx, ty1=(j + 1) * TH // ny)
+            for j in range(ny) for i in range(nx)]
+
+
 def leaf_estimate(cam, r: Rect_c, n_isect, cost=None, n_cells=0):
     cs = cost_struct(cost)
     return int(lib().gso_leaf_estimate(cam.width, cam.height, r, int(n_isect), int(n_cells), C.byref(cs)))

@@ -35,3 +35,30 @@ def test_default_cost_model_is_an_upper_bound_of_allocations():
     # per tile: 4 f64 L1 partials; fine work items (at most one per tile
     # beyond one per 512 pairs) with 64 u32 positions, super-tile id and offsets
     assert c["b_tile"] >= 32 + 64 * 4 + 4 + 12
+
+
+def test_grid_layout_matches_the_oracle_and_tiles_the_grid():
+    """gs_grid_leaves is host-only: its blocks are the oracle's fixed-block
+    layout, they tile the grid exactly, and invalid shapes are refused."""
+    import numpy as np
+    import oracle
+    lib = binding.load()
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        TW, TH = int(rng.integers(1, 400)), int(rng.integers(1, 300))
+        nx, ny = int(rng.integers(1, min(TW, 12) + 1)), int(rng.integers(1, min(TH, 12) + 1))
+        got = binding.gs_grid_leaves(lib, TW, TH, nx, ny)
+        assert [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in got] == \
+            [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in oracle.grid_leaves(TW, TH, nx, ny)]
+        cover = np.zeros((TH, TW), np.int32)
+        for L in got:
+            assert L["tx0"] < L["tx1"] and L["ty0"] < L["ty1"]
+            cover[L["ty0"]:L["ty1"], L["tx0"]:L["tx1"]] += 1
+        assert (cover == 1).all()
+    for bad in [(10, 10, 0, 1), (10, 10, 11, 1), (10, 10, 1, 11), (0, 10, 1, 1)]:
+        try:
+            binding.gs_grid_leaves(lib, *bad)
+        except binding.GsError as e:
+            assert binding.STATUS_NAMES[e.status] == "GS_ERR_INVALID_ARG"
+        else:
+            raise AssertionError(bad)
