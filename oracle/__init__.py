@@ -26,6 +26,7 @@ import os
 import numpy as np
 
 from . import build as _build
+from .skipgate import SkipGate, decide as gate_decide, rho_min_of  # noqa: F401
 
 _lib = None
 
