@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgsmi.so")
 SOURCES = ["gs_api.cpp", "scan.hip", "radix.hip", "project.hip", "binning.hip", "raster.hip", "planner.hip",
-           "loss.hip", "adam.hip"]
+           "loss.hip", "adam.hip", "gate.cpp"]
 HEADERS = ["gs_device.h", "gs_internal.h"]
 
 # Float discipline of the forward path: no contraction of a*b+c into fma (only

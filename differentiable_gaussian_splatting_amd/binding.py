@@ -91,6 +91,16 @@ class gs_view_opts(C.Structure):
                 ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32)]
 
 
+class gs_gate_decision(C.Structure):
+    _fields_ = [("backward", C.c_int32), ("forced", C.c_int32), ("score", C.c_double), ("rho_cum", C.c_double)]
+
+
+class gs_gate_stats(C.Structure):
+    _fields_ = [("steps", C.c_int64), ("backwards", C.c_int64), ("warmup_counted", C.c_int64),
+                ("warmup_proposed", C.c_int64), ("calibrated", C.c_int32), ("pad", C.c_int32),
+                ("rho_min", C.c_double)]
+
+
 class gs_view_result(C.Structure):
     _fields_ = [("loss", C.c_double), ("n_cand", C.c_int64), ("n_isect", C.c_int64), ("n_leaves", C.c_int32),
                 ("pad", C.c_int32), ("peak_bytes", C.c_uint64)]
@@ -134,6 +144,10 @@ def load(path: str = LIB_PATH):
         "gs_plan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, P(i32)]),
         "gs_replan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, vp, i32, P(i32)]),
         "gs_grid_leaves": (st, [i32, i32, i32, i32, vp]),
+        "gs_gate_create": (st, [i32, i32, C.c_double, C.c_double, C.c_double, P(vp)]),
+        "gs_gate_destroy": (None, [vp]),
+        "gs_gate_step": (st, [vp, i32, C.c_double, P(gs_gate_decision)]),
+        "gs_gate_get_stats": (st, [vp, P(gs_gate_stats)]),
         "gs_bin_sort": (st, [vp, P(gs_camera), vp, gs_tile_rect, P(vp), P(i64)]),
         "gs_render_fwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp, vp, P(vp)]),
         "gs_render_bwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp]),
@@ -326,6 +340,45 @@ def gs_grid_leaves(lib, tiles_x: int, tiles_y: int, nx: int, ny: int):
         raise GsError(stv, "gs_grid_leaves")
     return [dict(tx0=a.tx0, ty0=a.ty0, tx1=a.tx1, ty1=a.ty1, est_bytes=0, over_budget=False)
             for a in arr[:nx * ny]]
+
+
+class Gate:
+    """The library's SkipGS backward gate (host only; see gs_gate_* in include/gs.h)."""
+
+    def __init__(self, n_views, warmup=500, beta=0.95, rho_lo=0.5, eps=1e-8, lib=None):
+        self.lib = lib or load()
+        self.handle = C.c_void_p()
+        stv = self.lib.gs_gate_create(int(n_views), int(warmup), float(beta), float(rho_lo), float(eps),
+                                      C.byref(self.handle))
+        if stv != GS_OK:
+            raise GsError(stv, "gs_gate_create")
+
+    def step(self, view, loss):
+        d = gs_gate_decision()
+        stv = self.lib.gs_gate_step(self.handle, int(view), float(loss), C.byref(d))
+        if stv != GS_OK:
+            raise GsError(stv, "gs_gate_step")
+        return dict(backward=bool(d.backward), forced=bool(d.forced), score=d.score, rho_cum=d.rho_cum)
+
+    def stats(self):
+        s = gs_gate_stats()
+        stv = self.lib.gs_gate_get_stats(self.handle, C.byref(s))
+        if stv != GS_OK:
+            raise GsError(stv, "gs_gate_get_stats")
+        return dict(steps=s.steps, backwards=s.backwards, warmup_counted=s.warmup_counted,
+                    warmup_proposed=s.warmup_proposed, calibrated=bool(s.calibrated),
+                    rho_min=s.rho_min if s.calibrated else None)
+
+    def close(self):
+        if self.handle:
+            self.lib.gs_gate_destroy(self.handle)
+            self.handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def gs_bin_sort(ctx: Context, cam, proj, leaf):

@@ -331,6 +331,43 @@ gs_status gs_util_exp(gs_ctx* ctx, const float* x, float* y, int64_t n);
  * GS_ERR_INVALID_ARG for n < 0 or null pointers with n > 0. */
 gs_status gs_util_exp_falloff(gs_ctx* ctx, const float* x, float* y, int64_t n);
 
+/* ---- SkipGS backward gate ------------------------------------------------ */
+/* Host-side state of a sequence of training views (SkipGS notes, "key
+ * design" items 1-3; the "worked example" is its test).  Per view v the gate
+ * keeps an EMA of v's forward loss.  At step t with view v and loss L:
+ *   score = L / (EMA_v + eps), +inf for a view never seen;
+ *   a backward is proposed iff score > 1;
+ *   EMA_v = beta EMA_v + (1 - beta) L whatever the decision (a view's first
+ *   loss starts its EMA);
+ *   steps 1..warmup always run their backward and count the proposals of
+ *   views that had an EMA; at step warmup + 1 the floor rho_min = rho_lo +
+ *   (1 - rho_lo) rho_hat is fixed, rho_hat = proposed / counted (0 if none);
+ *   after that a proposed skip is overridden (forced = 1) while
+ *   rho_cum = backwards so far / max(t - 1, 1) < rho_min.
+ * All arithmetic in double, in that order.  The notes' values: warmup 500,
+ * beta 0.95, rho_lo 0.5, eps 1e-8. */
+typedef struct gs_gate gs_gate;
+typedef struct {
+    int32_t backward;   /* 1: run this view's backward and update            */
+    int32_t forced;     /* 1: a proposed skip overridden by the floor         */
+    double score;       /* L / (EMA + eps), +inf for a first visit            */
+    double rho_cum;     /* backwards / max(t - 1, 1) before this step          */
+} gs_gate_decision;
+typedef struct {
+    int64_t steps, backwards, warmup_counted, warmup_proposed;
+    int32_t calibrated, pad;
+    double rho_min;     /* valid once calibrated                              */
+} gs_gate_stats;
+/* n_views >= 1, warmup >= 0, 0 <= beta < 1, 0 <= rho_lo <= 1, eps > 0, else
+ * GS_ERR_INVALID_ARG; GS_ERR_OOM.  *out owned by the caller
+ * (gs_gate_destroy). */
+gs_status gs_gate_create(int32_t n_views, int32_t warmup, double beta, double rho_lo, double eps, gs_gate** out);
+void gs_gate_destroy(gs_gate* gate);
+/* One step of the sequence: view in [0, n_views), loss finite (else
+ * GS_ERR_INVALID_ARG, state unchanged). */
+gs_status gs_gate_step(gs_gate* gate, int32_t view, double loss, gs_gate_decision* decision);
+gs_status gs_gate_get_stats(const gs_gate* gate, gs_gate_stats* stats);
+
 /* ---- one whole view ---------------------------------------------------- */
 
 typedef struct {

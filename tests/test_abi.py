@@ -62,3 +62,53 @@ def test_grid_layout_matches_the_oracle_and_tiles_the_grid():
             assert binding.STATUS_NAMES[e.status] == "GS_ERR_INVALID_ARG"
         else:
             raise AssertionError(bad)
+
+
+def test_gate_decisions_equal_the_oracle_gate():
+    """The library's SkipGS gate (host only) against the oracle's gate on
+    random view / loss sequences: every decision, forced flag, score, ratio
+    and the calibrated floor identical (both compute in double, same order)."""
+    import numpy as np
+    import oracle
+    lib = binding.load()
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        nv = int(rng.integers(1, 9))
+        warm = int(rng.integers(0, 60))
+        beta = float(rng.choice([0.95, 0.9, 0.5]))
+        g = binding.Gate(nv, warmup=warm, beta=beta, lib=lib)
+        o = oracle.SkipGate(nv, warmup=warm, beta=beta)
+        loss = 1.0
+        for t in range(int(rng.integers(50, 400))):
+            v = int(rng.integers(0, nv))
+            loss = max(1e-6, loss * float(rng.choice([0.97, 0.99, 1.0, 1.02])) + float(rng.normal(0, 1e-3)))
+            a, b = g.step(v, loss), o.step(v, loss)
+            assert (a["backward"], a["forced"]) == (b["backward"], b["forced"]), (trial, t)
+            assert a["score"] == b["score"] and a["rho_cum"] == b["rho_cum"]
+        s = g.stats()
+        assert s["backwards"] == o.b and s["steps"] == o.t
+        assert (s["rho_min"] is None) == (o.rho_min is None)
+        if o.rho_min is not None:
+            assert s["rho_min"] == o.rho_min
+        g.close()
+
+
+def test_gate_rejects_bad_arguments():
+    lib = binding.load()
+    for args in [(0, 10, 0.95, 0.5, 1e-8), (2, -1, 0.95, 0.5, 1e-8), (2, 10, 1.0, 0.5, 1e-8),
+                 (2, 10, 0.95, 1.5, 1e-8), (2, 10, 0.95, 0.5, 0.0)]:
+        try:
+            binding.Gate(*args[:1], warmup=args[1], beta=args[2], rho_lo=args[3], eps=args[4], lib=lib)
+        except binding.GsError as e:
+            assert binding.STATUS_NAMES[e.status] == "GS_ERR_INVALID_ARG"
+        else:
+            raise AssertionError(args)
+    g = binding.Gate(2, lib=lib)
+    for view, loss in [(2, 1.0), (-1, 1.0), (0, float("nan")), (0, float("inf"))]:
+        try:
+            g.step(view, loss)
+        except binding.GsError:
+            pass
+        else:
+            raise AssertionError((view, loss))
+    assert g.stats()["steps"] == 0
