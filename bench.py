@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--per-block-update", action="store_true",
                     help="with --layout grid:N: one Adam step after every block (each block a view of its own: "
                          "projection, binning, raster, backward and update), instead of one per view")
+    ap.add_argument("--skip-gate", type=int, default=0, metavar="VIEWS",
+                    help="a sequence over this many posed views with the SkipGS backward gate (warm-up: one pass "
+                         "over the views); times --steps gated views after it and prints that line instead")
     ap.add_argument("--cached-layout", action="store_true",
                     help="second-round views: every step after the first re-checks the first step's leaf layout "
                          "against the current model instead of planning afresh")
@@ -114,6 +117,10 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
         del src, dst
+
+    if args.skip_gate:
+        gated_sequence(args, B, scenes, torch, ctx, w, params, m, v, budget)
+        return
 
     layout = []
     grid = None
@@ -412,6 +419,68 @@ def measured_traffic(workload, kernel, n_leaves):
         return None
     kv = fields[kernel]
     return int(dict(zip(kv[0::2], kv[1::2]))["traffic_bytes_per_launch"])
+
+
+def gated_sequence(args, B, scenes, torch, ctx, w, params, m, v, budget):
+    """A training sequence over posed views of one scene with the SkipGS
+    gate: the warm-up is one pass over the views (every view runs its
+    backward), then --steps views are timed one by one.  A view whose
+    backward is skipped runs binning, forward and loss only; one that runs it
+    renders its leaves twice (forward for the loss, then forward + backward),
+    since the leaves' buffers are not kept between the passes."""
+    import numpy as np
+    nv = args.skip_gate
+    rng = np.random.default_rng(5000)
+    cams = [scenes.random_pose_camera(w.camera.width, w.camera.height, rng) for _ in range(nv)]
+    targets = [torch.from_numpy(scenes.target_image(rng, w.camera.width, w.camera.height)).to(params.means.device)
+               for _ in range(nv)]
+    gate = B.Gate(nv, warmup=nv)
+    k = [0]
+
+    def view(i):
+        k[0] += 1
+        return B.gs_train_view(ctx, cams[i % nv], params, targets[i % nv], budget_bytes=budget, loss=w.loss,
+                               adam=dict(step=k[0], params=params, m=m, v=v, lr=1e-3), gate=gate,
+                               gate_view=i % nv)
+
+    for i in range(nv):   # the warm-up pass
+        view(i)
+    torch.cuda.synchronize()
+    times, runs, forced = [], [], 0
+    t_all = time.perf_counter()
+    for i in range(nv, nv + args.steps):
+        t0 = time.perf_counter()
+        r = view(i)
+        times.append(time.perf_counter() - t0)
+        runs.append(r["backward"])
+        forced += 1 if r["forced"] else 0
+    t_all = time.perf_counter() - t_all
+    ms = 1e3 * t_all / args.steps
+    ran = [t for t, b in zip(times, runs) if b]
+    skipped = [t for t, b in zip(times, runs) if not b]
+    st = gate.stats()
+    P = w.camera.width * w.camera.height
+    log(f"[bench] gated sequence: {args.steps} views in {t_all:.3f}s: {ms:.2f} ms/view, backward ratio "
+        f"{sum(runs) / len(runs):.3f} (forced {forced}), floor {st['rho_min']}")
+    out = {
+        "metric": "fwd+bwd Mpixel/s per view and peak working set (GiB) on one MI355X",
+        "value": round(P / (ms * 1e-3) / 1e6, 3),
+        "unit": "Mpixel/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": nv, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.scene.n} Gaussians SH{w.scene.sh_degree}, "
+                               f"{w.camera.width}x{w.camera.height}, leaf budget {args.budget_mib:g} MiB, L1, "
+                               f"SkipGS gate over {nv} posed views, one Adam step per view that runs its backward",
+                   "n_gaussians": w.scene.n, "width": w.camera.width, "height": w.camera.height,
+                   "leaf_budget_mib": args.budget_mib, "parallelism": "single GPU"},
+        "gate": {"views": nv, "warmup_steps": nv, "backward_ratio": round(sum(runs) / len(runs), 4),
+                 "forced": forced, "rho_min": st["rho_min"],
+                 "ms_view_with_backward": round(1e3 * sum(ran) / len(ran), 3) if ran else None,
+                 "ms_view_skipped": round(1e3 * sum(skipped) / len(skipped), 3) if skipped else None},
+        "peak_working_set_gib": None, "roofline": None, "cpu_baseline": None,
+    }
+    gate.close()
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(w, window):

@@ -88,7 +88,8 @@ class gs_view_opts(C.Structure):
                 ("leaves_out", C.c_void_p), ("cost", C.c_void_p), ("image_out", C.c_void_p),
                 ("grad3d_out", C.c_void_p), ("params_rw", C.c_void_p), ("adam_m", C.c_void_p),
                 ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64), ("leaves_in", C.c_void_p),
-                ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32)]
+                ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32), ("gate", C.c_void_p),
+                ("gate_view", C.c_int32), ("pad_gate", C.c_int32)]
 
 
 class gs_gate_decision(C.Structure):
@@ -103,7 +104,8 @@ class gs_gate_stats(C.Structure):
 
 class gs_view_result(C.Structure):
     _fields_ = [("loss", C.c_double), ("n_cand", C.c_int64), ("n_isect", C.c_int64), ("n_leaves", C.c_int32),
-                ("pad", C.c_int32), ("peak_bytes", C.c_uint64)]
+                ("pad", C.c_int32), ("peak_bytes", C.c_uint64), ("gate_backward", C.c_int32),
+                ("gate_forced", C.c_int32), ("gate_score", C.c_double)]
 
 
 ALLOC_FN = C.CFUNCTYPE(C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p)
@@ -490,7 +492,7 @@ def gs_default_cost_model():
 
 def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0, loss="l1", lam=0.2,
                   adam=None, image_out=None, grad3d_out=None, strict=False, cost=None, max_leaves=0,
-                  leaves_in=None, partial=False):
+                  leaves_in=None, partial=False, gate=None, gate_view=0):
     """One whole view in the library (see gs_train_view in include/gs.h).
     adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk).
     leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh."""
@@ -500,6 +502,9 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
         o.leaves_in = C.cast(src, C.c_void_p)
         o.n_leaves_in = len(leaves_in)
         o.leaves_in_partial = int(bool(partial))
+    if gate is not None:
+        o.gate = gate.handle
+        o.gate_view = int(gate_view)
     o.budget_bytes = int(budget_bytes)
     o.loss_kind = 0 if loss == "l1" else 1
     o.ssim_lambda = float(lam)
@@ -525,6 +530,8 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
                                     _ptr(target), C.byref(o), C.byref(res)))
     out = dict(loss=res.loss, n_cand=res.n_cand, n_isect=res.n_isect, n_leaves=res.n_leaves,
                peak_bytes=res.peak_bytes)
+    if gate is not None:
+        out.update(backward=bool(res.gate_backward), forced=bool(res.gate_forced), score=res.gate_score)
     if max_leaves:
         out["leaves"] = [dict(tx0=a.tx0, ty0=a.ty0, tx1=a.tx1, ty1=a.ty1, est_bytes=int(a.est_bytes),
                               over_budget=bool(a.over_budget)) for a in leaves_arr[:min(res.n_leaves, max_leaves)]]

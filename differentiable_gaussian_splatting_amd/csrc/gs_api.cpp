@@ -1131,6 +1131,108 @@ gs_status gs_util_exp_falloff(gs_ctx* ctx, const float* x, float* y, int64_t n)
 // ---------------------------------------------------------------------------
 // one whole view
 
+}  // extern "C"
+
+// The leaves of one view: binning (the next leaf's on a second stream while
+// the current one is rendered, when every leaf is planned and not every
+// kernel is timed), then per leaf the fused forward + L1 (+ backward when
+// `backward`), or for the SSIM loss the forward, the loss and (when
+// `backward`) the raster backward.  L1 partials go to l1_view (4 per tile,
+// leaves side by side); 2D gradients are added to grad2d.
+static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const float* target,
+                               const gs_view_opts* opts, const std::vector<gs_leaf>& leaves, bool backward,
+                               float* grad2d, double* l1_view, float* image, float* dl_dimage, double* loss_ssim,
+                               int64_t* isect_total)
+{
+    gs_status st = GS_OK;
+    int64_t l1_off = 0;
+    *isect_total = 0;
+    CoarseBins cbs[2];
+    bool pipe = leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
+    for (const gs_leaf& L : leaves) pipe = pipe && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
+    if (pipe) {
+        const gs_leaf& L = leaves[0];
+        if ((st = ensure_side(ctx)) != GS_OK) return st;
+        if ((st = coarse_alloc(ctx, proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, &cbs[0])) != GS_OK) return st;
+        if ((st = coarse_on_side(ctx, proj, &cbs[0], ctx->ev_done[0])) != GS_OK) goto done;
+    }
+    for (size_t li = 0; li < leaves.size(); ++li) {
+        const gs_leaf& L = leaves[li];
+        gs_bins* bins = nullptr;
+        gs_raster* ras = nullptr;
+        int64_t ni = 0;
+        gs_tile_rect r{L.tx0, L.ty0, L.tx1, L.ty1};
+        if (pipe) {
+            // this leaf's first stage is done on the side stream; its slot
+            // array is written here, and the next leaf's first stage starts
+            // on the side stream behind everything queued so far
+            if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
+                st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
+                goto done;
+            }
+            if ((st = fine_finish(ctx, proj, &cbs[li & 1], &bins)) != GS_OK) goto done;
+            ni = bins->n_isect;
+            if (li + 1 < leaves.size()) {
+                const gs_leaf& N = leaves[li + 1];
+                CoarseBins& nx = cbs[(li + 1) & 1];
+                if ((st = coarse_alloc(ctx, proj, gs_tile_rect{N.tx0, N.ty0, N.tx1, N.ty1}, &nx)) == GS_OK)
+                    st = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
+                if (st != GS_OK) {
+                    gs_release(ctx, bins);
+                    goto done;
+                }
+            }
+        } else if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) {
+            goto done;
+        }
+        *isect_total += ni;
+        if (opts->loss_kind == 0) {
+            // L1: each pixel's loss gradient is its own residual sign, so the
+            // forward, the loss and the backward of a tile run in one wavefront
+            st = launch_raster_fused(ctx, cam, proj, bins, target, image, l1_view + l1_off, backward ? grad2d : nullptr,
+                                     backward);
+            l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
+        } else {
+            st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, nullptr, &ras);
+            if (st == GS_OK)
+                st = gs_loss_ssim(ctx, cam->width, cam->height, image, target, opts->ssim_lambda, dl_dimage, loss_ssim,
+                                  nullptr);
+            if (st == GS_OK && backward) st = gs_render_bwd(ctx, cam, proj, bins, ras, dl_dimage, grad2d);
+        }
+        gs_release(ctx, ras);
+        gs_release(ctx, bins);
+        if (st != GS_OK) goto done;
+    }
+done:
+    if (pipe) {
+        // nothing may be freed while the side stream could still use it
+        (void)hipStreamSynchronize(ctx->side);
+        for (CoarseBins& cb : cbs) gs_free_all(ctx, &cb.allocs);
+    }
+    return st;
+}
+
+// The view's loss: L1 from the per-tile partials (one sum, one read-back),
+// SSIM as gs_loss_ssim left it (after a synchronisation).
+static gs_status view_loss(gs_ctx* ctx, const gs_view_opts* opts, double* l1_view, int64_t l1_n, double* loss_dev,
+                           int64_t P, double* loss)
+{
+    gs_status st;
+    if (opts->loss_kind == 0) {
+        double s = 0.0;
+        // the sum adds into loss_dev: start from zero (a gated view sums twice)
+        if ((st = launch_fill_u32(ctx, (uint32_t*)loss_dev, 0u, 2)) != GS_OK) return st;
+        if (l1_n > 0 && (st = launch_sum_f64(ctx, l1_view, l1_n, 1, loss_dev, 1)) != GS_OK) return st;
+        if ((st = readback(ctx, loss_dev, sizeof(double), &s)) != GS_OK) return st;
+        *loss = s / (3.0 * (double)P);
+    } else if (hipStreamSynchronize(ctx->stream) != hipSuccess) {
+        return gs_fail(ctx, GS_ERR_DEVICE, "stream synchronisation failed");
+    }
+    return GS_OK;
+}
+
+extern "C" {
+
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result)
 {
@@ -1192,25 +1294,12 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     double loss = 0.0;
     int64_t isect_total = 0;
     // L1: the per-tile partials of every leaf side by side, summed once
-    int64_t l1_n = 0, l1_off = 0;
+    int64_t l1_n = 0;
     for (const gs_leaf& L : leaves) l1_n += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
     double* l1_view = opts->loss_kind == 0 && l1_n > 0
                           ? (double*)gs_malloc(ctx, sizeof(double) * l1_n, GS_MEM_LOSS, &view)
                           : nullptr;
-    // Binning of a leaf runs on a second stream while the previous leaf is
-    // rendered, when every leaf is planned (no host read-back in binning)
-    // (not while every kernel is timed: the per-kernel times would then
-    // include the waits of kernels sharing the GPU)
-    CoarseBins cbs[2];
-    bool pipe = leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
-    for (const gs_leaf& L : leaves) pipe = pipe && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
     if (!grad2d || !loss_dev || (opts->loss_kind == 0 && l1_n > 0 && !l1_view)) { st = GS_ERR_OOM; goto done; }
-    if (pipe) {
-        const gs_leaf& L = leaves[0];
-        if ((st = ensure_side(ctx)) != GS_OK) goto done;
-        if ((st = coarse_alloc(ctx, proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, &cbs[0])) != GS_OK) goto done;
-        if ((st = coarse_on_side(ctx, proj, &cbs[0], ctx->ev_done[0])) != GS_OK) goto done;
-    }
     if ((st = launch_fill_f32(ctx, grad2d, 0.0f, 9 * nc)) != GS_OK) goto done;
     if (hipMemsetAsync(loss_dev, 0, sizeof(double), ctx->stream) != hipSuccess) {
         st = gs_fail(ctx, GS_ERR_DEVICE, "memset failed");
@@ -1221,52 +1310,28 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         dl_dimage = (float*)gs_malloc(ctx, sizeof(float) * 3 * P, GS_MEM_LOSS, &view);
         if (!image || !dl_dimage) { st = GS_ERR_OOM; goto done; }
     }
-    for (size_t li = 0; li < leaves.size(); ++li) {
-        const gs_leaf& L = leaves[li];
-        gs_bins* bins = nullptr;
-        gs_raster* ras = nullptr;
-        int64_t ni = 0;
-        gs_tile_rect r{L.tx0, L.ty0, L.tx1, L.ty1};
-        if (pipe) {
-            // this leaf's first stage is done on the side stream; its slot
-            // array is written here, and the next leaf's first stage starts
-            // on the side stream behind everything queued so far
-            if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
-                st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
-                goto done;
-            }
-            if ((st = fine_finish(ctx, proj, &cbs[li & 1], &bins)) != GS_OK) goto done;
-            ni = bins->n_isect;
-            if (li + 1 < leaves.size()) {
-                const gs_leaf& N = leaves[li + 1];
-                CoarseBins& nx = cbs[(li + 1) & 1];
-                if ((st = coarse_alloc(ctx, proj, gs_tile_rect{N.tx0, N.ty0, N.tx1, N.ty1}, &nx)) == GS_OK)
-                    st = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
-                if (st != GS_OK) {
-                    gs_release(ctx, bins);
-                    goto done;
-                }
-            }
-        } else if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) {
+    if (opts->gate) {
+        // SkipGS gate: the forward and the loss of every leaf first, the
+        // decision, then (when it asks for the backward) the full pass; the
+        // leaves' buffers are not kept between the passes, so a view that
+        // runs its backward renders twice
+        if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, false, grad2d, l1_view, image, dl_dimage,
+                                &loss, &isect_total)) != GS_OK)
+            goto done;
+        if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, P, &loss)) != GS_OK) goto done;
+        gs_gate_decision d{};
+        if ((st = gs_gate_step(opts->gate, opts->gate_view, loss, &d)) != GS_OK) {
+            st = gs_fail(ctx, st, "gate step (view %d, loss %g)", (int)opts->gate_view, loss);
             goto done;
         }
-        isect_total += ni;
-        if (opts->loss_kind == 0) {
-            // L1: each pixel's loss gradient is its own residual sign, so the
-            // forward, the loss and the backward of a tile run in one wavefront
-            st = launch_raster_fused(ctx, cam, proj, bins, target, image, l1_view + l1_off, grad2d);
-            l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
-        } else {
-            st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, nullptr, &ras);
-            if (st == GS_OK)
-                st = gs_loss_ssim(ctx, cam->width, cam->height, image, target, opts->ssim_lambda, dl_dimage, &loss,
-                                  nullptr);
-            if (st == GS_OK) st = gs_render_bwd(ctx, cam, proj, bins, ras, dl_dimage, grad2d);
-        }
-        gs_release(ctx, ras);
-        gs_release(ctx, bins);
-        if (st != GS_OK) goto done;
+        result->gate_backward = d.backward;
+        result->gate_forced = d.forced;
+        result->gate_score = d.score;
+        if (!d.backward) goto finish;
     }
+    if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, true, grad2d, l1_view, image, dl_dimage, &loss,
+                            &isect_total)) != GS_OK)
+        goto done;
     if (opts->grad3d_out || opts->adam_step <= 0) {
         float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * nc, GS_MEM_GRAD, &view);
         if (!grad3d) { st = GS_ERR_OOM; goto done; }
@@ -1307,26 +1372,14 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
                 goto done;
         }
     }
-    if (opts->loss_kind == 0) {
-        double s = 0.0;
-        if (l1_off > 0 && (st = launch_sum_f64(ctx, l1_view, l1_off, 1, loss_dev, 1)) != GS_OK) goto done;
-        if ((st = readback(ctx, loss_dev, sizeof(double), &s)) != GS_OK) goto done;
-        loss = s / (3.0 * (double)P);
-    } else if (hipStreamSynchronize(ctx->stream) != hipSuccess) {
-        st = gs_fail(ctx, GS_ERR_DEVICE, "stream synchronisation failed");
-        goto done;
-    }
+    if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, P, &loss)) != GS_OK) goto done;
+finish:
     result->loss = loss;
     result->n_cand = n_cand;
     result->n_isect = isect_total;
     result->n_leaves = (int32_t)leaves.size();
     result->peak_bytes = ctx->peak - live0;
 done:
-    if (pipe) {
-        // nothing may be freed while the side stream could still use it
-        (void)hipStreamSynchronize(ctx->side);
-        for (CoarseBins& cb : cbs) gs_free_all(ctx, &cb.allocs);
-    }
     gs_free_all(ctx, &view);
     gs_release(ctx, proj);
     ctx->peak = std::max(ctx->peak, peak_before);

@@ -200,7 +200,7 @@ gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
 // forward + L1 + backward of one leaf in one launch (no per-pixel state in
 // memory); l1_part receives 4 doubles per tile of the leaf
 gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                              const float* target, float* image_out, double* l1_part, float* grad2d);
+                              const float* target, float* image_out, double* l1_part, float* grad2d, bool backward);
 // tiles of each of n_sets offset arrays (set L at base[L], base[L + 1] - base[L]
 // - 1 tiles) in the fused raster's launch order, written at the same bases
 gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const uint64_t* base, const uint64_t* offsets,

@@ -540,6 +540,7 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
 // One wavefront per workgroup: a tile's wavefront frees its slot the moment
 // it ends, instead of waiting for the other tiles of a shared workgroup.
 constexpr int kFusedWaves = 1;
+template <bool BWD>   // false: forward and L1 only (a view whose backward is skipped)
 __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, int64_t n_tiles,
                                                       const uint64_t* __restrict__ offsets,
                                                       const uint32_t* __restrict__ values,
@@ -657,6 +658,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
     }
     l1 = gsd::wave_sum_d(l1);
     if (lane < 4) l1_part[lt * 4 + lane] = lane == 0 ? l1 : 0.0;
+    if (!BWD) return;
 
     // ---- backward
     bwd_walk(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d);
@@ -776,7 +778,7 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
 }
 
 gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                              const float* target, float* image_out, double* l1_part, float* grad2d)
+                              const float* target, float* image_out, double* l1_part, float* grad2d, bool backward)
 {
     LeafGeom g;
     g.W = cam->width;
@@ -801,11 +803,16 @@ gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* 
             order = o;
         }
         {
-            GsTimerScope ts(ctx, "raster_fused");
-            hipLaunchKernelGGL(k_raster_fused, dim3((unsigned)ceil_div(nt, kFusedWaves)), dim3(64 * kFusedWaves), 0,
-                               ctx->stream, g, nt,
-                               bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
-                               cam->bg[2], target, inv_norm, image_out, l1_part, grad2d, order);
+            GsTimerScope ts(ctx, backward ? "raster_fused" : "raster_fused_fwd");
+            const dim3 grid((unsigned)ceil_div(nt, kFusedWaves)), block(64 * kFusedWaves);
+            if (backward)
+                hipLaunchKernelGGL(k_raster_fused<true>, grid, block, 0, ctx->stream, g, nt, bins->offsets, bins->values,
+                                   proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2], target, inv_norm,
+                                   image_out, l1_part, grad2d, order);
+            else
+                hipLaunchKernelGGL(k_raster_fused<false>, grid, block, 0, ctx->stream, g, nt, bins->offsets,
+                                   bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
+                                   target, inv_norm, image_out, l1_part, grad2d, order);
         }
         gs_free_all(ctx, &tmp);
     }

@@ -401,6 +401,11 @@ typedef struct {
                                  /* overlaps): only those leaves are rendered, */
                                  /* loss and gradients are those of their      */
                                  /* pixels (normaliser still 1/(3WH)); L1 only */
+    gs_gate* gate;               /* nullable: SkipGS gate of the sequence; the */
+    int32_t gate_view;           /* view's forward loss over all leaves goes   */
+    int32_t pad_gate;            /* to gs_gate_step(gate, gate_view, loss) and */
+                                 /* the backward, projection backward and      */
+                                 /* update run only when it says so            */
 } gs_view_opts;
 
 typedef struct {
@@ -408,6 +413,9 @@ typedef struct {
     int64_t n_cand, n_isect;     /* n_isect summed over leaves                 */
     int32_t n_leaves, pad;
     uint64_t peak_bytes;         /* library high-water mark during the view    */
+    int32_t gate_backward;       /* with a gate: the decision (else 0)         */
+    int32_t gate_forced;
+    double gate_score;
 } gs_view_result;
 
 /* One training view: gs_project -> gs_plan_leaves -> for each leaf
@@ -421,8 +429,14 @@ typedef struct {
  * one planned leaf, the binning of each next leaf up to its slot array runs
  * on a second stream of the library (default priority, created on first use)
  * while the current leaf is rendered, ordered by events; not while every
- * kernel is timed (gs_set_timing on, no gs_set_timing_only).  target: device
- * [3][H][W].  Synchronises. */
+ * kernel is timed (gs_set_timing on, no gs_set_timing_only).  With a gate
+ * (SkipGS notes, "key design"): first the forward and the loss of every
+ * leaf, then gs_gate_step; when it asks for the backward the leaves are
+ * binned and rendered again with their backward (the leaves' buffers are
+ * bounded, so they are not kept between the two passes), then the projection
+ * backward and the update; otherwise the view ends after its forward
+ * (gradients and parameters untouched).  target: device [3][H][W].
+ * Synchronises. */
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result);
 

@@ -442,3 +442,57 @@ def test_fixed_grid_views_match_oracle(ctx, blocks):
         with pytest.raises(B.GsError):   # a partial layout with overlapping blocks
             B.gs_train_view(ctx, w.camera, ds, torch.from_numpy(w.target).to(ctx.device), budget_bytes=0,
                             leaves_in=[grid[0], grid[0]], partial=True)
+
+
+@pytest.mark.parametrize("budget,factors,falling", [
+    (0, [1.0, 1.0, 0.8, 1.25, 0.9, 1.1, 1.05, 0.7, 1.3, 0.85], False),
+    (1_400_000, [1.0, 1.0, 0.8, 1.25, 0.9, 1.1, 1.05, 0.7, 1.3, 0.85], False),
+    # falling losses: the skips bring the backward ratio under the floor,
+    # which then forces backwards
+    (1_400_000, [1.0, 1.0, 0.9, 0.9, 0.8, 0.8, 0.7, 0.7, 0.6, 0.6], True)])
+def test_gated_view_sequence_matches_oracle(ctx, budget, factors, falling):
+    """A sequence of views through gs_train_view with the SkipGS gate: every
+    step's loss and decision against the oracle's gate fed with the oracle's
+    loss; a step that runs its backward gives the oracle's gradients, one
+    that skips it leaves the gradient buffer untouched.  The targets change
+    from step to step so that no score sits near 1."""
+    import torch
+    cost = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
+    views = [scenes.make_workload("c3_gmm4k", n=20000, width=400, height=250, posed=True, seed=s)
+             for s in (141, 142)]
+    scene = views[0].scene
+    ds = B.DeviceScene(scene, ctx.device)
+    K = (scene.sh_degree + 1) ** 2
+    gate = B.Gate(2, warmup=2)
+    og = oracle.SkipGate(2, warmup=2)
+    ran = skipped = forced = 0
+    for t, f in enumerate(factors):
+        v = t % 2
+        w = views[v]
+        tgt = (w.target * np.float32(f)).astype(np.float32)
+        g3 = torch.full((scene.n, 11 + 3 * K), float("nan"), dtype=torch.float32, device=ctx.device)
+        r = B.gs_train_view(ctx, w.camera, ds, torch.from_numpy(tgt).to(ctx.device), budget_bytes=budget,
+                            cost=cost, grad3d_out=g3, gate=gate, gate_view=v)
+        o = oracle.train_view(w.camera, scene, tgt, budget=budget if budget else None, cost=cost)
+        od = og.step(v, o["loss"])
+        say(f"step {t + 1} view {v}: loss {r['loss']:.6f} / {o['loss']:.6f}, score {r['score']:.4f}, "
+            f"backward {r['backward']} forced {r['forced']}")
+        assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+        assert (r["backward"], r["forced"]) == (od["backward"], od["forced"])
+        assert np.isinf(od["score"]) or abs(od["score"] - 1.0) > 1e-3
+        got = g3.cpu().numpy()
+        forced += 1 if r["forced"] else 0
+        if r["backward"]:
+            ran += 1
+            gg, ogr = grad3d_groups(got, 3), grad3d_groups(o["grad3d"], 3)
+            for name in gg:
+                assert rel_l2(gg[name], ogr[name]) <= GRAD_TOL, name
+        else:
+            skipped += 1
+            assert np.isnan(got).all()
+    st = gate.stats()
+    assert st["backwards"] == og.b and st["rho_min"] == og.rho_min
+    assert ran > 2 and skipped > 0
+    if falling:
+        assert forced > 0
+    gate.close()
