@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--skip-gate", type=int, default=0, metavar="VIEWS",
                     help="a sequence over this many posed views with the SkipGS backward gate (warm-up: one pass "
                          "over the views); times --steps gated views after it and prints that line instead")
+    ap.add_argument("--serial-leaves", action="store_true",
+                    help="render one leaf at a time (no overlap of consecutive leaves' rasters: a smaller peak)")
     ap.add_argument("--cached-layout", action="store_true",
                     help="second-round views: every step after the first re-checks the first step's leaf layout "
                          "against the current model instead of planning afresh")
@@ -152,7 +154,8 @@ def main():
             return tot
         adam = None if args.no_adam else dict(step=k, params=params, m=m, v=v, lr=1e-3)
         if not args.cached_layout:
-            return B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam)
+            return B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam,
+                                   serial_leaves=args.serial_leaves)
         # the first step plans and returns its layout; later steps re-check it
         r = B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam,
                             max_leaves=0 if layout else 65536, leaves_in=layout or None)
@@ -273,7 +276,8 @@ def main():
                                   if grid else
                                   f"leaf budget {args.budget_mib:g} MiB, L1, leaf grads summed, "
                                   + ("one Adam step per view" if not args.no_adam else "no update")
-                                  + (", cached leaf layout re-checked per view" if args.cached_layout else "")),
+                                  + (", cached leaf layout re-checked per view" if args.cached_layout else "")
+                                  + (", leaves rendered one at a time" if args.serial_leaves else "")),
                    "n_gaussians": sc.n, "width": cam.width, "height": cam.height,
                    "leaf_budget_mib": None if grid else args.budget_mib, "layout": args.layout,
                    "parallelism": "single GPU"},

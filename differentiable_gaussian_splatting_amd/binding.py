@@ -89,7 +89,7 @@ class gs_view_opts(C.Structure):
                 ("grad3d_out", C.c_void_p), ("params_rw", C.c_void_p), ("adam_m", C.c_void_p),
                 ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64), ("leaves_in", C.c_void_p),
                 ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32), ("gate", C.c_void_p),
-                ("gate_view", C.c_int32), ("pad_gate", C.c_int32)]
+                ("gate_view", C.c_int32), ("serial_leaves", C.c_int32)]
 
 
 class gs_gate_decision(C.Structure):
@@ -492,11 +492,12 @@ def gs_default_cost_model():
 
 def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0, loss="l1", lam=0.2,
                   adam=None, image_out=None, grad3d_out=None, strict=False, cost=None, max_leaves=0,
-                  leaves_in=None, partial=False, gate=None, gate_view=0):
+                  leaves_in=None, partial=False, gate=None, gate_view=0, serial_leaves=False):
     """One whole view in the library (see gs_train_view in include/gs.h).
     adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk).
     leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh."""
     o = gs_view_opts()
+    o.serial_leaves = int(bool(serial_leaves))
     src = _leaf_array(leaves_in) if leaves_in else None
     if leaves_in:
         o.leaves_in = C.cast(src, C.c_void_p)

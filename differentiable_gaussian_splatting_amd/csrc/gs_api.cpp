@@ -390,6 +390,14 @@ void gs_ctx_destroy(gs_ctx* ctx)
     if (ctx->ev_alloc) (void)hipEventDestroy(ctx->ev_alloc);
     for (hipEvent_t e : ctx->ev_done)
         if (e) (void)hipEventDestroy(e);
+    for (int k = 0; k < 2; ++k) {
+        if (ctx->rstream[k]) {
+            (void)hipStreamSynchronize(ctx->rstream[k]);
+            (void)hipStreamDestroy(ctx->rstream[k]);
+        }
+        if (ctx->ev_ready[k]) (void)hipEventDestroy(ctx->ev_ready[k]);
+        if (ctx->ev_rendered[k]) (void)hipEventDestroy(ctx->ev_rendered[k]);
+    }
     for (auto& t : ctx->timers) {
         (void)hipEventDestroy(t.start);
         (void)hipEventDestroy(t.stop);
@@ -779,6 +787,11 @@ static gs_status ensure_side(gs_ctx* ctx)
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_alloc, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[0], hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[1], hipEventDisableTiming));
+    for (int k = 0; k < 2; ++k) {
+        GS_HIP(ctx, hipStreamCreateWithFlags(&ctx->rstream[k], hipStreamNonBlocking));
+        GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_ready[k], hipEventDisableTiming));
+        GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_rendered[k], hipEventDisableTiming));
+    }
     return GS_OK;
 }
 
@@ -1148,6 +1161,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     int64_t l1_off = 0;
     *isect_total = 0;
     CoarseBins cbs[2];
+    gs_bins* inflight[2] = {nullptr, nullptr};   // bins of the leaves on the render streams
     bool pipe = leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
     for (const gs_leaf& L : leaves) pipe = pipe && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
     if (pipe) {
@@ -1186,6 +1200,38 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
             goto done;
         }
         *isect_total += ni;
+        if (opts->loss_kind == 0 && pipe && !opts->serial_leaves) {
+            // the fused raster of this leaf on render stream li & 1, once the
+            // main stream has written its lists; the previous leaf's raster
+            // may still run on the other render stream, and its bins are
+            // released (on the main stream) only after it has ended
+            const int k = (int)(li & 1);
+            hipStream_t main = ctx->stream;
+            if (hipEventRecord(ctx->ev_ready[k], main) != hipSuccess ||
+                hipStreamWaitEvent(ctx->rstream[k], ctx->ev_ready[k], 0) != hipSuccess) {
+                gs_release(ctx, bins);
+                st = gs_fail(ctx, GS_ERR_DEVICE, "render stream ordering failed");
+                goto done;
+            }
+            ctx->stream = ctx->rstream[k];
+            st = launch_raster_fused(ctx, cam, proj, bins, target, image, l1_view + l1_off,
+                                     backward ? grad2d : nullptr, backward);
+            ctx->stream = main;
+            if (st == GS_OK && hipEventRecord(ctx->ev_rendered[k], ctx->rstream[k]) != hipSuccess)
+                st = gs_fail(ctx, GS_ERR_DEVICE, "render event failed");
+            l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
+            inflight[k] = bins;
+            if (st != GS_OK) goto done;
+            if (li >= 1 && inflight[k ^ 1]) {
+                if (hipStreamWaitEvent(main, ctx->ev_rendered[k ^ 1], 0) != hipSuccess) {
+                    st = gs_fail(ctx, GS_ERR_DEVICE, "render stream wait failed");
+                    goto done;
+                }
+                gs_release(ctx, inflight[k ^ 1]);
+                inflight[k ^ 1] = nullptr;
+            }
+            continue;
+        }
         if (opts->loss_kind == 0) {
             // L1: each pixel's loss gradient is its own residual sign, so the
             // forward, the loss and the backward of a tile run in one wavefront
@@ -1205,7 +1251,17 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     }
 done:
     if (pipe) {
-        // nothing may be freed while the side stream could still use it
+        // the main stream follows the render streams before the last bins are
+        // released; nothing may be freed while the side stream could still
+        // use it
+        for (int k = 0; k < 2; ++k)
+            if (inflight[k]) {
+                if (hipStreamWaitEvent(ctx->stream, ctx->ev_rendered[k], 0) != hipSuccess) {
+                    (void)hipStreamSynchronize(ctx->rstream[k]);
+                    if (st == GS_OK) st = gs_fail(ctx, GS_ERR_DEVICE, "render stream wait failed");
+                }
+                gs_release(ctx, inflight[k]);
+            }
         (void)hipStreamSynchronize(ctx->side);
         for (CoarseBins& cb : cbs) gs_free_all(ctx, &cb.allocs);
     }

@@ -40,6 +40,10 @@ struct gs_ctx {
     // bins the next leaf while the current one is rendered, and its events
     hipStream_t side = nullptr;
     hipEvent_t ev_alloc = nullptr, ev_done[2] = {nullptr, nullptr};
+    // two render streams: consecutive leaves' fused rasters overlap, the
+    // next one filling the compute units the current one's last tiles leave
+    hipStream_t rstream[2] = {nullptr, nullptr};
+    hipEvent_t ev_ready[2] = {nullptr, nullptr}, ev_rendered[2] = {nullptr, nullptr};
     int num_cu = 256;
     size_t max_lds = 65536;
 };

@@ -403,9 +403,13 @@ typedef struct {
                                  /* pixels (normaliser still 1/(3WH)); L1 only */
     gs_gate* gate;               /* nullable: SkipGS gate of the sequence; the */
     int32_t gate_view;           /* view's forward loss over all leaves goes   */
-    int32_t pad_gate;            /* to gs_gate_step(gate, gate_view, loss) and */
+                                 /* to gs_gate_step(gate, gate_view, loss) and */
                                  /* the backward, projection backward and      */
                                  /* update run only when it says so            */
+    int32_t serial_leaves;       /* 1: render one leaf at a time; 0: a planned */
+                                 /* leaf's fused raster may start while the    */
+                                 /* previous one ends (two leaves' slot arrays */
+                                 /* held at once)                              */
 } gs_view_opts;
 
 typedef struct {
@@ -429,7 +433,11 @@ typedef struct {
  * one planned leaf, the binning of each next leaf up to its slot array runs
  * on a second stream of the library (default priority, created on first use)
  * while the current leaf is rendered, ordered by events; not while every
- * kernel is timed (gs_set_timing on, no gs_set_timing_only).  With a gate
+ * kernel is timed (gs_set_timing on, no gs_set_timing_only); and, for L1
+ * views unless serial_leaves, each leaf's fused raster runs on one of two
+ * render streams so that it can start while the previous leaf's last tiles
+ * are still being rendered (the previous leaf's lists are released after
+ * its raster ends).  With a gate
  * (SkipGS notes, "key design"): first the forward and the loss of every
  * leaf, then gs_gate_step; when it asks for the backward the leaves are
  * binned and rendered again with their backward (the leaves' buffers are

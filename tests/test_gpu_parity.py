@@ -149,9 +149,9 @@ def test_train_view_entry_point(ctx):
     assert r["n_cand"] == o["n_cand"] and r["n_isect"] == o["n_isect"]
 
 
-@pytest.mark.parametrize("seed,budget,corner", [(109, 2_500_000, False), (110, 1_400_000, False),
-                                               (111, 1_400_000, True)])
-def test_train_view_leaves_pipelined(ctx, seed, budget, corner):
+@pytest.mark.parametrize("seed,budget,corner,serial", [(109, 2_500_000, False, False), (110, 1_400_000, False, False),
+                                                      (111, 1_400_000, True, False), (110, 1_400_000, False, True)])
+def test_train_view_leaves_pipelined(ctx, seed, budget, corner, serial):
     """gs_train_view over several planned leaves bins each next leaf on a
     second stream while the current one is rendered: loss, image, leaves,
     intersections and every 3D gradient group against the oracle's leaf mode,
@@ -175,7 +175,7 @@ def test_train_view_leaves_pipelined(ctx, seed, budget, corner):
     g3 = torch.zeros((w.scene.n, 11 + 3 * K), dtype=torch.float32, device=ctx.device)
     img = torch.zeros((3, w.camera.height, w.camera.width), dtype=torch.float32, device=ctx.device)
     r = B.gs_train_view(ctx, w.camera, ds, target, budget_bytes=budget, cost=cost, image_out=img, grad3d_out=g3,
-                        max_leaves=64)
+                        max_leaves=64, serial_leaves=serial)
     o = oracle.train_view(w.camera, w.scene, w.target, budget=budget, cost=cost, keep_bins=corner)
     say(f"case seed {seed} budget {budget} corner {corner}: {r['n_leaves']} leaves")
     assert r["n_leaves"] == len(o["leaves"]) and r["n_leaves"] > 2
