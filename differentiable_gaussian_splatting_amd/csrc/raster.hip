@@ -125,9 +125,10 @@ __device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by
 // include) become lane masks, and the updates of a lane that includes the
 // entry run under that mask.  A lane's values for an entry it includes are
 // computed in exactly the order given above.
+// Returns whether the pixel stops before this entry.
 template <bool STATS>
-__device__ __forceinline__ void fwd_step(const Staged& S, int j, const float4 a, const float4 b, float pxc, float pyc,
-                                         float& T, float& C0, float& C1, float& C2, bool& active, uint32_t& lastn,
+__device__ __forceinline__ bool fwd_step(const Staged& S, int j, const float4 a, const float4 b, float pxc, float pyc,
+                                         float& T, float& C0, float& C1, float& C2, bool active, uint32_t& lastn,
                                          uint32_t& n_eval, uint32_t& n_inc)
 {
     const float dx = pxc - a.x, dy = pyc - a.y;
@@ -149,7 +150,6 @@ __device__ __forceinline__ void fwd_step(const Staged& S, int j, const float4 a,
         n_eval += active ? 1u : 0u;
         n_inc += contrib ? 1u : 0u;
     }
-    active = active && !stop;
     // the empty volatile asm keeps the compiler from turning these branches
     // into selects on every lane
     if (contrib) {
@@ -166,6 +166,7 @@ __device__ __forceinline__ void fwd_step(const Staged& S, int j, const float4 a,
         asm volatile("");
         lastn = __builtin_bit_cast(uint32_t, S.c[j].y);
     }
+    return stop;
 }
 
 template <bool STATS>
@@ -223,7 +224,8 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
         const int nk = __builtin_popcountll(km);
         gsd::wave_sync();
         for (int j = 0; j < nk; ++j)
-            fwd_step<STATS>(S, j, S.a[j], S.b[j], pxc, pyc, T, C0, C1, C2, active, lastn, n_eval, n_inc);
+            active = active && !fwd_step<STATS>(S, j, S.a[j], S.b[j], pxc, pyc, T, C0, C1, C2, active, lastn, n_eval,
+                                                n_inc);
         gsd::wave_sync();
     }
 
@@ -569,24 +571,27 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
     const uint64_t start = offsets[lt], end = offsets[lt + 1];
 
     // ---- forward over the four quadrants
+    // a pixel is still compositing while its walk end is the list length:
+    // a stop sets it to the stopping entry's position, which is smaller;
+    // pixels outside the image start at 0 (nothing to walk)
     float T[4], C0[4], C1[4], C2[4];
     uint32_t lst[4];
-    bool act[4], inside[4];
+    bool inside[4];
+    const uint32_t len = (uint32_t)(end - start);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int px = tx * 16 + (k & 1) * 8 + qx, py = ty * 16 + (k >> 1) * 8 + qy;
         inside[k] = px < g.W && py < g.H;
-        act[k] = inside[k];
         T[k] = 1.0f;
         C0[k] = C1[k] = C2[k] = 0.0f;
-        lst[k] = (uint32_t)(end - start);
+        lst[k] = inside[k] ? len : 0u;
     }
     uint32_t n_eval = 0, n_inc = 0;   // unused (no statistics here)
     for (uint64_t base = start; base < end; base += 64) {
         uint32_t aq = 0;   // quadrants with a pixel still compositing
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            if (gsd::ballot(act[k]) != 0) aq |= 1u << k;
+            if (gsd::ballot(lst[k] == len) != 0) aq |= 1u << k;
         if (aq == 0) break;
         const uint64_t e = base + lane;
         uint32_t qb = 0;
@@ -619,8 +624,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 if ((qm >> k) & 1u)
-                    fwd_step<false>(S, j, ea, eb, pxc[k & 1], pyc[k >> 1], T[k], C0[k], C1[k], C2[k], act[k], lst[k],
-                                    n_eval, n_inc);
+                    (void)fwd_step<false>(S, j, ea, eb, pxc[k & 1], pyc[k >> 1], T[k], C0[k], C1[k], C2[k],
+                                          lst[k] == len, lst[k], n_eval, n_inc);
         }
         gsd::wave_sync();
     }
@@ -650,8 +655,6 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
             gr1[k] = d1 > 0.0f ? inv_norm : (d1 < 0.0f ? -inv_norm : 0.0f);
             gr2[k] = d2 > 0.0f ? inv_norm : (d2 < 0.0f ? -inv_norm : 0.0f);
             l1 += fabs((double)o0 - (double)t0) + fabs((double)o1 - (double)t1) + fabs((double)o2 - (double)t2);
-        } else {
-            lst[k] = 0;   // outside the image: no entry is revisited
         }
         GS[k] = T[k] * (gr0[k] * bg0 + gr1[k] * bg1 + gr2[k] * bg2);
         mq[k] = __builtin_amdgcn_readfirstlane(gsd::wave_max_u32(lst[k]));
