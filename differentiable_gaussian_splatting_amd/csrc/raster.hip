@@ -127,7 +127,7 @@ __device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by
 // computed in exactly the order given above.
 // Returns whether the pixel stops before this entry.
 template <bool STATS>
-__device__ __forceinline__ bool fwd_step(const Staged& S, int j, const float4 a, const float4 b, float pxc, float pyc,
+__device__ __forceinline__ bool fwd_step(const float4 a, const float4 b, float cb, uint32_t pos, float pxc, float pyc,
                                          float& T, float& C0, float& C1, float& C2, bool active, uint32_t& lastn,
                                          uint32_t& n_eval, uint32_t& n_inc)
 {
@@ -157,14 +157,14 @@ __device__ __forceinline__ bool fwd_step(const Staged& S, int j, const float4 a,
         const float w = alpha * T;
         C0 = __builtin_fmaf(b.z, w, C0);
         C1 = __builtin_fmaf(b.w, w, C1);
-        C2 = __builtin_fmaf(S.c[j].x, w, C2);
+        C2 = __builtin_fmaf(cb, w, C2);
         T = Tn;
     }
     // a lane stops once per list: the end of its walk is the stopping entry's
     // list position
     if (stop) {
         asm volatile("");
-        lastn = __builtin_bit_cast(uint32_t, S.c[j].y);
+        lastn = pos;
     }
     return stop;
 }
@@ -223,9 +223,11 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
         }
         const int nk = __builtin_popcountll(km);
         gsd::wave_sync();
-        for (int j = 0; j < nk; ++j)
-            active = active && !fwd_step<STATS>(S, j, S.a[j], S.b[j], pxc, pyc, T, C0, C1, C2, active, lastn, n_eval,
-                                                n_inc);
+        for (int j = 0; j < nk; ++j) {
+            const float4 ec = S.c[j];
+            active = active && !fwd_step<STATS>(S.a[j], S.b[j], ec.x, __builtin_bit_cast(uint32_t, ec.y), pxc, pyc, T,
+                                                C0, C1, C2, active, lastn, n_eval, n_inc);
+        }
         gsd::wave_sync();
     }
 
@@ -620,11 +622,13 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
         for (int j = 0; j < nk; ++j) {
             const float4 ea = S.a[j];
             const float4 eb = S.b[j];
-            const uint32_t qm = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, S.c[j].z));
+            const float4 ec = S.c[j];
+            const uint32_t qm = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, ec.z));
+            const uint32_t pos = __builtin_bit_cast(uint32_t, ec.y);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 if ((qm >> k) & 1u)
-                    (void)fwd_step<false>(S, j, ea, eb, pxc[k & 1], pyc[k >> 1], T[k], C0[k], C1[k], C2[k],
+                    (void)fwd_step<false>(ea, eb, ec.x, pos, pxc[k & 1], pyc[k >> 1], T[k], C0[k], C1[k], C2[k],
                                           lst[k] == len, lst[k], n_eval, n_inc);
         }
         gsd::wave_sync();
