@@ -120,8 +120,8 @@ __device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by
     return cull_test(cull_prep(a, b), bx0, by0);
 }
 
-// One kept entry j of the staged batch at one pixel of the forward walk.
-// Every lane evaluates the entry; the per-lane decisions (skip, stop,
+// One kept entry of the staged batch (geometry a, b, blue cb, list position
+// pos) at one pixel of the forward walk.  Every lane evaluates the entry; the per-lane decisions (skip, stop,
 // include) become lane masks, and the updates of a lane that includes the
 // entry run under that mask.  A lane's values for an entry it includes are
 // computed in exactly the order given above.
