@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--cached-layout", action="store_true",
                     help="second-round views: every step after the first re-checks the first step's leaf layout "
                          "against the current model instead of planning afresh")
+    ap.add_argument("--target-host", action="store_true",
+                    help="keep the target image in pinned host memory; the library copies each leaf's pixels")
+    ap.add_argument("--loss", default="auto", choices=["auto", "l1", "l1_ssim"],
+                    help="override the workload's loss (l1_ssim: leaves rendered with an SSIM halo)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (a known-traffic kernel for counter scaling)")
     return ap.parse_args()
@@ -109,7 +113,9 @@ def main():
     ctx = B.Context()
     params = B.DeviceScene(sc, dev)
     m, v = B.like_scene(params), B.like_scene(params)
-    target = torch.from_numpy(w.target).to(dev)
+    target = torch.from_numpy(w.target).pin_memory() if args.target_host else torch.from_numpy(w.target).to(dev)
+    if args.loss != "auto":
+        w.loss = args.loss
     torch.cuda.synchronize()
     P = cam.width * cam.height
     if args.calib_copy_mib:
@@ -274,10 +280,14 @@ def main():
                                   + ("one Adam step per block" if args.per_block_update
                                      else "block grads summed, one Adam step per view")
                                   if grid else
-                                  f"leaf budget {args.budget_mib:g} MiB, L1, leaf grads summed, "
+                                  f"leaf budget {args.budget_mib:g} MiB, "
+                                  + ("L1" if w.loss == "l1" else "L1 + SSIM (one-tile halo per leaf)")
+                                  + ", leaf grads summed, "
                                   + ("one Adam step per view" if not args.no_adam else "no update")
                                   + (", cached leaf layout re-checked per view" if args.cached_layout else "")
-                                  + (", leaves rendered one at a time" if args.serial_leaves else "")),
+                                  + (", leaves rendered one at a time" if args.serial_leaves else "")
+                                  + (", target in pinned host memory copied leaf by leaf" if args.target_host
+                                     else "")),
                    "n_gaussians": sc.n, "width": cam.width, "height": cam.height,
                    "leaf_budget_mib": None if grid else args.budget_mib, "layout": args.layout,
                    "parallelism": "single GPU"},

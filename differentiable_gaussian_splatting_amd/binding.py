@@ -89,7 +89,7 @@ class gs_view_opts(C.Structure):
                 ("grad3d_out", C.c_void_p), ("params_rw", C.c_void_p), ("adam_m", C.c_void_p),
                 ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64), ("leaves_in", C.c_void_p),
                 ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32), ("gate", C.c_void_p),
-                ("gate_view", C.c_int32), ("serial_leaves", C.c_int32)]
+                ("gate_view", C.c_int32), ("serial_leaves", C.c_int32), ("target_host", C.c_int32)]
 
 
 class gs_gate_decision(C.Structure):
@@ -495,9 +495,14 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
                   leaves_in=None, partial=False, gate=None, gate_view=0, serial_leaves=False):
     """One whole view in the library (see gs_train_view in include/gs.h).
     adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk).
-    leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh."""
+    leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh.
+    target: a device tensor, or a CPU tensor (pinned for the copies to overlap), which the
+    library copies leaf by leaf."""
     o = gs_view_opts()
     o.serial_leaves = int(bool(serial_leaves))
+    o.target_host = int(not target.is_cuda)
+    if not target.is_cuda and not target.is_contiguous():
+        raise ValueError("a host target must be contiguous [3][H][W] float32")
     src = _leaf_array(leaves_in) if leaves_in else None
     if leaves_in:
         o.leaves_in = C.cast(src, C.c_void_p)

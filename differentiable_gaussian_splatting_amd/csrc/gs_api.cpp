@@ -938,10 +938,10 @@ fail:
 // gs_render_fwd with an optional caller-owned destination for the per-tile
 // L1 partials (l1_dst, 4 doubles per tile of the leaf): then the partials are
 // left there for the caller to sum once for several leaves, and loss_accum is
-// not touched.
+// not touched; target and image_out may be slices (frames tf, imf).
 static gs_status render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                            const float* target, double* loss_accum, float* image_out, uint64_t* stats,
-                            double* l1_dst, gs_raster** out)
+                            const float* target, PixFrame tf, double* loss_accum, float* image_out, PixFrame imf,
+                            uint64_t* stats, double* l1_dst, gs_raster** out)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     gs_status st;
@@ -971,7 +971,7 @@ static gs_status render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
         destroy_handle(ctx, r);
         return GS_ERR_OOM;
     }
-    if ((st = launch_raster_fwd(ctx, cam, proj, bins, r, target, image_out, l1_dst ? nullptr : loss_accum,
+    if ((st = launch_raster_fwd(ctx, cam, proj, bins, r, target, tf, image_out, imf, l1_dst ? nullptr : loss_accum,
                                 stats)) != GS_OK) {
         destroy_handle(ctx, r);
         return st;
@@ -984,7 +984,8 @@ gs_status gs_render_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, 
                         const float* target, double* loss_accum, float* image_out, uint64_t* stats,
                         gs_raster** out)
 {
-    return render_fwd(ctx, cam, proj, bins, target, loss_accum, image_out, stats, nullptr, out);
+    const PixFrame f = full_frame(cam->width, cam->height);
+    return render_fwd(ctx, cam, proj, bins, target, f, loss_accum, image_out, f, stats, nullptr, out);
 }
 
 gs_status gs_render_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
@@ -999,7 +1000,7 @@ gs_status gs_render_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, 
     if (!grad2d && proj->n_cand > 0) return gs_fail(ctx, GS_ERR_INVALID_ARG, "grad2d is NULL");
     if (!dl_dimage && !raster->sgn)
         return gs_fail(ctx, GS_ERR_INVALID_ARG, "no dL/dimage given and no L1 target fused in the forward");
-    return launch_raster_bwd(ctx, cam, proj, bins, raster, dl_dimage, grad2d);
+    return launch_raster_bwd(ctx, cam, proj, bins, raster, dl_dimage, full_frame(cam->width, cam->height), grad2d);
 }
 
 gs_status gs_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const gs_proj* proj,
@@ -1034,7 +1035,8 @@ gs_status gs_loss_ssim(gs_ctx* ctx, int32_t width, int32_t height, const float* 
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
-    gs_status st = launch_ssim(ctx, width, height, image, target, lambda, dl_dimage, part, nb, scratch);
+    gs_status st = launch_ssim(ctx, width, height, 0, 0, width, height, (float)(1.0 / (3.0 * (double)P)), image,
+                               target, lambda, dl_dimage, part, nb, scratch);
     if (st == GS_OK && (loss || ssim)) {
         st = launch_sum_f64(ctx, part, nb, 2, part + 2 * nb, 0);
         if (st == GS_OK) st = launch_sum_f64(ctx, part + 1, nb, 2, part + 2 * nb + 1, 0);
@@ -1146,40 +1148,170 @@ gs_status gs_util_exp_falloff(gs_ctx* ctx, const float* x, float* y, int64_t n)
 
 }  // extern "C"
 
+// A device copy of the target over one pixel rectangle (a leaf's, or a
+// leaf's with its SSIM halo), and the frame it is read through.
+struct TargetSlice {
+    float* ptr = nullptr;
+    PixFrame f{};
+    std::vector<GsAlloc> allocs;
+};
+
+// The pixel rectangle [x0, x0 + w) x [y0, y0 + h) of a tile rectangle,
+// clipped to the image.
+struct PixRect {
+    int x0, y0, w, h;
+};
+static PixRect pix_rect(const gs_camera* cam, gs_tile_rect r)
+{
+    PixRect p;
+    p.x0 = r.tx0 * 16;
+    p.y0 = r.ty0 * 16;
+    p.w = std::min(r.tx1 * 16, cam->width) - p.x0;
+    p.h = std::min(r.ty1 * 16, cam->height) - p.y0;
+    return p;
+}
+
+// Allocates (on the main stream) a slice for rectangle pr and copies the
+// target's pixels there on stream s: from host memory (host != 0) or from the
+// device-resident image.  The three channel planes are one 2D copy each.
+static gs_status slice_target(gs_ctx* ctx, const gs_camera* cam, const float* target, bool host, PixRect pr,
+                              TargetSlice* sl, hipStream_t s)
+{
+    const int64_t P = (int64_t)cam->width * cam->height, n = (int64_t)pr.w * pr.h;
+    sl->ptr = (float*)gs_malloc(ctx, sizeof(float) * 3 * n, GS_MEM_LOSS, &sl->allocs);
+    if (!sl->ptr) return GS_ERR_OOM;
+    sl->f = PixFrame{pr.x0, pr.y0, pr.w, n};
+    if (s != ctx->stream) {
+        GS_HIP(ctx, hipEventRecord(ctx->ev_alloc, ctx->stream));
+        GS_HIP(ctx, hipStreamWaitEvent(s, ctx->ev_alloc, 0));
+    }
+    for (int c = 0; c < 3; ++c)
+        GS_HIP(ctx, hipMemcpy2DAsync(sl->ptr + c * n, sizeof(float) * pr.w,
+                                     target + c * P + (int64_t)pr.y0 * cam->width + pr.x0,
+                                     sizeof(float) * cam->width, sizeof(float) * pr.w, pr.h,
+                                     host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice, s));
+    return GS_OK;
+}
+
+// One leaf of an SSIM view: its tile rectangle grown by one tile (16 pixels,
+// at least the 10 the 11 x 11 windows of its pixels' gradients reach) on each
+// side inside the grid is binned and rendered into a buffer of that size;
+// the SSIM terms of the centres inside the leaf and the gradient of its
+// pixels are exactly the whole image's (see loss.hip); the raster backward
+// runs with that gradient (zero on the halo).  The sums of S and |x - y|
+// over the leaf are added to acc[0], acc[1]; the leaf's pixels of the image
+// go to image_out when given.
+static gs_status ssim_leaf(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const float* target,
+                           bool target_host, const gs_view_opts* opts, gs_tile_rect r, bool backward, float* grad2d,
+                           float* image_out, double* acc, int64_t* ni)
+{
+    gs_status st = GS_OK;
+    const gs_tile_rect e{std::max(r.tx0 - 1, 0), std::max(r.ty0 - 1, 0), std::min(r.tx1 + 1, proj->TW),
+                         std::min(r.ty1 + 1, proj->TH)};
+    const PixRect ep = pix_rect(cam, e), op = pix_rect(cam, r);
+    const int64_t n = (int64_t)ep.w * ep.h, P = (int64_t)cam->width * cam->height;
+    const bool whole = ep.w == cam->width && ep.h == cam->height;
+    const PixFrame ef{ep.x0, ep.y0, ep.w, n};
+    gs_bins* bins = nullptr;
+    gs_raster* ras = nullptr;
+    TargetSlice ts;
+    std::vector<GsAlloc> tmp;
+    const float* tgt = target;
+    float* image = whole && image_out ? image_out : nullptr;
+    float* dl = nullptr;
+    float* scratch = nullptr;
+    double* part = nullptr;
+    const int64_t nb = ssim_partial_blocks(ep.w, ep.h);
+    if ((st = gs_bin_sort(ctx, cam, proj, e, &bins, ni)) != GS_OK) return st;
+    if (!whole || target_host) {
+        if ((st = slice_target(ctx, cam, target, target_host, ep, &ts, ctx->stream)) != GS_OK) goto done;
+        tgt = ts.ptr;
+    }
+    if (!image) image = (float*)gs_malloc(ctx, sizeof(float) * 3 * n, GS_MEM_LOSS, &tmp);
+    dl = (float*)gs_malloc(ctx, sizeof(float) * 3 * n, GS_MEM_LOSS, &tmp);
+    scratch = (float*)gs_malloc(ctx, sizeof(float) * 24 * n, GS_MEM_LOSS, &tmp);
+    part = (double*)gs_malloc(ctx, sizeof(double) * 2 * nb, GS_MEM_LOSS, &tmp);
+    if (!image || !dl || !scratch || !part) { st = GS_ERR_OOM; goto done; }
+    if ((st = render_fwd(ctx, cam, proj, bins, nullptr, ef, nullptr, image, ef, nullptr, nullptr, &ras)) != GS_OK)
+        goto done;
+    if ((st = launch_ssim(ctx, ep.w, ep.h, op.x0 - ep.x0, op.y0 - ep.y0, op.x0 - ep.x0 + op.w, op.y0 - ep.y0 + op.h,
+                          (float)(1.0 / (3.0 * (double)P)), image, tgt, opts->ssim_lambda, dl, part, nb, scratch)) !=
+        GS_OK)
+        goto done;
+    if ((st = launch_sum_f64(ctx, part, nb, 2, acc, 1)) != GS_OK) goto done;
+    if ((st = launch_sum_f64(ctx, part + 1, nb, 2, acc + 1, 1)) != GS_OK) goto done;
+    if (backward && (st = launch_raster_bwd(ctx, cam, proj, bins, ras, dl, ef, grad2d)) != GS_OK) goto done;
+    if (image_out && image != image_out)
+        for (int c = 0; c < 3; ++c)
+            if (hipMemcpy2DAsync(image_out + c * P + (int64_t)op.y0 * cam->width + op.x0, sizeof(float) * cam->width,
+                                 image + c * n + (int64_t)(op.y0 - ep.y0) * ep.w + (op.x0 - ep.x0),
+                                 sizeof(float) * ep.w, sizeof(float) * op.w, op.h, hipMemcpyDeviceToDevice,
+                                 ctx->stream) != hipSuccess) {
+                st = gs_fail(ctx, GS_ERR_DEVICE, "image copy failed");
+                goto done;
+            }
+done:
+    gs_release(ctx, ras);
+    gs_release(ctx, bins);
+    gs_free_all(ctx, &tmp);
+    gs_free_all(ctx, &ts.allocs);
+    return st;
+}
+
 // The leaves of one view: binning (the next leaf's on a second stream while
 // the current one is rendered, when every leaf is planned and not every
 // kernel is timed), then per leaf the fused forward + L1 (+ backward when
-// `backward`), or for the SSIM loss the forward, the loss and (when
-// `backward`) the raster backward.  L1 partials go to l1_view (4 per tile,
-// leaves side by side); 2D gradients are added to grad2d.
+// `backward`), or for the SSIM loss the forward over the leaf with a halo,
+// the loss and (when `backward`) the raster backward.  L1 partials go to
+// l1_view (4 per tile, leaves side by side); SSIM sums are added to
+// ssim_acc[0..1]; 2D gradients are added to grad2d.  A host target is copied
+// leaf by leaf (for a binned-ahead leaf on the second stream, before its
+// binning), each slice freed once its leaf's raster has ended.
 static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const float* target,
                                const gs_view_opts* opts, const std::vector<gs_leaf>& leaves, bool backward,
-                               float* grad2d, double* l1_view, float* image, float* dl_dimage, double* loss_ssim,
-                               int64_t* isect_total)
+                               float* grad2d, double* l1_view, float* image, double* ssim_acc, int64_t* isect_total)
 {
     gs_status st = GS_OK;
     int64_t l1_off = 0;
     *isect_total = 0;
+    const bool host = opts->target_host != 0;
+    const PixFrame full = full_frame(cam->width, cam->height);
     CoarseBins cbs[2];
+    TargetSlice sl[3];   // leaf li uses sl[li % 3]
     gs_bins* inflight[2] = {nullptr, nullptr};   // bins of the leaves on the render streams
-    bool pipe = leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
+    bool pipe = opts->loss_kind == 0 && leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
     for (const gs_leaf& L : leaves) pipe = pipe && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
+    if (opts->loss_kind == 1) {
+        if ((st = launch_fill_u32(ctx, (uint32_t*)ssim_acc, 0u, 4)) != GS_OK) return st;
+        for (const gs_leaf& L : leaves) {
+            int64_t ni = 0;
+            if ((st = ssim_leaf(ctx, cam, proj, target, host, opts, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1},
+                                backward, grad2d, image, ssim_acc, &ni)) != GS_OK)
+                return st;
+            *isect_total += ni;
+        }
+        return GS_OK;
+    }
     if (pipe) {
         const gs_leaf& L = leaves[0];
         if ((st = ensure_side(ctx)) != GS_OK) return st;
-        if ((st = coarse_alloc(ctx, proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, &cbs[0])) != GS_OK) return st;
+        if (host && (st = slice_target(ctx, cam, target, true, pix_rect(cam, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}),
+                                       &sl[0], ctx->side)) != GS_OK)
+            goto done;
+        if ((st = coarse_alloc(ctx, proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, &cbs[0])) != GS_OK) goto done;
         if ((st = coarse_on_side(ctx, proj, &cbs[0], ctx->ev_done[0])) != GS_OK) goto done;
     }
     for (size_t li = 0; li < leaves.size(); ++li) {
         const gs_leaf& L = leaves[li];
         gs_bins* bins = nullptr;
-        gs_raster* ras = nullptr;
         int64_t ni = 0;
         gs_tile_rect r{L.tx0, L.ty0, L.tx1, L.ty1};
+        TargetSlice& ts = sl[li % 3];
         if (pipe) {
-            // this leaf's first stage is done on the side stream; its slot
-            // array is written here, and the next leaf's first stage starts
-            // on the side stream behind everything queued so far
+            // this leaf's first stage (and its target slice) is done on the
+            // side stream; its slot array is written here, and the next
+            // leaf's first stage starts on the side stream behind everything
+            // queued so far
             if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
                 st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
                 goto done;
@@ -1188,23 +1320,32 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
             ni = bins->n_isect;
             if (li + 1 < leaves.size()) {
                 const gs_leaf& N = leaves[li + 1];
+                const gs_tile_rect nr{N.tx0, N.ty0, N.tx1, N.ty1};
                 CoarseBins& nx = cbs[(li + 1) & 1];
-                if ((st = coarse_alloc(ctx, proj, gs_tile_rect{N.tx0, N.ty0, N.tx1, N.ty1}, &nx)) == GS_OK)
+                if (host) st = slice_target(ctx, cam, target, true, pix_rect(cam, nr), &sl[(li + 1) % 3], ctx->side);
+                if (st == GS_OK && (st = coarse_alloc(ctx, proj, nr, &nx)) == GS_OK)
                     st = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
                 if (st != GS_OK) {
                     gs_release(ctx, bins);
                     goto done;
                 }
             }
-        } else if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) {
-            goto done;
+        } else {
+            if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
+            if (host && (st = slice_target(ctx, cam, target, true, pix_rect(cam, r), &ts, ctx->stream)) != GS_OK) {
+                gs_release(ctx, bins);
+                goto done;
+            }
         }
         *isect_total += ni;
-        if (opts->loss_kind == 0 && pipe && !opts->serial_leaves) {
+        const float* tgt = host ? ts.ptr : target;
+        const PixFrame tf = host ? ts.f : full;
+        if (pipe && !opts->serial_leaves) {
             // the fused raster of this leaf on render stream li & 1, once the
             // main stream has written its lists; the previous leaf's raster
-            // may still run on the other render stream, and its bins are
-            // released (on the main stream) only after it has ended
+            // may still run on the other render stream, and its bins (and
+            // target slice) are released (on the main stream) only after it
+            // has ended
             const int k = (int)(li & 1);
             hipStream_t main = ctx->stream;
             if (hipEventRecord(ctx->ev_ready[k], main) != hipSuccess ||
@@ -1214,7 +1355,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                 goto done;
             }
             ctx->stream = ctx->rstream[k];
-            st = launch_raster_fused(ctx, cam, proj, bins, target, image, l1_view + l1_off,
+            st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off,
                                      backward ? grad2d : nullptr, backward);
             ctx->stream = main;
             if (st == GS_OK && hipEventRecord(ctx->ev_rendered[k], ctx->rstream[k]) != hipSuccess)
@@ -1229,24 +1370,17 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                 }
                 gs_release(ctx, inflight[k ^ 1]);
                 inflight[k ^ 1] = nullptr;
+                gs_free_all(ctx, &sl[(li - 1) % 3].allocs);
             }
             continue;
         }
-        if (opts->loss_kind == 0) {
-            // L1: each pixel's loss gradient is its own residual sign, so the
-            // forward, the loss and the backward of a tile run in one wavefront
-            st = launch_raster_fused(ctx, cam, proj, bins, target, image, l1_view + l1_off, backward ? grad2d : nullptr,
-                                     backward);
-            l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
-        } else {
-            st = gs_render_fwd(ctx, cam, proj, bins, nullptr, nullptr, image, nullptr, &ras);
-            if (st == GS_OK)
-                st = gs_loss_ssim(ctx, cam->width, cam->height, image, target, opts->ssim_lambda, dl_dimage, loss_ssim,
-                                  nullptr);
-            if (st == GS_OK && backward) st = gs_render_bwd(ctx, cam, proj, bins, ras, dl_dimage, grad2d);
-        }
-        gs_release(ctx, ras);
+        // L1: each pixel's loss gradient is its own residual sign, so the
+        // forward, the loss and the backward of a tile run in one wavefront
+        st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off, backward ? grad2d : nullptr,
+                                 backward);
+        l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
         gs_release(ctx, bins);
+        gs_free_all(ctx, &ts.allocs);
         if (st != GS_OK) goto done;
     }
 done:
@@ -1265,13 +1399,14 @@ done:
         (void)hipStreamSynchronize(ctx->side);
         for (CoarseBins& cb : cbs) gs_free_all(ctx, &cb.allocs);
     }
+    for (TargetSlice& t : sl) gs_free_all(ctx, &t.allocs);
     return st;
 }
 
-// The view's loss: L1 from the per-tile partials (one sum, one read-back),
-// SSIM as gs_loss_ssim left it (after a synchronisation).
+// The view's loss: L1 from the per-tile partials (one sum, one read-back);
+// L1 + SSIM from the sums of |x - y| and S over the leaves (ssim_acc).
 static gs_status view_loss(gs_ctx* ctx, const gs_view_opts* opts, double* l1_view, int64_t l1_n, double* loss_dev,
-                           int64_t P, double* loss)
+                           const double* ssim_acc, int64_t P, double* loss)
 {
     gs_status st;
     if (opts->loss_kind == 0) {
@@ -1281,8 +1416,11 @@ static gs_status view_loss(gs_ctx* ctx, const gs_view_opts* opts, double* l1_vie
         if (l1_n > 0 && (st = launch_sum_f64(ctx, l1_view, l1_n, 1, loss_dev, 1)) != GS_OK) return st;
         if ((st = readback(ctx, loss_dev, sizeof(double), &s)) != GS_OK) return st;
         *loss = s / (3.0 * (double)P);
-    } else if (hipStreamSynchronize(ctx->stream) != hipSuccess) {
-        return gs_fail(ctx, GS_ERR_DEVICE, "stream synchronisation failed");
+    } else {
+        double hv[2] = {0.0, 0.0};
+        if ((st = readback(ctx, ssim_acc, sizeof(hv), hv)) != GS_OK) return st;
+        const double ssim = hv[0] / (3.0 * (double)P), l1 = hv[1] / (3.0 * (double)P);
+        *loss = (1.0 - opts->ssim_lambda) * l1 + opts->ssim_lambda * (1.0 - ssim);
     }
     return GS_OK;
 }
@@ -1315,14 +1453,20 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         const int32_t nr = opts->n_leaves_in > 0 ? opts->n_leaves_in : 0;
         const uint64_t budget = opts->budget_bytes > 0 ? opts->budget_bytes : ~0ull;
         const bool partial = nr > 0 && opts->leaves_in_partial != 0;
+        // Without a caller's model, the default one plus what the view holds
+        // per pixel of a leaf beyond the L1 raster: for SSIM 33 floats
+        // (image, gradient, target slice, 24 filter maps), for an L1 view
+        // with a host target its 3-float slice.
+        gs_cost_model cm = opts->cost ? *opts->cost : gs_default_cost_model();
+        if (!opts->cost) cm.b_pixel += opts->loss_kind == 1 ? 33 * 4 : (opts->target_host ? 3 * 4 : 0);
         int32_t nl = 0;
         leaves.resize(4096);
-        st = plan_impl(ctx, cam, proj, budget, opts->cost, opts->strict_budget, roots, nr, leaves.data(),
+        st = plan_impl(ctx, cam, proj, budget, &cm, opts->strict_budget, roots, nr, leaves.data(),
                        (int32_t)leaves.size(), &nl, partial);
         if (st == GS_OK && nl > (int32_t)leaves.size()) {
             leaves.resize(nl);
-            st = plan_impl(ctx, cam, proj, budget, opts->cost, opts->strict_budget, roots, nr, leaves.data(), nl,
-                           &nl, partial);
+            st = plan_impl(ctx, cam, proj, budget, &cm, opts->strict_budget, roots, nr, leaves.data(), nl, &nl,
+                           partial);
         }
         if (st != GS_OK) { gs_release(ctx, proj); return st; }
         leaves.resize(nl);
@@ -1331,9 +1475,9 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         L.tx0 = 0; L.ty0 = 0; L.tx1 = TW; L.ty1 = TH;
         leaves.push_back(L);
     }
-    if (opts->loss_kind == 1 && (leaves.size() != 1 || (opts->n_leaves_in > 0 && opts->leaves_in_partial))) {
+    if (opts->loss_kind == 1 && opts->n_leaves_in > 0 && opts->leaves_in_partial) {
         gs_release(ctx, proj);
-        return gs_fail(ctx, GS_ERR_INVALID_ARG, "the SSIM loss is computed on the full image (one leaf)");
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "the SSIM loss needs a layout that covers the image");
     }
     if (opts->leaves_out && opts->max_leaves > 0)
         std::memcpy(opts->leaves_out, leaves.data(), sizeof(gs_leaf) * std::min<size_t>(leaves.size(), opts->max_leaves));
@@ -1343,10 +1487,11 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     std::vector<GsAlloc> view;
     const int64_t nc = std::max<int64_t>(n_cand, 1);
     float* grad2d = (float*)gs_malloc(ctx, sizeof(float) * 9 * nc, GS_MEM_GRAD, &view);
-    double* loss_dev = (double*)gs_malloc(ctx, sizeof(double), GS_MEM_SCRATCH, &view);
+    // loss_dev[0]: the L1 sum; loss_dev[1..2]: the SSIM view's sums of S and
+    // |x - y|
+    double* loss_dev = (double*)gs_malloc(ctx, 3 * sizeof(double), GS_MEM_SCRATCH, &view);
     const int64_t P = (int64_t)cam->width * cam->height;
     float* image = opts->image_out;
-    float* dl_dimage = nullptr;
     double loss = 0.0;
     int64_t isect_total = 0;
     // L1: the per-tile partials of every leaf side by side, summed once
@@ -1357,24 +1502,16 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
                           : nullptr;
     if (!grad2d || !loss_dev || (opts->loss_kind == 0 && l1_n > 0 && !l1_view)) { st = GS_ERR_OOM; goto done; }
     if ((st = launch_fill_f32(ctx, grad2d, 0.0f, 9 * nc)) != GS_OK) goto done;
-    if (hipMemsetAsync(loss_dev, 0, sizeof(double), ctx->stream) != hipSuccess) {
-        st = gs_fail(ctx, GS_ERR_DEVICE, "memset failed");
-        goto done;
-    }
-    if (opts->loss_kind == 1) {
-        if (!image) image = (float*)gs_malloc(ctx, sizeof(float) * 3 * P, GS_MEM_LOSS, &view);
-        dl_dimage = (float*)gs_malloc(ctx, sizeof(float) * 3 * P, GS_MEM_LOSS, &view);
-        if (!image || !dl_dimage) { st = GS_ERR_OOM; goto done; }
-    }
+    if ((st = launch_fill_u32(ctx, (uint32_t*)loss_dev, 0u, 6)) != GS_OK) goto done;
     if (opts->gate) {
         // SkipGS gate: the forward and the loss of every leaf first, the
         // decision, then (when it asks for the backward) the full pass; the
         // leaves' buffers are not kept between the passes, so a view that
         // runs its backward renders twice
-        if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, false, grad2d, l1_view, image, dl_dimage,
-                                &loss, &isect_total)) != GS_OK)
+        if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, false, grad2d, l1_view, image, loss_dev + 1,
+                                &isect_total)) != GS_OK)
             goto done;
-        if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, P, &loss)) != GS_OK) goto done;
+        if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss)) != GS_OK) goto done;
         gs_gate_decision d{};
         if ((st = gs_gate_step(opts->gate, opts->gate_view, loss, &d)) != GS_OK) {
             st = gs_fail(ctx, st, "gate step (view %d, loss %g)", (int)opts->gate_view, loss);
@@ -1385,7 +1522,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         result->gate_score = d.score;
         if (!d.backward) goto finish;
     }
-    if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, true, grad2d, l1_view, image, dl_dimage, &loss,
+    if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, true, grad2d, l1_view, image, loss_dev + 1,
                             &isect_total)) != GS_OK)
         goto done;
     if (opts->grad3d_out || opts->adam_step <= 0) {
@@ -1428,7 +1565,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
                 goto done;
         }
     }
-    if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, P, &loss)) != GS_OK) goto done;
+    if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss)) != GS_OK) goto done;
 finish:
     result->loss = loss;
     result->n_cand = n_cand;

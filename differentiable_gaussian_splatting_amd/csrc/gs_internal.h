@@ -197,20 +197,31 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
                             bool* off_written = nullptr, uint32_t* scratch = nullptr);
 int64_t radix_scratch_words(int64_t n);
 
+// Where pixel (px, py) of channel c of an image buffer lives:
+// c * plane + (py - oy) * stride + (px - ox).  The whole image is
+// {0, 0, W, W * H}; a device slice of a rectangle starting at (x0, y0) and
+// w pixels wide is {x0, y0, w, w * h}.
+struct PixFrame {
+    int32_t ox, oy;
+    int64_t stride, plane;
+};
+inline PixFrame full_frame(int W, int H) { return PixFrame{0, 0, W, (int64_t)W * H}; }
+
 // raster.hip
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                            gs_raster* r, const float* target, float* image_out, double* loss_accum,
-                            uint64_t* stats);
+                            gs_raster* r, const float* target, PixFrame tf, float* image_out, PixFrame imf,
+                            double* loss_accum, uint64_t* stats);
 // forward + L1 + backward of one leaf in one launch (no per-pixel state in
 // memory); l1_part receives 4 doubles per tile of the leaf
 gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                              const float* target, float* image_out, double* l1_part, float* grad2d, bool backward);
+                              const float* target, PixFrame tf, float* image_out, double* l1_part, float* grad2d,
+                              bool backward);
 // tiles of each of n_sets offset arrays (set L at base[L], base[L + 1] - base[L]
 // - 1 tiles) in the fused raster's launch order, written at the same bases
 gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const uint64_t* base, const uint64_t* offsets,
                                  uint32_t* order);
 gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                            const gs_raster* r, const float* dl_dimage, float* grad2d);
+                            const gs_raster* r, const float* dl_dimage, PixFrame dlf, float* grad2d);
 
 // planner.hip
 // candidates per tile of the whole grid ([TH][TW], from the rectangles)
@@ -234,9 +245,14 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
                               uint32_t* leaf_cells, uint64_t* leaf_isect, const uint64_t* toff_base, uint64_t* toff);
 
 // loss.hip
-gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,
-                      float* dl_dimage, double* partials /*[n_blocks*2]*/, int64_t n_blocks,
-                      float* scratch /*[15][3][H][W] */);
+// L1 + SSIM over a W x H buffer (image, target, dl_dimage [3][H][W]) that is
+// the whole image or a rectangle of it: the windows are zero-padded at the
+// buffer's edges, the loss partials sum the centres in the owned rectangle
+// [ox0, ox1) x [oy0, oy1) (buffer coordinates), dl_dimage is written there
+// and zero elsewhere, and inv is 1 / (3 x the whole image's pixel count).
+gs_status launch_ssim(gs_ctx* ctx, int W, int H, int ox0, int oy0, int ox1, int oy1, float inv, const float* image,
+                      const float* target, float lambda, float* dl_dimage, double* partials /*[n_blocks*2]*/,
+                      int64_t n_blocks, float* scratch /*[24][H][W] */);
 int64_t ssim_partial_blocks(int W, int H);
 gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate);
 

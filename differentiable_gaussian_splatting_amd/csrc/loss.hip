@@ -1,5 +1,5 @@
-// loss.hip -- deterministic f64 sums and the full-image L1 + SSIM loss with
-// its gradient.
+// loss.hip -- deterministic f64 sums and the L1 + SSIM loss with its
+// gradient, over the whole image or over a leaf's rectangle with a halo.
 //
 // SkipGS notes, "loss function": L = (1 - lambda) L1 + lambda (1 - SSIM),
 // lambda = 0.2.  SSIM reading: 11x11 Gaussian window (sigma 1.5, weights
@@ -8,6 +8,18 @@
 // statistic is a horizontal then a vertical 11-tap pass; the gradient pushes
 // the per-pixel partials of SSIM back through the same (symmetric, hence
 // self-adjoint) zero-padded filter.
+//
+// Per leaf (the BoundedGS page, "02 / method", notes that windows computed
+// inside a leaf differ from the whole image's at its edges): the buffer is
+// the leaf's pixel rectangle grown by at least 10 pixels on each side
+// (clipped to the image).  A window centred within 5 pixels of the leaf reads
+// only pixels within 10 pixels of it, so every centre whose window reaches a
+// leaf pixel sees the whole image's values; zero padding at the buffer's
+// edges is the image's own where they meet the image border and elsewhere
+// only touches centres further than 5 pixels from the leaf, which neither an
+// owned term nor an owned pixel's gradient uses.  Each centre's SSIM term is
+// summed by the leaf that owns it, so the leaves' sums and gradients are
+// those of the whole image.
 #include "gs_device.h"
 #include "gs_internal.h"
 
@@ -84,10 +96,17 @@ __global__ __launch_bounds__(kSB) void k_ssim_h(int W, int H, Win win, const flo
     out[(4 * 3 + ch) * P + p] = e;
 }
 
+// Owned rectangle of the buffer: the centres whose SSIM terms (and pixels
+// whose L1 terms) are summed, and the pixels whose gradient is written.
+struct Owned {
+    int x0, y0, x1, y1;
+    __device__ bool has(int x, int y) const { return x >= x0 && x < x1 && y >= y0 && y < y1; }
+};
+
 // vertical pass + SSIM map + per-pixel partials dS/d(mu_x), dS/d(E[x^2]),
 // dS/d(E[xy]) into grad[(s * 3 + ch) * P + p]; block partial sums of S and
-// |x - y| into part[2 * block], part[2 * block + 1]
-__global__ __launch_bounds__(kSB) void k_ssim_v(int W, int H, Win win, const float* __restrict__ hs,
+// |x - y| over the owned rectangle into part[2 * block], part[2 * block + 1]
+__global__ __launch_bounds__(kSB) void k_ssim_v(int W, int H, Win win, Owned own, const float* __restrict__ hs,
                                                 const float* __restrict__ x, const float* __restrict__ y,
                                                 float* __restrict__ grad, double* __restrict__ part)
 {
@@ -120,8 +139,10 @@ __global__ __launch_bounds__(kSB) void k_ssim_v(int W, int H, Win win, const flo
         grad[(0 * 3 + ch) * P + p] = dS_dmx - 2.f * mx * dS_dsxx - my * dS_dsxy;
         grad[(1 * 3 + ch) * P + p] = dS_dsxx;
         grad[(2 * 3 + ch) * P + p] = dS_dsxy;
-        s_sum = (double)S;
-        l1_sum = fabs((double)x[k] - (double)y[k]);
+        if (own.has(px, py)) {
+            s_sum = (double)S;
+            l1_sum = fabs((double)x[k] - (double)y[k]);
+        }
     }
     s_sum = gsd::wave_sum_d(s_sum);
     l1_sum = gsd::wave_sum_d(l1_sum);
@@ -162,8 +183,9 @@ __global__ __launch_bounds__(kSB) void k_ssim_h2(int W, int H, Win win, const fl
     out[k] = a;
 }
 
-// vertical pass + gradient of the loss w.r.t. the image
-__global__ __launch_bounds__(kSB) void k_ssim_v2(int W, int H, Win win, const float* __restrict__ hs,
+// vertical pass + gradient of the loss w.r.t. the image (zero outside the
+// owned rectangle)
+__global__ __launch_bounds__(kSB) void k_ssim_v2(int W, int H, Win win, Owned own, const float* __restrict__ hs,
                                                  const float* __restrict__ x, const float* __restrict__ y,
                                                  float lambda, float inv, float* __restrict__ dl)
 {
@@ -173,6 +195,10 @@ __global__ __launch_bounds__(kSB) void k_ssim_v2(int W, int H, Win win, const fl
     const int ch = (int)(k / P);
     const int64_t p = k % P;
     const int py = (int)(p / W), px = (int)(p % W);
+    if (!own.has(px, py)) {
+        dl[k] = 0.0f;
+        return;
+    }
     float f[3] = {0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 11; ++t) {
@@ -215,8 +241,9 @@ gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, d
 
 int64_t ssim_partial_blocks(int W, int H) { return ceil_div(3 * (int64_t)W * H, kSB); }
 
-gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float* target, float lambda,
-                      float* dl_dimage, double* partials, int64_t n_blocks, float* scratch)
+gs_status launch_ssim(gs_ctx* ctx, int W, int H, int ox0, int oy0, int ox1, int oy1, float inv, const float* image,
+                      const float* target, float lambda, float* dl_dimage, double* partials, int64_t n_blocks,
+                      float* scratch)
 {
     Win win;
     double g[11], s = 0.0;
@@ -228,16 +255,16 @@ gs_status launch_ssim(gs_ctx* ctx, int W, int H, const float* image, const float
     const int64_t P = (int64_t)W * H;
     float* bufA = scratch;            // 15 maps
     float* bufB = scratch + 15 * P;   // 9 maps
-    const float inv = (float)(1.0 / (3.0 * (double)P));
+    const Owned own{ox0, oy0, ox1, oy1};
     GsTimerScope ts(ctx, "ssim");
     hipLaunchKernelGGL(k_ssim_h, dim3((unsigned)ceil_div(3 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, image,
                        target, bufA);
-    hipLaunchKernelGGL(k_ssim_v, dim3((unsigned)n_blocks), dim3(kSB), 0, ctx->stream, W, H, win, bufA, image, target,
-                       bufB, partials);
+    hipLaunchKernelGGL(k_ssim_v, dim3((unsigned)n_blocks), dim3(kSB), 0, ctx->stream, W, H, win, own, bufA, image,
+                       target, bufB, partials);
     hipLaunchKernelGGL(k_ssim_h2, dim3((unsigned)ceil_div(9 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, bufB,
                        bufA);
-    hipLaunchKernelGGL(k_ssim_v2, dim3((unsigned)ceil_div(3 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, bufA,
-                       image, target, lambda, inv, dl_dimage);
+    hipLaunchKernelGGL(k_ssim_v2, dim3((unsigned)ceil_div(3 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, own,
+                       bufA, image, target, lambda, inv, dl_dimage);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -174,8 +174,9 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
                                                     const uint32_t* __restrict__ values,
                                                     const float4* __restrict__ g0, const float4* __restrict__ g1,
                                                     const float4* __restrict__ g2, float bg0, float bg1, float bg2,
-                                                    const float* __restrict__ target, float inv_norm,
-                                                    float* __restrict__ image, float* __restrict__ tfinal,
+                                                    const float* __restrict__ target, PixFrame tf, float inv_norm,
+                                                    float* __restrict__ image, PixFrame imf,
+                                                    float* __restrict__ tfinal,
                                                     uint32_t* __restrict__ last, uint8_t* __restrict__ sgn,
                                                     double* __restrict__ l1_part,
                                                     unsigned long long* __restrict__ stats)
@@ -236,18 +237,18 @@ __global__ __launch_bounds__(256) void k_raster_fwd(LeafGeom g, const uint64_t* 
         const float o0 = __builtin_fmaf(T, bg0, C0);
         const float o1 = __builtin_fmaf(T, bg1, C1);
         const float o2 = __builtin_fmaf(T, bg2, C2);
-        const int64_t P = (int64_t)g.W * g.H;
-        const int64_t gi = (int64_t)py * g.W + px;
         if (image) {
-            image[gi] = o0;
-            image[P + gi] = o1;
-            image[2 * P + gi] = o2;
+            const int64_t ii = (int64_t)(py - imf.oy) * imf.stride + (px - imf.ox);
+            image[ii] = o0;
+            image[imf.plane + ii] = o1;
+            image[2 * imf.plane + ii] = o2;
         }
         const int64_t lp = (int64_t)(py - g.py0) * g.WL + (px - g.px0);
         tfinal[lp] = T;
         last[lp] = lastn;
         if (target) {
-            const float t0 = target[gi], t1 = target[P + gi], t2 = target[2 * P + gi];
+            const int64_t ti = (int64_t)(py - tf.oy) * tf.stride + (px - tf.ox);
+            const float t0 = target[ti], t1 = target[tf.plane + ti], t2 = target[2 * tf.plane + ti];
             const float d0 = o0 - t0, d1 = o1 - t1, d2 = o2 - t2;   // sign exact in f32
             // dL/dout = sgn(out - target) / (3WH): 2 bits per channel, 1 = +, 2 = -
             const uint32_t c0 = d0 > 0.0f ? 1u : (d0 < 0.0f ? 2u : 0u);
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
                                                     const float* __restrict__ tfinal,
                                                     const uint32_t* __restrict__ last,
                                                     const uint8_t* __restrict__ sgn, float inv_norm,
-                                                    const float* __restrict__ dl_dimage,
+                                                    const float* __restrict__ dl_dimage, PixFrame dlf,
                                                     float* __restrict__ grad2d)
 {
     __shared__ Staged st[4];
@@ -509,11 +510,10 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
             T[k] = tfinal[lp];
             lst[k] = last[lp];
             if (dl_dimage) {
-                const int64_t P = (int64_t)g.W * g.H;
-                const int64_t gi = (int64_t)py * g.W + px;
-                gr0[k] = dl_dimage[gi];
-                gr1[k] = dl_dimage[P + gi];
-                gr2[k] = dl_dimage[2 * P + gi];
+                const int64_t di = (int64_t)(py - dlf.oy) * dlf.stride + (px - dlf.ox);
+                gr0[k] = dl_dimage[di];
+                gr1[k] = dl_dimage[dlf.plane + di];
+                gr2[k] = dl_dimage[2 * dlf.plane + di];
             } else {
                 const uint32_t c = sgn[lp];
                 auto dec = [&](uint32_t code) { return code == 1u ? inv_norm : (code == 2u ? -inv_norm : 0.0f); };
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
                                                       const uint32_t* __restrict__ values,
                                                       const float4* __restrict__ g0, const float4* __restrict__ g1,
                                                       const float4* __restrict__ g2, float bg0, float bg1, float bg2,
-                                                      const float* __restrict__ target, float inv_norm,
+                                                      const float* __restrict__ target, PixFrame tf, float inv_norm,
                                                       float* __restrict__ image, double* __restrict__ l1_part,
                                                       float* __restrict__ grad2d, const uint32_t* __restrict__ order)
 {
@@ -653,7 +653,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
                 image[P + gi] = o1;
                 image[2 * P + gi] = o2;
             }
-            const float t0 = target[gi], t1 = target[P + gi], t2 = target[2 * P + gi];
+            const int64_t ti = (int64_t)(py - tf.oy) * tf.stride + (px - tf.ox);
+            const float t0 = target[ti], t1 = target[tf.plane + ti], t2 = target[2 * tf.plane + ti];
             const float d0 = o0 - t0, d1 = o1 - t1, d2 = o2 - t2;   // sign exact in f32
             gr0[k] = d0 > 0.0f ? inv_norm : (d0 < 0.0f ? -inv_norm : 0.0f);
             gr1[k] = d1 > 0.0f ? inv_norm : (d1 < 0.0f ? -inv_norm : 0.0f);
@@ -745,8 +746,8 @@ __global__ __launch_bounds__(1024) void k_tile_order(int64_t n1, const uint64_t*
 }  // namespace
 
 gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                            gs_raster* r, const float* target, float* image_out, double* loss_accum,
-                            uint64_t* stats)
+                            gs_raster* r, const float* target, PixFrame tf, float* image_out, PixFrame imf,
+                            double* loss_accum, uint64_t* stats)
 {
     const LeafGeom g = make_geom(cam, bins, r);
     const float inv_norm = (float)(1.0 / (3.0 * (double)cam->width * (double)cam->height));
@@ -755,12 +756,12 @@ gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
         if (stats)
             hipLaunchKernelGGL(k_raster_fwd<true>, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g,
                                bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
-                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->sgn, r->l1_part,
+                               cam->bg[2], target, tf, inv_norm, image_out, imf, r->tfinal, r->last, r->sgn, r->l1_part,
                                (unsigned long long*)stats);
         else
             hipLaunchKernelGGL(k_raster_fwd<false>, dim3((unsigned)bins->n_tiles), dim3(256), 0, ctx->stream, g,
                                bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1],
-                               cam->bg[2], target, inv_norm, image_out, r->tfinal, r->last, r->sgn, r->l1_part,
+                               cam->bg[2], target, tf, inv_norm, image_out, imf, r->tfinal, r->last, r->sgn, r->l1_part,
                                nullptr);
     }
     GS_HIP(ctx, hipGetLastError());
@@ -769,7 +770,7 @@ gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
 }
 
 gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                            const gs_raster* r, const float* dl_dimage, float* grad2d)
+                            const gs_raster* r, const float* dl_dimage, PixFrame dlf, float* grad2d)
 {
     const LeafGeom g = make_geom(cam, bins, r);
     const float inv_norm = (float)(1.0 / (3.0 * (double)cam->width * (double)cam->height));
@@ -778,14 +779,15 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
         const int64_t nt = bins->n_tiles;
         hipLaunchKernelGGL(k_raster_bwd, dim3((unsigned)((nt + 3) / 4)), dim3(256), 0, ctx->stream, g, nt,
                            bins->offsets, bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
-                           r->tfinal, r->last, r->sgn, inv_norm, dl_dimage, grad2d);
+                           r->tfinal, r->last, r->sgn, inv_norm, dl_dimage, dlf, grad2d);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }
 
 gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                              const float* target, float* image_out, double* l1_part, float* grad2d, bool backward)
+                              const float* target, PixFrame tf, float* image_out, double* l1_part, float* grad2d,
+                              bool backward)
 {
     LeafGeom g;
     g.W = cam->width;
@@ -814,12 +816,12 @@ gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* 
             const dim3 grid((unsigned)ceil_div(nt, kFusedWaves)), block(64 * kFusedWaves);
             if (backward)
                 hipLaunchKernelGGL(k_raster_fused<true>, grid, block, 0, ctx->stream, g, nt, bins->offsets, bins->values,
-                                   proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2], target, inv_norm,
-                                   image_out, l1_part, grad2d, order);
+                                   proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2], target, tf,
+                                   inv_norm, image_out, l1_part, grad2d, order);
             else
                 hipLaunchKernelGGL(k_raster_fused<false>, grid, block, 0, ctx->stream, g, nt, bins->offsets,
                                    bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
-                                   target, inv_norm, image_out, l1_part, grad2d, order);
+                                   target, tf, inv_norm, image_out, l1_part, grad2d, order);
         }
         gs_free_all(ctx, &tmp);
     }

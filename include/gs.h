@@ -372,7 +372,7 @@ gs_status gs_gate_get_stats(const gs_gate* gate, gs_gate_stats* stats);
 
 typedef struct {
     uint64_t budget_bytes;       /* 0: one leaf = the whole tile grid          */
-    int32_t loss_kind;           /* 0: L1, 1: (1-l) L1 + l (1 - SSIM), one leaf */
+    int32_t loss_kind;           /* 0: L1, 1: (1-l) L1 + l (1 - SSIM)          */
     float ssim_lambda;           /* 0.2 usual                                  */
     int32_t adam_step;           /* 0: no update; >= 1: one Adam step          */
     float lr, beta1, beta2, eps;
@@ -410,6 +410,13 @@ typedef struct {
                                  /* leaf's fused raster may start while the    */
                                  /* previous one ends (two leaves' slot arrays */
                                  /* held at once)                              */
+    int32_t target_host;         /* 1: target is host memory [3][H][W] (page-  */
+                                 /* locked, e.g. hipHostMalloc, for the copies */
+                                 /* to overlap the rendering): each leaf's     */
+                                 /* pixels (with the SSIM halo) are copied to  */
+                                 /* a device slice before that leaf is         */
+                                 /* rendered, so the image is never resident   */
+                                 /* whole; 0: target is device memory          */
 } gs_view_opts;
 
 typedef struct {
@@ -417,6 +424,7 @@ typedef struct {
     int64_t n_cand, n_isect;     /* n_isect summed over leaves                 */
     int32_t n_leaves, pad;
     uint64_t peak_bytes;         /* library high-water mark during the view    */
+                                 /* (a device-resident target not included)    */
     int32_t gate_backward;       /* with a gate: the decision (else 0)         */
     int32_t gate_forced;
     double gate_score;
@@ -443,7 +451,20 @@ typedef struct {
  * binned and rendered again with their backward (the leaves' buffers are
  * bounded, so they are not kept between the two passes), then the projection
  * backward and the update; otherwise the view ends after its forward
- * (gradients and parameters untouched).  target: device [3][H][W].
+ * (gradients and parameters untouched).  SSIM (loss_kind 1; SkipGS notes,
+ * "loss function"): each leaf's tile rectangle grown by one tile on each
+ * side inside the grid is binned and rendered, so that the 11 x 11 windows
+ * centred within 5 pixels of the leaf see the whole image's pixels; the leaf
+ * sums the terms of the centres it owns and runs the raster backward with
+ * the exact gradient of its own pixels, so loss and gradients equal the
+ * whole image's for any layout (the BoundedGS page, "02 / method", notes
+ * that leaf-local windows would differ at the leaf edges).  Per leaf it
+ * holds 33 floats per pixel of the grown rectangle (image, gradient, target
+ * slice, 24 filter maps) on top of the binning.  The leaves are not binned
+ * ahead for SSIM.  When opts->cost is NULL the plan uses the default model
+ * with these 33 floats (SSIM) or a host target's 3-float slice (L1) added to
+ * b_pixel; with overlapped L1 leaves up to three slices are held at once.  target: device [3][H][W], or host memory with
+ * target_host (BoundedGS page, "02 / method": bounded image feeding).
  * Synchronises. */
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result);

@@ -1,0 +1,119 @@
+"""Bounded supervision feeding and leaf-local SSIM with a halo (BoundedGS
+page, "02 / method": bounded image feeding, and the note that windows
+computed inside a leaf would differ from the whole image's at its edges).
+
+* An SSIM view split into leaves (fixed grids down to one-tile columns, and
+  planned layouts) against the oracle's whole-image SSIM view: loss, image
+  and every gradient group at the usual bars.  The oracle never splits the
+  SSIM loss, so this pins the halo reading: each leaf's windows see the
+  whole image's pixels.
+* A view whose target is host memory (copied leaf by leaf) against the same
+  view with the target resident on the device: identical loss and image
+  (fixed-order sums), gradients against the oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from differentiable_gaussian_splatting_amd import binding as B
+from differentiable_gaussian_splatting_amd import scenes
+from tests.gpu_pipeline import grad3d_groups, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+IMG_TOL = 1e-4
+LOSS_TOL = 1e-4
+GRAD_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load()
+    return B.Context()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _view(ctx, w, target, **kw):
+    import torch
+    K = (w.scene.sh_degree + 1) ** 2
+    ds = B.DeviceScene(w.scene, ctx.device)
+    g3 = torch.zeros((w.scene.n, 11 + 3 * K), dtype=torch.float32, device=ctx.device)
+    img = torch.full((3, w.camera.height, w.camera.width), -1.0, dtype=torch.float32, device=ctx.device)
+    r = B.gs_train_view(ctx, w.camera, ds, target, image_out=img, grad3d_out=g3, max_leaves=256, **kw)
+    return r, img.cpu().numpy(), g3.cpu().numpy()
+
+
+def _check(w, r, img, g3, o):
+    say(f"  loss gpu {r['loss']:.9f} oracle {o['loss']:.9f}, {r['n_leaves']} leaves")
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    assert np.abs(img - o["image"]).max() <= IMG_TOL
+    gg, og = grad3d_groups(g3, w.scene.sh_degree), grad3d_groups(o["grad3d"], w.scene.sh_degree)
+    for name in gg:
+        e = rel_l2(gg[name], og[name])
+        say(f"  grad3d {name:10s} rel L2 {e:.2e}")
+        assert e <= GRAD_TOL, name
+
+
+@pytest.fixture(scope="module")
+def ssim_case():
+    w = scenes.make_workload("c2_hd", n=12000, width=262, height=170, posed=True, seed=141)
+    o = oracle.train_view(w.camera, w.scene, w.target, loss="l1_ssim")
+    return w, o
+
+
+@pytest.mark.parametrize("layout", ["grid3x2", "columns", "tiles", "planned"])
+def test_ssim_leaves_match_whole_image_oracle(ctx, ssim_case, layout):
+    import torch
+    w, o = ssim_case
+    TW, TH = w.camera.tiles_x, w.camera.tiles_y
+    lib = B.load()
+    kw = {}
+    if layout == "grid3x2":
+        kw = dict(budget_bytes=0, leaves_in=B.gs_grid_leaves(lib, TW, TH, 3, 2))
+    elif layout == "columns":   # one-tile-wide leaves: every halo spans a neighbour
+        kw = dict(budget_bytes=0, leaves_in=B.gs_grid_leaves(lib, TW, TH, TW, 1))
+    elif layout == "tiles":     # one leaf per tile (the image edge is ragged: 262 x 170)
+        kw = dict(budget_bytes=0, leaves_in=B.gs_grid_leaves(lib, TW, TH, TW, TH))
+    else:
+        kw = dict(budget_bytes=600_000, cost=dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 18))
+    say(f"case ssim layout {layout}")
+    r, img, g3 = _view(ctx, w, torch.from_numpy(w.target).to(ctx.device), loss="l1_ssim", **kw)
+    assert r["n_leaves"] > 1
+    if layout == "tiles":
+        assert r["n_leaves"] == TW * TH
+    _check(w, r, img, g3, o)
+
+
+@pytest.mark.parametrize("loss,budget,serial", [("l1", 1_400_000, False), ("l1", 1_400_000, True), ("l1", 0, False),
+                                               ("l1_ssim", 1_400_000, False)])
+def test_host_target_matches_device_target(ctx, loss, budget, serial):
+    import torch
+    w = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, seed=143)
+    cost = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
+    say(f"case host target loss {loss} budget {budget} serial {serial}")
+    host = torch.from_numpy(w.target).pin_memory()
+    assert host.is_pinned() and not host.is_cuda
+    rd, imgd, g3d = _view(ctx, w, torch.from_numpy(w.target).to(ctx.device), loss=loss, budget_bytes=budget,
+                          cost=cost, serial_leaves=serial)
+    rh, imgh, g3h = _view(ctx, w, host, loss=loss, budget_bytes=budget, cost=cost, serial_leaves=serial)
+    if budget:
+        assert rh["n_leaves"] > 2
+    assert rh["n_leaves"] == rd["n_leaves"] and rh["n_isect"] == rd["n_isect"]
+    assert rh["loss"] == rd["loss"]
+    assert np.array_equal(imgh, imgd)
+    # the gradients are sums of float atomics: equal up to their order
+    gh, gd = grad3d_groups(g3h, 3), grad3d_groups(g3d, 3)
+    for name in gh:
+        assert rel_l2(gh[name], gd[name]) <= 1e-5, name
+    o = oracle.train_view(w.camera, w.scene, w.target, loss=loss,
+                          **(dict(budget=budget, cost=cost) if budget and loss == "l1" else {}))
+    _check(w, rh, imgh, g3h, o)
+    # the library's peak holds no whole target: a leaf slice at most
+    say(f"  peak {rh['peak_bytes']} B (device target {rd['peak_bytes']} B)")
