@@ -1200,14 +1200,20 @@ static gs_status slice_target(gs_ctx* ctx, const gs_camera* cam, const float* ta
 // pixels are exactly the whole image's (see loss.hip); the raster backward
 // runs with that gradient (zero on the halo).  The sums of S and |x - y|
 // over the leaf are added to acc[0], acc[1]; the leaf's pixels of the image
-// go to image_out when given.
+// go to image_out when given.  `given`: the target over the grown
+// rectangle, already copied (else it is sliced here when needed).
+static gs_tile_rect ssim_grown(const gs_proj* proj, gs_tile_rect r)
+{
+    return gs_tile_rect{std::max(r.tx0 - 1, 0), std::max(r.ty0 - 1, 0), std::min(r.tx1 + 1, proj->TW),
+                        std::min(r.ty1 + 1, proj->TH)};
+}
+
 static gs_status ssim_leaf(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const float* target,
-                           bool target_host, const gs_view_opts* opts, gs_tile_rect r, bool backward, float* grad2d,
-                           float* image_out, double* acc, int64_t* ni)
+                           bool target_host, const TargetSlice* given, const gs_view_opts* opts, gs_tile_rect r,
+                           bool backward, float* grad2d, float* image_out, double* acc, int64_t* ni)
 {
     gs_status st = GS_OK;
-    const gs_tile_rect e{std::max(r.tx0 - 1, 0), std::max(r.ty0 - 1, 0), std::min(r.tx1 + 1, proj->TW),
-                         std::min(r.ty1 + 1, proj->TH)};
+    const gs_tile_rect e = ssim_grown(proj, r);
     const PixRect ep = pix_rect(cam, e), op = pix_rect(cam, r);
     const int64_t n = (int64_t)ep.w * ep.h, P = (int64_t)cam->width * cam->height;
     const bool whole = ep.w == cam->width && ep.h == cam->height;
@@ -1223,7 +1229,9 @@ static gs_status ssim_leaf(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
     double* part = nullptr;
     const int64_t nb = ssim_partial_blocks(ep.w, ep.h);
     if ((st = gs_bin_sort(ctx, cam, proj, e, &bins, ni)) != GS_OK) return st;
-    if (!whole || target_host) {
+    if (given) {
+        tgt = given->ptr;
+    } else if (!whole || target_host) {
         if ((st = slice_target(ctx, cam, target, target_host, ep, &ts, ctx->stream)) != GS_OK) goto done;
         tgt = ts.ptr;
     }
@@ -1282,15 +1290,45 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     bool pipe = opts->loss_kind == 0 && leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
     for (const gs_leaf& L : leaves) pipe = pipe && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
     if (opts->loss_kind == 1) {
+        // a host target: each next leaf's slice is copied on the second
+        // stream while the current leaf is rendered
         if ((st = launch_fill_u32(ctx, (uint32_t*)ssim_acc, 0u, 4)) != GS_OK) return st;
-        for (const gs_leaf& L : leaves) {
-            int64_t ni = 0;
-            if ((st = ssim_leaf(ctx, cam, proj, target, host, opts, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1},
-                                backward, grad2d, image, ssim_acc, &ni)) != GS_OK)
-                return st;
-            *isect_total += ni;
+        auto grown = [&](size_t li) {
+            const gs_leaf& L = leaves[li];
+            return pix_rect(cam, ssim_grown(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}));
+        };
+        if (host) {
+            if ((st = ensure_side(ctx)) != GS_OK) return st;
+            if ((st = slice_target(ctx, cam, target, true, grown(0), &sl[0], ctx->side)) == GS_OK &&
+                hipEventRecord(ctx->ev_done[0], ctx->side) != hipSuccess)
+                st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
         }
-        return GS_OK;
+        for (size_t li = 0; li < leaves.size() && st == GS_OK; ++li) {
+            const gs_leaf& L = leaves[li];
+            int64_t ni = 0;
+            if (host) {
+                if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
+                    st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
+                    break;
+                }
+                if (li + 1 < leaves.size()) {
+                    if ((st = slice_target(ctx, cam, target, true, grown(li + 1), &sl[(li + 1) % 3], ctx->side)) !=
+                        GS_OK)
+                        break;
+                    if (hipEventRecord(ctx->ev_done[(li + 1) & 1], ctx->side) != hipSuccess) {
+                        st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+                        break;
+                    }
+                }
+            }
+            st = ssim_leaf(ctx, cam, proj, target, host, host ? &sl[li % 3] : nullptr, opts,
+                           gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, backward, grad2d, image, ssim_acc, &ni);
+            *isect_total += ni;
+            gs_free_all(ctx, &sl[li % 3].allocs);
+        }
+        if (host) (void)hipStreamSynchronize(ctx->side);
+        for (TargetSlice& t : sl) gs_free_all(ctx, &t.allocs);
+        return st;
     }
     if (pipe) {
         const gs_leaf& L = leaves[0];

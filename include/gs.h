@@ -461,7 +461,8 @@ typedef struct {
  * that leaf-local windows would differ at the leaf edges).  Per leaf it
  * holds 33 floats per pixel of the grown rectangle (image, gradient, target
  * slice, 24 filter maps) on top of the binning.  The leaves are not binned
- * ahead for SSIM.  When opts->cost is NULL the plan uses the default model
+ * ahead for SSIM; with a host target each next leaf's slice is copied on the
+ * second stream while the current leaf is rendered.  When opts->cost is NULL the plan uses the default model
  * with these 33 floats (SSIM) or a host target's 3-float slice (L1) added to
  * b_pixel; with overlapped L1 leaves up to three slices are held at once.  target: device [3][H][W], or host memory with
  * target_host (BoundedGS page, "02 / method": bounded image feeding).
