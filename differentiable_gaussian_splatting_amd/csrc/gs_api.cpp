@@ -1029,7 +1029,7 @@ gs_status gs_loss_ssim(gs_ctx* ctx, int32_t width, int32_t height, const float* 
     const int64_t P = (int64_t)width * height;
     const int64_t nb = ssim_partial_blocks(width, height);
     std::vector<GsAlloc> tmp;
-    float* scratch = (float*)gs_malloc(ctx, sizeof(float) * 24 * P, GS_MEM_LOSS, &tmp);
+    float* scratch = (float*)gs_malloc(ctx, sizeof(float) * 9 * P, GS_MEM_LOSS, &tmp);
     double* part = (double*)gs_malloc(ctx, sizeof(double) * (2 * nb + 2), GS_MEM_LOSS, &tmp);
     if (!scratch || !part) {
         gs_free_all(ctx, &tmp);
@@ -1237,7 +1237,7 @@ static gs_status ssim_leaf(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
     }
     if (!image) image = (float*)gs_malloc(ctx, sizeof(float) * 3 * n, GS_MEM_LOSS, &tmp);
     dl = (float*)gs_malloc(ctx, sizeof(float) * 3 * n, GS_MEM_LOSS, &tmp);
-    scratch = (float*)gs_malloc(ctx, sizeof(float) * 24 * n, GS_MEM_LOSS, &tmp);
+    scratch = (float*)gs_malloc(ctx, sizeof(float) * 9 * n, GS_MEM_LOSS, &tmp);
     part = (double*)gs_malloc(ctx, sizeof(double) * 2 * nb, GS_MEM_LOSS, &tmp);
     if (!image || !dl || !scratch || !part) { st = GS_ERR_OOM; goto done; }
     if ((st = render_fwd(ctx, cam, proj, bins, nullptr, ef, nullptr, image, ef, nullptr, nullptr, &ras)) != GS_OK)
@@ -1492,11 +1492,11 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         const uint64_t budget = opts->budget_bytes > 0 ? opts->budget_bytes : ~0ull;
         const bool partial = nr > 0 && opts->leaves_in_partial != 0;
         // Without a caller's model, the default one plus what the view holds
-        // per pixel of a leaf beyond the L1 raster: for SSIM 33 floats
-        // (image, gradient, target slice, 24 filter maps), for an L1 view
+        // per pixel of a leaf beyond the L1 raster: for SSIM 18 floats
+        // (image, gradient, target slice, 9 partial maps), for an L1 view
         // with a host target its 3-float slice.
         gs_cost_model cm = opts->cost ? *opts->cost : gs_default_cost_model();
-        if (!opts->cost) cm.b_pixel += opts->loss_kind == 1 ? 33 * 4 : (opts->target_host ? 3 * 4 : 0);
+        if (!opts->cost) cm.b_pixel += opts->loss_kind == 1 ? 18 * 4 : (opts->target_host ? 3 * 4 : 0);
         int32_t nl = 0;
         leaves.resize(4096);
         st = plan_impl(ctx, cam, proj, budget, &cm, opts->strict_budget, roots, nr, leaves.data(),

@@ -252,7 +252,7 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
 // and zero elsewhere, and inv is 1 / (3 x the whole image's pixel count).
 gs_status launch_ssim(gs_ctx* ctx, int W, int H, int ox0, int oy0, int ox1, int oy1, float inv, const float* image,
                       const float* target, float lambda, float* dl_dimage, double* partials /*[n_blocks*2]*/,
-                      int64_t n_blocks, float* scratch /*[24][H][W] */);
+                      int64_t n_blocks, float* scratch /*[9][H][W] */);
 int64_t ssim_partial_blocks(int W, int H);
 gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate);
 

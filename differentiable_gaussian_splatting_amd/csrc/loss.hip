@@ -62,40 +62,6 @@ struct Win {
     float w[11];
 };
 
-constexpr int kSB = 256;
-
-// horizontal pass of the five statistics of each channel:
-// out[(s * 3 + ch) * P + p], s = x, y, x^2, y^2, xy
-__global__ __launch_bounds__(kSB) void k_ssim_h(int W, int H, Win win, const float* __restrict__ x,
-                                                const float* __restrict__ y, float* __restrict__ out)
-{
-    const int64_t P = (int64_t)W * H;
-    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
-    if (k >= 3 * P) return;
-    const int ch = (int)(k / P);
-    const int64_t p = k % P;
-    const int py = (int)(p / W), px = (int)(p % W);
-    const float* xr = x + ch * P + (int64_t)py * W;
-    const float* yr = y + ch * P + (int64_t)py * W;
-    float a = 0.f, b = 0.f, c = 0.f, d = 0.f, e = 0.f;
-#pragma unroll
-    for (int t = 0; t < 11; ++t) {
-        const int q = px + t - 5;
-        if (q < 0 || q >= W) continue;
-        const float wv = win.w[t], xv = xr[q], yv = yr[q];
-        a += wv * xv;
-        b += wv * yv;
-        c += wv * xv * xv;
-        d += wv * yv * yv;
-        e += wv * xv * yv;
-    }
-    out[(0 * 3 + ch) * P + p] = a;
-    out[(1 * 3 + ch) * P + p] = b;
-    out[(2 * 3 + ch) * P + p] = c;
-    out[(3 * 3 + ch) * P + p] = d;
-    out[(4 * 3 + ch) * P + p] = e;
-}
-
 // Owned rectangle of the buffer: the centres whose SSIM terms (and pixels
 // whose L1 terms) are summed, and the pixels whose gradient is written.
 struct Owned {
@@ -103,28 +69,78 @@ struct Owned {
     __device__ bool has(int x, int y) const { return x >= x0 && x < x1 && y >= y0 && y < y1; }
 };
 
-// vertical pass + SSIM map + per-pixel partials dS/d(mu_x), dS/d(E[x^2]),
-// dS/d(E[xy]) into grad[(s * 3 + ch) * P + p]; block partial sums of S and
-// |x - y| over the owned rectangle into part[2 * block], part[2 * block + 1]
-__global__ __launch_bounds__(kSB) void k_ssim_v(int W, int H, Win win, Owned own, const float* __restrict__ hs,
-                                                const float* __restrict__ x, const float* __restrict__ y,
-                                                float* __restrict__ grad, double* __restrict__ part)
+constexpr int kSB = 256;
+
+// Tiles of the two SSIM kernels: 32 x 16 outputs of one channel per
+// workgroup, read with a 5-pixel apron (zero outside the buffer) into LDS, so
+// that each separable pass reads its taps from LDS and each image or map is
+// read from memory about once.
+constexpr int kTX = 32, kTY = 16, kR = 5, kIX = kTX + 2 * kR, kIY = kTY + 2 * kR;
+
+__device__ __forceinline__ int64_t ssim_block_id()
 {
+    return ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+}
+
+// Five windowed statistics of channel ch (horizontal 11-tap pass into LDS,
+// then the vertical pass), the SSIM map and the per-pixel partials
+// dS/d(mu_x) - 2 mu_x dS/d(sigma_xx) - mu_y dS/d(sigma_xy), dS/d(sigma_xx),
+// dS/d(sigma_xy) into grad[(s * 3 + ch) * P + p]; the block's sums of S and
+// |x - y| over the owned rectangle into part[2 * block], part[2 * block + 1].
+// Each pass adds its taps in order, skipping those outside the buffer.
+__global__ __launch_bounds__(kSB) void k_ssim_stats(int W, int H, Win win, Owned own, const float* __restrict__ x,
+                                                    const float* __restrict__ y, float* __restrict__ grad,
+                                                    double* __restrict__ part)
+{
+    __shared__ float sx[kIY][kIX], sy[kIY][kIX];
+    __shared__ float hs[5][kIY][kTX];
+    const int ch = blockIdx.z;
     const int64_t P = (int64_t)W * H;
-    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
+    const int x0 = blockIdx.x * kTX, y0 = blockIdx.y * kTY;
+    const float* xc = x + ch * P;
+    const float* yc = y + ch * P;
+    for (int i = threadIdx.x; i < kIX * kIY; i += kSB) {
+        const int ly = i / kIX, lx = i % kIX;
+        const int gx = x0 + lx - kR, gy = y0 + ly - kR;
+        const bool in = gx >= 0 && gx < W && gy >= 0 && gy < H;
+        sx[ly][lx] = in ? xc[(int64_t)gy * W + gx] : 0.0f;
+        sy[ly][lx] = in ? yc[(int64_t)gy * W + gx] : 0.0f;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kIY * kTX; i += kSB) {
+        const int ly = i / kTX, lx = i % kTX;
+        float a = 0.f, b = 0.f, c = 0.f, d = 0.f, e = 0.f;
+#pragma unroll
+        for (int t = 0; t < 11; ++t) {
+            const int q = x0 + lx + t - kR;
+            if (q < 0 || q >= W) continue;
+            const float wv = win.w[t], xv = sx[ly][lx + t], yv = sy[ly][lx + t];
+            a += wv * xv;
+            b += wv * yv;
+            c += wv * xv * xv;
+            d += wv * yv * yv;
+            e += wv * xv * yv;
+        }
+        hs[0][ly][lx] = a;
+        hs[1][ly][lx] = b;
+        hs[2][ly][lx] = c;
+        hs[3][ly][lx] = d;
+        hs[4][ly][lx] = e;
+    }
+    __syncthreads();
     double s_sum = 0.0, l1_sum = 0.0;
-    if (k < 3 * P) {
-        const int ch = (int)(k / P);
-        const int64_t p = k % P;
-        const int py = (int)(p / W), px = (int)(p % W);
+    for (int i = threadIdx.x; i < kTY * kTX; i += kSB) {
+        const int ly = i / kTX, lx = i % kTX;
+        const int px = x0 + lx, py = y0 + ly;
+        if (px >= W || py >= H) continue;
         float st[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 11; ++t) {
-            const int q = py + t - 5;
+            const int q = py + t - kR;
             if (q < 0 || q >= H) continue;
             const float wv = win.w[t];
 #pragma unroll
-            for (int s = 0; s < 5; ++s) st[s] += wv * hs[(s * 3 + ch) * P + (int64_t)q * W + px];
+            for (int s = 0; s < 5; ++s) st[s] += wv * hs[s][ly + t][lx];
         }
         const float C1 = 0.0001f, C2 = 0.0009f;
         const float mx = st[0], my = st[1];
@@ -136,12 +152,13 @@ __global__ __launch_bounds__(kSB) void k_ssim_v(int W, int H, Win win, Owned own
         const float dS_dmx = 2.f * my * N2 * iD - S * 2.f * mx / D1;
         const float dS_dsxx = -S / D2;
         const float dS_dsxy = 2.f * N1 * iD;
+        const int64_t p = (int64_t)py * W + px;
         grad[(0 * 3 + ch) * P + p] = dS_dmx - 2.f * mx * dS_dsxx - my * dS_dsxy;
         grad[(1 * 3 + ch) * P + p] = dS_dsxx;
         grad[(2 * 3 + ch) * P + p] = dS_dsxy;
         if (own.has(px, py)) {
-            s_sum = (double)S;
-            l1_sum = fabs((double)x[k] - (double)y[k]);
+            s_sum += (double)S;
+            l1_sum += fabs((double)sx[ly + kR][lx + kR] - (double)sy[ly + kR][lx + kR]);
         }
     }
     s_sum = gsd::wave_sum_d(s_sum);
@@ -159,60 +176,72 @@ __global__ __launch_bounds__(kSB) void k_ssim_v(int W, int H, Win win, Owned own
             a += sh[0][w];
             b += sh[1][w];
         }
-        part[2 * blockIdx.x] = a;
-        part[2 * blockIdx.x + 1] = b;
+        const int64_t bid = ssim_block_id();
+        part[2 * bid] = a;
+        part[2 * bid + 1] = b;
     }
 }
 
-// horizontal pass of the three partial maps (9 maps)
-__global__ __launch_bounds__(kSB) void k_ssim_h2(int W, int H, Win win, const float* __restrict__ in,
-                                                 float* __restrict__ out)
+// The three partial maps of channel ch through the same filter (horizontal
+// pass into LDS, then vertical), and the gradient of the loss w.r.t. the
+// image (zero outside the owned rectangle).
+__global__ __launch_bounds__(kSB) void k_ssim_grad(int W, int H, Win win, Owned own, const float* __restrict__ gm,
+                                                   const float* __restrict__ x, const float* __restrict__ y,
+                                                   float lambda, float inv, float* __restrict__ dl)
 {
+    __shared__ float sm[3][kIY][kIX];
+    __shared__ float hs[3][kIY][kTX];
+    const int ch = blockIdx.z;
     const int64_t P = (int64_t)W * H;
-    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
-    if (k >= 9 * P) return;
-    const int64_t m = k / P, p = k % P;
-    const int py = (int)(p / W), px = (int)(p % W);
-    const float* r = in + m * P + (int64_t)py * W;
-    float a = 0.f;
+    const int x0 = blockIdx.x * kTX, y0 = blockIdx.y * kTY;
+    for (int i = threadIdx.x; i < kIX * kIY; i += kSB) {
+        const int ly = i / kIX, lx = i % kIX;
+        const int gx = x0 + lx - kR, gy = y0 + ly - kR;
+        const bool in = gx >= 0 && gx < W && gy >= 0 && gy < H;
+        const int64_t g = (int64_t)gy * W + gx;
 #pragma unroll
-    for (int t = 0; t < 11; ++t) {
-        const int q = px + t - 5;
-        if (q >= 0 && q < W) a += win.w[t] * r[q];
+        for (int s = 0; s < 3; ++s) sm[s][ly][lx] = in ? gm[(s * 3 + ch) * P + g] : 0.0f;
     }
-    out[k] = a;
-}
-
-// vertical pass + gradient of the loss w.r.t. the image (zero outside the
-// owned rectangle)
-__global__ __launch_bounds__(kSB) void k_ssim_v2(int W, int H, Win win, Owned own, const float* __restrict__ hs,
-                                                 const float* __restrict__ x, const float* __restrict__ y,
-                                                 float lambda, float inv, float* __restrict__ dl)
-{
-    const int64_t P = (int64_t)W * H;
-    const int64_t k = (int64_t)blockIdx.x * kSB + threadIdx.x;
-    if (k >= 3 * P) return;
-    const int ch = (int)(k / P);
-    const int64_t p = k % P;
-    const int py = (int)(p / W), px = (int)(p % W);
-    if (!own.has(px, py)) {
-        dl[k] = 0.0f;
-        return;
-    }
-    float f[3] = {0.f, 0.f, 0.f};
+    __syncthreads();
+    for (int i = threadIdx.x; i < kIY * kTX; i += kSB) {
+        const int ly = i / kTX, lx = i % kTX;
+        float a[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 11; ++t) {
-        const int q = py + t - 5;
-        if (q < 0 || q >= H) continue;
-        const float wv = win.w[t];
+        for (int t = 0; t < 11; ++t) {
+            const int q = x0 + lx + t - kR;
+            if (q >= 0 && q < W) {
 #pragma unroll
-        for (int s = 0; s < 3; ++s) f[s] += wv * hs[(s * 3 + ch) * P + (int64_t)q * W + px];
+                for (int s = 0; s < 3; ++s) a[s] += win.w[t] * sm[s][ly][lx + t];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 3; ++s) hs[s][ly][lx] = a[s];
     }
-    const float xv = x[k], yv = y[k];
-    const float dssim = f[0] + 2.f * xv * f[1] + yv * f[2];
-    const float d = xv - yv;
-    const float sg = d > 0.f ? 1.f : (d < 0.f ? -1.f : 0.f);
-    dl[k] = (1.0f - lambda) * sg * inv - lambda * dssim * inv;
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTY * kTX; i += kSB) {
+        const int ly = i / kTX, lx = i % kTX;
+        const int px = x0 + lx, py = y0 + ly;
+        if (px >= W || py >= H) continue;
+        const int64_t k = ch * P + (int64_t)py * W + px;
+        if (!own.has(px, py)) {
+            dl[k] = 0.0f;
+            continue;
+        }
+        float f[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 11; ++t) {
+            const int q = py + t - kR;
+            if (q < 0 || q >= H) continue;
+            const float wv = win.w[t];
+#pragma unroll
+            for (int s = 0; s < 3; ++s) f[s] += wv * hs[s][ly + t][lx];
+        }
+        const float xv = x[k], yv = y[k];
+        const float dssim = f[0] + 2.f * xv * f[1] + yv * f[2];
+        const float d = xv - yv;
+        const float sg = d > 0.f ? 1.f : (d < 0.f ? -1.f : 0.f);
+        dl[k] = (1.0f - lambda) * sg * inv - lambda * dssim * inv;
+    }
 }
 
 }  // namespace
@@ -239,7 +268,7 @@ gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, d
     return GS_OK;
 }
 
-int64_t ssim_partial_blocks(int W, int H) { return ceil_div(3 * (int64_t)W * H, kSB); }
+int64_t ssim_partial_blocks(int W, int H) { return 3 * ceil_div(W, kTX) * ceil_div(H, kTY); }
 
 gs_status launch_ssim(gs_ctx* ctx, int W, int H, int ox0, int oy0, int ox1, int oy1, float inv, const float* image,
                       const float* target, float lambda, float* dl_dimage, double* partials, int64_t n_blocks,
@@ -252,19 +281,14 @@ gs_status launch_ssim(gs_ctx* ctx, int W, int H, int ox0, int oy0, int ox1, int 
         s += g[i];
     }
     for (int i = 0; i < 11; ++i) win.w[i] = (float)(g[i] / s);
-    const int64_t P = (int64_t)W * H;
-    float* bufA = scratch;            // 15 maps
-    float* bufB = scratch + 15 * P;   // 9 maps
+    (void)n_blocks;   // = ssim_partial_blocks(W, H), one pair of sums per workgroup
     const Owned own{ox0, oy0, ox1, oy1};
+    const dim3 grid((unsigned)ceil_div(W, kTX), (unsigned)ceil_div(H, kTY), 3);
     GsTimerScope ts(ctx, "ssim");
-    hipLaunchKernelGGL(k_ssim_h, dim3((unsigned)ceil_div(3 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, image,
-                       target, bufA);
-    hipLaunchKernelGGL(k_ssim_v, dim3((unsigned)n_blocks), dim3(kSB), 0, ctx->stream, W, H, win, own, bufA, image,
-                       target, bufB, partials);
-    hipLaunchKernelGGL(k_ssim_h2, dim3((unsigned)ceil_div(9 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, bufB,
-                       bufA);
-    hipLaunchKernelGGL(k_ssim_v2, dim3((unsigned)ceil_div(3 * P, kSB)), dim3(kSB), 0, ctx->stream, W, H, win, own,
-                       bufA, image, target, lambda, inv, dl_dimage);
+    hipLaunchKernelGGL(k_ssim_stats, grid, dim3(kSB), 0, ctx->stream, W, H, win, own, image, target, scratch,
+                       partials);
+    hipLaunchKernelGGL(k_ssim_grad, grid, dim3(kSB), 0, ctx->stream, W, H, win, own, scratch, image, target, lambda,
+                       inv, dl_dimage);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -459,11 +459,11 @@ typedef struct {
  * the exact gradient of its own pixels, so loss and gradients equal the
  * whole image's for any layout (the BoundedGS page, "02 / method", notes
  * that leaf-local windows would differ at the leaf edges).  Per leaf it
- * holds 33 floats per pixel of the grown rectangle (image, gradient, target
- * slice, 24 filter maps) on top of the binning.  The leaves are not binned
+ * holds 18 floats per pixel of the grown rectangle (image, gradient, target
+ * slice, 9 partial maps) on top of the binning.  The leaves are not binned
  * ahead for SSIM; with a host target each next leaf's slice is copied on the
  * second stream while the current leaf is rendered.  When opts->cost is NULL the plan uses the default model
- * with these 33 floats (SSIM) or a host target's 3-float slice (L1) added to
+ * with these 18 floats (SSIM) or a host target's 3-float slice (L1) added to
  * b_pixel; with overlapped L1 leaves up to three slices are held at once.  target: device [3][H][W], or host memory with
  * target_host (BoundedGS page, "02 / method": bounded image feeding).
  * Synchronises. */
