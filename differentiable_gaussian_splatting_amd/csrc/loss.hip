@@ -74,7 +74,8 @@ constexpr int kSB = 256;
 // Tiles of the two SSIM kernels: 32 x 16 outputs of one channel per
 // workgroup, read with a 5-pixel apron (zero outside the buffer) into LDS, so
 // that each separable pass reads its taps from LDS and each image or map is
-// read from memory about once.
+// read from memory about once.  A tap outside the buffer reads the apron's
+// zero and adds a zero product: the zero padding, with no compare per tap.
 constexpr int kTX = 32, kTY = 16, kR = 5, kIX = kTX + 2 * kR, kIY = kTY + 2 * kR;
 
 __device__ __forceinline__ int64_t ssim_block_id()
@@ -87,7 +88,7 @@ __device__ __forceinline__ int64_t ssim_block_id()
 // dS/d(mu_x) - 2 mu_x dS/d(sigma_xx) - mu_y dS/d(sigma_xy), dS/d(sigma_xx),
 // dS/d(sigma_xy) into grad[(s * 3 + ch) * P + p]; the block's sums of S and
 // |x - y| over the owned rectangle into part[2 * block], part[2 * block + 1].
-// Each pass adds its taps in order, skipping those outside the buffer.
+// Each pass adds its 11 taps in order.
 __global__ __launch_bounds__(kSB) void k_ssim_stats(int W, int H, Win win, Owned own, const float* __restrict__ x,
                                                     const float* __restrict__ y, float* __restrict__ grad,
                                                     double* __restrict__ part)
@@ -112,8 +113,6 @@ __global__ __launch_bounds__(kSB) void k_ssim_stats(int W, int H, Win win, Owned
         float a = 0.f, b = 0.f, c = 0.f, d = 0.f, e = 0.f;
 #pragma unroll
         for (int t = 0; t < 11; ++t) {
-            const int q = x0 + lx + t - kR;
-            if (q < 0 || q >= W) continue;
             const float wv = win.w[t], xv = sx[ly][lx + t], yv = sy[ly][lx + t];
             a += wv * xv;
             b += wv * yv;
@@ -136,8 +135,6 @@ __global__ __launch_bounds__(kSB) void k_ssim_stats(int W, int H, Win win, Owned
         float st[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 11; ++t) {
-            const int q = py + t - kR;
-            if (q < 0 || q >= H) continue;
             const float wv = win.w[t];
 #pragma unroll
             for (int s = 0; s < 5; ++s) st[s] += wv * hs[s][ly + t][lx];
@@ -208,11 +205,8 @@ __global__ __launch_bounds__(kSB) void k_ssim_grad(int W, int H, Win win, Owned 
         float a[3] = {0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 11; ++t) {
-            const int q = x0 + lx + t - kR;
-            if (q >= 0 && q < W) {
 #pragma unroll
-                for (int s = 0; s < 3; ++s) a[s] += win.w[t] * sm[s][ly][lx + t];
-            }
+            for (int s = 0; s < 3; ++s) a[s] += win.w[t] * sm[s][ly][lx + t];
         }
 #pragma unroll
         for (int s = 0; s < 3; ++s) hs[s][ly][lx] = a[s];
@@ -230,8 +224,6 @@ __global__ __launch_bounds__(kSB) void k_ssim_grad(int W, int H, Win win, Owned 
         float f[3] = {0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 11; ++t) {
-            const int q = py + t - kR;
-            if (q < 0 || q >= H) continue;
             const float wv = win.w[t];
 #pragma unroll
             for (int s = 0; s < 3; ++s) f[s] += wv * hs[s][ly + t][lx];
