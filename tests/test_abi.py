@@ -112,3 +112,37 @@ def test_gate_rejects_bad_arguments():
         else:
             raise AssertionError((view, loss))
     assert g.stats()["steps"] == 0
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """Every struct the binding passes across the ABI has the header's size
+    and field offsets (a C program built with gcc from include/gs.h prints
+    them)."""
+    import os
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        import pytest
+        pytest.skip("gcc not available")
+    structs = [binding.gs_camera, binding.gs_params, binding.gs_param_ptrs, binding.gs_tile_rect, binding.gs_leaf,
+               binding.gs_cost_model, binding.gs_mem_stats, binding.gs_view_opts, binding.gs_gate_decision,
+               binding.gs_gate_stats, binding.gs_view_result]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gs.h"', "int main(void) {"]
+    for st in structs:
+        n = st.__name__
+        lines.append(f'    printf("{n} %zu\\n", sizeof({n}));')
+        for f in st._fields_:
+            lines.append(f'    printf("{n}.{f[0]} %zu\\n", offsetof({n}, {f[0]}));')
+    lines += ["    return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                        text=True).stdout.splitlines())
+    for st in structs:
+        n = st.__name__
+        assert int(got[n]) == ctypes.sizeof(st), n
+        for f in st._fields_:
+            assert int(got[f"{n}.{f[0]}"]) == getattr(st, f[0]).offset, (n, f[0])
