@@ -63,8 +63,12 @@ def parse():
     ap.add_argument("--budget-mib", type=float, default=384.0)
     ap.add_argument("--no-adam", action="store_true")
     ap.add_argument("--cpu-baseline", type=int, default=1)
-    ap.add_argument("--cpu-window", type=int, default=768,
-                    help="side (pixels) of the window the oracle rasterizes for the CPU baseline")
+    ap.add_argument("--cpu-window", type=int, default=384,
+                    help="side (pixels) of each window the oracle rasterizes for the CPU baseline")
+    ap.add_argument("--cpu-windows", type=int, default=16,
+                    help="windows of the CPU baseline, one at a seeded position in each cell of a grid over the view")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads of the CPU baseline (0: the cores the process may use, at most 16)")
     ap.add_argument("--attr-steps", type=int, default=2,
                     help="steps of the per-kernel attribution pass (events around every kernel)")
     ap.add_argument("--layout", default="auto",
@@ -210,6 +214,7 @@ def main():
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
+    ctx.reset_peak()
     B.gs_reset_timing(ctx)
     B.gs_set_timing_only(ctx, dom)
     B.gs_set_timing(ctx, True)
@@ -225,41 +230,71 @@ def main():
     B.gs_set_timing_only(ctx, None)
     dom_live = kernel_times(args.steps, [dom])[dom]
     torch_peak = torch.cuda.max_memory_allocated(dev) - base_alloc
+    mem = ctx.mem_stats()
     ms_step = 1e3 * t_total / args.steps
     r = results[-1]
     log(f"[bench] {args.steps} steps in {t_total:.3f}s: {ms_step:.2f} ms/step, loss {r['loss']:.6f}, "
         f"leaves {r['n_leaves']}, isect {r['n_isect']}; {dom} {dom_live['avg_ms']:.4f} ms per launch (live)")
+
+    # per leaf of one more (untimed) view: its estimate and the bytes the
+    # library held for it
+    leaf_rep = None
+    if grid is None and not args.cached_layout:
+        adam = None if args.no_adam else dict(step=k + 1, params=params, m=m, v=v, lr=1e-3)
+        rl = B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam,
+                             serial_leaves=args.serial_leaves, max_leaves=65536)
+        k += 1
+        est = [L["est_bytes"] for L in rl["leaves"]]
+        held = [L["bytes"] for L in rl["leaves"]]
+        leaf_rep = {"n_leaves": len(est), "max_est_mib": round(max(est) / MIB, 2),
+                    "max_held_mib": round(max(held) / MIB, 2),
+                    "max_held_over_est": round(max(h / e for h, e in zip(held, est)), 4),
+                    "all_within_est": all(h <= e for h, e in zip(held, est)),
+                    "held_mib_per_leaf": [round(h / MIB, 1) for h in held]}
+        log(f"[bench] per-leaf bytes held / estimate: max {leaf_rep['max_held_mib']} MiB held, "
+            f"max ratio {leaf_rep['max_held_over_est']}, all within: {leaf_rep['all_within_est']}")
 
     # work counters of the view (untimed pass): pairs examined / included /
     # revisited by the backward, intersections, candidates
     wc = count_work(B, ctx, cam, params, budget)
     work = kernel_work(wc, sc)
     rooflines = {}
+    attain_s = 0.0      # sum over the timed kernels of max(bytes / BW, ops / VALU)
+    step_bytes = 0      # algorithmic HBM bytes of the kernels that ran in the step
+    counted = []
     for name, (bound, amount, unit_desc) in work.items():
         kt = dom_live if name == dom else ktimes.get(name)
-        if not kt:
+        if not kt or kt["total_ms"] <= 0.0:
             continue
         sec = kt["total_ms"] * 1e-3
         if bound == "alu":
             ach = amount / sec / 1e12
             rooflines[name] = dict(bound="alu", achieved=round(ach, 3), peak=round(PEAK_VALU_TOPS, 2), unit="Top/s",
                                    frac=round(ach / PEAK_VALU_TOPS, 4), work=unit_desc)
+            hbm = wc["raster_bytes"] if name == "raster_fused" else 0
+            attain_s += max(amount / (PEAK_VALU_TOPS * 1e12), hbm / (PEAK_HBM_GBS * 1e9))
+            step_bytes += hbm
         else:
             ach = amount / sec / 1e9
             rooflines[name] = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                                    frac=round(ach / PEAK_HBM_GBS, 4), work=unit_desc)
+            attain_s += amount / (PEAK_HBM_GBS * 1e9)
+            step_bytes += amount
+        counted.append(name)
     roofline = dict(rooflines[dom])
     roofline.update(traffic=measured_traffic(args.workload, dom, wc["n_leaves"]),
                     traffic_unit="HBM bytes per launch (counters)",
                     kernel=dom, avg_launch_ms=round(dom_live["avg_ms"], 4), launches_per_step=dom_live["launches"],
                     timing="HIP events around this kernel's launches inside the timed steps")
-    # whole-step HBM fraction: the algorithmic bytes of every stage over the step time
-    step_bytes = sum(a for (b, a, _) in work.values() if b == "hbm") + wc["raster_bytes"]
+    # whole-step HBM fraction: the algorithmic bytes of the kernels that ran
+    # in the step (and the fused raster's own bytes) over the step time;
+    # attainable fraction: the step's time at the roof of each kernel's bound
     hbm_frac_step = step_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9)
+    attain_frac = attain_s / (ms_step * 1e-3)
 
     cpu = None
     if args.cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_window)
+        cpu = cpu_baseline(w, args.cpu_window, args.cpu_windows, args.cpu_threads)
 
     value = P / (ms_step * 1e-3) / 1e6
     out = {
@@ -294,6 +329,8 @@ def main():
         "gaussians_per_s": round(sc.n / (ms_step * 1e-3), 1),
         "peak_working_set_gib": round(r["peak_bytes"] / 2 ** 30, 4),
         "peak_working_set_torch_gib": round(torch_peak / 2 ** 30, 4),
+        "peak_by_category_gib": {c: round(b / 2 ** 30, 4) for c, b in mem["peak_by_cat"].items()},
+        "leaf_bytes": leaf_rep,
         "n_candidates": r["n_cand"],
         "n_intersections": r["n_isect"],
         "n_coarse_pairs": wc["cells"],
@@ -306,7 +343,11 @@ def main():
                           "current leaf's raster, so their step time is less than this sum)",
         "roofline": roofline,
         "rooflines_all": rooflines,
-        "step_hbm": {"algorithmic_bytes": int(step_bytes), "frac_of_8TBps": round(hbm_frac_step, 4)},
+        "step_hbm": {"algorithmic_bytes": int(step_bytes), "frac_of_8TBps": round(hbm_frac_step, 4),
+                     "kernels": counted, "raster_bytes": int(wc["raster_bytes"]),
+                     "raster_bytes_note": "fused raster: 4 B slot per intersection, 36 B attributes per (leaf, "
+                                          "candidate), 12 B target per pixel, 36 B 2D gradient per candidate"},
+        "attainable_roofline_frac": round(attain_frac, 4),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -354,11 +395,14 @@ def count_work(B, ctx, cam, params, budget):
     B.gs_release(ctx, proj)
     q = stats.cpu().tolist()
     P = cam.width * cam.height
-    # raster traffic per pixel: the fused forward + L1 + backward keeps the
-    # per-pixel state in registers and reads the target (12 B/px)
+    # algorithmic bytes of the fused forward + L1 + backward (per-pixel state
+    # stays in registers): every slot of the lists once, the attributes of
+    # each leaf's candidates once (36 B), the target (12 B/px) and the 2D
+    # gradient rows (36 B per candidate)
+    raster_bytes = 4 * n_isect + 36 * group_entries + 12 * P + 36 * n_cand
     return dict(q_f=int(q[0]), q_inc=int(q[1]), q_b=int(q[3]), sum_last=int(q[2]), n_isect=int(n_isect),
                 n_cand=int(n_cand),
-                n_leaves=len(leaves), tiles=int(tiles), pixels=P, raster_bytes=12 * P,
+                n_leaves=len(leaves), tiles=int(tiles), pixels=P, raster_bytes=int(raster_bytes),
                 radix_elems=int(radix_elems), group_entries=int(group_entries), cells=int(cells),
                 supers=int(supers))
 
@@ -497,56 +541,145 @@ def gated_sequence(args, B, scenes, torch, ctx, w, params, m, v, budget):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, window):
-    """The CPU oracle as it stands, single-threaded, on a bounded sample of the
-    same view: every per-Gaussian stage (f32 and f64 projection, binning of all
-    candidates, projection backward) over all N Gaussians, and per-pixel
-    compositing forward + backward on a window x window pixel window at the
-    image centre; the view time is the per-Gaussian time plus the window's
-    pixel time scaled by P / P_window."""
+def host_cpu():
+    """(logical CPUs the process may use, CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(w, window, n_windows, threads):
+    """The CPU oracle as it stands on a bounded sample of the same view, on
+    several host threads (its C routines run outside the GIL, each thread on
+    its own inputs and outputs; the arithmetic is the oracle's own):
+      - projection (f32 and f64) and projection backward over all N
+        Gaussians, split into equal bands of Gaussians over the threads;
+      - per window: binning, forward, L1 and raster backward, for n_windows
+        windows of window x window pixels, one at a seeded position in each
+        cell of a grid over the view, the windows spread over the threads.
+    The view time is the per-Gaussian time plus the windows' time scaled by
+    P / (pixels of the windows)."""
+    import concurrent.futures as cf
+
     import oracle
+    from differentiable_gaussian_splatting_amd import scenes
     cam, sc = w.camera, w.scene
+    W, H = cam.width, cam.height
     TW, TH = cam.tiles_x, cam.tiles_y
-    wt = max(1, window // 16)
-    tx0, ty0 = max(0, TW // 2 - wt // 2), max(0, TH // 2 - wt // 2)
-    leaf = oracle.rect(tx0, ty0, min(TW, tx0 + wt), min(TH, ty0 + wt))
-    p_win = (min(leaf.tx1 * 16, cam.width) - leaf.tx0 * 16) * (min(leaf.ty1 * 16, cam.height) - leaf.ty0 * 16)
+    avail, model = host_cpu()
+    nt = threads if threads > 0 else max(1, min(16, avail))
+    # the oracle's exp routines set up their constant tables on first use:
+    # take that first use here, before any thread runs
+    oracle.exp_cw(np.zeros(1, np.float32))
+    oracle.exp_falloff(np.zeros(1, np.float32))
+    pool = cf.ThreadPoolExecutor(max_workers=nt)
+
+    def bands(n):
+        e = np.linspace(0, n, nt + 1).astype(np.int64)
+        return [(int(a), int(b)) for a, b in zip(e[:-1], e[1:]) if b > a]
+
+    def sub(a, b):
+        return scenes.Scene(*(x[a:b] for x in sc.arrays()), sh_degree=sc.sh_degree)
+
+    # ---- projection over bands of Gaussians
     t = time.perf_counter()
-    p32 = oracle.project(cam, sc, "f32")
-    p64 = oracle.project(cam, sc, "f64")
+
+    def proj_band(ab):
+        s_ = sub(*ab)
+        return oracle.project(cam, s_, "f32"), oracle.project(cam, s_, "f64")
+
+    parts = list(pool.map(proj_band, bands(sc.n)))
+    p32 = {k: np.concatenate([p[0][k] for p in parts]) for k in parts[0][0]}
+    p64 = {k: np.concatenate([p[1][k] for p in parts]) for k in parts[0][1]}
+    del parts
+    t_proj = time.perf_counter() - t
     ids = np.nonzero(p32["cand"])[0]
     slot_of = np.full(sc.n, -1, np.int64)
     slot_of[ids] = np.arange(ids.size)
     c32 = {k: p32[k][ids] for k in ("rect", "xy", "conic", "depth", "opacity", "rgb")}
     c64 = {k: p64[k][ids] for k in ("xy", "conic", "opacity", "rgb")}
-    t_proj = time.perf_counter() - t
-    t = time.perf_counter()
-    bins = oracle.bin_leaf(TW, leaf, c32["rect"], c32["depth"], with_keys=False)
-    t_bin = time.perf_counter() - t
-    t = time.perf_counter()
-    H, W = cam.height, cam.width
+
+    # ---- windows: one per cell of a gx x gy grid, at a seeded position
+    wt = max(1, window // 16)
+    gx = max(1, min(TW, int(round(np.sqrt(n_windows * TW / TH)))))
+    gy = max(1, min(TH, int(round(n_windows / gx))))
+    rng = np.random.default_rng(12345)
+    wins = []
+    for j in range(gy):
+        for i in range(gx):
+            # inside its cell, so that no two windows share a pixel
+            cx0, cx1 = i * TW // gx, (i + 1) * TW // gx
+            cy0, cy1 = j * TH // gy, (j + 1) * TH // gy
+            if cx1 <= cx0 or cy1 <= cy0:
+                continue
+            tx0 = int(rng.integers(cx0, max(cx0 + 1, cx1 - wt + 1)))
+            ty0 = int(rng.integers(cy0, max(cy0 + 1, cy1 - wt + 1)))
+            wins.append(oracle.rect(tx0, ty0, min(cx1, tx0 + wt), min(cy1, ty0 + wt)))
     image = np.zeros((3, H, W), np.float32)
     tf = np.ones((H, W), np.float32)
     last = np.zeros((H, W), np.int32)
-    oracle.render_fwd(cam, leaf, bins, c32["xy"], c32["conic"], c32["opacity"], c32["rgb"], image, tf, last)
     dloss = np.zeros((3, H, W), np.float64)
-    oracle.loss_l1(cam, leaf, image.astype(np.float64), w.target, dloss)
-    grad2d = np.zeros((ids.size, 9), np.float64)
-    oracle.render_bwd(cam, leaf, bins, (c32["xy"], c32["conic"], c32["opacity"]),
-                      (c64["xy"], c64["conic"], c64["opacity"], c64["rgb"]), dloss, grad2d)
-    t_pix = time.perf_counter() - t
+
+    def win_pixels(r):
+        return (min(r.tx1 * 16, W) - r.tx0 * 16) * (min(r.ty1 * 16, H) - r.ty0 * 16)
+
+    def run_window(r):
+        bins = oracle.bin_leaf(TW, r, c32["rect"], c32["depth"], with_keys=False)
+        oracle.render_fwd(cam, r, bins, c32["xy"], c32["conic"], c32["opacity"], c32["rgb"], image, tf, last)
+        ys, xs = slice(r.ty0 * 16, min(r.ty1 * 16, H)), slice(r.tx0 * 16, min(r.tx1 * 16, W))
+        # the L1 term of the window's pixels (the oracle's own loss routine
+        # reads the window out of a full-size image)
+        full64 = window_image64(ys, xs)
+        oracle.loss_l1(cam, r, full64, w.target, dloss)
+        g2 = np.zeros((ids.size, 9), np.float64)
+        oracle.render_bwd(cam, r, bins, (c32["xy"], c32["conic"], c32["opacity"]),
+                          (c64["xy"], c64["conic"], c64["opacity"], c64["rgb"]), dloss, g2)
+        return g2
+
+    img64_all = np.zeros((3, H, W), np.float64)
+
+    def window_image64(ys, xs):
+        img64_all[:, ys, xs] = image[:, ys, xs]
+        return img64_all
+
     t = time.perf_counter()
-    oracle.project_bwd(cam, sc, p32["cand"], p32["flags"], slot_of, grad2d)
+    grads = list(pool.map(run_window, wins))
+    t_pix = time.perf_counter() - t
+    grad2d = grads[0]
+    for g in grads[1:]:
+        grad2d += g
+    del grads
+    p_win = sum(win_pixels(r) for r in wins)
+
+    # ---- projection backward over bands of Gaussians
+    t = time.perf_counter()
+    list(pool.map(lambda ab: oracle.project_bwd(cam, sub(*ab), p32["cand"][ab[0]:ab[1]],
+                                                p32["flags"][ab[0]:ab[1]], slot_of[ab[0]:ab[1]], grad2d),
+                  bands(sc.n)))
     t_pbwd = time.perf_counter() - t
+    pool.shutdown()
     P = W * H
-    t_view = t_proj + t_bin + t_pbwd + t_pix * (P / p_win)
-    log(f"[bench] cpu oracle: projection {t_proj:.1f}s, binning {t_bin:.1f}s, window raster {t_pix:.1f}s "
-        f"({p_win} px), projection backward {t_pbwd:.1f}s -> view {t_view:.1f}s")
-    return {"value": round(P / t_view / 1e6, 5), "unit": "Mpixel/s", "cores": 1, "kind": "oracle",
-            "sample": f"all {sc.n} Gaussians through projection (f32 + f64), binning and projection backward; "
-                      f"raster fwd+bwd on a {p_win}-pixel window at the image centre, scaled by P/P_window "
-                      f"= {P / p_win:.1f}",
-            "seconds_measured": round(t_proj + t_bin + t_pix + t_pbwd, 2), "seconds_view_estimate": round(t_view, 1)}
+    t_view = t_proj + t_pbwd + t_pix * (P / p_win)
+    log(f"[bench] cpu oracle on {nt} threads ({avail} available, {model}): projection {t_proj:.1f}s, "
+        f"{len(wins)} windows {t_pix:.1f}s ({p_win} px), projection backward {t_pbwd:.1f}s -> view {t_view:.1f}s")
+    return {"value": round(P / t_view / 1e6, 5), "unit": "Mpixel/s", "cores": nt, "kind": "oracle",
+            "host": {"cpus_available": avail, "cpu_model": model},
+            "sample": f"all {sc.n} Gaussians through projection (f32 + f64) and projection backward, in "
+                      f"{len(bands(sc.n))} bands over {nt} threads; binning + raster fwd + L1 + raster bwd on "
+                      f"{len(wins)} windows of {wt}x{wt} tiles ({p_win} px), one at a seeded position in each "
+                      f"cell of a {gx}x{gy} grid over the view, spread over {nt} threads; window time scaled by "
+                      f"P/P_windows = {P / p_win:.1f}",
+            "seconds_measured": round(t_proj + t_pix + t_pbwd, 2), "seconds_view_estimate": round(t_view, 1)}
 
 
 if __name__ == "__main__":

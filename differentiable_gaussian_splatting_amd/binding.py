@@ -89,7 +89,8 @@ class gs_view_opts(C.Structure):
                 ("grad3d_out", C.c_void_p), ("params_rw", C.c_void_p), ("adam_m", C.c_void_p),
                 ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64), ("leaves_in", C.c_void_p),
                 ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32), ("gate", C.c_void_p),
-                ("gate_view", C.c_int32), ("serial_leaves", C.c_int32), ("target_host", C.c_int32)]
+                ("gate_view", C.c_int32), ("serial_leaves", C.c_int32), ("target_host", C.c_int32),
+                ("leaf_bytes_out", C.c_void_p)]
 
 
 class gs_gate_decision(C.Structure):
@@ -230,6 +231,10 @@ class Context:
             self.close()
         except Exception:
             pass
+
+    def reset_peak(self):
+        """Restart the high-water marks (all and per category) at the live bytes."""
+        self.check(self.lib.gs_mem_reset_peak(self.handle))
 
     def mem_stats(self):
         s = gs_mem_stats()
@@ -496,6 +501,8 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     """One whole view in the library (see gs_train_view in include/gs.h).
     adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk).
     leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh.
+    max_leaves > 0: the view's leaves are returned, each with its est_bytes and the high-water
+    mark of the bytes the library held for it ("bytes").
     target: a device tensor, or a CPU tensor (pinned for the copies to overlap), which the
     library copies leaf by leaf."""
     o = gs_view_opts()
@@ -515,8 +522,10 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     o.loss_kind = 0 if loss == "l1" else 1
     o.ssim_lambda = float(lam)
     leaves_arr = (gs_leaf * max(max_leaves, 1))()
+    leaf_bytes = (C.c_uint64 * max(max_leaves, 1))()
     o.max_leaves = int(max_leaves)
     o.leaves_out = C.cast(leaves_arr, C.c_void_p) if max_leaves else None
+    o.leaf_bytes_out = C.cast(leaf_bytes, C.c_void_p) if max_leaves else None
     cs = cost_struct(cost) if cost else None
     o.cost = C.cast(C.pointer(cs), C.c_void_p) if cs is not None else None
     o.image_out = image_out.data_ptr() if image_out is not None else None
@@ -539,7 +548,9 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     if gate is not None:
         out.update(backward=bool(res.gate_backward), forced=bool(res.gate_forced), score=res.gate_score)
     if max_leaves:
+        nl = min(res.n_leaves, max_leaves)
         out["leaves"] = [dict(tx0=a.tx0, ty0=a.ty0, tx1=a.tx1, ty1=a.ty1, est_bytes=int(a.est_bytes),
-                              over_budget=bool(a.over_budget)) for a in leaves_arr[:min(res.n_leaves, max_leaves)]]
+                              over_budget=bool(a.over_budget), bytes=int(leaf_bytes[i]))
+                         for i, a in enumerate(leaves_arr[:nl])]
     del keep
     return out

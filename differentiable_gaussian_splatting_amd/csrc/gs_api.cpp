@@ -51,7 +51,12 @@ void* gs_malloc(gs_ctx* ctx, size_t bytes, int cat, std::vector<GsAlloc>* owner)
     ctx->peak = std::max(ctx->peak, ctx->live);
     ctx->peak_cat[cat] = std::max(ctx->peak_cat[cat], ctx->live_cat[cat]);
     ctx->n_alloc += 1;
-    owner->push_back(GsAlloc{p, bytes, cat});
+    const int32_t tag = ctx->tag >= 0 && (size_t)ctx->tag < ctx->tag_live.size() ? ctx->tag : -1;
+    if (tag >= 0) {
+        ctx->tag_live[tag] += bytes;
+        ctx->tag_peak[tag] = std::max(ctx->tag_peak[tag], ctx->tag_live[tag]);
+    }
+    owner->push_back(GsAlloc{p, bytes, cat, tag});
     return p;
 }
 
@@ -61,6 +66,7 @@ static void release_alloc(gs_ctx* ctx, const GsAlloc& a)
     else (void)hipFreeAsync(a.ptr, ctx->stream);
     ctx->live -= a.bytes;
     ctx->live_cat[a.cat] -= a.bytes;
+    if (a.tag >= 0 && (size_t)a.tag < ctx->tag_live.size()) ctx->tag_live[a.tag] -= a.bytes;
     ctx->n_free += 1;
 }
 
@@ -1299,6 +1305,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
         };
         if (host) {
             if ((st = ensure_side(ctx)) != GS_OK) return st;
+            LeafTag tag(ctx, 0);
             if ((st = slice_target(ctx, cam, target, true, grown(0), &sl[0], ctx->side)) == GS_OK &&
                 hipEventRecord(ctx->ev_done[0], ctx->side) != hipSuccess)
                 st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
@@ -1312,6 +1319,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                     break;
                 }
                 if (li + 1 < leaves.size()) {
+                    LeafTag tag(ctx, (int32_t)li + 1);
                     if ((st = slice_target(ctx, cam, target, true, grown(li + 1), &sl[(li + 1) % 3], ctx->side)) !=
                         GS_OK)
                         break;
@@ -1321,8 +1329,11 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                     }
                 }
             }
-            st = ssim_leaf(ctx, cam, proj, target, host, host ? &sl[li % 3] : nullptr, opts,
-                           gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, backward, grad2d, image, ssim_acc, &ni);
+            {
+                LeafTag tag(ctx, (int32_t)li);
+                st = ssim_leaf(ctx, cam, proj, target, host, host ? &sl[li % 3] : nullptr, opts,
+                               gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}, backward, grad2d, image, ssim_acc, &ni);
+            }
             *isect_total += ni;
             gs_free_all(ctx, &sl[li % 3].allocs);
         }
@@ -1333,6 +1344,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     if (pipe) {
         const gs_leaf& L = leaves[0];
         if ((st = ensure_side(ctx)) != GS_OK) return st;
+        LeafTag tag(ctx, 0);
         if (host && (st = slice_target(ctx, cam, target, true, pix_rect(cam, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1}),
                                        &sl[0], ctx->side)) != GS_OK)
             goto done;
@@ -1354,12 +1366,16 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                 st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
                 goto done;
             }
-            if ((st = fine_finish(ctx, proj, &cbs[li & 1], &bins)) != GS_OK) goto done;
+            {
+                LeafTag tag(ctx, (int32_t)li);
+                if ((st = fine_finish(ctx, proj, &cbs[li & 1], &bins)) != GS_OK) goto done;
+            }
             ni = bins->n_isect;
             if (li + 1 < leaves.size()) {
                 const gs_leaf& N = leaves[li + 1];
                 const gs_tile_rect nr{N.tx0, N.ty0, N.tx1, N.ty1};
                 CoarseBins& nx = cbs[(li + 1) & 1];
+                LeafTag tag(ctx, (int32_t)li + 1);
                 if (host) st = slice_target(ctx, cam, target, true, pix_rect(cam, nr), &sl[(li + 1) % 3], ctx->side);
                 if (st == GS_OK && (st = coarse_alloc(ctx, proj, nr, &nx)) == GS_OK)
                     st = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
@@ -1369,6 +1385,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                 }
             }
         } else {
+            LeafTag tag(ctx, (int32_t)li);
             if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
             if (host && (st = slice_target(ctx, cam, target, true, pix_rect(cam, r), &ts, ctx->stream)) != GS_OK) {
                 gs_release(ctx, bins);
@@ -1393,8 +1410,11 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                 goto done;
             }
             ctx->stream = ctx->rstream[k];
-            st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off,
-                                     backward ? grad2d : nullptr, backward);
+            {
+                LeafTag tag(ctx, (int32_t)li);
+                st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off,
+                                         backward ? grad2d : nullptr, backward);
+            }
             ctx->stream = main;
             if (st == GS_OK && hipEventRecord(ctx->ev_rendered[k], ctx->rstream[k]) != hipSuccess)
                 st = gs_fail(ctx, GS_ERR_DEVICE, "render event failed");
@@ -1414,8 +1434,11 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
         }
         // L1: each pixel's loss gradient is its own residual sign, so the
         // forward, the loss and the backward of a tile run in one wavefront
-        st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off, backward ? grad2d : nullptr,
-                                 backward);
+        {
+            LeafTag tag(ctx, (int32_t)li);
+            st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off,
+                                     backward ? grad2d : nullptr, backward);
+        }
         l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
         gs_release(ctx, bins);
         gs_free_all(ctx, &ts.allocs);
@@ -1519,6 +1542,9 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     }
     if (opts->leaves_out && opts->max_leaves > 0)
         std::memcpy(opts->leaves_out, leaves.data(), sizeof(gs_leaf) * std::min<size_t>(leaves.size(), opts->max_leaves));
+    // per-leaf accounting: allocations made for leaf i count in slot i
+    ctx->tag_live.assign(leaves.size(), 0);
+    ctx->tag_peak.assign(leaves.size(), 0);
 
     const int K = (params->sh_degree + 1) * (params->sh_degree + 1);
     const int F = 11 + 3 * K;
@@ -1591,11 +1617,14 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
             st = gs_fail(ctx, GS_ERR_INVALID_ARG, "Adam parameters / moments NULL");
             goto done;
         }
+        // The slot ranges cover [0, n_cand) exactly; a view without
+        // candidates runs one Adam launch over the empty range (0, 0), which
+        // updates every Gaussian with a zero gradient and reads no slot.
         const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(nc, opts->adam_chunk));
         float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * chunk, GS_MEM_GRAD, &view);
         if (!grad3d) { st = GS_ERR_OOM; goto done; }
-        for (int64_t s0 = 0; s0 < std::max<int64_t>(nc, 1); s0 += chunk) {
-            const int64_t s1 = std::min<int64_t>(nc, s0 + chunk);
+        for (int64_t s0 = 0; s0 < n_cand || s0 == 0; s0 += chunk) {
+            const int64_t s1 = std::min<int64_t>(n_cand, s0 + chunk);
             if ((st = launch_project_bwd(ctx, cam, params, proj, grad2d, s0, s1, grad3d)) != GS_OK) goto done;
             if ((st = launch_adam(ctx, proj, params->n, params->sh_degree, opts->params_rw, opts->adam_m,
                                   opts->adam_v, grad3d, s0, s1, opts->adam_step, opts->lr, opts->beta1, opts->beta2,
@@ -1610,10 +1639,15 @@ finish:
     result->n_isect = isect_total;
     result->n_leaves = (int32_t)leaves.size();
     result->peak_bytes = ctx->peak - live0;
+    if (opts->leaf_bytes_out && opts->max_leaves > 0)
+        std::memcpy(opts->leaf_bytes_out, ctx->tag_peak.data(),
+                    sizeof(uint64_t) * std::min<size_t>(ctx->tag_peak.size(), opts->max_leaves));
 done:
     gs_free_all(ctx, &view);
     gs_release(ctx, proj);
     ctx->peak = std::max(ctx->peak, peak_before);
+    ctx->tag_live.clear();
+    ctx->tag_peak.clear();
     return st;
 }
 

@@ -15,6 +15,7 @@ struct GsAlloc {
     void* ptr = nullptr;
     size_t bytes = 0;
     int cat = GS_MEM_SCRATCH;
+    int32_t tag = -1;              // leaf of the view it belongs to, or -1
 };
 
 struct GsTimerRec {
@@ -31,6 +32,10 @@ struct gs_ctx {
     std::string err;
     uint64_t live = 0, peak = 0, n_alloc = 0, n_free = 0;
     uint64_t live_cat[GS_MEM_NCAT] = {0}, peak_cat[GS_MEM_NCAT] = {0};
+    // per-leaf accounting of a view: allocations made while tag >= 0 count
+    // for that leaf (live and high-water bytes per leaf index)
+    int32_t tag = -1;
+    std::vector<uint64_t> tag_live, tag_peak;
     bool timing = false;
     std::string timing_only;       // time only kernels of this name (empty: all)
     std::vector<GsTimerRec> timers;
@@ -118,6 +123,14 @@ gs_status gs_fail(gs_ctx* ctx, gs_status st, const char* fmt, ...);
 void* gs_malloc(gs_ctx* ctx, size_t bytes, int cat, std::vector<GsAlloc>* owner);
 void gs_free_all(gs_ctx* ctx, std::vector<GsAlloc>* owner);
 void gs_free_one(gs_ctx* ctx, std::vector<GsAlloc>* owner, void* ptr);
+
+// Allocations made while a LeafTag is alive count for leaf `t` of the view.
+struct LeafTag {
+    gs_ctx* ctx;
+    int32_t prev;
+    LeafTag(gs_ctx* c, int32_t t) : ctx(c), prev(c->tag) { ctx->tag = t; }
+    ~LeafTag() { ctx->tag = prev; }
+};
 
 // ---- timing -----------------------------------------------------------------
 struct GsTimerScope {

@@ -417,6 +417,14 @@ typedef struct {
                                  /* a device slice before that leaf is         */
                                  /* rendered, so the image is never resident   */
                                  /* whole; 0: target is device memory          */
+    uint64_t* leaf_bytes_out;    /* host, nullable, max_leaves entries: per    */
+                                 /* leaf (same order as leaves_out) the high-  */
+                                 /* water mark of the library bytes that leaf  */
+                                 /* held: its binning buffers, slot array,     */
+                                 /* target slice and SSIM buffers; to compare  */
+                                 /* with its est_bytes (BoundedGS "02 /        */
+                                 /* method": the budget bounds each local      */
+                                 /* raster's buffers)                          */
 } gs_view_opts;
 
 typedef struct {

@@ -281,6 +281,40 @@ def test_train_view_chunked_update_matches_oracle(ctx, chunk, deg):
         assert np.all(np.abs(got - p) <= 1e-3 * np.abs(p - p0) + 2 * ulp), name
 
 
+@pytest.mark.parametrize("chunk", [0, 1, 700])
+def test_train_view_update_without_candidates(ctx, chunk):
+    """A view in which every Gaussian is culled still takes its one Adam step
+    (zero gradients: the moments decay and the parameters move by the decayed
+    first moment), in the fused form (chunk 0) and chunk by chunk of
+    candidate slots (no slot exists, so no projection backward runs)."""
+    import torch
+    w = scenes.make_workload("c2_hd", n=3000, width=120, height=90, seed=112)
+    w.scene.means[:, 2] = -5.0
+    o = oracle.train_view(w.camera, w.scene, w.target)
+    assert o["n_cand"] == 0
+    rng = np.random.default_rng(2)
+    m0 = [rng.normal(0, 1e-3, size=t.shape) for t in w.scene.arrays()]
+    v0 = [rng.uniform(1e-8, 1e-6, size=t.shape) for t in w.scene.arrays()]
+    ds = B.DeviceScene(w.scene, ctx.device)
+    m, v = B.like_scene(ds), B.like_scene(ds)
+    for dst, src in zip(m.tensors(), m0):
+        dst.copy_(torch.from_numpy(src.astype(np.float32)))
+    for dst, src in zip(v.tensors(), v0):
+        dst.copy_(torch.from_numpy(src.astype(np.float32)))
+    target = torch.from_numpy(w.target).to(ctx.device)
+    r = B.gs_train_view(ctx, w.camera, ds, target, adam=dict(step=4, params=ds, m=m, v=v, chunk=chunk))
+    assert r["n_cand"] == 0 and r["n_isect"] == 0
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    for k, t in enumerate(ds.tensors()):
+        p0 = w.scene.arrays()[k].astype(np.float64)
+        p, mm, vv = oracle.adam(np.zeros_like(p0), p0, m0[k].astype(np.float32), v0[k].astype(np.float32), step=4)
+        got = t.cpu().numpy().astype(np.float64)
+        ulp = np.spacing(np.abs(p).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - p) <= 1e-3 * np.abs(p - p0) + 2 * ulp), k
+        assert rel_l2(m.tensors()[k].cpu().numpy(), mm) <= 1e-6, k
+        assert rel_l2(v.tensors()[k].cpu().numpy(), vv) <= 1e-6, k
+
+
 @pytest.mark.parametrize("case", ["empty", "all_culled", "one_pixel", "ragged", "huge", "dense_tile"])
 def test_edge_cases(ctx, case):
     rng = np.random.default_rng(200)
@@ -315,6 +349,37 @@ def test_edge_cases(ctx, case):
     if case == "huge":
         assert (o["proj32"]["rect"][:5, 2] - o["proj32"]["rect"][:5, 0] > 10).all()
     compare_view(w, g, o)
+
+
+def test_cull_threshold_at_box_edges_and_corners(ctx):
+    """Gaussians whose alpha is exactly at 1/255 (one f32 logit step either
+    side) at the corner or edge pixel of an 8 x 8 box they lie outside
+    (tests/cull_cases.py): the sub-tile cull keeps every entry some pixel
+    includes, so lists, images, T_final and walk ends are bit-exact against
+    the oracle (which culls nothing), through the separate kernels and the
+    fused raster, and the gradients meet the bar."""
+    import torch
+    from tests import cull_cases as cc
+    cam, sc, cases = cc.threshold_scene()
+    rng = np.random.default_rng(301)
+    w = scenes.Workload(name="threshold", scene=sc, camera=cam,
+                        target=scenes.target_image(rng, cam.width, cam.height), loss="l1", budgets=())
+    o = oracle.train_view(cam, sc, w.target, keep_bins=True)
+    inc = [bool(o["image"][:, py, px].any()) for (_, _, _, side, px, py) in cases]
+    say(f"  {len(cases)} threshold Gaussians, {sum(inc)} of their pixels lit in the oracle image")
+    g = run_gpu_view(ctx, w)
+    compare_view(w, g, o)
+    assert np.array_equal(bits(g["t_final"]), bits(o["t_final"]))
+    assert np.array_equal(g["last"], o["last"].astype(np.int64))
+    ds = B.DeviceScene(sc, ctx.device)
+    img = torch.zeros((3, cam.height, cam.width), dtype=torch.float32, device=ctx.device)
+    g3 = torch.zeros((sc.n, 14), dtype=torch.float32, device=ctx.device)
+    r = B.gs_train_view(ctx, cam, ds, torch.from_numpy(w.target).to(ctx.device), image_out=img, grad3d_out=g3)
+    assert np.array_equal(bits(img.cpu().numpy()), bits(o["image"]))
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    gg, og = grad3d_groups(g3.cpu().numpy(), 0), grad3d_groups(o["grad3d"], 0)
+    for name in gg:
+        assert rel_l2(gg[name], og[name]) <= GRAD_TOL, name
 
 
 def test_isotropic_rotation_gradient_is_negligible(ctx):

@@ -115,5 +115,20 @@ def test_host_target_matches_device_target(ctx, loss, budget, serial):
     o = oracle.train_view(w.camera, w.scene, w.target, loss=loss,
                           **(dict(budget=budget, cost=cost) if budget and loss == "l1" else {}))
     _check(w, rh, imgh, g3h, o)
-    # the library's peak holds no whole target: a leaf slice at most
-    say(f"  peak {rh['peak_bytes']} B (device target {rd['peak_bytes']} B)")
+    # beyond the device-target view's peak, the library holds target slices
+    # only: at most three leaves' (the previous leaf's until its raster
+    # ends, the current one and the next one copied ahead), each leaf grown
+    # by one tile for SSIM; so with several leaves never the whole target
+    W, H = w.camera.width, w.camera.height
+    grow = 1 if loss == "l1_ssim" else 0
+
+    def slice_px(L):
+        x0, y0 = max(L["tx0"] - grow, 0) * 16, max(L["ty0"] - grow, 0) * 16
+        return (min((L["tx1"] + grow) * 16, W) - x0) * (min((L["ty1"] + grow) * 16, H) - y0)
+
+    bound = 3 * 12 * max(slice_px(L) for L in rh["leaves"]) + 3 * 256
+    say(f"  peak {rh['peak_bytes']} B (device target {rd['peak_bytes']} B; slices bound {bound} B, "
+        f"whole target {12 * W * H} B)")
+    assert rh["peak_bytes"] <= rd["peak_bytes"] + bound
+    if budget and bound < 12 * W * H:
+        assert rh["peak_bytes"] - rd["peak_bytes"] < 12 * W * H

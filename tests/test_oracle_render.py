@@ -207,3 +207,25 @@ def test_ssim_gradient_finite_differences(oracle_lib):
             continue
         fd = (oracle_lib.loss_ssim(cam, xp, y)[0] - oracle_lib.loss_ssim(cam, xm, y)[0]) / (2 * h)
         assert fd == pytest.approx(d[c, i, j], rel=1e-5, abs=1e-10)
+
+
+def test_threshold_scene_straddles_alpha_min_by_one_f32_step(oracle_lib):
+    """The cull-threshold scene (tests/cull_cases.py): every 'in' Gaussian is
+    included at its box's corner or edge pixel and skipped there at the next
+    smaller f32 logit; every 'out' Gaussian is skipped there and included at
+    the next larger one; each is centred outside the box of its box's pixel centres."""
+    from tests import cull_cases as cc
+    cam, sc, cases = cc.threshold_scene(n_cases=24, seed=301)
+    assert len(cases) == 48
+    p = oracle_lib.project(cam, sc, "f32")
+    for i, (bx, by, feat, side, px, py) in enumerate(cases):
+        g = dict(means=sc.means[i:i + 1], log_scales=sc.log_scales[i:i + 1], quats=sc.quats[i:i + 1],
+                 sh=sc.sh[i:i + 1])
+        lg = np.float32(sc.logits[i])
+        nxt = np.nextafter(lg, np.float32(-np.inf) if side == "in" else np.float32(np.inf))
+        assert cc.included(cam, g, float(lg), px, py) == (side == "in"), i
+        assert cc.included(cam, g, float(nxt), px, py) == (side != "in"), i
+        x, y = p["xy"][i]
+        # outside the box of the box's pixel centres, which the cull tests
+        assert not (bx + 0.5 <= x <= bx + 7.5 and by + 0.5 <= y <= by + 7.5), i
+        assert bx <= px < bx + 8 and by <= py < by + 8
