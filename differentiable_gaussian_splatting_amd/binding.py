@@ -156,6 +156,7 @@ def load(path: str = LIB_PATH):
         "gs_render_bwd": (st, [vp, P(gs_camera), vp, vp, vp, vp, vp]),
         "gs_project_bwd": (st, [vp, P(gs_camera), P(gs_params), vp, vp, vp]),
         "gs_loss_ssim": (st, [vp, i32, i32, vp, vp, C.c_float, vp, P(C.c_double), P(C.c_double)]),
+        "gs_loss_ssim_static": (st, [vp, i32, i32, vp, vp, C.c_float, vp, P(C.c_double), P(C.c_double)]),
         "gs_adam_step": (st, [vp, vp, i64, i32, P(gs_param_ptrs), P(gs_param_ptrs), P(gs_param_ptrs), vp, i32,
                               C.c_float, C.c_float, C.c_float, C.c_float]),
         "gs_release": (None, [vp, vp]),
@@ -422,6 +423,16 @@ def gs_loss_ssim(ctx: Context, image, target, dl_dimage, lam=0.2):
     ctx.check(ctx.lib.gs_loss_ssim(ctx.handle, W, H, _ptr(image), _ptr(target), float(lam), _ptr(dl_dimage),
                                    C.byref(loss), C.byref(ssim)))
     return float(loss.value), float(ssim.value)
+
+
+def gs_loss_ssim_static(ctx: Context, image, target, dl_dimage, lam=0.2, sums=True):
+    """gs_loss_ssim with the library's static work buffers (allocates
+    nothing); sums=False: the gradient only, asynchronous."""
+    loss, ssim = C.c_double(), C.c_double()
+    H, W = int(image.shape[1]), int(image.shape[2])
+    ctx.check(ctx.lib.gs_loss_ssim_static(ctx.handle, W, H, _ptr(image), _ptr(target), float(lam), _ptr(dl_dimage),
+                                          C.byref(loss) if sums else None, C.byref(ssim) if sums else None))
+    return (float(loss.value), float(ssim.value)) if sums else None
 
 
 def gs_adam_step(ctx: Context, proj, params: DeviceScene, m: DeviceScene, v: DeviceScene, grad3d, step,

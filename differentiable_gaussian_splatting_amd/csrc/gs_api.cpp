@@ -376,6 +376,12 @@ gs_status gs_ctx_create(gs_ctx** out, void* stream, gs_alloc_fn alloc, gs_free_f
         delete c;
         return GS_ERR_DEVICE;
     }
+    // the device address of the static SSIM work buffers, once per device
+    if (ssim_static_init(c) != GS_OK) {
+        (void)hipHostFree(c->pinned);
+        delete c;
+        return GS_ERR_DEVICE;
+    }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, c->device) == hipSuccess) {
         c->num_cu = prop.multiProcessorCount;
@@ -1055,6 +1061,34 @@ gs_status gs_loss_ssim(gs_ctx* ctx, int32_t width, int32_t height, const float* 
         }
     }
     gs_free_all(ctx, &tmp);
+    return st;
+}
+
+gs_status gs_loss_ssim_static(gs_ctx* ctx, int32_t width, int32_t height, const float* image, const float* target,
+                              float lambda, float* dl_dimage, double* loss, double* ssim)
+{
+    if (!ctx) return GS_ERR_INVALID_ARG;
+    if (width < 1 || height < 1 || !image || !target || !dl_dimage)
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "gs_loss_ssim_static arguments");
+    SsimStatic sb;
+    gs_status st = ssim_static_buffers(ctx, width, height, &sb);
+    if (st != GS_OK) return st;
+    const int64_t P = (int64_t)width * height;
+    const int64_t nb = ssim_partial_blocks(width, height);
+    // every map and block sum is written before it is read in this call
+    st = launch_ssim(ctx, width, height, 0, 0, width, height, (float)(1.0 / (3.0 * (double)P)), image, target, lambda,
+                     dl_dimage, sb.part, nb, sb.maps);
+    if (st == GS_OK && (loss || ssim)) {
+        st = launch_sum_f64(ctx, sb.part, nb, 2, sb.sums, 0, sb.chunk);
+        if (st == GS_OK) st = launch_sum_f64(ctx, sb.part + 1, nb, 2, sb.sums + 1, 0, sb.chunk);
+        double hv[2] = {0, 0};
+        if (st == GS_OK) st = readback(ctx, sb.sums, sizeof(hv), hv);
+        if (st == GS_OK) {
+            const double s = hv[0] / (3.0 * (double)P), l1 = hv[1] / (3.0 * (double)P);
+            if (ssim) *ssim = s;
+            if (loss) *loss = (1.0 - lambda) * l1 + lambda * (1.0 - s);
+        }
+    }
     return st;
 }
 

@@ -267,7 +267,23 @@ gs_status launch_ssim(gs_ctx* ctx, int W, int H, int ox0, int oy0, int ox1, int 
                       const float* target, float lambda, float* dl_dimage, double* partials /*[n_blocks*2]*/,
                       int64_t n_blocks, float* scratch /*[9][H][W] */);
 int64_t ssim_partial_blocks(int W, int H);
-gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate);
+// out = (accumulate ? out : 0) + sum of n values in[k * stride] in a fixed
+// order; chunk_sums: 256 doubles of device scratch for long inputs (null:
+// allocated and released by the call)
+gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate,
+                         double* chunk_sums = nullptr);
+// The static work buffers of gs_loss_ssim_static on the context's device:
+// ssim_static_init (called by gs_ctx_create with the device current) looks up
+// their address once per device; ssim_static_buffers hands out the parts for
+// a W x H image (GS_ERR_OVERFLOW beyond their capacity).
+struct SsimStatic {
+    float* maps;     // [9][W H]
+    double* part;    // [2 x ssim_partial_blocks]
+    double* chunk;   // [256]
+    double* sums;    // [2]: SSIM and L1 totals
+};
+gs_status ssim_static_init(gs_ctx* ctx);
+gs_status ssim_static_buffers(gs_ctx* ctx, int W, int H, SsimStatic* out);
 
 // adam.hip
 // Adam over the Gaussians whose candidates are the slots [s0, s1), with their

@@ -20,6 +20,8 @@
 // owned term nor an owned pixel's gradient uses.  Each centre's SSIM term is
 // summed by the leaf that owns it, so the leaves' sums and gradients are
 // those of the whole image.
+#include <mutex>
+
 #include "gs_device.h"
 #include "gs_internal.h"
 
@@ -238,7 +240,8 @@ __global__ __launch_bounds__(kSB) void k_ssim_grad(int W, int H, Win win, Owned 
 
 }  // namespace
 
-gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate)
+gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate,
+                         double* chunk_sums)
 {
     // two stages for long inputs: up to 256 blocks each sum a contiguous
     // chunk (fixed order), then one block sums the chunk sums
@@ -251,7 +254,7 @@ gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, d
     const int64_t nb = std::min<int64_t>(256, ceil_div(n, kChunk));
     const int64_t per = ceil_div(n, nb);
     std::vector<GsAlloc> tmp;
-    double* part = (double*)gs_malloc(ctx, sizeof(double) * nb, GS_MEM_SCRATCH, &tmp);
+    double* part = chunk_sums ? chunk_sums : (double*)gs_malloc(ctx, sizeof(double) * nb, GS_MEM_SCRATCH, &tmp);
     if (!part) return GS_ERR_OOM;
     hipLaunchKernelGGL(k_sum_chunks, dim3((unsigned)nb), dim3(256), 0, ctx->stream, in, n, stride, per, part);
     hipLaunchKernelGGL(k_sum_f64, dim3(1), dim3(256), 0, ctx->stream, part, nb, 1, out, accumulate);
@@ -282,5 +285,61 @@ gs_status launch_ssim(gs_ctx* ctx, int W, int H, int ox0, int oy0, int ox1, int 
     hipLaunchKernelGGL(k_ssim_grad, grid, dim3(kSB), 0, ctx->stream, W, H, win, own, scratch, image, target, lambda,
                        inv, dl_dimage);
     GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Work buffers of gs_loss_ssim_static: one static device array per device the
+// library runs on (held until the process ends), so that the SSIM loss can
+// run without allocating.  Layout: the 9 per-pixel partial maps of an image
+// of up to GS_SSIM_STATIC_MAX_PIXELS pixels, then the two sums of every
+// workgroup of the largest grid such an image can take (3 x ceil(W / 32) x
+// ceil(H / 16) <= 3 x 131072 for W H <= 2^21), 256 chunk sums and the two
+// totals.  Nothing in it accumulates across calls: every value a call reads
+// was written earlier in the same call.
+namespace {
+constexpr int64_t kStaticPixels = GS_SSIM_STATIC_MAX_PIXELS;
+constexpr int64_t kStaticBlocks = 3 * (kStaticPixels / kTY);
+constexpr size_t kStaticMapBytes = sizeof(float) * 9 * (size_t)kStaticPixels;
+constexpr size_t kStaticBytes = kStaticMapBytes + sizeof(double) * (2 * (size_t)kStaticBlocks + 256 + 2);
+static_assert(kStaticMapBytes % 256 == 0, "block sums start 256-byte aligned");
+constexpr int kStaticDevices = 64;
+
+static __device__ __align__(256) unsigned char ssim_scratch[kStaticBytes];
+
+std::mutex g_static_mu;
+unsigned char* g_static_ptr[kStaticDevices] = {};
+}  // namespace
+
+gs_status ssim_static_init(gs_ctx* ctx)
+{
+    if (ctx->device < 0 || ctx->device >= kStaticDevices)
+        return gs_fail(ctx, GS_ERR_DEVICE, "device %d beyond the static SSIM buffers' table", ctx->device);
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (g_static_ptr[ctx->device]) return GS_OK;
+    // the array's device address on the current device (each device holds
+    // its own copy); host code uses this address, never the symbol itself
+    void* p = nullptr;
+    GS_HIP(ctx, hipGetSymbolAddress(&p, HIP_SYMBOL(ssim_scratch)));
+    if (!p) return gs_fail(ctx, GS_ERR_DEVICE, "no device address for the static SSIM buffers");
+    g_static_ptr[ctx->device] = (unsigned char*)p;
+    return GS_OK;
+}
+
+gs_status ssim_static_buffers(gs_ctx* ctx, int W, int H, SsimStatic* out)
+{
+    if ((int64_t)W * H > kStaticPixels || ssim_partial_blocks(W, H) > kStaticBlocks)
+        return gs_fail(ctx, GS_ERR_OVERFLOW, "%d x %d image: the static SSIM buffers hold at most %lld pixels", W,
+                       H, (long long)kStaticPixels);
+    unsigned char* base = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        if (ctx->device >= 0 && ctx->device < kStaticDevices) base = g_static_ptr[ctx->device];
+    }
+    if (!base) return gs_fail(ctx, GS_ERR_STATE, "static SSIM buffers not set up on device %d", ctx->device);
+    out->maps = (float*)base;
+    out->part = (double*)(base + kStaticMapBytes);
+    out->chunk = out->part + 2 * kStaticBlocks;
+    out->sums = out->chunk + 256;
     return GS_OK;
 }

@@ -280,6 +280,25 @@ gs_status gs_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* par
 gs_status gs_loss_ssim(gs_ctx* ctx, int32_t width, int32_t height, const float* image, const float* target,
                        float lambda, float* dl_dimage, double* loss, double* ssim);
 
+/* gs_loss_ssim that allocates nothing, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments, results and kernels as gs_loss_ssim, with its
+ * work buffers (the 9 per-pixel partial maps and the per-workgroup sums) in a
+ * static device array of the library instead of allocated ones.  The array
+ * (about 78 MiB: GS_SSIM_STATIC_MAX_PIXELS pixels' maps and the sums of the
+ * largest grid such an image takes) exists once on each device the library
+ * runs on and is held until the process ends; its address is looked up per
+ * device when a context is created.  Every call on a device uses that
+ * device's array and overwrites it: calls that overlap on one device (two
+ * streams, two host threads) race and must not be issued.  Nothing carries
+ * over from one call to the next.  Errors: GS_ERR_INVALID_ARG (sizes < 1,
+ * NULL image / target / dl_dimage), GS_ERR_OVERFLOW (width x height above
+ * GS_SSIM_STATIC_MAX_PIXELS), GS_ERR_DEVICE.  Asynchronous when loss and
+ * ssim are both NULL (the gradient only), else synchronises. */
+#define GS_SSIM_STATIC_MAX_PIXELS (1 << 21)   /* 2,097,152: a 1920 x 1080 image fits */
+gs_status gs_loss_ssim_static(gs_ctx* ctx, int32_t width, int32_t height, const float* image, const float* target,
+                              float lambda, float* dl_dimage, double* loss, double* ssim);
+
 /* One Adam step (beta1, beta2, eps, bias correction at `step` >= 1) over all
  * N x F parameters; Gaussians that are not candidates get a zero gradient.
  * BoundedGS page "01": one update per view after the whole view's gradient.
