@@ -76,7 +76,10 @@ def regions_for(ov, leaves, name):
         heavy = int(np.argmax(ov.counts))
         aims, R = [(heavy % TW, heavy // TW), (TW // 4, TH // 4)], 24
     else:
-        aims, R = [(TW // 2, TH - 1), (TW // 2, TH // 2)], 32 if ov.sc.n > 8_000_000 else 40
+        # near the camera at the bottom (the largest rectangles), the centre
+        # (the dense clusters) and two off-axis quarters
+        aims = [(TW // 2, TH - 1), (TW // 2, TH // 2), (TW // 4, 3 * TH // 4), (3 * TW // 4, TH // 4)]
+        R = 32 if ov.sc.n > 8_000_000 else 40
     return F.leaf_regions(leaves, TW, TH, R, aims)
 
 
