@@ -232,17 +232,21 @@ static void clear_plan(gs_ctx* ctx, gs_proj* proj, bool retire)
 // what binning a planned leaf needs besides its own kernels: the leaf's
 // candidates in depth order, the offsets of their coarse pairs and the leaf's
 // tile offsets.
-static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ldev, int32_t nl)
+static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ldev, const gs_leaf* hleaves,
+                                   int32_t nl)
 {
     clear_plan(ctx, proj, true);
     const int64_t T = (int64_t)proj->TW * proj->TH;
     const int64_t nc = proj->n_cand;
     std::vector<GsAlloc> tmp;
     gs_status st = GS_OK;
-    std::vector<gs_leaf> plan(nl);
+    std::vector<gs_leaf> plan(hleaves, hleaves + nl);
     std::vector<uint64_t> hoff(nl + 1, 0), hcells(nl, 0), tbase(nl + 1, 0);
-    std::vector<uint32_t> hlc(2 * (size_t)nl, 0), cbase(nl, 0);
+    std::vector<uint32_t> cbase(nl, 0);
     std::vector<uint64_t> hisect(nl, 0);
+    // per-leaf results read back together: group offsets [nl + 1], then
+    // intersections [nl] (u64), then (first coarse offset, pairs) [2 nl] (u32)
+    std::vector<unsigned char> hres(sizeof(uint64_t) * (2 * (size_t)nl + 1) + sizeof(uint32_t) * 2 * (size_t)nl);
     uint64_t* lisect = nullptr;
     uint64_t G = 0;
     bool second = false;
@@ -255,49 +259,49 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(nc, 1), GS_MEM_SCRATCH, &tmp);
     uint64_t* goff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nc + 1), GS_MEM_SCRATCH, &tmp);
     if (!lot || !cnt || !goff) { st = GS_ERR_OOM; goto out; }
-    e = hipMemcpyAsync(plan.data(), ldev, sizeof(gs_leaf) * nl, hipMemcpyDeviceToHost, ctx->stream);
-    if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
-    if ((st = launch_leaf_map(ctx, ldev, nl, proj->TW, proj->TH, lot)) != GS_OK) goto out;
-    if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
-    if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
-    if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;   // also completes the plan copy
     for (int32_t L = 0; L < nl; ++L)
         tbase[L + 1] = tbase[L] + (uint64_t)(plan[L].tx1 - plan[L].tx0) * (uint64_t)(plan[L].ty1 - plan[L].ty0) + 1;
+    if ((st = launch_leaf_map(ctx, ldev, plan.data(), nl, proj->TW, proj->TH, lot)) != GS_OK) goto out;
+    if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
+    if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
+    if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;
     k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
     v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_PROJ, &proj->plan_allocs);
-    segoff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
+    segoff = (uint64_t*)gs_malloc(ctx, hres.size(), GS_MEM_SCRATCH, &tmp);
     ccnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     coff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (G + 1), GS_MEM_PROJ, &proj->plan_allocs);
-    lcells = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * 2 * nl, GS_MEM_SCRATCH, &tmp);
-    lisect = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * nl, GS_MEM_SCRATCH, &tmp);
     dtbase = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
     toff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
     torder = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
-    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !lcells || !lisect || !dtbase || !toff || !torder) {
+    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !dtbase || !toff || !torder) {
         st = GS_ERR_OOM;
         goto out;
     }
+    lisect = segoff + (nl + 1);
+    lcells = (uint32_t*)(lisect + nl);
     e = hipMemcpyAsync(dtbase, tbase.data(), sizeof(uint64_t) * (nl + 1), hipMemcpyHostToDevice, ctx->stream);
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, goff, k0, v0)) != GS_OK) goto out;
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
     if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, 0xFFFFFFFFu, segoff)) != GS_OK) goto out;
-    if ((st = launch_plan_offsets(ctx, proj, ldev, nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0, segoff, ccnt,
-                                  coff, lcells, lisect, dtbase, toff)) != GS_OK)
+    if ((st = launch_plan_offsets(ctx, proj, ldev, plan.data(), nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0,
+                                  segoff, ccnt, coff, lcells, lisect, dtbase, toff)) != GS_OK)
         goto out;
-    if ((st = launch_tile_order_sets(ctx, nl, dtbase, toff, torder)) != GS_OK) goto out;
-    e = hipMemcpyAsync(hoff.data(), segoff, sizeof(uint64_t) * (nl + 1), hipMemcpyDeviceToHost, ctx->stream);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(hlc.data(), lcells, sizeof(uint32_t) * 2 * nl, hipMemcpyDeviceToHost, ctx->stream);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(hisect.data(), lisect, sizeof(uint64_t) * nl, hipMemcpyDeviceToHost, ctx->stream);
+    if ((st = launch_tile_order_sets(ctx, nl, plan.data(), dtbase, toff, torder)) != GS_OK) goto out;
+    e = hipMemcpyAsync(hres.data(), segoff, hres.size(), hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
-    for (int32_t L = 0; L < nl; ++L) {
-        cbase[L] = hlc[2 * (size_t)L];
-        hcells[L] = hlc[2 * (size_t)L + 1];
+    {
+        const uint64_t* r64 = (const uint64_t*)hres.data();
+        const uint32_t* r32 = (const uint32_t*)(r64 + 2 * (size_t)nl + 1);
+        for (int32_t L = 0; L <= nl; ++L) hoff[L] = r64[L];
+        for (int32_t L = 0; L < nl; ++L) {
+            hisect[L] = r64[nl + 1 + L];
+            cbase[L] = r32[2 * (size_t)L];
+            hcells[L] = r32[2 * (size_t)L + 1];
+        }
     }
     gs_free_one(ctx, &proj->plan_allocs, second ? v0 : v1);
     proj->plan_cands = second ? v1 : v0;
@@ -618,11 +622,17 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
     if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) return st;
     uint64_t* sat = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (proj->TW + 1) * (int64_t)(proj->TH + 1),
                                          GS_MEM_SCRATCH, &tmp);
-    gs_leaf* ldev = (gs_leaf*)gs_malloc(ctx, sizeof(gs_leaf) * cap, GS_MEM_SCRATCH, &tmp);
-    int32_t* small = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * 2, GS_MEM_SCRATCH, &tmp);
+    // the leaf count and the over-budget flag (64 bytes), then the leaves:
+    // read back together, the first kFirst leaves with the count
+    constexpr int32_t kFirst = 128;
+    unsigned char* blk = (unsigned char*)gs_malloc(ctx, 64 + sizeof(gs_leaf) * (size_t)cap, GS_MEM_SCRATCH, &tmp);
+    int32_t* small = (int32_t*)blk;
+    gs_leaf* ldev = (gs_leaf*)(blk + 64);
     gs_leaf* rdev = n_roots > 0 ? (gs_leaf*)gs_malloc(ctx, sizeof(gs_leaf) * n_roots, GS_MEM_SCRATCH, &tmp) : nullptr;
     int32_t hv[2] = {0, 0};
-    if (!sat || !ldev || !small || (n_roots > 0 && !rdev)) {
+    std::vector<unsigned char> hblk(64 + sizeof(gs_leaf) * (size_t)std::min(cap, kFirst));
+    std::vector<gs_leaf> hleaves;
+    if (!sat || !blk || (n_roots > 0 && !rdev)) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
@@ -634,17 +644,32 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
         }
     }
     st = launch_plan(ctx, proj, sat, budget_bytes, &cm, rdev, n_roots, ldev, cap, small, small + 1);
-    if (st == GS_OK) st = readback(ctx, small, sizeof(hv), hv);
-    if (st == GS_OK && max_leaves > 0 && hv[0] > 0) {
-        const int32_t nw = std::min(hv[0], max_leaves);
-        hipError_t e = hipMemcpyAsync(leaves, ldev, sizeof(gs_leaf) * nw, hipMemcpyDeviceToHost, ctx->stream);
+    if (st == GS_OK) {
+        hipError_t e = hipMemcpyAsync(hblk.data(), blk, hblk.size(), hipMemcpyDeviceToHost, ctx->stream);
         if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
-        if (e != hipSuccess) st = gs_fail(ctx, GS_ERR_DEVICE, "leaf copy failed: %s", hipGetErrorString(e));
+        if (e != hipSuccess) st = gs_fail(ctx, GS_ERR_DEVICE, "plan read-back failed: %s", hipGetErrorString(e));
+    }
+    if (st == GS_OK) {
+        std::memcpy(hv, hblk.data(), sizeof(hv));
+        const int32_t nh = std::min(hv[0], cap);
+        if (nh > 0) {
+            hleaves.resize(nh);
+            const int32_t n1 = std::min(nh, kFirst);
+            std::memcpy(hleaves.data(), hblk.data() + 64, sizeof(gs_leaf) * n1);
+            if (nh > n1) {
+                hipError_t e = hipMemcpyAsync(hleaves.data() + n1, ldev + n1, sizeof(gs_leaf) * (nh - n1),
+                                              hipMemcpyDeviceToHost, ctx->stream);
+                if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+                if (e != hipSuccess) st = gs_fail(ctx, GS_ERR_DEVICE, "leaf copy failed: %s", hipGetErrorString(e));
+            }
+            if (st == GS_OK && max_leaves > 0)
+                std::memcpy(leaves, hleaves.data(), sizeof(gs_leaf) * std::min(nh, max_leaves));
+        }
     }
     // Attach the leaf -> candidate groups of this plan to the projection, so
     // that gs_bin_sort of a planned leaf visits only the candidates meeting it.
     if (st == GS_OK && hv[0] > 0 && hv[0] <= cap) {
-        st = build_plan_groups(ctx, const_cast<gs_proj*>(proj), ldev, hv[0]);
+        st = build_plan_groups(ctx, const_cast<gs_proj*>(proj), ldev, hleaves.data(), hv[0]);
         const_cast<gs_proj*>(proj)->plan_cost = cm;
     }
     gs_free_all(ctx, &tmp);
@@ -1391,11 +1416,28 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
         int64_t ni = 0;
         gs_tile_rect r{L.tx0, L.ty0, L.tx1, L.ty1};
         TargetSlice& ts = sl[li % 3];
+        // the next leaf's first stage (and its target slice) on the side
+        // stream, behind everything the main stream has queued so far
+        auto stage_next = [&]() -> gs_status {
+            if (li + 1 >= leaves.size()) return GS_OK;
+            const gs_leaf& N = leaves[li + 1];
+            const gs_tile_rect nr{N.tx0, N.ty0, N.tx1, N.ty1};
+            CoarseBins& nx = cbs[(li + 1) & 1];
+            LeafTag tag(ctx, (int32_t)li + 1);
+            gs_status s2 = GS_OK;
+            if (host) s2 = slice_target(ctx, cam, target, true, pix_rect(cam, nr), &sl[(li + 1) % 3], ctx->side);
+            if (s2 == GS_OK && (s2 = coarse_alloc(ctx, proj, nr, &nx)) == GS_OK)
+                s2 = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
+            return s2;
+        };
         if (pipe) {
             // this leaf's first stage (and its target slice) is done on the
-            // side stream; its slot array is written here, and the next
-            // leaf's first stage starts on the side stream behind everything
-            // queued so far
+            // side stream; its slot array is written here.  With overlapped
+            // rasters the next leaf's first stage is queued once this leaf's
+            // raster is launched (its buffers' allocations take host time
+            // the raster need not wait for); rendering one leaf at a time on
+            // the main stream, it is queued before the raster, so that it
+            // runs beside it
             if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
                 st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
                 goto done;
@@ -1405,18 +1447,9 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                 if ((st = fine_finish(ctx, proj, &cbs[li & 1], &bins)) != GS_OK) goto done;
             }
             ni = bins->n_isect;
-            if (li + 1 < leaves.size()) {
-                const gs_leaf& N = leaves[li + 1];
-                const gs_tile_rect nr{N.tx0, N.ty0, N.tx1, N.ty1};
-                CoarseBins& nx = cbs[(li + 1) & 1];
-                LeafTag tag(ctx, (int32_t)li + 1);
-                if (host) st = slice_target(ctx, cam, target, true, pix_rect(cam, nr), &sl[(li + 1) % 3], ctx->side);
-                if (st == GS_OK && (st = coarse_alloc(ctx, proj, nr, &nx)) == GS_OK)
-                    st = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
-                if (st != GS_OK) {
-                    gs_release(ctx, bins);
-                    goto done;
-                }
+            if (opts->serial_leaves && (st = stage_next()) != GS_OK) {
+                gs_release(ctx, bins);
+                goto done;
             }
         } else {
             LeafTag tag(ctx, (int32_t)li);
@@ -1455,6 +1488,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
             l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
             inflight[k] = bins;
             if (st != GS_OK) goto done;
+            if ((st = stage_next()) != GS_OK) goto done;
             if (li >= 1 && inflight[k ^ 1]) {
                 if (hipStreamWaitEvent(main, ctx->ev_rendered[k ^ 1], 0) != hipSuccess) {
                     st = gs_fail(ctx, GS_ERR_DEVICE, "render stream wait failed");

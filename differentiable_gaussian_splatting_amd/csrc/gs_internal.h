@@ -230,9 +230,13 @@ gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* 
                               const float* target, PixFrame tf, float* image_out, double* l1_part, float* grad2d,
                               bool backward);
 // tiles of each of n_sets offset arrays (set L at base[L], base[L + 1] - base[L]
-// - 1 tiles) in the fused raster's launch order, written at the same bases
-gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const uint64_t* base, const uint64_t* offsets,
-                                 uint32_t* order);
+// - 1 tiles; hleaves: the sets' leaves on the host, for the grid) in the
+// fused raster's launch order, written at the same bases
+gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const gs_leaf* hleaves, const uint64_t* base,
+                                 const uint64_t* offsets, uint32_t* order);
+// the same for base = null: one set of n1 tiles at 0 (hleaves[0] its extent)
+gs_status launch_tile_order(gs_ctx* ctx, int32_t n_sets, const gs_leaf* hleaves, const uint64_t* base, int64_t n1,
+                            const uint64_t* offsets, uint32_t* order);
 gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
                             const gs_raster* r, const float* dl_dimage, PixFrame dlf, float* grad2d);
 
@@ -245,15 +249,17 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
                       int32_t* count_dev, int32_t* over_dev);
 
 // leaf -> candidate groups (planner.hip)
-gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int TH, int32_t* lot);
+// hleaves: the same leaves on the host (their sizes shape the launch grids)
+gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, const gs_leaf* hleaves, int32_t n_leaves, int TW,
+                          int TH, int32_t* lot);
 gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
                             const int32_t* lot, uint32_t* cnt, const uint64_t* off, uint32_t* keys, uint32_t* vals);
 // Per-view offsets of a plan: per grouped entry (sorted by leaf) its coarse
 // pair count and their exclusive scan (u32, modulo 2^32), per leaf the scan
 // value at its first entry and its pair count (leaf_cells [2 * n_leaves]),
 // and per leaf the exclusive scan of its tile counts at toff + toff_base[L].
-gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
-                              int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
+gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
+                              int32_t n_leaves, int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
                               const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
                               uint32_t* leaf_cells, uint64_t* leaf_isect, const uint64_t* toff_base, uint64_t* toff);
 

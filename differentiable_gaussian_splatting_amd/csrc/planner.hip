@@ -290,13 +290,21 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
 
 namespace {
 
-__global__ void k_leaf_map(const gs_leaf* __restrict__ leaves, int TW, int32_t* __restrict__ lot)
+// Per-leaf passes over a leaf's tiles run on a grid of (chunk, leaf): block
+// (c, L) takes tiles [c kLeafChunk, (c + 1) kLeafChunk) of leaf L in its
+// leaf-local row-major order (blocks past the leaf's end return), so that a
+// view's leaves keep the whole GPU busy whatever their number.
+constexpr int kLeafChunk = 4096;
+
+__global__ __launch_bounds__(256) void k_leaf_map(const gs_leaf* __restrict__ leaves, int TW,
+                                                  int32_t* __restrict__ lot)
 {
-    const gs_leaf L = leaves[blockIdx.x];
+    const gs_leaf L = leaves[blockIdx.y];
     const int w = L.tx1 - L.tx0;
     const int64_t tot = (int64_t)w * (L.ty1 - L.ty0);
-    for (int64_t k = threadIdx.x; k < tot; k += blockDim.x)
-        lot[(int64_t)(L.ty0 + k / w) * TW + (L.tx0 + k % w)] = (int32_t)blockIdx.x;
+    const int64_t k0 = (int64_t)blockIdx.x * kLeafChunk, k1 = min(tot, k0 + kLeafChunk);
+    for (int64_t k = k0 + threadIdx.x; k < k1; k += 256)
+        lot[(int64_t)(L.ty0 + k / w) * TW + (L.tx0 + k % w)] = (int32_t)blockIdx.y;
 }
 
 __device__ __forceinline__ bool rect_meets(int4 r, const gs_leaf& L)
@@ -379,64 +387,100 @@ __global__ void k_leaf_cell_bounds(int nl, const uint64_t* __restrict__ goff, co
     isect[L] = toff[toff_base[L] + (uint64_t)(lf.tx1 - lf.tx0) * (uint64_t)(lf.ty1 - lf.ty0)];
 }
 
-// per leaf (one workgroup): exclusive scan of its tiles' candidate counts in
-// leaf-local row-major order, written at out + base[L] (T_L + 1 entries).
-// Wavefront w owns a contiguous segment of the leaf's tiles, read in
-// coalesced chunks of 64: it sums the segment (four chunks' loads in flight
-// at a time), one scan over the 16 segment sums gives each segment's offset,
-// and a second walk scans chunk by chunk (wave scan plus a carry) and writes.
+// Per leaf, the exclusive scan of its tiles' candidate counts in leaf-local
+// row-major order, written at out + base[L] (T_L + 1 entries, the last the
+// leaf's total), in three steps over the (chunk, leaf) grid: each block sums
+// its chunk; one thread per leaf scans its chunk sums (in place) and writes
+// the total; each block scans its chunk (256 tiles per round: a wavefront
+// scan, the four wavefront totals through LDS, a running carry) from its
+// chunk's offset.
 __device__ __forceinline__ uint64_t leaf_tile_count(const int32_t* __restrict__ tile_cnt, int TW, const gs_leaf& lf,
                                                     int TWL, int64_t t, int64_t t1)
 {
     return t < t1 ? (uint64_t)tile_cnt[(int64_t)(lf.ty0 + t / TWL) * TW + lf.tx0 + t % TWL] : 0ull;
 }
 
-__global__ __launch_bounds__(1024) void k_leaf_toff(const gs_leaf* __restrict__ leaves,
-                                                    const int32_t* __restrict__ tile_cnt, int TW,
-                                                    const uint64_t* __restrict__ base, uint64_t* __restrict__ out)
+__global__ __launch_bounds__(256) void k_toff_sums(const gs_leaf* __restrict__ leaves,
+                                                   const int32_t* __restrict__ tile_cnt, int TW,
+                                                   uint64_t* __restrict__ csum)
 {
-    __shared__ uint64_t wsum[16];
-    const gs_leaf lf = leaves[blockIdx.x];
+    __shared__ uint64_t ws[4];
+    const gs_leaf lf = leaves[blockIdx.y];
     const int TWL = lf.tx1 - lf.tx0;
     const int64_t n = (int64_t)TWL * (lf.ty1 - lf.ty0);
-    uint64_t* o = out + base[blockIdx.x];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t seg = ((n + 15) / 16 + 63) / 64 * 64;   // tiles per wavefront, a multiple of 64
-    const int64_t t0 = min(n, (int64_t)wave * seg), t1 = min(n, t0 + seg);
+    const int64_t t0 = (int64_t)blockIdx.x * kLeafChunk, t1 = min(n, t0 + kLeafChunk);
     uint64_t s = 0;
-    for (int64_t c = t0; c < t1; c += 256) {
-        const uint64_t a0 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + lane, t1);
-        const uint64_t a1 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + 64 + lane, t1);
-        const uint64_t a2 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + 128 + lane, t1);
-        const uint64_t a3 = leaf_tile_count(tile_cnt, TW, lf, TWL, c + 192 + lane, t1);
-        s += (a0 + a1) + (a2 + a3);
-    }
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) s += leaf_tile_count(tile_cnt, TW, lf, TWL, t, t1);
     s = gsd::wave_sum_u64(s);
-    if (lane == 0) wsum[wave] = s;
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
     __syncthreads();
-    uint64_t carry = 0;
-    for (int w = 0; w < wave; ++w) carry += wsum[w];
-    for (int64_t c = t0; c < t1; c += 64) {
-        const uint64_t v = leaf_tile_count(tile_cnt, TW, lf, TWL, c + lane, t1);
+    if (threadIdx.x == 0) csum[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
+}
+
+__global__ __launch_bounds__(256) void k_toff_chunk_scan(int nl, int nchunk, const gs_leaf* __restrict__ leaves,
+                                                         uint64_t* __restrict__ csum,
+                                                         const uint64_t* __restrict__ base, uint64_t* __restrict__ out)
+{
+    for (int L = blockIdx.x * 256 + threadIdx.x; L < nl; L += gridDim.x * 256) {
+        const gs_leaf lf = leaves[L];
+        const int64_t n = (int64_t)(lf.tx1 - lf.tx0) * (lf.ty1 - lf.ty0);
+        uint64_t run = 0;
+        for (int c = 0; c < nchunk; ++c) {
+            uint64_t& x = csum[(int64_t)L * nchunk + c];
+            const uint64_t v = x;
+            x = run;
+            run += v;
+        }
+        out[base[L] + n] = run;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_toff_write(const gs_leaf* __restrict__ leaves,
+                                                    const int32_t* __restrict__ tile_cnt, int TW,
+                                                    const uint64_t* __restrict__ csum,
+                                                    const uint64_t* __restrict__ base, uint64_t* __restrict__ out)
+{
+    __shared__ uint64_t ws[4];
+    const gs_leaf lf = leaves[blockIdx.y];
+    const int TWL = lf.tx1 - lf.tx0;
+    const int64_t n = (int64_t)TWL * (lf.ty1 - lf.ty0);
+    const int64_t t0 = (int64_t)blockIdx.x * kLeafChunk, t1 = min(n, t0 + kLeafChunk);
+    if (t0 >= t1) return;
+    uint64_t* o = out + base[blockIdx.y];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t carry = csum[(int64_t)blockIdx.y * gridDim.x + blockIdx.x];
+    for (int64_t c = t0; c < t1; c += 256) {
+        const int64_t t = c + threadIdx.x;
+        const uint64_t v = leaf_tile_count(tile_cnt, TW, lf, TWL, t, t1);
         uint64_t x = v;
         for (int d = 1; d < 64; d <<= 1) {
             const uint64_t u = __shfl_up((unsigned long long)x, d, 64);
             if (lane >= d) x += u;
         }
-        if (c + lane < t1) o[c + lane] = carry + x - v;
-        carry += __shfl((unsigned long long)x, 63, 64);
-    }
-    if (tid == 0) {
-        uint64_t tot = 0;
-        for (int w = 0; w < 16; ++w) tot += wsum[w];
-        o[n] = tot;
+        if (lane == 63) ws[wave] = x;
+        __syncthreads();
+        uint64_t before = 0;
+        for (int w = 0; w < wave; ++w) before += ws[w];
+        if (t < t1) o[t] = carry + before + x - v;
+        carry += ws[0] + ws[1] + ws[2] + ws[3];
+        __syncthreads();
     }
 }
 
 }  // namespace
 
-gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
-                              int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
+// chunks of kLeafChunk tiles of the largest leaf (host leaves)
+static int leaf_chunks(const gs_leaf* hleaves, int32_t n_leaves)
+{
+    int64_t m = 1;
+    for (int32_t L = 0; L < n_leaves; ++L)
+        m = std::max<int64_t>(m, ceil_div((int64_t)(hleaves[L].tx1 - hleaves[L].tx0) * (hleaves[L].ty1 - hleaves[L].ty0),
+                                          kLeafChunk));
+    return (int)m;
+}
+
+gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
+                              int32_t n_leaves, int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
                               const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
                               uint32_t* leaf_cells, uint64_t* leaf_isect, const uint64_t* toff_base, uint64_t* toff)
 {
@@ -447,22 +491,33 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
     gs_status st = launch_scan_u32_to_u32(ctx, cell_cnt, cell_off, n_entries);
     if (st != GS_OK) return st;
     if (n_leaves > 0) {
-        hipLaunchKernelGGL(k_leaf_toff, dim3((unsigned)n_leaves), dim3(1024), 0, ctx->stream, leaves_dev,
-                           proj->tile_cnt, proj->TW, toff_base, toff);
+        const int nch = leaf_chunks(hleaves, n_leaves);
+        std::vector<GsAlloc> tmp;
+        uint64_t* csum = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (size_t)nch * n_leaves, GS_MEM_SCRATCH, &tmp);
+        if (!csum) return GS_ERR_OOM;
+        const dim3 grid((unsigned)nch, (unsigned)n_leaves);
+        hipLaunchKernelGGL(k_toff_sums, grid, dim3(256), 0, ctx->stream, leaves_dev, proj->tile_cnt, proj->TW, csum);
+        hipLaunchKernelGGL(k_toff_chunk_scan, dim3((unsigned)ceil_div(n_leaves, 256)), dim3(256), 0, ctx->stream,
+                           n_leaves, nch, leaves_dev, csum, toff_base, toff);
+        hipLaunchKernelGGL(k_toff_write, grid, dim3(256), 0, ctx->stream, leaves_dev, proj->tile_cnt, proj->TW, csum,
+                           toff_base, toff);
         hipLaunchKernelGGL(k_leaf_cell_bounds, dim3((unsigned)ceil_div(n_leaves, 256)), dim3(256), 0, ctx->stream,
                            n_leaves, group_off, cell_off, leaves_dev, toff_base, toff, leaf_cells, leaf_isect);
+        gs_free_all(ctx, &tmp);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }
 
-gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, int TW, int TH, int32_t* lot)
+gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, const gs_leaf* hleaves, int32_t n_leaves, int TW,
+                          int TH, int32_t* lot)
 {
     // -1 on tiles no leaf covers (a layout that renders part of the view)
     gs_status st = launch_fill_u32(ctx, (uint32_t*)lot, 0xFFFFFFFFu, (int64_t)TW * TH);
     if (st != GS_OK) return st;
     if (n_leaves > 0)
-        hipLaunchKernelGGL(k_leaf_map, dim3((unsigned)n_leaves), dim3(256), 0, ctx->stream, leaves_dev, TW, lot);
+        hipLaunchKernelGGL(k_leaf_map, dim3((unsigned)leaf_chunks(hleaves, n_leaves), (unsigned)n_leaves), dim3(256), 0,
+                           ctx->stream, leaves_dev, TW, lot);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

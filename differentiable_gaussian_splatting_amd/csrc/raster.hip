@@ -705,41 +705,88 @@ __device__ __forceinline__ uint32_t wave_bucket_add(int b, uint32_t* ctr, int la
     return slot;
 }
 
-// Workgroup L orders the tiles of list set L: its offsets start at
-// offsets + base[L] and its order goes to order + base[L], with
-// base[L + 1] - base[L] - 1 tiles (base = null: one set of n tiles at 0).
-__global__ __launch_bounds__(1024) void k_tile_order(int64_t n1, const uint64_t* __restrict__ base,
-                                                     const uint64_t* __restrict__ offsets0,
-                                                     uint32_t* __restrict__ order0)
+// The tiles of list set L (its offsets start at offsets0 + base[L], its
+// order goes to order0 + base[L], base[L + 1] - base[L] - 1 tiles; base =
+// null: one set of n1 tiles at 0) by bucket, longest first, on a grid of
+// (chunk of kOrderChunk tiles, set): every block counts its tiles per bucket
+// in LDS and adds the counts to the set's (k_order_count); one thread per set
+// turns them into the buckets' starts, longest bucket first (k_order_base);
+// every block counts again, reserves a range of each bucket of its set with
+// one atomic per bucket, and places its tiles there (k_order_place).  The
+// order of the tiles inside a bucket depends on the order of those atomics.
+constexpr int kOrderChunk = 4096;
+
+__device__ __forceinline__ void order_set(const uint64_t* base, int64_t n1, int set, uint64_t& b0, int64_t& n)
+{
+    b0 = base ? base[set] : 0;
+    n = base ? (int64_t)(base[set + 1] - b0) - 1 : n1;
+}
+
+__global__ __launch_bounds__(256) void k_order_count(int64_t n1, const uint64_t* __restrict__ base,
+                                                     const uint64_t* __restrict__ offsets0, uint32_t* __restrict__ cnt)
 {
     __shared__ uint32_t ctr[128];
-    const uint64_t b0 = base ? base[blockIdx.x] : 0;
-    const int64_t n = base ? (int64_t)(base[blockIdx.x + 1] - b0) - 1 : n1;
+    uint64_t b0;
+    int64_t n;
+    order_set(base, n1, blockIdx.y, b0, n);
+    const int64_t i0 = (int64_t)blockIdx.x * kOrderChunk, i1 = min(n, i0 + kOrderChunk);
+    if (i0 >= i1) return;
+    const uint64_t* __restrict__ offsets = offsets0 + b0;
+    const int t = threadIdx.x, lane = t & 63;
+    if (t < 128) ctr[t] = 0;
+    __syncthreads();
+    for (int64_t c = i0; c < i1; c += 256) {
+        const int64_t i = c + t;
+        const int b = i < i1 ? len_bucket(offsets[i + 1] - offsets[i]) : -1;
+        (void)wave_bucket_add(b, ctr, lane);
+    }
+    __syncthreads();
+    if (t < 128 && ctr[t]) atomicAdd(&cnt[(int64_t)blockIdx.y * 128 + t], ctr[t]);
+}
+
+__global__ __launch_bounds__(256) void k_order_base(int n_sets, uint32_t* __restrict__ cnt)
+{
+    for (int L = blockIdx.x * 256 + threadIdx.x; L < n_sets; L += gridDim.x * 256) {
+        uint32_t run = 0;
+        for (int b = 127; b >= 0; --b) {
+            const uint32_t c = cnt[(int64_t)L * 128 + b];
+            cnt[(int64_t)L * 128 + b] = run;
+            run += c;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_order_place(int64_t n1, const uint64_t* __restrict__ base,
+                                                     const uint64_t* __restrict__ offsets0, uint32_t* __restrict__ cursor,
+                                                     uint32_t* __restrict__ order0)
+{
+    __shared__ uint32_t ctr[128], start[128];
+    uint64_t b0;
+    int64_t n;
+    order_set(base, n1, blockIdx.y, b0, n);
+    const int64_t i0 = (int64_t)blockIdx.x * kOrderChunk, i1 = min(n, i0 + kOrderChunk);
+    if (i0 >= i1) return;
     const uint64_t* __restrict__ offsets = offsets0 + b0;
     uint32_t* __restrict__ order = order0 + b0;
     const int t = threadIdx.x, lane = t & 63;
     if (t < 128) ctr[t] = 0;
     __syncthreads();
-    for (int64_t i0 = 0; i0 < n; i0 += 1024) {
-        const int64_t i = i0 + t;
-        const int b = i < n ? len_bucket(offsets[i + 1] - offsets[i]) : -1;
+    for (int64_t c = i0; c < i1; c += 256) {
+        const int64_t i = c + t;
+        const int b = i < i1 ? len_bucket(offsets[i + 1] - offsets[i]) : -1;
         (void)wave_bucket_add(b, ctr, lane);
     }
     __syncthreads();
-    if (t == 0) {   // exclusive prefix, longest bucket first
-        uint32_t run = 0;
-        for (int b = 127; b >= 0; --b) {
-            const uint32_t c = ctr[b];
-            ctr[b] = run;
-            run += c;
-        }
+    if (t < 128) {
+        start[t] = ctr[t] ? atomicAdd(&cursor[(int64_t)blockIdx.y * 128 + t], ctr[t]) : 0u;
+        ctr[t] = 0;
     }
     __syncthreads();
-    for (int64_t i0 = 0; i0 < n; i0 += 1024) {
-        const int64_t i = i0 + t;
-        const int b = i < n ? len_bucket(offsets[i + 1] - offsets[i]) : -1;
+    for (int64_t c = i0; c < i1; c += 256) {
+        const int64_t i = c + t;
+        const int b = i < i1 ? len_bucket(offsets[i + 1] - offsets[i]) : -1;
         const uint32_t pos = wave_bucket_add(b, ctr, lane);
-        if (b >= 0) order[pos] = (uint32_t)i;
+        if (b >= 0) order[start[b] + pos] = (uint32_t)i;
     }
 }
 
@@ -807,8 +854,14 @@ gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* 
         if (!order) {
             uint32_t* o = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nt, GS_MEM_RASTER, &tmp);
             if (!o) return GS_ERR_OOM;
-            GsTimerScope ts(ctx, "tile_order");
-            hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, ctx->stream, nt, nullptr, bins->offsets, o);
+            gs_leaf one{};
+            one.tx1 = bins->TWL;
+            one.ty1 = bins->THL;
+            const gs_status so = launch_tile_order(ctx, 1, &one, nullptr, nt, bins->offsets, o);
+            if (so != GS_OK) {
+                gs_free_all(ctx, &tmp);
+                return so;
+            }
             order = o;
         }
         {
@@ -829,14 +882,33 @@ gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* 
     return GS_OK;
 }
 
-gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const uint64_t* base, const uint64_t* offsets,
-                                 uint32_t* order)
+gs_status launch_tile_order(gs_ctx* ctx, int32_t n_sets, const gs_leaf* hleaves, const uint64_t* base, int64_t n1,
+                            const uint64_t* offsets, uint32_t* order)
 {
-    if (n_sets > 0) {
+    if (n_sets <= 0) return GS_OK;
+    int64_t nch = 1;
+    for (int32_t L = 0; L < n_sets; ++L)
+        nch = std::max<int64_t>(nch, ceil_div((int64_t)(hleaves[L].tx1 - hleaves[L].tx0) *
+                                              (hleaves[L].ty1 - hleaves[L].ty0), kOrderChunk));
+    std::vector<GsAlloc> tmp;
+    uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * 128 * (size_t)n_sets, GS_MEM_SCRATCH, &tmp);
+    if (!cnt) return GS_ERR_OOM;
+    gs_status st = launch_fill_u32(ctx, cnt, 0u, 128 * (int64_t)n_sets);
+    if (st == GS_OK) {
         GsTimerScope ts(ctx, "tile_order");
-        hipLaunchKernelGGL(k_tile_order, dim3((unsigned)n_sets), dim3(1024), 0, ctx->stream, (int64_t)0, base, offsets,
-                           order);
+        const dim3 grid((unsigned)nch, (unsigned)n_sets);
+        hipLaunchKernelGGL(k_order_count, grid, dim3(256), 0, ctx->stream, n1, base, offsets, cnt);
+        hipLaunchKernelGGL(k_order_base, dim3((unsigned)ceil_div(n_sets, 256)), dim3(256), 0, ctx->stream, n_sets, cnt);
+        hipLaunchKernelGGL(k_order_place, grid, dim3(256), 0, ctx->stream, n1, base, offsets, cnt, order);
     }
+    gs_free_all(ctx, &tmp);
+    if (st != GS_OK) return st;
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
+}
+
+gs_status launch_tile_order_sets(gs_ctx* ctx, int32_t n_sets, const gs_leaf* hleaves, const uint64_t* base,
+                                 const uint64_t* offsets, uint32_t* order)
+{
+    return launch_tile_order(ctx, n_sets, hleaves, base, 0, offsets, order);
 }
