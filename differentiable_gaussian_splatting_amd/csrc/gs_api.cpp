@@ -493,21 +493,23 @@ gs_status gs_kernel_time(gs_ctx* ctx, const char* name, double* total_ms, int64_
 
 gs_cost_model gs_default_cost_model(void)
 {
-    // Upper bounds of the bytes the library allocates for a planned leaf (L1
-    // fused), each phase bounded by the sum of the terms:
+    // Upper bounds of the bytes the library allocates for a planned leaf,
+    // all of a leaf's buffers counted as held at once:
     //   coarse sort of the C coarse pairs (C <= Cb): keys u32 x 2 and slots
-    //     u32 x 2 (ping-pong) + histograms and their scan (2 x 256 u32 per
-    //     2048 pairs) -> 17 B per pair;
-    //   fine lists: slots u32 per intersection, the grouped slots u32 per
-    //     pair, per work item (at most one per super-tile, so per tile, plus
-    //     one per 512 pairs) 64 u32 positions, its super-tile and offsets
-    //     -> 4 B per intersection, 5 B per pair, 272 B per tile;
-    //   rasterization: the slots, T_final f32 + last u32 + L1 signs u8 per
-    //     pixel, 4 f64 L1 partials per tile -> 4 B, 9 B, 32 B;
-    //   constant: scan block sums, allocation rounding, small buffers.
+    //     u32 x 2 (ping-pong) + the digit histogram of a single 10-bit pass
+    //     (1024 u32 per 2048 pairs) -> 18 B per pair;
+    //   fine lists: per work item (at most one per super-tile, so per tile,
+    //     plus one per 512 pairs) 64 u32 positions, its super-tile and
+    //     offsets -> 0.5 B per pair (19 B per pair in all), 272 B per tile;
+    //     the slots u32 per intersection -> 4 B per intersection;
+    //   rasterization (gs_render_fwd): T_final f32 + last u32 + L1 signs u8
+    //     per pixel, 4 f64 L1 partials per tile -> 9 B, 32 B;
+    //   constant: scan block sums, digit totals, allocation rounding.
+    // The fused forward + L1 + backward of gs_train_view allocates no
+    // per-pixel state, so for it the 9 B per pixel are slack.
     gs_cost_model c;
     c.b_isect = 4;
-    c.b_cell = 17;
+    c.b_cell = 19;
     c.b_pixel = 9;
     c.b_tile = 320;
     c.b_const = 1u << 20;

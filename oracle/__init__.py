@@ -251,7 +251,7 @@ def project_bwd(cam, scene, cand, flags, slot_of, grad2d):
     return grad3d
 
 
-DEFAULT_COST = dict(b_isect=4, b_cell=17, b_pixel=9, b_tile=320, b_const=1 << 20)
+DEFAULT_COST = dict(b_isect=4, b_cell=19, b_pixel=9, b_tile=320, b_const=1 << 20)
 
 
 def cost_struct(cost=None) -> Cost_c:

@@ -25,9 +25,10 @@ def test_the_six_calls_and_binding_names():
 
 def test_default_cost_model_is_an_upper_bound_of_allocations():
     c = dgs.gs_default_cost_model()   # a pure host function: no device needed
-    # per coarse pair: keys u32 x 2 and slots u32 x 2 (radix ping-pong) + 256
-    # u32 histogram bins and their scan per 2048 pairs
-    assert c["b_cell"] >= 16 + 2 * 256 * 4 / 2048
+    # per coarse pair: keys u32 x 2 and slots u32 x 2 (radix ping-pong), the
+    # 1024 u32 digit counts of a 10-bit pass per 2048 pairs, and the fine
+    # level's 64 u32 positions per work item of up to 512 pairs
+    assert c["b_cell"] >= 16 + 1024 * 4 / 2048 + 64 * 4 / 512
     # per intersection: the sorted slot u32
     assert c["b_isect"] >= 4
     # per pixel: T_final f32 + last u32 + packed L1 signs u8
