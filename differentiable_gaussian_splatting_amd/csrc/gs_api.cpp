@@ -404,6 +404,7 @@ void gs_ctx_destroy(gs_ctx* ctx)
         (void)hipStreamDestroy(ctx->side);
     }
     if (ctx->ev_alloc) (void)hipEventDestroy(ctx->ev_alloc);
+    if (ctx->ev_order) (void)hipEventDestroy(ctx->ev_order);
     for (hipEvent_t e : ctx->ev_done)
         if (e) (void)hipEventDestroy(e);
     for (int k = 0; k < 2; ++k) {
@@ -519,6 +520,8 @@ gs_cost_model gs_default_cost_model(void)
 // ---------------------------------------------------------------------------
 // projection
 
+static gs_status ensure_side(gs_ctx* ctx);
+
 gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, gs_proj** out, int64_t* n_cand)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
@@ -535,6 +538,7 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
     p->TW = (cam->width + 15) / 16;
     p->TH = (cam->height + 15) / 16;
     std::vector<GsAlloc> tmp;
+    bool side_used = false;
     const int64_t n = params->n;
     uint32_t* flag = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n, 1), GS_MEM_SCRATCH, &tmp);
     uint32_t* slot = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n + 1), GS_MEM_SCRATCH, &tmp);
@@ -556,7 +560,11 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
     if ((st = launch_project_write(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
     {
         // candidates in (depth, slot) order: stable radix sort of the depth
-        // bits over slots in ascending order
+        // bits over slots in ascending order.  It runs on the second stream
+        // while this one counts the candidates of each tile (which planning
+        // and the binning of an unplanned leaf read); this stream then waits
+        // for the sort, so the projection is complete in its order.  With
+        // every kernel timed, both stay on this stream.
         const int64_t nc = std::max<int64_t>(cnt, 1);
         uint32_t* k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &tmp);
         uint32_t* k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &tmp);
@@ -564,8 +572,28 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
         uint32_t* v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
         bool second = false;
         if (!k0 || !k1 || !v0 || !v1) { st = GS_ERR_OOM; goto fail; }
-        if ((st = launch_depth_pairs(ctx, p, k0, v0)) != GS_OK) goto fail;
-        if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)cnt, 32, &second)) != GS_OK) goto fail;
+        const bool beside = !(ctx->timing && ctx->timing_only.empty()) && ensure_side(ctx) == GS_OK;
+        hipStream_t main = ctx->stream;
+        if (beside) {
+            if (hipEventRecord(ctx->ev_alloc, main) != hipSuccess ||
+                hipStreamWaitEvent(ctx->side, ctx->ev_alloc, 0) != hipSuccess) {
+                st = gs_fail(ctx, GS_ERR_DEVICE, "stream ordering failed");
+                goto fail;
+            }
+            ctx->stream = ctx->side;
+            side_used = true;
+        }
+        st = launch_depth_pairs(ctx, p, k0, v0);
+        if (st == GS_OK) st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)cnt, 32, &second);
+        ctx->stream = main;
+        if (beside && st == GS_OK && hipEventRecord(ctx->ev_order, ctx->side) != hipSuccess)
+            st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+        if (st != GS_OK) goto fail;
+        if ((st = ensure_tile_counts(ctx, p)) != GS_OK) goto fail;
+        if (beside && hipStreamWaitEvent(main, ctx->ev_order, 0) != hipSuccess) {
+            st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
+            goto fail;
+        }
         gs_free_one(ctx, &p->allocs, second ? v0 : v1);
         p->order = second ? v1 : v0;
     }
@@ -574,6 +602,8 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
     *n_cand = (int64_t)cnt;
     return GS_OK;
 fail:
+    // nothing is released while the second stream may still use it
+    if (side_used) (void)hipStreamSynchronize(ctx->side);
     gs_free_all(ctx, &tmp);
     destroy_handle(ctx, p);
     return st;
@@ -824,6 +854,7 @@ static gs_status ensure_side(gs_ctx* ctx)
     if (ctx->side) return GS_OK;
     GS_HIP(ctx, hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_alloc, hipEventDisableTiming));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_order, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[0], hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[1], hipEventDisableTiming));
     for (int k = 0; k < 2; ++k) {

@@ -45,6 +45,7 @@ struct gs_ctx {
     // bins the next leaf while the current one is rendered, and its events
     hipStream_t side = nullptr;
     hipEvent_t ev_alloc = nullptr, ev_done[2] = {nullptr, nullptr};
+    hipEvent_t ev_order = nullptr;   // the depth sort of a projection done (on the second stream)
     // two render streams: consecutive leaves' fused rasters overlap, the
     // next one filling the compute units the current one's last tiles leave
     hipStream_t rstream[2] = {nullptr, nullptr};
