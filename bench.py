@@ -345,7 +345,7 @@ def main():
         "rooflines_all": rooflines,
         "step_hbm": {"algorithmic_bytes": int(step_bytes), "frac_of_8TBps": round(hbm_frac_step, 4),
                      "kernels": counted, "raster_bytes": int(wc["raster_bytes"]),
-                     "raster_bytes_note": "fused raster: 4 B slot per intersection, 36 B attributes per (leaf, "
+                     "raster_bytes_note": "fused raster: 8 B slot + key per super-tile group entry, 36 B attributes per (leaf, "
                                           "candidate), 12 B target per pixel, 36 B 2D gradient per candidate"},
         "attainable_roofline_frac": round(attain_frac, 4),
         "cpu_baseline": cpu,
@@ -360,7 +360,8 @@ def count_work(B, ctx, cam, params, budget):
     (q_b: those examined), intersections, candidates, leaves, tiles, pixels."""
     import torch
     proj, n_cand = B.gs_project(ctx, cam, params)
-    leaves = (B.gs_plan_leaves(ctx, cam, proj, budget) if budget > 0 else
+    # the leaves of the benchmarked L1 view (its own load model)
+    leaves = (B.gs_plan_leaves(ctx, cam, proj, budget, cost=B.gs_train_cost_model()) if budget > 0 else
               [dict(tx0=0, ty0=0, tx1=cam.tiles_x, ty1=cam.tiles_y)])
     stats = torch.zeros(4, dtype=torch.int64, device=ctx.device)
     n_isect = 0
@@ -396,10 +397,11 @@ def count_work(B, ctx, cam, params, budget):
     q = stats.cpu().tolist()
     P = cam.width * cam.height
     # algorithmic bytes of the fused forward + L1 + backward (per-pixel state
-    # stays in registers): every slot of the lists once, the attributes of
-    # each leaf's candidates once (36 B), the target (12 B/px) and the 2D
-    # gradient rows (36 B per candidate)
-    raster_bytes = 4 * n_isect + 36 * group_entries + 12 * P + 36 * n_cand
+    # stays in registers; tiles walk their super-tile groups): every group
+    # entry once (slot + coarse key, 8 B), the attributes of each leaf's
+    # candidates once (36 B), the target (12 B/px) and the 2D gradient rows
+    # (36 B per candidate)
+    raster_bytes = 8 * cells + 36 * group_entries + 12 * P + 36 * n_cand
     return dict(q_f=int(q[0]), q_inc=int(q[1]), q_b=int(q[3]), sum_last=int(q[2]), n_isect=int(n_isect),
                 n_cand=int(n_cand),
                 n_leaves=len(leaves), tiles=int(tiles), pixels=P, raster_bytes=int(raster_bytes),

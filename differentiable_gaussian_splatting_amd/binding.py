@@ -143,6 +143,7 @@ def load(path: str = LIB_PATH):
         "gs_reset_timing": (st, [vp]),
         "gs_set_timing_only": (st, [vp, C.c_char_p]),
         "gs_default_cost_model": (gs_cost_model, []),
+        "gs_train_cost_model": (gs_cost_model, []),
         "gs_project": (st, [vp, P(gs_camera), P(gs_params), P(vp), P(i64)]),
         "gs_plan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, P(i32)]),
         "gs_replan_leaves": (st, [vp, P(gs_camera), vp, u64, vp, i32, vp, i32, vp, i32, P(i32)]),
@@ -503,6 +504,11 @@ def gs_kernel_time(ctx: Context, name: str):
 
 def gs_default_cost_model():
     c = load().gs_default_cost_model()
+    return dict(b_isect=c.b_isect, b_pixel=c.b_pixel, b_tile=c.b_tile, b_const=c.b_const, b_cell=c.b_cell)
+
+
+def gs_train_cost_model():
+    c = load().gs_train_cost_model()
     return dict(b_isect=c.b_isect, b_pixel=c.b_pixel, b_tile=c.b_tile, b_const=c.b_const, b_cell=c.b_cell)
 
 

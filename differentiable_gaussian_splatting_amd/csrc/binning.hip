@@ -237,10 +237,8 @@ __global__ __launch_bounds__(256) void k_leaf_counts(const int32_t* __restrict__
     out[t] = (uint32_t)grid[(int64_t)(lty0 + t / TWL) * TW + ltx0 + t % TWL];
 }
 
-// coarse key: bits [0, kCellBits) the leaf's super-tile, above them the
-// entry's rectangle inside that super-tile (x0, x1 - 1, y0, y1 - 1 in its
-// 8 x 8 local tiles, 3 bits each), carried through the sort for the fine level
-constexpr int kCellBits = 20;
+// coarse keys (kCellBits) carry the entry's rectangle inside its super-tile
+// through the sort, for the fine level and the group-walking raster
 
 // (super-tile, slot) pairs of the listed candidates, in list order and
 // row-major super-tile order within a rectangle.  eoff[k] - ebase is the
@@ -426,7 +424,6 @@ __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* _
 // entries' rectangles (carried in their sort keys, local to the super-tile)
 // gives the covering entries, and the rank of an entry is the number of set
 // bits below its lane.
-constexpr int kSuperShift = 3;
 constexpr int kSeg = 512;
 
 struct FineItem {

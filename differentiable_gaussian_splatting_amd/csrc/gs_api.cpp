@@ -517,6 +517,25 @@ gs_cost_model gs_default_cost_model(void)
     return c;
 }
 
+gs_cost_model gs_train_cost_model(void)
+{
+    // Upper bounds of the bytes gs_train_view allocates for a planned leaf of
+    // an L1 view (the fused raster walks the super-tile groups):
+    //   coarse sort of the C coarse pairs (C <= Cb): keys u32 x 2 and slots
+    //     u32 x 2 (ping-pong) + the digit counts of a single 10-bit pass
+    //     (1024 u32 per 2048 pairs) -> 18 B per pair;
+    //   group offsets: a u64 per super-tile, at most one per tile -> 8 B;
+    //   constant: digit totals, allocation rounding.
+    // No per-tile list, no per-intersection and no per-pixel buffer.
+    gs_cost_model c;
+    c.b_isect = 0;
+    c.b_cell = 19;
+    c.b_pixel = 0;
+    c.b_tile = 8;
+    c.b_const = 1u << 20;
+    return c;
+}
+
 // ---------------------------------------------------------------------------
 // projection
 
@@ -747,21 +766,21 @@ gs_status gs_replan_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
 // binning
 
 // ---------------------------------------------------------------------------
-// Binning of a planned leaf in two stages, so that gs_train_view can bin the
-// next leaf on a second stream while the current one is rendered:
-//   coarse_alloc (main stream): every buffer the first stage needs;
-//   coarse_launch (any stream, allocates nothing): emission, the coarse sort,
-//     the super-tile group offsets, the fine items, counts and positions;
-//   fine_finish (main stream): the slot array, the bins handle, and the
-//     release of the stage's buffers.
-// The same kernels and launch shapes as gs_bin_sort.
+// The coarse stage of a planned leaf, which is all the binning an L1 view's
+// fused raster needs (it walks the super-tile groups itself), split so that
+// gs_train_view can run it on a second stream for the next leaf while the
+// current one is rendered:
+//   coarse_alloc (main stream): every buffer the stage needs;
+//   coarse_launch (any stream, allocates nothing): emission, the coarse sort
+//     and the super-tile group offsets.
+// The buffers stay until the leaf's raster has ended.  The same kernels and
+// launch shapes as the first half of gs_bin_sort.
 struct CoarseBins {
     gs_tile_rect leaf{};
     PlanLeaf pl{};
-    int64_t n_super = 0, items = 0;
+    int64_t n_super = 0;
     uint64_t C = 0, I = 0;
-    uint32_t *k0 = nullptr, *v0 = nullptr, *k1 = nullptr, *v1 = nullptr;
-    uint32_t *item_sc = nullptr, *ioff = nullptr, *pos = nullptr, *scratch = nullptr;
+    uint32_t *k0 = nullptr, *v0 = nullptr, *k1 = nullptr, *v1 = nullptr, *scratch = nullptr;
     uint64_t* soff = nullptr;
     bool second = false;
     std::vector<GsAlloc> allocs;
@@ -770,7 +789,7 @@ struct CoarseBins {
 static bool leaf_pipelinable(const gs_proj* proj, gs_tile_rect leaf)
 {
     const PlanLeaf pl = plan_leaf(proj, leaf);
-    return pl.found && pl.isect >= 0 && super_cells(leaf) < super_cells_max() && (uint64_t)pl.isect < (1ull << 32) &&
+    return pl.found && pl.isect >= 0 && pl.order && super_cells(leaf) < super_cells_max() &&
            (uint64_t)pl.cells < (1ull << 32);
 }
 
@@ -781,7 +800,6 @@ static gs_status coarse_alloc(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect lea
     cb->n_super = super_cells(leaf);
     cb->C = (uint64_t)cb->pl.cells;
     cb->I = (uint64_t)cb->pl.isect;
-    cb->items = fine_items_bound(leaf, cb->C);
     const uint64_t nc = std::max<uint64_t>(cb->C, 1);
     auto get = [&](size_t bytes) { return gs_malloc(ctx, bytes, GS_MEM_RASTER, &cb->allocs); };
     cb->k0 = (uint32_t*)get(sizeof(uint32_t) * nc);
@@ -789,12 +807,8 @@ static gs_status coarse_alloc(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect lea
     cb->k1 = (uint32_t*)get(sizeof(uint32_t) * nc);
     cb->v1 = (uint32_t*)get(sizeof(uint32_t) * nc);
     cb->soff = (uint64_t*)get(sizeof(uint64_t) * (cb->n_super + 1));
-    cb->item_sc = (uint32_t*)get(sizeof(uint32_t) * cb->items);
-    cb->ioff = (uint32_t*)get(sizeof(uint32_t) * (cb->n_super + 1));
-    cb->pos = (uint32_t*)get(sizeof(uint32_t) * 64 * cb->items);
     cb->scratch = (uint32_t*)get(sizeof(uint32_t) * radix_scratch_words((int64_t)cb->C));
-    if (!cb->k0 || !cb->v0 || !cb->k1 || !cb->v1 || !cb->soff || !cb->item_sc || !cb->ioff || !cb->pos ||
-        !cb->scratch) {
+    if (!cb->k0 || !cb->v0 || !cb->k1 || !cb->v1 || !cb->soff || !cb->scratch) {
         gs_free_all(ctx, &cb->allocs);
         return GS_ERR_OOM;
     }
@@ -811,44 +825,12 @@ static gs_status coarse_launch(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb)
                                 &cb->second, cb->soff, cb->n_super, &have_soff, cb->scratch)) != GS_OK)
         return st;
     const uint32_t* gkey = cb->second ? cb->k1 : cb->k0;
-    const uint32_t* group = cb->second ? cb->v1 : cb->v0;
     if (!have_soff &&
         (st = launch_seg_offsets(ctx, gkey, (int64_t)cb->C, cb->n_super, super_key_mask(), cb->soff)) != GS_OK)
         return st;
-    return launch_fine_prepare(ctx, proj, cb->leaf, cb->soff, group, gkey, cb->C, cb->pl.toff, cb->item_sc, cb->ioff,
-                               cb->pos);
-}
-
-static gs_status fine_finish(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb, gs_bins** out)
-{
-    gs_bins* b = new_handle<gs_bins>(ctx, kMagicBins);
-    if (!b) {
-        gs_free_all(ctx, &cb->allocs);
-        return gs_fail(ctx, GS_ERR_OOM, "host allocation failed");
-    }
-    b->proj = proj;
-    b->leaf = cb->leaf;
-    b->TWL = cb->leaf.tx1 - cb->leaf.tx0;
-    b->THL = cb->leaf.ty1 - cb->leaf.ty0;
-    b->n_tiles = (int64_t)b->TWL * b->THL;
-    b->offsets = cb->pl.toff;
-    b->order = cb->pl.order;
-    b->n_isect = (int64_t)cb->I;
-    b->values = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(cb->I, 1), GS_MEM_RASTER, &b->allocs);
-    gs_status st = b->values ? GS_OK : GS_ERR_OOM;
-    if (st == GS_OK)
-        st = launch_fine_write(ctx, proj, cb->leaf, cb->soff, cb->second ? cb->v1 : cb->v0,
-                               cb->second ? cb->k1 : cb->k0, cb->C, cb->item_sc, cb->ioff, cb->pos, cb->I, b->values);
-    gs_free_all(ctx, &cb->allocs);   // stream-ordered after the write
-    if (st != GS_OK) {
-        destroy_handle(ctx, b);
-        return st;
-    }
-    *out = b;
     return GS_OK;
 }
 
-// the side stream and its events, made on first use
 static gs_status ensure_side(gs_ctx* ctx)
 {
     if (ctx->side) return GS_OK;
@@ -1382,11 +1364,16 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     *isect_total = 0;
     const bool host = opts->target_host != 0;
     const PixFrame full = full_frame(cam->width, cam->height);
-    CoarseBins cbs[2];
+    CoarseBins cbs[3];   // leaf li uses cbs[li % 3]
     TargetSlice sl[3];   // leaf li uses sl[li % 3]
-    gs_bins* inflight[2] = {nullptr, nullptr};   // bins of the leaves on the render streams
-    bool pipe = opts->loss_kind == 0 && leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
-    for (const gs_leaf& L : leaves) pipe = pipe && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
+    int inflight[2] = {-1, -1};   // leaves on the render streams (their cbs and slices are held)
+    // L1 views of planned leaves: the fused raster walks each leaf's
+    // super-tile groups (no per-tile lists); overlapped unless every kernel
+    // is timed or there is a single leaf
+    bool groups = opts->loss_kind == 0;
+    for (const gs_leaf& L : leaves)
+        groups = groups && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
+    const bool pipe = groups && leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
     if (opts->loss_kind == 1) {
         // a host target: each next leaf's slice is copied on the second
         // stream while the current leaf is rendered
@@ -1445,17 +1432,17 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     }
     for (size_t li = 0; li < leaves.size(); ++li) {
         const gs_leaf& L = leaves[li];
-        gs_bins* bins = nullptr;
         int64_t ni = 0;
         gs_tile_rect r{L.tx0, L.ty0, L.tx1, L.ty1};
         TargetSlice& ts = sl[li % 3];
-        // the next leaf's first stage (and its target slice) on the side
+        CoarseBins& cb = cbs[li % 3];
+        // the next leaf's coarse stage (and its target slice) on the side
         // stream, behind everything the main stream has queued so far
         auto stage_next = [&]() -> gs_status {
             if (li + 1 >= leaves.size()) return GS_OK;
             const gs_leaf& N = leaves[li + 1];
             const gs_tile_rect nr{N.tx0, N.ty0, N.tx1, N.ty1};
-            CoarseBins& nx = cbs[(li + 1) & 1];
+            CoarseBins& nx = cbs[(li + 1) % 3];
             LeafTag tag(ctx, (int32_t)li + 1);
             gs_status s2 = GS_OK;
             if (host) s2 = slice_target(ctx, cam, target, true, pix_rect(cam, nr), &sl[(li + 1) % 3], ctx->side);
@@ -1463,104 +1450,110 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
                 s2 = coarse_on_side(ctx, proj, &nx, ctx->ev_done[(li + 1) & 1]);
             return s2;
         };
-        if (pipe) {
-            // this leaf's first stage (and its target slice) is done on the
-            // side stream; its slot array is written here.  With overlapped
-            // rasters the next leaf's first stage is queued once this leaf's
-            // raster is launched (its buffers' allocations take host time
-            // the raster need not wait for); rendering one leaf at a time on
-            // the main stream, it is queued before the raster, so that it
-            // runs beside it
-            if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
-                st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
-                goto done;
-            }
+        if (!groups) {
+            // lists per tile (gs_bin_sort), then the fused raster on the main
+            // stream
+            gs_bins* bins = nullptr;
             {
                 LeafTag tag(ctx, (int32_t)li);
-                if ((st = fine_finish(ctx, proj, &cbs[li & 1], &bins)) != GS_OK) goto done;
+                if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
+                if (host && (st = slice_target(ctx, cam, target, true, pix_rect(cam, r), &ts, ctx->stream)) != GS_OK) {
+                    gs_release(ctx, bins);
+                    goto done;
+                }
+                *isect_total += ni;
+                st = launch_raster_fused(ctx, cam, proj, bins, host ? ts.ptr : target, host ? ts.f : full, image,
+                                         l1_view + l1_off, backward ? grad2d : nullptr, backward);
             }
-            ni = bins->n_isect;
-            if (opts->serial_leaves && (st = stage_next()) != GS_OK) {
-                gs_release(ctx, bins);
-                goto done;
-            }
-        } else {
-            LeafTag tag(ctx, (int32_t)li);
-            if ((st = gs_bin_sort(ctx, cam, proj, r, &bins, &ni)) != GS_OK) goto done;
-            if (host && (st = slice_target(ctx, cam, target, true, pix_rect(cam, r), &ts, ctx->stream)) != GS_OK) {
-                gs_release(ctx, bins);
-                goto done;
-            }
+            l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
+            gs_release(ctx, bins);
+            gs_free_all(ctx, &ts.allocs);
+            if (st != GS_OK) goto done;
+            continue;
         }
+        if (!pipe) {
+            // every stage of the leaf on the main stream, in series
+            LeafTag tag(ctx, (int32_t)li);
+            if ((st = coarse_alloc(ctx, proj, r, &cb)) != GS_OK) goto done;
+            if ((st = coarse_launch(ctx, proj, &cb)) != GS_OK) goto done;
+            if (host && (st = slice_target(ctx, cam, target, true, pix_rect(cam, r), &ts, ctx->stream)) != GS_OK)
+                goto done;
+        }
+        ni = (int64_t)cb.I;
         *isect_total += ni;
         const float* tgt = host ? ts.ptr : target;
         const PixFrame tf = host ? ts.f : full;
         if (pipe && !opts->serial_leaves) {
-            // the fused raster of this leaf on render stream li & 1, once the
-            // main stream has written its lists; the previous leaf's raster
-            // may still run on the other render stream, and its bins (and
-            // target slice) are released (on the main stream) only after it
-            // has ended
+            // the fused raster of this leaf on render stream li & 1 once its
+            // coarse stage (side stream) is done; the previous leaf's raster
+            // may still run on the other render stream, and its coarse
+            // buffers (and target slice) are released on the main stream
+            // only after it has ended
             const int k = (int)(li & 1);
             hipStream_t main = ctx->stream;
-            if (hipEventRecord(ctx->ev_ready[k], main) != hipSuccess ||
-                hipStreamWaitEvent(ctx->rstream[k], ctx->ev_ready[k], 0) != hipSuccess) {
-                gs_release(ctx, bins);
+            if (hipStreamWaitEvent(ctx->rstream[k], ctx->ev_done[li & 1], 0) != hipSuccess) {
                 st = gs_fail(ctx, GS_ERR_DEVICE, "render stream ordering failed");
                 goto done;
             }
             ctx->stream = ctx->rstream[k];
             {
                 LeafTag tag(ctx, (int32_t)li);
-                st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off,
-                                         backward ? grad2d : nullptr, backward);
+                st = launch_raster_groups(ctx, cam, proj, r, cb.soff, cb.second ? cb.v1 : cb.v0,
+                                          cb.second ? cb.k1 : cb.k0, cb.pl.order, tgt, tf, image, l1_view + l1_off,
+                                          backward ? grad2d : nullptr, backward);
             }
             ctx->stream = main;
             if (st == GS_OK && hipEventRecord(ctx->ev_rendered[k], ctx->rstream[k]) != hipSuccess)
                 st = gs_fail(ctx, GS_ERR_DEVICE, "render event failed");
             l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
-            inflight[k] = bins;
+            inflight[k] = (int)li;
             if (st != GS_OK) goto done;
             if ((st = stage_next()) != GS_OK) goto done;
-            if (li >= 1 && inflight[k ^ 1]) {
+            if (li >= 1 && inflight[k ^ 1] >= 0) {
                 if (hipStreamWaitEvent(main, ctx->ev_rendered[k ^ 1], 0) != hipSuccess) {
                     st = gs_fail(ctx, GS_ERR_DEVICE, "render stream wait failed");
                     goto done;
                 }
-                gs_release(ctx, inflight[k ^ 1]);
-                inflight[k ^ 1] = nullptr;
-                gs_free_all(ctx, &sl[(li - 1) % 3].allocs);
+                gs_free_all(ctx, &cbs[inflight[k ^ 1] % 3].allocs);
+                gs_free_all(ctx, &sl[inflight[k ^ 1] % 3].allocs);
+                inflight[k ^ 1] = -1;
             }
             continue;
         }
-        // L1: each pixel's loss gradient is its own residual sign, so the
-        // forward, the loss and the backward of a tile run in one wavefront
+        if (pipe) {
+            // one leaf at a time on the main stream: this leaf's coarse
+            // stage is done on the side stream, and the next leaf's is queued
+            // before this raster, so that it runs beside it
+            if (hipStreamWaitEvent(ctx->stream, ctx->ev_done[li & 1], 0) != hipSuccess) {
+                st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
+                goto done;
+            }
+            if ((st = stage_next()) != GS_OK) goto done;
+        }
         {
             LeafTag tag(ctx, (int32_t)li);
-            st = launch_raster_fused(ctx, cam, proj, bins, tgt, tf, image, l1_view + l1_off,
-                                     backward ? grad2d : nullptr, backward);
+            st = launch_raster_groups(ctx, cam, proj, r, cb.soff, cb.second ? cb.v1 : cb.v0, cb.second ? cb.k1 : cb.k0,
+                                      cb.pl.order, tgt, tf, image, l1_view + l1_off, backward ? grad2d : nullptr,
+                                      backward);
         }
         l1_off += 4 * (int64_t)(L.tx1 - L.tx0) * (L.ty1 - L.ty0);
-        gs_release(ctx, bins);
+        gs_free_all(ctx, &cb.allocs);   // stream-ordered after the raster
         gs_free_all(ctx, &ts.allocs);
         if (st != GS_OK) goto done;
     }
 done:
     if (pipe) {
-        // the main stream follows the render streams before the last bins are
-        // released; nothing may be freed while the side stream could still
-        // use it
+        // the main stream follows the render streams before the last leaves'
+        // buffers are released; nothing may be freed while the side stream
+        // could still use it
         for (int k = 0; k < 2; ++k)
-            if (inflight[k]) {
-                if (hipStreamWaitEvent(ctx->stream, ctx->ev_rendered[k], 0) != hipSuccess) {
-                    (void)hipStreamSynchronize(ctx->rstream[k]);
-                    if (st == GS_OK) st = gs_fail(ctx, GS_ERR_DEVICE, "render stream wait failed");
-                }
-                gs_release(ctx, inflight[k]);
+            if (inflight[k] >= 0 && hipStreamWaitEvent(ctx->stream, ctx->ev_rendered[k], 0) != hipSuccess) {
+                (void)hipStreamSynchronize(ctx->rstream[k]);
+                if (st == GS_OK) st = gs_fail(ctx, GS_ERR_DEVICE, "render stream wait failed");
             }
         (void)hipStreamSynchronize(ctx->side);
-        for (CoarseBins& cb : cbs) gs_free_all(ctx, &cb.allocs);
     }
+    for (CoarseBins& c : cbs) gs_free_all(ctx, &c.allocs);
     for (TargetSlice& t : sl) gs_free_all(ctx, &t.allocs);
     return st;
 }
@@ -1615,11 +1608,12 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         const int32_t nr = opts->n_leaves_in > 0 ? opts->n_leaves_in : 0;
         const uint64_t budget = opts->budget_bytes > 0 ? opts->budget_bytes : ~0ull;
         const bool partial = nr > 0 && opts->leaves_in_partial != 0;
-        // Without a caller's model, the default one plus what the view holds
-        // per pixel of a leaf beyond the L1 raster: for SSIM 18 floats
-        // (image, gradient, target slice, 9 partial maps), for an L1 view
-        // with a host target its 3-float slice.
-        gs_cost_model cm = opts->cost ? *opts->cost : gs_default_cost_model();
+        // Without a caller's model: for SSIM the default one plus 18 floats
+        // per pixel of a leaf (image, gradient, target slice, 9 partial
+        // maps); for L1 the group-walking bound plus, with a host target,
+        // its 3-float slice.
+        gs_cost_model cm = opts->cost ? *opts->cost
+                                      : (opts->loss_kind == 1 ? gs_default_cost_model() : gs_train_cost_model());
         if (!opts->cost) cm.b_pixel += opts->loss_kind == 1 ? 18 * 4 : (opts->target_host ? 3 * 4 : 0);
         int32_t nl = 0;
         leaves.resize(4096);

@@ -166,6 +166,11 @@ gs_status launch_exp(gs_ctx* ctx, const float* x, float* y, int64_t n, bool fall
 gs_status launch_rect_diff(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                            int64_t n_list, int32_t* diff);
 // super-tiles (8 x 8 tiles, aligned to the image) meeting a leaf
+constexpr int kSuperShift = 3;
+// coarse key: bits [0, kCellBits) the leaf's super-tile, above them the
+// entry's rectangle inside that super-tile (x0, x1 - 1, y0, y1 - 1 in its
+// 8 x 8 local tiles, 3 bits each)
+constexpr int kCellBits = 20;
 int super_cols(gs_tile_rect leaf);
 int super_rows(gs_tile_rect leaf);
 int64_t super_cells(gs_tile_rect leaf);
@@ -230,6 +235,13 @@ gs_status launch_raster_fwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
 gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
                               const float* target, PixFrame tf, float* image_out, double* l1_part, float* grad2d,
                               bool backward);
+// The fused raster walking super-tile groups: soff = group offsets of the
+// leaf's super-tiles [super_cells(leaf) + 1], group / gkey = the sorted slots
+// and coarse keys, order = the plan's tile order (required).
+gs_status launch_raster_groups(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs_tile_rect leaf,
+                               const uint64_t* soff, const uint32_t* group, const uint32_t* gkey,
+                               const uint32_t* order, const float* target, PixFrame tf, float* image_out,
+                               double* l1_part, float* grad2d, bool backward);
 // tiles of each of n_sets offset arrays (set L at base[L], base[L + 1] - base[L]
 // - 1 tiles; hleaves: the sets' leaves on the host, for the grid) in the
 // fused raster's launch order, written at the same bases

@@ -120,6 +120,16 @@ __device__ __forceinline__ bool cull_box(float4 a, float4 b, float bx0, float by
     return cull_test(cull_prep(a, b), bx0, by0);
 }
 
+// Whether a super-tile group entry (coarse key: its rectangle inside the
+// super-tile above bit kCellBits) covers the tile at local position cr =
+// column | row << 3 of the super-tile.  A tile's list is the subsequence of
+// its super-tile's group that covers it, in group order.
+__device__ __forceinline__ bool covers(uint32_t key, uint32_t cr)
+{
+    const uint32_t lr = key >> kCellBits, c = cr & 7u, r = cr >> 3;
+    return (lr & 7u) <= c && c <= ((lr >> 3) & 7u) && ((lr >> 6) & 7u) <= r && r <= ((lr >> 9) & 7u);
+}
+
 // One kept entry of the staged batch (geometry a, b, blue cb, list position
 // pos) at one pixel of the forward walk.  Every lane evaluates the entry; the per-lane decisions (skip, stop,
 // include) become lane masks, and the updates of a lane that includes the
@@ -343,13 +353,15 @@ __device__ __forceinline__ float wave_reduce9(const float* p, int lane, int* vid
 // The backward walk of one tile by one wavefront (see k_raster_bwd): T, GS,
 // the dL/dout factors gr0..gr2 and the walk ends lst of the lane's pixel in
 // each quadrant, mq the largest end in each quadrant.
+template <bool GROUPS>
 __device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, const float (&pxc)[2],
                                          const float (&pyc)[2], const float (&bx)[2], const float (&by)[2],
                                          float (&T)[4], float (&GS)[4], const float (&gr0)[4],
                                          const float (&gr1)[4], const float (&gr2)[4], const uint32_t (&lst)[4],
                                          const uint32_t (&mq)[4], const uint32_t* __restrict__ values,
                                          const float4* __restrict__ g0, const float4* __restrict__ g1,
-                                         const float4* __restrict__ g2, float* __restrict__ grad2d)
+                                         const float4* __restrict__ g2, float* __restrict__ grad2d,
+                                         const uint32_t* __restrict__ keys = nullptr, uint32_t cr = 0)
 {
     const uint32_t maxl = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
 
@@ -357,7 +369,7 @@ __device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, co
         const int64_t lo = hi > 64 ? hi - 64 : 0;
         const int cnt = (int)(hi - lo);
         uint32_t qb = 0;
-        if (lane < cnt) {
+        if (lane < cnt && (!GROUPS || covers(keys[start + lo + lane], cr))) {
             const uint32_t s = values[start + lo + lane];
             const float4 a = g0[s], b = g1[s];
             S.a[lane] = a;
@@ -525,7 +537,7 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
         GS[k] = T[k] * (gr0[k] * bg0 + gr1[k] * bg1 + gr2[k] * bg2);
         mq[k] = __builtin_amdgcn_readfirstlane(gsd::wave_max_u32(lst[k]));
     }
-    bwd_walk(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d);
+    bwd_walk<false>(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d);
 }
 
 
@@ -543,8 +555,14 @@ __global__ __launch_bounds__(256) void k_raster_bwd(LeafGeom g, int64_t n_tiles,
 // sgn(out - target) / (3WH) follow, then the backward walk (bwd_walk).
 // One wavefront per workgroup: a tile's wavefront frees its slot the moment
 // it ends, instead of waiting for the other tiles of a shared workgroup.
+// GROUPS = false: the tile's list is [offsets[lt], offsets[lt + 1]) of
+// `values`.  GROUPS = true: the tile walks its super-tile's group
+// [offsets[sc], offsets[sc + 1]) of `values` (slots) and `keys` (coarse keys),
+// taking the entries that cover it (`covers`) -- the same entries in the same
+// order, so every value is the same, and no per-tile list is written.  List
+// positions (walk ends) then count group entries.
 constexpr int kFusedWaves = 1;
-template <bool BWD>   // false: forward and L1 only (a view whose backward is skipped)
+template <bool BWD, bool GROUPS>   // BWD false: forward and L1 only (a view whose backward is skipped)
 __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, int64_t n_tiles,
                                                       const uint64_t* __restrict__ offsets,
                                                       const uint32_t* __restrict__ values,
@@ -552,7 +570,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
                                                       const float4* __restrict__ g2, float bg0, float bg1, float bg2,
                                                       const float* __restrict__ target, PixFrame tf, float inv_norm,
                                                       float* __restrict__ image, double* __restrict__ l1_part,
-                                                      float* __restrict__ grad2d, const uint32_t* __restrict__ order)
+                                                      float* __restrict__ grad2d, const uint32_t* __restrict__ order,
+                                                      const uint32_t* __restrict__ keys, int SW)
 {
     __shared__ Staged st[kFusedWaves];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -570,7 +589,12 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
         bx[h] = (float)(tx * 16 + h * 8) + 0.5f;
         by[h] = (float)(ty * 16 + h * 8) + 0.5f;
     }
-    const uint64_t start = offsets[lt], end = offsets[lt + 1];
+    // the tile's own list, or its super-tile's group and its place in it
+    const int64_t li = GROUPS ? (int64_t)((ty >> kSuperShift) - (g.lty0 >> kSuperShift)) * SW +
+                                    ((tx >> kSuperShift) - (g.ltx0 >> kSuperShift))
+                              : lt;
+    const uint32_t cr = (uint32_t)(tx & 7) | ((uint32_t)(ty & 7) << 3);
+    const uint64_t start = offsets[li], end = offsets[li + 1];
 
     // ---- forward over the four quadrants
     // a pixel is still compositing while its walk end is the list length:
@@ -599,7 +623,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
         uint32_t qb = 0;
         float4 a, b;
         float c = 0.0f;
-        if (e < end) {
+        if (e < end && (!GROUPS || covers(keys[e], cr))) {
             const uint32_t s = values[e];
             a = g0[s];
             b = g1[s];
@@ -669,7 +693,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
     if (!BWD) return;
 
     // ---- backward
-    bwd_walk(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d);
+    bwd_walk<GROUPS>(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d,
+                     keys, cr);
 }
 
 
@@ -832,32 +857,38 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
     return GS_OK;
 }
 
-gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
-                              const float* target, PixFrame tf, float* image_out, double* l1_part, float* grad2d,
-                              bool backward)
+// The fused raster of one leaf over its tiles in `order` (null: longest list
+// first, computed here from the tile offsets; lists only).  groups: the tiles
+// walk their super-tiles' groups (offsets = group offsets, values = slots,
+// keys = coarse keys); else their own lists.
+static gs_status fused_launch(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs_tile_rect leaf,
+                              const uint64_t* offsets, const uint32_t* values, const uint32_t* keys, bool groups,
+                              const uint32_t* order, const float* target, PixFrame tf, float* image_out,
+                              double* l1_part, float* grad2d, bool backward)
 {
     LeafGeom g;
     g.W = cam->width;
     g.H = cam->height;
-    g.ltx0 = bins->leaf.tx0;
-    g.lty0 = bins->leaf.ty0;
-    g.TWL = bins->TWL;
-    g.px0 = bins->leaf.tx0 * 16;
-    g.py0 = bins->leaf.ty0 * 16;
-    g.WL = std::min(bins->leaf.tx1 * 16, cam->width) - g.px0;
-    g.PL = (int64_t)g.WL * (std::min(bins->leaf.ty1 * 16, cam->height) - g.py0);
+    g.ltx0 = leaf.tx0;
+    g.lty0 = leaf.ty0;
+    g.TWL = leaf.tx1 - leaf.tx0;
+    g.px0 = leaf.tx0 * 16;
+    g.py0 = leaf.ty0 * 16;
+    g.WL = std::min(leaf.tx1 * 16, cam->width) - g.px0;
+    g.PL = (int64_t)g.WL * (std::min(leaf.ty1 * 16, cam->height) - g.py0);
+    const int SW = super_cols(leaf);
     const float inv_norm = (float)(1.0 / (3.0 * (double)cam->width * (double)cam->height));
-    if (bins->n_tiles > 0) {
-        const int64_t nt = bins->n_tiles;
+    const int64_t nt = (int64_t)g.TWL * (leaf.ty1 - leaf.ty0);
+    if (nt > 0) {
         std::vector<GsAlloc> tmp;
-        const uint32_t* order = bins->order;   // from the plan
         if (!order) {
+            if (groups) return gs_fail(ctx, GS_ERR_INVALID_ARG, "group-walking raster without a tile order");
             uint32_t* o = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nt, GS_MEM_RASTER, &tmp);
             if (!o) return GS_ERR_OOM;
             gs_leaf one{};
-            one.tx1 = bins->TWL;
-            one.ty1 = bins->THL;
-            const gs_status so = launch_tile_order(ctx, 1, &one, nullptr, nt, bins->offsets, o);
+            one.tx1 = g.TWL;
+            one.ty1 = leaf.ty1 - leaf.ty0;
+            const gs_status so = launch_tile_order(ctx, 1, &one, nullptr, nt, offsets, o);
             if (so != GS_OK) {
                 gs_free_all(ctx, &tmp);
                 return so;
@@ -867,19 +898,40 @@ gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* 
         {
             GsTimerScope ts(ctx, backward ? "raster_fused" : "raster_fused_fwd");
             const dim3 grid((unsigned)ceil_div(nt, kFusedWaves)), block(64 * kFusedWaves);
-            if (backward)
-                hipLaunchKernelGGL(k_raster_fused<true>, grid, block, 0, ctx->stream, g, nt, bins->offsets, bins->values,
-                                   proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2], target, tf,
-                                   inv_norm, image_out, l1_part, grad2d, order);
-            else
-                hipLaunchKernelGGL(k_raster_fused<false>, grid, block, 0, ctx->stream, g, nt, bins->offsets,
-                                   bins->values, proj->g0, proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2],
-                                   target, tf, inv_norm, image_out, l1_part, grad2d, order);
+#define GS_FUSED(B, G)                                                                                            \
+    hipLaunchKernelGGL((k_raster_fused<B, G>), grid, block, 0, ctx->stream, g, nt, offsets, values, proj->g0,     \
+                       proj->g1, proj->g2, cam->bg[0], cam->bg[1], cam->bg[2], target, tf, inv_norm, image_out,   \
+                       l1_part, grad2d, order, keys, SW)
+            if (backward) {
+                if (groups) GS_FUSED(true, true);
+                else GS_FUSED(true, false);
+            } else {
+                if (groups) GS_FUSED(false, true);
+                else GS_FUSED(false, false);
+            }
+#undef GS_FUSED
         }
         gs_free_all(ctx, &tmp);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
+}
+
+gs_status launch_raster_fused(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const gs_bins* bins,
+                              const float* target, PixFrame tf, float* image_out, double* l1_part, float* grad2d,
+                              bool backward)
+{
+    return fused_launch(ctx, cam, proj, bins->leaf, bins->offsets, bins->values, nullptr, false, bins->order, target,
+                        tf, image_out, l1_part, grad2d, backward);
+}
+
+gs_status launch_raster_groups(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs_tile_rect leaf,
+                               const uint64_t* soff, const uint32_t* group, const uint32_t* gkey,
+                               const uint32_t* order, const float* target, PixFrame tf, float* image_out,
+                               double* l1_part, float* grad2d, bool backward)
+{
+    return fused_launch(ctx, cam, proj, leaf, soff, group, gkey, true, order, target, tf, image_out, l1_part, grad2d,
+                        backward);
 }
 
 gs_status launch_tile_order(gs_ctx* ctx, int32_t n_sets, const gs_leaf* hleaves, const uint64_t* base, int64_t n1,

@@ -125,7 +125,11 @@ typedef struct {
  * of the coarse pairs the leaf's binning sorts), P = its pixels inside the
  * image, T = its tiles.  gs_default_cost_model() returns the library's own
  * allocation sizes, which make est an upper bound of the bytes that
- * gs_bin_sort + gs_render_fwd allocate for a planned leaf (L1 loss inline). */
+ * gs_bin_sort + gs_render_fwd allocate for a planned leaf (L1 loss inline).
+ * gs_train_cost_model() bounds what gs_train_view allocates for a planned
+ * leaf of an L1 view, whose fused raster walks the leaf's super-tile groups
+ * and holds no per-tile lists or per-pixel state: b_isect = b_pixel = 0,
+ * b_cell for the coarse sort, b_tile for the group offsets. */
 typedef struct { uint64_t b_isect, b_pixel, b_tile, b_const, b_cell; } gs_cost_model;
 
 enum { GS_MEM_PROJ = 0, GS_MEM_RASTER = 1, GS_MEM_GRAD = 2, GS_MEM_LOSS = 3, GS_MEM_SCRATCH = 4,
@@ -158,6 +162,7 @@ gs_status gs_reset_timing(gs_ctx* ctx);
  * that a measured run carries events around one kernel only. */
 gs_status gs_set_timing_only(gs_ctx* ctx, const char* name);
 gs_cost_model gs_default_cost_model(void);
+gs_cost_model gs_train_cost_model(void);
 
 /* ---- the six calls of one view ----------------------------------------- */
 
@@ -459,20 +464,25 @@ typedef struct {
 
 /* One training view: gs_project -> gs_plan_leaves -> for each leaf
  * (gs_bin_sort, gs_render_fwd, loss, gs_render_bwd, release) ->
- * gs_project_bwd -> optional gs_adam_step; the 2D gradients of all leaves are
+ * gs_project_bwd -> optional gs_adam_step; for an L1 view of planned leaves
+ * the binning stops at the coarse level (emission, the super-tile sort and
+ * its group offsets) and one fused kernel per leaf renders, takes the L1
+ * loss and runs the raster backward, each tile walking its super-tile's
+ * group and taking the entries that cover it (the same entries in the same
+ * order as its gs_bin_sort list, so the same values).  The 2D gradients of all leaves are
  * summed in one buffer before the single projection backward (BoundedGS
  * page "01", Fig. 3, Fig. 5 conclusion).  With Adam and no grad3d_out the
  * projection backward and the update run as one fused pass over the
  * Gaussians (adam_chunk 0), or chunk by chunk of candidate slots; both give
  * the result of gs_project_bwd followed by gs_adam_step.  With more than
- * one planned leaf, the binning of each next leaf up to its slot array runs
- * on a second stream of the library (default priority, created on first use)
+ * one planned leaf, the binning of each next leaf (L1: its coarse level)
+ * runs on a second stream of the library (default priority, created on first use)
  * while the current leaf is rendered, ordered by events; not while every
  * kernel is timed (gs_set_timing on, no gs_set_timing_only); and, for L1
  * views unless serial_leaves, each leaf's fused raster runs on one of two
  * render streams so that it can start while the previous leaf's last tiles
- * are still being rendered (the previous leaf's lists are released after
- * its raster ends).  With a gate
+ * are still being rendered (the previous leaf's coarse buffers are released
+ * after its raster ends).  With a gate
  * (SkipGS notes, "key design"): first the forward and the loss of every
  * leaf, then gs_gate_step; when it asks for the backward the leaves are
  * binned and rendered again with their backward (the leaves' buffers are
@@ -489,9 +499,11 @@ typedef struct {
  * holds 18 floats per pixel of the grown rectangle (image, gradient, target
  * slice, 9 partial maps) on top of the binning.  The leaves are not binned
  * ahead for SSIM; with a host target each next leaf's slice is copied on the
- * second stream while the current leaf is rendered.  When opts->cost is NULL the plan uses the default model
- * with these 18 floats (SSIM) or a host target's 3-float slice (L1) added to
- * b_pixel; with overlapped L1 leaves up to three slices are held at once.  target: device [3][H][W], or host memory with
+ * second stream while the current leaf is rendered.  When opts->cost is
+ * NULL the plan uses gs_default_cost_model() with these 18 floats added to
+ * b_pixel (SSIM), or gs_train_cost_model() with a host target's 3-float
+ * slice as b_pixel (L1; with overlapped leaves up to three slices are held
+ * at once).  target: device [3][H][W], or host memory with
  * target_host (BoundedGS page, "02 / method": bounded image feeding).
  * Synchronises. */
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,

@@ -252,6 +252,10 @@ def project_bwd(cam, scene, cand, flags, slot_of, grad2d):
 
 
 DEFAULT_COST = dict(b_isect=4, b_cell=19, b_pixel=9, b_tile=320, b_const=1 << 20)
+# the load model of a leaf whose L1 raster walks its super-tile groups (no
+# per-tile lists, no per-pixel state): coarse sort per pair, group offsets
+# per tile
+TRAIN_COST = dict(b_isect=0, b_cell=19, b_pixel=0, b_tile=8, b_const=1 << 20)
 
 
 def cost_struct(cost=None) -> Cost_c:
@@ -330,6 +334,8 @@ def train_view(cam, scene, target, loss="l1", budget=None, leaves=None, mode="pa
     cdec = c32 if mode == "parity" else c64
     if leaves is None:
         if budget is not None:
+            if cost is None and loss == "l1":
+                cost = TRAIN_COST
             leaves = plan_leaves(cam, cdec["rect"], budget, cost)
         else:
             leaves = [dict(tx0=0, ty0=0, tx1=TW, ty1=(H + 15) // 16, est_bytes=0, over_budget=False)]

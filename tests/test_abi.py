@@ -38,6 +38,19 @@ def test_default_cost_model_is_an_upper_bound_of_allocations():
     assert c["b_tile"] >= 32 + 64 * 4 + 4 + 12
 
 
+def test_train_cost_model_is_an_upper_bound_of_the_group_walking_view():
+    import oracle
+    c = dgs.gs_train_cost_model()
+    # an L1 view's leaf holds its coarse sort only (keys and slots ping-pong
+    # plus the 10-bit digit counts per 2048 pairs) and its group offsets (a
+    # u64 per super-tile, at most one per tile); no per-tile list, no
+    # per-pixel state
+    assert c["b_cell"] >= 16 + 1024 * 4 / 2048
+    assert c["b_tile"] >= 8
+    assert c["b_isect"] == 0 and c["b_pixel"] == 0
+    assert c == oracle.TRAIN_COST
+
+
 def test_grid_layout_matches_the_oracle_and_tiles_the_grid():
     """gs_grid_leaves is host-only: its blocks are the oracle's fixed-block
     layout, they tile the grid exactly, and invalid shapes are refused."""
