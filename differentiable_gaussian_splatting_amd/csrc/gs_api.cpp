@@ -636,7 +636,8 @@ fail:
 // within the budget and split by the halving rule otherwise.
 static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, uint64_t budget_bytes,
                            const gs_cost_model* cost, int32_t strict, const gs_leaf* roots, int32_t n_roots,
-                           gs_leaf* leaves, int32_t max_leaves, int32_t* n_leaves, bool partial = false)
+                           gs_leaf* leaves, int32_t max_leaves, int32_t* n_leaves, bool partial = false,
+                           uint64_t* totals = nullptr)
 {
     if (!ctx) return GS_ERR_INVALID_ARG;
     gs_status st;
@@ -694,7 +695,10 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
             return gs_fail(ctx, GS_ERR_DEVICE, "cached leaf copy failed: %s", hipGetErrorString(e));
         }
     }
-    st = launch_plan(ctx, proj, sat, budget_bytes, &cm, rdev, n_roots, ldev, cap, small, small + 1);
+    // header: leaf count, over-budget flag, then (u64 at byte 8) the whole
+    // grid's intersections and (candidate, super-cell) pairs
+    st = launch_plan(ctx, proj, sat, budget_bytes, &cm, rdev, n_roots, ldev, cap, small, small + 1,
+                     (uint64_t*)(blk + 8));
     if (st == GS_OK) {
         hipError_t e = hipMemcpyAsync(hblk.data(), blk, hblk.size(), hipMemcpyDeviceToHost, ctx->stream);
         if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
@@ -702,6 +706,7 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
     }
     if (st == GS_OK) {
         std::memcpy(hv, hblk.data(), sizeof(hv));
+        if (totals) std::memcpy(totals, hblk.data() + 8, 2 * sizeof(uint64_t));
         const int32_t nh = std::min(hv[0], cap);
         if (nh > 0) {
             hleaves.resize(nh);
@@ -1357,7 +1362,8 @@ done:
 // binning), each slice freed once its leaf's raster has ended.
 static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const float* target,
                                const gs_view_opts* opts, const std::vector<gs_leaf>& leaves, bool backward,
-                               float* grad2d, double* l1_view, float* image, double* ssim_acc, int64_t* isect_total)
+                               float* grad2d, double* l1_view, float* image, double* ssim_acc, int64_t* isect_total,
+                               bool walk)
 {
     gs_status st = GS_OK;
     int64_t l1_off = 0;
@@ -1367,10 +1373,11 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     CoarseBins cbs[3];   // leaf li uses cbs[li % 3]
     TargetSlice sl[3];   // leaf li uses sl[li % 3]
     int inflight[2] = {-1, -1};   // leaves on the render streams (their cbs and slices are held)
-    // L1 views of planned leaves: the fused raster walks each leaf's
-    // super-tile groups (no per-tile lists); overlapped unless every kernel
-    // is timed or there is a single leaf
-    bool groups = opts->loss_kind == 0;
+    // L1 views of planned leaves whose coverage calls for it (walk_rule):
+    // the fused raster walks each leaf's super-tile groups (no per-tile
+    // lists); overlapped unless every kernel is timed or there is a single
+    // leaf
+    bool groups = opts->loss_kind == 0 && walk;
     for (const gs_leaf& L : leaves)
         groups = groups && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
     const bool pipe = groups && leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
@@ -1582,6 +1589,14 @@ static gs_status view_loss(gs_ctx* ctx, const gs_view_opts* opts, double* l1_vie
 
 extern "C" {
 
+// Which raster an L1 view of planned leaves takes.  Walking the super-tile
+// groups visits, per tile, the entries of its super-tile's group; a tile's
+// own list holds the fraction of them that covers it, I / (64 Cb) on average
+// over the view (I intersections, Cb (candidate, super-cell) pairs).  When
+// that coverage is at least 0.18 the walk pays for the per-tile lists it
+// saves; below it the lists are built (gs_bin_sort) and walked.
+static bool walk_rule(uint64_t I, uint64_t Cb) { return 100 * I >= 1152 * Cb; }
+
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result)
 {
@@ -1601,6 +1616,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
 
     std::vector<gs_leaf> leaves;
     const int32_t TW = proj->TW, TH = proj->TH;
+    bool walk = false;   // L1: the leaves' rasters walk their super-tile groups
     if (opts->budget_bytes > 0 || opts->n_leaves_in > 0) {
         // a fresh plan, the re-check of the caller's cached layout, or (budget
         // 0) the caller's layout as it is
@@ -1610,19 +1626,39 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         const bool partial = nr > 0 && opts->leaves_in_partial != 0;
         // Without a caller's model: for SSIM the default one plus 18 floats
         // per pixel of a leaf (image, gradient, target slice, 9 partial
-        // maps); for L1 the group-walking bound plus, with a host target,
-        // its 3-float slice.
-        gs_cost_model cm = opts->cost ? *opts->cost
-                                      : (opts->loss_kind == 1 ? gs_default_cost_model() : gs_train_cost_model());
-        if (!opts->cost) cm.b_pixel += opts->loss_kind == 1 ? 18 * 4 : (opts->target_host ? 3 * 4 : 0);
+        // maps); for L1 the model of the raster the view takes (walk_rule):
+        // the group-walking bound, or the per-tile-list one, plus with a
+        // host target its 3-float slice.  The planner reports the view's
+        // totals the rule reads; an L1 view starts from the previous view's
+        // choice and is planned again only when the rule picks the other.
+        const bool l1_auto = !opts->cost && opts->loss_kind == 0;
+        auto model = [&](bool w) {
+            gs_cost_model c = opts->cost ? *opts->cost
+                                         : (opts->loss_kind == 1 || !w ? gs_default_cost_model() : gs_train_cost_model());
+            if (!opts->cost) c.b_pixel += opts->loss_kind == 1 ? 18 * 4 : (opts->target_host ? 3 * 4 : 0);
+            return c;
+        };
+        uint64_t tot[2] = {0, 0};
         int32_t nl = 0;
-        leaves.resize(4096);
-        st = plan_impl(ctx, cam, proj, budget, &cm, opts->strict_budget, roots, nr, leaves.data(),
-                       (int32_t)leaves.size(), &nl, partial);
-        if (st == GS_OK && nl > (int32_t)leaves.size()) {
-            leaves.resize(nl);
-            st = plan_impl(ctx, cam, proj, budget, &cm, opts->strict_budget, roots, nr, leaves.data(), nl, &nl,
-                           partial);
+        auto plan = [&](bool w) {
+            const gs_cost_model cm = model(w);
+            leaves.resize(4096);
+            gs_status s2 = plan_impl(ctx, cam, proj, budget, &cm, opts->strict_budget, roots, nr, leaves.data(),
+                                     (int32_t)leaves.size(), &nl, partial, tot);
+            if (s2 == GS_OK && nl > (int32_t)leaves.size()) {
+                leaves.resize(nl);
+                s2 = plan_impl(ctx, cam, proj, budget, &cm, opts->strict_budget, roots, nr, leaves.data(), nl, &nl,
+                               partial, tot);
+            }
+            return s2;
+        };
+        walk = ctx->walk_guess;
+        st = plan(walk);
+        if (st == GS_OK && opts->loss_kind == 0) {
+            const bool want = walk_rule(tot[0], tot[1]);
+            if (l1_auto && want != walk) st = plan(want);
+            walk = want;
+            if (l1_auto) ctx->walk_guess = want;
         }
         if (st != GS_OK) { gs_release(ctx, proj); return st; }
         leaves.resize(nl);
@@ -1668,7 +1704,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         // leaves' buffers are not kept between the passes, so a view that
         // runs its backward renders twice
         if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, false, grad2d, l1_view, image, loss_dev + 1,
-                                &isect_total)) != GS_OK)
+                                &isect_total, walk)) != GS_OK)
             goto done;
         if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss)) != GS_OK) goto done;
         gs_gate_decision d{};
@@ -1682,7 +1718,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         if (!d.backward) goto finish;
     }
     if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, true, grad2d, l1_view, image, loss_dev + 1,
-                            &isect_total)) != GS_OK)
+                            &isect_total, walk)) != GS_OK)
         goto done;
     if (opts->grad3d_out || opts->adam_step <= 0) {
         float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * nc, GS_MEM_GRAD, &view);

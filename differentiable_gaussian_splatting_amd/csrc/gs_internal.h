@@ -50,6 +50,7 @@ struct gs_ctx {
     // next one filling the compute units the current one's last tiles leave
     hipStream_t rstream[2] = {nullptr, nullptr};
     hipEvent_t ev_ready[2] = {nullptr, nullptr}, ev_rendered[2] = {nullptr, nullptr};
+    bool walk_guess = true;        // the last L1 view's raster choice (gs_train_view)
     int num_cu = 256;
     size_t max_lds = 65536;
 };
@@ -259,7 +260,7 @@ gs_status launch_tile_counts(gs_ctx* ctx, const gs_proj* proj, int32_t* grid);
 // leaf plan from proj->tile_cnt
 gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t budget, const gs_cost_model* cost,
                       const gs_leaf* roots_dev, int32_t n_roots, gs_leaf* leaves_dev, int32_t max_leaves,
-                      int32_t* count_dev, int32_t* over_dev);
+                      int32_t* count_dev, int32_t* over_dev, uint64_t* totals_dev = nullptr);
 
 // leaf -> candidate groups (planner.hip)
 // hleaves: the same leaves on the host (their sizes shape the launch grids)

@@ -133,10 +133,16 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a,
                                                        const gs_leaf* __restrict__ roots, int32_t n_roots,
                                                        gs_leaf* __restrict__ leaves, int32_t max_leaves,
                                                        int32_t* __restrict__ count_out,
-                                                       int32_t* __restrict__ over_out)
+                                                       int32_t* __restrict__ over_out,
+                                                       uint64_t* __restrict__ totals_out)
 {
     __shared__ uint32_t sh[kPlanThreads / 64];
     __shared__ uint32_t s_total, s_any;
+    // the whole grid's intersections and (candidate, super-cell) pairs
+    if (totals_out && threadIdx.x == 0) {
+        totals_out[0] = sat_rect(a.sat, a.TW + 1, 0, 0, a.TW, a.TH);
+        totals_out[1] = sat_rect(a.sat8, a.SW + 1, 0, 0, a.SW, (a.TH + 7) >> 3);
+    }
     int4* cur = fa;
     int4* nxt = fb;
     uint32_t n = 1;
@@ -221,7 +227,7 @@ gs_status launch_tile_counts(gs_ctx* ctx, const gs_proj* proj, int32_t* grid)
 
 gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t budget, const gs_cost_model* cost,
                       const gs_leaf* roots_dev, int32_t n_roots, gs_leaf* leaves_dev, int32_t max_leaves,
-                      int32_t* count_dev, int32_t* over_dev)
+                      int32_t* count_dev, int32_t* over_dev, uint64_t* totals_dev)
 {
     const int TW = proj->TW, TH = proj->TH;
     const int SW = (TW + 7) >> 3, SH = (TH + 7) >> 3;
@@ -273,7 +279,7 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
     {
         GsTimerScope ts(ctx, "plan_split");
         hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, ctx->stream, a, fa, fb, T, roots_dev, n_roots,
-                           leaves_dev, max_leaves, count_dev, over_dev);
+                           leaves_dev, max_leaves, count_dev, over_dev, totals_dev);
     }
     gs_free_all(ctx, &tmp);
     GS_HIP(ctx, hipGetLastError());

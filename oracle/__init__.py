@@ -258,6 +258,17 @@ DEFAULT_COST = dict(b_isect=4, b_cell=19, b_pixel=9, b_tile=320, b_const=1 << 20
 TRAIN_COST = dict(b_isect=0, b_cell=19, b_pixel=0, b_tile=8, b_const=1 << 20)
 
 
+def walks_groups(rect_c):
+    """Whether an L1 view's rasters walk the super-tile groups: when the
+    candidates' intersections I are at least 0.18 of 64 times their
+    (candidate, super-cell) pairs Cb (the super-cells of 8 x 8 tiles, aligned
+    to the image, that each rectangle meets)."""
+    r = np.asarray(rect_c, np.int64).reshape(-1, 4)
+    I = int(((r[:, 2] - r[:, 0]) * (r[:, 3] - r[:, 1])).sum())
+    Cb = int(((((r[:, 2] - 1) >> 3) - (r[:, 0] >> 3) + 1) * (((r[:, 3] - 1) >> 3) - (r[:, 1] >> 3) + 1)).sum())
+    return 100 * I >= 1152 * Cb
+
+
 def cost_struct(cost=None) -> Cost_c:
     """A cost given without b_cell has no super-cell term."""
     c = dict(DEFAULT_COST) if cost is None else dict(dict(b_cell=0), **cost)
@@ -335,7 +346,7 @@ def train_view(cam, scene, target, loss="l1", budget=None, leaves=None, mode="pa
     if leaves is None:
         if budget is not None:
             if cost is None and loss == "l1":
-                cost = TRAIN_COST
+                cost = TRAIN_COST if walks_groups(cdec["rect"]) else DEFAULT_COST
             leaves = plan_leaves(cam, cdec["rect"], budget, cost)
         else:
             leaves = [dict(tx0=0, ty0=0, tx1=TW, ty1=(H + 15) // 16, est_bytes=0, over_budget=False)]

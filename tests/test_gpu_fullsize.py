@@ -119,8 +119,9 @@ def test_full_size_parity(ctx, name, budget_mib, path):
     ids, rect_c = ov.ids, ov.rect_c
     budget = budget_mib * MIB
     say(f"  N={sc.n} {W}x{H}: {ids.size} candidates (oracle ready in {time.time() - t0:.0f}s)")
-    # the view plans with the L1 view's load model, the six calls with the default one
-    o_leaves = oracle.plan_leaves(cam, rect_c, budget, oracle.TRAIN_COST if path == "view" else None) if budget else \
+    # the view plans with the load model of the raster it takes, the six calls with the default one
+    view_cost = oracle.TRAIN_COST if oracle.walks_groups(rect_c) else None
+    o_leaves = oracle.plan_leaves(cam, rect_c, budget, view_cost if path == "view" else None) if budget else \
         [dict(tx0=0, ty0=0, tx1=TW, ty1=TH, est_bytes=0, over_budget=False)]
     area = int(((rect_c[:, 2] - rect_c[:, 0]).astype(np.int64) * (rect_c[:, 3] - rect_c[:, 1])).sum())
     assert area == int(ov.counts.sum())

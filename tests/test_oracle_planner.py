@@ -167,3 +167,28 @@ def test_recheck_of_a_cached_layout(oracle_lib, budget_a, budget_b):
             assert L["est_bytes"] <= budget_b or L["over_budget"]
     if budget_b >= budget_a:
         assert len(got) <= len(cached) or len(kept) < len(roots)
+
+
+def test_raster_choice_reads_the_coverage_of_the_super_tiles(oracle_lib):
+    """The L1 view's raster choice compares the intersections with 0.18 of 64
+    times the (candidate, super-cell) pairs, both taken here by brute force:
+    an aligned 8 x 8-tile rectangle covers its whole super-cell, a one-tile
+    rectangle 1/64 of it, and random mixes fall on the side the brute-force
+    ratio says."""
+    assert oracle_lib.walks_groups(np.array([[8, 8, 16, 16]]))
+    assert not oracle_lib.walks_groups(np.array([[3, 3, 4, 4]]))
+    # 12 tiles in 1 super-cell: 12/64 = 0.1875 >= 0.18; 11 tiles over 2: 11/128 < 0.18
+    assert oracle_lib.walks_groups(np.array([[0, 0, 4, 3]]))
+    assert not oracle_lib.walks_groups(np.array([[0, 0, 11, 1]]))
+    rng = np.random.default_rng(31)
+    for _ in range(50):
+        TW, TH = 200, 150
+        n = int(rng.integers(1, 300))
+        x0 = rng.integers(0, TW, n)
+        y0 = rng.integers(0, TH, n)
+        w = rng.integers(1, int(rng.choice([3, 12, 40])) + 1, n)
+        h = rng.integers(1, int(rng.choice([3, 12, 40])) + 1, n)
+        rect = np.stack([x0, y0, np.minimum(x0 + w, TW), np.minimum(y0 + h, TH)], 1)
+        I = int(brute_counts(rect, TW, TH).sum())
+        Cb = int(brute_cells(rect, TW, TH).sum())
+        assert oracle_lib.walks_groups(rect) == (I / (64 * Cb) >= 0.18)
