@@ -63,8 +63,10 @@ LeafGeom make_geom(const gs_camera* cam, const gs_bins* b, const gs_raster* r)
 struct Staged {        // one wavefront's staged batch (entry j at byte 16 j of each array,
     float4 a[64];      // so one address register serves all three reads)
     float4 b[64];      // x, y, -A/2, -B | -C/2, opacity, r, g
-    float4 c[64];      // b, slot (bits), -, -
+    float4 c[64];      // b, slot (bits), list position (bits, backward), -
+    uint32_t idx[64];  // group walk: list positions of the batch's covering entries
 };
+
 
 // Per-entry part of the sub-tile cull: the conic, the reciprocals of its
 // diagonal and the threshold 2 ln(255 o), shared by every box the entry is
@@ -128,6 +130,41 @@ __device__ __forceinline__ bool covers(uint32_t key, uint32_t cr)
 {
     const uint32_t lr = key >> kCellBits, c = cr & 7u, r = cr >> 3;
     return (lr & 7u) <= c && c <= ((lr >> 3) & 7u) && ((lr >> 6) & 7u) <= r && r <= ((lr >> 9) & 7u);
+}
+
+// The next batch of a tile's group walk: up to 64 entries of the group that
+// cover the tile, in group order (FWD: ascending from *scan, into idx[0..n);
+// else descending from *scan - 1, into idx[64 - n..64)), examining 64 group
+// positions per step; *scan moves past what was examined, stopping at the
+// first covering entry that did not fit.  Returns n; the caller waits
+// (wave_sync) before reading idx.
+template <bool FWD>
+__device__ __forceinline__ int collect_covering(Staged& S, int lane, const uint32_t* __restrict__ keys,
+                                                uint64_t start, uint64_t end_pos, uint32_t cr, uint64_t* scan)
+{
+    int n = 0;
+    uint64_t sc = *scan;
+    while (n < 64 && (FWD ? sc < end_pos : sc > 0)) {
+        const int64_t p = FWD ? (int64_t)(sc + (uint64_t)lane) : (int64_t)sc - 1 - lane;
+        const bool cov = (FWD ? p < (int64_t)end_pos : p >= 0) && covers(keys[start + (uint64_t)p], cr);
+        const uint64_t m = gsd::ballot(cov);
+        const int cnt = __builtin_popcountll(m);
+        const int take = min(cnt, 64 - n);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (cov && rank < take) S.idx[FWD ? n + rank : 63 - n - rank] = (uint32_t)p;
+        if (take < cnt) {
+            // the first covering lane left over starts the next batch
+            uint64_t mm = m;
+            for (int t = 0; t < take; ++t) mm &= mm - 1ull;
+            const uint64_t L = (uint64_t)__builtin_ctzll(mm);
+            sc = FWD ? sc + L : sc - L;
+        } else {
+            sc = FWD ? sc + 64 : (sc > 64 ? sc - 64 : 0);
+        }
+        n += take;
+    }
+    *scan = sc;
+    return n;
 }
 
 // One kept entry of the staged batch (geometry a, b, blue cb, list position
@@ -365,21 +402,33 @@ __device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, co
 {
     const uint32_t maxl = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
 
-    for (int64_t hi = maxl; hi > 0; hi -= 64) {
-        const int64_t lo = hi > 64 ? hi - 64 : 0;
-        const int cnt = (int)(hi - lo);
+    // batches of 64 list entries, back to front; a group walk batches the
+    // covering entries (collect_covering), the highest position in slot 63
+    uint64_t scan = maxl;
+    for (int64_t hi = maxl; GROUPS ? scan > 0 : hi > 0; hi -= 64) {
+        bool has;
+        uint32_t n_l;   // the lane's list position
+        if constexpr (GROUPS) {
+            const int nb = collect_covering<false>(S, lane, keys, start, 0, cr, &scan);
+            gsd::wave_sync();
+            has = lane >= 64 - nb;
+            n_l = has ? S.idx[lane] : 0u;
+        } else {
+            const int64_t lo = hi > 64 ? hi - 64 : 0;
+            has = lane < (int)(hi - lo);
+            n_l = (uint32_t)(lo + lane);
+        }
         uint32_t qb = 0;
-        if (lane < cnt && (!GROUPS || covers(keys[start + lo + lane], cr))) {
-            const uint32_t s = values[start + lo + lane];
+        if (has) {
+            const uint32_t s = values[start + n_l];
             const float4 a = g0[s], b = g1[s];
             S.a[lane] = a;
             S.b[lane] = b;
-            S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), 0.0f, 0.0f);
-            const uint32_t n = (uint32_t)(lo + lane);
+            S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), __builtin_bit_cast(float, n_l), 0.0f);
             const CullPrep cp = cull_prep(a, b);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                if (n < mq[k] && !cull_test(cp, bx[k & 1], by[k >> 1])) qb |= 1u << k;
+                if (n_l < mq[k] && !cull_test(cp, bx[k & 1], by[k >> 1])) qb |= 1u << k;
         }
         gsd::wave_sync();
         uint64_t mask = gsd::ballot(qb != 0);
@@ -387,10 +436,10 @@ __device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, co
             const int j = 63 - __builtin_clzll(mask);
             mask &= ~(1ull << j);
             const uint32_t qm = __builtin_amdgcn_readlane(qb, j);
-            const uint32_t n = (uint32_t)(lo + j);
             const float4 a = S.a[j];
             const float4 bb = S.b[j];
             const float4 cs = S.c[j];
+            const uint32_t n = __builtin_bit_cast(uint32_t, cs.z);
             float p[9];
 #pragma unroll
             for (int v = 0; v < 9; ++v) p[v] = 0.0f;
@@ -613,18 +662,32 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
         lst[k] = inside[k] ? len : 0u;
     }
     uint32_t n_eval = 0, n_inc = 0;   // unused (no statistics here)
-    for (uint64_t base = start; base < end; base += 64) {
+    // batches of 64 list entries; a group walk batches the covering entries
+    uint64_t scan = start;
+    for (uint64_t base = start; GROUPS ? scan < end : base < end; base += 64) {
         uint32_t aq = 0;   // quadrants with a pixel still compositing
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (gsd::ballot(lst[k] == len) != 0) aq |= 1u << k;
         if (aq == 0) break;
-        const uint64_t e = base + lane;
+        bool has;
+        uint32_t ep;   // the lane's list position
+        if constexpr (GROUPS) {
+            uint64_t rel = scan - start;
+            const int nb = collect_covering<true>(S, lane, keys, start, end - start, cr, &rel);
+            scan = start + rel;
+            gsd::wave_sync();
+            has = lane < nb;
+            ep = has ? S.idx[lane] : 0u;
+        } else {
+            has = base + lane < end;
+            ep = (uint32_t)(base - start) + (uint32_t)lane;
+        }
         uint32_t qb = 0;
         float4 a, b;
         float c = 0.0f;
-        if (e < end && (!GROUPS || covers(keys[e], cr))) {
-            const uint32_t s = values[e];
+        if (has) {
+            const uint32_t s = values[start + ep];
             a = g0[s];
             b = g1[s];
             c = g2[s].x;
@@ -638,8 +701,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
             const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
             S.a[pos] = a;
             S.b[pos] = b;
-            S.c[pos] = make_float4(c, __builtin_bit_cast(float, (uint32_t)(base - start) + (uint32_t)lane),
-                                   __builtin_bit_cast(float, qb), 0.0f);
+            S.c[pos] = make_float4(c, __builtin_bit_cast(float, ep), __builtin_bit_cast(float, qb), 0.0f);
         }
         const int nk = __builtin_popcountll(km);
         gsd::wave_sync();
