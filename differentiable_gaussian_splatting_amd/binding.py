@@ -105,7 +105,7 @@ class gs_gate_stats(C.Structure):
 
 class gs_view_result(C.Structure):
     _fields_ = [("loss", C.c_double), ("n_cand", C.c_int64), ("n_isect", C.c_int64), ("n_leaves", C.c_int32),
-                ("pad", C.c_int32), ("peak_bytes", C.c_uint64), ("gate_backward", C.c_int32),
+                ("groups_walked", C.c_int32), ("peak_bytes", C.c_uint64), ("gate_backward", C.c_int32),
                 ("gate_forced", C.c_int32), ("gate_score", C.c_double)]
 
 
@@ -561,7 +561,7 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     ctx.check(ctx.lib.gs_train_view(ctx.handle, C.byref(camera_struct(cam)), C.byref(params.struct()),
                                     _ptr(target), C.byref(o), C.byref(res)))
     out = dict(loss=res.loss, n_cand=res.n_cand, n_isect=res.n_isect, n_leaves=res.n_leaves,
-               peak_bytes=res.peak_bytes)
+               peak_bytes=res.peak_bytes, groups_walked=bool(res.groups_walked))
     if gate is not None:
         out.update(backward=bool(res.gate_backward), forced=bool(res.gate_forced), score=res.gate_score)
     if max_leaves:

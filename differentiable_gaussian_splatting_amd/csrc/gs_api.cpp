@@ -1363,7 +1363,7 @@ done:
 static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, const float* target,
                                const gs_view_opts* opts, const std::vector<gs_leaf>& leaves, bool backward,
                                float* grad2d, double* l1_view, float* image, double* ssim_acc, int64_t* isect_total,
-                               bool walk)
+                               bool walk, bool* walked)
 {
     gs_status st = GS_OK;
     int64_t l1_off = 0;
@@ -1381,6 +1381,7 @@ static gs_status render_leaves(gs_ctx* ctx, const gs_camera* cam, const gs_proj*
     for (const gs_leaf& L : leaves)
         groups = groups && leaf_pipelinable(proj, gs_tile_rect{L.tx0, L.ty0, L.tx1, L.ty1});
     const bool pipe = groups && leaves.size() > 1 && !(ctx->timing && ctx->timing_only.empty());
+    *walked = groups;
     if (opts->loss_kind == 1) {
         // a host target: each next leaf's slice is copied on the second
         // stream while the current leaf is rendered
@@ -1617,6 +1618,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     std::vector<gs_leaf> leaves;
     const int32_t TW = proj->TW, TH = proj->TH;
     bool walk = false;   // L1: the leaves' rasters walk their super-tile groups
+    bool walk_used = false;
     if (opts->budget_bytes > 0 || opts->n_leaves_in > 0) {
         // a fresh plan, the re-check of the caller's cached layout, or (budget
         // 0) the caller's layout as it is
@@ -1704,7 +1706,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         // leaves' buffers are not kept between the passes, so a view that
         // runs its backward renders twice
         if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, false, grad2d, l1_view, image, loss_dev + 1,
-                                &isect_total, walk)) != GS_OK)
+                                &isect_total, walk, &walk_used)) != GS_OK)
             goto done;
         if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss)) != GS_OK) goto done;
         gs_gate_decision d{};
@@ -1718,7 +1720,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         if (!d.backward) goto finish;
     }
     if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, true, grad2d, l1_view, image, loss_dev + 1,
-                            &isect_total, walk)) != GS_OK)
+                            &isect_total, walk, &walk_used)) != GS_OK)
         goto done;
     if (opts->grad3d_out || opts->adam_step <= 0) {
         float* grad3d = (float*)gs_malloc(ctx, sizeof(float) * (int64_t)F * nc, GS_MEM_GRAD, &view);
@@ -1769,6 +1771,7 @@ finish:
     result->n_cand = n_cand;
     result->n_isect = isect_total;
     result->n_leaves = (int32_t)leaves.size();
+    result->groups_walked = walk_used ? 1 : 0;
     result->peak_bytes = ctx->peak - live0;
     if (opts->leaf_bytes_out && opts->max_leaves > 0)
         std::memcpy(opts->leaf_bytes_out, ctx->tag_peak.data(),

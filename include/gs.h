@@ -454,7 +454,9 @@ typedef struct {
 typedef struct {
     double loss;
     int64_t n_cand, n_isect;     /* n_isect summed over leaves                 */
-    int32_t n_leaves, pad;
+    int32_t n_leaves;
+    int32_t groups_walked;       /* 1: the L1 rasters walked the super-tile    */
+                                 /* groups (coverage rule), 0: per-tile lists  */
     uint64_t peak_bytes;         /* library high-water mark during the view    */
                                  /* (a device-resident target not included)    */
     int32_t gate_backward;       /* with a gate: the decision (else 0)         */

@@ -141,7 +141,9 @@ def test_full_size_parity(ctx, name, budget_mib, path):
         r = B.gs_train_view(ctx, cam, ds, target, budget_bytes=budget, image_out=image,
                             adam=dict(step=1, params=ds, m=m, v=v), max_leaves=1 << 14)
         torch.cuda.synchronize()
-        say(f"  GPU view: {r['n_leaves']} leaves, {r['n_isect']} intersections, loss {r['loss']:.9f}")
+        say(f"  GPU view: {r['n_leaves']} leaves, {r['n_isect']} intersections, loss {r['loss']:.9f}, "
+            f"groups walked {r['groups_walked']}")
+        assert r["groups_walked"] == (bool(budget) and oracle.walks_groups(rect_c))
         assert r["n_cand"] == ids.size and r["n_isect"] == area
         if budget:
             assert leaf_tuples(r["leaves"]) == leaf_tuples(o_leaves)

@@ -246,6 +246,73 @@ def test_adam_step_matches_oracle(ctx):
         assert rel_l2(got - p0, p - p0) <= 1e-3, name
 
 
+def _walk_workload():
+    """C1's generator at 1024 x 768 with splats e^0.7 times larger: its
+    Gaussians cover 0.48 of their super-tiles' tiles, so an L1 view walks the
+    super-tile groups (the small scenes above cover 0.03-0.06 and take the
+    per-tile lists)."""
+    w = scenes.make_workload("c1_small", n=2000, width=1024, height=768, seed=121)
+    w.scene.log_scales = (w.scene.log_scales + np.float32(0.7)).astype(np.float32)
+    return w
+
+
+@pytest.mark.parametrize("budget,serial", [(1_110_000, False), (1_150_000, False), (1_110_000, True), (None, False)])
+def test_train_view_group_walk(ctx, budget, serial):
+    """gs_train_view of a view whose coverage calls for the group-walking
+    raster, with the default load model (L1 group walk), over several leaves
+    pipelined and one at a time (and the whole image as one planned leaf):
+    the raster choice, the leaves, loss, image and every 3D gradient group
+    against the oracle's train_view with its own default."""
+    import torch
+    w = _walk_workload()
+    p32 = oracle.project(w.camera, w.scene, "f32")
+    assert oracle.walks_groups(p32["rect"][p32["cand"]])
+    ds = B.DeviceScene(w.scene, ctx.device)
+    target = torch.from_numpy(w.target).to(ctx.device)
+    K = (w.scene.sh_degree + 1) ** 2
+    g3 = torch.zeros((w.scene.n, 11 + 3 * K), dtype=torch.float32, device=ctx.device)
+    img = torch.zeros((3, w.camera.height, w.camera.width), dtype=torch.float32, device=ctx.device)
+    b = budget if budget is not None else 1 << 40
+    r = B.gs_train_view(ctx, w.camera, ds, target, budget_bytes=b, image_out=img, grad3d_out=g3,
+                        max_leaves=64, serial_leaves=serial)
+    o = oracle.train_view(w.camera, w.scene, w.target, budget=b)
+    say(f"group walk budget {budget} serial {serial}: {r['n_leaves']} leaves, walked {r['groups_walked']}")
+    assert r["groups_walked"]
+    assert r["n_leaves"] == len(o["leaves"]) and (budget is None or r["n_leaves"] > 2)
+    got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in r["leaves"]]
+    assert got == [(L["tx0"], L["ty0"], L["tx1"], L["ty1"], L["est_bytes"]) for L in o["leaves"]]
+    assert all(L["bytes"] <= L["est_bytes"] for L in r["leaves"])
+    assert r["n_isect"] == o["n_isect"]
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    assert np.array_equal(bits(img.cpu().numpy()), bits(o["image"].astype(np.float32)))
+    gg, og = grad3d_groups(g3.cpu().numpy(), 3 if K == 16 else 0), grad3d_groups(o["grad3d"], 3 if K == 16 else 0)
+    for name in gg:
+        e = rel_l2(gg[name], og[name])
+        say(f"  grad3d {name:10s} rel L2 {e:.2e}")
+        assert e <= GRAD_TOL, name
+
+
+def test_low_coverage_view_takes_the_lists(ctx):
+    """A view whose Gaussians cover few of their super-tiles' tiles renders
+    from per-tile lists, planned with the default model, as the oracle's
+    train_view plans it."""
+    import torch
+    w = scenes.make_workload("c3_gmm4k", n=40000, width=497, height=283, seed=109)
+    p32 = oracle.project(w.camera, w.scene, "f32")
+    assert not oracle.walks_groups(p32["rect"][p32["cand"]])
+    ds = B.DeviceScene(w.scene, ctx.device)
+    target = torch.from_numpy(w.target).to(ctx.device)
+    img = torch.zeros((3, w.camera.height, w.camera.width), dtype=torch.float32, device=ctx.device)
+    r = B.gs_train_view(ctx, w.camera, ds, target, budget_bytes=3_000_000, image_out=img, max_leaves=64)
+    o = oracle.train_view(w.camera, w.scene, w.target, budget=3_000_000)
+    assert not r["groups_walked"]
+    assert [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in r["leaves"]] == \
+        [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in o["leaves"]]
+    assert r["n_leaves"] > 1
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    assert np.array_equal(bits(img.cpu().numpy()), bits(o["image"].astype(np.float32)))
+
+
 @pytest.mark.parametrize("chunk,deg", [(700, 3), (0, 3), (0, 1), (0, 0)])
 def test_train_view_chunked_update_matches_oracle(ctx, chunk, deg):
     """gs_train_view with Adam and no dense gradient output: chunk 0 (the
