@@ -34,6 +34,30 @@ def _compile(src: str) -> str:
     return out
 
 
+TORCH_ALLOC = os.path.join(HERE, "libgsmi_torchalloc.so")
+
+
+def build_torch_alloc() -> str | None:
+    """libgsmi_torchalloc.so: C allocator callbacks over PyTorch's HIP caching
+    allocator (host code only, linked against libc10_hip), for the binding.
+    None when torch is not importable."""
+    try:
+        import torch
+    except ImportError:
+        return None
+    tp = os.path.dirname(torch.__file__)
+    tmp = TORCH_ALLOC + ".tmp"
+    cmd = ["hipcc", "-std=c++17", "-O2", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__=1", "-DUSE_ROCM=1",
+           "-I" + os.path.join(tp, "include"), "-I" + os.path.join(tp, "include", "torch", "csrc", "api", "include"),
+           os.path.join(CSRC, "torch_alloc.cpp"), "-L" + os.path.join(tp, "lib"), "-lc10_hip", "-lc10",
+           "-Wl,-rpath," + os.path.join(tp, "lib"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on torch_alloc.cpp:\n{r.stderr}")
+    os.replace(tmp, TORCH_ALLOC)
+    return TORCH_ALLOC
+
+
 def build(force: bool = True, jobs: int = 8) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES] + [os.path.join(CSRC, h) for h in HEADERS] + \
         [os.path.join(ROOT, "include", "gs.h")]
@@ -45,6 +69,7 @@ def build(force: bool = True, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, check=True)
     os.replace(tmp, LIB)
+    build_torch_alloc()
     return LIB
 
 

@@ -181,9 +181,26 @@ def _ptr(t):
 
 # ---------------------------------------------------------------------------- context
 
+TORCH_ALLOC_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsmi_torchalloc.so")
+_talloc = None
+
+
+def _torch_alloc_lib():
+    """The C allocator callbacks over torch's HIP caching allocator
+    (libgsmi_torchalloc.so, built with libgsmi.so), or None if not built."""
+    global _talloc
+    if _talloc is None and os.path.exists(TORCH_ALLOC_LIB):
+        import torch  # noqa: F401  (loads libc10_hip, which the callbacks call)
+        _talloc = C.CDLL(TORCH_ALLOC_LIB)
+    return _talloc
+
+
 class Context:
     """A library context on the current torch device and stream, allocating
-    through torch's caching allocator."""
+    through torch's caching allocator: by C callbacks into it when
+    libgsmi_torchalloc.so is built, else (or with torch_allocator="python")
+    by Python callbacks; torch_allocator=False: the library's own
+    hipMallocAsync."""
 
     def __init__(self, device=None, stream=None, torch_allocator=True):
         import torch
@@ -209,7 +226,11 @@ class Context:
             except Exception:
                 traceback.print_exc()
 
-        if torch_allocator:
+        shim = _torch_alloc_lib() if torch_allocator is True else None
+        if shim is not None:
+            self._alloc_cb = ALLOC_FN(("gs_torch_alloc", shim))
+            self._free_cb = FREE_FN(("gs_torch_free", shim))
+        elif torch_allocator:
             self._alloc_cb, self._free_cb = ALLOC_FN(_alloc), FREE_FN(_free)
         else:
             self._alloc_cb, self._free_cb = C.cast(None, ALLOC_FN), C.cast(None, FREE_FN)
