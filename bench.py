@@ -239,7 +239,7 @@ def main():
     # per leaf of one more (untimed) view: its estimate and the bytes the
     # library held for it
     leaf_rep = None
-    if grid is None and not args.cached_layout:
+    if grid is None and not args.cached_layout and budget > 0:
         adam = None if args.no_adam else dict(step=k + 1, params=params, m=m, v=v, lr=1e-3)
         rl = B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam,
                              serial_leaves=args.serial_leaves, max_leaves=65536)
