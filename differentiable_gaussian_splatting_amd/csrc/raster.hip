@@ -60,6 +60,11 @@ LeafGeom make_geom(const gs_camera* cam, const gs_bins* b, const gs_raster* r)
     return g;
 }
 
+// list positions whose forward quadrant masks the fused kernel keeps in LDS
+// for its backward (one byte each); entries further down the list are culled
+// again by the backward
+constexpr uint32_t kQCache = 2048;
+
 struct Staged {        // one wavefront's staged batch (entry j at byte 16 j of each array,
     float4 a[64];      // so one address register serves all three reads)
     float4 b[64];      // x, y, -A/2, -B | -C/2, opacity, r, g
@@ -398,7 +403,8 @@ __device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, co
                                          const uint32_t (&mq)[4], const uint32_t* __restrict__ values,
                                          const float4* __restrict__ g0, const float4* __restrict__ g1,
                                          const float4* __restrict__ g2, float* __restrict__ grad2d,
-                                         const uint32_t* __restrict__ keys = nullptr, uint32_t cr = 0)
+                                         const uint32_t* __restrict__ keys = nullptr, uint32_t cr = 0,
+                                         const uint8_t* qcache = nullptr)
 {
     const uint32_t maxl = max(max(mq[0], mq[1]), max(mq[2], mq[3]));
 
@@ -425,10 +431,18 @@ __device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, co
             S.a[lane] = a;
             S.b[lane] = b;
             S.c[lane] = make_float4(g2[s].x, __builtin_bit_cast(float, s), __builtin_bit_cast(float, n_l), 0.0f);
-            const CullPrep cp = cull_prep(a, b);
+            if (qcache && n_l < kQCache) {
+                // the forward's cull of this entry, for the quadrants whose
+                // walks reach it (they were compositing when it was culled)
+                const uint32_t live = (n_l < mq[0] ? 1u : 0u) | (n_l < mq[1] ? 2u : 0u) | (n_l < mq[2] ? 4u : 0u) |
+                                      (n_l < mq[3] ? 8u : 0u);
+                qb = (uint32_t)qcache[n_l] & live;
+            } else {
+                const CullPrep cp = cull_prep(a, b);
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (n_l < mq[k] && !cull_test(cp, bx[k & 1], by[k >> 1])) qb |= 1u << k;
+                for (int k = 0; k < 4; ++k)
+                    if (n_l < mq[k] && !cull_test(cp, bx[k & 1], by[k >> 1])) qb |= 1u << k;
+            }
         }
         gsd::wave_sync();
         uint64_t mask = gsd::ballot(qb != 0);
@@ -623,6 +637,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
                                                       const uint32_t* __restrict__ keys, int SW)
 {
     __shared__ Staged st[kFusedWaves];
+    __shared__ uint8_t qc[kFusedWaves][kQCache];   // the forward's quadrant mask of each list position
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * kFusedWaves + wave;
     if (w >= n_tiles) return;
@@ -695,6 +710,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 if (((aq >> k) & 1u) && !cull_test(cp, bx[k & 1], by[k >> 1])) qb |= 1u << k;
+            if (BWD && ep < kQCache) qc[wave][ep] = (uint8_t)qb;
         }
         const uint64_t km = gsd::ballot(qb != 0);
         if (qb != 0) {
@@ -756,7 +772,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
 
     // ---- backward
     bwd_walk<GROUPS>(S, lane, start, pxc, pyc, bx, by, T, GS, gr0, gr1, gr2, lst, mq, values, g0, g1, g2, grad2d,
-                     keys, cr);
+                     keys, cr, qc[wave]);
 }
 
 
