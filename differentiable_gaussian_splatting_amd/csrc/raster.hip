@@ -145,13 +145,17 @@ __device__ __forceinline__ bool covers(uint32_t key, uint32_t cr)
 // (wave_sync) before reading idx.
 template <bool FWD>
 __device__ __forceinline__ int collect_covering(Staged& S, int lane, const uint32_t* __restrict__ keys,
-                                                uint64_t start, uint64_t end_pos, uint32_t cr, uint64_t* scan)
+                                                uint64_t start, uint64_t end_pos, uint32_t cr, uint64_t* scan,
+                                                uint8_t* qmark = nullptr)
 {
     int n = 0;
     uint64_t sc = *scan;
     while (n < 64 && (FWD ? sc < end_pos : sc > 0)) {
         const int64_t p = FWD ? (int64_t)(sc + (uint64_t)lane) : (int64_t)sc - 1 - lane;
-        const bool cov = (FWD ? p < (int64_t)end_pos : p >= 0) && covers(keys[start + (uint64_t)p], cr);
+        const bool in = FWD ? p < (int64_t)end_pos : p >= 0;
+        const bool cov = in && covers(keys[start + (uint64_t)p], cr);
+        // qmark: positions that do not cover the tile get an empty quadrant mask
+        if (qmark && in && !cov && (uint64_t)p < kQCache) qmark[p] = 0;
         const uint64_t m = gsd::ballot(cov);
         const int cnt = __builtin_popcountll(m);
         const int take = min(cnt, 64 - n);
@@ -165,6 +169,50 @@ __device__ __forceinline__ int collect_covering(Staged& S, int lane, const uint3
             sc = FWD ? sc + L : sc - L;
         } else {
             sc = FWD ? sc + 64 : (sc > 64 ? sc - 64 : 0);
+        }
+        n += take;
+    }
+    *scan = sc;
+    return n;
+}
+
+// The next backward batch of a fused tile: up to 64 list positions below
+// *scan (descending, into idx[64 - n..64)) whose entry the backward must
+// evaluate: below kQCache, those whose forward quadrant mask has a quadrant
+// whose walks reach the position (entries culled there, or not covering the
+// tile, are skipped); further down, every entry of a list, or every group
+// entry that covers the tile.
+template <bool GROUPS>
+__device__ __forceinline__ int collect_live(Staged& S, int lane, const uint32_t* __restrict__ keys, uint64_t start,
+                                            uint32_t cr, const uint8_t* qc, const uint32_t (&mq)[4],
+                                            uint64_t* scan)
+{
+    int n = 0;
+    uint64_t sc = *scan;
+    while (n < 64 && sc > 0) {
+        const int64_t p = (int64_t)sc - 1 - lane;
+        bool keep = false;
+        if (p >= 0) {
+            const uint32_t up = (uint32_t)p;
+            if (up < kQCache) {
+                const uint32_t live = (up < mq[0] ? 1u : 0u) | (up < mq[1] ? 2u : 0u) | (up < mq[2] ? 4u : 0u) |
+                                      (up < mq[3] ? 8u : 0u);
+                keep = ((uint32_t)qc[up] & live) != 0;
+            } else {
+                keep = !GROUPS || covers(keys[start + (uint64_t)p], cr);
+            }
+        }
+        const uint64_t m = gsd::ballot(keep);
+        const int cnt = __builtin_popcountll(m);
+        const int take = min(cnt, 64 - n);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (keep && rank < take) S.idx[63 - n - rank] = (uint32_t)p;
+        if (take < cnt) {
+            uint64_t mm = m;
+            for (int t = 0; t < take; ++t) mm &= mm - 1ull;
+            sc -= (uint64_t)__builtin_ctzll(mm);
+        } else {
+            sc = sc > 64 ? sc - 64 : 0;
         }
         n += take;
     }
@@ -411,10 +459,15 @@ __device__ __forceinline__ void bwd_walk(Staged& S, int lane, uint64_t start, co
     // batches of 64 list entries, back to front; a group walk batches the
     // covering entries (collect_covering), the highest position in slot 63
     uint64_t scan = maxl;
-    for (int64_t hi = maxl; GROUPS ? scan > 0 : hi > 0; hi -= 64) {
+    for (int64_t hi = maxl; (GROUPS || qcache) ? scan > 0 : hi > 0; hi -= 64) {
         bool has;
         uint32_t n_l;   // the lane's list position
-        if constexpr (GROUPS) {
+        if (qcache) {
+            const int nb = collect_live<GROUPS>(S, lane, keys, start, cr, qcache, mq, &scan);
+            gsd::wave_sync();
+            has = lane >= 64 - nb;
+            n_l = has ? S.idx[lane] : 0u;
+        } else if constexpr (GROUPS) {
             const int nb = collect_covering<false>(S, lane, keys, start, 0, cr, &scan);
             gsd::wave_sync();
             has = lane >= 64 - nb;
@@ -689,7 +742,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_raster_fused(LeafGeom g, i
         uint32_t ep;   // the lane's list position
         if constexpr (GROUPS) {
             uint64_t rel = scan - start;
-            const int nb = collect_covering<true>(S, lane, keys, start, end - start, cr, &rel);
+            const int nb = collect_covering<true>(S, lane, keys, start, end - start, cr, &rel,
+                                                  BWD ? qc[wave] : nullptr);
             scan = start + rel;
             gsd::wave_sync();
             has = lane < nb;
