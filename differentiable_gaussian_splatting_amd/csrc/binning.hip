@@ -217,13 +217,14 @@ __device__ __forceinline__ Cells leaf_cells(int4 r, int ltx0, int lty0, int ltx1
 }
 
 // super-tiles of the leaf that each listed candidate's rectangle meets
+// (list: positions in the depth order, NULL: all of them)
 __global__ __launch_bounds__(256) void k_count_cells(int64_t n, const uint32_t* __restrict__ list,
-                                                     const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
+                                                     const uint2* __restrict__ rect_d, int ltx0, int lty0, int ltx1,
                                                      int lty1, int sh, uint32_t* __restrict__ cnt)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
-    const Cells c = leaf_cells(rect[list[k]], ltx0, lty0, ltx1, lty1, sh);
+    const Cells c = leaf_cells(gsd::rect_unpack(rect_d[list ? list[k] : (uint32_t)k]), ltx0, lty0, ltx1, lty1, sh);
     cnt[k] = (uint32_t)(c.w * c.h);
 }
 
@@ -241,7 +242,10 @@ __global__ __launch_bounds__(256) void k_leaf_counts(const int32_t* __restrict__
 // through the sort, for the fine level and the group-walking raster
 
 // (super-tile, slot) pairs of the listed candidates, in list order and
-// row-major super-tile order within a rectangle.  eoff[k] - ebase is the
+// row-major super-tile order within a rectangle.  The list holds positions in
+// the depth order (NULL: every position), so a candidate's slot and packed
+// rectangle are read at its position in order and rect_d, near-contiguously
+// for an ascending list.  eoff[k] - ebase is the
 // first output of candidate k (exclusive scan of the per-candidate super-tile
 // counts, n + 1 entries, ascending).  A block writes kEO consecutive outputs,
 // so that one candidate with many super-tiles does not hold up a block:
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(256) void k_leaf_counts(const int32_t* __restrict__
 //   - the offsets of the next kEO + 1 candidates are loaded (every listed
 //     candidate meets the leaf, so no more can overlap the block's outputs),
 //     and the slots and rectangles of those that start before the block's
-//     last output are gathered into LDS;
+//     last output are staged in LDS;
 //   - each candidate whose outputs start inside the block marks that
 //     position with its index, and a prefix maximum over the positions gives
 //     every output its candidate;
@@ -273,16 +277,15 @@ __device__ __forceinline__ int wave_prefix_max(int v, int lane)
 }
 
 __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
-                                                    const int4* __restrict__ rect, int ltx0, int lty0, int ltx1,
+                                                    const uint32_t* __restrict__ order,
+                                                    const uint2* __restrict__ rect_d, int ltx0, int lty0, int ltx1,
                                                     int lty1, int sh, int SW, const uint32_t* __restrict__ eoff,
                                                     uint32_t ebase, uint32_t total, uint32_t* __restrict__ keys,
                                                     uint32_t* __restrict__ vals)
 {
     __shared__ uint32_t se[kEO + 2];
-    __shared__ uint32_t sj[kEO + 1];
-    __shared__ int4 sc[kEO + 1];       // cx0, cy0, w, h of each staged candidate's super-cells
-    __shared__ int4 sr[kEO + 1];       // its rectangle clipped to the leaf
-    __shared__ float srw[kEO + 1];     // 1 / w
+    __shared__ uint32_t sj[kEO + 1];   // slot of each staged candidate
+    __shared__ uint2 sr[kEO + 1];      // its rectangle, packed (its super-cells follow per output)
     __shared__ int owner[kEO];         // candidate whose outputs start at this position, else -1
     __shared__ int wred[4];
     __shared__ int64_t s_lo;
@@ -321,13 +324,9 @@ __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* _
     const int ns = wred[0] + wred[1] + wred[2] + wred[3];   // >= 1
     __syncthreads();
     for (int i = tid; i < ns; i += 256) {
-        const uint32_t j = list[k0 + i];
-        const int4 r = rect[j];
-        const Cells cl = leaf_cells(r, ltx0, lty0, ltx1, lty1, sh);
-        sj[i] = j;
-        sc[i] = make_int4(cl.cx0, cl.cy0, cl.w, cl.h);
-        sr[i] = make_int4(max(r.x, ltx0), max(r.y, lty0), min(r.z, ltx1), min(r.w, lty1));
-        srw[i] = 1.0f / (float)max(cl.w, 1);
+        const uint32_t p = list ? list[k0 + i] : (uint32_t)(k0 + i);
+        sj[i] = order[p];
+        sr[i] = rect_d[p];
     }
     for (int i = tid; i < kEO; i += 256) owner[i] = -1;
     __syncthreads();
@@ -359,15 +358,12 @@ __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* _
         vq[q] = 0u;
         if (o >= oe) continue;
         int v = max(om[q], exc);
-        int4 cl, r;
+        uint2 pr;
         uint32_t t, j;
-        float rw;
         if (o < end_staged) {
-            cl = sc[v];
-            r = sr[v];
+            pr = sr[v];
             t = o - se[v];
             j = sj[v];
-            rw = srw[v];
         } else {
             // past the staged candidates: the last k with eoff[k] - ebase <= o
             int64_t a = k0, b = n - 1;
@@ -376,14 +372,16 @@ __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* _
                 if (eoff[mid] - ebase <= o) a = mid;
                 else b = mid - 1;
             }
-            j = list[a];
-            const int4 rr = rect[j];
-            const Cells c = leaf_cells(rr, ltx0, lty0, ltx1, lty1, sh);
-            cl = make_int4(c.cx0, c.cy0, c.w, c.h);
-            r = make_int4(max(rr.x, ltx0), max(rr.y, lty0), min(rr.z, ltx1), min(rr.w, lty1));
+            const uint32_t p = list ? list[a] : (uint32_t)a;
+            j = order[p];
+            pr = rect_d[p];
             t = o - (eoff[a] - ebase);
-            rw = 1.0f / (float)max(c.w, 1);
         }
+        const int4 rr = gsd::rect_unpack(pr);
+        const Cells c = leaf_cells(rr, ltx0, lty0, ltx1, lty1, sh);
+        const int4 cl = make_int4(c.cx0, c.cy0, c.w, c.h);
+        const int4 r = make_int4(max(rr.x, ltx0), max(rr.y, lty0), min(rr.z, ltx1), min(rr.w, lty1));
+        const float rw = 1.0f / (float)max(c.w, 1);
         const uint32_t wd = (uint32_t)cl.z;
         uint32_t ty = (uint32_t)((float)t * rw);
         int32_t rem = (int32_t)(t - ty * wd);
@@ -628,6 +626,16 @@ __global__ __launch_bounds__(256) void k_depth_pairs(int64_t n, const float4* __
     vals[j] = (uint32_t)j;
 }
 
+// the rectangles in depth order, packed: what the per-leaf passes over the
+// depth order read, contiguously, instead of gathering rect by slot
+__global__ __launch_bounds__(256) void k_rect_depth(int64_t n, const uint32_t* __restrict__ order,
+                                                    const int4* __restrict__ rect, uint2* __restrict__ rect_d)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    rect_d[k] = gsd::rect_pack(rect[order[k]]);
+}
+
 __global__ void k_export_keys(int64_t n_tiles, int ltx0, int lty0, int TWL, int TW, const uint64_t* __restrict__ offsets,
                               const uint32_t* __restrict__ values, const float4* __restrict__ g2,
                               uint64_t* __restrict__ keys)
@@ -704,7 +712,7 @@ gs_status launch_count_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf
     if (n_list > 0) {
         GsTimerScope ts(ctx, "bin_count");
         hipLaunchKernelGGL(k_count_cells, dim3((unsigned)ceil_div(n_list, 256)), dim3(256), 0, ctx->stream, n_list,
-                           list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift, cnt);
+                           list, proj->rect_d, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift, cnt);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
@@ -730,7 +738,7 @@ gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
     if (n_list > 0 && total > 0) {
         GsTimerScope ts(ctx, "emit");
         hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div((int64_t)total, kEO)), dim3(256), 0, ctx->stream,
-                           n_list, list, proj->rect, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift,
+                           n_list, list, proj->order, proj->rect_d, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift,
                            super_cols(leaf), eoff, ebase, (uint32_t)total, keys, vals);
     }
     GS_HIP(ctx, hipGetLastError());
@@ -808,6 +816,15 @@ gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, u
     if (proj->n_cand > 0)
         hipLaunchKernelGGL(k_depth_pairs, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream,
                            proj->n_cand, proj->g2, keys, vals);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_rect_depth(gs_ctx* ctx, const gs_proj* proj, const uint32_t* order, uint2* rect_d)
+{
+    if (proj->n_cand > 0)
+        hipLaunchKernelGGL(k_rect_depth, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream,
+                           proj->n_cand, order, proj->rect, rect_d);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -142,6 +142,9 @@ static bool handle_ok(const gs_ctx* ctx, const void* h, uint32_t magic)
 
 static void destroy_handle(gs_ctx* ctx, GsHandle* h)
 {
+    // the second stream may still write a projection's rect_d
+    if (h->magic == kMagicProj && static_cast<gs_proj*>(h)->rect_d_pending)
+        (void)hipStreamWaitEvent(ctx->stream, ctx->ev_rectd, 0);
     gs_free_all(ctx, &h->allocs);
     if (h->magic == kMagicProj) {
         gs_free_all(ctx, &static_cast<gs_proj*>(h)->plan_allocs);
@@ -190,6 +193,17 @@ static gs_status check_params(gs_ctx* ctx, const gs_params* p)
     return GS_OK;
 }
 
+// A projection's rect_d is written on the second stream after the depth
+// sort, beside the per-tile counts and the plan; the first reader on
+// ctx->stream waits for it there (later readers are ordered after it).
+static gs_status rect_d_ready(gs_ctx* ctx, const gs_proj* proj)
+{
+    if (!proj->rect_d_pending) return GS_OK;
+    GS_HIP(ctx, hipStreamWaitEvent(ctx->stream, ctx->ev_rectd, 0));
+    proj->rect_d_pending = false;
+    return GS_OK;
+}
+
 // leaf -> candidate groups of a plan (leaves on the device), attached to
 // proj; every group keeps the candidates' (depth, slot) order
 // Candidates per tile of the whole grid, made once per projection.
@@ -230,8 +244,8 @@ static void clear_plan(gs_ctx* ctx, gs_proj* proj, bool retire)
 
 // Groups the candidates by planned leaf and precomputes, for the whole view,
 // what binning a planned leaf needs besides its own kernels: the leaf's
-// candidates in depth order, the offsets of their coarse pairs and the leaf's
-// tile offsets.
+// candidates in depth order (as positions in proj->order), the offsets of
+// their coarse pairs and the leaf's tile offsets.
 static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ldev, const gs_leaf* hleaves,
                                    int32_t nl)
 {
@@ -262,6 +276,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     for (int32_t L = 0; L < nl; ++L)
         tbase[L + 1] = tbase[L] + (uint64_t)(plan[L].tx1 - plan[L].tx0) * (uint64_t)(plan[L].ty1 - plan[L].ty0) + 1;
     if ((st = launch_leaf_map(ctx, ldev, plan.data(), nl, proj->TW, proj->TH, lot)) != GS_OK) goto out;
+    if ((st = rect_d_ready(ctx, proj)) != GS_OK) goto out;
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
     if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
     if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;
@@ -324,7 +339,7 @@ out:
 // when the leaf is not part of the plan.
 struct PlanLeaf {
     bool found = false;
-    const uint32_t* list = nullptr;   // candidates meeting the leaf, depth order
+    const uint32_t* list = nullptr;   // candidates meeting the leaf: depth positions, ascending
     int64_t n = 0;
     int64_t isect = -1;               // from the plan's tile offsets
     int64_t cells = 0;                // coarse pairs
@@ -405,6 +420,7 @@ void gs_ctx_destroy(gs_ctx* ctx)
     }
     if (ctx->ev_alloc) (void)hipEventDestroy(ctx->ev_alloc);
     if (ctx->ev_order) (void)hipEventDestroy(ctx->ev_order);
+    if (ctx->ev_rectd) (void)hipEventDestroy(ctx->ev_rectd);
     for (hipEvent_t e : ctx->ev_done)
         if (e) (void)hipEventDestroy(e);
     for (int k = 0; k < 2; ++k) {
@@ -589,8 +605,9 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
         uint32_t* k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &tmp);
         uint32_t* v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
         uint32_t* v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
+        p->rect_d = (uint2*)gs_malloc(ctx, sizeof(uint2) * nc, GS_MEM_PROJ, &p->allocs);
         bool second = false;
-        if (!k0 || !k1 || !v0 || !v1) { st = GS_ERR_OOM; goto fail; }
+        if (!k0 || !k1 || !v0 || !v1 || !p->rect_d) { st = GS_ERR_OOM; goto fail; }
         const bool beside = !(ctx->timing && ctx->timing_only.empty()) && ensure_side(ctx) == GS_OK;
         hipStream_t main = ctx->stream;
         if (beside) {
@@ -604,9 +621,18 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
         }
         st = launch_depth_pairs(ctx, p, k0, v0);
         if (st == GS_OK) st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)cnt, 32, &second);
-        ctx->stream = main;
         if (beside && st == GS_OK && hipEventRecord(ctx->ev_order, ctx->side) != hipSuccess)
             st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+        // the rectangles in that order, for the passes over the depth order;
+        // this stream waits for them only where they are first read
+        if (st == GS_OK) st = launch_rect_depth(ctx, p, second ? v1 : v0, p->rect_d);
+        if (beside && st == GS_OK) {
+            if (hipEventRecord(ctx->ev_rectd, ctx->side) != hipSuccess)
+                st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+            else
+                p->rect_d_pending = true;
+        }
+        ctx->stream = main;
         if (st != GS_OK) goto fail;
         if ((st = ensure_tile_counts(ctx, p)) != GS_OK) goto fail;
         if (beside && hipStreamWaitEvent(main, ctx->ev_order, 0) != hipSuccess) {
@@ -822,7 +848,9 @@ static gs_status coarse_alloc(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect lea
 
 static gs_status coarse_launch(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb)
 {
-    gs_status st = launch_emit_cells(ctx, proj, cb->leaf, cb->pl.list, cb->pl.n, cb->pl.eoff, cb->pl.ebase, cb->C,
+    gs_status st = rect_d_ready(ctx, proj);
+    if (st != GS_OK) return st;
+    st = launch_emit_cells(ctx, proj, cb->leaf, cb->pl.list, cb->pl.n, cb->pl.eoff, cb->pl.ebase, cb->C,
                                      cb->k0, cb->v0);
     if (st != GS_OK) return st;
     bool have_soff = false;
@@ -842,6 +870,7 @@ static gs_status ensure_side(gs_ctx* ctx)
     GS_HIP(ctx, hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_alloc, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_order, hipEventDisableTiming));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_rectd, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[0], hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[1], hipEventDisableTiming));
     for (int k = 0; k < 2; ++k) {
@@ -899,7 +928,11 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     uint32_t* eoff_own = nullptr;
     uint64_t* soff = nullptr;
     const PlanLeaf pl = plan_leaf(proj, leaf);
-    const uint32_t* list = pl.found ? pl.list : proj->order;   // not planned: every candidate
+    const uint32_t* list = pl.found ? pl.list : nullptr;   // depth positions; not planned: every candidate
+    if ((st = rect_d_ready(ctx, proj)) != GS_OK) {
+        destroy_handle(ctx, b);
+        return st;
+    }
     const int64_t n_list = pl.found ? pl.n : proj->n_cand;
     const uint32_t* eoff = pl.eoff;
     const uint32_t ebase = pl.ebase;

@@ -300,4 +300,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// A candidate's tile rectangle [x0, x1) x [y0, y1) in 8 bytes: x0 | y0 << 16
+// and (x1 - 1) | (y1 - 1) << 16.  Exact for non-empty rectangles of a grid
+// at most 2^16 tiles wide and high (every candidate's, for images up to 2^20
+// pixels a side).
+__device__ __forceinline__ uint2 rect_pack(int4 r)
+{
+    return make_uint2((uint32_t)r.x | ((uint32_t)r.y << 16), (uint32_t)(r.z - 1) | ((uint32_t)(r.w - 1) << 16));
+}
+
+__device__ __forceinline__ int4 rect_unpack(uint2 p)
+{
+    return make_int4((int)(p.x & 0xFFFFu), (int)(p.x >> 16), (int)(p.y & 0xFFFFu) + 1, (int)(p.y >> 16) + 1);
+}
+
 }  // namespace gsd

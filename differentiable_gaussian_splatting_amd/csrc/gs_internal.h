@@ -46,6 +46,7 @@ struct gs_ctx {
     hipStream_t side = nullptr;
     hipEvent_t ev_alloc = nullptr, ev_done[2] = {nullptr, nullptr};
     hipEvent_t ev_order = nullptr;   // the depth sort of a projection done (on the second stream)
+    hipEvent_t ev_rectd = nullptr;   // its depth-ordered rectangles written (on the second stream)
     // two render streams: consecutive leaves' fused rasters overlap, the
     // next one filling the compute units the current one's last tiles leave
     hipStream_t rstream[2] = {nullptr, nullptr};
@@ -74,6 +75,8 @@ struct gs_proj : GsHandle {
     float4* g2 = nullptr;         // [n_cand] b, depth, radius, flags (bits)
     int32_t* slot_of = nullptr;   // [n] slot or -1
     uint32_t* order = nullptr;    // [n_cand] slots sorted by (depth, slot)
+    uint2* rect_d = nullptr;      // [n_cand] rect of order[k] at k, packed (gsd::rect_pack)
+    mutable bool rect_d_pending = false;   // rect_d written on the second stream: wait for ctx->ev_rectd
     int32_t* tile_cnt = nullptr;  // [TH][TW] candidates per tile (made on first use)
     // leaf plan of the view (set by gs_plan_leaves): the candidates whose
     // rectangle meets each leaf, so that binning a leaf visits only those
@@ -87,7 +90,7 @@ struct gs_proj : GsHandle {
     uint64_t* plan_toff = nullptr;    // device: per leaf, its tile offsets [T_L + 1]
     uint32_t* plan_order = nullptr;   // device: per leaf at plan_tbase, its tiles longest list first [T_L]
     std::vector<GsAlloc> plan_retired; // earlier plans (bins may still point into them)
-    uint32_t* plan_cands = nullptr;   // device [plan_off.back()] candidate slots, depth order per group
+    uint32_t* plan_cands = nullptr;   // device [plan_off.back()] depth positions (indices into order), ascending per group
     std::vector<GsAlloc> plan_allocs;
     gs_cost_model plan_cost{};        // cost model the plan was made with
 };
@@ -178,7 +181,9 @@ int64_t super_cells(gs_tile_rect leaf);
 int super_shift();
 uint32_t super_key_mask();      // bits of a coarse key that hold the super-tile
 int64_t super_cells_max();      // super-tiles a leaf may have
-// per listed candidate: super-tiles of the leaf its rectangle meets
+// per listed candidate: super-tiles of the leaf its rectangle meets.  Here
+// and in launch_emit_cells, list holds positions in the depth order
+// (indices into proj->order and proj->rect_d), NULL: every candidate.
 gs_status launch_count_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                              int64_t n_list, uint32_t* cnt);
 // per-tile candidate counts of the leaf (row-major in the leaf) from proj->tile_cnt
@@ -208,6 +213,8 @@ gs_status launch_fine_write(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint32_t kmask,
                              uint64_t* offsets);
 gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
+// rect_d[k] = the packed rectangle of slot order[k]
+gs_status launch_rect_depth(gs_ctx* ctx, const gs_proj* proj, const uint32_t* order, uint2* rect_d);
 gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);
 int bits_for(int64_t n_keys);
 

@@ -289,10 +289,11 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
 // ---------------------------------------------------------------------------
 // leaf -> candidate groups.  Binning a leaf only needs the candidates whose
 // rectangle meets it, in depth order.  The candidates are visited in depth
-// order; each emits (leaf, slot) for every leaf it meets -- one leaf when its
-// four rectangle corners share a leaf (leaves are rectangles), otherwise every
-// leaf its rectangle meets -- and a stable radix sort on the leaf id groups
-// them with the depth order kept inside each group.
+// order (their packed rectangles, rect_d, contiguous); each emits (leaf,
+// depth position) for every leaf it meets -- one leaf when its four rectangle
+// corners share a leaf (leaves are rectangles), otherwise every leaf its
+// rectangle meets -- and a stable radix sort on the leaf id groups them with
+// the depth order kept inside each group.
 
 namespace {
 
@@ -318,19 +319,47 @@ __device__ __forceinline__ bool rect_meets(int4 r, const gs_leaf& L)
     return r.x < L.tx1 && L.tx0 < r.z && r.y < L.ty1 && L.ty0 < r.w;
 }
 
-// EMIT = false: number of leaves met; true: write the (leaf, slot) pairs
+// Up to this many leaves, a candidate tests every leaf rectangle (from LDS)
+// instead of looking its corners up in the tile -> leaf map.
+constexpr int kLeafDirect = 64;
+
+// EMIT = false: number of leaves met; true: write the (leaf, depth position)
+// pairs, leaves in ascending order
 template <bool EMIT>
-__global__ __launch_bounds__(256) void k_leaf_pairs(int64_t n, const uint32_t* __restrict__ order,
-                                                    const int4* __restrict__ rect,
+__global__ __launch_bounds__(256) void k_leaf_pairs(int64_t n, const uint2* __restrict__ rect_d,
                                                     const gs_leaf* __restrict__ leaves, int nl,
                                                     const int32_t* __restrict__ lot, int TW,
                                                     uint32_t* __restrict__ cnt, const uint64_t* __restrict__ off,
                                                     uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
 {
+    __shared__ int4 sl[kLeafDirect];
+    const bool direct = nl <= kLeafDirect;
+    if (direct) {
+        for (int L = threadIdx.x; L < nl; L += blockDim.x)
+            sl[L] = make_int4(leaves[L].tx0, leaves[L].ty0, leaves[L].tx1, leaves[L].ty1);
+        __syncthreads();
+    }
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
-    const uint32_t j = order[k];
-    const int4 r = rect[j];
+    const uint32_t j = (uint32_t)k;   // the depth position
+    const int4 r = gsd::rect_unpack(rect_d[k]);
+    if (direct) {
+        uint64_t o = EMIT ? off[k] : 0;
+        uint32_t m = 0;
+        for (int L = 0; L < nl; ++L) {
+            const int4 q = sl[L];
+            if (r.x < q.z && q.x < r.z && r.y < q.w && q.y < r.w) {
+                if (EMIT) {
+                    keys[o] = (uint32_t)L;
+                    vals[o] = j;
+                    ++o;
+                }
+                ++m;
+            }
+        }
+        if (!EMIT) cnt[k] = m;
+        return;
+    }
     const int a = lot[(int64_t)r.y * TW + r.x], b = lot[(int64_t)r.y * TW + r.z - 1];
     const int c = lot[(int64_t)(r.w - 1) * TW + r.x], d = lot[(int64_t)(r.w - 1) * TW + r.z - 1];
     if (a >= 0 && a == b && a == c && a == d) {   // the four corners in one leaf: the rectangle inside it
@@ -356,17 +385,17 @@ __global__ __launch_bounds__(256) void k_leaf_pairs(int64_t n, const uint32_t* _
     if (!EMIT) cnt[k] = m;
 }
 
-// per grouped (leaf, slot) entry: the super-tiles of its leaf that the
-// rectangle meets (the entry's coarse pairs)
+// per grouped (leaf, depth position) entry: the super-tiles of its leaf that
+// the rectangle meets (the entry's coarse pairs)
 __global__ __launch_bounds__(256) void k_group_cells(int64_t n, const uint32_t* __restrict__ leaf_of,
-                                                     const uint32_t* __restrict__ slot, const int4* __restrict__ rect,
+                                                     const uint32_t* __restrict__ pos, const uint2* __restrict__ rect_d,
                                                      const gs_leaf* __restrict__ leaves, int sh,
                                                      uint32_t* __restrict__ cnt)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
     const gs_leaf lf = leaves[leaf_of[k]];
-    const int4 r = rect[slot[k]];
+    const int4 r = gsd::rect_unpack(rect_d[pos[k]]);
     // image-aligned super-cells that the rectangle meets inside the leaf
     const int x0 = max(r.x, lf.tx0), x1 = min(r.z, lf.tx1);
     const int y0 = max(r.y, lf.ty0), y1 = min(r.w, lf.ty1);
@@ -493,7 +522,7 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
     GsTimerScope ts(ctx, "leaf_groups");
     if (n_entries > 0)
         hipLaunchKernelGGL(k_group_cells, dim3((unsigned)ceil_div(n_entries, 256)), dim3(256), 0, ctx->stream,
-                           n_entries, leaf_of, slot, proj->rect, leaves_dev, super_shift(), cell_cnt);
+                           n_entries, leaf_of, slot, proj->rect_d, leaves_dev, super_shift(), cell_cnt);
     gs_status st = launch_scan_u32_to_u32(ctx, cell_cnt, cell_off, n_entries);
     if (st != GS_OK) return st;
     if (n_leaves > 0) {
@@ -518,6 +547,8 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
 gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, const gs_leaf* hleaves, int32_t n_leaves, int TW,
                           int TH, int32_t* lot)
 {
+    // k_leaf_pairs reads the map only for more than kLeafDirect leaves
+    if (n_leaves <= kLeafDirect) return GS_OK;
     // -1 on tiles no leaf covers (a layout that renders part of the view)
     gs_status st = launch_fill_u32(ctx, (uint32_t*)lot, 0xFFFFFFFFu, (int64_t)TW * TH);
     if (st != GS_OK) return st;
@@ -536,10 +567,10 @@ gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* lea
         GsTimerScope ts(ctx, "leaf_groups");
         if (!off)
             hipLaunchKernelGGL(k_leaf_pairs<false>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n,
-                               proj->order, proj->rect, leaves_dev, n_leaves, lot, proj->TW, cnt, off, keys, vals);
+                               proj->rect_d, leaves_dev, n_leaves, lot, proj->TW, cnt, off, keys, vals);
         else
             hipLaunchKernelGGL(k_leaf_pairs<true>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n,
-                               proj->order, proj->rect, leaves_dev, n_leaves, lot, proj->TW, cnt, off, keys, vals);
+                               proj->rect_d, leaves_dev, n_leaves, lot, proj->TW, cnt, off, keys, vals);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;

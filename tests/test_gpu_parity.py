@@ -536,26 +536,29 @@ def test_replan_rejects_a_layout_that_does_not_tile_the_grid(ctx):
     B.gs_release(ctx, p)
 
 
-@pytest.mark.parametrize("blocks", [None, [1, 4]])
-def test_fixed_grid_views_match_oracle(ctx, blocks):
+@pytest.mark.parametrize("nx,ny,blocks", [(3, 2, None), (3, 2, [1, 4]), (9, 8, None)])
+def test_fixed_grid_views_match_oracle(ctx, nx, ny, blocks):
     """The fixed-block baselines: a 3 x 2 grid rendered as given (budget 0),
     all blocks (one update per view) or some of them (the view of one
     per-block update step: only those pixels are rendered and differentiated).
     Loss, image (pixels outside the blocks untouched), leaves and every
-    gradient group against the oracle's view over the same blocks."""
+    gradient group against the oracle's view over the same blocks.  The 9 x 8
+    grid has more leaves than the candidate-to-leaf grouping tests one by one
+    (it looks the rectangle corners up in a tile -> leaf map)."""
     import torch
     w = scenes.make_workload("c3_gmm4k", n=30000, width=400, height=250, posed=True, seed=131)
     lib = B.load()
-    grid = B.gs_grid_leaves(lib, w.camera.tiles_x, w.camera.tiles_y, 3, 2)
+    grid = B.gs_grid_leaves(lib, w.camera.tiles_x, w.camera.tiles_y, nx, ny)
     assert [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in grid] == \
-        [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in oracle.grid_leaves(w.camera.tiles_x, w.camera.tiles_y, 3, 2)]
+        [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in oracle.grid_leaves(w.camera.tiles_x, w.camera.tiles_y, nx, ny)]
+    assert len(grid) == nx * ny
     layout = grid if blocks is None else [grid[k] for k in blocks]
     ds = B.DeviceScene(w.scene, ctx.device)
     K = (w.scene.sh_degree + 1) ** 2
     g3 = torch.zeros((w.scene.n, 11 + 3 * K), dtype=torch.float32, device=ctx.device)
     img = torch.full((3, w.camera.height, w.camera.width), -1.0, dtype=torch.float32, device=ctx.device)
     r = B.gs_train_view(ctx, w.camera, ds, torch.from_numpy(w.target).to(ctx.device), budget_bytes=0,
-                        leaves_in=layout, partial=blocks is not None, image_out=img, grad3d_out=g3, max_leaves=16)
+                        leaves_in=layout, partial=blocks is not None, image_out=img, grad3d_out=g3, max_leaves=128)
     o = oracle.train_view(w.camera, w.scene, w.target, leaves=[dict(L, est_bytes=0, over_budget=False)
                                                                for L in layout])
     assert [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in r["leaves"]] == \
