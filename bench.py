@@ -432,10 +432,11 @@ def kernel_work(wc, sc):
                          f"+ backward ({OPS_EXAMINED} x revisited-only + {OPS_INCLUDED_BWD} x included)"),
         "radix": ("hbm", 20 * wc["radix_elems"], "per pass and element: read the key twice, the value once, "
                                                    "write key and value (20 B)"),
-        "emit": ("hbm", 8 * C + 28 * wc["group_entries"], "write 8 B (super-tile, slot) per coarse pair; read "
-                                                           "list entry, rectangle, offset per candidate visit"),
-        "bin_count": ("hbm", 24 * wc["group_entries"] + 8 * T, "read list entry and rectangle, write the count; "
-                                                             "gather the leaf's tile counts"),
+        "emit": ("hbm", 8 * C + 20 * wc["group_entries"], "write 8 B (super-tile, slot) per coarse pair; read "
+                                                           "depth position, slot, packed rectangle (8 B) and "
+                                                           "offset per candidate visit"),
+        "bin_count": ("hbm", 16 * wc["group_entries"] + 8 * T, "read depth position and packed rectangle, write "
+                                                             "the count; gather the leaf's tile counts"),
         "seg_offsets": ("hbm", 4 * C + 8 * wc["supers"], "read sorted super-tile keys, write group offsets"),
         "fine": ("hbm", 4 * I + 20 * C + 8 * T, "read each coarse entry and its rectangle, the tile offsets; "
                                                 "write one slot per intersection"),

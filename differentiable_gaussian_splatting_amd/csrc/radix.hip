@@ -1,7 +1,7 @@
 // radix.hip -- stable LSD radix sort of (u32 key, u32 value) pairs.
 //
-// Each pass takes 8 key bits (fewer on the last pass), or a single pass takes
-// up to 10 bits: a per-block digit histogram (LDS atomics) laid out
+// Each pass takes at most 8 key bits (the passes share them evenly), or a
+// single pass takes up to 10 bits: a per-block digit histogram (LDS atomics) laid out
 // digit-major (digit * n_blocks + block), an exclusive scan of each digit's
 // row with its total (one workgroup per digit), and a stable scatter, whose
 // blocks add the scan of the digit totals.  The scatter ranks a
@@ -256,7 +256,12 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
     }
     gs_status st = GS_OK;
     uint32_t *ki = k0, *vi = v0, *ko = k1, *vo = v1;
-    const int step = wide ? key_bits : 8;
+    // 8-bit passes share the bits evenly (13 bits: 7 + 6, not 8 + 5): a
+    // block's elements land in one run per digit present, and with 2^8
+    // digits over a block of 2048 those runs average 8 elements, too short
+    // for whole-line writes
+    const int n_pass = wide ? 1 : (key_bits + 7) / 8;
+    const int step = wide ? key_bits : (key_bits + n_pass - 1) / n_pass;
     const bool want_off = digit_off && off_written && wide && n_seg >= 0 && n_seg <= radix;
     for (int shift = 0; shift < key_bits && st == GS_OK; shift += step) {
         const int bits = std::min(step, key_bits - shift);
