@@ -142,11 +142,14 @@ static bool handle_ok(const gs_ctx* ctx, const void* h, uint32_t magic)
 
 static void destroy_handle(gs_ctx* ctx, GsHandle* h)
 {
-    // the second stream may still write a projection's rect_d
+    // the other streams may still write a projection's rect_d and tile counts
     if (h->magic == kMagicProj && static_cast<gs_proj*>(h)->rect_d_pending)
         (void)hipStreamWaitEvent(ctx->stream, ctx->ev_rectd, 0);
+    if (h->magic == kMagicProj && static_cast<gs_proj*>(h)->tile_cnt_pending)
+        (void)hipStreamWaitEvent(ctx->stream, ctx->ev_counts, 0);
     gs_free_all(ctx, &h->allocs);
     if (h->magic == kMagicProj) {
+        gs_free_all(ctx, &static_cast<gs_proj*>(h)->deferred);
         gs_free_all(ctx, &static_cast<gs_proj*>(h)->plan_allocs);
         gs_free_all(ctx, &static_cast<gs_proj*>(h)->plan_retired);
     }
@@ -193,14 +196,16 @@ static gs_status check_params(gs_ctx* ctx, const gs_params* p)
     return GS_OK;
 }
 
-// A projection's rect_d is written on the second stream after the depth
-// sort, beside the per-tile counts and the plan; the first reader on
-// ctx->stream waits for it there (later readers are ordered after it).
+// A projection's depth order and rect_d are written on the second stream,
+// beside the per-tile counts and the plan; the first reader of either on
+// ctx->stream waits for them there (later readers are ordered after it),
+// and the sort's buffers are released after that wait.
 static gs_status rect_d_ready(gs_ctx* ctx, const gs_proj* proj)
 {
     if (!proj->rect_d_pending) return GS_OK;
     GS_HIP(ctx, hipStreamWaitEvent(ctx->stream, ctx->ev_rectd, 0));
     proj->rect_d_pending = false;
+    gs_free_all(ctx, &proj->deferred);
     return GS_OK;
 }
 
@@ -209,7 +214,13 @@ static gs_status rect_d_ready(gs_ctx* ctx, const gs_proj* proj)
 // Candidates per tile of the whole grid, made once per projection.
 static gs_status ensure_tile_counts(gs_ctx* ctx, gs_proj* proj)
 {
-    if (proj->tile_cnt) return GS_OK;
+    if (proj->tile_cnt) {
+        if (proj->tile_cnt_pending) {
+            GS_HIP(ctx, hipStreamWaitEvent(ctx->stream, ctx->ev_counts, 0));
+            proj->tile_cnt_pending = false;
+        }
+        return GS_OK;
+    }
     int32_t* g = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * (int64_t)proj->TW * proj->TH, GS_MEM_PROJ, &proj->allocs);
     if (!g) return GS_ERR_OOM;
     const gs_status st = launch_tile_counts(ctx, proj, g);
@@ -218,6 +229,34 @@ static gs_status ensure_tile_counts(gs_ctx* ctx, gs_proj* proj)
         return st;
     }
     proj->tile_cnt = g;
+    return GS_OK;
+}
+
+// The per-tile counts of a projection on render stream 0 (idle outside a
+// view's rasters), launched by a plan that does not price intersections
+// once its own kernels are queued, so that they run beside the plan's
+// read-back and the leaf groups: only the leaves' tile offsets (and a plan
+// that prices intersections) read them, through ensure_tile_counts, which
+// makes ctx->stream wait for them.
+static gs_status tile_counts_beside(gs_ctx* ctx, gs_proj* proj)
+{
+    int32_t* g = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * (int64_t)proj->TW * proj->TH, GS_MEM_PROJ, &proj->allocs);
+    if (!g) return GS_ERR_OOM;
+    GS_HIP(ctx, hipEventRecord(ctx->ev_alloc, ctx->stream));
+    GS_HIP(ctx, hipStreamWaitEvent(ctx->rstream[0], ctx->ev_alloc, 0));
+    hipStream_t main = ctx->stream;
+    ctx->stream = ctx->rstream[0];
+    gs_status st = launch_tile_counts(ctx, proj, g);
+    ctx->stream = main;
+    // the grid is attached even on failure, so that its release waits
+    proj->tile_cnt = g;
+    if (st == GS_OK && hipEventRecord(ctx->ev_counts, ctx->rstream[0]) != hipSuccess)
+        st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+    if (st != GS_OK) {
+        (void)hipStreamSynchronize(ctx->rstream[0]);
+        return st;
+    }
+    proj->tile_cnt_pending = true;
     return GS_OK;
 }
 
@@ -301,6 +340,8 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, goff, k0, v0)) != GS_OK) goto out;
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
     if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, 0xFFFFFFFFu, segoff)) != GS_OK) goto out;
+    // the leaves' tile offsets read the per-tile counts
+    if ((st = ensure_tile_counts(ctx, proj)) != GS_OK) goto out;
     if ((st = launch_plan_offsets(ctx, proj, ldev, plan.data(), nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0,
                                   segoff, ccnt, coff, lcells, lisect, dtbase, toff)) != GS_OK)
         goto out;
@@ -419,8 +460,8 @@ void gs_ctx_destroy(gs_ctx* ctx)
         (void)hipStreamDestroy(ctx->side);
     }
     if (ctx->ev_alloc) (void)hipEventDestroy(ctx->ev_alloc);
-    if (ctx->ev_order) (void)hipEventDestroy(ctx->ev_order);
     if (ctx->ev_rectd) (void)hipEventDestroy(ctx->ev_rectd);
+    if (ctx->ev_counts) (void)hipEventDestroy(ctx->ev_counts);
     for (hipEvent_t e : ctx->ev_done)
         if (e) (void)hipEventDestroy(e);
     for (int k = 0; k < 2; ++k) {
@@ -595,24 +636,31 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
     if ((st = launch_project_write(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
     {
         // candidates in (depth, slot) order: stable radix sort of the depth
-        // bits over slots in ascending order.  It runs on the second stream
-        // while this one counts the candidates of each tile (which planning
-        // and the binning of an unplanned leaf read); this stream then waits
-        // for the sort, so the projection is complete in its order.  With
-        // every kernel timed, both stay on this stream.
+        // bits over slots in ascending order, then the rectangles in that
+        // order (rect_d).  Both run on the second stream while this stream
+        // goes on (a view plans its leaves meanwhile); readers of the order
+        // and of rect_d wait for the second stream first (rect_d_ready), and
+        // the sort's buffers are released after that wait.  With every
+        // kernel timed, all of it runs on this stream.
         const int64_t nc = std::max<int64_t>(cnt, 1);
-        uint32_t* k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &tmp);
-        uint32_t* k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &tmp);
+        std::vector<GsAlloc> sortbuf;   // the sort's keys and its spare value buffer
+        uint32_t* k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &sortbuf);
+        uint32_t* k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &sortbuf);
         uint32_t* v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
         uint32_t* v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
         p->rect_d = (uint2*)gs_malloc(ctx, sizeof(uint2) * nc, GS_MEM_PROJ, &p->allocs);
         bool second = false;
-        if (!k0 || !k1 || !v0 || !v1 || !p->rect_d) { st = GS_ERR_OOM; goto fail; }
+        if (!k0 || !k1 || !v0 || !v1 || !p->rect_d) {
+            gs_free_all(ctx, &sortbuf);
+            st = GS_ERR_OOM;
+            goto fail;
+        }
         const bool beside = !(ctx->timing && ctx->timing_only.empty()) && ensure_side(ctx) == GS_OK;
         hipStream_t main = ctx->stream;
         if (beside) {
             if (hipEventRecord(ctx->ev_alloc, main) != hipSuccess ||
                 hipStreamWaitEvent(ctx->side, ctx->ev_alloc, 0) != hipSuccess) {
+                gs_free_all(ctx, &sortbuf);
                 st = gs_fail(ctx, GS_ERR_DEVICE, "stream ordering failed");
                 goto fail;
             }
@@ -621,26 +669,28 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
         }
         st = launch_depth_pairs(ctx, p, k0, v0);
         if (st == GS_OK) st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)cnt, 32, &second);
-        if (beside && st == GS_OK && hipEventRecord(ctx->ev_order, ctx->side) != hipSuccess)
-            st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
-        // the rectangles in that order, for the passes over the depth order;
-        // this stream waits for them only where they are first read
         if (st == GS_OK) st = launch_rect_depth(ctx, p, second ? v1 : v0, p->rect_d);
-        if (beside && st == GS_OK) {
-            if (hipEventRecord(ctx->ev_rectd, ctx->side) != hipSuccess)
-                st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
-            else
-                p->rect_d_pending = true;
-        }
         ctx->stream = main;
-        if (st != GS_OK) goto fail;
-        if ((st = ensure_tile_counts(ctx, p)) != GS_OK) goto fail;
-        if (beside && hipStreamWaitEvent(main, ctx->ev_order, 0) != hipSuccess) {
-            st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
-            goto fail;
-        }
-        gs_free_one(ctx, &p->allocs, second ? v0 : v1);
+        if (beside && st == GS_OK && hipEventRecord(ctx->ev_rectd, ctx->side) != hipSuccess)
+            st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+        // the spare value buffer joins the sort's keys
+        for (size_t k = 0; k < p->allocs.size(); ++k)
+            if (p->allocs[k].ptr == (second ? (void*)v0 : (void*)v1)) {
+                sortbuf.push_back(p->allocs[k]);
+                p->allocs.erase(p->allocs.begin() + (long)k);
+                break;
+            }
         p->order = second ? v1 : v0;
+        if (beside) {
+            p->deferred.swap(sortbuf);   // released by rect_d_ready or with the projection
+            p->rect_d_pending = st == GS_OK;
+        } else {
+            gs_free_all(ctx, &sortbuf);
+        }
+        if (st != GS_OK) goto fail;
+        // the per-tile counts: with the streams in use, launched by the
+        // first plan (beside it) or made on first use
+        if (!beside && (st = ensure_tile_counts(ctx, p)) != GS_OK) goto fail;
     }
     gs_free_all(ctx, &tmp);
     *out = p;
@@ -697,9 +747,12 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
             if (!cover[t]) return gs_fail(ctx, GS_ERR_INVALID_ARG, "cached leaves leave tile %zu uncovered", t);
     }
     std::vector<GsAlloc> tmp;
-    if ((st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) return st;
-    uint64_t* sat = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (proj->TW + 1) * (int64_t)(proj->TH + 1),
-                                         GS_MEM_SCRATCH, &tmp);
+    // the tile counts only when the model prices intersections
+    const bool priced = cm.b_isect != 0;
+    if (priced && (st = ensure_tile_counts(ctx, const_cast<gs_proj*>(proj))) != GS_OK) return st;
+    uint64_t* sat = priced ? (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (proj->TW + 1) * (int64_t)(proj->TH + 1),
+                                                  GS_MEM_SCRATCH, &tmp)
+                           : nullptr;
     // the leaf count and the over-budget flag (64 bytes), then the leaves:
     // read back together, the first kFirst leaves with the count
     constexpr int32_t kFirst = 128;
@@ -710,7 +763,7 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
     int32_t hv[2] = {0, 0};
     std::vector<unsigned char> hblk(64 + sizeof(gs_leaf) * (size_t)std::min(cap, kFirst));
     std::vector<gs_leaf> hleaves;
-    if (!sat || !blk || (n_roots > 0 && !rdev)) {
+    if ((priced && !sat) || !blk || (n_roots > 0 && !rdev)) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
     }
@@ -725,6 +778,8 @@ static gs_status plan_impl(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pro
     // grid's intersections and (candidate, super-cell) pairs
     st = launch_plan(ctx, proj, sat, budget_bytes, &cm, rdev, n_roots, ldev, cap, small, small + 1,
                      (uint64_t*)(blk + 8));
+    if (st == GS_OK && !proj->tile_cnt && !(ctx->timing && ctx->timing_only.empty()) && ensure_side(ctx) == GS_OK)
+        st = tile_counts_beside(ctx, const_cast<gs_proj*>(proj));
     if (st == GS_OK) {
         hipError_t e = hipMemcpyAsync(hblk.data(), blk, hblk.size(), hipMemcpyDeviceToHost, ctx->stream);
         if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
@@ -869,8 +924,8 @@ static gs_status ensure_side(gs_ctx* ctx)
     if (ctx->side) return GS_OK;
     GS_HIP(ctx, hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_alloc, hipEventDisableTiming));
-    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_order, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_rectd, hipEventDisableTiming));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_counts, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[0], hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[1], hipEventDisableTiming));
     for (int k = 0; k < 2; ++k) {

@@ -45,8 +45,8 @@ struct gs_ctx {
     // bins the next leaf while the current one is rendered, and its events
     hipStream_t side = nullptr;
     hipEvent_t ev_alloc = nullptr, ev_done[2] = {nullptr, nullptr};
-    hipEvent_t ev_order = nullptr;   // the depth sort of a projection done (on the second stream)
-    hipEvent_t ev_rectd = nullptr;   // its depth-ordered rectangles written (on the second stream)
+    hipEvent_t ev_rectd = nullptr;   // a projection's depth order and rect_d written (on the second stream)
+    hipEvent_t ev_counts = nullptr;  // its per-tile counts made (on render stream 0)
     // two render streams: consecutive leaves' fused rasters overlap, the
     // next one filling the compute units the current one's last tiles leave
     hipStream_t rstream[2] = {nullptr, nullptr};
@@ -76,8 +76,10 @@ struct gs_proj : GsHandle {
     int32_t* slot_of = nullptr;   // [n] slot or -1
     uint32_t* order = nullptr;    // [n_cand] slots sorted by (depth, slot)
     uint2* rect_d = nullptr;      // [n_cand] rect of order[k] at k, packed (gsd::rect_pack)
-    mutable bool rect_d_pending = false;   // rect_d written on the second stream: wait for ctx->ev_rectd
+    mutable bool rect_d_pending = false;   // order, rect_d written on the second stream: wait for ctx->ev_rectd
+    mutable std::vector<GsAlloc> deferred;  // the depth sort's buffers, released after that wait
     int32_t* tile_cnt = nullptr;  // [TH][TW] candidates per tile (made on first use)
+    mutable bool tile_cnt_pending = false;   // tile_cnt made on render stream 0: wait for ctx->ev_counts
     // leaf plan of the view (set by gs_plan_leaves): the candidates whose
     // rectangle meets each leaf, so that binning a leaf visits only those
     std::vector<gs_leaf> plan;
@@ -264,7 +266,8 @@ gs_status launch_raster_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_proj* pr
 // planner.hip
 // candidates per tile of the whole grid ([TH][TW], from the rectangles)
 gs_status launch_tile_counts(gs_ctx* ctx, const gs_proj* proj, int32_t* grid);
-// leaf plan from proj->tile_cnt
+// leaf plan; sat: scratch for the table of proj->tile_cnt, which must be
+// there when cost->b_isect != 0 (else NULL: the tile counts are not read)
 gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t budget, const gs_cost_model* cost,
                       const gs_leaf* roots_dev, int32_t n_roots, gs_leaf* leaves_dev, int32_t max_leaves,
                       int32_t* count_dev, int32_t* over_dev, uint64_t* totals_dev = nullptr);

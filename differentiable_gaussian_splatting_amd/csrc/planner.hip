@@ -36,8 +36,9 @@ __global__ void k_counts_to_sat(const int32_t* __restrict__ cnt, int TW, int TH,
 struct PlanArgs {
     int W, H, TW, TH, SW;
     uint64_t budget, bI, bP, bT, b0, bC;
-    const uint64_t* sat;     // (TH + 1) x (TW + 1), tile counts
+    const uint64_t* sat;     // (TH + 1) x (TW + 1), tile counts (NULL when bI = 0)
     const uint64_t* sat8;    // (SH + 1) x (SW + 1), super-cell counts
+    const uint64_t* isum;    // the whole grid's intersections (when sat is NULL)
 };
 
 __device__ __forceinline__ uint64_t sat_rect(const uint64_t* __restrict__ sat, int64_t S, int x0, int y0, int x1,
@@ -49,7 +50,7 @@ __device__ __forceinline__ uint64_t sat_rect(const uint64_t* __restrict__ sat, i
 
 __device__ __forceinline__ uint64_t region_est(const PlanArgs& a, int4 r)
 {
-    const uint64_t I = sat_rect(a.sat, a.TW + 1, r.x, r.y, r.z, r.w);
+    const uint64_t I = a.bI ? sat_rect(a.sat, a.TW + 1, r.x, r.y, r.z, r.w) : 0ull;
     const uint64_t Cb = sat_rect(a.sat8, a.SW + 1, r.x >> 3, r.y >> 3, ((r.z - 1) >> 3) + 1, ((r.w - 1) >> 3) + 1);
     const int64_t x1 = min<int64_t>((int64_t)r.z * 16, a.W), y1 = min<int64_t>((int64_t)r.w * 16, a.H);
     const uint64_t P = (uint64_t)(x1 - (int64_t)r.x * 16) * (uint64_t)(y1 - (int64_t)r.y * 16);
@@ -67,12 +68,16 @@ __device__ __forceinline__ bool region_split(const PlanArgs& a, int4 r)
 // [SH][SW] grid (add its 2D prefix for the counts).  A block takes
 // kCellBlock candidates into an LDS copy of the grid, then adds its nonzero
 // cells to the global grid: far fewer global atomics on the few cells.
+// isum (optional): the candidates' tile rectangle areas are added to it (the
+// grid's intersections, one atomic per block).
 constexpr int kCellBlock = 8192;
 constexpr int kCellLds = 16384;    // cells of the LDS copy (64 KB)
 
 __global__ __launch_bounds__(256) void k_cell_diff(int64_t n, const int4* __restrict__ rect, int SW, int SH,
-                                                   int32_t* __restrict__ diff)
+                                                   int32_t* __restrict__ diff, unsigned long long* __restrict__ isum)
 {
+    __shared__ uint64_t ws[4];
+    uint64_t area = 0;
     extern __shared__ int32_t hd[];
     const int64_t cells = (int64_t)SW * SH;
     const bool lds = cells <= kCellLds;
@@ -84,6 +89,7 @@ __global__ __launch_bounds__(256) void k_cell_diff(int64_t n, const int4* __rest
     for (int64_t k = c0 + threadIdx.x; k < min<int64_t>(n, c0 + kCellBlock); k += blockDim.x) {
         const int4 r = rect[k];
         if (!(r.x < r.z && r.y < r.w)) continue;
+        area += (uint64_t)(r.z - r.x) * (uint64_t)(r.w - r.y);
         const int x0 = r.x >> 3, y0 = r.y >> 3, x1 = ((r.z - 1) >> 3) + 1, y1 = ((r.w - 1) >> 3) + 1;
         auto add = [&](int y, int x, int v) {
             if (lds) atomicAdd(&hd[(int64_t)y * SW + x], v);
@@ -98,6 +104,12 @@ __global__ __launch_bounds__(256) void k_cell_diff(int64_t n, const int4* __rest
         __syncthreads();
         for (int64_t k = threadIdx.x; k < cells; k += blockDim.x)
             if (hd[k]) atomicAdd(&diff[k], hd[k]);
+    }
+    if (isum) {
+        area = gsd::wave_sum_u64(area);
+        if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = area;
+        __syncthreads();
+        if (threadIdx.x == 0) atomicAdd(isum, (unsigned long long)(ws[0] + ws[1] + ws[2] + ws[3]));
     }
 }
 
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a,
     __shared__ uint32_t s_total, s_any;
     // the whole grid's intersections and (candidate, super-cell) pairs
     if (totals_out && threadIdx.x == 0) {
-        totals_out[0] = sat_rect(a.sat, a.TW + 1, 0, 0, a.TW, a.TH);
+        totals_out[0] = a.sat ? sat_rect(a.sat, a.TW + 1, 0, 0, a.TW, a.TH) : *a.isum;
         totals_out[1] = sat_rect(a.sat8, a.SW + 1, 0, 0, a.SW, (a.TH + 7) >> 3);
     }
     int4* cur = fa;
@@ -232,20 +244,31 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
     const int TW = proj->TW, TH = proj->TH;
     const int SW = (TW + 7) >> 3, SH = (TH + 7) >> 3;
     const int64_t T = (int64_t)TW * TH;
-    const int32_t* diff = proj->tile_cnt;
-    const int64_t S = (int64_t)(TW + 1) * (TH + 1);
-    hipLaunchKernelGGL(k_counts_to_sat, dim3((unsigned)ceil_div(S, 256)), dim3(256), 0, ctx->stream, diff, TW, TH, sat);
-    gs_status st = launch_prefix2d_u64(ctx, sat, TH + 1, TW + 1);
-    if (st != GS_OK) return st;
+    // the tile counts' table only when the model prices intersections (sat
+    // given); otherwise the grid's total comes from the super-cell pass
+    gs_status st = GS_OK;
+    if (sat) {
+        const int64_t S = (int64_t)(TW + 1) * (TH + 1);
+        hipLaunchKernelGGL(k_counts_to_sat, dim3((unsigned)ceil_div(S, 256)), dim3(256), 0, ctx->stream,
+                           proj->tile_cnt, TW, TH, sat);
+        if ((st = launch_prefix2d_u64(ctx, sat, TH + 1, TW + 1)) != GS_OK) return st;
+    } else if (cost->b_isect != 0) {
+        return gs_fail(ctx, GS_ERR_STATE, "the cost model prices intersections: the tile counts are needed");
+    }
 
     std::vector<GsAlloc> tmp;
     int4* fa = (int4*)gs_malloc(ctx, sizeof(int4) * T, GS_MEM_SCRATCH, &tmp);
     int4* fb = (int4*)gs_malloc(ctx, sizeof(int4) * T, GS_MEM_SCRATCH, &tmp);
     int32_t* cgrid = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * SW * SH, GS_MEM_SCRATCH, &tmp);
     uint64_t* sat8 = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (SW + 1) * (SH + 1), GS_MEM_SCRATCH, &tmp);
-    if (!fa || !fb || !cgrid || !sat8) {
+    uint64_t* isum = sat ? nullptr : (uint64_t*)gs_malloc(ctx, sizeof(uint64_t), GS_MEM_SCRATCH, &tmp);
+    if (!fa || !fb || !cgrid || !sat8 || (!sat && !isum)) {
         gs_free_all(ctx, &tmp);
         return GS_ERR_OOM;
+    }
+    if (isum && (st = launch_fill_u32(ctx, (uint32_t*)isum, 0u, 2)) != GS_OK) {
+        gs_free_all(ctx, &tmp);
+        return st;
     }
     // candidates per image-aligned super-cell of 8 x 8 tiles, and their table
     if ((st = launch_fill_u32(ctx, (uint32_t*)cgrid, 0u, (int64_t)SW * SH)) != GS_OK) {
@@ -256,7 +279,7 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
         GsTimerScope ts(ctx, "rect_diff");
         const size_t lds = (int64_t)SW * SH <= kCellLds ? sizeof(int32_t) * SW * SH : 0;
         hipLaunchKernelGGL(k_cell_diff, dim3((unsigned)ceil_div(proj->n_cand, kCellBlock)), dim3(256), lds,
-                           ctx->stream, proj->n_cand, proj->rect, SW, SH, cgrid);
+                           ctx->stream, proj->n_cand, proj->rect, SW, SH, cgrid, (unsigned long long*)isum);
     }
     if ((st = launch_prefix2d_i32(ctx, cgrid, SH, SW)) != GS_OK) {
         gs_free_all(ctx, &tmp);
@@ -275,6 +298,7 @@ gs_status launch_plan(gs_ctx* ctx, const gs_proj* proj, uint64_t* sat, uint64_t 
     a.bI = cost->b_isect; a.bP = cost->b_pixel; a.bT = cost->b_tile; a.b0 = cost->b_const; a.bC = cost->b_cell;
     a.sat = sat;
     a.sat8 = sat8;
+    a.isum = isum;
     GS_HIP(ctx, hipMemsetAsync(over_dev, 0, sizeof(int32_t), ctx->stream));
     {
         GsTimerScope ts(ctx, "plan_split");
