@@ -60,7 +60,9 @@ __device__ __forceinline__ float exp_cw_core(float x)
 //   t = fma(x, log2 e, 1.5 2^23)   (the sum's ulp is 1: t - 1.5 2^23 is x log2 e
 //                                  rounded to the nearest integer k, ties to even)
 //   r = fma(-k, ln2, x)            (one f32 ln 2: |k (ln2 - ln2_f32)| < 2e-8)
-//   e^r by the degree-7 Taylor polynomial (Horner, fma)
+//   e^r = 1 + r + r^2 (c2 + c3 r + ... + c6 r^4) (Horner, fma), the degree-6
+//         polynomial with the least maximum relative error on |r| <= ln2 / 2
+//         (4.9e-9 with the f32 coefficients below, under a tenth of an ulp)
 //   result = p 2^k, formed by adding k to p's exponent field: the low 9 bits of
 //   t's pattern above the significand are those of 1.5 2^23, so (bits(t) << 23)
 //   is k << 23 modulo 2^32, and p 2^k stays normal.
@@ -69,17 +71,21 @@ __device__ __forceinline__ float exp_cw_core(float x)
 // unclamped: lanes outside the range skip the entry, so their value is unused.
 constexpr float kLn2F = 0.693147180559945309417232121458f;
 constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
+constexpr float kFall2 = __builtin_bit_cast(float, 0x3efffffeu);   // 0.49999994
+constexpr float kFall3 = __builtin_bit_cast(float, 0x3e2aaa2du);   // 0.16666479
+constexpr float kFall4 = __builtin_bit_cast(float, 0x3d2aabbeu);   // 0.041667692
+constexpr float kFall5 = __builtin_bit_cast(float, 0x3c092e32u);   // 0.0083728302
+constexpr float kFall6 = __builtin_bit_cast(float, 0x3ab5dcf3u);   // 0.0013875052
 __device__ __forceinline__ float exp_falloff_core(float x)
 {
     const float t = __builtin_fmaf(x, kLog2e, kRoundMagic);
     const float k = t - kRoundMagic;
     const float r = __builtin_fmaf(-k, kLn2F, x);
-    float p = kInvFact7;
-    p = __builtin_fmaf(p, r, kInvFact6);
-    p = __builtin_fmaf(p, r, kInvFact5);
-    p = __builtin_fmaf(p, r, kInvFact4);
-    p = __builtin_fmaf(p, r, kInvFact3);
-    p = __builtin_fmaf(p, r, kInvFact2);
+    float p = kFall6;
+    p = __builtin_fmaf(p, r, kFall5);
+    p = __builtin_fmaf(p, r, kFall4);
+    p = __builtin_fmaf(p, r, kFall3);
+    p = __builtin_fmaf(p, r, kFall2);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
     return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, t) << 23) + __builtin_bit_cast(uint32_t, p));

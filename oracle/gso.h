@@ -84,7 +84,7 @@ typedef struct {          /* leaf load model: bytes = bI*I + bP*P + bT*T + b0 + 
 float gso_exp_cw(float x);
 void  gso_exp_cw_array(const float* x, float* y, int64_t n);
 /* exp of the Gaussian falloff in alpha (f32 pass of the rasterizer): the
- * argument clamped into [-6, 0], one-constant reduction, degree-7 Taylor */
+ * argument clamped into [-6, 0], one-constant reduction, degree-6 minimax */
 float gso_exp_falloff(float x);
 void  gso_exp_falloff_array(const float* x, float* y, int64_t n);
 /* real orthonormal SH basis (no Condon-Shortley phase), order l then m=-l..l */
