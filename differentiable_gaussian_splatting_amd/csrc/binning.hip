@@ -617,13 +617,18 @@ __global__ __launch_bounds__(256) void k_seg_offsets(const uint32_t* __restrict_
     }
 }
 
-__global__ __launch_bounds__(256) void k_depth_pairs(int64_t n, const float4* __restrict__ g2,
-                                                     uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
+// the depth sort's input, from the flag pass: candidate i goes to its slot
+// with its depth bits (depth > 0: the bits order like the values)
+__global__ __launch_bounds__(256) void k_depth_pairs(int64_t n, const uint32_t* __restrict__ flag,
+                                                     const uint32_t* __restrict__ slot,
+                                                     const uint32_t* __restrict__ dkey, uint32_t* __restrict__ keys,
+                                                     uint32_t* __restrict__ vals)
 {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= n) return;
-    keys[j] = __builtin_bit_cast(uint32_t, g2[j].y);   // depth > 0: the bits order like the values
-    vals[j] = (uint32_t)j;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n || !flag[i]) return;
+    const uint32_t s = slot[i];
+    keys[s] = dkey[i];
+    vals[s] = s;
 }
 
 // the rectangles in depth order, packed: what the per-leaf passes over the
@@ -811,11 +816,12 @@ gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n
     return GS_OK;
 }
 
-gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals)
+gs_status launch_depth_pairs(gs_ctx* ctx, int64_t n, const uint32_t* flag, const uint32_t* slot, const uint32_t* dkey,
+                             uint32_t* keys, uint32_t* vals)
 {
-    if (proj->n_cand > 0)
-        hipLaunchKernelGGL(k_depth_pairs, dim3((unsigned)ceil_div(proj->n_cand, 256)), dim3(256), 0, ctx->stream,
-                           proj->n_cand, proj->g2, keys, vals);
+    if (n > 0)
+        hipLaunchKernelGGL(k_depth_pairs, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, n, flag, slot,
+                           dkey, keys, vals);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

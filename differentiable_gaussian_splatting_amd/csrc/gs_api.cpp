@@ -462,6 +462,7 @@ void gs_ctx_destroy(gs_ctx* ctx)
     if (ctx->ev_alloc) (void)hipEventDestroy(ctx->ev_alloc);
     if (ctx->ev_rectd) (void)hipEventDestroy(ctx->ev_rectd);
     if (ctx->ev_counts) (void)hipEventDestroy(ctx->ev_counts);
+    if (ctx->ev_written) (void)hipEventDestroy(ctx->ev_written);
     for (hipEvent_t e : ctx->ev_done)
         if (e) (void)hipEventDestroy(e);
     for (int k = 0; k < 2; ++k) {
@@ -614,13 +615,22 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
     p->TW = (cam->width + 15) / 16;
     p->TH = (cam->height + 15) / 16;
     std::vector<GsAlloc> tmp;
+    // flags, slots and depth keys of all N Gaussians, and the depth sort's
+    // keys and spare value buffer: the second stream reads them, so with it
+    // in use they are released by rect_d_ready (or with the projection)
+    std::vector<GsAlloc> sortbuf;
     bool side_used = false;
+    bool second = false;
     const int64_t n = params->n;
-    uint32_t* flag = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n, 1), GS_MEM_SCRATCH, &tmp);
-    uint32_t* slot = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n + 1), GS_MEM_SCRATCH, &tmp);
+    const bool beside = !(ctx->timing && ctx->timing_only.empty()) && ensure_side(ctx) == GS_OK;
+    hipStream_t main = ctx->stream;
+    uint32_t* flag = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n, 1), GS_MEM_SCRATCH, &sortbuf);
+    uint32_t* slot = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (n + 1), GS_MEM_SCRATCH, &sortbuf);
+    uint32_t* dkey = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(n, 1), GS_MEM_SCRATCH, &sortbuf);
+    uint32_t *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
     uint32_t cnt = 0;
-    if (!flag || !slot) { st = GS_ERR_OOM; goto fail; }
-    if ((st = launch_project(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
+    if (!flag || !slot || !dkey) { st = GS_ERR_OOM; goto fail; }
+    if ((st = launch_project(ctx, cam, params, p, flag, slot, dkey)) != GS_OK) goto fail;
     if ((st = readback(ctx, slot + n, sizeof(uint32_t), &cnt)) != GS_OK) goto fail;
     p->n_cand = cnt;
     {
@@ -631,66 +641,64 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
         p->g1 = (float4*)gs_malloc(ctx, sizeof(float4) * nc, GS_MEM_PROJ, &p->allocs);
         p->g2 = (float4*)gs_malloc(ctx, sizeof(float4) * nc, GS_MEM_PROJ, &p->allocs);
         p->slot_of = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * std::max<int64_t>(n, 1), GS_MEM_PROJ, &p->allocs);
-        if (!p->ids || !p->rect || !p->g0 || !p->g1 || !p->g2 || !p->slot_of) { st = GS_ERR_OOM; goto fail; }
-    }
-    if ((st = launch_project_write(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
-    {
-        // candidates in (depth, slot) order: stable radix sort of the depth
-        // bits over slots in ascending order, then the rectangles in that
-        // order (rect_d).  Both run on the second stream while this stream
-        // goes on (a view plans its leaves meanwhile); readers of the order
-        // and of rect_d wait for the second stream first (rect_d_ready), and
-        // the sort's buffers are released after that wait.  With every
-        // kernel timed, all of it runs on this stream.
-        const int64_t nc = std::max<int64_t>(cnt, 1);
-        std::vector<GsAlloc> sortbuf;   // the sort's keys and its spare value buffer
-        uint32_t* k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &sortbuf);
-        uint32_t* k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &sortbuf);
-        uint32_t* v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
-        uint32_t* v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
+        k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &sortbuf);
+        k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_SCRATCH, &sortbuf);
+        v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
+        v1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_PROJ, &p->allocs);
         p->rect_d = (uint2*)gs_malloc(ctx, sizeof(uint2) * nc, GS_MEM_PROJ, &p->allocs);
-        bool second = false;
-        if (!k0 || !k1 || !v0 || !v1 || !p->rect_d) {
-            gs_free_all(ctx, &sortbuf);
+        if (!p->ids || !p->rect || !p->g0 || !p->g1 || !p->g2 || !p->slot_of || !k0 || !k1 || !v0 || !v1 ||
+            !p->rect_d) {
             st = GS_ERR_OOM;
             goto fail;
         }
-        const bool beside = !(ctx->timing && ctx->timing_only.empty()) && ensure_side(ctx) == GS_OK;
-        hipStream_t main = ctx->stream;
-        if (beside) {
-            if (hipEventRecord(ctx->ev_alloc, main) != hipSuccess ||
-                hipStreamWaitEvent(ctx->side, ctx->ev_alloc, 0) != hipSuccess) {
-                gs_free_all(ctx, &sortbuf);
-                st = gs_fail(ctx, GS_ERR_DEVICE, "stream ordering failed");
-                goto fail;
-            }
-            ctx->stream = ctx->side;
-            side_used = true;
+    }
+    // Candidates in (depth, slot) order: a stable radix sort of the depth
+    // bits (kept per Gaussian by the flag pass) over slots in ascending
+    // order, on the second stream while this one writes the compact state
+    // (queued first, so that it runs while the host queues the sort); then,
+    // once that is written, the rectangles in that order (rect_d).  This
+    // stream goes on (a view plans its leaves meanwhile); readers of the
+    // order and of rect_d wait for the second stream first (rect_d_ready).
+    // With every kernel timed, all of it runs on this stream.
+    if (beside && hipEventRecord(ctx->ev_alloc, main) != hipSuccess) {
+        st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+        goto fail;
+    }
+    if ((st = launch_project_write(ctx, cam, params, p, flag, slot)) != GS_OK) goto fail;
+    if (beside) {
+        if (hipEventRecord(ctx->ev_written, main) != hipSuccess ||
+            hipStreamWaitEvent(ctx->side, ctx->ev_alloc, 0) != hipSuccess) {
+            st = gs_fail(ctx, GS_ERR_DEVICE, "stream ordering failed");
+            goto fail;
         }
-        st = launch_depth_pairs(ctx, p, k0, v0);
-        if (st == GS_OK) st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)cnt, 32, &second);
-        if (st == GS_OK) st = launch_rect_depth(ctx, p, second ? v1 : v0, p->rect_d);
-        ctx->stream = main;
-        if (beside && st == GS_OK && hipEventRecord(ctx->ev_rectd, ctx->side) != hipSuccess)
-            st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
-        // the spare value buffer joins the sort's keys
-        for (size_t k = 0; k < p->allocs.size(); ++k)
-            if (p->allocs[k].ptr == (second ? (void*)v0 : (void*)v1)) {
-                sortbuf.push_back(p->allocs[k]);
-                p->allocs.erase(p->allocs.begin() + (long)k);
-                break;
-            }
-        p->order = second ? v1 : v0;
-        if (beside) {
-            p->deferred.swap(sortbuf);   // released by rect_d_ready or with the projection
-            p->rect_d_pending = st == GS_OK;
-        } else {
-            gs_free_all(ctx, &sortbuf);
+        ctx->stream = ctx->side;
+        side_used = true;
+    }
+    st = launch_depth_pairs(ctx, n, flag, slot, dkey, k0, v0);
+    if (st == GS_OK) st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)cnt, 32, &second);
+    if (st == GS_OK && beside && hipStreamWaitEvent(ctx->side, ctx->ev_written, 0) != hipSuccess)
+        st = gs_fail(ctx, GS_ERR_DEVICE, "stream ordering failed");
+    if (st == GS_OK) st = launch_rect_depth(ctx, p, second ? v1 : v0, p->rect_d);
+    ctx->stream = main;
+    if (beside && st == GS_OK && hipEventRecord(ctx->ev_rectd, ctx->side) != hipSuccess)
+        st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+    if (st != GS_OK) goto fail;
+    // the spare value buffer joins the sort's keys
+    for (size_t k = 0; k < p->allocs.size(); ++k)
+        if (p->allocs[k].ptr == (second ? (void*)v0 : (void*)v1)) {
+            sortbuf.push_back(p->allocs[k]);
+            p->allocs.erase(p->allocs.begin() + (long)k);
+            break;
         }
-        if (st != GS_OK) goto fail;
-        // the per-tile counts: with the streams in use, launched by the
-        // first plan (beside it) or made on first use
-        if (!beside && (st = ensure_tile_counts(ctx, p)) != GS_OK) goto fail;
+    p->order = second ? v1 : v0;
+    if (beside) {
+        p->deferred.swap(sortbuf);   // released by rect_d_ready or with the projection
+        p->rect_d_pending = true;
+    } else {
+        gs_free_all(ctx, &sortbuf);
+        // the per-tile counts (with the streams in use they are launched by
+        // the first plan, beside it, or made on first use)
+        if ((st = ensure_tile_counts(ctx, p)) != GS_OK) goto fail;
     }
     gs_free_all(ctx, &tmp);
     *out = p;
@@ -698,7 +706,9 @@ gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params,
     return GS_OK;
 fail:
     // nothing is released while the second stream may still use it
+    ctx->stream = main;
     if (side_used) (void)hipStreamSynchronize(ctx->side);
+    gs_free_all(ctx, &sortbuf);
     gs_free_all(ctx, &tmp);
     destroy_handle(ctx, p);
     return st;
@@ -926,6 +936,7 @@ static gs_status ensure_side(gs_ctx* ctx)
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_alloc, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_rectd, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_counts, hipEventDisableTiming));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_written, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[0], hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[1], hipEventDisableTiming));
     for (int k = 0; k < 2; ++k) {

@@ -47,6 +47,7 @@ struct gs_ctx {
     hipEvent_t ev_alloc = nullptr, ev_done[2] = {nullptr, nullptr};
     hipEvent_t ev_rectd = nullptr;   // a projection's depth order and rect_d written (on the second stream)
     hipEvent_t ev_counts = nullptr;  // its per-tile counts made (on render stream 0)
+    hipEvent_t ev_written = nullptr; // its compact state written (on the main stream)
     // two render streams: consecutive leaves' fused rasters overlap, the
     // next one filling the compute units the current one's last tiles leave
     hipStream_t rstream[2] = {nullptr, nullptr};
@@ -159,8 +160,10 @@ gs_status launch_prefix2d_i32(gs_ctx* ctx, int32_t* grid, int rows, int cols);
 gs_status launch_prefix2d_u64(gs_ctx* ctx, uint64_t* grid, int rows, int cols);
 
 // project.hip
+// flags and their exclusive scan (the slots) of all N Gaussians; dkey
+// (optional): their depth bits
 gs_status launch_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
-                         uint32_t* flag_scratch, uint32_t* slot_scratch);
+                         uint32_t* flag_scratch, uint32_t* slot_scratch, uint32_t* dkey = nullptr);
 // compact gradient rows of slots [s0, s1) into grad3d (row s - s0)
 gs_status launch_project_bwd(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, const gs_proj* proj,
                              const float* grad2d, int64_t s0, int64_t s1, float* grad3d);
@@ -214,7 +217,10 @@ gs_status launch_fine_write(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf,
                             const uint32_t* ioff, uint32_t* pos, uint64_t n_values, uint32_t* values);
 gs_status launch_seg_offsets(gs_ctx* ctx, const uint32_t* sorted_keys, int64_t n, int64_t n_seg, uint32_t kmask,
                              uint64_t* offsets);
-gs_status launch_depth_pairs(gs_ctx* ctx, const gs_proj* proj, uint32_t* keys, uint32_t* vals);
+// the depth sort's input over all n Gaussians: at each candidate's slot s,
+// (its depth bits, s)
+gs_status launch_depth_pairs(gs_ctx* ctx, int64_t n, const uint32_t* flag, const uint32_t* slot, const uint32_t* dkey,
+                             uint32_t* keys, uint32_t* vals);
 // rect_d[k] = the packed rectangle of slot order[k]
 gs_status launch_rect_depth(gs_ctx* ctx, const gs_proj* proj, const uint32_t* order, uint2* rect_d);
 gs_status launch_export_keys(gs_ctx* ctx, const gs_bins* bins, uint64_t* keys);

@@ -157,13 +157,18 @@ __device__ __forceinline__ Proj2D project_geom(const CamDev& cam, const GaussIn&
     return o;
 }
 
+// dkey (optional): each Gaussian's depth bits (the depth sort's key; the
+// same value the compact state's depth gets)
 __global__ __launch_bounds__(256) void k_project_flags(CamDev cam, int64_t n, const float* __restrict__ means,
                                                        const float* __restrict__ log_scales,
-                                                       const float* __restrict__ quats, uint32_t* __restrict__ flag)
+                                                       const float* __restrict__ quats, uint32_t* __restrict__ flag,
+                                                       uint32_t* __restrict__ dkey)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    flag[i] = project_geom(cam, load_gauss(means, log_scales, quats, i)).ok ? 1u : 0u;
+    const auto g = project_geom(cam, load_gauss(means, log_scales, quats, i));
+    flag[i] = g.ok ? 1u : 0u;
+    if (dkey) dkey[i] = __builtin_bit_cast(uint32_t, g.depth);
 }
 
 // Compact state of every candidate.  A wavefront covers 64 consecutive
@@ -660,14 +665,14 @@ __global__ void k_exp_falloff(int64_t n, const float* __restrict__ x, float* __r
 }  // namespace
 
 gs_status launch_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* p, gs_proj* proj,
-                         uint32_t* flag, uint32_t* slot)
+                         uint32_t* flag, uint32_t* slot, uint32_t* dkey)
 {
     const CamDev cd = make_cam(cam);
     const int64_t n = p->n;
     if (n > 0) {
         GsTimerScope ts(ctx, "project_flags");
         hipLaunchKernelGGL(k_project_flags, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, ctx->stream, cd, n,
-                           p->means, p->log_scales, p->quats, flag);
+                           p->means, p->log_scales, p->quats, flag, dkey);
     }
     GS_HIP(ctx, hipGetLastError());
     return launch_scan_u32_to_u32(ctx, flag, slot, n);
