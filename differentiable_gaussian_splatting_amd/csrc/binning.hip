@@ -276,12 +276,24 @@ __device__ __forceinline__ int wave_prefix_max(int v, int lane)
     return v;
 }
 
+// First candidate of every emission block (bst[b]: the candidate whose
+// outputs hold output b kEO), written by the candidates whose output ranges
+// cross a block start; every block start has exactly one such candidate.
+__global__ __launch_bounds__(256) void k_emit_starts(int64_t n, const uint32_t* __restrict__ eoff, uint32_t ebase,
+                                                     uint32_t* __restrict__ bst)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const uint64_t a = eoff[k] - ebase, b = eoff[k + 1] - ebase;
+    for (uint64_t m = (a + kEO - 1) / kEO; m * kEO < b; ++m) bst[m] = (uint32_t)k;
+}
+
 __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* __restrict__ list,
                                                     const uint32_t* __restrict__ order,
                                                     const uint2* __restrict__ rect_d, int ltx0, int lty0, int ltx1,
                                                     int lty1, int sh, int SW, const uint32_t* __restrict__ eoff,
-                                                    uint32_t ebase, uint32_t total, uint32_t* __restrict__ keys,
-                                                    uint32_t* __restrict__ vals)
+                                                    uint32_t ebase, uint32_t total, const uint32_t* __restrict__ bst,
+                                                    uint32_t* __restrict__ keys, uint32_t* __restrict__ vals)
 {
     __shared__ uint32_t se[kEO + 2];
     __shared__ uint32_t sj[kEO + 1];   // slot of each staged candidate
@@ -292,8 +304,9 @@ __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* _
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t ob = blockIdx.x * (uint32_t)kEO;
     const uint32_t oe = min(ob + (uint32_t)kEO, total);
-    // ---- first candidate: 256-ary search for the last k with eoff[k] - ebase <= ob
-    int64_t lo = 0, len = n;
+    // ---- first candidate: the last k with eoff[k] - ebase <= ob, from bst
+    // or by a 256-ary search
+    int64_t lo = bst ? (int64_t)bst[blockIdx.x] : 0, len = bst ? 1 : n;
     while (len > 1) {
         const int64_t st = (len + 255) / 256;
         const int64_t idx = lo + (int64_t)tid * st;
@@ -307,9 +320,12 @@ __global__ __launch_bounds__(256) void k_emit_pairs(int64_t n, const uint32_t* _
         len = min(st, lo + len - nlo);
         lo = nlo;
     }
-    if (tid == 0) s_lo = lo;
-    __syncthreads();
-    const int64_t k0 = s_lo;
+    if (!bst) {
+        if (tid == 0) s_lo = lo;
+        __syncthreads();
+        lo = s_lo;
+    }
+    const int64_t k0 = lo;
     const int nmax = (int)min<int64_t>(kEO + 1, n - k0);
     for (int i = tid; i <= nmax; i += 256) se[i] = eoff[k0 + i] - ebase;
     __syncthreads();
@@ -736,15 +752,20 @@ gs_status launch_leaf_counts(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf
     return GS_OK;
 }
 
+int64_t emit_blocks(uint64_t total) { return ceil_div((int64_t)total, kEO); }
+
 gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                             int64_t n_list, const uint32_t* eoff, uint32_t ebase, uint64_t total, uint32_t* keys,
-                            uint32_t* vals)
+                            uint32_t* vals, uint32_t* bst)
 {
     if (n_list > 0 && total > 0) {
         GsTimerScope ts(ctx, "emit");
-        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)ceil_div((int64_t)total, kEO)), dim3(256), 0, ctx->stream,
-                           n_list, list, proj->order, proj->rect_d, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift,
-                           super_cols(leaf), eoff, ebase, (uint32_t)total, keys, vals);
+        if (bst)
+            hipLaunchKernelGGL(k_emit_starts, dim3((unsigned)ceil_div(n_list, 256)), dim3(256), 0, ctx->stream, n_list,
+                               eoff, ebase, bst);
+        hipLaunchKernelGGL(k_emit_pairs, dim3((unsigned)emit_blocks(total)), dim3(256), 0, ctx->stream, n_list, list,
+                           proj->order, proj->rect_d, leaf.tx0, leaf.ty0, leaf.tx1, leaf.ty1, kSuperShift,
+                           super_cols(leaf), eoff, ebase, (uint32_t)total, bst, keys, vals);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;

@@ -915,8 +915,9 @@ static gs_status coarse_launch(gs_ctx* ctx, const gs_proj* proj, CoarseBins* cb)
 {
     gs_status st = rect_d_ready(ctx, proj);
     if (st != GS_OK) return st;
+    // the radix scratch (idle until the sort) holds the emission's block starts
     st = launch_emit_cells(ctx, proj, cb->leaf, cb->pl.list, cb->pl.n, cb->pl.eoff, cb->pl.ebase, cb->C,
-                                     cb->k0, cb->v0);
+                           cb->k0, cb->v0, cb->scratch);
     if (st != GS_OK) return st;
     bool have_soff = false;
     if ((st = launch_radix_sort(ctx, cb->k0, cb->v0, cb->k1, cb->v1, (int64_t)cb->C, bits_for(cb->n_super),
@@ -992,6 +993,7 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
     }
     uint32_t *cnt = nullptr, *lc = nullptr, *k0 = nullptr, *k1 = nullptr, *v0 = nullptr, *v1 = nullptr;
     uint32_t* eoff_own = nullptr;
+    uint32_t* rsc = nullptr;
     uint64_t* soff = nullptr;
     const PlanLeaf pl = plan_leaf(proj, leaf);
     const uint32_t* list = pl.found ? pl.list : nullptr;   // depth positions; not planned: every candidate
@@ -1042,9 +1044,11 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         const uint64_t nc = std::max<uint64_t>(C, 1);
         k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
         v0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * nc, GS_MEM_RASTER, &tmp);
-        if (!k0 || !v0) { st = GS_ERR_OOM; goto fail; }
+        // the sort's histogram, and before it the emission's block starts
+        rsc = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * radix_scratch_words((int64_t)C), GS_MEM_SCRATCH, &tmp);
+        if (!k0 || !v0 || !rsc) { st = GS_ERR_OOM; goto fail; }
     }
-    if ((st = launch_emit_cells(ctx, proj, leaf, list, n_list, eoff, ebase, C, k0, v0)) != GS_OK) goto fail;
+    if ((st = launch_emit_cells(ctx, proj, leaf, list, n_list, eoff, ebase, C, k0, v0, rsc)) != GS_OK) goto fail;
     if (eoff_own) gs_free_one(ctx, &tmp, eoff_own);
     {
         const uint64_t nc = std::max<uint64_t>(C, 1);
@@ -1058,7 +1062,7 @@ gs_status gs_bin_sort(gs_ctx* ctx, const gs_camera* cam, const gs_proj* proj, gs
         // a single-pass sort writes the super-tile group offsets itself
         bool have_soff = false;
         if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)C, bits_for(n_super), &second, soff, n_super,
-                                    &have_soff)) != GS_OK)
+                                    &have_soff, rsc)) != GS_OK)
             goto fail;
         if (!have_soff &&
             (st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)C, n_super, super_key_mask(), soff)) != GS_OK)

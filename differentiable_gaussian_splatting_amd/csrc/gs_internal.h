@@ -194,9 +194,12 @@ gs_status launch_count_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf
 // per-tile candidate counts of the leaf (row-major in the leaf) from proj->tile_cnt
 gs_status launch_leaf_counts(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, uint32_t* out);
 // (super-tile, slot) pairs at the offsets eoff - ebase (exclusive scan of the counts)
+// bst (optional, emit_blocks(total) u32 of scratch): each emission block's
+// first candidate is precomputed there instead of searched by the block
 gs_status launch_emit_cells(gs_ctx* ctx, const gs_proj* proj, gs_tile_rect leaf, const uint32_t* list,
                             int64_t n_list, const uint32_t* eoff, uint32_t ebase, uint64_t total, uint32_t* keys,
-                            uint32_t* vals);
+                            uint32_t* vals, uint32_t* bst = nullptr);
+int64_t emit_blocks(uint64_t total);
 // per-tile lists from the super-tile groups (soff: group offsets, toff: tile offsets)
 // Work items of the fine level (segments of the super-tile groups), an upper
 // bound for n_cells coarse pairs; scratch: item_sc u32 [items], ioff u32
