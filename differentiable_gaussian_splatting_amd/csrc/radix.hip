@@ -57,17 +57,20 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* sh)
     return before + x - v;
 }
 
-// Per digit (one workgroup): exclusive scan of its row of per-block counts
-// (the histogram is digit-major, so a row is contiguous), in place, and the
-// digit's total.  Each wavefront owns a quarter of the row: it sums it in
-// coalesced chunks, then rescans it chunk by chunk with a carry.
-__global__ __launch_bounds__(256) void k_radix_digit_scan(uint32_t* __restrict__ hist, int64_t nb,
-                                                          uint32_t* __restrict__ dtot)
+// Per digit (one workgroup of kDSW wavefronts): exclusive scan of its row of
+// per-block counts (the histogram is digit-major, so a row is contiguous), in
+// place, and the digit's total.  Each wavefront owns 1/kDSW of the row: it
+// sums it in coalesced chunks, then rescans it chunk by chunk with a carry.
+// With only 2^bits rows, the rescans' chains of dependent 64-entry chunks set
+// the time, hence many wavefronts per row.
+constexpr int kDSW = 16;
+__global__ __launch_bounds__(64 * kDSW) void k_radix_digit_scan(uint32_t* __restrict__ hist, int64_t nb,
+                                                                uint32_t* __restrict__ dtot)
 {
-    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t wsum[kDSW];
     uint32_t* row = hist + (int64_t)blockIdx.x * nb;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t seg = ((nb + 3) / 4 + 63) / 64 * 64;
+    const int64_t seg = ((nb + kDSW - 1) / kDSW + 63) / 64 * 64;
     const int64_t t0 = min(nb, (int64_t)wave * seg), t1 = min(nb, t0 + seg);
     uint64_t s = 0;
     for (int64_t c = t0; c < t1; c += 256) {
@@ -91,7 +94,11 @@ __global__ __launch_bounds__(256) void k_radix_digit_scan(uint32_t* __restrict__
         if (c + lane < t1) row[c + lane] = carry + x - v;
         carry += (uint32_t)__shfl((int)x, 63, 64);
     }
-    if (threadIdx.x == 0) dtot[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (threadIdx.x == 0) {
+        uint32_t tot = 0;
+        for (int w = 0; w < kDSW; ++w) tot += wsum[w];
+        dtot[blockIdx.x] = tot;
+    }
 }
 
 // Stable scatter of one block's kRTile elements: (1) local ranks in element
@@ -279,7 +286,7 @@ gs_status launch_radix_sort(gs_ctx* ctx, uint32_t* k0, uint32_t* v0, uint32_t* k
             // per digit that can occur: its row of block counts scanned in
             // place, and its total
             GsTimerScope ts(ctx, "radix");
-            hipLaunchKernelGGL(k_radix_digit_scan, dim3(mask + 1u), dim3(256), 0, ctx->stream, hist, nb, dtot);
+            hipLaunchKernelGGL(k_radix_digit_scan, dim3(mask + 1u), dim3(64 * kDSW), 0, ctx->stream, hist, nb, dtot);
         }
         {
             GsTimerScope ts(ctx, "radix");
