@@ -141,7 +141,7 @@ def main():
         grid = B.gs_grid_leaves(B.load(), cam.tiles_x, cam.tiles_y, nb, nb)
     upd = [0]   # Adam steps taken
 
-    def step(k):
+    def step(k, loss_out=None):
         if grid is not None:
             if not args.per_block_update:
                 upd[0] += 1
@@ -164,8 +164,11 @@ def main():
             return tot
         adam = None if args.no_adam else dict(step=k, params=params, m=m, v=v, lr=1e-3)
         if not args.cached_layout:
+            # loss_out: each view's loss stays on the device (a training loop
+            # reads it when it needs it), so the host queues the next view
+            # while this one's last kernels run
             return B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam,
-                                   serial_leaves=args.serial_leaves)
+                                   serial_leaves=args.serial_leaves, loss_out=loss_out)
         # the first step plans and returns its layout; later steps re-check it
         r = B.gs_train_view(ctx, cam, params, target, budget_bytes=budget, loss=w.loss, adam=adam,
                             max_leaves=0 if layout else 65536, leaves_in=layout or None)
@@ -218,14 +221,22 @@ def main():
     B.gs_reset_timing(ctx)
     B.gs_set_timing_only(ctx, dom)
     B.gs_set_timing(ctx, True)
+    losses = torch.full((args.steps,), float("nan"), dtype=torch.float64, device=dev)
+    async_loss = grid is None and not args.cached_layout
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     results = []
-    for _ in range(args.steps):
+    for i in range(args.steps):
         k += 1
-        results.append(step(k))
+        results.append(step(k, losses[i:i + 1] if async_loss else None))
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
+    if async_loss:
+        lv = losses.cpu().numpy()
+        if not np.isfinite(lv).all():
+            raise RuntimeError(f"non-finite loss in the timed steps: {lv}")
+        for rr, lo in zip(results, lv):
+            rr["loss"] = float(lo)
     B.gs_set_timing(ctx, False)
     B.gs_set_timing_only(ctx, None)
     dom_live = kernel_times(args.steps, [dom])[dom]

@@ -90,7 +90,7 @@ class gs_view_opts(C.Structure):
                 ("adam_v", C.c_void_p), ("adam_chunk", C.c_int64), ("leaves_in", C.c_void_p),
                 ("n_leaves_in", C.c_int32), ("leaves_in_partial", C.c_int32), ("gate", C.c_void_p),
                 ("gate_view", C.c_int32), ("serial_leaves", C.c_int32), ("target_host", C.c_int32),
-                ("leaf_bytes_out", C.c_void_p)]
+                ("leaf_bytes_out", C.c_void_p), ("loss_out", C.c_void_p)]
 
 
 class gs_gate_decision(C.Structure):
@@ -535,14 +535,16 @@ def gs_train_cost_model():
 
 def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0, loss="l1", lam=0.2,
                   adam=None, image_out=None, grad3d_out=None, strict=False, cost=None, max_leaves=0,
-                  leaves_in=None, partial=False, gate=None, gate_view=0, serial_leaves=False):
+                  leaves_in=None, partial=False, gate=None, gate_view=0, serial_leaves=False, loss_out=None):
     """One whole view in the library (see gs_train_view in include/gs.h).
     adam: None or dict(step, params=DeviceScene (updated), m, v, lr, beta1, beta2, eps, chunk).
     leaves_in: a cached layout (list of leaf dicts) to re-check instead of planning afresh.
     max_leaves > 0: the view's leaves are returned, each with its est_bytes and the high-water
     mark of the bytes the library held for it ("bytes").
     target: a device tensor, or a CPU tensor (pinned for the copies to overlap), which the
-    library copies leaf by leaf."""
+    library copies leaf by leaf.
+    loss_out: a device float64 tensor (one element used): the loss is written there and not read
+    back (the call does not wait for the view's end); the returned "loss" is then None."""
     o = gs_view_opts()
     o.serial_leaves = int(bool(serial_leaves))
     o.target_host = int(not target.is_cuda)
@@ -568,6 +570,11 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     o.cost = C.cast(C.pointer(cs), C.c_void_p) if cs is not None else None
     o.image_out = image_out.data_ptr() if image_out is not None else None
     o.grad3d_out = grad3d_out.data_ptr() if grad3d_out is not None else None
+    if loss_out is not None:
+        import torch
+        if not loss_out.is_cuda or loss_out.dtype != torch.float64 or loss_out.numel() < 1:
+            raise ValueError("loss_out must be a device float64 tensor")
+        o.loss_out = loss_out.data_ptr()
     o.strict_budget = int(strict)
     keep = []
     if adam is not None:
@@ -581,7 +588,8 @@ def gs_train_view(ctx: Context, cam, params: DeviceScene, target, budget_bytes=0
     res = gs_view_result()
     ctx.check(ctx.lib.gs_train_view(ctx.handle, C.byref(camera_struct(cam)), C.byref(params.struct()),
                                     _ptr(target), C.byref(o), C.byref(res)))
-    out = dict(loss=res.loss, n_cand=res.n_cand, n_isect=res.n_isect, n_leaves=res.n_leaves,
+    out = dict(loss=None if loss_out is not None else res.loss, n_cand=res.n_cand, n_isect=res.n_isect,
+               n_leaves=res.n_leaves,
                peak_bytes=res.peak_bytes, groups_walked=bool(res.groups_walked))
     if gate is not None:
         out.update(backward=bool(res.gate_backward), forced=bool(res.gate_forced), score=res.gate_score)

@@ -4,6 +4,7 @@
 // files; this file only allocates, launches, synchronises and checks.
 #include <cstdarg>
 #include <cstring>
+#include <limits>
 #include <algorithm>
 #include <cmath>
 #include <new>
@@ -1680,8 +1681,16 @@ static gs_status view_loss(gs_ctx* ctx, const gs_view_opts* opts, double* l1_vie
         // the sum adds into loss_dev: start from zero (a gated view sums twice)
         if ((st = launch_fill_u32(ctx, (uint32_t*)loss_dev, 0u, 2)) != GS_OK) return st;
         if (l1_n > 0 && (st = launch_sum_f64(ctx, l1_view, l1_n, 1, loss_dev, 1)) != GS_OK) return st;
+        if (opts->loss_out) {
+            // left on the device: the caller reads it when it needs it
+            *loss = std::numeric_limits<double>::quiet_NaN();
+            return launch_view_loss(ctx, 0, loss_dev, P, opts->ssim_lambda, opts->loss_out);
+        }
         if ((st = readback(ctx, loss_dev, sizeof(double), &s)) != GS_OK) return st;
         *loss = s / (3.0 * (double)P);
+    } else if (opts->loss_out) {
+        *loss = std::numeric_limits<double>::quiet_NaN();
+        return launch_view_loss(ctx, 1, ssim_acc, P, opts->ssim_lambda, opts->loss_out);
     } else {
         double hv[2] = {0.0, 0.0};
         if ((st = readback(ctx, ssim_acc, sizeof(hv), hv)) != GS_OK) return st;
@@ -1709,6 +1718,8 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     if (opts->loss_kind != 0 && opts->loss_kind != 1) return gs_fail(ctx, GS_ERR_INVALID_ARG, "loss_kind");
     if (opts->adam_step > 0 && (!opts->params_rw || !opts->adam_m || !opts->adam_v))
         return gs_fail(ctx, GS_ERR_INVALID_ARG, "Adam needs params_rw, adam_m, adam_v");
+    if (opts->gate && opts->loss_out)
+        return gs_fail(ctx, GS_ERR_INVALID_ARG, "a gated view needs its loss on the host (loss_out must be NULL)");
     std::memset(result, 0, sizeof(*result));
     gs_status st;
     gs_proj* proj = nullptr;

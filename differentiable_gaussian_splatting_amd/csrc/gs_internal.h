@@ -311,6 +311,10 @@ int64_t ssim_partial_blocks(int W, int H);
 // allocated and released by the call)
 gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate,
                          double* chunk_sums = nullptr);
+// A view's loss on the device: kind 0 (L1) from the sum of |x - y| at
+// sums[0]; kind 1 (L1 + SSIM) from the sums of S and |x - y| at sums[0],
+// sums[1]; normalised by 3 P, in the host's double operations.
+gs_status launch_view_loss(gs_ctx* ctx, int kind, const double* sums, int64_t P, double lambda, double* out);
 // The static work buffers of gs_loss_ssim_static on the context's device:
 // ssim_static_init (called by gs_ctx_create with the device current) looks up
 // their address once per device; ssim_static_buffers hands out the parts for

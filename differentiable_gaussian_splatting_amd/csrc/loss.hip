@@ -240,6 +240,29 @@ __global__ __launch_bounds__(kSB) void k_ssim_grad(int W, int H, Win win, Owned 
 
 }  // namespace
 
+namespace {
+
+__global__ void k_view_loss(int kind, const double* __restrict__ sums, double P3, double lambda,
+                            double* __restrict__ out)
+{
+    if (threadIdx.x != 0) return;
+    if (kind == 0) {
+        out[0] = sums[0] / P3;
+    } else {
+        const double ssim = sums[0] / P3, l1 = sums[1] / P3;
+        out[0] = (1.0 - lambda) * l1 + lambda * (1.0 - ssim);
+    }
+}
+
+}  // namespace
+
+gs_status launch_view_loss(gs_ctx* ctx, int kind, const double* sums, int64_t P, double lambda, double* out)
+{
+    hipLaunchKernelGGL(k_view_loss, dim3(1), dim3(64), 0, ctx->stream, kind, sums, 3.0 * (double)P, lambda, out);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
 gs_status launch_sum_f64(gs_ctx* ctx, const double* in, int64_t n, int stride, double* out, int accumulate,
                          double* chunk_sums)
 {

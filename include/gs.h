@@ -449,6 +449,15 @@ typedef struct {
                                  /* with its est_bytes (BoundedGS "02 /        */
                                  /* method": the budget bounds each local      */
                                  /* raster's buffers)                          */
+    double* loss_out;            /* device, nullable: the view's loss is       */
+                                 /* written there, stream-ordered, instead of  */
+                                 /* being read back, so the call returns with  */
+                                 /* the view's last kernels still queued (a    */
+                                 /* training loop reads its losses when it     */
+                                 /* needs them); result->loss is then NaN.     */
+                                 /* Same bits as the read-back value.  Not     */
+                                 /* with a gate, whose decision needs the loss */
+                                 /* on the host: GS_ERR_INVALID_ARG            */
 } gs_view_opts;
 
 typedef struct {

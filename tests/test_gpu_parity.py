@@ -579,6 +579,27 @@ def test_fixed_grid_views_match_oracle(ctx, nx, ny, blocks):
                             leaves_in=[grid[0], grid[0]], partial=True)
 
 
+@pytest.mark.parametrize("loss", ["l1", "l1_ssim"])
+def test_train_view_loss_left_on_device(ctx, loss):
+    """loss_out: the view's loss is written to the device (no read-back), with
+    the bits of the read-back value; the returned loss is None, the element
+    before it is untouched, and a gated view refuses the option."""
+    import torch
+    w = scenes.make_workload("c3_gmm4k", n=20000, width=400, height=250, posed=True, seed=151)
+    ds = B.DeviceScene(w.scene, ctx.device)
+    target = torch.from_numpy(w.target).to(ctx.device)
+    kw = dict(budget_bytes=1_400_000, cost=dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20), loss=loss)
+    say(f"case loss_out {loss}")
+    r = B.gs_train_view(ctx, w.camera, ds, target, **kw)
+    out = torch.full((2,), float("nan"), dtype=torch.float64, device=ctx.device)
+    r2 = B.gs_train_view(ctx, w.camera, ds, target, loss_out=out[1:], **kw)
+    assert r2["loss"] is None and r2["n_leaves"] == r["n_leaves"] and r["n_leaves"] > 1
+    got = out.cpu().numpy()
+    assert np.isnan(got[0]) and got[1] == r["loss"]
+    with pytest.raises(B.GsError):
+        B.gs_train_view(ctx, w.camera, ds, target, loss_out=out[1:], gate=B.Gate(2, warmup=2), gate_view=0, **kw)
+
+
 @pytest.mark.parametrize("budget,factors,falling", [
     (0, [1.0, 1.0, 0.8, 1.25, 0.9, 1.1, 1.05, 0.7, 1.3, 0.85], False),
     (1_400_000, [1.0, 1.0, 0.8, 1.25, 0.9, 1.1, 1.05, 0.7, 1.3, 0.85], False),
