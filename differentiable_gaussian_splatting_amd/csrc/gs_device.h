@@ -183,13 +183,17 @@ __device__ __forceinline__ void sh_basis_grad(int deg, float x, float y, float z
 // LDS staging of the rows of W floats of a wavefront's mw (<= 64) consecutive
 // items (src: the first item's row) into rows of stride RS.  With `aligned`
 // (src 16-byte aligned) every lane issues all of its float4 loads before the
-// first LDS store, so the loads are in flight together.
+// first LDS store, so the loads are in flight together.  need: bit r set for
+// the rows that are read later; the others are left unloaded (their LDS
+// values are unspecified).
 template <int W, int RS>
-__device__ __forceinline__ void stage_rows(float* S, const float* __restrict__ src, int mw, int lane, bool aligned)
+__device__ __forceinline__ void stage_rows(float* S, const float* __restrict__ src, int mw, int lane, bool aligned,
+                                           uint64_t need = ~0ull)
 {
     const int nv = mw * W;
     if (!aligned) {
-        for (int q = lane; q < nv; q += 64) S[(q / W) * RS + q % W] = src[q];
+        for (int q = lane; q < nv; q += 64)
+            if ((need >> (q / W)) & 1ull) S[(q / W) * RS + q % W] = src[q];
         return;
     }
     constexpr int NQ = (16 * W + 63) / 64;   // float4s per lane
@@ -197,7 +201,13 @@ __device__ __forceinline__ void stage_rows(float* S, const float* __restrict__ s
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
         const int q = 4 * (lane + 64 * r);
-        if (q + 3 < nv) {
+        // the rows the float4 touches (indices clamped into the wavefront's rows)
+        const int qa = q < nv ? q : nv - 1, qb = q + 3 < nv ? q + 3 : nv - 1;
+        const bool wanted = ((need >> (qa / W)) | (need >> (qb / W))) & 1ull;
+        if (!wanted) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[r][e] = 0.0f;
+        } else if (q + 3 < nv) {
             const float4 v = *reinterpret_cast<const float4*>(src + q);
             t[r][0] = v.x;
             t[r][1] = v.y;

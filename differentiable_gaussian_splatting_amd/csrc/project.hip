@@ -206,7 +206,12 @@ __global__ __launch_bounds__(256) void k_project_write(CamDev cam, int64_t n, co
         j = slot[i];
         logit = logits[i];
     }
-    if (w0 < n) gsd::stage_rows<3 * K, RS>(S, sh + w0 * 3 * K, (int)(n - w0 < 64 ? n - w0 : 64), lane, sh_aligned);
+    // only the candidates' SH rows are read (a wavefront's rows are contiguous:
+    // a row beside a candidate's shares its cache lines, the others are
+    // skipped)
+    const uint64_t need = gsd::ballot(cand != 0);
+    if (w0 < n)
+        gsd::stage_rows<3 * K, RS>(S, sh + w0 * 3 * K, (int)(n - w0 < 64 ? n - w0 : 64), lane, sh_aligned, need);
     gsd::wave_sync();
     if (!live) return;
     if (!cand) {
