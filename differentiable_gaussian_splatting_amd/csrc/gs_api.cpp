@@ -233,6 +233,8 @@ static gs_status ensure_tile_counts(gs_ctx* ctx, gs_proj* proj)
     return GS_OK;
 }
 
+static gs_status ensure_side(gs_ctx* ctx);
+
 // The per-tile counts of a projection on render stream 0 (idle outside a
 // view's rasters), launched by a plan that does not price intersections
 // once its own kernels are queued, so that they run beside the plan's
@@ -309,12 +311,40 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     uint64_t *segoff = nullptr, *dtbase = nullptr, *toff = nullptr;
     uint32_t* torder = nullptr;
     hipError_t e;
+    // the leaves' tile offsets and launch order need only the plan and the
+    // per-tile counts: with the streams in use they run on render stream 0
+    // (behind the counts) beside the leaf groups, and join before the leaf
+    // bounds
+    const bool toff_beside = !(ctx->timing && ctx->timing_only.empty()) && ensure_side(ctx) == GS_OK;
+    bool toff_queued = false;
+    hipStream_t main = ctx->stream;
     int32_t* lot = (int32_t*)gs_malloc(ctx, sizeof(int32_t) * T, GS_MEM_SCRATCH, &tmp);
     uint32_t* cnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<int64_t>(nc, 1), GS_MEM_SCRATCH, &tmp);
     uint64_t* goff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nc + 1), GS_MEM_SCRATCH, &tmp);
-    if (!lot || !cnt || !goff) { st = GS_ERR_OOM; goto out; }
     for (int32_t L = 0; L < nl; ++L)
         tbase[L + 1] = tbase[L] + (uint64_t)(plan[L].tx1 - plan[L].tx0) * (uint64_t)(plan[L].ty1 - plan[L].ty0) + 1;
+    dtbase = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
+    toff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
+    torder = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
+    if (!lot || !cnt || !goff || !dtbase || !toff || !torder) { st = GS_ERR_OOM; goto out; }
+    if (toff_beside) {
+        if (!proj->tile_cnt && (st = tile_counts_beside(ctx, proj)) != GS_OK) goto out;
+        if (hipEventRecord(ctx->ev_alloc, main) != hipSuccess ||
+            hipStreamWaitEvent(ctx->rstream[0], ctx->ev_alloc, 0) != hipSuccess) {
+            st = gs_fail(ctx, GS_ERR_DEVICE, "stream ordering failed");
+            goto out;
+        }
+        ctx->stream = ctx->rstream[0];
+        toff_queued = true;
+        e = hipMemcpyAsync(dtbase, tbase.data(), sizeof(uint64_t) * (nl + 1), hipMemcpyHostToDevice, ctx->stream);
+        if (e != hipSuccess) st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e));
+        if (st == GS_OK) st = launch_leaf_toff(ctx, proj, ldev, plan.data(), nl, dtbase, toff);
+        if (st == GS_OK) st = launch_tile_order_sets(ctx, nl, plan.data(), dtbase, toff, torder);
+        ctx->stream = main;
+        if (st == GS_OK && hipEventRecord(ctx->ev_toff, ctx->rstream[0]) != hipSuccess)
+            st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+        if (st != GS_OK) goto out;
+    }
     if ((st = launch_leaf_map(ctx, ldev, plan.data(), nl, proj->TW, proj->TH, lot)) != GS_OK) goto out;
     if ((st = rect_d_ready(ctx, proj)) != GS_OK) goto out;
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
@@ -327,26 +357,32 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     segoff = (uint64_t*)gs_malloc(ctx, hres.size(), GS_MEM_SCRATCH, &tmp);
     ccnt = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     coff = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * (G + 1), GS_MEM_PROJ, &proj->plan_allocs);
-    dtbase = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (nl + 1), GS_MEM_SCRATCH, &tmp);
-    toff = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
-    torder = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * tbase[nl], GS_MEM_PROJ, &proj->plan_allocs);
-    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff || !dtbase || !toff || !torder) {
+    if (!k0 || !k1 || !v0 || !v1 || !segoff || !ccnt || !coff) {
         st = GS_ERR_OOM;
         goto out;
     }
     lisect = segoff + (nl + 1);
     lcells = (uint32_t*)(lisect + nl);
-    e = hipMemcpyAsync(dtbase, tbase.data(), sizeof(uint64_t) * (nl + 1), hipMemcpyHostToDevice, ctx->stream);
-    if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
     if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, goff, k0, v0)) != GS_OK) goto out;
     if ((st = launch_radix_sort(ctx, k0, v0, k1, v1, (int64_t)G, bits_for(nl), &second)) != GS_OK) goto out;
     if ((st = launch_seg_offsets(ctx, second ? k1 : k0, (int64_t)G, nl, 0xFFFFFFFFu, segoff)) != GS_OK) goto out;
-    // the leaves' tile offsets read the per-tile counts
-    if ((st = ensure_tile_counts(ctx, proj)) != GS_OK) goto out;
-    if ((st = launch_plan_offsets(ctx, proj, ldev, plan.data(), nl, (int64_t)G, second ? k1 : k0, second ? v1 : v0,
-                                  segoff, ccnt, coff, lcells, lisect, dtbase, toff)) != GS_OK)
+    if ((st = launch_plan_offsets(ctx, proj, ldev, (int64_t)G, second ? k1 : k0, second ? v1 : v0, ccnt, coff)) !=
+        GS_OK)
         goto out;
-    if ((st = launch_tile_order_sets(ctx, nl, plan.data(), dtbase, toff, torder)) != GS_OK) goto out;
+    if (toff_beside) {
+        if (hipStreamWaitEvent(main, ctx->ev_toff, 0) != hipSuccess) {
+            st = gs_fail(ctx, GS_ERR_DEVICE, "stream wait failed");
+            goto out;
+        }
+    } else {
+        // on this stream: the counts, the tile offsets, the launch order
+        if ((st = ensure_tile_counts(ctx, proj)) != GS_OK) goto out;
+        e = hipMemcpyAsync(dtbase, tbase.data(), sizeof(uint64_t) * (nl + 1), hipMemcpyHostToDevice, ctx->stream);
+        if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
+        if ((st = launch_leaf_toff(ctx, proj, ldev, plan.data(), nl, dtbase, toff)) != GS_OK) goto out;
+        if ((st = launch_tile_order_sets(ctx, nl, plan.data(), dtbase, toff, torder)) != GS_OK) goto out;
+    }
+    if ((st = launch_leaf_bounds(ctx, ldev, nl, segoff, coff, dtbase, toff, lcells, lisect)) != GS_OK) goto out;
     e = hipMemcpyAsync(hres.data(), segoff, hres.size(), hipMemcpyDeviceToHost, ctx->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
     if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
@@ -372,6 +408,8 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     proj->plan_tbase.swap(tbase);
     proj->plan_isect.swap(hisect);
 out:
+    // render stream 0 may still use the plan's buffers on an error
+    if (st != GS_OK && toff_queued) (void)hipStreamSynchronize(ctx->rstream[0]);
     gs_free_all(ctx, &tmp);
     if (st != GS_OK) clear_plan(ctx, proj, false);
     return st;
@@ -463,6 +501,7 @@ void gs_ctx_destroy(gs_ctx* ctx)
     if (ctx->ev_alloc) (void)hipEventDestroy(ctx->ev_alloc);
     if (ctx->ev_rectd) (void)hipEventDestroy(ctx->ev_rectd);
     if (ctx->ev_counts) (void)hipEventDestroy(ctx->ev_counts);
+    if (ctx->ev_toff) (void)hipEventDestroy(ctx->ev_toff);
     if (ctx->ev_written) (void)hipEventDestroy(ctx->ev_written);
     for (hipEvent_t e : ctx->ev_done)
         if (e) (void)hipEventDestroy(e);
@@ -597,8 +636,6 @@ gs_cost_model gs_train_cost_model(void)
 
 // ---------------------------------------------------------------------------
 // projection
-
-static gs_status ensure_side(gs_ctx* ctx);
 
 gs_status gs_project(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, gs_proj** out, int64_t* n_cand)
 {
@@ -938,6 +975,7 @@ static gs_status ensure_side(gs_ctx* ctx)
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_alloc, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_rectd, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_counts, hipEventDisableTiming));
+    GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_toff, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_written, hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[0], hipEventDisableTiming));
     GS_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_done[1], hipEventDisableTiming));

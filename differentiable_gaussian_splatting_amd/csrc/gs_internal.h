@@ -47,6 +47,7 @@ struct gs_ctx {
     hipEvent_t ev_alloc = nullptr, ev_done[2] = {nullptr, nullptr};
     hipEvent_t ev_rectd = nullptr;   // a projection's depth order and rect_d written (on the second stream)
     hipEvent_t ev_counts = nullptr;  // its per-tile counts made (on render stream 0)
+    hipEvent_t ev_toff = nullptr;    // a plan's tile offsets and launch order made (render stream 0)
     hipEvent_t ev_written = nullptr; // its compact state written (on the main stream)
     // two render streams: consecutive leaves' fused rasters overlap, the
     // next one filling the compute units the current one's last tiles leave
@@ -287,14 +288,21 @@ gs_status launch_leaf_map(gs_ctx* ctx, const gs_leaf* leaves_dev, const gs_leaf*
                           int TH, int32_t* lot);
 gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int32_t n_leaves,
                             const int32_t* lot, uint32_t* cnt, const uint64_t* off, uint32_t* keys, uint32_t* vals);
-// Per-view offsets of a plan: per grouped entry (sorted by leaf) its coarse
-// pair count and their exclusive scan (u32, modulo 2^32), per leaf the scan
-// value at its first entry and its pair count (leaf_cells [2 * n_leaves]),
-// and per leaf the exclusive scan of its tile counts at toff + toff_base[L].
-gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
-                              int32_t n_leaves, int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
-                              const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
-                              uint32_t* leaf_cells, uint64_t* leaf_isect, const uint64_t* toff_base, uint64_t* toff);
+// Per-view offsets of a plan, in three parts:
+// - launch_leaf_toff: per leaf the exclusive scan of its tile counts
+//   (proj->tile_cnt) at toff + toff_base[L] (T_L + 1 entries);
+// - launch_plan_offsets: per grouped entry (sorted by leaf) its coarse pair
+//   count and their exclusive scan (u32, modulo 2^32);
+// - launch_leaf_bounds: per leaf the scan value at its first entry and its
+//   pair count (leaf_cells [2 * n_leaves]) and its intersections (the last of
+//   its tile offsets).
+gs_status launch_leaf_toff(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
+                           int32_t n_leaves, const uint64_t* toff_base, uint64_t* toff);
+gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int64_t n_entries,
+                              const uint32_t* leaf_of, const uint32_t* slot, uint32_t* cell_cnt, uint32_t* cell_off);
+gs_status launch_leaf_bounds(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, const uint64_t* group_off,
+                             const uint32_t* cell_off, const uint64_t* toff_base, const uint64_t* toff,
+                             uint32_t* leaf_cells, uint64_t* leaf_isect);
 
 // loss.hip
 // L1 + SSIM over a W x H buffer (image, target, dl_dimage [3][H][W]) that is

@@ -538,18 +538,11 @@ static int leaf_chunks(const gs_leaf* hleaves, int32_t n_leaves)
     return (int)m;
 }
 
-gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
-                              int32_t n_leaves, int64_t n_entries, const uint32_t* leaf_of, const uint32_t* slot,
-                              const uint64_t* group_off, uint32_t* cell_cnt, uint32_t* cell_off,
-                              uint32_t* leaf_cells, uint64_t* leaf_isect, const uint64_t* toff_base, uint64_t* toff)
+gs_status launch_leaf_toff(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
+                           int32_t n_leaves, const uint64_t* toff_base, uint64_t* toff)
 {
-    GsTimerScope ts(ctx, "leaf_groups");
-    if (n_entries > 0)
-        hipLaunchKernelGGL(k_group_cells, dim3((unsigned)ceil_div(n_entries, 256)), dim3(256), 0, ctx->stream,
-                           n_entries, leaf_of, slot, proj->rect_d, leaves_dev, super_shift(), cell_cnt);
-    gs_status st = launch_scan_u32_to_u32(ctx, cell_cnt, cell_off, n_entries);
-    if (st != GS_OK) return st;
     if (n_leaves > 0) {
+        GsTimerScope ts(ctx, "leaf_groups");
         const int nch = leaf_chunks(hleaves, n_leaves);
         std::vector<GsAlloc> tmp;
         uint64_t* csum = (uint64_t*)gs_malloc(ctx, sizeof(uint64_t) * (size_t)nch * n_leaves, GS_MEM_SCRATCH, &tmp);
@@ -560,9 +553,33 @@ gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* l
                            n_leaves, nch, leaves_dev, csum, toff_base, toff);
         hipLaunchKernelGGL(k_toff_write, grid, dim3(256), 0, ctx->stream, leaves_dev, proj->tile_cnt, proj->TW, csum,
                            toff_base, toff);
+        gs_free_all(ctx, &tmp);
+    }
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int64_t n_entries,
+                              const uint32_t* leaf_of, const uint32_t* slot, uint32_t* cell_cnt, uint32_t* cell_off)
+{
+    GsTimerScope ts(ctx, "leaf_groups");
+    if (n_entries > 0)
+        hipLaunchKernelGGL(k_group_cells, dim3((unsigned)ceil_div(n_entries, 256)), dim3(256), 0, ctx->stream,
+                           n_entries, leaf_of, slot, proj->rect_d, leaves_dev, super_shift(), cell_cnt);
+    gs_status st = launch_scan_u32_to_u32(ctx, cell_cnt, cell_off, n_entries);
+    if (st != GS_OK) return st;
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
+gs_status launch_leaf_bounds(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, const uint64_t* group_off,
+                             const uint32_t* cell_off, const uint64_t* toff_base, const uint64_t* toff,
+                             uint32_t* leaf_cells, uint64_t* leaf_isect)
+{
+    if (n_leaves > 0) {
+        GsTimerScope ts(ctx, "leaf_groups");
         hipLaunchKernelGGL(k_leaf_cell_bounds, dim3((unsigned)ceil_div(n_leaves, 256)), dim3(256), 0, ctx->stream,
                            n_leaves, group_off, cell_off, leaves_dev, toff_base, toff, leaf_cells, leaf_isect);
-        gs_free_all(ctx, &tmp);
     }
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
