@@ -329,15 +329,25 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     if (!lot || !cnt || !goff || !dtbase || !toff || !torder) { st = GS_ERR_OOM; goto out; }
     if (toff_beside) {
         if (!proj->tile_cnt && (st = tile_counts_beside(ctx, proj)) != GS_OK) goto out;
-        if (hipEventRecord(ctx->ev_alloc, main) != hipSuccess ||
-            hipStreamWaitEvent(ctx->rstream[0], ctx->ev_alloc, 0) != hipSuccess) {
+        if (hipEventRecord(ctx->ev_alloc, main) != hipSuccess) {
+            st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
+            goto out;
+        }
+    }
+    if ((st = launch_leaf_map(ctx, ldev, plan.data(), nl, proj->TW, proj->TH, lot)) != GS_OK) goto out;
+    if ((st = rect_d_ready(ctx, proj)) != GS_OK) goto out;
+    if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
+    if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
+    if (toff_beside) {
+        // queued after the leaf pairs' count so that the GPU starts on those
+        // first; the render stream waits only for the allocations above
+        if (hipStreamWaitEvent(ctx->rstream[0], ctx->ev_alloc, 0) != hipSuccess) {
             st = gs_fail(ctx, GS_ERR_DEVICE, "stream ordering failed");
             goto out;
         }
         ctx->stream = ctx->rstream[0];
         toff_queued = true;
-        e = hipMemcpyAsync(dtbase, tbase.data(), sizeof(uint64_t) * (nl + 1), hipMemcpyHostToDevice, ctx->stream);
-        if (e != hipSuccess) st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e));
+        st = launch_tile_bases(ctx, ldev, nl, dtbase);
         if (st == GS_OK) st = launch_leaf_toff(ctx, proj, ldev, plan.data(), nl, dtbase, toff);
         if (st == GS_OK) st = launch_tile_order_sets(ctx, nl, plan.data(), dtbase, toff, torder);
         ctx->stream = main;
@@ -345,10 +355,6 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
             st = gs_fail(ctx, GS_ERR_DEVICE, "event record failed");
         if (st != GS_OK) goto out;
     }
-    if ((st = launch_leaf_map(ctx, ldev, plan.data(), nl, proj->TW, proj->TH, lot)) != GS_OK) goto out;
-    if ((st = rect_d_ready(ctx, proj)) != GS_OK) goto out;
-    if ((st = launch_leaf_pairs(ctx, proj, ldev, nl, lot, cnt, nullptr, nullptr, nullptr)) != GS_OK) goto out;
-    if ((st = launch_scan_u32_to_u64(ctx, cnt, goff, nc)) != GS_OK) goto out;
     if ((st = readback(ctx, goff + nc, sizeof(uint64_t), &G)) != GS_OK) goto out;
     k0 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
     k1 = (uint32_t*)gs_malloc(ctx, sizeof(uint32_t) * std::max<uint64_t>(G, 1), GS_MEM_SCRATCH, &tmp);
@@ -377,8 +383,7 @@ static gs_status build_plan_groups(gs_ctx* ctx, gs_proj* proj, const gs_leaf* ld
     } else {
         // on this stream: the counts, the tile offsets, the launch order
         if ((st = ensure_tile_counts(ctx, proj)) != GS_OK) goto out;
-        e = hipMemcpyAsync(dtbase, tbase.data(), sizeof(uint64_t) * (nl + 1), hipMemcpyHostToDevice, ctx->stream);
-        if (e != hipSuccess) { st = gs_fail(ctx, GS_ERR_DEVICE, "plan copy failed: %s", hipGetErrorString(e)); goto out; }
+        if ((st = launch_tile_bases(ctx, ldev, nl, dtbase)) != GS_OK) goto out;
         if ((st = launch_leaf_toff(ctx, proj, ldev, plan.data(), nl, dtbase, toff)) != GS_OK) goto out;
         if ((st = launch_tile_order_sets(ctx, nl, plan.data(), dtbase, toff, torder)) != GS_OK) goto out;
     }

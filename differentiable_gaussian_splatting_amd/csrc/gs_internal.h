@@ -298,6 +298,9 @@ gs_status launch_leaf_pairs(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* lea
 //   its tile offsets).
 gs_status launch_leaf_toff(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
                            int32_t n_leaves, const uint64_t* toff_base, uint64_t* toff);
+// the leaves' bases in the tile-offset arrays (n_leaves + 1 entries: the sums
+// of T_L + 1 over the leaves before)
+gs_status launch_tile_bases(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, uint64_t* base);
 gs_status launch_plan_offsets(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, int64_t n_entries,
                               const uint32_t* leaf_of, const uint32_t* slot, uint32_t* cell_cnt, uint32_t* cell_off);
 gs_status launch_leaf_bounds(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, const uint64_t* group_off,

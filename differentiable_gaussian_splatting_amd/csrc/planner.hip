@@ -538,6 +538,30 @@ static int leaf_chunks(const gs_leaf* hleaves, int32_t n_leaves)
     return (int)m;
 }
 
+namespace {
+
+// base[L] = sum over the leaves before L of (their tiles + 1): where each
+// leaf's tile offsets (T_L + 1 entries) and launch order start
+__global__ void k_tile_bases(const gs_leaf* __restrict__ leaves, int nl, uint64_t* __restrict__ base)
+{
+    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    uint64_t s = 0;
+    base[0] = 0;
+    for (int L = 0; L < nl; ++L) {
+        s += (uint64_t)(leaves[L].tx1 - leaves[L].tx0) * (uint64_t)(leaves[L].ty1 - leaves[L].ty0) + 1;
+        base[L + 1] = s;
+    }
+}
+
+}  // namespace
+
+gs_status launch_tile_bases(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, uint64_t* base)
+{
+    hipLaunchKernelGGL(k_tile_bases, dim3(1), dim3(64), 0, ctx->stream, leaves_dev, (int)n_leaves, base);
+    GS_HIP(ctx, hipGetLastError());
+    return GS_OK;
+}
+
 gs_status launch_leaf_toff(gs_ctx* ctx, const gs_proj* proj, const gs_leaf* leaves_dev, const gs_leaf* hleaves,
                            int32_t n_leaves, const uint64_t* toff_base, uint64_t* toff)
 {
