@@ -652,3 +652,28 @@ def test_gated_view_sequence_matches_oracle(ctx, budget, factors, falling):
     if falling:
         assert forced > 0
     gate.close()
+
+
+@pytest.mark.parametrize("opaque", ["none", "some", "all"])
+def test_alpha_clamp_batches_bit_exact(ctx, opaque):
+    """Opacities above the alpha clamp (0.99) in none, some or all of the
+    Gaussians, so that the clamp binds on some pixels: the image is bit-exact
+    against the oracle, and the gradients (zero through a clamped alpha) and
+    the loss meet the bar, in every mix."""
+    import torch
+    w = scenes.make_workload("c1_small", n=2500, width=96, height=64, seed=205)
+    if opaque == "some":
+        w.scene.logits[::7] = 6.0          # opacity 0.9975
+    elif opaque == "all":
+        w.scene.logits[:] = 6.0
+    sc, cam = w.scene, w.camera
+    o = oracle.train_view(cam, sc, w.target)
+    ds = B.DeviceScene(sc, ctx.device)
+    img = torch.zeros((3, cam.height, cam.width), dtype=torch.float32, device=ctx.device)
+    g3 = torch.zeros((sc.n, 11 + 3 * (sc.sh_degree + 1) ** 2), dtype=torch.float32, device=ctx.device)
+    r = B.gs_train_view(ctx, cam, ds, torch.from_numpy(w.target).to(ctx.device), image_out=img, grad3d_out=g3)
+    assert np.array_equal(bits(img.cpu().numpy()), bits(o["image"]))
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    gg, og = grad3d_groups(g3.cpu().numpy(), sc.sh_degree), grad3d_groups(o["grad3d"], sc.sh_degree)
+    for name in gg:
+        assert rel_l2(gg[name], og[name]) <= GRAD_TOL, name

@@ -36,6 +36,24 @@ def test_exp_falloff_within_1ulp_of_libm(oracle_lib):
     assert ulp_diff(y, np.exp(x.astype(np.float64))).max() <= 1.0
 
 
+def test_exp_falloff_never_exceeds_one(oracle_lib):
+    # G <= 1 on [-6, 0], as exp is there: alpha = o G never exceeds o, so the
+    # clamp at 0.99 binds only for opacities above it.  A dense sweep, the f32
+    # values next to 0 and to the steps of k (where the reduced argument
+    # changes sign), every one checked.
+    x = np.linspace(-6.0, 0.0, 3_000_001, dtype=np.float32)
+    wins = [np.arange(0x80000000, 0x80000000 + 400_000, dtype=np.uint32).view(np.float32)]
+    for k in range(1, 9):
+        c = np.float32(-(k - 0.5) * math.log(2.0))
+        u = c.view(np.uint32)
+        wins.append(np.arange(u - 50_000, u + 50_000, dtype=np.uint32).view(np.float32))
+    x = np.concatenate([x] + wins)
+    x = x[(x >= -6.0) & (x <= 0.0)]
+    y = oracle_lib.exp_falloff(x)
+    assert (y <= np.float32(1.0)).all()
+    assert (y[np.abs(x) < 1e-8] == np.float32(1.0)).all()
+
+
 def test_exp_falloff_clamp_keeps_every_skip_decision(oracle_lib):
     y = oracle_lib.exp_falloff(np.array([0.0, -0.0, 0.5, 1e30, -6.0, -6.5, -87.0, -1e30], np.float32))
     assert y[0] == 1.0 and y[1] == 1.0 and y[2] == 1.0 and y[3] == 1.0
