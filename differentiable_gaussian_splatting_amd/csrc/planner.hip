@@ -541,15 +541,38 @@ static int leaf_chunks(const gs_leaf* hleaves, int32_t n_leaves)
 namespace {
 
 // base[L] = sum over the leaves before L of (their tiles + 1): where each
-// leaf's tile offsets (T_L + 1 entries) and launch order start
-__global__ void k_tile_bases(const gs_leaf* __restrict__ leaves, int nl, uint64_t* __restrict__ base)
+// leaf's tile offsets (T_L + 1 entries) and launch order start.  One block:
+// thread t sums a run of consecutive leaves, the runs are scanned across the
+// block, and each thread writes its run's bases.
+constexpr int kBaseThreads = 1024;
+
+__device__ __forceinline__ uint64_t leaf_slots(const gs_leaf& L)
 {
-    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    return (uint64_t)(L.tx1 - L.tx0) * (uint64_t)(L.ty1 - L.ty0) + 1;
+}
+
+__global__ __launch_bounds__(kBaseThreads) void k_tile_bases(const gs_leaf* __restrict__ leaves, int nl,
+                                                             uint64_t* __restrict__ base)
+{
+    __shared__ uint64_t ws[kBaseThreads / 64];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int per = (nl + kBaseThreads - 1) / kBaseThreads;
+    const int l0 = min(nl, t * per), l1 = min(nl, l0 + per);
     uint64_t s = 0;
-    base[0] = 0;
-    for (int L = 0; L < nl; ++L) {
-        s += (uint64_t)(leaves[L].tx1 - leaves[L].tx0) * (uint64_t)(leaves[L].ty1 - leaves[L].ty0) + 1;
-        base[L + 1] = s;
+    for (int L = l0; L < l1; ++L) s += leaf_slots(leaves[L]);
+    uint64_t x = s;   // inclusive scan over the wavefront
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t u = __shfl_up(x, o, 64);
+        if (lane >= o) x += u;
+    }
+    if (lane == 63) ws[w] = x;
+    __syncthreads();
+    uint64_t run = x - s;
+    for (int v = 0; v < w; ++v) run += ws[v];
+    if (t == 0) base[0] = 0;
+    for (int L = l0; L < l1; ++L) {
+        run += leaf_slots(leaves[L]);
+        base[L + 1] = run;
     }
 }
 
@@ -557,7 +580,7 @@ __global__ void k_tile_bases(const gs_leaf* __restrict__ leaves, int nl, uint64_
 
 gs_status launch_tile_bases(gs_ctx* ctx, const gs_leaf* leaves_dev, int32_t n_leaves, uint64_t* base)
 {
-    hipLaunchKernelGGL(k_tile_bases, dim3(1), dim3(64), 0, ctx->stream, leaves_dev, (int)n_leaves, base);
+    hipLaunchKernelGGL(k_tile_bases, dim3(1), dim3(kBaseThreads), 0, ctx->stream, leaves_dev, (int)n_leaves, base);
     GS_HIP(ctx, hipGetLastError());
     return GS_OK;
 }

@@ -677,3 +677,30 @@ def test_alpha_clamp_batches_bit_exact(ctx, opaque):
     gg, og = grad3d_groups(g3.cpu().numpy(), sc.sh_degree), grad3d_groups(o["grad3d"], sc.sh_degree)
     for name in gg:
         assert rel_l2(gg[name], og[name]) <= GRAD_TOL, name
+
+
+def test_train_view_more_leaves_than_a_block(ctx):
+    """A budget below every single tile's estimate: the plan is one leaf per
+    tile, 1200 of them, more than the 1024 threads that sum the leaves' tile
+    bases (so each thread takes a run of leaves).  Leaves, intersections,
+    loss, image and the 3D gradient groups against the oracle's leaf mode."""
+    import torch
+    w = scenes.make_workload("c3_gmm4k", n=6000, width=640, height=480, seed=206)
+    cost = dict(b_isect=20, b_pixel=20, b_tile=64, b_const=1 << 20)
+    ds = B.DeviceScene(w.scene, ctx.device)
+    K = (w.scene.sh_degree + 1) ** 2
+    g3 = torch.zeros((w.scene.n, 11 + 3 * K), dtype=torch.float32, device=ctx.device)
+    img = torch.zeros((3, w.camera.height, w.camera.width), dtype=torch.float32, device=ctx.device)
+    r = B.gs_train_view(ctx, w.camera, ds, torch.from_numpy(w.target).to(ctx.device), budget_bytes=1, cost=cost,
+                        image_out=img, grad3d_out=g3, max_leaves=2048)
+    o = oracle.train_view(w.camera, w.scene, w.target, budget=1, cost=cost)
+    say(f"{r['n_leaves']} leaves")
+    assert r["n_leaves"] == 40 * 30 == len(o["leaves"])
+    got = [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in r["leaves"]]
+    assert got == [(L["tx0"], L["ty0"], L["tx1"], L["ty1"]) for L in o["leaves"]]
+    assert r["n_isect"] == o["n_isect"]
+    assert abs(r["loss"] - o["loss"]) <= LOSS_TOL
+    assert np.abs(img.cpu().numpy() - o["image"]).max() <= IMG_TOL
+    gg, og = grad3d_groups(g3.cpu().numpy(), w.scene.sh_degree), grad3d_groups(o["grad3d"], w.scene.sh_degree)
+    for name in gg:
+        assert rel_l2(gg[name], og[name]) <= GRAD_TOL, name
