@@ -1716,14 +1716,14 @@ done:
 // The view's loss: L1 from the per-tile partials (one sum, one read-back);
 // L1 + SSIM from the sums of |x - y| and S over the leaves (ssim_acc).
 static gs_status view_loss(gs_ctx* ctx, const gs_view_opts* opts, double* l1_view, int64_t l1_n, double* loss_dev,
-                           const double* ssim_acc, int64_t P, double* loss)
+                           const double* ssim_acc, int64_t P, double* loss, double* sum_chunks)
 {
     gs_status st;
     if (opts->loss_kind == 0) {
         double s = 0.0;
         // the sum adds into loss_dev: start from zero (a gated view sums twice)
         if ((st = launch_fill_u32(ctx, (uint32_t*)loss_dev, 0u, 2)) != GS_OK) return st;
-        if (l1_n > 0 && (st = launch_sum_f64(ctx, l1_view, l1_n, 1, loss_dev, 1)) != GS_OK) return st;
+        if (l1_n > 0 && (st = launch_sum_f64(ctx, l1_view, l1_n, 1, loss_dev, 1, sum_chunks)) != GS_OK) return st;
         if (opts->loss_out) {
             // left on the device: the caller reads it when it needs it
             *loss = std::numeric_limits<double>::quiet_NaN();
@@ -1844,6 +1844,9 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     // loss_dev[0]: the L1 sum; loss_dev[1..2]: the SSIM view's sums of S and
     // |x - y|
     double* loss_dev = (double*)gs_malloc(ctx, 3 * sizeof(double), GS_MEM_SCRATCH, &view);
+    // the loss sum's chunk sums, allocated here so that nothing is allocated
+    // once the update has started
+    double* sum_chunks = (double*)gs_malloc(ctx, 256 * sizeof(double), GS_MEM_SCRATCH, &view);
     const int64_t P = (int64_t)cam->width * cam->height;
     float* image = opts->image_out;
     double loss = 0.0;
@@ -1854,7 +1857,10 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
     double* l1_view = opts->loss_kind == 0 && l1_n > 0
                           ? (double*)gs_malloc(ctx, sizeof(double) * l1_n, GS_MEM_LOSS, &view)
                           : nullptr;
-    if (!grad2d || !loss_dev || (opts->loss_kind == 0 && l1_n > 0 && !l1_view)) { st = GS_ERR_OOM; goto done; }
+    if (!grad2d || !loss_dev || !sum_chunks || (opts->loss_kind == 0 && l1_n > 0 && !l1_view)) {
+        st = GS_ERR_OOM;
+        goto done;
+    }
     if ((st = launch_fill_f32(ctx, grad2d, 0.0f, 9 * nc)) != GS_OK) goto done;
     if ((st = launch_fill_u32(ctx, (uint32_t*)loss_dev, 0u, 6)) != GS_OK) goto done;
     if (opts->gate) {
@@ -1865,7 +1871,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
         if ((st = render_leaves(ctx, cam, proj, target, opts, leaves, false, grad2d, l1_view, image, loss_dev + 1,
                                 &isect_total, walk, &walk_used)) != GS_OK)
             goto done;
-        if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss)) != GS_OK) goto done;
+        if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss, sum_chunks)) != GS_OK) goto done;
         gs_gate_decision d{};
         if ((st = gs_gate_step(opts->gate, opts->gate_view, loss, &d)) != GS_OK) {
             st = gs_fail(ctx, st, "gate step (view %d, loss %g)", (int)opts->gate_view, loss);
@@ -1922,7 +1928,7 @@ gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* para
                 goto done;
         }
     }
-    if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss)) != GS_OK) goto done;
+    if ((st = view_loss(ctx, opts, l1_view, l1_n, loss_dev, loss_dev + 1, P, &loss, sum_chunks)) != GS_OK) goto done;
 finish:
     result->loss = loss;
     result->n_cand = n_cand;

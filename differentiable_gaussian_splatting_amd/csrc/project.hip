@@ -516,7 +516,9 @@ __global__ __launch_bounds__(256) void k_bwd_adam(CamDev cam, int64_t n, const f
         gi = load_gauss(means, log_scales, quats, i);
         logit = logits[i];
     }
-    gsd::stage_rows<W, RS>(S, sh + w0 * W, mw, lane, sh_aligned);
+    // only the candidates' SH rows are staged (the projection backward reads
+    // them; the update below reads every row from memory)
+    gsd::stage_rows<W, RS>(S, sh + w0 * W, mw, lane, sh_aligned, gsd::ballot(s >= 0));
     gsd::wave_sync();
     float geo[11], Y[16], grm[3];
 #pragma unroll

@@ -90,13 +90,16 @@ def _workload(name="c3_gmm4k", **kw):
     return scenes.make_workload(name, **kw)
 
 
-@pytest.mark.parametrize("mode", ["pipelined", "serial", "one_leaf", "ssim", "host_target", "chunked"])
+@pytest.mark.parametrize("mode", ["pipelined", "serial", "one_leaf", "ssim", "host_target", "chunked", "wide"])
 def test_train_view_allocation_failure_at_every_call(fctx, mode):
     """gs_train_view with the allocator failing at each of its calls in turn:
     GS_ERR_OOM, live bytes back, parameters and moments untouched; then a
-    view without failures equals the one before."""
+    view without failures equals the one before.  "wide": 640 x 480, enough
+    tiles (over 1024) that the view's L1 sum runs in chunks, whose buffer
+    must be allocated before the update starts."""
     import torch
-    w = _workload(n=20000, width=300, height=200, seed=151)
+    wide = mode == "wide"
+    w = _workload(n=20000, width=640 if wide else 300, height=480 if wide else 200, seed=151)
     dev = fctx.device
     ds = B.DeviceScene(w.scene, dev)
     m, v = B.like_scene(ds), B.like_scene(ds)
