@@ -516,6 +516,12 @@ typedef struct {
  * slice as b_pixel (L1; with overlapped leaves up to three slices are held
  * at once).  target: device [3][H][W], or host memory with
  * target_host (BoundedGS page, "02 / method": bounded image feeding).
+ * Errors: INVALID_ARG, OOM, BUDGET (strict planning), OVERFLOW, DEVICE.  On
+ * error the parameters and moments are untouched (everything the view
+ * allocates is allocated before its update is queued), but image_out and
+ * grad3d_out may hold a partial result: the leaves are rendered one after
+ * another in bounded memory, so a failure at a later leaf comes after the
+ * earlier leaves wrote their pixels.
  * Synchronises. */
 gs_status gs_train_view(gs_ctx* ctx, const gs_camera* cam, const gs_params* params, const float* target,
                         const gs_view_opts* opts, gs_view_result* result);
