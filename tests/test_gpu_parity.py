@@ -488,8 +488,8 @@ def test_replan_cached_layout_matches_oracle(ctx, budget_b):
 
 
 def test_train_view_with_cached_layout(ctx):
-    """Round 1 of a view returns its layout; round 2 (another view of the
-    sequence) re-checks that layout instead of planning afresh: loss, image,
+    """The first view of a sequence returns its layout; the next view
+    re-checks that layout instead of planning afresh: loss, image,
     leaves and every gradient group against the oracle's view over the
     oracle's re-check of the same layout."""
     import torch
@@ -510,7 +510,7 @@ def test_train_view_with_cached_layout(ctx):
     o32 = oracle.project(wb.camera, wb.scene, "f32")
     leaves = oracle.plan_leaves(wb.camera, o32["rect"][o32["cand"]], budget, cost, roots=cached)
     o = oracle.train_view(wb.camera, wb.scene, wb.target, leaves=leaves, cost=cost)
-    say(f"round 2: {len(cached)} cached leaves -> {rb['n_leaves']}")
+    say(f"next view: {len(cached)} cached leaves -> {rb['n_leaves']}")
     assert _rects(rb["leaves"]) == _rects(leaves)
     assert abs(rb["loss"] - o["loss"]) <= LOSS_TOL
     assert np.abs(img.cpu().numpy() - o["image"]).max() <= IMG_TOL
